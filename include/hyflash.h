@@ -1,0 +1,177 @@
+/*
+ * libhyflash — the hot path of one HyFlash drafter layer on AMD MI355X (gfx950).
+ *
+ * HyFlash ("HyFlash: A Prefix-Memory Prior for On-Device Speculative Decoding")
+ * drafts a block of seven future positions plus an anchor slot in one pass.  Each
+ * drafter layer has two branches (HyFlash explainer, "That is HyFlash"):
+ *   - a local-attention branch over the most recent committed target features and
+ *     the block's own rows, in both directions;
+ *   - a recurrent memory (Mamba-2) holding the committed history in a fixed-size
+ *     state H, read while drafting and written only after verification, by the
+ *     newly committed features alone (explainer FAQ, "Why does the memory update
+ *     only from committed features?").
+ *
+ * Conventions shared by every call
+ *   - Pointers are DEVICE pointers unless marked (host).  The caller owns all memory:
+ *     weights, the state pool, inputs, outputs and the workspace.  The library never
+ *     allocates or frees device memory and keeps no mutable global state.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls only
+ *     enqueue work on it and return without synchronizing.
+ *   - Every call returns an hyf_status.  All conditions that can be checked on the
+ *     host are checked before the first launch, so a call that returns an error other
+ *     than HYF_EHIP has not touched device memory.  HYF_EHIP means a launch failed;
+ *     the states named in that call are then undefined and must be reset.
+ *   - Calls on different streams are safe when they name disjoint state slots and
+ *     disjoint workspaces.
+ *   - Storage dtype (cfg.dtype) applies to weights, features, block rows, ring K/V and
+ *     outputs; the recurrent state H is always fp32 (explainer, "Where it earns its
+ *     keep": the recurrent state is FP32).
+ */
+#ifndef HYFLASH_H
+#define HYFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HYF_ABI_VERSION 1
+/* Requests per call (state slots touched by one commit or draft call). */
+#define HYF_MAX_REQUESTS 128
+/* Rows of the draft block: anchor + seven draft positions (explainer, "Jargon"). */
+#define HYF_BLOCK 8
+
+typedef enum {
+  HYF_OK = 0,
+  HYF_EINVAL = 1,       /* null pointer, misaligned pointer, bad count or offsets   */
+  HYF_ESHAPE = 2,       /* unsupported or inconsistent shape                         */
+  HYF_ECAPACITY = 3,    /* too many requests or rows, slot outside the pool          */
+  HYF_EDTYPE = 4,       /* unknown dtype                                             */
+  HYF_EWORKSPACE = 5,   /* ws_bytes smaller than the size the matching query returns */
+  HYF_EUNSUPPORTED = 6, /* a mode this build does not implement                      */
+  HYF_EHIP = 7          /* a HIP launch failed                                       */
+} hyf_status;
+
+typedef enum { HYF_F32 = 0, HYF_BF16 = 1 } hyf_dtype;
+typedef enum { HYF_MEM_MAMBA2 = 0, HYF_MEM_GDN = 1 } hyf_memory;
+
+/* Layer shape.  48 bytes, all int32. */
+typedef struct {
+  int32_t d_model;    /* d                                                             */
+  int32_t n_heads;    /* nh; attention heads = memory heads; nh*head_dim is the q/k/v width */
+  int32_t head_dim;   /* P: multiple of 16, at most 256                                 */
+  int32_t d_state;    /* N: multiple of 16, at most 256                                 */
+  int32_t n_groups;   /* G: B and C are shared by nh/G heads each; must divide nh       */
+  int32_t window;     /* W: ring capacity in committed rows (1..8192)                   */
+  int32_t block;      /* must be HYF_BLOCK                                             */
+  int32_t chunk;      /* SSD chunk length L (16..1024, multiple of 16)                  */
+  int32_t dtype;      /* hyf_dtype                                                      */
+  int32_t memory;     /* hyf_memory; only HYF_MEM_MAMBA2 is implemented                 */
+  int32_t cross_slot; /* 1: block rows attend to each other; 0: each only to itself     */
+  int32_t reserved;   /* must be 0                                                      */
+} hyf_config;
+
+/* Layer weights, nn.Linear layout ([out_features][in_features], row-major).
+ * w_in rows come in groups, in this order:
+ *   q [nh*P] | C [G*N] | k [nh*P] | v [nh*P] | B [G*N] | dt [nh]      (n_in rows in all)
+ * The value projection v is also the memory's input x.  a_log, dt_bias and d_skip are
+ * fp32 per head: A = -exp(a_log), dt = softplus(raw + dt_bias), D = d_skip. */
+typedef struct {
+  const void* w_in;     /* [n_in][d_model], storage dtype, 16-byte aligned */
+  const void* w_out;    /* [d_model][nh*P], storage dtype, 16-byte aligned */
+  const float* a_log;   /* [nh] */
+  const float* dt_bias; /* [nh] */
+  const float* d_skip;  /* [nh] */
+} hyf_weights;
+
+/* Byte offsets inside one request's state blob (each section 256-byte aligned):
+ *   header: int64 committed count at offset 0 (the ring head is count mod W), rest 0
+ *   H:      fp32 [nh][P][N]
+ *   K, V:   storage dtype [nh][W][P]; committed row c of the request sits in slot c mod W */
+typedef struct {
+  uint64_t count_off, h_off, k_off, v_off, total;
+} hyf_state_layout;
+
+int hyf_abi_version(void);
+const char* hyf_status_str(int status);
+
+/* Host only.  HYF_OK if cfg describes a shape this build runs. */
+int hyf_config_check(const hyf_config* cfg);
+
+/* Host only.  Size of the input projection's output (n_in above); 0 on a bad cfg. */
+int64_t hyf_n_in(const hyf_config* cfg);
+
+/* Host only.  Fills *out; one request's state for one layer. */
+int hyf_state_layout_get(const hyf_config* cfg, hyf_state_layout* out);
+/* Host only.  Bytes of one state blob (= layout.total, a multiple of 256); 0 on a bad cfg.
+ * A state pool is pool_slots blobs back to back. */
+size_t hyf_state_bytes(const hyf_config* cfg);
+
+/* Host only.  Workspace bytes that hyf_memory_commit and hyf_draft_block need for up to
+ * max_requests requests and up to max_rows committed rows in one call (summed over the
+ * requests).  0 on bad arguments. */
+size_t hyf_workspace_bytes(const hyf_config* cfg, int32_t max_requests, int64_t max_rows);
+
+/* Empties the named states: count = 0, H = 0, ring zeroed.
+ * slots (host, nullable): pool index of each request; NULL means 0..n_req-1. */
+int hyf_state_reset(const hyf_config* cfg, void* state_pool, int32_t pool_slots,
+                    const int32_t* slots, int32_t n_req, void* stream);
+
+/* Commit: the only writer of committed state (explainer, "That is HyFlash": after
+ * verification only the newly committed features update the memory).
+ * Request i folds rows feats[cu_rows[i] .. cu_rows[i+1]) — its newly committed target
+ * features, [rows][d_model] in storage dtype — into its state, in order:
+ *   k, v, B, dt_raw from w_in; H <- exp(dt*A) H + dt * (v outer B) token by token
+ *   (computed as a chunked scan); the last min(rows, W) (k, v) pairs enter the ring at
+ *   slots (count + j) mod W; count += rows.
+ * Any row count works (a prefill of a whole prefix, or the 1-8 rows of a round).
+ * cu_rows (host): int64 [n_req + 1], cu_rows[0] = 0, non-decreasing.  Empty requests
+ * are left bit-identical.
+ * y_opt (nullable): [cu_rows[n_req]][nh][P] storage dtype, per-token memory outputs
+ * y_t = H_t . C_t + D * v_t (H_t after token t).
+ * ws: at least hyf_workspace_bytes(cfg, n_req, cu_rows[n_req]) bytes, 256-byte aligned. */
+int hyf_memory_commit(const hyf_config* cfg, const hyf_weights* w, void* state_pool,
+                      int32_t pool_slots, const int32_t* slots, int32_t n_req, const void* feats,
+                      const int64_t* cu_commit, void* y_opt, void* ws, size_t ws_bytes,
+                      void* stream);
+
+/* One draft step for n_req requests (paper Abstract; explainer "That is HyFlash").
+ * If commit_feats is not NULL, the call first performs exactly hyf_memory_commit on those
+ * rows (cu_commit (host) as cu_rows above, at most `block` rows per request), sharing one
+ * pass over w_in with the block rows.  Then, per request and head, with block rows
+ * block_in [n_req][block][d_model]:
+ *   q, k, v, C_q from w_in;
+ *   attn = softmax(q . keys / sqrt(P)) . values, keys = the last min(count, W) committed
+ *          rows in the ring plus all block rows (no causal mask; cross_slot = 0 hides the
+ *          other block rows);
+ *   mem  = H . C_q + D * v   (H is read, never written);
+ *   block_out [n_req][block][d_model] = concat_heads(attn + mem) . w_out^T.
+ * Drafting never writes the state: with commit_feats == NULL the state pool is left bit-
+ * identical.  ws: at least hyf_workspace_bytes(cfg, n_req, cu_commit[n_req]) bytes. */
+int hyf_draft_block(const hyf_config* cfg, const hyf_weights* w, void* state_pool,
+                    int32_t pool_slots, const int32_t* slots, int32_t n_req,
+                    const void* commit_feats, const int64_t* cu_commit, const void* block_in,
+                    void* block_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Host only.  Workspace bytes hyf_ssd_scan needs for T tokens. */
+size_t hyf_ssd_scan_workspace_bytes(const hyf_config* cfg, int64_t T);
+
+/* The memory's chunked scan on pre-projected inputs, one request (explainer "Jargon":
+ * Mamba-2 folds each input into a fixed-size state with an input-dependent step size and a
+ * learned decay).  For t = 0..T-1, per head h:
+ *   dt = softplus(dt_raw[t][h] + dt_bias[h]);  H_h <- exp(dt * A_h) H_h + dt * x[t][h] outer B[t][g(h)]
+ *   y[t][h] = H_h . C[t][g(h)] + d_skip[h] * x[t][h]           (only if y_opt)
+ * x [T][nh][P], B and C_opt [T][G*N] storage dtype; dt_raw [T][nh] fp32;
+ * H_inout [nh][P][N] fp32 holds the initial state on entry and the final state on exit.
+ * C_opt is required iff y_opt is given.  T = 0 is a no-op. */
+int hyf_ssd_scan(const hyf_config* cfg, const void* x, const void* B, const void* C_opt,
+                 const float* dt_raw, const float* a_log, const float* dt_bias,
+                 const float* d_skip, float* H_inout, void* y_opt, int64_t T, void* ws,
+                 size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HYFLASH_H */

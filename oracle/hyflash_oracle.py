@@ -1,0 +1,291 @@
+"""CPU oracle for the HyFlash drafter-layer hot path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or run
+this module: only the tests, the smoke check of the package entry file and the
+CPU-baseline leg of the benchmark do.  It shares no code with the HIP library.
+
+Plain NumPy in float64, written for a reader to check against the HyFlash
+pages by eye, not for speed.  Sources (page title, then section):
+
+* HyFlash paper page, Abstract: local attention over recent context and the
+  draft positions; a recurrent memory that compresses the committed history of
+  target features into a fixed-size state.
+* HyFlash explainer, "That is HyFlash": every layer has a local-attention
+  branch (last committed features plus all seven draft positions, in both
+  directions) and a Mamba-2 branch that holds the committed history, is only
+  read while drafting, and is updated after verification by the newly
+  committed features alone.
+* HyFlash explainer, "Jargon": Mamba-2 folds each input into a fixed-size
+  state with an input-dependent step size and a learned decay; a block is
+  seven draft positions.
+* HyFlash explainer, FAQ "Why does the memory update only from committed
+  features?": drafting reads the state and never writes it.
+* HyFlash explainer, "Where it earns its keep": the recurrent state is fp32.
+
+The pages print no formulas.  Readings taken here (each listed in the design
+notes of the repository):
+
+* Recurrence: the plain Mamba-2 / SSD form with one scalar decay per head,
+      h_t = exp(dt_t * A) * h_{t-1} + dt_t * (x_t outer B_t),   y_t = h_t . C_t + D * x_t,
+  dt_t = softplus(raw_t + dt_bias), A = -exp(A_log); y uses the state after
+  token t.  The SSM input x is the value projection v.  B and C are shared by
+  the heads of a group (one group by default).
+* Attention: scale 1/sqrt(head_dim), no positional encoding, no causal mask
+  inside the block (all block rows, anchor included, are queries and keys);
+  keys are the last min(count, window) committed rows plus the block rows.
+* The two branches are summed per head, then one output projection.
+* Ring slot of committed row c (0-based over the request's life) is c mod W.
+* Stored values (ring K/V) are rounded to the storage dtype; everything else
+  stays float64.
+
+Parity is pinned for every function below by tests that compare against
+closed forms, library routines or brute force (see tests/test_oracle_pins.py).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+F64 = np.float64
+
+
+# ----------------------------------------------------------------------------
+# small helpers
+
+
+def softplus(z):
+    """log(1 + e^z), evaluated without overflow (NumPy's logaddexp with 0)."""
+    return np.logaddexp(0.0, np.asarray(z, dtype=F64))
+
+
+def round_storage(a, dtype: str) -> np.ndarray:
+    """Round float64 values to the storage dtype (nearest even), returned as float64.
+
+    bf16 rounding goes through float32 first; torch's CPU cast does the
+    float32 -> bfloat16 step.
+    """
+    a32 = np.asarray(a, dtype=F64).astype(np.float32)
+    if dtype == "f32":
+        return a32.astype(F64)
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(a32)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def head_groups(n_heads: int, n_groups: int) -> np.ndarray:
+    """Group index of each head (B and C are shared by the heads of a group)."""
+    assert n_heads % n_groups == 0
+    return np.arange(n_heads) // (n_heads // n_groups)
+
+
+def per_head(bc, n_heads: int, n_groups: int) -> np.ndarray:
+    """[T][G*N] -> [T][nh][N]: each head sees its group's B (or C) row."""
+    T, GN = bc.shape
+    N = GN // n_groups
+    return np.asarray(bc, dtype=F64).reshape(T, n_groups, N)[:, head_groups(n_heads, n_groups), :]
+
+
+def step_and_decay(dt_raw, dt_bias, a_log):
+    """Input-dependent step dt = softplus(raw + bias) and log-decay ell = dt * A, A = -exp(A_log).
+
+    HyFlash explainer, "Jargon", Mamba-2 entry (input-dependent step size, learned decay).
+    Returns (dt, ell), each [T][nh] float64.
+    """
+    dt = softplus(np.asarray(dt_raw, F64) + np.asarray(dt_bias, F64)[None, :])
+    A = -np.exp(np.asarray(a_log, F64))
+    return dt, dt * A[None, :]
+
+
+# ----------------------------------------------------------------------------
+# the recurrent memory (Mamba-2 / SSD) on pre-projected inputs
+
+
+def ssd_sequential(x, B, C, dt_raw, a_log, dt_bias, d_skip, H0, n_groups: int = 1):
+    """The definition: one token at a time.
+
+    x [T][nh][P], B and C [T][G*N] (C may be None), dt_raw [T][nh], H0 [nh][P][N].
+    Returns (H_T [nh][P][N], y [T][nh][P] or None), float64.
+    """
+    x = np.asarray(x, F64)
+    T, nh, P = x.shape
+    Bh = per_head(B, nh, n_groups)
+    Ch = per_head(C, nh, n_groups) if C is not None else None
+    dt, ell = step_and_decay(dt_raw, dt_bias, a_log)
+    D = np.asarray(d_skip, F64)
+    H = np.array(H0, dtype=F64, copy=True)
+    y = np.zeros((T, nh, P), F64) if Ch is not None else None
+    for t in range(T):
+        decay = np.exp(ell[t])                                   # [nh]
+        write = (dt[t][:, None] * x[t])[:, :, None] * Bh[t][:, None, :]   # [nh][P][N]
+        H = decay[:, None, None] * H + write
+        if y is not None:
+            y[t] = np.einsum("hpn,hn->hp", H, Ch[t]) + D[:, None] * x[t]
+    return H, y
+
+
+def ssd_chunked(x, B, C, dt_raw, a_log, dt_bias, d_skip, H0, chunk: int, n_groups: int = 1):
+    """The chunked SSD algorithm; equal to ssd_sequential up to rounding.
+
+    Per chunk of `chunk` tokens:
+      1. Lam = inclusive cumulative sum of ell inside the chunk;
+      2. chunk state S = sum_tau exp(Lam_end - Lam_tau) * dt_tau * x_tau outer B_tau;
+      3. outputs (if C): intra-chunk quadratic form
+            y_t = sum_{tau <= t} (C_t . B_tau) * exp(Lam_t - Lam_tau) * dt_tau * x_tau
+         plus the carried state exp(Lam_t) * (H_prev . C_t), plus D * x_t;
+      4. state pass H = exp(Lam_end) * H_prev + S.
+    Exponents are always differences of log-decays (never ratios of exps).
+    """
+    x = np.asarray(x, F64)
+    T, nh, P = x.shape
+    Bh = per_head(B, nh, n_groups)
+    Ch = per_head(C, nh, n_groups) if C is not None else None
+    dt, ell = step_and_decay(dt_raw, dt_bias, a_log)
+    D = np.asarray(d_skip, F64)
+    H = np.array(H0, dtype=F64, copy=True)
+    y = np.zeros((T, nh, P), F64) if Ch is not None else None
+    for c0 in range(0, T, chunk):
+        s = slice(c0, min(c0 + chunk, T))
+        Lam = np.cumsum(ell[s], axis=0)                          # [Lc][nh]
+        w_end = np.exp(Lam[-1][None, :] - Lam) * dt[s]           # [Lc][nh]
+        S = np.einsum("th,thp,thn->hpn", w_end, x[s], Bh[s])
+        if y is not None:
+            Lc = Lam.shape[0]
+            causal = np.tril(np.ones((Lc, Lc), dtype=bool))      # [t][tau], tau <= t
+            diff = np.where(causal[:, :, None], Lam[:, None, :] - Lam[None, :, :], -np.inf)
+            M = np.exp(diff) * dt[s][None, :, :]                 # [t][tau][nh]
+            CB = np.einsum("thn,shn->tsh", Ch[s], Bh[s])          # [t][tau][nh]
+            y_intra = np.einsum("tsh,shp->thp", CB * M, x[s])
+            y_carry = np.exp(Lam)[:, :, None] * np.einsum("hpn,thn->thp", H, Ch[s])
+            y[s] = y_intra + y_carry + D[None, :, None] * x[s]
+        H = np.exp(Lam[-1])[:, None, None] * H + S
+    return H, y
+
+
+# ----------------------------------------------------------------------------
+# the layer: projections, ring, attention, readout, output projection
+
+
+def split_projection(proj, shape):
+    """Columns of [rows][n_in] in storage order q | C | k | v | B | dt -> dict of views."""
+    n = proj.shape[0]
+    out = {}
+    for name, (a, b) in shape.in_groups.items():
+        out[name] = proj[:, a:b]
+    nh, P = shape.n_heads, shape.head_dim
+    for name in ("q", "k", "v"):
+        out[name] = out[name].reshape(n, nh, P)
+    return out
+
+
+def project(rows, w):
+    """rows [n][in] times an nn.Linear weight [out][in] -> [n][out], float64."""
+    return np.asarray(rows, F64) @ np.asarray(w, F64).T
+
+
+def new_state(shape) -> dict:
+    """Empty per-request state: nothing committed, H = 0, empty ring."""
+    nh, P, N, W = shape.n_heads, shape.head_dim, shape.d_state, shape.window
+    return dict(count=0, H=np.zeros((nh, P, N), F64),
+                K=np.zeros((nh, W, P), F64), V=np.zeros((nh, W, P), F64))
+
+
+def copy_state(st: dict) -> dict:
+    return dict(count=st["count"], H=st["H"].copy(), K=st["K"].copy(), V=st["V"].copy())
+
+
+def ring_append(shape, st: dict, k, v) -> None:
+    """Committed row c (0-based over the request) goes to slot c mod W; values stored rounded."""
+    W = shape.window
+    kr = round_storage(k, shape.dtype)
+    vr = round_storage(v, shape.dtype)
+    for i in range(kr.shape[0]):
+        slot = st["count"] % W
+        st["K"][:, slot, :] = kr[i]
+        st["V"][:, slot, :] = vr[i]
+        st["count"] += 1
+
+
+def ring_window(shape, st: dict):
+    """Keys/values of the last min(count, W) committed rows, as [n][nh][P] (order irrelevant)."""
+    n = min(st["count"], shape.window)
+    if n == st["count"]:
+        slots = np.arange(n)
+    else:
+        slots = (st["count"] - n + np.arange(n)) % shape.window
+    return st["K"][:, slots, :].transpose(1, 0, 2), st["V"][:, slots, :].transpose(1, 0, 2)
+
+
+def commit(shape, wts: dict, st: dict, feats, want_y: bool = False):
+    """Fold newly committed feature rows into the memory and the window (the only writer).
+
+    Returns (new state, y or None).  The input state is not modified.
+    """
+    st = copy_state(st)
+    feats = np.asarray(feats, F64)
+    if feats.shape[0] == 0:
+        return st, (np.zeros((0, shape.n_heads, shape.head_dim)) if want_y else None)
+    pr = split_projection(project(feats, wts["w_in"]), shape)
+    H, y = ssd_sequential(pr["v"], pr["B"], pr["C"] if want_y else None, pr["dt"],
+                          wts["a_log"], wts["dt_bias"], wts["d_skip"], st["H"], shape.n_groups)
+    st["H"] = H
+    ring_append(shape, st, pr["k"], pr["v"])
+    return st, y
+
+
+def block_attention(q, k_ctx, v_ctx, k_blk, v_blk, cross_slot: int = 1):
+    """Softmax attention of the block rows over (context rows + block rows), per head.
+
+    q, k_blk, v_blk [nb][nh][P]; k_ctx, v_ctx [n][nh][P].  No causal mask; with
+    cross_slot = 0 block row j sees only itself among the block keys.
+    """
+    q = np.asarray(q, F64)
+    nb, nh, P = q.shape
+    out = np.zeros((nb, nh, P), F64)
+    for h in range(nh):
+        keys = np.concatenate([np.asarray(k_ctx, F64)[:, h], np.asarray(k_blk, F64)[:, h]], axis=0)
+        vals = np.concatenate([np.asarray(v_ctx, F64)[:, h], np.asarray(v_blk, F64)[:, h]], axis=0)
+        s = q[:, h] @ keys.T / np.sqrt(P)                       # [nb][n + nb]
+        if not cross_slot:
+            n = k_ctx.shape[0]
+            off = ~np.eye(nb, dtype=bool)
+            s[:, n:][off] = -np.inf
+        s = s - s.max(axis=1, keepdims=True)
+        p = np.exp(s)
+        p = p / p.sum(axis=1, keepdims=True)
+        out[:, h] = p @ vals
+    return out
+
+
+def memory_readout(H, Cq, v, d_skip, n_groups: int = 1):
+    """mem_j,h = H_h . C_q,j + D_h * v_j,h; H is only read."""
+    nb, nh, P = v.shape
+    Ch = per_head(Cq, nh, n_groups)
+    return np.einsum("hpn,jhn->jhp", np.asarray(H, F64), Ch) + np.asarray(d_skip, F64)[None, :, None] * v
+
+
+def draft(shape, wts: dict, st: dict, block_in):
+    """One draft step over the block rows (anchor + draft slots).  Reads the state, never writes it.
+
+    Returns out [nb][d_model] float64.
+    """
+    x = np.asarray(block_in, F64)
+    nb = x.shape[0]
+    pr = split_projection(project(x, wts["w_in"]), shape)
+    k_ctx, v_ctx = ring_window(shape, st)
+    attn = block_attention(pr["q"], k_ctx, v_ctx, pr["k"], pr["v"], shape.cross_slot)
+    mem = memory_readout(st["H"], pr["C"], pr["v"], wts["d_skip"], shape.n_groups)
+    o = (attn + mem).reshape(nb, shape.dq)
+    return project(o, wts["w_out"])
+
+
+def round_step(shape, wts: dict, st: dict, commit_feats, block_in):
+    """One verification round: commit the accepted rows first, then draft the next block."""
+    st2, _ = commit(shape, wts, st, commit_feats)
+    return st2, draft(shape, wts, st2, block_in)
+
+
+def draft_two_layer(shape, wts1: dict, wts2: dict, st1: dict, st2: dict, block_in):
+    """Two chained layers: the second layer's block input is block_in plus the first layer's output."""
+    o1 = draft(shape, wts1, st1, block_in)
+    x2 = np.asarray(block_in, F64) + round_storage(o1, shape.dtype)
+    return o1, draft(shape, wts2, st2, x2)

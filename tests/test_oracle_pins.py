@@ -1,0 +1,387 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each test names what it pins: a closed form, a special case that reduces to a
+textbook or library routine, brute force on tiny inputs, a hand-worked value,
+or a figure the HyFlash pages print.  A plausible mistake in the oracle (a
+dropped term, a wrong sign, a transposed operand, an off-by-one in the window
+or the chunking) fails at least one of them.
+"""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.signal
+import torch
+
+from hybrid_ssm_local_amd import inputs as I
+from oracle import hyflash_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+def _scan_case(T, nh=3, P=5, N=4, G=1, seed=0, h0=0.5, dt_shift=0.0):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, nh, P))
+    B = rng.standard_normal((T, G * N))
+    C = rng.standard_normal((T, G * N))
+    dt_raw = rng.standard_normal((T, nh)) + dt_shift
+    a_log = rng.uniform(0.0, math.log(16.0), nh)
+    dt_bias = np.full(nh, -2.0)
+    d_skip = rng.standard_normal(nh)
+    H0 = rng.standard_normal((nh, P, N)) * h0
+    return x, B, C, dt_raw, a_log, dt_bias, d_skip, H0
+
+
+# ---------------------------------------------------------------- scalar helpers
+
+
+def test_softplus_values():
+    # softplus(0) = ln 2; for large z it equals z to double precision; log1p(exp(z)) elsewhere.
+    assert O.softplus(0.0) == pytest.approx(math.log(2.0), rel=1e-15)
+    assert O.softplus(800.0) == 800.0
+    assert O.softplus(-800.0) == 0.0
+    z = np.linspace(-30, 30, 61)
+    np.testing.assert_allclose(O.softplus(z), np.log1p(np.exp(z)), rtol=1e-14)
+
+
+def test_round_storage_bf16_ties_to_even():
+    # bf16 keeps 8 significant bits: 1 + 2^-8 is a tie between 1 and 1 + 2^-7 -> even (1.0);
+    # 1 + 3*2^-8 is a tie between 1 + 2^-7 and 1 + 2^-6 -> even (1 + 2^-6).
+    vals = np.array([1 + 2.0**-8, 1 + 3 * 2.0**-8, 1 + 2.0**-8 + 2.0**-20, -(1 + 2.0**-8)])
+    got = O.round_storage(vals, "bf16")
+    np.testing.assert_array_equal(got, [1.0, 1 + 2.0**-6, 1 + 2.0**-7, -1.0])
+    np.testing.assert_array_equal(O.round_storage([1 + 2.0**-30], "f32"), [np.float32(1 + 2.0**-30)])
+
+
+# ---------------------------------------------------------------- the recurrence
+
+
+def test_single_token_by_hand():
+    # One head, P = N = 2.  raw + bias = log(e - 1) gives dt = 1; A_log = 0 gives A = -1.
+    # H1 = e^-1 * H0 + x outer B with x = (2, -1), B = (0.5, 3): outer = [[1, 6], [-0.5, -3]].
+    # y = H1 . C + D x with C = (1, 1), D = 0.25.
+    e = math.exp(-1.0)
+    H0 = np.array([[[1.0, 2.0], [3.0, 4.0]]])
+    H, y = O.ssd_sequential(np.array([[[2.0, -1.0]]]), np.array([[0.5, 3.0]]), np.array([[1.0, 1.0]]),
+                            np.array([[math.log(math.e - 1.0) + 2.0]]), np.array([0.0]),
+                            np.array([-2.0]), np.array([0.25]), H0)
+    expect_H = np.array([[[e + 1.0, 2 * e + 6.0], [3 * e - 0.5, 4 * e - 3.0]]])
+    np.testing.assert_allclose(H, expect_H, rtol=1e-14)
+    np.testing.assert_allclose(y[0, 0], [3 * e + 7.0 + 0.5, 7 * e - 3.5 - 0.25], rtol=1e-14)
+
+
+def test_closed_form_state():
+    # H_T = e^{Lam_T} H0 + sum_t e^{Lam_T - Lam_t} dt_t x_t outer B_t with Lam = cumsum(dt*A).
+    x, B, C, dt_raw, a_log, dt_bias, d_skip, H0 = _scan_case(T=40, G=1)
+    H, _ = O.ssd_sequential(x, B, None, dt_raw, a_log, dt_bias, d_skip, H0)
+    dt = np.log1p(np.exp(dt_raw + dt_bias))
+    A = -np.exp(a_log)
+    Lam = np.cumsum(dt * A, axis=0)                       # [T][nh]
+    w = np.exp(Lam[-1] - Lam) * dt                        # [T][nh]
+    expect = np.exp(Lam[-1])[:, None, None] * H0 + np.einsum("th,thp,tn->hpn", w, x, B)
+    assert _rel(H, expect) < 1e-12
+
+
+def test_groups_route_b_to_their_heads():
+    # With G = 2 groups over 4 heads, heads 0-1 use B[:, :N] and heads 2-3 use B[:, N:].
+    x, B, C, dt_raw, a_log, dt_bias, d_skip, H0 = _scan_case(T=12, nh=4, N=3, G=2)
+    H, y = O.ssd_sequential(x, B, C, dt_raw, a_log, dt_bias, d_skip, H0, n_groups=2)
+    for h in range(4):
+        g = h // 2
+        sl = slice(3 * g, 3 * g + 3)
+        Hh, yh = O.ssd_sequential(x[:, h:h + 1], B[:, sl], C[:, sl], dt_raw[:, h:h + 1], a_log[h:h + 1],
+                                  dt_bias[h:h + 1], d_skip[h:h + 1], H0[h:h + 1])
+        assert _rel(H[h], Hh[0]) < 1e-14 and _rel(y[:, h], yh[:, 0]) < 1e-14
+
+
+def test_zero_step_is_a_bitwise_noop():
+    # dt = softplus(-1e4) = 0 exactly: exp(0*A) = 1 and the write is 0, so H is untouched bit for bit.
+    x, B, C, dt_raw, a_log, dt_bias, d_skip, H0 = _scan_case(T=9)
+    H, _ = O.ssd_sequential(x, B, None, np.full_like(dt_raw, -1e4), a_log, dt_bias, d_skip, H0)
+    assert np.array_equal(H, H0)
+
+
+def test_no_decay_is_a_weighted_matmul():
+    # A_log = -inf gives A = 0: H = H0 + X_h^T diag(dt_h) B for each head (np.matmul).
+    x, B, C, dt_raw, a_log, dt_bias, d_skip, H0 = _scan_case(T=33)
+    a_zero = np.full_like(a_log, -np.inf)
+    H, _ = O.ssd_sequential(x, B, None, dt_raw, a_zero, dt_bias, d_skip, H0)
+    dt = np.log1p(np.exp(dt_raw + dt_bias))
+    for h in range(x.shape[1]):
+        expect = H0[h] + np.matmul(x[:, h, :].T * dt[:, h][None, :], B)
+        assert _rel(H[h], expect) < 1e-13
+
+
+def test_scalar_state_is_a_first_order_iir():
+    # P = N = 1 with a constant step: h_t = a h_{t-1} + u_t, u_t = dt x_t B_t, a = exp(dt A).
+    # scipy.signal.lfilter([1], [1, -a]) with initial condition a*h0 is that filter.
+    T = 200
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((T, 1, 1))
+    B = rng.standard_normal((T, 1))
+    C = rng.standard_normal((T, 1))
+    raw = np.full((T, 1), 0.3)
+    a_log, dt_bias, D = np.array([0.7]), np.array([-2.0]), np.array([0.4])
+    h0 = np.array([[[1.7]]])
+    H, y = O.ssd_sequential(x, B, C, raw, a_log, dt_bias, D, h0)
+    dt = math.log1p(math.exp(0.3 - 2.0))
+    a = math.exp(-dt * math.exp(0.7))
+    u = dt * x[:, 0, 0] * B[:, 0]
+    h, _ = scipy.signal.lfilter([1.0], [1.0, -a], u, zi=[a * 1.7])
+    assert _rel(H[0, 0, 0], h[-1]) < 1e-12
+    assert _rel(y[:, 0, 0], C[:, 0] * h + 0.4 * x[:, 0, 0]) < 1e-12
+
+
+def test_outputs_equal_the_quadratic_attention_form():
+    # With H0 = 0: y = (M o C B^T) X + D X, M[t, tau] = exp(Lam_t - Lam_tau) dt_tau for tau <= t
+    # (brute force over every pair).
+    T = 48
+    x, B, C, dt_raw, a_log, dt_bias, d_skip, H0 = _scan_case(T=T, h0=0.0)
+    _, y = O.ssd_sequential(x, B, C, dt_raw, a_log, dt_bias, d_skip, H0)
+    dt = np.log1p(np.exp(dt_raw + dt_bias))
+    Lam = np.cumsum(dt * -np.exp(a_log), axis=0)
+    for h in range(x.shape[1]):
+        M = np.zeros((T, T))
+        for t in range(T):
+            for tau in range(t + 1):
+                M[t, tau] = math.exp(Lam[t, h] - Lam[tau, h]) * dt[tau, h] * float(C[t] @ B[tau])
+        expect = M @ x[:, h, :] + d_skip[h] * x[:, h, :]
+        assert _rel(y[:, h, :], expect) < 1e-12
+
+
+@pytest.mark.parametrize("chunk", [1, 2, 7, 16, 64, 256])
+def test_chunked_equals_sequential(chunk):
+    # The chunked algorithm must equal the definition; T = 150 is not a multiple of any chunk > 1.
+    args = _scan_case(T=150, nh=2, P=4, N=6, h0=0.8)
+    H1, y1 = O.ssd_sequential(*args)
+    H2, y2 = O.ssd_chunked(*args, chunk=chunk)
+    assert _rel(H2, H1) < 1e-12
+    assert _rel(y2, y1) < 1e-12
+
+
+def test_chunked_survives_deep_decay():
+    # Strong decay (|Lam| reaches hundreds inside one chunk): differences of log-decays keep the
+    # chunked form finite and equal to the definition; a ratio of exps would give 0/0.
+    args = list(_scan_case(T=300, nh=2, P=3, N=3, h0=1.0, dt_shift=3.0))
+    H1, y1 = O.ssd_sequential(*args)
+    H2, y2 = O.ssd_chunked(*args, chunk=256)
+    assert np.all(np.isfinite(H2)) and np.all(np.isfinite(y2))
+    assert _rel(H2, H1) < 1e-12 and _rel(y2, y1) < 1e-12
+
+
+# ---------------------------------------------------------------- attention, ring, readout
+
+
+def _sdpa(q, k, v, mask):
+    """torch's reference attention on CPU in float64 (bool mask: True = may attend)."""
+    return torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+        attn_mask=torch.from_numpy(mask)).numpy()
+
+
+@pytest.mark.parametrize("cross_slot", [1, 0])
+def test_block_attention_matches_library_attention(cross_slot):
+    rng = np.random.default_rng(7)
+    nb, n, nh, P = 8, 37, 3, 16
+    q, kb, vb = (rng.standard_normal((nb, nh, P)) for _ in range(3))
+    kc, vc = (rng.standard_normal((n, nh, P)) for _ in range(2))
+    got = O.block_attention(q, kc, vc, kb, vb, cross_slot)
+    mask = np.ones((nb, n + nb), dtype=bool)
+    if not cross_slot:
+        mask[:, n:] = np.eye(nb, dtype=bool)
+    for h in range(nh):
+        keys = np.concatenate([kc[:, h], kb[:, h]])
+        vals = np.concatenate([vc[:, h], vb[:, h]])
+        ref = _sdpa(q[:, h], keys, vals, mask)
+        assert _rel(got[:, h], ref) < 1e-13
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(8)
+    nh, P = 2, 8
+    # All keys equal -> uniform weights -> the mean of the values.
+    q = rng.standard_normal((1, nh, P))
+    k = np.repeat(rng.standard_normal((1, nh, P)), 6, axis=0)
+    v = rng.standard_normal((6, nh, P))
+    got = O.block_attention(q, k[:5], v[:5], k[5:], v[5:])
+    np.testing.assert_allclose(got[0], v.mean(axis=0), rtol=1e-13, atol=1e-15)
+    # A single key (empty context, one block row) returns its value exactly.
+    got1 = O.block_attention(q, np.zeros((0, nh, P)), np.zeros((0, nh, P)), k[:1], v[:1])
+    np.testing.assert_allclose(got1[0], v[0], rtol=1e-15)
+
+
+def test_ring_slots():
+    # count = W + 3: the oldest three slots hold committed rows W, W+1, W+2.
+    shape = I.LayerShape(d_model=8, n_heads=1, head_dim=2, d_state=2, window=5, dtype="f32")
+    st = O.new_state(shape)
+    rows = np.arange(8, dtype=np.float64)
+    k = np.repeat(rows[:, None, None], 2, axis=2)
+    O.ring_append(shape, st, k, -k)
+    assert st["count"] == 8
+    np.testing.assert_array_equal(st["K"][0, :, 0], [5, 6, 7, 3, 4])
+    np.testing.assert_array_equal(st["V"][0, :, 0], [-5, -6, -7, -3, -4])
+    kw, _ = O.ring_window(shape, st)
+    assert sorted(kw[:, 0, 0].tolist()) == [3, 4, 5, 6, 7]
+
+
+@pytest.mark.parametrize("total", [0, 3, 16, 17, 40])
+def test_ring_window_equals_full_history_under_a_window_mask(total):
+    # Keep every committed K/V; attention over all of them with all but the last W masked
+    # (torch SDPA, library routine) must equal attention over the ring.
+    W, nh, P, nb = 16, 2, 8, 8
+    shape = I.LayerShape(d_model=8, n_heads=nh, head_dim=P, d_state=4, window=W, dtype="bf16")
+    rng = np.random.default_rng(total)
+    st = O.new_state(shape)
+    hist_k, hist_v = [], []
+    done = 0
+    while done < total:
+        a = min(int(rng.integers(1, 9)), total - done)
+        k = rng.standard_normal((a, nh, P))
+        v = rng.standard_normal((a, nh, P))
+        O.ring_append(shape, st, k, v)
+        hist_k.append(O.round_storage(k, "bf16"))
+        hist_v.append(O.round_storage(v, "bf16"))
+        done += a
+    q, kb, vb = (rng.standard_normal((nb, nh, P)) for _ in range(3))
+    kc, vc = O.ring_window(shape, st)
+    got = O.block_attention(q, kc, vc, kb, vb)
+    hk = np.concatenate(hist_k + [np.zeros((0, nh, P))])
+    hv = np.concatenate(hist_v + [np.zeros((0, nh, P))])
+    mask = np.ones((nb, total + nb), dtype=bool)
+    mask[:, : max(total - W, 0)] = False
+    for h in range(nh):
+        ref = _sdpa(q[:, h], np.concatenate([hk[:, h], kb[:, h]]), np.concatenate([hv[:, h], vb[:, h]]), mask)
+        assert _rel(got[:, h], ref) < 1e-13
+
+
+def test_readout_rank_one_and_identity_states():
+    rng = np.random.default_rng(9)
+    nh, P, nb = 3, 4, 8
+    Cq = rng.standard_normal((nb, P))
+    v = rng.standard_normal((nb, nh, P))
+    D = rng.standard_normal(nh)
+    # H_h = u_h outer w_h  ->  mem_j,h = u_h (w_h . C_j) + D_h v_j,h.
+    u, w = rng.standard_normal((nh, P)), rng.standard_normal((nh, P))
+    H = u[:, :, None] * w[:, None, :]
+    got = O.memory_readout(H, Cq, v, D)
+    for j in range(nb):
+        for h in range(nh):
+            expect = u[h] * float(w[h] @ Cq[j]) + D[h] * v[j, h]
+            np.testing.assert_allclose(got[j, h], expect, rtol=1e-13)
+    # H_h = identity (P = N) -> mem = C + D v.
+    got = O.memory_readout(np.repeat(np.eye(P)[None], nh, 0), Cq, v, D)
+    np.testing.assert_allclose(got, Cq[:, None, :] + D[None, :, None] * v, rtol=1e-14)
+
+
+def test_projection_matches_torch_linear():
+    rng = np.random.default_rng(10)
+    a, w = rng.standard_normal((5, 12)), rng.standard_normal((7, 12))
+    ref = torch.nn.functional.linear(torch.from_numpy(a), torch.from_numpy(w)).numpy()
+    np.testing.assert_allclose(O.project(a, w), ref, rtol=1e-13)
+
+
+# ---------------------------------------------------------------- round semantics
+
+
+def _tiny_layer(seed=0, dtype="f32", window=6):
+    shape = I.LayerShape(d_model=16, n_heads=2, head_dim=4, d_state=3, window=window, dtype=dtype)
+    rng = I.rng_streams(seed)[0]
+    wts = {k: np.asarray(v, np.float64) for k, v in I.make_weights(shape, rng, d_random=True).items()}
+    return shape, wts, rng
+
+
+def _state_bytes(st):
+    return (st["count"], st["H"].tobytes(), st["K"].tobytes(), st["V"].tobytes())
+
+
+def test_draft_reads_and_never_writes_the_state():
+    shape, wts, rng = _tiny_layer()
+    st, _ = O.commit(shape, wts, O.new_state(shape), rng.standard_normal((9, 16)))
+    before = _state_bytes(st)
+    out = O.draft(shape, wts, st, rng.standard_normal((8, 16)))
+    assert _state_bytes(st) == before and out.shape == (8, 16)
+
+
+def test_rejected_rows_never_enter_the_memory():
+    # Per round 8 candidate rows; only the first a are committed.  Changing the other 8 - a
+    # rows leaves the state bit-identical and equal to a replay of the accepted rows alone.
+    shape, wts, rng = _tiny_layer(seed=1)
+    st_a, st_b, st_r = O.new_state(shape), O.new_state(shape), O.new_state(shape)
+    for _ in range(6):
+        a = int(rng.integers(1, 9))
+        cand = rng.standard_normal((8, 16))
+        alt = cand.copy()
+        alt[a:] = rng.standard_normal((8 - a, 16))
+        blk = rng.standard_normal((8, 16))
+        st_a, out_a = O.round_step(shape, wts, st_a, cand[:a], blk)
+        st_b, out_b = O.round_step(shape, wts, st_b, alt[:a], blk)
+        st_r, _ = O.commit(shape, wts, st_r, cand[:a])
+        assert _state_bytes(st_a) == _state_bytes(st_b) == _state_bytes(st_r)
+        assert np.array_equal(out_a, out_b)
+
+
+def _compositions(n, max_part):
+    for cuts in itertools.product([0, 1], repeat=n - 1):
+        parts, run = [], 1
+        for c in cuts:
+            if c:
+                parts.append(run)
+                run = 1
+            else:
+                run += 1
+        parts.append(run)
+        if max(parts) <= max_part:
+            yield parts
+
+
+def test_split_invariance_over_all_compositions():
+    # commit(F[0:i]); commit(F[i:j]) ... equals commit(F) for every way of cutting 10 rows into
+    # rounds of at most 8 (509 compositions).
+    comps = list(_compositions(10, 8))
+    assert len(comps) == 509
+    shape, wts, rng = _tiny_layer(seed=2, window=4)
+    F = rng.standard_normal((10, 16))
+    ref, _ = O.commit(shape, wts, O.new_state(shape), F)
+    for parts in comps:
+        st, i = O.new_state(shape), 0
+        for p in parts:
+            st, _ = O.commit(shape, wts, st, F[i:i + p])
+            i += p
+        assert st["count"] == 10
+        assert _rel(st["H"], ref["H"]) < 1e-13
+        assert np.array_equal(st["K"], ref["K"]) and np.array_equal(st["V"], ref["V"])
+
+
+def test_empty_commit_is_a_noop_and_empty_state_reads_only_the_skip():
+    shape, wts, rng = _tiny_layer(seed=3)
+    st0 = O.new_state(shape)
+    st1, _ = O.commit(shape, wts, st0, np.zeros((0, 16)))
+    assert _state_bytes(st1) == _state_bytes(st0)
+    # count = 0: no window, H = 0, so mem = D v and attention runs over the block alone.
+    blk = rng.standard_normal((8, 16))
+    pr = O.split_projection(O.project(blk, wts["w_in"]), shape)
+    mem = O.memory_readout(st0["H"], pr["C"], pr["v"], wts["d_skip"])
+    np.testing.assert_array_equal(mem, wts["d_skip"][None, :, None] * pr["v"])
+
+
+# ---------------------------------------------------------------- the pages' memory arithmetic
+
+
+def test_fp32_state_size_matches_the_pages():
+    g = json.load(open(os.path.join(GOLDEN, "memory_footprint.json")))
+    st = O.new_state(I.PHI4)
+    assert st["H"].size * 4 == g["fp32_state_MiB"] * 2**20
+    # The page's own target-KV arithmetic (Phi-4 geometry: 40 layers, 10 KV heads of 128).
+    kv = 40 * 2 * 10 * 128 * 2 * 32768
+    assert kv == g["target_kv_GiB_at_32k"] * 2**30
+    assert round(kv / (g["drafter_context_MiB"] * 2**20)) == g["target_over_drafter_ratio"]
