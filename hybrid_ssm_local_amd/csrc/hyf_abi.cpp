@@ -1,0 +1,433 @@
+// libhyflash C ABI: argument validation, state layout, workspace carving and launch order.
+// Every host-checkable condition is validated before the first launch, so an error return
+// (other than HYF_EHIP) leaves device memory untouched.
+#include <string.h>
+
+#include "hyf_launch.h"
+
+using namespace hyf;
+
+namespace {
+
+constexpr uint64_t ALIGN = 256;
+constexpr int SCAN_TARGET_WGS = 512;  // scan workgroups the segment split aims for
+
+uint64_t align_up(uint64_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
+int esize(int dtype) { return dtype == HYF_BF16 ? 2 : 4; }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_cfg(const hyf_config* c) {
+  if (!c) return HYF_EINVAL;
+  if (c->dtype != HYF_F32 && c->dtype != HYF_BF16) return HYF_EDTYPE;
+  if (c->memory == HYF_MEM_GDN) return HYF_EUNSUPPORTED;
+  if (c->memory != HYF_MEM_MAMBA2) return HYF_EINVAL;
+  if (c->reserved != 0) return HYF_EINVAL;
+  if (c->cross_slot != 0 && c->cross_slot != 1) return HYF_EINVAL;
+  if (c->d_model < 16 || c->d_model > 65536 || c->d_model % 16) return HYF_ESHAPE;
+  if (c->n_heads < 1 || c->n_heads > 1024) return HYF_ESHAPE;
+  if (c->head_dim < 16 || c->head_dim > 256 || c->head_dim % 16) return HYF_ESHAPE;
+  if (c->d_state < 16 || c->d_state > 256 || c->d_state % 16) return HYF_ESHAPE;
+  if (c->n_groups < 1 || c->n_heads % c->n_groups) return HYF_ESHAPE;
+  if (c->window < 1 || c->window > 8192) return HYF_ESHAPE;
+  if (c->block != HYF_BLOCK) return HYF_ESHAPE;
+  if (c->chunk < 16 || c->chunk > 1024 || c->chunk % 16) return HYF_ESHAPE;
+  if ((int64_t)c->n_heads * c->head_dim > 65536) return HYF_ESHAPE;
+  return HYF_OK;
+}
+
+void fill_layout(const hyf_config* c, hyf_state_layout* L) {
+  const uint64_t es = esize(c->dtype);
+  L->count_off = 0;
+  L->h_off = ALIGN;
+  L->k_off = L->h_off + align_up((uint64_t)c->n_heads * c->head_dim * c->d_state * 4);
+  const uint64_t ring = align_up((uint64_t)c->n_heads * c->window * c->head_dim * es);
+  L->v_off = L->k_off + ring;
+  L->total = L->v_off + ring;
+}
+
+Shape make_shape(const hyf_config* c) {
+  Shape s;
+  s.d = c->d_model;
+  s.nh = c->n_heads;
+  s.P = c->head_dim;
+  s.N = c->d_state;
+  s.G = c->n_groups;
+  s.W = c->window;
+  s.L = c->chunk;
+  s.cross = c->cross_slot;
+  s.dq = s.nh * s.P;
+  s.gn = s.G * s.N;
+  s.off_q = 0;
+  s.off_c = s.off_q + s.dq;
+  s.off_k = s.off_c + s.gn;
+  s.off_v = s.off_k + s.dq;
+  s.off_b = s.off_v + s.dq;
+  s.off_dt = s.off_b + s.gn;
+  s.n_in = s.off_dt + s.nh;
+  hyf_state_layout L;
+  fill_layout(c, &L);
+  s.st_bytes = L.total;
+  s.st_h = L.h_off;
+  s.st_k = L.k_off;
+  s.st_v = L.v_off;
+  return s;
+}
+
+int n_att_split(const Shape& s) { return (s.W + 63) / 64 + 1; }
+
+// Segment policy of the scan: whole chunks per segment, the same count for every request.
+int32_t scan_chunks_per_seg(const Shape& s, int64_t total_chunks) {
+  const int64_t seg_target = (SCAN_TARGET_WGS + s.nh - 1) / s.nh;
+  int64_t cps = (total_chunks + seg_target - 1) / seg_target;
+  return (int32_t)(cps < 1 ? 1 : cps);
+}
+int64_t scan_max_segs(const Shape& s, int32_t n_req) {
+  return (SCAN_TARGET_WGS + s.nh - 1) / s.nh + n_req;
+}
+
+struct WsDraft {
+  uint64_t proj, mem, att_part, att_ml, o_in, end;
+};
+WsDraft ws_draft(const Shape& s, int dtype, int32_t R, int64_t rows) {
+  WsDraft w;
+  const int ns = n_att_split(s);
+  uint64_t o = 0;
+  w.proj = o;
+  o += align_up((uint64_t)(rows + (int64_t)HYF_BLOCK * R) * s.n_in * 4);
+  w.mem = o;
+  o += align_up((uint64_t)R * HYF_BLOCK * s.dq * 4);
+  w.att_part = o;
+  o += align_up((uint64_t)R * s.nh * ns * HYF_BLOCK * s.P * 4);
+  w.att_ml = o;
+  o += align_up((uint64_t)R * s.nh * ns * HYF_BLOCK * 2 * 4);
+  w.o_in = o;
+  o += align_up((uint64_t)R * HYF_BLOCK * s.dq * esize(dtype));
+  w.end = o;
+  return w;
+}
+
+struct WsCommit {
+  uint64_t vb, dt, kb, part, lam, end;
+};
+WsCommit ws_commit(const Shape& s, int dtype, int32_t R, int64_t rows) {
+  WsCommit w;
+  uint64_t o = 0;
+  const int64_t krows = rows < (int64_t)R * s.W ? rows : (int64_t)R * s.W;
+  const int64_t segs = scan_max_segs(s, R);
+  w.vb = o;
+  o += align_up((uint64_t)rows * (s.dq + s.gn) * esize(dtype));
+  w.dt = o;
+  o += align_up((uint64_t)rows * s.nh * 4);
+  w.kb = o;
+  o += align_up((uint64_t)krows * s.dq * esize(dtype));
+  w.part = o;
+  o += align_up((uint64_t)segs * s.nh * s.P * s.N * 4);
+  w.lam = o;
+  o += align_up((uint64_t)segs * s.nh * 4);
+  w.end = o;
+  return w;
+}
+
+// Request table from host slots / row offsets.  Fills seg0 with the scan's segment split when
+// chunks_per_seg > 0.
+int build_table(const Shape& s, int32_t pool_slots, const int32_t* slots, int32_t n_req, const int64_t* cu,
+                ReqTable* rt) {
+  if (n_req < 1 || n_req > HYF_MAX_REQUESTS) return HYF_ECAPACITY;
+  memset(rt, 0, sizeof(*rt));
+  rt->n_req = n_req;
+  for (int i = 0; i < n_req; ++i) {
+    const int32_t sl = slots ? slots[i] : i;
+    if (sl < 0 || sl >= pool_slots) return HYF_ECAPACITY;
+    for (int j = 0; j < i; ++j)
+      if (rt->slot[j] == sl) return HYF_EINVAL;  // two requests of one call on one state
+    rt->slot[i] = sl;
+  }
+  if (cu) {
+    if (cu[0] != 0) return HYF_EINVAL;
+    for (int i = 0; i < n_req; ++i)
+      if (cu[i + 1] < cu[i]) return HYF_EINVAL;
+    if (cu[n_req] > ((int64_t)1 << 30)) return HYF_ECAPACITY;
+    for (int i = 0; i <= n_req; ++i) rt->row0[i] = (int32_t)cu[i];
+  }
+  return HYF_OK;
+}
+
+void fill_segments(const Shape& s, ReqTable* rt, int32_t* cps_out, int32_t* total_out, int32_t* max_out) {
+  int64_t total_chunks = 0;
+  for (int i = 0; i < rt->n_req; ++i) total_chunks += (rt->row0[i + 1] - rt->row0[i] + s.L - 1) / s.L;
+  const int32_t cps = scan_chunks_per_seg(s, total_chunks);
+  int32_t q = 0, mx = 0;
+  for (int i = 0; i < rt->n_req; ++i) {
+    rt->seg0[i] = q;
+    const int64_t ch = (rt->row0[i + 1] - rt->row0[i] + s.L - 1) / s.L;
+    const int32_t ns = (int32_t)((ch + cps - 1) / cps);
+    q += ns;
+    if (ns > mx) mx = ns;
+  }
+  rt->seg0[rt->n_req] = q;
+  *cps_out = cps;
+  *total_out = q;
+  *max_out = mx;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? HYF_OK : HYF_EHIP; }
+
+int check_weights(const hyf_weights* w) {
+  if (!w || !w->w_in || !w->w_out || !w->a_log || !w->dt_bias || !w->d_skip) return HYF_EINVAL;
+  if (!aligned(w->w_in, 16) || !aligned(w->w_out, 16)) return HYF_EINVAL;
+  return HYF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hyf_abi_version(void) { return HYF_ABI_VERSION; }
+
+const char* hyf_status_str(int st) {
+  switch (st) {
+    case HYF_OK: return "ok";
+    case HYF_EINVAL: return "invalid argument";
+    case HYF_ESHAPE: return "unsupported or inconsistent shape";
+    case HYF_ECAPACITY: return "capacity exceeded";
+    case HYF_EDTYPE: return "unknown dtype";
+    case HYF_EWORKSPACE: return "workspace too small";
+    case HYF_EUNSUPPORTED: return "mode not implemented";
+    case HYF_EHIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int hyf_config_check(const hyf_config* cfg) { return check_cfg(cfg); }
+
+int64_t hyf_n_in(const hyf_config* cfg) {
+  if (check_cfg(cfg) != HYF_OK) return 0;
+  return make_shape(cfg).n_in;
+}
+
+int hyf_state_layout_get(const hyf_config* cfg, hyf_state_layout* out) {
+  const int st = check_cfg(cfg);
+  if (st != HYF_OK) return st;
+  if (!out) return HYF_EINVAL;
+  fill_layout(cfg, out);
+  return HYF_OK;
+}
+
+size_t hyf_state_bytes(const hyf_config* cfg) {
+  if (check_cfg(cfg) != HYF_OK) return 0;
+  hyf_state_layout L;
+  fill_layout(cfg, &L);
+  return (size_t)L.total;
+}
+
+size_t hyf_workspace_bytes(const hyf_config* cfg, int32_t max_requests, int64_t max_rows) {
+  if (check_cfg(cfg) != HYF_OK || max_requests < 1 || max_requests > HYF_MAX_REQUESTS || max_rows < 0) return 0;
+  const Shape s = make_shape(cfg);
+  const uint64_t a = ws_draft(s, cfg->dtype, max_requests, max_rows).end;
+  const uint64_t b = ws_commit(s, cfg->dtype, max_requests, max_rows).end;
+  return (size_t)(a > b ? a : b);
+}
+
+size_t hyf_ssd_scan_workspace_bytes(const hyf_config* cfg, int64_t T) {
+  if (check_cfg(cfg) != HYF_OK || T < 0) return 0;
+  const Shape s = make_shape(cfg);
+  const int64_t segs = scan_max_segs(s, 1);
+  return (size_t)(align_up((uint64_t)segs * s.nh * s.P * s.N * 4) + align_up((uint64_t)segs * s.nh * 4));
+}
+
+int hyf_state_reset(const hyf_config* cfg, void* state_pool, int32_t pool_slots, const int32_t* slots, int32_t n_req,
+                    void* stream) {
+  int st = check_cfg(cfg);
+  if (st != HYF_OK) return st;
+  if (!state_pool || !aligned(state_pool, ALIGN) || pool_slots < 1) return HYF_EINVAL;
+  const Shape s = make_shape(cfg);
+  ReqTable rt;
+  st = build_table(s, pool_slots, slots, n_req, nullptr, &rt);
+  if (st != HYF_OK) return st;
+  return hip_status(launch_reset_states(static_cast<char*>(state_pool), s, rt, static_cast<hipStream_t>(stream)));
+}
+
+int hyf_memory_commit(const hyf_config* cfg, const hyf_weights* w, void* state_pool, int32_t pool_slots,
+                      const int32_t* slots, int32_t n_req, const void* feats, const int64_t* cu_rows, void* y_opt,
+                      void* ws, size_t ws_bytes, void* stream) {
+  int st = check_cfg(cfg);
+  if (st != HYF_OK) return st;
+  if ((st = check_weights(w)) != HYF_OK) return st;
+  if (!state_pool || !aligned(state_pool, ALIGN) || pool_slots < 1 || !cu_rows) return HYF_EINVAL;
+  if (y_opt) return HYF_EUNSUPPORTED;
+  const Shape s = make_shape(cfg);
+  ReqTable rt;
+  if ((st = build_table(s, pool_slots, slots, n_req, cu_rows, &rt)) != HYF_OK) return st;
+  const int64_t rows = cu_rows[n_req];
+  if (rows == 0) return HYF_OK;
+  if (!feats || !aligned(feats, 16)) return HYF_EINVAL;
+  if (!ws || !aligned(ws, ALIGN) || ws_bytes < hyf_workspace_bytes(cfg, n_req, rows)) return HYF_EWORKSPACE;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  char* wsb = static_cast<char*>(ws);
+  char* pool = static_cast<char*>(state_pool);
+  const int dt = cfg->dtype;
+  const int es = esize(dt);
+
+  int64_t max_n = 0;
+  for (int i = 0; i < n_req; ++i) max_n = cu_rows[i + 1] - cu_rows[i] > max_n ? cu_rows[i + 1] - cu_rows[i] : max_n;
+
+  if (max_n <= 16) {
+    // Round-sized commit: one weight pass over the k | v | B | dt rows, then one read-modify-write of H.
+    const WsDraft L = ws_draft(s, dt, n_req, rows);
+    float* proj = reinterpret_cast<float*>(wsb + L.proj);
+    RowSrc xs{feats, feats, rows};
+    Epi e{proj + s.off_k, s.n_in, 1, s.n_in, nullptr, 0};
+    hipError_t he = launch_linear(dt, xs, rows, s.d, static_cast<const char*>(w->w_in) + (int64_t)s.off_k * s.d * es,
+                                  s.n_in - s.off_k, e, hs);
+    if (he != hipSuccess) return HYF_EHIP;
+    RoundArgs ra{};
+    ra.proj = proj;
+    ra.blk_row0 = rows;
+    ra.state_pool = pool;
+    ra.a_log = w->a_log;
+    ra.dt_bias = w->dt_bias;
+    ra.d_skip = w->d_skip;
+    ra.do_commit = 1;
+    ra.do_draft = 0;
+    if ((he = launch_commit_small(dt, s, ra, rt, hs)) != hipSuccess) return HYF_EHIP;
+    return hip_status(launch_bump_counts(pool, s, rt, hs));
+  }
+
+  // Prefill-sized commit: GEMM -> ring append -> chunked scan -> count.
+  const WsCommit L = ws_commit(s, dt, n_req, rows);
+  void* vb = wsb + L.vb;
+  float* dtb = reinterpret_cast<float*>(wsb + L.dt);
+  void* kb = wsb + L.kb;
+  RowSrc xs{feats, feats, rows};
+  const int nvb = s.dq + s.gn;
+  Epi e{vb, nvb, 0, nvb, dtb, s.nh};
+  hipError_t he = launch_linear(dt, xs, rows, s.d, static_cast<const char*>(w->w_in) + (int64_t)s.off_v * s.d * es,
+                                nvb + s.nh, e, hs);
+  if (he != hipSuccess) return HYF_EHIP;
+  // k only for the rows that stay in the window: the last min(n_i, W) of each request.
+  int64_t krow = 0;
+  for (int i = 0; i < n_req; ++i) {
+    const int64_t n = cu_rows[i + 1] - cu_rows[i];
+    const int64_t m = n < s.W ? n : s.W;
+    if (m == 0) continue;
+    const char* src = static_cast<const char*>(feats) + (cu_rows[i] + n - m) * (int64_t)s.d * es;
+    RowSrc ks{src, src, m};
+    Epi ek{static_cast<char*>(kb) + krow * s.dq * es, s.dq, 0, s.dq, nullptr, 0};
+    he = launch_linear(dt, ks, m, s.d, static_cast<const char*>(w->w_in) + (int64_t)s.off_k * s.d * es, s.dq, ek, hs);
+    if (he != hipSuccess) return HYF_EHIP;
+    krow += m;
+  }
+  if ((he = launch_ring_append(dt, s, pool, rt, kb, s.dq, 0, vb, nvb, hs)) != hipSuccess) return HYF_EHIP;
+  ScanArgs sa{};
+  sa.x = vb;
+  sa.B = static_cast<const char*>(vb) + (int64_t)s.dq * es;
+  sa.dt = dtb;
+  sa.ld_x = nvb;
+  sa.ld_b = nvb;
+  sa.ld_dt = s.nh;
+  sa.a_log = w->a_log;
+  sa.dt_bias = w->dt_bias;
+  sa.state_pool = pool;
+  sa.h_direct = nullptr;
+  sa.part = reinterpret_cast<float*>(wsb + L.part);
+  sa.lam = reinterpret_cast<float*>(wsb + L.lam);
+  int32_t max_segs = 0;
+  fill_segments(s, &rt, &sa.chunks_per_seg, &sa.total_segs, &max_segs);
+  if ((he = launch_ssd_state(dt, s, sa, rt, max_segs, hs)) != hipSuccess) return HYF_EHIP;
+  return hip_status(launch_bump_counts(pool, s, rt, hs));
+}
+
+int hyf_draft_block(const hyf_config* cfg, const hyf_weights* w, void* state_pool, int32_t pool_slots,
+                    const int32_t* slots, int32_t n_req, const void* commit_feats, const int64_t* cu_commit,
+                    const void* block_in, void* block_out, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_cfg(cfg);
+  if (st != HYF_OK) return st;
+  if ((st = check_weights(w)) != HYF_OK) return st;
+  if (!state_pool || !aligned(state_pool, ALIGN) || pool_slots < 1) return HYF_EINVAL;
+  if (!block_in || !block_out || !aligned(block_in, 16) || !aligned(block_out, 16)) return HYF_EINVAL;
+  if ((commit_feats == nullptr) != (cu_commit == nullptr)) return HYF_EINVAL;
+  const Shape s = make_shape(cfg);
+  ReqTable rt;
+  if ((st = build_table(s, pool_slots, slots, n_req, cu_commit, &rt)) != HYF_OK) return st;
+  int64_t rows = 0;
+  if (cu_commit) {
+    rows = cu_commit[n_req];
+    for (int i = 0; i < n_req; ++i)
+      if (cu_commit[i + 1] - cu_commit[i] > HYF_BLOCK) return HYF_ECAPACITY;
+    if (rows > 0 && !aligned(commit_feats, 16)) return HYF_EINVAL;
+  }
+  if (!ws || !aligned(ws, ALIGN) || ws_bytes < hyf_workspace_bytes(cfg, n_req, rows)) return HYF_EWORKSPACE;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  char* wsb = static_cast<char*>(ws);
+  char* pool = static_cast<char*>(state_pool);
+  const int dt = cfg->dtype;
+  const WsDraft L = ws_draft(s, dt, n_req, rows);
+  float* proj = reinterpret_cast<float*>(wsb + L.proj);
+
+  // 1. one pass over w_in for [commit rows ; block rows]
+  RowSrc xs{rows > 0 ? commit_feats : block_in, block_in, rows};
+  Epi e{proj, s.n_in, 1, s.n_in, nullptr, 0};
+  hipError_t he = launch_linear(dt, xs, rows + (int64_t)HYF_BLOCK * n_req, s.d, w->w_in, s.n_in, e, hs);
+  if (he != hipSuccess) return HYF_EHIP;
+
+  RoundArgs ra{};
+  ra.proj = proj;
+  ra.blk_row0 = rows;
+  ra.state_pool = pool;
+  ra.a_log = w->a_log;
+  ra.dt_bias = w->dt_bias;
+  ra.d_skip = w->d_skip;
+  ra.mem = reinterpret_cast<float*>(wsb + L.mem);
+  ra.att_part = reinterpret_cast<float*>(wsb + L.att_part);
+  ra.att_ml = reinterpret_cast<float*>(wsb + L.att_ml);
+  ra.o_in = wsb + L.o_in;
+  ra.n_split = n_att_split(s);
+  ra.keys_per_split = 64;
+  ra.do_commit = rows > 0;
+  ra.do_draft = 1;
+  // 2. commit (if any) + memory readout, 3. attention, 4. merge (+ count), 5. output projection
+  if ((he = launch_commit_small(dt, s, ra, rt, hs)) != hipSuccess) return HYF_EHIP;
+  if ((he = launch_attention(dt, s, ra, rt, hs)) != hipSuccess) return HYF_EHIP;
+  if ((he = launch_merge(dt, s, ra, rt, hs)) != hipSuccess) return HYF_EHIP;
+  RowSrc xo{ra.o_in, ra.o_in, (int64_t)HYF_BLOCK * n_req};
+  Epi eo{block_out, s.d, 0, s.d, nullptr, 0};
+  return hip_status(launch_linear(dt, xo, (int64_t)HYF_BLOCK * n_req, s.dq, w->w_out, s.d, eo, hs));
+}
+
+int hyf_ssd_scan(const hyf_config* cfg, const void* x, const void* B, const void* C_opt, const float* dt_raw,
+                 const float* a_log, const float* dt_bias, const float* d_skip, float* H_inout, void* y_opt, int64_t T,
+                 void* ws, size_t ws_bytes, void* stream) {
+  int st = check_cfg(cfg);
+  if (st != HYF_OK) return st;
+  if (T < 0 || T > ((int64_t)1 << 30)) return HYF_ECAPACITY;
+  if (!a_log || !dt_bias || !d_skip || !H_inout || !aligned(H_inout, 16)) return HYF_EINVAL;
+  if ((y_opt != nullptr) != (C_opt != nullptr)) return HYF_EINVAL;
+  if (y_opt) return HYF_EUNSUPPORTED;
+  if (T == 0) return HYF_OK;
+  if (!x || !B || !dt_raw || !aligned(x, 16) || !aligned(B, 16)) return HYF_EINVAL;
+  if (!ws || !aligned(ws, ALIGN) || ws_bytes < hyf_ssd_scan_workspace_bytes(cfg, T)) return HYF_EWORKSPACE;
+  const Shape s = make_shape(cfg);
+  ReqTable rt;
+  memset(&rt, 0, sizeof(rt));
+  rt.n_req = 1;
+  rt.row0[1] = (int32_t)T;
+  ScanArgs sa{};
+  sa.x = x;
+  sa.B = B;
+  sa.dt = dt_raw;
+  sa.ld_x = (int64_t)s.nh * s.P;
+  sa.ld_b = s.gn;
+  sa.ld_dt = s.nh;
+  sa.a_log = a_log;
+  sa.dt_bias = dt_bias;
+  sa.state_pool = nullptr;
+  sa.h_direct = H_inout;
+  const int64_t segs = scan_max_segs(s, 1);
+  sa.part = static_cast<float*>(ws);
+  sa.lam = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((uint64_t)segs * s.nh * s.P * s.N * 4));
+  int32_t max_segs = 0;
+  fill_segments(s, &rt, &sa.chunks_per_seg, &sa.total_segs, &max_segs);
+  return hip_status(launch_ssd_state(cfg->dtype, s, sa, rt, max_segs, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

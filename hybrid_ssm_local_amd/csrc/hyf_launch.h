@@ -1,0 +1,88 @@
+// Host-side launchers of the libhyflash kernels (implemented in the .hip files).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hyf_device.h"
+
+namespace hyf {
+
+// Where a projection writes its output columns: columns < n_split go to out0 (fp32 when
+// out0_f32, else the storage dtype) with row stride ld0; columns >= n_split go to out1 (fp32)
+// at column (col - n_split) with row stride ld1.
+struct Epi {
+  void* out0;
+  int64_t ld0;
+  int32_t out0_f32;
+  int32_t n_split;
+  float* out1;
+  int64_t ld1;
+};
+
+// Rows of the projection input: rows m < M1 come from X1 (row stride K), the rest from X2.
+struct RowSrc {
+  const void* X1;
+  const void* X2;
+  int64_t M1;
+};
+
+// out[m][f] = sum_k X[m][k] * W[f][k]   for m < M, f < Nout (W is [Nout][K], row-major).
+// Picks the weight-streaming kernel (small M) or the tiled MFMA GEMM (large M).
+hipError_t launch_linear(int dtype, RowSrc x, int64_t M, int K, const void* W, int Nout,
+                         const Epi& epi, hipStream_t s);
+
+// Memory scan over segments (see hyf_scan.hip).
+struct ScanArgs {
+  const void* x;      // [rows][ld_x], head h at column h*P
+  const void* B;      // [rows][ld_b], group g at column g*N
+  const float* dt;    // [rows][ld_dt] raw step (before bias)
+  int64_t ld_x, ld_b, ld_dt;
+  const float* a_log;
+  const float* dt_bias;
+  char* state_pool;   // H of request i at state_pool + slot*st_bytes + st_h (if h_direct == null)
+  float* h_direct;    // single-request H (hyf_ssd_scan); overrides the pool when non-null
+  float* part;        // [total_segs][nh][P][N] partial states
+  float* lam;         // [total_segs][nh] segment log-decays
+  int32_t chunks_per_seg;
+  int32_t total_segs;
+};
+hipError_t launch_ssd_state(int dtype, const Shape& sh, const ScanArgs& a, const ReqTable& rt,
+                            int32_t max_segs_per_req, hipStream_t s);
+
+// Round kernels (see hyf_round.hip).
+struct RoundArgs {
+  const float* proj;   // [rows][n_in] fp32: commit rows first (row0 table), then block rows
+  int64_t blk_row0;    // first block row in proj
+  char* state_pool;
+  const float* a_log;
+  const float* dt_bias;
+  const float* d_skip;
+  float* mem;          // [n_req][8][nh][P]
+  float* att_part;     // [n_req][nh][n_split][8][P]
+  float* att_ml;       // [n_req][nh][n_split][8][2]
+  void* o_in;          // [n_req*8][dq] storage dtype
+  int32_t n_split;     // attention splits per (request, head), the last one holds the block keys
+  int32_t keys_per_split;
+  int32_t do_commit;   // commit rows present
+  int32_t do_draft;    // block rows present
+};
+hipError_t launch_commit_small(int dtype, const Shape& sh, const RoundArgs& a, const ReqTable& rt,
+                               hipStream_t s);
+hipError_t launch_attention(int dtype, const Shape& sh, const RoundArgs& a, const ReqTable& rt,
+                            hipStream_t s);
+hipError_t launch_merge(int dtype, const Shape& sh, const RoundArgs& a, const ReqTable& rt,
+                        hipStream_t s);
+
+// Prefill ring append: rows [row0[i] + max(0, n_i - W), row0[i+1]) of request i go to slots
+// (count + j) mod W, from k (row stride ld_k) and v (row stride ld_v), storage dtype.
+hipError_t launch_ring_append(int dtype, const Shape& sh, char* pool, const ReqTable& rt,
+                              const void* k, int64_t ld_k, int64_t k_row0, const void* v,
+                              int64_t ld_v, hipStream_t s);
+// count += rows committed, per request (the last launch of a commit).
+hipError_t launch_bump_counts(char* pool, const Shape& sh, const ReqTable& rt, hipStream_t s);
+// Zero fill (a kernel, not a memset, so graph replays stay correct).
+hipError_t launch_zero(void* p, uint64_t bytes, hipStream_t s);
+hipError_t launch_reset_states(char* pool, const Shape& sh, const ReqTable& rt, hipStream_t s);
+
+}  // namespace hyf

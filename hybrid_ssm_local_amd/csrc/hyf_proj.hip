@@ -1,0 +1,238 @@
+// Projections of the drafter layer: out[m][f] = sum_k X[m][k] * W[f][k].
+//
+// Two kernels, chosen by the number of rows M:
+//  * k_proj_small (M <= 64): the batch-1 round.  The layer's weights are read from HBM exactly
+//    once; every 16 output features are one workgroup whose waves split K into slabs and
+//    reduce their partial tiles through LDS in a fixed order (deterministic).  MFMA 16x16
+//    tiles: W is the A operand (16 features), X^T the B operand (16 rows per tile).
+//  * k_gemm_bf16 (large M): prefill and batched rounds.  128x128 macro tiles, K step 64,
+//    double-buffered LDS, 4 waves of 64x64 each built from 16x16x32 bf16 MFMAs.
+#include "hyf_launch.h"
+
+namespace hyf {
+
+template <typename T>
+__device__ __forceinline__ typename Vec16<T>::type ld_vec(const T* p) {
+  return *reinterpret_cast<const typename Vec16<T>::type*>(p);
+}
+
+template <typename T>
+__device__ __forceinline__ void epi_store(const Epi& e, int64_t m, int f, float v) {
+  if (f < e.n_split) {
+    if (e.out0_f32)
+      static_cast<float*>(e.out0)[m * e.ld0 + f] = v;
+    else
+      static_cast<T*>(e.out0)[m * e.ld0 + f] = from_f32<T>(v);
+  } else {
+    e.out1[m * e.ld1 + (f - e.n_split)] = v;
+  }
+}
+
+__device__ __forceinline__ const void* row_ptr(const RowSrc& xs, int64_t m, int K, int esz) {
+  if (m < xs.M1) return static_cast<const char*>(xs.X1) + m * (int64_t)K * esz;
+  return static_cast<const char*>(xs.X2) + (m - xs.M1) * (int64_t)K * esz;
+}
+
+// ---------------------------------------------------------------------------------------------
+template <typename T, int NW, int MT>
+__global__ void __launch_bounds__(NW * 64)
+k_proj_small(RowSrc xs, int M, int K, const T* __restrict__ W, int Nout, Epi epi) {
+  constexpr int KE = Mfma16<T>::KE;
+  constexpr int VN = Vec16<T>::n;
+  constexpr int U = 4;                // MFMAs per slab
+  constexpr int LANE_K = U * KE;      // contiguous k values a lane covers per slab
+  constexpr int NV = LANE_K / VN;     // 16-byte loads per lane per slab and operand row
+  constexpr int SLAB = 4 * LANE_K;    // k per slab
+  typedef typename Vec16<T>::type V;
+  typedef typename Mfma16<T>::frag Fr;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = lane & 15, g = lane >> 4;
+  const int f0 = blockIdx.x * 16;
+  const int m_base = blockIdx.y * 16 * MT;
+
+  const T* wrow = W + (int64_t)min(f0 + i, Nout - 1) * K;
+  const T* xrow[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = min(m_base + mt * 16 + i, M - 1);
+    xrow[mt] = static_cast<const T*>(row_ptr(xs, m, K, sizeof(T)));
+  }
+
+  f32x4 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nslab = (K + SLAB - 1) / SLAB;
+  for (int s = wave; s < nslab; s += NW) {
+    const int kb = s * SLAB + g * LANE_K;
+    V wv[NV];
+    V xv[MT][NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int k = kb + v * VN;
+      const bool ok = k + VN <= K;
+      wv[v] = ok ? ld_vec<T>(wrow + k) : V{};
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) xv[mt][v] = ok ? ld_vec<T>(xrow[mt] + k) : V{};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      Fr a;
+      if constexpr (KE == 8) a = wv[u]; else a = wv[0][u];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        Fr b;
+        if constexpr (KE == 8) b = xv[mt][u]; else b = xv[mt][0][u];
+        acc[mt] = Mfma16<T>::mma(a, b, acc[mt]);
+      }
+    }
+  }
+
+  // Cross-wave reduction in a fixed order.
+  __shared__ float red[NW][MT][4][64];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave][mt][r][lane] = acc[mt][r];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < MT * 256; idx += NW * 64) {
+    const int mt = idx >> 8, rem = idx & 255;
+    const int fl = rem & 15, ml = rem >> 4;
+    const int src_lane = (fl >> 2) * 16 + ml, r = fl & 3;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) v += red[w][mt][r][src_lane];
+    const int f = f0 + fl;
+    const int m = m_base + mt * 16 + ml;
+    if (f < Nout && m < M) epi_store<T>(epi, m, f, v);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// bf16 GEMM, 128x128 macro tile, K step 64.
+constexpr int GB_M = 128, GB_N = 128, GB_K = 64, GB_LD = GB_K + 8;  // LDS row pitch (elements)
+
+__device__ __forceinline__ void gemm_load_tile(const RowSrc& xs, int M, int K, const bf16* W, int Nout,
+                                               int m0, int n0, int k0, bf16x8 (&ra)[4], bf16x8 (&rb)[4]) {
+  const int t = threadIdx.x;
+  const int gcol = (t & 7) * 8;
+  const int k = k0 + gcol;
+  const bool kok = k + 8 <= K;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = (t >> 3) + 32 * j;
+    const int m = min(m0 + row, M - 1);
+    const bf16* xr = static_cast<const bf16*>(row_ptr(xs, m, K, 2));
+    ra[j] = kok ? *reinterpret_cast<const bf16x8*>(xr + k) : bf16x8{};
+    const int f = min(n0 + row, Nout - 1);
+    rb[j] = kok ? *reinterpret_cast<const bf16x8*>(W + (int64_t)f * K + k) : bf16x8{};
+  }
+}
+
+__device__ __forceinline__ void gemm_store_lds(bf16* la, bf16* lb, const bf16x8 (&ra)[4], const bf16x8 (&rb)[4]) {
+  const int t = threadIdx.x;
+  const int gcol = (t & 7) * 8;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = (t >> 3) + 32 * j;
+    *reinterpret_cast<bf16x8*>(la + row * GB_LD + gcol) = ra[j];
+    *reinterpret_cast<bf16x8*>(lb + row * GB_LD + gcol) = rb[j];
+  }
+}
+
+template <typename TO>
+__global__ void __launch_bounds__(256)
+k_gemm_bf16(RowSrc xs, int M, int K, const bf16* __restrict__ W, int Nout, Epi epi) {
+  __shared__ __attribute__((aligned(16))) bf16 lds[2][2][GB_M * GB_LD];  // [buf][A/B]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = lane & 15, g = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int n0 = blockIdx.x * GB_N, m0 = blockIdx.y * GB_M;
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  bf16x8 ra[4], rb[4];
+  const int nk = (K + GB_K - 1) / GB_K;
+  gemm_load_tile(xs, M, K, W, Nout, m0, n0, 0, ra, rb);
+  gemm_store_lds(lds[0][0], lds[0][1], ra, rb);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) gemm_load_tile(xs, M, K, W, Nout, m0, n0, (kt + 1) * GB_K, ra, rb);
+    const bf16* la = lds[cur][0];
+    const bf16* lb = lds[cur][1];
+#pragma unroll
+    for (int ks = 0; ks < GB_K / 32; ++ks) {
+      bf16x8 fa[4], fb[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        fa[t] = *reinterpret_cast<const bf16x8*>(la + (wm * 64 + t * 16 + i) * GB_LD + ks * 32 + g * 8);
+        fb[t] = *reinterpret_cast<const bf16x8*>(lb + (wn * 64 + t * 16 + i) * GB_LD + ks * 32 + g * 8);
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
+    }
+    if (kt + 1 < nk) gemm_store_lds(lds[cur ^ 1][0], lds[cur ^ 1][1], ra, rb);
+    __syncthreads();
+  }
+  // lane holds C[4g + r][i] of tile (a, b): row m, column f.
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wm * 64 + a * 16 + 4 * g + r;
+        const int f = n0 + wn * 64 + b * 16 + i;
+        if (m < M && f < Nout) epi_store<TO>(epi, m, f, acc[a][b][r]);
+      }
+}
+
+// ---------------------------------------------------------------------------------------------
+template <typename T, int NW>
+static hipError_t launch_small_nw(RowSrc x, int M, int K, const T* W, int Nout, const Epi& epi, hipStream_t s) {
+  const int mt = (M + 15) / 16;
+  const int MT = mt >= 4 ? 4 : mt;
+  dim3 grid((Nout + 15) / 16, (M + 16 * MT - 1) / (16 * MT));
+  dim3 block(NW * 64);
+  switch (MT) {
+    case 1: hipLaunchKernelGGL((k_proj_small<T, NW, 1>), grid, block, 0, s, x, M, K, W, Nout, epi); break;
+    case 2: hipLaunchKernelGGL((k_proj_small<T, NW, 2>), grid, block, 0, s, x, M, K, W, Nout, epi); break;
+    case 3: hipLaunchKernelGGL((k_proj_small<T, NW, 3>), grid, block, 0, s, x, M, K, W, Nout, epi); break;
+    default: hipLaunchKernelGGL((k_proj_small<T, NW, 4>), grid, block, 0, s, x, M, K, W, Nout, epi); break;
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_small(RowSrc x, int M, int K, const T* W, int Nout, const Epi& epi, hipStream_t s) {
+  // The split of K over waves depends on K alone, so an output element is reduced in the same
+  // order whatever rows and columns share the launch (a fused round and a standalone commit give
+  // bit-identical projections).  Long rows use 8 waves to keep more loads in flight.
+  if (K >= 2048) return launch_small_nw<T, 8>(x, M, K, W, Nout, epi, s);
+  return launch_small_nw<T, 4>(x, M, K, W, Nout, epi, s);
+}
+
+hipError_t launch_linear(int dtype, RowSrc x, int64_t M, int K, const void* W, int Nout, const Epi& epi,
+                         hipStream_t s) {
+  if (M <= 0 || Nout <= 0) return hipSuccess;
+  if (dtype == HYF_BF16) {
+    if (M <= 64) return launch_small<bf16>(x, (int)M, K, static_cast<const bf16*>(W), Nout, epi, s);
+    dim3 grid((Nout + GB_N - 1) / GB_N, (unsigned)((M + GB_M - 1) / GB_M));
+    hipLaunchKernelGGL((k_gemm_bf16<bf16>), grid, dim3(256), 0, s, x, (int)M, K, static_cast<const bf16*>(W),
+                       Nout, epi);
+    return hipGetLastError();
+  }
+  // fp32: the streaming kernel, one 64-row block per grid row (the weights stay in L2).
+  return launch_small<float>(x, (int)M, K, static_cast<const float*>(W), Nout, epi, s);
+}
+
+}  // namespace hyf

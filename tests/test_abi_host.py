@@ -1,0 +1,125 @@
+"""Host-only checks of the C ABI: the library loads, exports what the header declares, and
+validates arguments before any device work (no GPU needed: every call here fails validation
+or is a pure host query)."""
+
+import ctypes
+import subprocess
+
+import pytest
+
+from hybrid_ssm_local_amd import hyflash as hf
+from hybrid_ssm_local_amd import inputs as I
+
+
+def test_library_exports_every_declared_function():
+    names = hf.header_functions()
+    assert len(names) >= 12
+    out = subprocess.run(["nm", "-D", "--defined-only", hf.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = {line.split()[-1] for line in out.stdout.splitlines() if " T " in line}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    L = hf.lib()
+    for n in names:
+        assert getattr(L, n) is not None
+    assert hf.hyf_abi_version() == 1
+
+
+def test_struct_sizes_match_the_header():
+    assert ctypes.sizeof(hf.HyfConfig) == 48
+    assert ctypes.sizeof(hf.HyfWeights) == 40
+    assert ctypes.sizeof(hf.HyfStateLayout) == 40
+
+
+@pytest.mark.parametrize("shape", [I.TINY, I.QWEN, I.PHI4, I.PHI4_LONG])
+def test_named_shapes_are_accepted(shape):
+    cfg = hf.make_config(shape)
+    assert hf.hyf_config_check(cfg) == hf.HYF_OK
+    assert hf.hyf_n_in(cfg) == shape.n_in
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 72, hf.HYF_ESHAPE), ("head_dim", 0, hf.HYF_ESHAPE), ("d_state", 300, hf.HYF_ESHAPE),
+    ("n_groups", 3, hf.HYF_ESHAPE), ("window", 0, hf.HYF_ESHAPE), ("block", 7, hf.HYF_ESHAPE),
+    ("chunk", 8, hf.HYF_ESHAPE), ("dtype", 5, hf.HYF_EDTYPE), ("memory", hf.HYF_MEM_GDN, hf.HYF_EUNSUPPORTED),
+    ("cross_slot", 2, hf.HYF_EINVAL), ("reserved", 1, hf.HYF_EINVAL), ("d_model", 100, hf.HYF_ESHAPE),
+])
+def test_bad_configs_are_rejected(field, value, status):
+    cfg = hf.make_config(I.QWEN)
+    setattr(cfg, field, value)
+    assert hf.hyf_config_check(cfg) == status
+    assert hf.hyf_state_bytes(cfg) == 0
+    assert hf.hyf_workspace_bytes(cfg, 1, 8) == 0
+
+
+def test_state_layout_and_the_pages_fp32_state_size():
+    # One Phi-4-shaped layer's H is 40 x 128 x 128 fp32 = 2.5 MiB (the pages' FP32 recurrent state).
+    L = hf.hyf_state_layout_get(hf.make_config(I.PHI4))
+    assert L.k_off - L.h_off == 40 * 128 * 128 * 4 == int(2.5 * 2**20)
+    assert L.count_off == 0 and L.h_off == 256
+    assert L.v_off - L.k_off == L.total - L.v_off == 40 * 512 * 128 * 2
+    for sh in (I.TINY, I.QWEN):
+        L = hf.hyf_state_layout_get(hf.make_config(sh))
+        es = 4 if sh.dtype == "f32" else 2
+        assert L.k_off - L.h_off >= sh.n_heads * sh.head_dim * sh.d_state * 4
+        assert L.v_off - L.k_off >= sh.n_heads * sh.window * sh.head_dim * es
+        assert all(v % 256 == 0 for v in (L.h_off, L.k_off, L.v_off, L.total))
+        assert hf.hyf_state_bytes(hf.make_config(sh)) == L.total
+
+
+def test_workspace_grows_with_requests_and_rows():
+    cfg = hf.make_config(I.QWEN)
+    a = hf.hyf_workspace_bytes(cfg, 1, 8)
+    b = hf.hyf_workspace_bytes(cfg, 1, 8192)
+    c = hf.hyf_workspace_bytes(cfg, 64, 8192)
+    assert 0 < a < b < c
+    assert hf.hyf_workspace_bytes(cfg, 0, 8) == 0
+    assert hf.hyf_workspace_bytes(cfg, hf.HYF_MAX_REQUESTS + 1, 8) == 0
+    assert hf.hyf_ssd_scan_workspace_bytes(cfg, 8192) > 0
+
+
+def test_invalid_calls_fail_before_any_device_work():
+    cfg = hf.make_config(I.TINY)
+    w = hf.HyfWeights(None, None, None, None, None)
+    fake = 1 << 20  # never dereferenced: validation fails first
+    assert hf.hyf_memory_commit(cfg, w, fake, 1, None, 1, fake, [0, 4], None, fake, 1 << 30, 0) == hf.HYF_EINVAL
+    good_w = hf.HyfWeights(fake, fake, fake, fake, fake)
+    # misaligned pool, bad offsets, too many requests, slot outside the pool, duplicate slots
+    assert hf.hyf_memory_commit(cfg, good_w, fake + 8, 1, None, 1, fake, [0, 4], None, fake, 1 << 30, 0) == \
+        hf.HYF_EINVAL
+    assert hf.hyf_memory_commit(cfg, good_w, fake, 1, None, 1, fake, [1, 4], None, fake, 1 << 30, 0) == hf.HYF_EINVAL
+    assert hf.hyf_memory_commit(cfg, good_w, fake, 2, None, 2, fake, [0, 4, 2], None, fake, 1 << 30, 0) == \
+        hf.HYF_EINVAL
+    assert hf.hyf_memory_commit(cfg, good_w, fake, 1, [3], 1, fake, [0, 4], None, fake, 1 << 30, 0) == \
+        hf.HYF_ECAPACITY
+    assert hf.hyf_memory_commit(cfg, good_w, fake, 4, [1, 1], 2, fake, [0, 1, 2], None, fake, 1 << 30, 0) == \
+        hf.HYF_EINVAL
+    n = hf.HYF_MAX_REQUESTS + 1
+    assert hf.hyf_memory_commit(cfg, good_w, fake, n, None, n, fake, list(range(n + 1)), None, fake, 1 << 30, 0) == \
+        hf.HYF_ECAPACITY
+    # workspace too small
+    assert hf.hyf_memory_commit(cfg, good_w, fake, 1, None, 1, fake, [0, 4], None, fake, 16, 0) == \
+        hf.HYF_EWORKSPACE
+    # a round may commit at most `block` rows per request
+    assert hf.hyf_draft_block(cfg, good_w, fake, 1, None, 1, fake, [0, 9], fake, fake, fake, 1 << 30, 0) == \
+        hf.HYF_ECAPACITY
+    # commit rows without offsets
+    assert hf.hyf_draft_block(cfg, good_w, fake, 1, None, 1, fake, None, fake, fake, fake, 1 << 30, 0) == \
+        hf.HYF_EINVAL
+    # scan: y requested without C, negative length
+    assert hf.hyf_ssd_scan(cfg, fake, fake, None, fake, fake, fake, fake, fake, fake, 4, fake, 1 << 30, 0) == \
+        hf.HYF_EINVAL
+    assert hf.hyf_ssd_scan(cfg, fake, fake, None, fake, fake, fake, fake, fake, None, -1, fake, 1 << 30, 0) == \
+        hf.HYF_ECAPACITY
+
+
+def test_empty_commit_is_accepted_without_device_work():
+    cfg = hf.make_config(I.TINY)
+    fake = 1 << 20
+    w = hf.HyfWeights(fake, fake, fake, fake, fake)
+    assert hf.hyf_memory_commit(cfg, w, fake, 1, None, 1, None, [0, 0], None, None, 0, 0) == hf.HYF_OK
+    assert hf.hyf_ssd_scan(cfg, None, None, None, None, fake, fake, fake, fake, None, 0, None, 0, 0) == hf.HYF_OK
+
+
+def test_status_strings():
+    assert hf.status_str(hf.HYF_OK) == "ok"
+    assert "workspace" in hf.status_str(hf.HYF_EWORKSPACE)

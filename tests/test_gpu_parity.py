@@ -1,0 +1,337 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, and the layer's invariants.
+
+Tolerance (max-norm relative, per output tensor): fp32 1e-4; bf16 2e-2 with max abs error 5e-2.
+Each GPU step prints its case before it runs.
+"""
+
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+from hybrid_ssm_local_amd import hyflash as hf
+from hybrid_ssm_local_amd import inputs as I
+from oracle import hyflash_oracle as O
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def assert_close(got, ref, dtype, what=""):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), what
+    err = np.max(np.abs(got - ref)) if got.size else 0.0
+    scale = max(np.max(np.abs(ref)) if ref.size else 0.0, 1e-30)
+    rel = err / scale
+    if dtype == "f32":
+        assert rel <= 1e-4, f"{what}: rel {rel:.3e} (abs {err:.3e})"
+    else:
+        assert rel <= 2e-2 and err <= 5e-2, f"{what}: rel {rel:.3e} abs {err:.3e}"
+    return rel
+
+
+def small_shape(dtype, **kw):
+    base = dict(d_model=256, n_heads=4, head_dim=64, d_state=64, window=128, chunk=64, dtype=dtype)
+    base.update(kw)
+    return I.LayerShape(**base)
+
+
+# ---------------------------------------------------------------- scan level
+
+
+def run_scan(shape, sc, T):
+    cfg = hf.make_config(shape)
+    x = hf.to_device(sc["x"], shape)
+    B = hf.to_device(sc["B"], shape)
+    dt = torch.from_numpy(sc["dt_raw"]).to(DEV)
+    a_log = torch.from_numpy(sc["a_log"]).to(DEV)
+    dt_bias = torch.from_numpy(sc["dt_bias"]).to(DEV)
+    d_skip = torch.from_numpy(sc["d_skip"]).to(DEV)
+    H = torch.from_numpy(sc["H0"]).to(DEV).contiguous()
+    wsb = hf.hyf_ssd_scan_workspace_bytes(cfg, T)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=DEV)
+    hf.check(hf.hyf_ssd_scan(cfg, x, B, None, dt, a_log, dt_bias, d_skip, H, None, T, ws, wsb), "hyf_ssd_scan")
+    torch.cuda.synchronize()
+    return H.cpu().numpy()
+
+
+SCAN_CASES = [
+    ("tiny_fp32", I.TINY, [1, 63, 64, 65, 300, 1024]),
+    ("qwen_bf16", I.QWEN, [7, 64, 129, 1000]),
+    ("phi4_bf16_L256", I.PHI4_LONG, [255, 700]),
+    ("odd_bf16", small_shape("bf16", n_heads=3, head_dim=48, d_state=80, n_groups=3, chunk=32), [1, 100]),
+    ("odd_fp32", small_shape("f32", n_heads=6, head_dim=32, d_state=48, n_groups=2, chunk=16), [37, 200]),
+]
+
+
+@pytest.mark.parametrize("name,shape,Ts", SCAN_CASES, ids=[c[0] for c in SCAN_CASES])
+def test_scan_state_matches_the_sequential_recurrence(name, shape, Ts):
+    for T in Ts:
+        rng = I.rng_streams(T)[0]
+        sc = I.make_scan_inputs(shape, T, rng, with_c=False, h0_scale=0.5)
+        say("hyf_ssd_scan", name, "T", T)
+        H = run_scan(shape, sc, T)
+        ref, _ = O.ssd_sequential(sc["x"], sc["B"], None, sc["dt_raw"], sc["a_log"], sc["dt_bias"], sc["d_skip"],
+                                  sc["H0"], shape.n_groups)
+        assert_close(H, ref, shape.dtype, f"{name} T={T}")
+
+
+def test_scan_full_size_qwen_prefix_sampled_heads():
+    # The 8192-token Qwen-shaped prefix as the benchmark runs it; the oracle checks 4 of 32 heads.
+    shape, T = I.QWEN, 8192
+    sc = I.make_scan_inputs(shape, T, I.rng_streams(11)[0], with_c=False, h0_scale=0.5)
+    say("hyf_ssd_scan qwen T", T)
+    H = run_scan(shape, sc, T)
+    for h in (0, 9, 22, 31):
+        sl = slice(h, h + 1)
+        ref, _ = O.ssd_sequential(sc["x"][:, sl], sc["B"], None, sc["dt_raw"][:, sl], sc["a_log"][sl],
+                                  sc["dt_bias"][sl], sc["d_skip"][sl], sc["H0"][sl])
+        assert_close(H[sl], ref, "bf16", f"head {h}")
+
+
+def test_scan_is_deterministic():
+    shape, T = I.QWEN, 3000
+    sc = I.make_scan_inputs(shape, T, I.rng_streams(12)[0], with_c=False, h0_scale=0.5)
+    say("hyf_ssd_scan determinism")
+    a = run_scan(shape, sc, T)
+    b = run_scan(shape, sc, T)
+    assert np.array_equal(a, b)
+
+
+def test_scan_zero_length_is_a_noop():
+    shape = I.TINY
+    sc = I.make_scan_inputs(shape, 4, I.rng_streams(13)[0], with_c=False, h0_scale=1.0)
+    say("hyf_ssd_scan T=0")
+    cfg = hf.make_config(shape)
+    H = torch.from_numpy(sc["H0"]).to(DEV)
+    f = torch.zeros(4, device=DEV)
+    hf.check(hf.hyf_ssd_scan(cfg, None, None, None, None, f, f, f, H, None, 0, None, 0))
+    torch.cuda.synchronize()
+    assert np.array_equal(H.cpu().numpy(), sc["H0"])
+
+
+# ---------------------------------------------------------------- layer level
+
+
+class Pair:
+    """The HIP layer and the oracle side by side, fed the same rows."""
+
+    def __init__(self, shape, seed, pool_slots=1, max_requests=1, max_rows=8, d_random=True):
+        self.shape = shape
+        self.rng = I.rng_streams(seed)
+        self.w = I.make_weights(shape, self.rng[0], d_random=d_random)
+        self.wo = {k: np.asarray(v, np.float64) for k, v in self.w.items()}
+        self.gpu = hf.DrafterLayer(shape, self.w, pool_slots=pool_slots, max_requests=max_requests,
+                                   max_rows=max_rows)
+        self.ost = [O.new_state(shape) for _ in range(pool_slots)]
+
+    def rows(self, n, stream=1):
+        return I.make_rows(self.rng[stream], n, self.shape.d_model, 1.0 / np.sqrt(self.shape.d_model),
+                           self.shape.dtype)
+
+    def commit(self, feats_list, slots=None):
+        cu = np.concatenate([[0], np.cumsum([len(f) for f in feats_list])]).astype(np.int64)
+        allf = np.concatenate(feats_list) if cu[-1] else np.zeros((0, self.shape.d_model), np.float32)
+        self.gpu.commit(hf.to_device(allf, self.shape) if cu[-1] else None, cu, slots)
+        for i, f in enumerate(feats_list):
+            s = slots[i] if slots is not None else i
+            self.ost[s], _ = O.commit(self.shape, self.wo, self.ost[s], f)
+
+    def draft(self, blocks, commits=None, slots=None):
+        R = len(blocks)
+        bi = hf.to_device(np.concatenate(blocks), self.shape)
+        bo = torch.empty_like(bi)
+        cf = cu = None
+        if commits is not None:
+            cu = np.concatenate([[0], np.cumsum([len(f) for f in commits])]).astype(np.int64)
+            cf = hf.to_device(np.concatenate(commits), self.shape) if cu[-1] else None
+            if cf is None:
+                cf = hf.to_device(np.zeros((1, self.shape.d_model), np.float32), self.shape)
+        self.gpu.draft(bi, bo, cf, cu, slots)
+        outs = []
+        for i in range(R):
+            s = slots[i] if slots is not None else i
+            if commits is not None:
+                self.ost[s], _ = O.commit(self.shape, self.wo, self.ost[s], commits[i])
+            outs.append(O.draft(self.shape, self.wo, self.ost[s], blocks[i]))
+        torch.cuda.synchronize()
+        return bo.float().cpu().numpy().reshape(R, hf.HYF_BLOCK, -1), np.stack(outs)
+
+    def check_state(self, slot=0, what=""):
+        torch.cuda.synchronize()
+        g = self.gpu.state(slot)
+        o = self.ost[slot]
+        assert int(g["count"].item()) == o["count"], what
+        assert_close(g["H"].cpu().numpy(), o["H"], self.shape.dtype, f"{what} H")
+        n = min(o["count"], self.shape.window)
+        assert_close(g["K"].float().cpu().numpy()[:, :n], o["K"][:, :n], self.shape.dtype, f"{what} K")
+        assert_close(g["V"].float().cpu().numpy()[:, :n], o["V"][:, :n], self.shape.dtype, f"{what} V")
+
+
+LAYER_SHAPES = [
+    ("tiny_fp32", I.TINY),
+    ("small_bf16", small_shape("bf16", window=40)),
+    ("odd_bf16", small_shape("bf16", n_heads=5, head_dim=48, d_state=32, n_groups=5, window=20, chunk=32)),
+    ("noncross_fp32", small_shape("f32", window=24, cross_slot=0)),
+]
+
+
+@pytest.mark.parametrize("name,shape", LAYER_SHAPES, ids=[c[0] for c in LAYER_SHAPES])
+def test_rounds_match_the_oracle(name, shape):
+    pr = Pair(shape, seed=21, max_rows=400)
+    say("hyf_state_reset", name)
+    pr.gpu.reset()
+    say("hyf_draft_block on an empty state", name)
+    g, o = pr.draft([pr.rows(8, 3)])
+    assert_close(g, o, shape.dtype, f"{name} empty")
+    say("hyf_memory_commit prefill 300", name)
+    pr.commit([pr.rows(300)])
+    pr.check_state(what=f"{name} prefill")
+    acc_rng = pr.rng[4]
+    for rnd in range(12):
+        a = int(acc_rng.integers(1, 9))
+        say("hyf_draft_block round", rnd, "a", a, name)
+        g, o = pr.draft([pr.rows(8, 3)], commits=[pr.rows(a)])
+        assert_close(g, o, shape.dtype, f"{name} round {rnd}")
+    pr.check_state(what=f"{name} after rounds")
+    say("hyf_memory_commit small", name)
+    pr.commit([pr.rows(5)])
+    pr.check_state(what=f"{name} small commit")
+
+
+def test_qwen_full_size_prefill_and_rounds():
+    # The 8192-row Qwen-shaped prefix and a few rounds, exactly as the benchmark launches them.
+    shape = I.QWEN
+    pr = Pair(shape, seed=31, max_rows=8192, d_random=False)
+    pr.gpu.reset()
+    say("hyf_memory_commit qwen prefill 8192")
+    pr.commit([pr.rows(8192)])
+    pr.check_state(what="qwen prefill")
+    for rnd in range(3):
+        a = [3, 8, 1][rnd]
+        say("hyf_draft_block qwen round", rnd, "a", a)
+        g, o = pr.draft([pr.rows(8, 3)], commits=[pr.rows(a)])
+        assert_close(g, o, "bf16", f"qwen round {rnd}")
+    pr.check_state(what="qwen rounds")
+
+
+def test_draft_never_writes_the_state():
+    shape = small_shape("bf16", window=40)
+    pr = Pair(shape, seed=41, max_rows=100)
+    pr.gpu.reset()
+    pr.commit([pr.rows(57)])
+    torch.cuda.synchronize()
+    before = pr.gpu.state()["blob"].clone()
+    say("hyf_draft_block read-only")
+    pr.draft([pr.rows(8, 3)])
+    assert torch.equal(pr.gpu.state()["blob"], before)
+
+
+def test_state_after_a_round_is_independent_of_the_block_rows():
+    # H and the ring after draft(commit=F, block=X) equal those after draft(commit=F, block=X'), and
+    # those after a standalone commit of F, bit for bit: block rows never enter the memory.
+    shape = small_shape("bf16", window=40)
+    seeds = []
+    for variant in range(3):
+        pr = Pair(shape, seed=51, max_rows=100)
+        pr.gpu.reset()
+        pr.commit([pr.rows(33)])
+        F = pr.rows(6)
+        X = pr.rows(8, 3) if variant != 1 else pr.rows(8, 5)
+        say("I3/I4 variant", variant)
+        if variant < 2:
+            pr.draft([X], commits=[F])
+        else:
+            pr.commit([F])
+        torch.cuda.synchronize()
+        seeds.append(pr.gpu.state()["blob"].clone())
+    assert torch.equal(seeds[0], seeds[1])
+    assert torch.equal(seeds[0], seeds[2])
+
+
+def test_split_invariance_of_commits():
+    # Cutting 10 committed rows into rounds of at most 8 leaves H within tolerance of one commit.
+    shape = small_shape("f32", window=6)
+    comps = [p for p in (list(c) for c in itertools.product(range(1, 9), repeat=2)) if sum(p) == 10]
+    comps += [[1] * 10, [10], [8, 2], [2, 8], [3, 3, 4], [1, 8, 1]]
+    ref = None
+    for parts in comps:
+        pr = Pair(shape, seed=61, max_rows=16)
+        F = pr.rows(10)
+        pr.gpu.reset()
+        say("split", parts)
+        i = 0
+        for p in parts:
+            pr.commit([F[i:i + p]])
+            i += p
+        pr.check_state(what=f"split {parts}")
+        H = pr.gpu.state()["H"].cpu().numpy()
+        if ref is None:
+            ref = H
+        assert_close(H, ref, "f32", f"split {parts}")
+
+
+def test_batched_requests_with_a_slot_table():
+    shape = small_shape("bf16", window=48)
+    R, pool = 5, 8
+    slots = [6, 1, 3, 0, 7]
+    pr = Pair(shape, seed=71, pool_slots=pool, max_requests=R, max_rows=2000)
+    pr.gpu.reset()
+    lens = [300, 17, 0, 129, 64]
+    say("batched prefill", lens)
+    pr.commit([pr.rows(n) for n in lens], slots=slots)
+    for s in slots:
+        pr.check_state(s, what=f"prefill slot {s}")
+    arng = pr.rng[4]
+    for rnd in range(4):
+        a = [int(arng.integers(0 if rnd == 2 else 1, 9)) for _ in range(R)]
+        say("batched round", rnd, a)
+        g, o = pr.draft([pr.rows(8, 3) for _ in range(R)], commits=[pr.rows(n) for n in a], slots=slots)
+        assert_close(g, o, "bf16", f"batched round {rnd}")
+    for s in slots:
+        pr.check_state(s, what=f"rounds slot {s}")
+    # untouched slots stay zero
+    for s in set(range(pool)) - set(slots):
+        assert int(torch.count_nonzero(pr.gpu.state(s)["blob"]).item()) == 0
+
+
+def test_rejected_call_leaves_the_state_untouched():
+    shape = I.TINY
+    pr = Pair(shape, seed=81, max_rows=64)
+    pr.gpu.reset()
+    pr.commit([pr.rows(20)])
+    torch.cuda.synchronize()
+    before = pr.gpu.state()["blob"].clone()
+    f = hf.to_device(pr.rows(4), shape)
+    say("rejected calls")
+    st = hf.hyf_memory_commit(pr.gpu.cfg, pr.gpu.w, pr.gpu.pool, 1, None, 1, f, [0, 4], None, pr.gpu.ws, 64)
+    assert st == hf.HYF_EWORKSPACE
+    bi = hf.to_device(pr.rows(8), shape)
+    st = hf.hyf_draft_block(pr.gpu.cfg, pr.gpu.w, pr.gpu.pool, 1, None, 1, f, [0, 9], bi, torch.empty_like(bi),
+                            pr.gpu.ws, pr.gpu.ws_bytes)
+    assert st == hf.HYF_ECAPACITY
+    torch.cuda.synchronize()
+    assert torch.equal(pr.gpu.state()["blob"], before)
+
+
+def test_round_is_deterministic():
+    shape = I.QWEN
+    outs = []
+    for _ in range(2):
+        pr = Pair(shape, seed=91, max_rows=600, d_random=False)
+        pr.gpu.reset()
+        pr.gpu.commit(hf.to_device(pr.rows(600), shape), [0, 600])
+        bi = hf.to_device(pr.rows(8, 3), shape)
+        bo = torch.empty_like(bi)
+        say("determinism round")
+        pr.gpu.draft(bi, bo, hf.to_device(pr.rows(5), shape), [0, 5])
+        torch.cuda.synchronize()
+        outs.append((bo.clone(), pr.gpu.state()["blob"].clone()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
