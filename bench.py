@@ -1,0 +1,339 @@
+#!/usr/bin/env python3
+"""Throughput of the HyFlash drafter-layer hot path on one MI355X.
+
+A step is one episode of the Qwen3-4B-shaped drafter layer (bf16, d_model 2560, 32 heads x 80,
+d_state 128, chunk 64, window 512, block 7 + anchor, batch 1): reset the request's state, commit
+an 8192-feature prefix (projection GEMM, ring append, chunked scan), then 256 verification
+rounds, each committing 1-8 accepted features and drafting one block (hyf_draft_block).
+All inputs are synthetic and resident in HBM before the timed region.
+
+Printed: one JSON line.  `value` = draft blocks/s per layer over whole steps (prefill included).
+Kernel-level loops time the dominant kernel (the weight-streaming input projection of a round),
+the commit scan on pre-projected inputs and the prefill projection GEMM, each with HIP events on
+the stream the kernels run on.  Six copies of the weights and of the scan inputs are rotated so
+that the working set exceeds the 256 MB last-level cache and the figures are HBM figures.
+The CPU oracle is timed on a bounded sample of the same workload on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "committed feats/s (SSD commit scan) + draft blocks/s per layer; % roofline"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+N_COPIES = 6                 # 6 x 54 MB of weights > 256 MB last-level cache
+WORKLOAD = "qwen3_4b_bf16"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--kernel-reps", type=int, default=60)
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    p.add_argument("--profile", action="store_true", help="short run for a profiler (2 steps, few reps)")
+    return p.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+class Episode:
+    """Device-resident inputs of one step and the precomputed C-ABI arguments."""
+
+    def __init__(self, torch, hf, I):
+        wl = I.WORKLOADS[WORKLOAD]
+        self.shape = sh = wl["shape"]
+        self.T, self.R = wl["prefix"], wl["rounds"]
+        d = sh.d_model
+        rng = I.rng_streams(wl["seed"])
+        w = I.make_weights(sh, rng[0])
+        prefix = I.make_rows(rng[1], self.T, d, wl["feat_scale"], sh.dtype)
+        self.acc = I.acceptance_lengths(rng[4], self.R)
+        commits = I.make_rows(rng[2], int(self.acc.sum()), d, wl["feat_scale"], sh.dtype)
+        blocks = I.make_rows(rng[3], self.R * 8, d, wl["block_scale"], sh.dtype)
+        self.host_w = w
+
+        self.cfg = hf.make_config(sh)
+        dev = "cuda"
+        self.w_in = [hf.to_device(w["w_in"], sh, dev) for _ in range(N_COPIES)]
+        self.w_out = [hf.to_device(w["w_out"], sh, dev) for _ in range(N_COPIES)]
+        self.a_log = hf.to_device(w["a_log"], sh, dev, storage=False)
+        self.dt_bias = hf.to_device(w["dt_bias"], sh, dev, storage=False)
+        self.d_skip = hf.to_device(w["d_skip"], sh, dev, storage=False)
+        self.wts = [hf.HyfWeights(self.w_in[i].data_ptr(), self.w_out[i].data_ptr(), self.a_log.data_ptr(),
+                                  self.dt_bias.data_ptr(), self.d_skip.data_ptr()) for i in range(N_COPIES)]
+        self.state_bytes = hf.hyf_state_bytes(self.cfg)
+        self.pool = torch.zeros(self.state_bytes, dtype=torch.uint8, device=dev)
+        self.ws_bytes = hf.hyf_workspace_bytes(self.cfg, 1, self.T)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        self.prefix = hf.to_device(prefix, sh, dev)
+        self.commits = hf.to_device(commits, sh, dev)
+        self.blocks = hf.to_device(blocks, sh, dev)
+        self.out = torch.empty_like(self.blocks)
+
+        es = 2
+        self.cu_pre = (ctypes.c_int64 * 2)(0, self.T)
+        self.cu = [(ctypes.c_int64 * 2)(0, int(a)) for a in self.acc]
+        offs = [0]
+        for a in self.acc:
+            offs.append(offs[-1] + int(a))
+        cb, bb, ob = self.commits.data_ptr(), self.blocks.data_ptr(), self.out.data_ptr()
+        self.c_ptr = [ctypes.c_void_p(cb + offs[i] * d * es) for i in range(self.R)]
+        self.b_ptr = [ctypes.c_void_p(bb + i * 8 * d * es) for i in range(self.R)]
+        self.o_ptr = [ctypes.c_void_p(ob + i * 8 * d * es) for i in range(self.R)]
+        self.lib = hf.lib()
+        self.cfg_ref = ctypes.byref(self.cfg)
+        self.w_ref = [ctypes.byref(x) for x in self.wts]
+        self.pool_p = ctypes.c_void_p(self.pool.data_ptr())
+        self.ws_p = ctypes.c_void_p(self.ws.data_ptr())
+        self.pre_p = ctypes.c_void_p(self.prefix.data_ptr())
+        self.copy = 0
+
+    def step(self, stream, events=None):
+        L, s = self.lib, ctypes.c_void_p(stream)
+        if events:
+            events[0].record()
+        st = L.hyf_state_reset(self.cfg_ref, self.pool_p, 1, None, 1, s)
+        st |= L.hyf_memory_commit(self.cfg_ref, self.w_ref[self.copy], self.pool_p, 1, None, 1, self.pre_p,
+                                  self.cu_pre, None, self.ws_p, self.ws_bytes, s)
+        if events:
+            events[1].record()
+        for i in range(self.R):
+            self.copy = (self.copy + 1) % N_COPIES
+            st |= L.hyf_draft_block(self.cfg_ref, self.w_ref[self.copy], self.pool_p, 1, None, 1, self.c_ptr[i],
+                                    self.cu[i], self.b_ptr[i], self.o_ptr[i], self.ws_p, self.ws_bytes, s)
+        if events:
+            events[2].record()
+        if st:
+            raise RuntimeError(f"libhyflash call failed (status bits {st})")
+
+
+def time_calls(torch, fn, reps):
+    """Per-call HIP events on the current stream; returns mean milliseconds per call."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for i in range(reps):
+        ev[i][0].record()
+        fn(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    return sum(ms) / len(ms), sorted(ms)[len(ms) // 2]
+
+
+def kernel_loops(torch, hf, I, ep, reps):
+    sh = ep.shape
+    d, nh, P, N = sh.d_model, sh.n_heads, sh.head_dim, sh.d_state
+    cfg = ep.cfg
+    out = {}
+    # 1. input projection of a round: the weight-streaming kernel, 12 rows (a = 4 committed + 8 block)
+    M = 12
+    X = ep.blocks[:M]
+    y = torch.empty((M, sh.n_in), dtype=torch.float32, device="cuda")
+    st = [0]
+
+    def proj(i):
+        st[0] |= hf.hyf_linear(cfg, X, M, d, ep.w_in[i % N_COPIES], sh.n_in, y, 1)
+
+    proj(0)
+    mean_ms, med_ms = time_calls(torch, proj, reps)
+    bytes_ = sh.n_in * d * 2 + M * d * 2 + M * sh.n_in * 4
+    out["proj"] = dict(mean_us=mean_ms * 1e3, median_us=med_ms * 1e3, bytes=bytes_,
+                       gbs=bytes_ / (mean_ms * 1e-3) / 1e9)
+    # 2. commit scan on pre-projected inputs (x, B, dt_raw), T = prefix, rotated copies
+    T = ep.T
+    sc = I.make_scan_inputs(sh, T, I.rng_streams(100)[0], with_c=False, h0_scale=0.0)
+    # time-blocked operands, the layout the prefill GEMM hands the scan
+    xT = hf.to_device(hf.time_tiled(sc["x"], T, hf.elem_bytes(sh)), sh)
+    BT = hf.to_device(hf.time_tiled(sc["B"], T, hf.elem_bytes(sh)), sh)
+    dtT = torch.from_numpy(hf.time_blocked(sc["dt_raw"], T)).cuda()
+    scan_in = [dict(x=xT.clone(), B=BT.clone(), dt=dtT.clone(), H=torch.zeros((nh, P, N), device="cuda"))
+               for _ in range(N_COPIES)]
+    wsb = hf.hyf_ssd_scan_workspace_bytes(cfg, T)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+
+    def scan(i):
+        c = scan_in[i % N_COPIES]
+        st[0] |= hf.hyf_ssd_scan(cfg, c["x"], c["B"], None, c["dt"], ep.a_log, ep.dt_bias, ep.d_skip, c["H"],
+                                 None, T, ws, wsb)
+
+    scan(0)
+    mean_ms, med_ms = time_calls(torch, scan, reps)
+    sbytes = T * (nh * P * 2 + sh.gn * 2 + nh * 4) + 2 * nh * P * N * 4
+    out["scan"] = dict(mean_us=mean_ms * 1e3, median_us=med_ms * 1e3, bytes=sbytes,
+                       gbs=sbytes / (mean_ms * 1e-3) / 1e9, feats_per_s=T / (mean_ms * 1e-3))
+    # 3. prefill projection GEMM (v | B | dt columns over the whole prefix)
+    nvbd = sh.dq + sh.gn + nh
+    g = torch.empty((T, nvbd), dtype=torch.bfloat16, device="cuda")
+    off = (sh.in_groups["v"][0]) * d * 2
+
+    def gemm(i):
+        st[0] |= hf.hyf_linear(cfg, ep.prefix, T, d, ep.w_in[i % N_COPIES].data_ptr() + off, nvbd, g, 0)
+
+    gemm(0)
+    mean_ms, med_ms = time_calls(torch, gemm, max(4, reps // 6))
+    flops = 2.0 * T * d * nvbd
+    out["gemm"] = dict(mean_us=mean_ms * 1e3, median_us=med_ms * 1e3, flops=flops,
+                       tflops=flops / (mean_ms * 1e-3) / 1e12)
+    if st[0]:
+        raise RuntimeError("kernel loop call failed")
+    return out
+
+
+def cpu_baseline(I, ep):
+    """The float64 oracle on a bounded slice of the same workload (4096-row prefix + 128 rounds)."""
+    import numpy as np
+
+    from oracle import hyflash_oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([x["num_threads"] for x in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    sh = ep.shape
+    wl = I.WORKLOADS[WORKLOAD]
+    w = {k: np.asarray(v, np.float64) for k, v in ep.host_w.items()}
+    rng = I.rng_streams(wl["seed"] + 1000)
+    n_pre, n_rounds = 4096, 128
+    pre = I.make_rows(rng[1], n_pre, sh.d_model, wl["feat_scale"], sh.dtype)
+    t0 = time.perf_counter()
+    st, _ = O.commit(sh, w, O.new_state(sh), pre)
+    t_commit = time.perf_counter() - t0
+    acc = I.acceptance_lengths(rng[4], n_rounds)
+    t0 = time.perf_counter()
+    for a in acc:
+        cf = I.make_rows(rng[2], int(a), sh.d_model, wl["feat_scale"], sh.dtype)
+        blk = I.make_rows(rng[3], 8, sh.d_model, wl["block_scale"], sh.dtype)
+        st, _ = O.round_step(sh, w, st, cf, blk)
+    t_rounds = time.perf_counter() - t0
+    return {"value": n_rounds / t_rounds, "unit": "draft blocks/s per layer", "cores": cores, "kind": "oracle",
+            "sample": f"float64 NumPy oracle: {n_pre}-feature prefix commit, then {n_rounds} rounds "
+                      f"(acceptance 1-8) of the same Qwen3-4B-shaped layer",
+            "commit_feats_per_s": n_pre / t_commit, "seconds": t_commit + t_rounds}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+    if args.profile:
+        args.steps, args.warmup, args.kernel_reps, args.no_cpu = 2, 1, 12, True
+
+    import torch
+
+    from hybrid_ssm_local_amd import hyflash as hf
+    from hybrid_ssm_local_amd import inputs as I
+
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    log("building episode inputs")
+    ep = Episode(torch, hf, I)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    # ---- eager steps
+    log("warmup", args.warmup)
+    for _ in range(args.warmup):
+        ep.step(stream)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    log("timed eager steps", args.steps)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for k in range(args.steps):
+        ep.step(stream, evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    step_ms = [e[0].elapsed_time(e[2]) for e in evs]
+    pre_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    rnd_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    eager_ms = sum(step_ms) / len(step_ms)
+
+    # ---- the same step replayed from a captured HIP graph (no host launch cost per kernel)
+    log("graph capture")
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    with torch.cuda.stream(cs):
+        ep.step(cs.cuda_stream)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=cs):
+        ep.step(cs.cuda_stream)
+    for _ in range(max(1, args.warmup)):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    graph_ms = e0.elapsed_time(e1) / args.steps
+
+    log("kernel loops")
+    kl = kernel_loops(torch, hf, I, ep, args.kernel_reps)
+    cpu = None if args.no_cpu else cpu_baseline(I, ep)
+
+    sh = ep.shape
+    R = ep.R
+    proj, scan, gemm = kl["proj"], kl["scan"], kl["gemm"]
+    res = {
+        "metric": METRIC,
+        "value": R / (eager_ms * 1e-3),
+        "unit": "draft blocks/s per layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": eager_ms,
+        "wall_s": wall,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1)/sqrt(d) features, Xavier-normal weights)",
+        "config": {"workload": "Qwen3-4B-shaped HyFlash drafter layer: prefix commit of 8192 features, then "
+                               "256 rounds of commit (1-8 accepted) + draft block, batch 1",
+                   "d_model": sh.d_model, "n_heads": sh.n_heads, "head_dim": sh.head_dim, "d_state": sh.d_state,
+                   "chunk": sh.chunk, "window": sh.window, "block": sh.block, "prefix": ep.T, "rounds": R,
+                   "committed_rows": int(ep.acc.sum()), "parallelism": "single GPU"},
+        "breakdown": {"prefill_commit_us": 1e3 * sum(pre_ms) / len(pre_ms),
+                      "rounds_us": 1e3 * sum(rnd_ms) / len(rnd_ms),
+                      "round_us": 1e3 * sum(rnd_ms) / len(rnd_ms) / R,
+                      "graph_replay_ms_per_step": graph_ms,
+                      "graph_blocks_per_s": R / (graph_ms * 1e-3)},
+        "commit_scan": {"value": scan["feats_per_s"], "unit": "committed feats/s", "T": ep.T,
+                        "avg_us": scan["mean_us"],
+                        "roofline": {"bound": "hbm", "achieved": scan["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                     "frac": scan["gbs"] / HBM_PEAK_GBS, "traffic": None,
+                                     "bytes_per_launch": scan["bytes"]}},
+        "roofline": {"bound": "hbm", "achieved": proj["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": proj["gbs"] / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "k_proj_small<bf16,8,1>: input projection of a round (12 rows x w_in)",
+                     "bytes_per_launch": proj["bytes"], "avg_us": proj["mean_us"]},
+        "gemm_roofline": {"bound": "mfma", "achieved": gemm["tflops"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                          "frac": gemm["tflops"] / BF16_PEAK_TFLOPS,
+                          "kernel": "k_gemm_bf16: prefill projection 8192 x 2560 x 2720", "avg_us": gemm["mean_us"]},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -10,7 +10,8 @@ using namespace hyf;
 namespace {
 
 constexpr uint64_t ALIGN = 256;
-constexpr int SCAN_TARGET_WGS = 512;  // scan workgroups the segment split aims for
+constexpr int SCAN_TARGET_WGS = 256;         // scan workgroups the segment split aims for (one per CU)
+constexpr int64_t SCAN_MIN_SEG_TOKENS = 2048;  // shortest segment the split makes
 
 uint64_t align_up(uint64_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 int esize(int dtype) { return dtype == HYF_BF16 ? 2 : 4; }
@@ -30,7 +31,7 @@ int check_cfg(const hyf_config* c) {
   if (c->n_groups < 1 || c->n_heads % c->n_groups) return HYF_ESHAPE;
   if (c->window < 1 || c->window > 8192) return HYF_ESHAPE;
   if (c->block != HYF_BLOCK) return HYF_ESHAPE;
-  if (c->chunk < 16 || c->chunk > 1024 || c->chunk % 16) return HYF_ESHAPE;
+  if (c->chunk < 16 || c->chunk > 1024 || (c->chunk & (c->chunk - 1))) return HYF_ESHAPE;
   if ((int64_t)c->n_heads * c->head_dim > 65536) return HYF_ESHAPE;
   return HYF_OK;
 }
@@ -75,15 +76,43 @@ Shape make_shape(const hyf_config* c) {
 
 int n_att_split(const Shape& s) { return (s.W + 63) / 64 + 1; }
 
-// Segment policy of the scan: whole chunks per segment, the same count for every request.
-int32_t scan_chunks_per_seg(const Shape& s, int64_t total_chunks) {
-  const int64_t seg_target = (SCAN_TARGET_WGS + s.nh - 1) / s.nh;
+// Segment policy of the scan: whole chunks per segment, the same count for every request, about
+// SCAN_TARGET_WGS workgroups in all, segments no shorter than SCAN_MIN_SEG_TOKENS (each segment
+// costs one partial state written and read back) and no longer than one workgroup's LDS holds
+// weights for.
+int64_t scan_seg_target(const Shape& s) {
+  const int64_t per_seg = scan_items_per_seg(s);
+  const int64_t t = (SCAN_TARGET_WGS + per_seg - 1) / per_seg;
+  return t < 1 ? 1 : t;
+}
+int64_t scan_cap_chunks(const Shape& s, int dtype) {
+  const int64_t c = scan_max_seg_tokens(s, esize(dtype)) / s.L;
+  return c < 1 ? 1 : c;
+}
+// Segments start on a block boundary of the time-blocked layout: chunks per segment is a
+// multiple of HYF_TBLK / L when the chunk is shorter than a block (chunk lengths are powers of 2).
+int64_t scan_cps_unit(const Shape& s) { return s.L >= HYF_TBLK ? 1 : HYF_TBLK / s.L; }
+int32_t scan_chunks_per_seg(const Shape& s, int dtype, int64_t total_chunks) {
+  const int64_t seg_target = scan_seg_target(s);
+  const int64_t unit = scan_cps_unit(s);
   int64_t cps = (total_chunks + seg_target - 1) / seg_target;
-  return (int32_t)(cps < 1 ? 1 : cps);
+  const int64_t min_cps = SCAN_MIN_SEG_TOKENS / s.L;
+  if (cps < min_cps) cps = min_cps;
+  const int64_t cap = scan_cap_chunks(s, dtype) / unit * unit;
+  cps = (cps + unit - 1) / unit * unit;
+  if (cps > cap) cps = cap;
+  return (int32_t)(cps < unit ? unit : cps);
 }
-int64_t scan_max_segs(const Shape& s, int32_t n_req) {
-  return (SCAN_TARGET_WGS + s.nh - 1) / s.nh + n_req;
+// Bound on sum_i ceil(chunks_i / cps): at most (total chunks) / cps + n_req, with total chunks at
+// most rows / L + n_req, and (total chunks) / cps at most seg_target unless the cap binds.
+int64_t scan_max_segs(const Shape& s, int dtype, int32_t n_req, int64_t rows) {
+  const int64_t unit = s.L >= HYF_TBLK ? 1 : HYF_TBLK / s.L;
+  int64_t cap = scan_cap_chunks(s, dtype) / unit * unit;
+  if (cap < unit) cap = unit;
+  return scan_seg_target(s) + 2 * (int64_t)n_req + rows / (cap * s.L) + 1;
 }
+// Blocks of the time-blocked buffers for `rows` tokens over R requests (each request starts a block).
+int64_t time_blocks(int64_t rows, int32_t R) { return rows / HYF_TBLK + R + 1; }
 
 struct WsDraft {
   uint64_t proj, mem, att_part, att_ml, o_in, end;
@@ -113,11 +142,12 @@ WsCommit ws_commit(const Shape& s, int dtype, int32_t R, int64_t rows) {
   WsCommit w;
   uint64_t o = 0;
   const int64_t krows = rows < (int64_t)R * s.W ? rows : (int64_t)R * s.W;
-  const int64_t segs = scan_max_segs(s, R);
-  w.vb = o;
-  o += align_up((uint64_t)rows * (s.dq + s.gn) * esize(dtype));
-  w.dt = o;
-  o += align_up((uint64_t)rows * s.nh * 4);
+  const int64_t segs = scan_max_segs(s, dtype, R, rows);
+  const int64_t nblk = time_blocks(rows, R);
+  w.vb = o;  // v | B time-blocked: [nblk][dq + gn][HYF_TBLK]
+  o += align_up((uint64_t)nblk * (s.dq + s.gn) * HYF_TBLK * esize(dtype));
+  w.dt = o;  // raw step time-blocked: [nblk][nh][HYF_TBLK] fp32
+  o += align_up((uint64_t)nblk * s.nh * HYF_TBLK * 4);
   w.kb = o;
   o += align_up((uint64_t)krows * s.dq * esize(dtype));
   w.part = o;
@@ -148,14 +178,20 @@ int build_table(const Shape& s, int32_t pool_slots, const int32_t* slots, int32_
       if (cu[i + 1] < cu[i]) return HYF_EINVAL;
     if (cu[n_req] > ((int64_t)1 << 30)) return HYF_ECAPACITY;
     for (int i = 0; i <= n_req; ++i) rt->row0[i] = (int32_t)cu[i];
+    int64_t c = 0;
+    for (int i = 0; i < n_req; ++i) {
+      rt->blk0[i] = (int32_t)c;
+      c += (cu[i + 1] - cu[i] + HYF_TBLK - 1) / HYF_TBLK;
+    }
+    rt->blk0[n_req] = (int32_t)c;
   }
   return HYF_OK;
 }
 
-void fill_segments(const Shape& s, ReqTable* rt, int32_t* cps_out, int32_t* total_out, int32_t* max_out) {
+void fill_segments(const Shape& s, int dtype, ReqTable* rt, int32_t* cps_out, int32_t* total_out, int32_t* max_out) {
   int64_t total_chunks = 0;
   for (int i = 0; i < rt->n_req; ++i) total_chunks += (rt->row0[i + 1] - rt->row0[i] + s.L - 1) / s.L;
-  const int32_t cps = scan_chunks_per_seg(s, total_chunks);
+  const int32_t cps = scan_chunks_per_seg(s, dtype, total_chunks);
   int32_t q = 0, mx = 0;
   for (int i = 0; i < rt->n_req; ++i) {
     rt->seg0[i] = q;
@@ -231,7 +267,7 @@ size_t hyf_workspace_bytes(const hyf_config* cfg, int32_t max_requests, int64_t 
 size_t hyf_ssd_scan_workspace_bytes(const hyf_config* cfg, int64_t T) {
   if (check_cfg(cfg) != HYF_OK || T < 0) return 0;
   const Shape s = make_shape(cfg);
-  const int64_t segs = scan_max_segs(s, 1);
+  const int64_t segs = scan_max_segs(s, cfg->dtype, 1, T);
   return (size_t)(align_up((uint64_t)segs * s.nh * s.P * s.N * 4) + align_up((uint64_t)segs * s.nh * 4));
 }
 
@@ -293,38 +329,43 @@ int hyf_memory_commit(const hyf_config* cfg, const hyf_weights* w, void* state_p
     return hip_status(launch_bump_counts(pool, s, rt, hs));
   }
 
-  // Prefill-sized commit: GEMM -> ring append -> chunked scan -> count.
+  // Prefill-sized commit: projection GEMMs -> ring append -> scan -> count.
+  // The scan's operands v, B and dt are written time-contiguous (feature-major, each request's
+  // tokens starting at a multiple of 8) so the scan streams them as plain 16-byte rows.
   const WsCommit L = ws_commit(s, dt, n_req, rows);
-  void* vb = wsb + L.vb;
-  float* dtb = reinterpret_cast<float*>(wsb + L.dt);
-  void* kb = wsb + L.kb;
-  RowSrc xs{feats, feats, rows};
+  char* vbT = wsb + L.vb;
+  float* dtT = reinterpret_cast<float*>(wsb + L.dt);
+  char* kb = wsb + L.kb;
   const int nvb = s.dq + s.gn;
-  Epi e{vb, nvb, 0, nvb, dtb, s.nh};
-  hipError_t he = launch_linear(dt, xs, rows, s.d, static_cast<const char*>(w->w_in) + (int64_t)s.off_v * s.d * es,
-                                nvb + s.nh, e, hs);
-  if (he != hipSuccess) return HYF_EHIP;
-  // k only for the rows that stay in the window: the last min(n_i, W) of each request.
+  const int64_t vb_blk = (int64_t)nvb * HYF_TBLK;  // block strides (elements) of v | B and of dt
+  const int64_t dt_blk = (int64_t)s.nh * HYF_TBLK;
+  const char* w_vbd = static_cast<const char*>(w->w_in) + (int64_t)s.off_v * s.d * es;
+  const char* w_k = static_cast<const char*>(w->w_in) + (int64_t)s.off_k * s.d * es;
+  hipError_t he;
   int64_t krow = 0;
   for (int i = 0; i < n_req; ++i) {
     const int64_t n = cu_rows[i + 1] - cu_rows[i];
+    if (n == 0) continue;
+    const char* src = static_cast<const char*>(feats) + cu_rows[i] * (int64_t)s.d * es;
+    RowSrc xs{src, src, n};
+    Epi e{vbT + rt.blk0[i] * vb_blk * es, vb_blk, 0, nvb, dtT + rt.blk0[i] * dt_blk, dt_blk, 1};
+    if ((he = launch_linear(dt, xs, n, s.d, w_vbd, nvb + s.nh, e, hs)) != hipSuccess) return HYF_EHIP;
+    // k only for the rows that stay in the window: the last min(n_i, W) of the request.
     const int64_t m = n < s.W ? n : s.W;
-    if (m == 0) continue;
-    const char* src = static_cast<const char*>(feats) + (cu_rows[i] + n - m) * (int64_t)s.d * es;
-    RowSrc ks{src, src, m};
-    Epi ek{static_cast<char*>(kb) + krow * s.dq * es, s.dq, 0, s.dq, nullptr, 0};
-    he = launch_linear(dt, ks, m, s.d, static_cast<const char*>(w->w_in) + (int64_t)s.off_k * s.d * es, s.dq, ek, hs);
-    if (he != hipSuccess) return HYF_EHIP;
+    const char* ksrc = src + (n - m) * (int64_t)s.d * es;
+    RowSrc ks{ksrc, ksrc, m};
+    Epi ek{kb + krow * s.dq * es, s.dq, 0, s.dq, nullptr, 0, 0};
+    if ((he = launch_linear(dt, ks, m, s.d, w_k, s.dq, ek, hs)) != hipSuccess) return HYF_EHIP;
     krow += m;
   }
-  if ((he = launch_ring_append(dt, s, pool, rt, kb, s.dq, 0, vb, nvb, hs)) != hipSuccess) return HYF_EHIP;
+  if ((he = launch_ring_append(dt, s, pool, rt, kb, s.dq, vbT, vb_blk, hs)) != hipSuccess) return HYF_EHIP;
   ScanArgs sa{};
-  sa.x = vb;
-  sa.B = static_cast<const char*>(vb) + (int64_t)s.dq * es;
-  sa.dt = dtb;
-  sa.ld_x = nvb;
-  sa.ld_b = nvb;
-  sa.ld_dt = s.nh;
+  sa.x = vbT;
+  sa.B = vbT + (int64_t)s.dq * HYF_TBLK * es;
+  sa.dt = dtT;
+  sa.xblk = vb_blk;
+  sa.bblk = vb_blk;
+  sa.dblk = dt_blk;
   sa.a_log = w->a_log;
   sa.dt_bias = w->dt_bias;
   sa.state_pool = pool;
@@ -332,7 +373,7 @@ int hyf_memory_commit(const hyf_config* cfg, const hyf_weights* w, void* state_p
   sa.part = reinterpret_cast<float*>(wsb + L.part);
   sa.lam = reinterpret_cast<float*>(wsb + L.lam);
   int32_t max_segs = 0;
-  fill_segments(s, &rt, &sa.chunks_per_seg, &sa.total_segs, &max_segs);
+  fill_segments(s, dt, &rt, &sa.chunks_per_seg, &sa.total_segs, &max_segs);
   if ((he = launch_ssd_state(dt, s, sa, rt, max_segs, hs)) != hipSuccess) return HYF_EHIP;
   return hip_status(launch_bump_counts(pool, s, rt, hs));
 }
@@ -394,6 +435,18 @@ int hyf_draft_block(const hyf_config* cfg, const hyf_weights* w, void* state_poo
   return hip_status(launch_linear(dt, xo, (int64_t)HYF_BLOCK * n_req, s.dq, w->w_out, s.d, eo, hs));
 }
 
+int hyf_linear(const hyf_config* cfg, const void* X, int64_t M, int32_t K, const void* W, int32_t Nout, void* out,
+               int32_t out_f32, void* stream) {
+  const int st = check_cfg(cfg);
+  if (st != HYF_OK) return st;
+  if (M < 0 || M > ((int64_t)1 << 30) || K < 8 || K % 8 || Nout < 1) return HYF_ESHAPE;
+  if (M == 0) return HYF_OK;
+  if (!X || !W || !out || !aligned(X, 16) || !aligned(W, 16) || !aligned(out, 4)) return HYF_EINVAL;
+  RowSrc xs{X, X, M};
+  Epi e{out, Nout, out_f32 ? 1 : 0, Nout, nullptr, 0};
+  return hip_status(launch_linear(cfg->dtype, xs, M, K, W, Nout, e, static_cast<hipStream_t>(stream)));
+}
+
 int hyf_ssd_scan(const hyf_config* cfg, const void* x, const void* B, const void* C_opt, const float* dt_raw,
                  const float* a_log, const float* dt_bias, const float* d_skip, float* H_inout, void* y_opt, int64_t T,
                  void* ws, size_t ws_bytes, void* stream) {
@@ -404,29 +457,30 @@ int hyf_ssd_scan(const hyf_config* cfg, const void* x, const void* B, const void
   if ((y_opt != nullptr) != (C_opt != nullptr)) return HYF_EINVAL;
   if (y_opt) return HYF_EUNSUPPORTED;
   if (T == 0) return HYF_OK;
-  if (!x || !B || !dt_raw || !aligned(x, 16) || !aligned(B, 16)) return HYF_EINVAL;
+  if (!x || !B || !dt_raw || !aligned(x, 16) || !aligned(B, 16) || !aligned(dt_raw, 16)) return HYF_EINVAL;
   if (!ws || !aligned(ws, ALIGN) || ws_bytes < hyf_ssd_scan_workspace_bytes(cfg, T)) return HYF_EWORKSPACE;
   const Shape s = make_shape(cfg);
   ReqTable rt;
   memset(&rt, 0, sizeof(rt));
   rt.n_req = 1;
   rt.row0[1] = (int32_t)T;
+  rt.blk0[1] = (int32_t)((T + HYF_TBLK - 1) / HYF_TBLK);
   ScanArgs sa{};
   sa.x = x;
   sa.B = B;
   sa.dt = dt_raw;
-  sa.ld_x = (int64_t)s.nh * s.P;
-  sa.ld_b = s.gn;
-  sa.ld_dt = s.nh;
+  sa.xblk = (int64_t)s.nh * s.P * HYF_TBLK;
+  sa.bblk = (int64_t)s.gn * HYF_TBLK;
+  sa.dblk = (int64_t)s.nh * HYF_TBLK;
   sa.a_log = a_log;
   sa.dt_bias = dt_bias;
   sa.state_pool = nullptr;
   sa.h_direct = H_inout;
-  const int64_t segs = scan_max_segs(s, 1);
+  const int64_t segs = scan_max_segs(s, cfg->dtype, 1, T);
   sa.part = static_cast<float*>(ws);
   sa.lam = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((uint64_t)segs * s.nh * s.P * s.N * 4));
   int32_t max_segs = 0;
-  fill_segments(s, &rt, &sa.chunks_per_seg, &sa.total_segs, &max_segs);
+  fill_segments(s, cfg->dtype, &rt, &sa.chunks_per_seg, &sa.total_segs, &max_segs);
   return hip_status(launch_ssd_state(cfg->dtype, s, sa, rt, max_segs, static_cast<hipStream_t>(stream)));
 }
 

@@ -15,13 +15,27 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 // Per-call request table, passed by value in the kernel arguments (no host->device copy, so
 // a call can be captured in a graph).  Request i owns pool blob slot[i]; its commit rows are
-// rows row0[i] .. row0[i+1] of the call's commit-row space; seg0 indexes scan segments.
+// rows row0[i] .. row0[i+1] of the call's commit-row space; in time-blocked buffers its tokens
+// start at block blk0[i] (blocks of HYF_TBLK tokens); seg0 indexes scan segments.
 struct ReqTable {
   int32_t n_req;
   int32_t slot[HYF_MAX_REQUESTS];
   int32_t row0[HYF_MAX_REQUESTS + 1];
+  int32_t blk0[HYF_MAX_REQUESTS + 1];
   int32_t seg0[HYF_MAX_REQUESTS + 1];
 };
+
+// Tiled time-blocked layout of the scan's MFMA operands x and B.  A block holds HYF_TBLK tokens of
+// F features (F a multiple of 16).  Features come in groups of 16 and tokens in runs of
+// KT = 4 VN, where VN = 16 / sizeof(T) tokens fill 16 bytes; a 16 x KT tile is 4 slices of VN
+// tokens, and slice s holds, feature by feature, VN consecutive tokens.  One tile is thus the
+// 16-byte chunks that the 64 lanes of one 16x16 MFMA load, in lane order (1 KiB, contiguous).
+// Returns the element offset of (feature f, token t < HYF_TBLK) inside its block.
+template <typename T>
+__host__ __device__ __forceinline__ int64_t tile_off(int64_t f, int t) {
+  constexpr int VN = 16 / (int)sizeof(T), KT = 4 * VN, NJ = HYF_TBLK / KT;
+  return (((f / 16) * NJ + t / KT) * 64 + ((t % KT) / VN) * 16 + f % 16) * VN + t % VN;
+}
 
 // Static layer shape as the kernels see it.
 struct Shape {

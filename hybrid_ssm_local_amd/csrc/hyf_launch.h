@@ -10,7 +10,10 @@ namespace hyf {
 
 // Where a projection writes its output columns: columns < n_split go to out0 (fp32 when
 // out0_f32, else the storage dtype) with row stride ld0; columns >= n_split go to out1 (fp32)
-// at column (col - n_split) with row stride ld1.
+// at column (col - n_split) with row stride ld1.  With trans != 0 the output is written
+// time-blocked instead (rows m are tokens, blocks of HYF_TBLK): element (m, f) lands at
+// out0[(m / HYF_TBLK) * ld0 + f * HYF_TBLK + m % HYF_TBLK] (f < n_split) or at the same place in
+// out1 with ld1 and f - n_split; ld0 and ld1 are then block strides.
 struct Epi {
   void* out0;
   int64_t ld0;
@@ -18,6 +21,7 @@ struct Epi {
   int32_t n_split;
   float* out1;
   int64_t ld1;
+  int32_t trans;
 };
 
 // Rows of the projection input: rows m < M1 come from X1 (row stride K), the rest from X2.
@@ -32,12 +36,13 @@ struct RowSrc {
 hipError_t launch_linear(int dtype, RowSrc x, int64_t M, int K, const void* W, int Nout,
                          const Epi& epi, hipStream_t s);
 
-// Memory scan over segments (see hyf_scan.hip).
+// Memory scan over segments (see hyf_scan.hip).  Inputs are time-blocked: element (feature f,
+// token t) of request i sits at [(blk0[i] + t / HYF_TBLK) * block_stride + f * HYF_TBLK + t % HYF_TBLK].
 struct ScanArgs {
-  const void* x;      // [rows][ld_x], head h at column h*P
-  const void* B;      // [rows][ld_b], group g at column g*N
-  const float* dt;    // [rows][ld_dt] raw step (before bias)
-  int64_t ld_x, ld_b, ld_dt;
+  const void* x;      // x, feature h*P + p
+  const void* B;      // B, feature g*N + n
+  const float* dt;    // raw step (before bias), feature h
+  int64_t xblk, bblk, dblk;  // block strides (elements) of x, B and dt
   const float* a_log;
   const float* dt_bias;
   char* state_pool;   // H of request i at state_pool + slot*st_bytes + st_h (if h_direct == null)
@@ -47,6 +52,10 @@ struct ScanArgs {
   int32_t chunks_per_seg;
   int32_t total_segs;
 };
+// Longest segment (tokens) one scan workgroup takes: its per-token weights live in LDS.
+int64_t scan_max_seg_tokens(const Shape& sh, int esz);
+// Scan workgroups per segment: heads x P-blocks x N-blocks.
+int64_t scan_items_per_seg(const Shape& sh);
 hipError_t launch_ssd_state(int dtype, const Shape& sh, const ScanArgs& a, const ReqTable& rt,
                             int32_t max_segs_per_req, hipStream_t s);
 
@@ -74,11 +83,12 @@ hipError_t launch_attention(int dtype, const Shape& sh, const RoundArgs& a, cons
 hipError_t launch_merge(int dtype, const Shape& sh, const RoundArgs& a, const ReqTable& rt,
                         hipStream_t s);
 
-// Prefill ring append: rows [row0[i] + max(0, n_i - W), row0[i+1]) of request i go to slots
-// (count + j) mod W, from k (row stride ld_k) and v (row stride ld_v), storage dtype.
+// Prefill ring append: the last m_i = min(n_i, W) rows of request i go to slots
+// (count + n_i - m_i + j) mod W.  k: token-major [sum m_i][ld_k] (the requests' last rows back to
+// back); v: time-blocked with block stride ld_v (feature h*P + p, token n_i - m_i + j).
 hipError_t launch_ring_append(int dtype, const Shape& sh, char* pool, const ReqTable& rt,
-                              const void* k, int64_t ld_k, int64_t k_row0, const void* v,
-                              int64_t ld_v, hipStream_t s);
+                              const void* k, int64_t ld_k, const void* vT, int64_t ld_v,
+                              hipStream_t s);
 // count += rows committed, per request (the last launch of a commit).
 hipError_t launch_bump_counts(char* pool, const Shape& sh, const ReqTable& rt, hipStream_t s);
 // Zero fill (a kernel, not a memset, so graph replays stay correct).

@@ -18,6 +18,19 @@ __device__ __forceinline__ typename Vec16<T>::type ld_vec(const T* p) {
 
 template <typename T>
 __device__ __forceinline__ void epi_store(const Epi& e, int64_t m, int f, float v) {
+  if (e.trans) {
+    const int64_t blk = m / HYF_TBLK, off = m % HYF_TBLK;
+    if (f < e.n_split) {
+      // out0: the tiled layout of the storage dtype (or plain [f][HYF_TBLK] for fp32 output)
+      if (e.out0_f32)
+        static_cast<float*>(e.out0)[blk * e.ld0 + (int64_t)f * HYF_TBLK + off] = v;
+      else
+        static_cast<T*>(e.out0)[blk * e.ld0 + tile_off<T>(f, (int)off)] = from_f32<T>(v);
+    } else {
+      e.out1[blk * e.ld1 + (int64_t)(f - e.n_split) * HYF_TBLK + off] = v;
+    }
+    return;
+  }
   if (f < e.n_split) {
     if (e.out0_f32)
       static_cast<float*>(e.out0)[m * e.ld0 + f] = v;
@@ -183,6 +196,46 @@ k_gemm_bf16(RowSrc xs, int M, int K, const bf16* __restrict__ W, int Nout, Epi e
     if (kt + 1 < nk) gemm_store_lds(lds[cur ^ 1][0], lds[cur ^ 1][1], ra, rb);
     __syncthreads();
   }
+  if (epi.trans) {
+    // Time-blocked output: the 128-row tile is one block (m0 is a multiple of 128).  Stage the fp32
+    // tile as [f][m] in LDS, then write 8 tokens of one feature per item: one 16-byte chunk of the
+    // tiled layout for out0 (consecutive items take consecutive features, so 16 of them fill a
+    // contiguous 256 bytes), two 16-byte runs of the plain [f][HYF_TBLK] rows for out1.
+    constexpr int CP = GB_M + 4;  // float pitch
+    float* ct = reinterpret_cast<float*>(&lds[0][0][0]);
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          ct[(wn * 64 + b * 16 + i) * CP + wm * 64 + a * 16 + 4 * g + r] = acc[a][b][r];
+    __syncthreads();
+    for (int it = threadIdx.x; it < GB_N * (GB_M / 8); it += 256) {
+      const int fl = it % GB_N, m8 = (it / GB_N) * 8;
+      const int f = n0 + fl;
+      const int64_t m = (int64_t)m0 + m8;
+      if (f >= Nout || m >= M) continue;
+      const float* src = ct + fl * CP + m8;
+      if (m + 8 <= M) {
+        const int64_t blk = m0 / GB_M;
+        if (f < epi.n_split && !epi.out0_f32) {
+          bf16x8 v;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = static_cast<bf16>(src[e]);
+          *reinterpret_cast<bf16x8*>(static_cast<bf16*>(epi.out0) + blk * epi.ld0 + tile_off<bf16>(f, m8)) = v;
+        } else {
+          float* dst = f < epi.n_split ? static_cast<float*>(epi.out0) + blk * epi.ld0 + (int64_t)f * GB_M + m8
+                                       : epi.out1 + blk * epi.ld1 + (int64_t)(f - epi.n_split) * GB_M + m8;
+          *reinterpret_cast<f32x4*>(dst) = f32x4{src[0], src[1], src[2], src[3]};
+          *reinterpret_cast<f32x4*>(dst + 4) = f32x4{src[4], src[5], src[6], src[7]};
+        }
+      } else {
+        for (int e = 0; m + e < M; ++e) epi_store<TO>(epi, m + e, f, src[e]);
+      }
+    }
+    return;
+  }
   // lane holds C[4g + r][i] of tile (a, b): row m, column f.
 #pragma unroll
   for (int a = 0; a < 4; ++a)
@@ -225,7 +278,7 @@ hipError_t launch_linear(int dtype, RowSrc x, int64_t M, int K, const void* W, i
                          hipStream_t s) {
   if (M <= 0 || Nout <= 0) return hipSuccess;
   if (dtype == HYF_BF16) {
-    if (M <= 64) return launch_small<bf16>(x, (int)M, K, static_cast<const bf16*>(W), Nout, epi, s);
+    if (M <= 64 && !epi.trans) return launch_small<bf16>(x, (int)M, K, static_cast<const bf16*>(W), Nout, epi, s);
     dim3 grid((Nout + GB_N - 1) / GB_N, (unsigned)((M + GB_M - 1) / GB_M));
     hipLaunchKernelGGL((k_gemm_bf16<bf16>), grid, dim3(256), 0, s, x, (int)M, K, static_cast<const bf16*>(W),
                        Nout, epi);

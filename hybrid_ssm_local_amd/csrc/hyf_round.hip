@@ -10,6 +10,8 @@
 //                  themselves), written as (max, sum, unnormalised output) partials.
 //  k_merge         per (request, head): merges the splits, adds mem, stores the output
 //                  projection's input, and advances the committed count.
+#include <mutex>
+
 #include "hyf_launch.h"
 
 namespace hyf {
@@ -261,15 +263,14 @@ __global__ void __launch_bounds__(256) k_merge(Shape sh, RoundArgs a, ReqTable r
 // ---------------------------------------------------------------------------------------------
 template <typename T>
 __global__ void __launch_bounds__(256) k_ring_append(Shape sh, char* pool, ReqTable rt, const T* __restrict__ k,
-                                                     int64_t ld_k, int64_t k_row0, const T* __restrict__ v,
-                                                     int64_t ld_v) {
+                                                     int64_t ld_k, const T* __restrict__ vT, int64_t ld_v) {
   const int nh = sh.nh, P = sh.P, W = sh.W;
   const int r = blockIdx.x / nh, h = blockIdx.x % nh;
   const int64_t n = rt.row0[r + 1] - rt.row0[r];
   if (n <= 0) return;
   const int64_t m = n < W ? n : W;
   // k rows of this request sit after those of the earlier requests (the last min(n, W) each)
-  int64_t krow = k_row0;
+  int64_t krow = 0;
   for (int q = 0; q < r; ++q) {
     const int64_t nq = rt.row0[q + 1] - rt.row0[q];
     krow += nq < W ? nq : W;
@@ -278,13 +279,13 @@ __global__ void __launch_bounds__(256) k_ring_append(Shape sh, char* pool, ReqTa
   const int64_t count = *count_ptr(pool, sh, slot);
   T* K = ring_ptr<T>(pool, sh, slot, sh.st_k, h);
   T* V = ring_ptr<T>(pool, sh, slot, sh.st_v, h);
-  const int64_t vrow = rt.row0[r] + n - m;
   for (int64_t idx = (int64_t)blockIdx.y * 256 + threadIdx.x; idx < m * P; idx += (int64_t)gridDim.y * 256) {
     const int64_t j = idx / P;
     const int pp = (int)(idx % P);
     const int64_t s = (count + n - m + j) % W;
+    const int64_t tok = n - m + j;  // token of the request in the time-blocked v
     K[s * P + pp] = k[(krow + j) * ld_k + h * P + pp];
-    V[s * P + pp] = v[(vrow + j) * ld_v + h * P + pp];
+    V[s * P + pp] = vT[(rt.blk0[r] + tok / HYF_TBLK) * ld_v + tile_off<T>(h * P + pp, (int)(tok % HYF_TBLK))];
   }
 }
 
@@ -326,12 +327,19 @@ hipError_t launch_attention(int dtype, const Shape& sh, const RoundArgs& a, cons
   const size_t lds = attn_lds_bytes(sh);
   if (lds > 65536) {
     // Above 64 KiB of dynamic LDS the kernel has to opt in (gfx950 has 160 KiB per workgroup).
-    hipError_t e = dtype == HYF_BF16
-                       ? hipFuncSetAttribute(reinterpret_cast<const void*>(k_attn<bf16>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)
-                       : hipFuncSetAttribute(reinterpret_cast<const void*>(k_attn<float>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
+    // Done once per process with the largest size any shape needs, so later calls (possibly under
+    // stream capture) launch only kernels.
+    static std::once_flag once;
+    static hipError_t set_err = hipSuccess;
+    std::call_once(once, [] {
+      const int mx = 160 * 1024;
+      set_err = hipFuncSetAttribute(reinterpret_cast<const void*>(k_attn<bf16>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, mx);
+      if (set_err == hipSuccess)
+        set_err = hipFuncSetAttribute(reinterpret_cast<const void*>(k_attn<float>),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, mx);
+    });
+    if (set_err != hipSuccess) return set_err;
   }
   if (dtype == HYF_BF16)
     hipLaunchKernelGGL(k_attn<bf16>, grid, dim3(256), lds, s, sh, a, rt);
@@ -350,15 +358,15 @@ hipError_t launch_merge(int dtype, const Shape& sh, const RoundArgs& a, const Re
 }
 
 hipError_t launch_ring_append(int dtype, const Shape& sh, char* pool, const ReqTable& rt, const void* k,
-                              int64_t ld_k, int64_t k_row0, const void* v, int64_t ld_v, hipStream_t s) {
+                              int64_t ld_k, const void* vT, int64_t ld_v, hipStream_t s) {
   const int64_t per = (int64_t)sh.W * sh.P;
   dim3 grid((unsigned)rt.n_req * sh.nh, (unsigned)((per + 255) / 256 < 16 ? (per + 255) / 256 : 16));
   if (dtype == HYF_BF16)
     hipLaunchKernelGGL(k_ring_append<bf16>, grid, dim3(256), 0, s, sh, pool, rt, static_cast<const bf16*>(k), ld_k,
-                       k_row0, static_cast<const bf16*>(v), ld_v);
+                       static_cast<const bf16*>(vT), ld_v);
   else
     hipLaunchKernelGGL(k_ring_append<float>, grid, dim3(256), 0, s, sh, pool, rt, static_cast<const float*>(k), ld_k,
-                       k_row0, static_cast<const float*>(v), ld_v);
+                       static_cast<const float*>(vT), ld_v);
   return hipGetLastError();
 }
 

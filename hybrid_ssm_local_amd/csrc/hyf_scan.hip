@@ -1,26 +1,43 @@
-// The recurrent memory's chunked scan (state-only), one request or many.
+// The recurrent memory's state-only commit scan, one request or many.
 //
 // Recurrence per head h (plain Mamba-2 / SSD with a scalar decay per head):
 //   H <- exp(dt_t * A) H + dt_t * x_t outer B_t,   dt_t = softplus(raw_t + dt_bias), A = -exp(A_log).
-// Chunked form: for chunk c with inclusive log-decay sums Lam inside the chunk,
-//   H_c = exp(Lam_end) H_{c-1} + sum_{t in c} dt_t exp(Lam_end - Lam_t) x_t outer B_t.
-// Only differences of log-decays are exponentiated, so deep decays underflow to 0 instead of 0/0.
+// Over a segment of tokens [t0, t1) this folds, exactly, into
+//   H_t1 = exp(Lam) H_t0 + sum_t dt_t exp(suf_t) x_t outer B_t,
+// where Lam is the segment's total log-decay and suf_t = sum_{t < tau < t1} dt_tau A is the suffix
+// log-decay after token t.  Only such sums of log-decays (differences, never ratios of
+// exponentials) are exponentiated, so deep decays underflow to 0 instead of becoming 0/0.
 //
-// Work split: the rows of each request are cut into segments of whole chunks.  One workgroup
-// (4 waves) owns one (segment, head, N-chunk); it walks its chunks in order with the state tile
-// in MFMA accumulators (fp32), rescaling by exp(Lam_end) once per chunk.  The chunk's sum over
-// tokens is an MFMA contraction over tokens: A = (dt*w*x)^T [P][tokens], B = B [tokens][N]; both
-// are staged transposed in LDS through 8x8 (bf16) or 4x4 (fp32) register transposes, so every
-// HBM read is a 16-byte, row-contiguous access.  Segment 0 starts from the request's H; if a
-// request has one segment its workgroups write H directly, otherwise k_ssd_combine folds the
-// segment states in order: H = P_0, then H = exp(lam_s) H + P_s.  No atomics: deterministic.
+// The sum over tokens is a per-head contraction (P x tokens) . (tokens x N) on MFMA, with a small
+// output (one head's state) and a long reduction: HBM-bound.  x and B come time-blocked and tiled
+// (tile_off): tokens in blocks of TB = 128, and inside a block each group of 16 features and run
+// of 4 VN tokens (VN = 16 bytes of elements) is one 1 KiB tile holding exactly the 16-byte chunks
+// the 64 lanes of one 16x16 MFMA supply, in lane order (16x16x32 bf16: eight k values per lane;
+// 16x16x4 fp32: four k values spread over four instructions, the same token order on both
+// operands).  So MFMA fragments load straight from global memory into registers with fully
+// contiguous 1 KiB wave loads: no LDS staging and no barriers in the main loop.  dt comes
+// time-blocked without tiles ([block][feature][TB]).
+//
+// Work split: each request's chunks are cut into segments (split-K over time); a workgroup owns
+// one (segment, head, P-block, N-block), sized so one wave holds the whole output block in
+// registers, and its four waves split the segment's tokens again (in 128-byte macro-steps, loads of
+// the next macro-step in flight while the current one multiplies).  The waves' partial states meet
+// in LDS in a fixed order.  Segment 0 starts from the request's H; a request with one segment
+// writes H directly, otherwise k_ssd_combine folds the segment states in order
+// (H = P_0, then H = exp(lam_s) H + P_s).  No atomics: the result is deterministic.
+#include <array>
+#include <mutex>
+#include <utility>
+
 #include "hyf_launch.h"
 
 namespace hyf {
 
-constexpr int SC_THREADS = 256;
-constexpr int SC_KB = 64;      // tokens staged per sub-block
-constexpr int SC_LMAX = 1024;  // largest chunk
+constexpr int SG_WAVES = 4;                 // waves per workgroup, one per SIMD
+constexpr int SG_THREADS = 64 * SG_WAVES;
+constexpr int SG_MAX_TILES = 40;            // 16x16 fp32 accumulator tiles per wave (160 registers)
+constexpr int SG_MAX_T16 = 8;               // at most 8 tiles along P or along N
+constexpr int TB = HYF_TBLK;                // tokens per block of the time-blocked layout
 
 template <typename T>
 __device__ __forceinline__ typename Vec16<T>::type ldv(const T* p) {
@@ -33,206 +50,280 @@ __device__ __forceinline__ int find_request(const ReqTable& rt, int q) {
   return r;
 }
 
-template <typename T, int PTM, int NTW>
-__global__ void __launch_bounds__(SC_THREADS)
-k_ssd_seg(Shape sh, ScanArgs a, ReqTable rt, int nch) {
-  constexpr int VN = Vec16<T>::n;
-  constexpr int KE = Mfma16<T>::KE;
-  constexpr int KSTEP = 4 * KE;
-  // LDS pitch in elements: rows stay 16-byte aligned and consecutive rows start 4 banks apart
-  // (36 dwords for bf16, 68 for fp32), so the 16 rows of one MFMA fragment read do not collide.
-  constexpr int LDP = SC_KB + 16 / (int)sizeof(T);
+template <typename T, int PB16, int NB16>
+__global__ void __launch_bounds__(SG_THREADS)
+k_ssd_seg(Shape sh, ScanArgs a, ReqTable rt, int npb, int nnb, int n_items, int per_xcd) {
   typedef typename Vec16<T>::type V;
-  typedef typename Mfma16<T>::frag Fr;
+  constexpr int VN = Vec16<T>::n;  // tokens per 16-byte lane load
+  constexpr int GT = 4 * VN;       // tokens per load group (four lane groups)
+  constexpr int MS = 2 * GT;       // tokens per macro-step: 128 bytes of every feature row
+  static_assert(PB16 * NB16 <= SG_MAX_TILES && PB16 <= SG_MAX_T16 && NB16 <= SG_MAX_T16, "tile budget");
 
-  __shared__ __attribute__((aligned(16))) T xs[PTM * 16 * LDP];
-  __shared__ __attribute__((aligned(16))) T bs[NTW * 4 * 16 * LDP];
-  __shared__ float wsh[SC_LMAX];
-  __shared__ float gtot[SC_LMAX / 64];
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  float* red = reinterpret_cast<float*>(smem);  // [64] pre-pass scratch
+  float* wt = red + 64;                         // [segment tokens] per-token weights
 
-  const int nh = sh.nh, P = sh.P, N = sh.N, L = sh.L;
-  const int h = blockIdx.x % nh;
-  const int q = blockIdx.x / nh;
-  const int nc = blockIdx.y;
-  const int n_base = nc * nch;
-  const int ncols = min(nch, N - n_base);
-  const int PT = P / 16, NTc = ncols / 16;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // block b runs on XCD b % 8: consecutive items (the blocks and heads of one segment) share an
+  // XCD, so its L2 serves the x rows of a head to all its N-blocks and B to all heads
+  const int item = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (item >= n_items) return;
+  const int nh = sh.nh, N = sh.N, P = sh.P;
+  const int nb = item % nnb;
+  const int pb = (item / nnb) % npb;
+  const int h = (item / (nnb * npb)) % nh;
+  const int q = item / (nnb * npb * nh);
+  const int p0 = pb * PB16 * 16, n0 = nb * NB16 * 16;
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int li = lane & 15, lg = lane >> 4;
-
   const int r = find_request(rt, q);
   const int ls = q - rt.seg0[r];
   const int nseg = rt.seg0[r + 1] - rt.seg0[r];
-  const int64_t row0 = rt.row0[r];
   const int Tr = rt.row0[r + 1] - rt.row0[r];
-  const int nchunk = (Tr + L - 1) / L;
-  const int c_begin = ls * a.chunks_per_seg;
-  const int c_end = min(c_begin + a.chunks_per_seg, nchunk);
+  const int seg_len = a.chunks_per_seg * sh.L;
+  const int s_begin = ls * seg_len;
+  const int len = min(s_begin + seg_len, Tr) - s_begin;
   const int grp = h / (nh / sh.G);
-
   const float A = -expf(a.a_log[h]);
   const float bias = a.dt_bias[h];
-  float* Hh = a.h_direct ? a.h_direct + (int64_t)h * P * N
-                         : reinterpret_cast<float*>(a.state_pool + (int64_t)rt.slot[r] * sh.st_bytes + sh.st_h) +
-                               (int64_t)h * P * N;
+  // token u of the segment sits in block blk0 + u / TB at offset u % TB (segments start on a
+  // block boundary)
+  const int64_t blk0 = rt.blk0[r] + s_begin / TB;
 
-  f32x4 acc[PTM][NTW];
+  // ---- pre-pass: the per-token weights dt_t exp(suf_t) into LDS.  Thread t owns the run of RUN
+  // consecutive tokens from t RUN (RUN = 4 run4 with run4 odd, so 16-byte LDS accesses of
+  // neighbouring threads fall in different banks).  Forward over the run: raw steps (in batches
+  // of 8 x 4 tokens, all loads of a batch in flight together) -> dt, kept in LDS, and the run's
+  // log-decay total.  A wave scan and a workgroup scan of the run totals give each run the
+  // log-decay of all later tokens; backward over the run, each token's weight replaces its dt.
+  // Tokens past the segment end (up to the end of its last macro-step) get dt = 0, weight 0.
+  const int wlen = (len + MS - 1) / MS * MS;
+  const int run4 = ((len + 4 * SG_THREADS - 1) / (4 * SG_THREADS)) | 1;
+  const int tk0 = t * 4 * run4;
+  float run_tot = 0.f;
+  for (int c0 = 0; c0 < run4; c0 += 8) {
+    f32x4 raw[8];
 #pragma unroll
-  for (int pt = 0; pt < PTM; ++pt)
+    for (int i = 0; i < 8; ++i) {
+      const int tk = min(tk0 + 4 * (c0 + i), (len - 1) & ~3);  // clamped: always a valid address
+      raw[i] = *reinterpret_cast<const f32x4*>(a.dt + (blk0 + tk / TB) * a.dblk + (int64_t)h * TB + tk % TB);
+    }
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-      acc[pt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int nt = wave + 4 * j;
-      if (ls == 0 && pt < PT && nt < NTc) {
+    for (int i = 0; i < 8; ++i) {
+      const int tk = tk0 + 4 * (c0 + i);
+      if (c0 + i < run4 && tk < wlen) {
+        f32x4 d;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          acc[pt][j][rr] = Hh[(int64_t)(pt * 16 + 4 * lg + rr) * N + n_base + nt * 16 + li];
+        for (int e = 0; e < 4; ++e) {
+          d[e] = tk + e < len ? softplus_f(raw[i][e] + bias) : 0.f;
+          run_tot += d[e] * A;
+        }
+        *reinterpret_cast<f32x4*>(wt + tk) = d;
       }
     }
-
+  }
+  // exclusive suffix over the runs: later lanes of this wave, then later waves
+  float inc = run_tot;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float v = __shfl_down(inc, o, 64);
+    if (lane + o < 64) inc += v;
+  }
+  if (lane == 0) red[wave] = inc;
+  __syncthreads();
+  float suf = __shfl_down(inc, 1, 64);
+  if (lane == 63) suf = 0.f;
   float lam_seg = 0.f;
-  for (int c = c_begin; c < c_end; ++c) {
-    const int ct0 = c * L;
-    const int clen = min(L, Tr - ct0);
-    // --- step, log-decay and in-chunk exclusive suffix sums -> weights w_t = dt_t exp(suffix)
-    const int ngroups = (clen + 63) / 64;
-    float ell[SC_LMAX / SC_THREADS], dtv[SC_LMAX / SC_THREADS], incl[SC_LMAX / SC_THREADS];
 #pragma unroll
-    for (int j = 0; j < SC_LMAX / SC_THREADS; ++j) {
-      const int t = j * SC_THREADS + threadIdx.x;
-      ell[j] = 0.f;
-      dtv[j] = 0.f;
-      if (t < clen) {
-        const float raw = a.dt[(row0 + ct0 + t) * a.ld_dt + h];
-        dtv[j] = softplus_f(raw + bias);
-        ell[j] = dtv[j] * A;
+  for (int w2 = 0; w2 < SG_WAVES; ++w2) {
+    if (w2 > wave) suf += red[w2];
+    lam_seg += red[w2];
+  }
+  for (int c = run4 - 1; c >= 0; --c) {
+    const int tk = tk0 + 4 * c;
+    if (tk < wlen) {
+      f32x4 d = *reinterpret_cast<const f32x4*>(wt + tk);
+#pragma unroll
+      for (int e = 3; e >= 0; --e) {
+        const float w = d[e] * expf(suf);
+        suf += d[e] * A;
+        d[e] = w;
       }
-      // inclusive suffix sum inside this wave's 64 tokens
-      float v = ell[j];
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const float u = __shfl_down(v, o, 64);
-        if (lane + o < 64) v += u;
-      }
-      incl[j] = v;
-      if (lane == 0 && j * SC_THREADS + wave * 64 < SC_LMAX) gtot[j * 4 + wave] = v;
-    }
-    __syncthreads();
-    float ctot = 0.f;
-    for (int gI = 0; gI < ngroups; ++gI) ctot += gtot[gI];
-#pragma unroll
-    for (int j = 0; j < SC_LMAX / SC_THREADS; ++j) {
-      const int t = j * SC_THREADS + threadIdx.x;
-      const int gI = j * 4 + wave;
-      float later = 0.f;
-      for (int g2 = gI + 1; g2 < ngroups; ++g2) later += gtot[g2];
-      float ex = __shfl_down(incl[j], 1, 64);
-      if (lane == 63) ex = 0.f;
-      if (t < clen) wsh[t] = dtv[j] * expf(ex + later);
-    }
-    lam_seg += ctot;
-    const float cdecay = expf(ctot);
-#pragma unroll
-    for (int pt = 0; pt < PTM; ++pt)
-#pragma unroll
-      for (int j = 0; j < NTW; ++j) acc[pt][j] *= cdecay;
-    __syncthreads();
-
-    // --- sub-blocks of SC_KB tokens: stage (w*x)^T and B^T, contract over tokens
-    for (int sb = 0; sb < clen; sb += SC_KB) {
-      const int xblocks = (SC_KB / VN) * (P / VN);
-      for (int blk = threadIdx.x; blk < xblocks; blk += SC_THREADS) {
-        const int tb = blk / (P / VN), pb = blk % (P / VN);
-        V vals[VN];
-#pragma unroll
-        for (int e = 0; e < VN; ++e) {
-          const int t = sb + tb * VN + e;
-          if (t < clen) {
-            const V raw = ldv<T>(static_cast<const T*>(a.x) + (row0 + ct0 + t) * a.ld_x + h * P + pb * VN);
-            const float w = wsh[t];
-#pragma unroll
-            for (int u = 0; u < VN; ++u) vals[e][u] = from_f32<T>(to_f32(raw[u]) * w);
-          } else {
-            vals[e] = V{};
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < VN; ++u) {
-          V o;
-#pragma unroll
-          for (int e = 0; e < VN; ++e) o[e] = vals[e][u];
-          *reinterpret_cast<V*>(&xs[(pb * VN + u) * LDP + tb * VN]) = o;
-        }
-      }
-      const int bblocks = (SC_KB / VN) * (ncols / VN);
-      for (int blk = threadIdx.x; blk < bblocks; blk += SC_THREADS) {
-        const int tb = blk / (ncols / VN), nb = blk % (ncols / VN);
-        V vals[VN];
-#pragma unroll
-        for (int e = 0; e < VN; ++e) {
-          const int t = sb + tb * VN + e;
-          vals[e] = t < clen ? ldv<T>(static_cast<const T*>(a.B) + (row0 + ct0 + t) * a.ld_b + grp * N + n_base +
-                                      nb * VN)
-                             : V{};
-        }
-#pragma unroll
-        for (int u = 0; u < VN; ++u) {
-          V o;
-#pragma unroll
-          for (int e = 0; e < VN; ++e) o[e] = vals[e][u];
-          *reinterpret_cast<V*>(&bs[(nb * VN + u) * LDP + tb * VN]) = o;
-        }
-      }
-      __syncthreads();
-#pragma unroll
-      for (int ks = 0; ks < SC_KB / KSTEP; ++ks) {
-        const int kk = ks * KSTEP + lg * KE;
-        Fr fb[NTW];
-#pragma unroll
-        for (int j = 0; j < NTW; ++j) {
-          const int nt = min(wave + 4 * j, max(NTc - 1, 0));
-          if constexpr (KE == 8)
-            fb[j] = *reinterpret_cast<const Fr*>(&bs[(nt * 16 + li) * LDP + kk]);
-          else
-            fb[j] = bs[(nt * 16 + li) * LDP + kk];
-        }
-#pragma unroll
-        for (int pt = 0; pt < PTM; ++pt) {
-          if (pt < PT) {
-            Fr fa;
-            if constexpr (KE == 8)
-              fa = *reinterpret_cast<const Fr*>(&xs[(pt * 16 + li) * LDP + kk]);
-            else
-              fa = xs[(pt * 16 + li) * LDP + kk];
-#pragma unroll
-            for (int j = 0; j < NTW; ++j) acc[pt][j] = Mfma16<T>::mma(fa, fb[j], acc[pt][j]);
-          }
-        }
-      }
-      __syncthreads();
+      *reinterpret_cast<f32x4*>(wt + tk) = d;
     }
   }
 
-  // --- write the state (single segment) or the segment partial
+  // ---- accumulators.  Tile (pt, nt), lane (li, lg), register rr holds state row
+  // p0 + 16 pt + 4 lg + rr, column n0 + 16 nt + li (the MFMA output layout).  The request's first
+  // segment starts from exp(lam_seg) H: this workgroup's block of H is staged in LDS behind the
+  // weights (16-byte loads by every thread, row pitch RP) and wave 0 starts from it; every other
+  // accumulator starts at 0.
+  constexpr int PB = PB16 * 16, NB = NB16 * 16, RP = NB + 4;
+  float* Hh = a.h_direct ? a.h_direct + (int64_t)h * P * N
+                         : reinterpret_cast<float*>(a.state_pool + (int64_t)rt.slot[r] * sh.st_bytes + sh.st_h) +
+                               (int64_t)h * P * N;
+  float* hs = wt + (seg_len + MS - 1) / MS * MS;
+  if (ls == 0) {
+    for (int idx = t; idx < PB * NB / 4; idx += SG_THREADS) {
+      const int p = idx / (NB / 4), n = (idx % (NB / 4)) * 4;
+      *reinterpret_cast<f32x4*>(hs + p * RP + n) = *reinterpret_cast<const f32x4*>(Hh + (int64_t)(p0 + p) * N + n0 + n);
+    }
+  }
+  __syncthreads();  // weights (and the staged H) complete
+  f32x4 acc[PB16][NB16];
+#pragma unroll
+  for (int pt = 0; pt < PB16; ++pt)
+#pragma unroll
+    for (int nt = 0; nt < NB16; ++nt) acc[pt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (ls == 0 && wave == 0) {
+    const float d0 = expf(lam_seg);
+#pragma unroll
+    for (int pt = 0; pt < PB16; ++pt)
+#pragma unroll
+      for (int nt = 0; nt < NB16; ++nt)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) acc[pt][nt][rr] = d0 * hs[(pt * 16 + 4 * lg + rr) * RP + nt * 16 + li];
+  }
+
+  // ---- operand loads.  With the tiled layout the 16-byte chunk lane l brings for an MFMA sits at
+  // byte 16 l of a 1 KiB tile, so a load is a scalar base (the segment's first block, in a buffer
+  // resource), a scalar offset (block, feature group, token run) and the lane offset 16 l.  The
+  // segment's blocks span less than 2 GiB, so every offset fits in 32 bits; the resource's size
+  // also turns any read past the segment's last block into zeros.
+  constexpr int NJ = TB / GT;  // token runs (tiles) per feature group and block
+  const int nblk_seg = (len + TB - 1) / TB;
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T*>(static_cast<const T*>(a.x) + blk0 * a.xblk), 0, (int)(nblk_seg * a.xblk * sizeof(T)), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T*>(static_cast<const T*>(a.B) + blk0 * a.bblk), 0, (int)(nblk_seg * a.bblk * sizeof(T)), 0x00020000);
+  const int fga = (h * P + p0) / 16, fgb = (grp * N + n0) / 16;  // first feature group of x, B
+  const int loff = lane * 16;
+  auto load = [&](V (&fa)[PB16][2], V (&fb)[NB16][2], int m) __attribute__((always_inline)) {
+    const int u = m * MS;
+    const int j0 = (u % TB) / GT;
+    const int sx = (int)(((u / TB) * a.xblk + ((int64_t)fga * NJ + j0) * 64 * VN) * sizeof(T));
+    const int sb = (int)(((u / TB) * a.bblk + ((int64_t)fgb * NJ + j0) * 64 * VN) * sizeof(T));
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+#pragma unroll
+      for (int pt = 0; pt < PB16; ++pt)
+        fa[pt][g] = __builtin_bit_cast(
+            V, __builtin_amdgcn_raw_buffer_load_b128(rx, loff, sx + (pt * NJ + g) * 1024, 0));
+#pragma unroll
+      for (int nt = 0; nt < NB16; ++nt)
+        fb[nt][g] = __builtin_bit_cast(
+            V, __builtin_amdgcn_raw_buffer_load_b128(rb, loff, sb + (nt * NJ + g) * 1024, 0));
+    }
+  };
+
+  // ---- main loop.  Wave w takes macro-steps [w M / 4, (w + 1) M / 4) of the segment.  In a
+  // macro-step, for load group g = 0, 1, lane (li, lg) holds the VN tokens
+  // u + g GT + lg VN .. + VN - 1 of x row p0 + 16 pt + li (every pt) and of B row n0 + 16 nt + li
+  // (every nt); x is scaled by the tokens' weights and the pair enters the MFMAs.
+  const int M = wlen / MS;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // uniform: keeps offsets scalar
+  const int m_lo = wave_u * M / SG_WAVES, m_hi = (wave_u + 1) * M / SG_WAVES;
+  auto compute = [&](V (&fa)[PB16][2], V (&fb)[NB16][2], int m) __attribute__((always_inline)) {
+    const int u = m * MS;
+    const bool tail = u + MS > len;  // the segment's last macro-step: mask tokens past its end
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int tb = u + g * GT + lg * VN;  // first token of this lane's VN tokens
+      float w[VN];
+#pragma unroll
+      for (int e4 = 0; e4 < VN; e4 += 4) {
+        const f32x4 w4 = *reinterpret_cast<const f32x4*>(wt + tb + e4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e4 + e] = w4[e];
+      }
+      V sa[PB16];
+#pragma unroll
+      for (int pt = 0; pt < PB16; ++pt)
+#pragma unroll
+        for (int e = 0; e < VN; ++e) sa[pt][e] = from_f32<T>(to_f32(fa[pt][g][e]) * w[e]);
+      if (tail) {
+        // the inputs past the end hold anything (NaN included): zero both operands there
+#pragma unroll
+        for (int e = 0; e < VN; ++e) {
+          if (tb + e >= len) {
+#pragma unroll
+            for (int pt = 0; pt < PB16; ++pt) sa[pt][e] = from_f32<T>(0.f);
+#pragma unroll
+            for (int nt = 0; nt < NB16; ++nt) fb[nt][g][e] = from_f32<T>(0.f);
+          }
+        }
+      }
+      if constexpr (VN == 8) {
+#pragma unroll
+        for (int pt = 0; pt < PB16; ++pt)
+#pragma unroll
+          for (int nt = 0; nt < NB16; ++nt) acc[pt][nt] = Mfma16<T>::mma(sa[pt], fb[nt][g], acc[pt][nt]);
+      } else {
+        // fp32: k index lg of instruction j is token tb + j on both operands
+#pragma unroll
+        for (int j = 0; j < VN; ++j)
+#pragma unroll
+          for (int pt = 0; pt < PB16; ++pt)
+#pragma unroll
+            for (int nt = 0; nt < NB16; ++nt) acc[pt][nt] = Mfma16<T>::mma(sa[pt][j], fb[nt][g][j], acc[pt][nt]);
+      }
+    }
+  };
+
+  if (m_lo < m_hi) {
+    V fa0[PB16][2], fb0[NB16][2], fa1[PB16][2], fb1[NB16][2];
+    load(fa0, fb0, m_lo);
+    for (int m = m_lo; m < m_hi; m += 2) {
+      // the next macro-step's loads go out before this one's MFMAs (a clamped index repeats the
+      // last macro-step's loads at the end instead of branching around them)
+      load(fa1, fb1, min(m + 1, m_hi - 1));
+      compute(fa0, fb0, m);
+      if (m + 1 >= m_hi) break;
+      load(fa0, fb0, min(m + 2, m_hi - 1));
+      compute(fa1, fb1, m + 1);
+    }
+  }
+
+  // ---- the four waves' states meet in LDS (weights and staged H are dead now), row-major with
+  // row pitch RP (the 4 row groups of a tile land in different banks): (w0 + w2) + (w1 + w3),
+  // written as 16-byte runs by all threads.
+  __syncthreads();
+  float* slot = reinterpret_cast<float*>(smem);
+  auto put = [&](int sl) __attribute__((always_inline)) {
+#pragma unroll
+    for (int pt = 0; pt < PB16; ++pt)
+#pragma unroll
+      for (int nt = 0; nt < NB16; ++nt)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) slot[(sl * PB + pt * 16 + 4 * lg + rr) * RP + nt * 16 + li] = acc[pt][nt][rr];
+  };
+  auto add = [&](int sl) __attribute__((always_inline)) {
+#pragma unroll
+    for (int pt = 0; pt < PB16; ++pt)
+#pragma unroll
+      for (int nt = 0; nt < NB16; ++nt)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) acc[pt][nt][rr] += slot[(sl * PB + pt * 16 + 4 * lg + rr) * RP + nt * 16 + li];
+  };
+  if (wave >= 2) put(wave - 2);
+  __syncthreads();
+  if (wave < 2) add(wave);
+  __syncthreads();
+  if (wave < 2) put(wave);
+  __syncthreads();
+
   float* dst;
-  int64_t dst_ld = N;
   if (nseg == 1) {
     dst = Hh;
   } else {
     dst = a.part + ((int64_t)q * nh + h) * P * N;
-    if (nc == 0 && threadIdx.x == 0) a.lam[(int64_t)q * nh + h] = lam_seg;
+    if (pb == 0 && nb == 0 && t == 0) a.lam[(int64_t)q * nh + h] = lam_seg;
   }
-#pragma unroll
-  for (int pt = 0; pt < PTM; ++pt)
-#pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-      const int nt = wave + 4 * j;
-      if (pt < PT && nt < NTc) {
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          dst[(int64_t)(pt * 16 + 4 * lg + rr) * dst_ld + n_base + nt * 16 + li] = acc[pt][j][rr];
-      }
-    }
+  for (int idx = t; idx < PB * NB / 4; idx += SG_THREADS) {
+    const int p = idx / (NB / 4), n = (idx % (NB / 4)) * 4;
+    const f32x4 v = *reinterpret_cast<const f32x4*>(slot + p * RP + n) + *reinterpret_cast<const f32x4*>(slot + (PB + p) * RP + n);
+    *reinterpret_cast<f32x4*>(dst + (int64_t)(p0 + p) * N + n0 + n) = v;
+  }
 }
 
 // Folds the segment states of requests with more than one segment, in segment order.
@@ -256,20 +347,91 @@ __global__ void __launch_bounds__(256) k_ssd_combine(Shape sh, ScanArgs a, ReqTa
   *reinterpret_cast<f32x4*>(Hh + e) = acc;
 }
 
+// Workgroup geometry: an output block of PB16 x NB16 tiles of 16 x 16, the largest divisors of
+// P / 16 and N / 16 (N first) that keep both at most 8 and the block within SG_MAX_TILES.
+struct SegGeo {
+  int pb16, nb16, npb, nnb;
+};
+static SegGeo seg_geo(const Shape& sh) {
+  const int P16 = sh.P / 16, N16 = sh.N / 16;
+  int nb16 = 1, pb16 = 1;
+  for (int d = 1; d <= SG_MAX_T16; ++d)
+    if (N16 % d == 0) nb16 = d;
+  for (int d = 1; d <= SG_MAX_T16; ++d)
+    if (P16 % d == 0 && d * nb16 <= SG_MAX_TILES) pb16 = d;
+  return {pb16, nb16, P16 / pb16, N16 / nb16};
+}
+
+int64_t scan_items_per_seg(const Shape& sh) {
+  const SegGeo g = seg_geo(sh);
+  return (int64_t)sh.nh * g.npb * g.nnb;
+}
+
+// LDS of one workgroup: the pre-pass scratch, one weight per token (whole macro-steps) and a
+// staged block of H (row pitch NB + 4); afterwards two row-major accumulator blocks.
+static size_t scan_acc_block_bytes(const Shape& sh) {
+  const SegGeo g = seg_geo(sh);
+  return sizeof(float) * (16 * g.pb16) * (16 * g.nb16 + 4);
+}
+static size_t scan_lds_bytes(const Shape& sh, int esz, int64_t seg_tokens) {
+  const int64_t ms = 128 / esz;
+  const size_t main_bytes = sizeof(float) * (64 + (seg_tokens + ms - 1) / ms * ms) + scan_acc_block_bytes(sh);
+  const size_t red_bytes = 2 * scan_acc_block_bytes(sh);
+  return main_bytes > red_bytes ? main_bytes : red_bytes;
+}
+
+// Longest segment: its weights fit in LDS next to the staged H, and its blocks span less than
+// 2 GiB of the widest time-blocked tensor a caller passes (x and B in one buffer: nh P + G N
+// feature rows), so buffer offsets stay 32-bit.
+int64_t scan_max_seg_tokens(const Shape& sh, int esz) {
+  const int64_t lds_cap = ((int64_t)160 * 1024 - 64 * 4 - (int64_t)scan_acc_block_bytes(sh)) / 4 / TB * TB;
+  const int64_t blk_bytes = (int64_t)(sh.dq + sh.gn) * TB * esz;
+  int64_t off_cap = (int64_t)0x7fffffff / blk_bytes * TB;
+  if (off_cap < TB) off_cap = TB;
+  return off_cap < lds_cap ? off_cap : lds_cap;
+}
+
+typedef hipError_t (*SegLaunch)(const Shape&, const ScanArgs&, const ReqTable&, hipStream_t);
+
+template <typename T, int PB16, int NB16>
+static hipError_t launch_seg_t(const Shape& sh, const ScanArgs& a, const ReqTable& rt, hipStream_t s) {
+  const SegGeo g = seg_geo(sh);
+  const int n_items = (int)(a.total_segs * scan_items_per_seg(sh));
+  const int per_xcd = (n_items + 7) / 8;
+  const size_t lds = scan_lds_bytes(sh, sizeof(T), (int64_t)a.chunks_per_seg * sh.L);
+  static std::once_flag once;
+  static hipError_t set_err = hipSuccess;
+  std::call_once(once, [] {
+    set_err = hipFuncSetAttribute(reinterpret_cast<const void*>(k_ssd_seg<T, PB16, NB16>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  });
+  if (set_err != hipSuccess) return set_err;
+  hipLaunchKernelGGL((k_ssd_seg<T, PB16, NB16>), dim3(8 * per_xcd), dim3(SG_THREADS), lds, s, sh, a, rt, g.npb,
+                     g.nnb, n_items, per_xcd);
+  return hipGetLastError();
+}
+
+// One instantiation per (PB16, NB16) pair within the tile budget; entry (pb16 - 1) * 8 + nb16 - 1.
+template <typename T, int I>
+constexpr SegLaunch seg_entry() {
+  constexpr int pb = I / SG_MAX_T16 + 1, nb = I % SG_MAX_T16 + 1;
+  if constexpr (pb * nb <= SG_MAX_TILES)
+    return &launch_seg_t<T, pb, nb>;
+  else
+    return nullptr;
+}
+template <typename T, size_t... I>
+constexpr std::array<SegLaunch, sizeof...(I)> seg_table(std::index_sequence<I...>) {
+  return {seg_entry<T, (int)I>()...};
+}
+
 template <typename T>
 static hipError_t launch_seg(const Shape& sh, const ScanArgs& a, const ReqTable& rt, hipStream_t s) {
-  const int PT = sh.P / 16;
-  // N-chunk per workgroup: 4 waves x NTW tiles of 16 columns.
-  if (PT <= 8) {
-    const int nch = sh.N < 128 ? sh.N : 128;
-    dim3 grid((unsigned)a.total_segs * sh.nh, (sh.N + nch - 1) / nch);
-    hipLaunchKernelGGL((k_ssd_seg<T, 8, 2>), grid, dim3(SC_THREADS), 0, s, sh, a, rt, nch);
-  } else {
-    const int nch = sh.N < 64 ? sh.N : 64;
-    dim3 grid((unsigned)a.total_segs * sh.nh, (sh.N + nch - 1) / nch);
-    hipLaunchKernelGGL((k_ssd_seg<T, 16, 1>), grid, dim3(SC_THREADS), 0, s, sh, a, rt, nch);
-  }
-  return hipGetLastError();
+  static constexpr std::array<SegLaunch, SG_MAX_T16 * SG_MAX_T16> table =
+      seg_table<T>(std::make_index_sequence<SG_MAX_T16 * SG_MAX_T16>());
+  const SegGeo g = seg_geo(sh);
+  const SegLaunch f = table[(g.pb16 - 1) * SG_MAX_T16 + g.nb16 - 1];
+  return f ? f(sh, a, rt, s) : hipErrorInvalidValue;
 }
 
 hipError_t launch_ssd_state(int dtype, const Shape& sh, const ScanArgs& a, const ReqTable& rt,

@@ -64,6 +64,7 @@ _SIGS = {
                                          _vp, _sz, _vp]),
     "hyf_draft_block": (ctypes.c_int, [_P(HyfConfig), _P(HyfWeights), _vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp,
                                        _vp, _sz, _vp]),
+    "hyf_linear": (ctypes.c_int, [_P(HyfConfig), _vp, _i64, _i32, _vp, _i32, _vp, _i32, _vp]),
     "hyf_ssd_scan": (ctypes.c_int, [_P(HyfConfig), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _sz,
                                     _vp]),
 }
@@ -192,6 +193,10 @@ def hyf_draft_block(cfg, w: HyfWeights, pool, pool_slots, slots, n_req, commit_f
                                  _stream(stream))
 
 
+def hyf_linear(cfg, X, M, K, W, Nout, out, out_f32, stream=None) -> int:
+    return lib().hyf_linear(ctypes.byref(cfg), _ptr(X), M, K, _ptr(W), Nout, _ptr(out), out_f32, _stream(stream))
+
+
 def hyf_ssd_scan(cfg, x, B, C, dt_raw, a_log, dt_bias, d_skip, H, y, T, ws, ws_bytes, stream=None) -> int:
     return lib().hyf_ssd_scan(ctypes.byref(cfg), _ptr(x), _ptr(B), _ptr(C), _ptr(dt_raw), _ptr(a_log),
                               _ptr(dt_bias), _ptr(d_skip), _ptr(H), _ptr(y), T, _ptr(ws), ws_bytes,
@@ -199,6 +204,42 @@ def hyf_ssd_scan(cfg, x, B, C, dt_raw, a_log, dt_bias, d_skip, H, y, T, ws, ws_b
 
 
 # ------------------------------------------------------------------ device-memory owner
+
+
+HYF_TBLK = 128
+
+
+def time_blocked(a, T: int, pad=0.0) -> np.ndarray:
+    """[T][features...] -> [ceil(T/HYF_TBLK)][F][HYF_TBLK], the layout hyf_ssd_scan reads.
+
+    Tokens past T in the last block are filled with `pad`."""
+    f = np.asarray(a, np.float32).reshape(T, -1)
+    F = f.shape[1]
+    nb = (T + HYF_TBLK - 1) // HYF_TBLK
+    out = np.full((nb * HYF_TBLK, F), pad, dtype=np.float32)
+    out[:T] = f
+    return np.ascontiguousarray(out.reshape(nb, HYF_TBLK, F).transpose(0, 2, 1))
+
+
+def time_tiled(a, T: int, elem_bytes: int, pad=0.0) -> np.ndarray:
+    """[T][F] -> the tiled time-blocked layout hyf_ssd_scan reads for x and B (F a multiple of 16).
+
+    Blocks of HYF_TBLK tokens; inside a block, feature f and token t sit at element
+    (((f // 16) * NJ + t // KT) * 64 + ((t % KT) // VN) * 16 + f % 16) * VN + t % VN, with
+    VN = 16 // elem_bytes and KT = 4 * VN, NJ = HYF_TBLK // KT.  Returned as [blocks][F][HYF_TBLK]
+    (the same size as time_blocked; only the order inside a block differs)."""
+    blk = time_blocked(a, T, pad)
+    nb, F, _ = blk.shape
+    if F % 16:
+        raise ValueError("tiled layout needs a multiple of 16 features")
+    vn = 16 // elem_bytes
+    kt = 4 * vn
+    t = blk.reshape(nb, F // 16, 16, HYF_TBLK // kt, 4, vn).transpose(0, 1, 3, 4, 2, 5)
+    return np.ascontiguousarray(t).reshape(nb, F, HYF_TBLK)
+
+
+def elem_bytes(shape: LayerShape) -> int:
+    return 2 if shape.dtype == BF16 else 4
 
 
 def torch_dtype(shape: LayerShape):

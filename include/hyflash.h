@@ -42,6 +42,8 @@ extern "C" {
 #define HYF_MAX_REQUESTS 128
 /* Rows of the draft block: anchor + seven draft positions (explainer, "Jargon"). */
 #define HYF_BLOCK 8
+/* Tokens per block of the time-blocked layout hyf_ssd_scan reads (see there). */
+#define HYF_TBLK 128
 
 typedef enum {
   HYF_OK = 0,
@@ -66,7 +68,7 @@ typedef struct {
   int32_t n_groups;   /* G: B and C are shared by nh/G heads each; must divide nh       */
   int32_t window;     /* W: ring capacity in committed rows (1..8192)                   */
   int32_t block;      /* must be HYF_BLOCK                                             */
-  int32_t chunk;      /* SSD chunk length L (16..1024, multiple of 16)                  */
+  int32_t chunk;      /* SSD chunk length L: a power of two, 16..1024                   */
   int32_t dtype;      /* hyf_dtype                                                      */
   int32_t memory;     /* hyf_memory; only HYF_MEM_MAMBA2 is implemented                 */
   int32_t cross_slot; /* 1: block rows attend to each other; 0: each only to itself     */
@@ -155,17 +157,38 @@ int hyf_draft_block(const hyf_config* cfg, const hyf_weights* w, void* state_poo
                     const void* commit_feats, const int64_t* cu_commit, const void* block_in,
                     void* block_out, void* ws, size_t ws_bytes, void* stream);
 
+/* The projection building block of the layer (explainer, "That is HyFlash": each layer
+ * projects committed features and block rows; the draft step ends in an output projection):
+ *   out[m][f] = sum_k X[m][k] * W[f][k]      m < M, f < Nout
+ * X [M][K] and W [Nout][K] (nn.Linear layout) in the storage dtype, 16-byte aligned, K a
+ * multiple of 8; out [M][Nout] is fp32 when out_f32 != 0, else the storage dtype.  It runs the
+ * same kernels, with the same launch shapes, as hyf_draft_block and hyf_memory_commit do for
+ * the same M and K (a weight-streaming kernel up to 64 rows, a tiled MFMA GEMM above). */
+int hyf_linear(const hyf_config* cfg, const void* X, int64_t M, int32_t K, const void* W,
+               int32_t Nout, void* out, int32_t out_f32, void* stream);
+
 /* Host only.  Workspace bytes hyf_ssd_scan needs for T tokens. */
 size_t hyf_ssd_scan_workspace_bytes(const hyf_config* cfg, int64_t T);
 
-/* The memory's chunked scan on pre-projected inputs, one request (explainer "Jargon":
- * Mamba-2 folds each input into a fixed-size state with an input-dependent step size and a
- * learned decay).  For t = 0..T-1, per head h:
- *   dt = softplus(dt_raw[t][h] + dt_bias[h]);  H_h <- exp(dt * A_h) H_h + dt * x[t][h] outer B[t][g(h)]
- *   y[t][h] = H_h . C[t][g(h)] + d_skip[h] * x[t][h]           (only if y_opt)
- * x [T][nh][P], B and C_opt [T][G*N] storage dtype; dt_raw [T][nh] fp32;
+/* The memory's scan on pre-projected inputs, one request (explainer "Jargon": Mamba-2 folds
+ * each input into a fixed-size state with an input-dependent step size and a learned decay).
+ * For t = 0..T-1, per head h (g(h) = h / (nh/G)):
+ *   dt = softplus(dt_raw(h,t) + dt_bias[h]);  H_h <- exp(dt * A_h) H_h + dt * x(h,t) outer B(g(h),t)
+ *   y[t][h] = H_h . C(g(h),t) + d_skip[h] * x(h,t)              (only if y_opt)
+ * Inputs are time-blocked: tokens come in blocks of HYF_TBLK; a tensor of F features holds
+ * ceil(T / HYF_TBLK) blocks of F * HYF_TBLK elements, block b holding tokens b*HYF_TBLK .. +127.
+ *   dt_raw F = nh    fp32, plain: feature f of token t at (t / HYF_TBLK) * F * HYF_TBLK +
+ *                    f * HYF_TBLK + t % HYF_TBLK;
+ *   x      F = nh*P  storage dtype, feature h*P + p, tiled;
+ *   B, C   F = G*N   storage dtype, feature g*N + n, tiled (C_opt is required iff y_opt is given).
+ * Tiled (the operand order of the 16x16 MFMAs that consume it): with VN = 16 / sizeof(element)
+ * (8 bf16, 4 fp32), KT = 4*VN and NJ = HYF_TBLK / KT, feature f of token t sits in its block at
+ *   (((f / 16) * NJ + (t % HYF_TBLK) / KT) * 64 + ((t % KT) / VN) * 16 + f % 16) * VN + t % VN,
+ * i.e. each group of 16 features and run of KT tokens is one contiguous 1 KiB tile.
+ * Entries of the last block past T are never read into the result (they may hold anything).
+ * x, B and dt_raw 16-byte aligned.
  * H_inout [nh][P][N] fp32 holds the initial state on entry and the final state on exit.
- * C_opt is required iff y_opt is given.  T = 0 is a no-op. */
+ * y_opt [T][nh][P] storage dtype.  T = 0 is a no-op. */
 int hyf_ssd_scan(const hyf_config* cfg, const void* x, const void* B, const void* C_opt,
                  const float* dt_raw, const float* a_log, const float* dt_bias,
                  const float* d_skip, float* H_inout, void* y_opt, int64_t T, void* ws,

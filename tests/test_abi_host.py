@@ -5,6 +5,8 @@ or is a pure host query)."""
 import ctypes
 import subprocess
 
+import numpy as np
+
 import pytest
 
 from hybrid_ssm_local_amd import hyflash as hf
@@ -40,7 +42,7 @@ def test_named_shapes_are_accepted(shape):
 @pytest.mark.parametrize("field,value,status", [
     ("head_dim", 72, hf.HYF_ESHAPE), ("head_dim", 0, hf.HYF_ESHAPE), ("d_state", 300, hf.HYF_ESHAPE),
     ("n_groups", 3, hf.HYF_ESHAPE), ("window", 0, hf.HYF_ESHAPE), ("block", 7, hf.HYF_ESHAPE),
-    ("chunk", 8, hf.HYF_ESHAPE), ("dtype", 5, hf.HYF_EDTYPE), ("memory", hf.HYF_MEM_GDN, hf.HYF_EUNSUPPORTED),
+    ("chunk", 8, hf.HYF_ESHAPE), ("chunk", 48, hf.HYF_ESHAPE), ("dtype", 5, hf.HYF_EDTYPE), ("memory", hf.HYF_MEM_GDN, hf.HYF_EUNSUPPORTED),
     ("cross_slot", 2, hf.HYF_EINVAL), ("reserved", 1, hf.HYF_EINVAL), ("d_model", 100, hf.HYF_ESHAPE),
 ])
 def test_bad_configs_are_rejected(field, value, status):
@@ -110,6 +112,9 @@ def test_invalid_calls_fail_before_any_device_work():
         hf.HYF_EINVAL
     assert hf.hyf_ssd_scan(cfg, fake, fake, None, fake, fake, fake, fake, fake, None, -1, fake, 1 << 30, 0) == \
         hf.HYF_ECAPACITY
+    # misaligned operand
+    assert hf.hyf_ssd_scan(cfg, fake + 4, fake, None, fake, fake, fake, fake, fake, None, 10, fake, 1 << 30, 0) == \
+        hf.HYF_EINVAL
 
 
 def test_empty_commit_is_accepted_without_device_work():
@@ -123,3 +128,19 @@ def test_empty_commit_is_accepted_without_device_work():
 def test_status_strings():
     assert hf.status_str(hf.HYF_OK) == "ok"
     assert "workspace" in hf.status_str(hf.HYF_EWORKSPACE)
+
+
+@pytest.mark.parametrize("elem_bytes", [2, 4])
+def test_time_tiled_layout_places_each_element_as_documented(elem_bytes):
+    # the header's formula, element by element, on a ragged length
+    T, F = 300, 48
+    a = np.arange(T * F, dtype=np.float64).reshape(T, F)
+    out = hf.time_tiled(a, T, elem_bytes, pad=-1.0).reshape(-1)
+    vn = 16 // elem_bytes
+    kt, nj = 4 * vn, hf.HYF_TBLK // (4 * vn)
+    for t in range(0, T, 7):
+        for f in range(0, F, 5):
+            tt = t % hf.HYF_TBLK
+            off = (((f // 16) * nj + tt // kt) * 64 + ((tt % kt) // vn) * 16 + f % 16) * vn + tt % vn
+            assert out[(t // hf.HYF_TBLK) * F * hf.HYF_TBLK + off] == a[t, f]
+    assert out.size == 3 * F * hf.HYF_TBLK and (out == -1.0).sum() == (3 * hf.HYF_TBLK - T) * F

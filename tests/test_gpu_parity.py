@@ -47,10 +47,11 @@ def small_shape(dtype, **kw):
 
 
 def run_scan(shape, sc, T):
+    # Tokens past T in the last time block hold NaN: none may reach the state.
     cfg = hf.make_config(shape)
-    x = hf.to_device(sc["x"], shape)
-    B = hf.to_device(sc["B"], shape)
-    dt = torch.from_numpy(sc["dt_raw"]).to(DEV)
+    x = hf.to_device(hf.time_tiled(sc["x"], T, hf.elem_bytes(shape), np.nan), shape)
+    B = hf.to_device(hf.time_tiled(sc["B"], T, hf.elem_bytes(shape), np.nan), shape)
+    dt = torch.from_numpy(hf.time_blocked(sc["dt_raw"], T, np.nan)).to(DEV)
     a_log = torch.from_numpy(sc["a_log"]).to(DEV)
     dt_bias = torch.from_numpy(sc["dt_bias"]).to(DEV)
     d_skip = torch.from_numpy(sc["d_skip"]).to(DEV)
@@ -67,7 +68,7 @@ SCAN_CASES = [
     ("qwen_bf16", I.QWEN, [7, 64, 129, 1000]),
     ("phi4_bf16_L256", I.PHI4_LONG, [255, 700]),
     ("odd_bf16", small_shape("bf16", n_heads=3, head_dim=48, d_state=80, n_groups=3, chunk=32), [1, 100]),
-    ("odd_fp32", small_shape("f32", n_heads=6, head_dim=32, d_state=48, n_groups=2, chunk=16), [37, 200]),
+    ("odd_fp32", small_shape("f32", n_heads=6, head_dim=32, d_state=48, n_groups=2, chunk=32), [37, 200]),
 ]
 
 
@@ -335,3 +336,48 @@ def test_round_is_deterministic():
         torch.cuda.synchronize()
         outs.append((bo.clone(), pr.gpu.state()["blob"].clone()))
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def test_graph_replay_matches_eager():
+    # A captured episode (reset, prefill, 4 rounds) replayed several times, with eager work and
+    # synchronizations in between, reproduces the eager outputs and state bit for bit.
+    shape = small_shape("bf16", window=40)
+    pr = Pair(shape, seed=101, max_rows=300)
+    L = pr.gpu
+    feats = hf.to_device(pr.rows(300), shape)
+    rounds = [(hf.to_device(pr.rows(a), shape), [0, a], hf.to_device(pr.rows(8, 3), shape)) for a in (3, 8, 1, 5)]
+    outs = [torch.empty_like(r[2]) for r in rounds]
+
+    def episode(stream):
+        hf.check(hf.hyf_state_reset(L.cfg, L.pool, 1, None, 1, stream))
+        hf.check(hf.hyf_memory_commit(L.cfg, L.w, L.pool, 1, None, 1, feats, [0, 300], None, L.ws, L.ws_bytes,
+                                      stream))
+        for (cf, cu, bi), bo in zip(rounds, outs):
+            hf.check(hf.hyf_draft_block(L.cfg, L.w, L.pool, 1, None, 1, cf, cu, bi, bo, L.ws, L.ws_bytes, stream))
+
+    say("graph: eager reference")
+    episode(None)
+    torch.cuda.synchronize()
+    ref_out = [o.clone() for o in outs]
+    ref_state = L.state()["blob"].clone()
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    with torch.cuda.stream(cs):
+        episode(cs)
+    torch.cuda.synchronize()
+    say("graph: capture")
+    with torch.cuda.graph(g, stream=cs):
+        episode(cs)
+    for rep in range(3):
+        for o in outs:
+            o.zero_()
+        L.reset()
+        junk = torch.empty((16, shape.n_in), dtype=torch.float32, device=DEV)
+        hf.check(hf.hyf_linear(L.cfg, feats, 16, shape.d_model, L.w_in, shape.n_in, junk, 1))
+        torch.cuda.synchronize()
+        say("graph: replay", rep)
+        g.replay()
+        torch.cuda.synchronize()
+        for o, r in zip(outs, ref_out):
+            assert torch.equal(o, r)
+        assert torch.equal(L.state()["blob"], ref_state)
