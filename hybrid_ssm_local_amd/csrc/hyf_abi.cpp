@@ -114,6 +114,10 @@ int64_t scan_max_segs(const Shape& s, int dtype, int32_t n_req, int64_t rows) {
 // Blocks of the time-blocked buffers for `rows` tokens over R requests (each request starts a block).
 int64_t time_blocks(int64_t rows, int32_t R) { return rows / HYF_TBLK + R + 1; }
 
+// Row stride of the round's fp32 projection output: n_in rounded up to 4 floats, so every column
+// group starts 16-byte aligned.
+int64_t proj_ld(const Shape& s) { return (s.n_in + 3) / 4 * 4; }
+
 struct WsDraft {
   uint64_t proj, mem, att_part, att_ml, o_in, end;
 };
@@ -122,7 +126,7 @@ WsDraft ws_draft(const Shape& s, int dtype, int32_t R, int64_t rows) {
   const int ns = n_att_split(s);
   uint64_t o = 0;
   w.proj = o;
-  o += align_up((uint64_t)(rows + (int64_t)HYF_BLOCK * R) * s.n_in * 4);
+  o += align_up((uint64_t)(rows + (int64_t)HYF_BLOCK * R) * proj_ld(s) * 4);
   w.mem = o;
   o += align_up((uint64_t)R * HYF_BLOCK * s.dq * 4);
   w.att_part = o;
@@ -308,25 +312,29 @@ int hyf_memory_commit(const hyf_config* cfg, const hyf_weights* w, void* state_p
   for (int i = 0; i < n_req; ++i) max_n = cu_rows[i + 1] - cu_rows[i] > max_n ? cu_rows[i + 1] - cu_rows[i] : max_n;
 
   if (max_n <= 16) {
-    // Round-sized commit: one weight pass over the k | v | B | dt rows, then one read-modify-write of H.
+    // Round-sized commit: one weight pass over the k | v | B | dt rows, then the round kernel folds
+    // the rows into H (one read-modify-write) and appends them to the ring; count advances last.
     const WsDraft L = ws_draft(s, dt, n_req, rows);
     float* proj = reinterpret_cast<float*>(wsb + L.proj);
+    const int64_t ld = proj_ld(s);
     RowSrc xs{feats, feats, rows};
-    Epi e{proj + s.off_k, s.n_in, 1, s.n_in, nullptr, 0};
+    Epi e{proj + s.off_k, ld, 1, s.n_in, nullptr, 0, 0};
     hipError_t he = launch_linear(dt, xs, rows, s.d, static_cast<const char*>(w->w_in) + (int64_t)s.off_k * s.d * es,
                                   s.n_in - s.off_k, e, hs);
     if (he != hipSuccess) return HYF_EHIP;
     RoundArgs ra{};
     ra.proj = proj;
+    ra.ld = ld;
     ra.blk_row0 = rows;
     ra.state_pool = pool;
     ra.a_log = w->a_log;
     ra.dt_bias = w->dt_bias;
     ra.d_skip = w->d_skip;
+    ra.n_tiles = round_tiles(s);
+    ra.n_split = 0;
     ra.do_commit = 1;
     ra.do_draft = 0;
-    if ((he = launch_commit_small(dt, s, ra, rt, hs)) != hipSuccess) return HYF_EHIP;
-    return hip_status(launch_bump_counts(pool, s, rt, hs));
+    return hip_status(launch_round(dt, s, ra, rt, hs));
   }
 
   // Prefill-sized commit: projection GEMMs -> ring append -> scan -> count.
@@ -406,13 +414,16 @@ int hyf_draft_block(const hyf_config* cfg, const hyf_weights* w, void* state_poo
   float* proj = reinterpret_cast<float*>(wsb + L.proj);
 
   // 1. one pass over w_in for [commit rows ; block rows]
+  const int64_t ld = proj_ld(s);
   RowSrc xs{rows > 0 ? commit_feats : block_in, block_in, rows};
-  Epi e{proj, s.n_in, 1, s.n_in, nullptr, 0};
+  Epi e{proj, ld, 1, s.n_in, nullptr, 0, 0};
   hipError_t he = launch_linear(dt, xs, rows + (int64_t)HYF_BLOCK * n_req, s.d, w->w_in, s.n_in, e, hs);
   if (he != hipSuccess) return HYF_EHIP;
 
+  // 2. the round kernels: commit + readout tiles and attention splits, then the merge per head
   RoundArgs ra{};
   ra.proj = proj;
+  ra.ld = ld;
   ra.blk_row0 = rows;
   ra.state_pool = pool;
   ra.a_log = w->a_log;
@@ -422,16 +433,14 @@ int hyf_draft_block(const hyf_config* cfg, const hyf_weights* w, void* state_poo
   ra.att_part = reinterpret_cast<float*>(wsb + L.att_part);
   ra.att_ml = reinterpret_cast<float*>(wsb + L.att_ml);
   ra.o_in = wsb + L.o_in;
+  ra.n_tiles = round_tiles(s);
   ra.n_split = n_att_split(s);
-  ra.keys_per_split = 64;
   ra.do_commit = rows > 0;
   ra.do_draft = 1;
-  // 2. commit (if any) + memory readout, 3. attention, 4. merge (+ count), 5. output projection
-  if ((he = launch_commit_small(dt, s, ra, rt, hs)) != hipSuccess) return HYF_EHIP;
-  if ((he = launch_attention(dt, s, ra, rt, hs)) != hipSuccess) return HYF_EHIP;
-  if ((he = launch_merge(dt, s, ra, rt, hs)) != hipSuccess) return HYF_EHIP;
+  if ((he = launch_round(dt, s, ra, rt, hs)) != hipSuccess) return HYF_EHIP;
+  // 3. output projection
   RowSrc xo{ra.o_in, ra.o_in, (int64_t)HYF_BLOCK * n_req};
-  Epi eo{block_out, s.d, 0, s.d, nullptr, 0};
+  Epi eo{block_out, s.d, 0, s.d, nullptr, 0, 0};
   return hip_status(launch_linear(dt, xo, (int64_t)HYF_BLOCK * n_req, s.dq, w->w_out, s.d, eo, hs));
 }
 

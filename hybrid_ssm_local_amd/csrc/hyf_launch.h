@@ -11,9 +11,9 @@ namespace hyf {
 // Where a projection writes its output columns: columns < n_split go to out0 (fp32 when
 // out0_f32, else the storage dtype) with row stride ld0; columns >= n_split go to out1 (fp32)
 // at column (col - n_split) with row stride ld1.  With trans != 0 the output is written
-// time-blocked instead (rows m are tokens, blocks of HYF_TBLK): element (m, f) lands at
-// out0[(m / HYF_TBLK) * ld0 + f * HYF_TBLK + m % HYF_TBLK] (f < n_split) or at the same place in
-// out1 with ld1 and f - n_split; ld0 and ld1 are then block strides.
+// time-blocked instead (rows m are tokens, blocks of HYF_TBLK; ld0 and ld1 are block strides):
+// out0 in the tiled layout of tile_off (storage dtype) or plain [f][HYF_TBLK] rows (fp32), out1
+// in plain rows.
 struct Epi {
   void* out0;
   int64_t ld0;
@@ -59,9 +59,10 @@ int64_t scan_items_per_seg(const Shape& sh);
 hipError_t launch_ssd_state(int dtype, const Shape& sh, const ScanArgs& a, const ReqTable& rt,
                             int32_t max_segs_per_req, hipStream_t s);
 
-// Round kernels (see hyf_round.hip).
+// Round kernel (see hyf_round.hip).
 struct RoundArgs {
-  const float* proj;   // [rows][n_in] fp32: commit rows first (row0 table), then block rows
+  const float* proj;   // [rows][ld] fp32: commit rows first (row0 table), then block rows
+  int64_t ld;          // row stride of proj (n_in rounded up to a multiple of 4)
   int64_t blk_row0;    // first block row in proj
   char* state_pool;
   const float* a_log;
@@ -71,17 +72,14 @@ struct RoundArgs {
   float* att_part;     // [n_req][nh][n_split][8][P]
   float* att_ml;       // [n_req][nh][n_split][8][2]
   void* o_in;          // [n_req*8][dq] storage dtype
+  int32_t n_tiles;     // commit / readout tiles per (request, head)
   int32_t n_split;     // attention splits per (request, head), the last one holds the block keys
-  int32_t keys_per_split;
   int32_t do_commit;   // commit rows present
   int32_t do_draft;    // block rows present
 };
-hipError_t launch_commit_small(int dtype, const Shape& sh, const RoundArgs& a, const ReqTable& rt,
-                               hipStream_t s);
-hipError_t launch_attention(int dtype, const Shape& sh, const RoundArgs& a, const ReqTable& rt,
-                            hipStream_t s);
-hipError_t launch_merge(int dtype, const Shape& sh, const RoundArgs& a, const ReqTable& rt,
-                        hipStream_t s);
+int round_tiles(const Shape& sh);
+// k_round, then k_round_merge (draft) or the count update (commit only).
+hipError_t launch_round(int dtype, const Shape& sh, const RoundArgs& a, const ReqTable& rt, hipStream_t s);
 
 // Prefill ring append: the last m_i = min(n_i, W) rows of request i go to slots
 // (count + n_i - m_i + j) mod W.  k: token-major [sum m_i][ld_k] (the requests' last rows back to

@@ -76,28 +76,37 @@ k_proj_small(RowSrc xs, int M, int K, const T* __restrict__ W, int Nout, Epi epi
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // A wave takes slabs wave, wave + NW, ...; it loads SB of them before it multiplies, so a whole
+  // row of weights is in flight at once (same order of MFMAs as one slab at a time).
+  constexpr int SB = MT == 1 ? 4 : (MT == 2 ? 2 : 1);
   const int nslab = (K + SLAB - 1) / SLAB;
-  for (int s = wave; s < nslab; s += NW) {
-    const int kb = s * SLAB + g * LANE_K;
-    V wv[NV];
-    V xv[MT][NV];
+  for (int s0 = wave; s0 < nslab; s0 += SB * NW) {
+    V wv[SB][NV];
+    V xv[SB][MT][NV];
 #pragma unroll
-    for (int v = 0; v < NV; ++v) {
-      const int k = kb + v * VN;
-      const bool ok = k + VN <= K;
-      wv[v] = ok ? ld_vec<T>(wrow + k) : V{};
+    for (int sb = 0; sb < SB; ++sb) {
+      const int kb = (s0 + sb * NW) * SLAB + g * LANE_K;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) xv[mt][v] = ok ? ld_vec<T>(xrow[mt] + k) : V{};
+      for (int v = 0; v < NV; ++v) {
+        const int k = kb + v * VN;
+        const bool ok = k + VN <= K;
+        wv[sb][v] = ok ? ld_vec<T>(wrow + k) : V{};
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) xv[sb][mt][v] = ok ? ld_vec<T>(xrow[mt] + k) : V{};
+      }
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      Fr a;
-      if constexpr (KE == 8) a = wv[u]; else a = wv[0][u];
+    for (int sb = 0; sb < SB; ++sb) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        Fr b;
-        if constexpr (KE == 8) b = xv[mt][u]; else b = xv[mt][0][u];
-        acc[mt] = Mfma16<T>::mma(a, b, acc[mt]);
+      for (int u = 0; u < U; ++u) {
+        Fr a;
+        if constexpr (KE == 8) a = wv[sb][u]; else a = wv[sb][0][u];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          Fr b;
+          if constexpr (KE == 8) b = xv[sb][mt][u]; else b = xv[sb][mt][0][u];
+          acc[mt] = Mfma16<T>::mma(a, b, acc[mt]);
+        }
       }
     }
   }

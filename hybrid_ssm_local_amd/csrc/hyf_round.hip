@@ -1,15 +1,5 @@
-// Kernels of one draft/commit round (and the ring/state helpers of a prefill commit).
-//
-//  k_commit_small  per (request, head, rows of H): folds the round's committed rows into H with
-//                  one read-modify-write (chunk form, weights relative to the last row), appends
-//                  their (k, v) to the ring, and computes the memory readout of the block rows
-//                  from the updated H: mem_j = H . C_q,j + D * v_j.  H is read-only when the call
-//                  commits nothing.
-//  k_attn          per (request, head, split): softmax attention of the 8 block rows over a
-//                  slice of the ring window (or, in the last split, over the block rows
-//                  themselves), written as (max, sum, unnormalised output) partials.
-//  k_merge         per (request, head): merges the splits, adds mem, stores the output
-//                  projection's input, and advances the committed count.
+// Kernels of one draft/commit round (k_round, see below) and the ring/state helpers of a prefill
+// commit (k_ring_append, k_bump_counts, k_reset_states, k_zero).
 #include <mutex>
 
 #include "hyf_launch.h"
@@ -17,8 +7,9 @@
 namespace hyf {
 
 constexpr int RB = HYF_BLOCK;   // block rows
-constexpr int RMAXC = 16;       // largest per-request commit handled by k_commit_small
+constexpr int RMAXC = 16;       // largest per-request commit a round kernel folds in
 constexpr int ATT_KS = 64;      // keys per attention split
+constexpr int RT = 256;         // threads per round workgroup
 
 __device__ __forceinline__ int64_t* count_ptr(char* pool, const Shape& sh, int slot) {
   return reinterpret_cast<int64_t*>(pool + (int64_t)slot * sh.st_bytes);
@@ -32,66 +23,93 @@ __device__ __forceinline__ T* ring_ptr(char* pool, const Shape& sh, int slot, ui
 }
 
 // ---------------------------------------------------------------------------------------------
-template <typename T>
-__global__ void __launch_bounds__(256) k_commit_small(Shape sh, RoundArgs a, ReqTable rt) {
-  __shared__ float Bl[RMAXC][256];
-  __shared__ float Cl[RB][256];
-  __shared__ float red[RB][256];
-  __shared__ float wl[RMAXC];
-  __shared__ float decay_s;
+// One round in two launches.  k_round: workgroup roles per (request r, head h), in block-index
+// order:
+//   tiles  [0, n_tiles):   rows p0 .. p0 + rows_wg of H: fold the round's committed rows in (one
+//                          read-modify-write), memory readout of the block rows from the updated
+//                          rows, and (tile 0) the ring append of the committed (k, v);
+//   splits [n_tiles, +n_split): attention of the 8 block rows over 64 ring slots (the last split:
+//                          over the block rows themselves), written as (max, sum, output) partials.
+// A split sees the ring as it is after this round's append without waiting for it: a slot that
+// the append overwrites is read from the projection instead (rounded to the storage dtype, as the
+// ring stores it).  k_round_merge then merges the splits per (r, h), adds the readout, writes the
+// output projection's input and advances the committed count.  (Merging inside k_round by its
+// last workgroup per head needs a device-scope release per workgroup, which on this chip writes
+// back the L2 and cost more than the extra launch.)
 
+template <typename T>
+__device__ __forceinline__ void round_tile(const Shape& sh, const RoundArgs& a, const ReqTable& rt, int r, int h,
+                                           int tile, float* smem) {
   const int nh = sh.nh, P = sh.P, N = sh.N;
-  const int r = blockIdx.x / nh, h = blockIdx.x % nh;
-  const int slot = rt.slot[r];
-  const int grp = h / (nh / sh.G);
-  const int tpr = N / 4;                    // threads per H row (float4 each)
-  const int rows_wg = 256 / tpr;            // H rows per workgroup
-  const int p0 = blockIdx.y * rows_wg;
+  const int tpr = N / 4;           // threads per H row (4 columns each)
+  const int rows_wg = RT / tpr;    // H rows per tile
   const int t = threadIdx.x;
   const int prow = t / tpr, c4 = t % tpr;
-  const int p = p0 + prow;
+  const int p0 = tile * rows_wg, p = p0 + prow;
   const bool active = prow < rows_wg && p < P;
+  const int slot = rt.slot[r];
+  const int grp = h / (nh / sh.G);
   const int nrows = a.do_commit ? rt.row0[r + 1] - rt.row0[r] : 0;
   const int64_t crow0 = rt.row0[r];
   const int64_t brow0 = a.blk_row0 + (int64_t)r * RB;
-  const int ld = sh.n_in;
+  const int64_t ld = a.ld;
+  float* Bl = smem;                     // [RMAXC][N]  B of the committed rows
+  float* Cl = Bl + RMAXC * N;           // [RB][N]     C of the block rows
+  float* xv = Cl + RB * N;              // [RMAXC][rows_wg] x (= v) of the committed rows
+  float* vb = xv + RMAXC * rows_wg;     // [RB][rows_wg]    v of the block rows
+  float* wl = vb + RB * rows_wg;        // [RMAXC] weights, then the total decay
+  float* red = wl + RMAXC + 4;          // [RB][RT]
 
-  // stage B rows of the commit and C rows of the block
-  for (int idx = t; idx < nrows * N; idx += 256) {
-    const int tt = idx / N, n = idx % N;
-    Bl[tt][n] = a.proj[(crow0 + tt) * ld + sh.off_b + grp * N + n];
+  // every load first (one round trip), then the arithmetic
+  float* Hh = h_ptr(a.state_pool, sh, slot, h);
+  f32x4 hv = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (active) hv = *reinterpret_cast<const f32x4*>(Hh + (int64_t)p * N + 4 * c4);
+  for (int idx = t; idx < nrows * tpr; idx += RT) {
+    const int tt = idx / tpr, c = idx % tpr;
+    *reinterpret_cast<f32x4*>(Bl + tt * N + 4 * c) =
+        *reinterpret_cast<const f32x4*>(a.proj + (crow0 + tt) * ld + sh.off_b + grp * N + 4 * c);
   }
   if (a.do_draft)
-    for (int idx = t; idx < RB * N; idx += 256) {
-      const int j = idx / N, n = idx % N;
-      Cl[j][n] = a.proj[(brow0 + j) * ld + sh.off_c + grp * N + n];
+    for (int idx = t; idx < RB * tpr; idx += RT) {
+      const int j = idx / tpr, c = idx % tpr;
+      *reinterpret_cast<f32x4*>(Cl + j * N + 4 * c) =
+          *reinterpret_cast<const f32x4*>(a.proj + (brow0 + j) * ld + sh.off_c + grp * N + 4 * c);
     }
-  if (t == 0) {
-    // weights relative to the last committed row: w_t = dt_t exp(sum_{tau > t} dt_tau A)
+  for (int idx = t; idx < nrows * rows_wg; idx += RT) {
+    const int tt = idx / rows_wg, pp = p0 + idx % rows_wg;
+    xv[idx] = pp < P ? a.proj[(crow0 + tt) * ld + sh.off_v + h * P + pp] : 0.f;
+  }
+  if (a.do_draft)
+    for (int idx = t; idx < RB * rows_wg; idx += RT) {
+      const int j = idx / rows_wg, pp = p0 + idx % rows_wg;
+      vb[idx] = pp < P ? a.proj[(brow0 + j) * ld + sh.off_v + h * P + pp] : 0.f;
+    }
+  if (t < 64) {
+    // weights relative to the last committed row: w_t = dt_t exp(sum_{tau > t} dt_tau A), and
+    // the decay exp(sum_t dt_t A) of the old state; lane t < nrows holds row t
+    const float raw = t < nrows ? a.proj[(crow0 + t) * ld + sh.off_dt + h] : 0.f;
     const float A = -expf(a.a_log[h]);
-    float suffix = 0.f;
-    for (int tt = nrows - 1; tt >= 0; --tt) {
-      const float dt = softplus_f(a.proj[(crow0 + tt) * ld + sh.off_dt + h] + a.dt_bias[h]);
-      wl[tt] = dt * expf(suffix);
-      suffix += dt * A;
+    const float dt = t < nrows ? softplus_f(raw + a.dt_bias[h]) : 0.f;
+    const float ell = dt * A;
+    float inc = ell;  // sum over lanes t .. RMAXC - 1
+#pragma unroll
+    for (int o = 1; o < RMAXC; o <<= 1) {
+      const float v = __shfl_down(inc, o, 64);
+      if (t + o < RMAXC) inc += v;
     }
-    decay_s = expf(suffix);
+    if (t < nrows) wl[t] = dt * expf(inc - ell);
+    if (t == 0) wl[RMAXC] = expf(inc);
   }
   __syncthreads();
 
-  float* Hh = h_ptr(a.state_pool, sh, slot, h);
-  f32x4 hv = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (active) {
-    hv = *reinterpret_cast<const f32x4*>(Hh + (int64_t)p * N + 4 * c4);
-    if (nrows > 0) {
-      hv *= decay_s;
-      for (int tt = 0; tt < nrows; ++tt) {
-        const float xv = a.proj[(crow0 + tt) * ld + sh.off_v + h * P + p] * wl[tt];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) hv[u] += xv * Bl[tt][4 * c4 + u];
-      }
-      *reinterpret_cast<f32x4*>(Hh + (int64_t)p * N + 4 * c4) = hv;
+  if (active && nrows > 0) {
+    hv *= wl[RMAXC];
+    for (int tt = 0; tt < nrows; ++tt) {
+      const float xw = xv[tt * rows_wg + prow] * wl[tt];
+      const f32x4 b = *reinterpret_cast<const f32x4*>(Bl + tt * N + 4 * c4);
+      hv += xw * b;
     }
+    *reinterpret_cast<f32x4*>(Hh + (int64_t)p * N + 4 * c4) = hv;
   }
 
   if (a.do_draft) {
@@ -99,32 +117,31 @@ __global__ void __launch_bounds__(256) k_commit_small(Shape sh, RoundArgs a, Req
     for (int j = 0; j < RB; ++j) {
       float s = 0.f;
       if (active) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) s += hv[u] * Cl[j][4 * c4 + u];
+        const f32x4 c = *reinterpret_cast<const f32x4*>(Cl + j * N + 4 * c4);
+        s = hv[0] * c[0] + hv[1] * c[1] + hv[2] * c[2] + hv[3] * c[3];
       }
-      red[j][t] = s;
+      red[j * RT + t] = s;
     }
     __syncthreads();
     const float D = a.d_skip[h];
-    for (int idx = t; idx < RB * rows_wg; idx += 256) {
+    for (int idx = t; idx < RB * rows_wg; idx += RT) {
       const int j = idx / rows_wg, pr = idx % rows_wg;
       const int pp = p0 + pr;
       if (pp >= P) continue;
       float s = 0.f;
-      for (int c = 0; c < tpr; ++c) s += red[j][pr * tpr + c];
-      const float vj = a.proj[(brow0 + j) * ld + sh.off_v + h * P + pp];
-      a.mem[(((int64_t)r * RB + j) * nh + h) * P + pp] = s + D * vj;
+      for (int c = 0; c < tpr; ++c) s += red[j * RT + pr * tpr + c];
+      a.mem[(((int64_t)r * RB + j) * nh + h) * P + pp] = s + D * vb[idx];
     }
   }
 
-  // ring append of this round's rows (first row-tile workgroup of each head)
-  if (blockIdx.y == 0 && nrows > 0) {
+  // ring append of this round's rows (tile 0 of each head): the last min(n, W) rows
+  if (tile == 0 && nrows > 0) {
     const int64_t count = *count_ptr(a.state_pool, sh, slot);
     const int W = sh.W;
     const int first = nrows > W ? nrows - W : 0;
     T* K = ring_ptr<T>(a.state_pool, sh, slot, sh.st_k, h);
     T* V = ring_ptr<T>(a.state_pool, sh, slot, sh.st_v, h);
-    for (int idx = t; idx < (nrows - first) * P; idx += 256) {
+    for (int idx = t; idx < (nrows - first) * P; idx += RT) {
       const int tt = first + idx / P, pp = idx % P;
       const int64_t s = (count + tt) % W;
       K[s * P + pp] = from_f32<T>(a.proj[(crow0 + tt) * ld + sh.off_k + h * P + pp]);
@@ -133,98 +150,122 @@ __global__ void __launch_bounds__(256) k_commit_small(Shape sh, RoundArgs a, Req
   }
 }
 
-// ---------------------------------------------------------------------------------------------
 template <typename T>
-__global__ void __launch_bounds__(256) k_attn(Shape sh, RoundArgs a, ReqTable rt) {
-  extern __shared__ float dsm[];
-  const int nh = sh.nh, P = sh.P;
+__device__ __forceinline__ void round_attn(const Shape& sh, const RoundArgs& a, const ReqTable& rt, int r, int h,
+                                           int sp, float* smem) {
+  constexpr int VN = Vec16<T>::n;
+  typedef typename Vec16<T>::type Vv;
+  const int nh = sh.nh, P = sh.P, W = sh.W;
   const int PK = P + 1;  // key rows padded so consecutive keys fall in different banks
-  float* qs = dsm;                    // [8][P]
-  float* ks = qs + RB * P;            // [64][P+1]
-  float* vs = ks + ATT_KS * PK;       // [64][P]
-  float* pl = vs + ATT_KS * P;        // [8][64]
-
-  const int r = blockIdx.x / nh, h = blockIdx.x % nh;
-  const int sp = blockIdx.y;
+  float* qs = smem;                   // [RB][P]
+  float* ks = qs + RB * P;            // [ATT_KS][P + 1]
+  float* vs = ks + ATT_KS * PK;       // [ATT_KS][P]
+  float* pl = vs + ATT_KS * P;        // [RB][ATT_KS]
   const int slot = rt.slot[r];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int ld = sh.n_in;
+  const int64_t ld = a.ld;
   const int64_t brow0 = a.blk_row0 + (int64_t)r * RB;
   const bool blk = sp == a.n_split - 1;
+  const int nrows = a.do_commit ? rt.row0[r + 1] - rt.row0[r] : 0;
+  const int64_t crow0 = rt.row0[r];
 
+  const float scale = rsqrtf((float)P);
+  for (int idx = t; idx < RB * P / 4; idx += RT) {
+    const int j = 4 * idx / P, pp = 4 * idx % P;
+    *reinterpret_cast<f32x4*>(qs + j * P + pp) =
+        *reinterpret_cast<const f32x4*>(a.proj + (brow0 + j) * ld + sh.off_q + h * P + pp) * scale;
+  }
   int nk;
   if (blk) {
     nk = RB;
+    for (int idx = t; idx < RB * P / 4; idx += RT) {
+      const int j = 4 * idx / P, pp = 4 * idx % P;
+      const f32x4 kk = *reinterpret_cast<const f32x4*>(a.proj + (brow0 + j) * ld + sh.off_k + h * P + pp);
+      const f32x4 vv = *reinterpret_cast<const f32x4*>(a.proj + (brow0 + j) * ld + sh.off_v + h * P + pp);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ks[j * PK + pp + e] = kk[e];
+      *reinterpret_cast<f32x4*>(vs + j * P + pp) = vv;
+    }
   } else {
+    // ring slots k0 .. k0 + nk - 1 of the window after this round's append
     const int64_t count = *count_ptr(a.state_pool, sh, slot);
-    const int64_t added = a.do_commit ? rt.row0[r + 1] - rt.row0[r] : 0;
-    const int64_t tot = count + added;
-    const int valid = (int)(tot < sh.W ? tot : sh.W);
-    const int k0 = sp * a.keys_per_split;
+    const int64_t tot = count + nrows;
+    const int valid = (int)(tot < W ? tot : W);
+    const int k0 = sp * ATT_KS;
     nk = valid - k0;
-    nk = nk < 0 ? 0 : (nk > a.keys_per_split ? a.keys_per_split : nk);
+    nk = nk < 0 ? 0 : (nk > ATT_KS ? ATT_KS : nk);
+    const int m = nrows < W ? nrows : W;             // rows of this round that land in the ring
+    const int lead = (int)((count + nrows - m) % W);  // slot of the first of them
+    const T* K = ring_ptr<T>(a.state_pool, sh, slot, sh.st_k, h);
+    const T* V = ring_ptr<T>(a.state_pool, sh, slot, sh.st_v, h);
+    const int CH = P / VN;  // 16-byte chunks per key row
+    for (int idx = t; idx < nk * CH; idx += RT) {
+      const int key = idx / CH, c = idx % CH;
+      const int s = k0 + key;
+      const int jn = (s - lead + W) % W;  // index among the landing rows, if this slot is one
+      float kf[VN], vf[VN];
+      if (jn < m) {
+        const int64_t row = crow0 + (nrows - m) + jn;
+#pragma unroll
+        for (int e = 0; e < VN; ++e) {
+          kf[e] = to_f32(from_f32<T>(a.proj[row * ld + sh.off_k + h * P + c * VN + e]));
+          vf[e] = to_f32(from_f32<T>(a.proj[row * ld + sh.off_v + h * P + c * VN + e]));
+        }
+      } else {
+        const Vv kv = *reinterpret_cast<const Vv*>(K + (int64_t)s * P + c * VN);
+        const Vv vv = *reinterpret_cast<const Vv*>(V + (int64_t)s * P + c * VN);
+#pragma unroll
+        for (int e = 0; e < VN; ++e) {
+          kf[e] = to_f32(kv[e]);
+          vf[e] = to_f32(vv[e]);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < VN; ++e) {
+        ks[key * PK + c * VN + e] = kf[e];
+        vs[key * P + c * VN + e] = vf[e];
+      }
+    }
   }
   float* op = a.att_part + ((((int64_t)r * nh + h) * a.n_split + sp) * RB) * P;
   float* ml = a.att_ml + ((((int64_t)r * nh + h) * a.n_split + sp) * RB) * 2;
   if (nk == 0) {
-    for (int idx = t; idx < RB * P; idx += 256) op[idx] = 0.f;
+    for (int idx = t; idx < RB * P; idx += RT) op[idx] = 0.f;
     if (t < RB) {
       ml[2 * t] = -INFINITY;
       ml[2 * t + 1] = 0.f;
     }
     return;
   }
-
-  const float scale = rsqrtf((float)P);
-  for (int idx = t; idx < RB * P; idx += 256) {
-    const int j = idx / P, pp = idx % P;
-    qs[idx] = a.proj[(brow0 + j) * ld + sh.off_q + h * P + pp] * scale;
-  }
-  if (blk) {
-    for (int idx = t; idx < RB * P; idx += 256) {
-      const int j = idx / P, pp = idx % P;
-      ks[j * PK + pp] = a.proj[(brow0 + j) * ld + sh.off_k + h * P + pp];
-      vs[j * P + pp] = a.proj[(brow0 + j) * ld + sh.off_v + h * P + pp];
-    }
-  } else {
-    const T* K = ring_ptr<T>(a.state_pool, sh, slot, sh.st_k, h) + (int64_t)sp * a.keys_per_split * P;
-    const T* V = ring_ptr<T>(a.state_pool, sh, slot, sh.st_v, h) + (int64_t)sp * a.keys_per_split * P;
-    for (int idx = t; idx < nk * P; idx += 256) {
-      const int key = idx / P, pp = idx % P;
-      ks[key * PK + pp] = to_f32(K[idx]);
-      vs[key * P + pp] = to_f32(V[idx]);
-    }
-  }
   __syncthreads();
 
   // scores: lane = key, wave w handles block rows w and w + 4
   const int key = lane;
-  float s[2];
+  float sc[2];
 #pragma unroll
   for (int q2 = 0; q2 < 2; ++q2) {
     const int j = wave + 4 * q2;
     float acc = 0.f;
-    if (key < nk) {
+    if (key < nk)
       for (int pp = 0; pp < P; ++pp) acc += qs[j * P + pp] * ks[key * PK + pp];
-    }
     bool ok = key < nk;
     if (blk && !sh.cross && key != j) ok = false;
-    s[q2] = ok ? acc : -INFINITY;
+    sc[q2] = ok ? acc : -INFINITY;
   }
 #pragma unroll
   for (int q2 = 0; q2 < 2; ++q2) {
     const int j = wave + 4 * q2;
-    const float m = wave_max(s[q2]);
-    const float e = s[q2] == -INFINITY ? 0.f : expf(s[q2] - m);
+    const float mx = wave_max(sc[q2]);
+    const float e = sc[q2] == -INFINITY ? 0.f : expf(sc[q2] - mx);
     const float l = wave_sum(e);
     pl[j * ATT_KS + key] = e;
     if (lane == 0) {
-      ml[2 * j] = m;
+      ml[2 * j] = mx;
       ml[2 * j + 1] = l;
     }
   }
   __syncthreads();
-  for (int idx = t; idx < RB * P; idx += 256) {
+  for (int idx = t; idx < RB * P; idx += RT) {
     const int j = idx / P, pp = idx % P;
     float acc = 0.f;
     for (int k2 = 0; k2 < nk; ++k2) acc += pl[j * ATT_KS + k2] * vs[k2 * P + pp];
@@ -232,35 +273,57 @@ __global__ void __launch_bounds__(256) k_attn(Shape sh, RoundArgs a, ReqTable rt
   }
 }
 
-// ---------------------------------------------------------------------------------------------
 template <typename T>
-__global__ void __launch_bounds__(256) k_merge(Shape sh, RoundArgs a, ReqTable rt) {
-  const int nh = sh.nh, P = sh.P;
-  const int r = blockIdx.x / nh, h = blockIdx.x % nh;
-  const int t = threadIdx.x;
-  const float* ml = a.att_ml + (((int64_t)r * nh + h) * a.n_split) * RB * 2;
-  const float* op = a.att_part + (((int64_t)r * nh + h) * a.n_split) * RB * P;
+__device__ __forceinline__ void round_merge(const Shape& sh, const RoundArgs& a, int r, int h, float* smem) {
+  const int nh = sh.nh, P = sh.P, t = threadIdx.x;
+  const int ns = a.n_split;
+  const float* ml = a.att_ml + (((int64_t)r * nh + h) * ns) * RB * 2;
+  const float* op = a.att_part + (((int64_t)r * nh + h) * ns) * RB * P;
+  float* sml = smem;  // [ns][RB][2]
+  for (int idx = t; idx < ns * RB * 2; idx += RT) sml[idx] = ml[idx];
+  __syncthreads();
   T* out = static_cast<T*>(a.o_in);
-  for (int idx = t; idx < RB * P; idx += 256) {
+  for (int idx = t; idx < RB * P; idx += RT) {
     const int j = idx / P, pp = idx % P;
     float m = -INFINITY;
-    for (int s = 0; s < a.n_split; ++s) m = fmaxf(m, ml[(s * RB + j) * 2]);
+    for (int s = 0; s < ns; ++s) m = fmaxf(m, sml[(s * RB + j) * 2]);
     float l = 0.f, o = 0.f;
-    for (int s = 0; s < a.n_split; ++s) {
-      const float ms = ml[(s * RB + j) * 2];
-      if (ms == -INFINITY) continue;
-      const float f = expf(ms - m);
-      l += f * ml[(s * RB + j) * 2 + 1];
+#pragma unroll 4
+    for (int s = 0; s < ns; ++s) {
+      const float ms = sml[(s * RB + j) * 2];
+      const float f = ms == -INFINITY ? 0.f : expf(ms - m);
+      l += f * sml[(s * RB + j) * 2 + 1];
       o += f * op[((int64_t)s * RB + j) * P + pp];
     }
-    const float att = o / l;
     const float mem = a.mem[(((int64_t)r * RB + j) * nh + h) * P + pp];
-    out[((int64_t)r * RB + j) * sh.dq + h * P + pp] = from_f32<T>(att + mem);
+    out[((int64_t)r * RB + j) * sh.dq + h * P + pp] = from_f32<T>(o / l + mem);
   }
-  if (h == 0 && t == 0 && a.do_commit) *count_ptr(a.state_pool, sh, rt.slot[r]) += rt.row0[r + 1] - rt.row0[r];
 }
 
-// ---------------------------------------------------------------------------------------------
+template <typename T>
+__global__ void __launch_bounds__(RT) k_round(Shape sh, RoundArgs a, ReqTable rt) {
+  extern __shared__ __attribute__((aligned(16))) float dsm[];
+  const int per = a.n_tiles + a.n_split;
+  const int rh = blockIdx.x / per, role = blockIdx.x % per;
+  const int r = rh / sh.nh, h = rh % sh.nh;
+  if (role < a.n_tiles)
+    round_tile<T>(sh, a, rt, r, h, role, dsm);
+  else
+    round_attn<T>(sh, a, rt, r, h, role - a.n_tiles, dsm);
+}
+
+// Per (request, head): merge the attention splits, add the readout, write the output
+// projection's input; head 0 then advances the request's committed count (every reader of the
+// count ran in the previous launch).
+template <typename T>
+__global__ void __launch_bounds__(RT) k_round_merge(Shape sh, RoundArgs a, ReqTable rt) {
+  extern __shared__ __attribute__((aligned(16))) float dsm[];
+  const int r = blockIdx.x / sh.nh, h = blockIdx.x % sh.nh;
+  round_merge<T>(sh, a, r, h, dsm);
+  if (h == 0 && threadIdx.x == 0 && a.do_commit)
+    *count_ptr(a.state_pool, sh, rt.slot[r]) += rt.row0[r + 1] - rt.row0[r];
+}
+
 template <typename T>
 __global__ void __launch_bounds__(256) k_ring_append(Shape sh, char* pool, ReqTable rt, const T* __restrict__ k,
                                                      int64_t ld_k, const T* __restrict__ vT, int64_t ld_v) {
@@ -307,24 +370,22 @@ __global__ void k_reset_states(char* pool, Shape sh, ReqTable rt) {
     p[i] = 0u;
 }
 
-// ---------------------------------------------------------------------------------------------
-hipError_t launch_commit_small(int dtype, const Shape& sh, const RoundArgs& a, const ReqTable& rt, hipStream_t s) {
-  const int rows_wg = 256 / (sh.N / 4);
-  dim3 grid((unsigned)rt.n_req * sh.nh, (sh.P + rows_wg - 1) / rows_wg);
-  if (dtype == HYF_BF16)
-    hipLaunchKernelGGL(k_commit_small<bf16>, grid, dim3(256), 0, s, sh, a, rt);
-  else
-    hipLaunchKernelGGL(k_commit_small<float>, grid, dim3(256), 0, s, sh, a, rt);
-  return hipGetLastError();
+// Rows of H per commit tile and tiles per head.
+int round_rows_per_tile(const Shape& sh) { return RT / (sh.N / 4); }
+int round_tiles(const Shape& sh) { return (sh.P + round_rows_per_tile(sh) - 1) / round_rows_per_tile(sh); }
+
+size_t round_lds_bytes(const Shape& sh, int n_split) {
+  const size_t rw = round_rows_per_tile(sh);
+  const size_t tile = sizeof(float) * ((size_t)(RMAXC + RB) * sh.N + (RMAXC + RB) * rw + RMAXC + 4 + RB * RT);
+  const size_t attn = sizeof(float) * ((size_t)RB * sh.P + (size_t)ATT_KS * (sh.P + 1) + (size_t)ATT_KS * sh.P + RB * ATT_KS);
+  const size_t merge = sizeof(float) * (size_t)n_split * RB * 2;
+  size_t m = tile > attn ? tile : attn;
+  return m > merge ? m : merge;
 }
 
-size_t attn_lds_bytes(const Shape& sh) {
-  return sizeof(float) * ((size_t)RB * sh.P + (size_t)ATT_KS * (sh.P + 1) + (size_t)ATT_KS * sh.P + RB * ATT_KS);
-}
-
-hipError_t launch_attention(int dtype, const Shape& sh, const RoundArgs& a, const ReqTable& rt, hipStream_t s) {
-  dim3 grid((unsigned)rt.n_req * sh.nh, a.n_split);
-  const size_t lds = attn_lds_bytes(sh);
+hipError_t launch_round(int dtype, const Shape& sh, const RoundArgs& a, const ReqTable& rt, hipStream_t s) {
+  const int per = a.n_tiles + a.n_split;
+  const size_t lds = round_lds_bytes(sh, a.n_split);
   if (lds > 65536) {
     // Above 64 KiB of dynamic LDS the kernel has to opt in (gfx950 has 160 KiB per workgroup).
     // Done once per process with the largest size any shape needs, so later calls (possibly under
@@ -333,27 +394,28 @@ hipError_t launch_attention(int dtype, const Shape& sh, const RoundArgs& a, cons
     static hipError_t set_err = hipSuccess;
     std::call_once(once, [] {
       const int mx = 160 * 1024;
-      set_err = hipFuncSetAttribute(reinterpret_cast<const void*>(k_attn<bf16>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, mx);
-      if (set_err == hipSuccess)
-        set_err = hipFuncSetAttribute(reinterpret_cast<const void*>(k_attn<float>),
-                                      hipFuncAttributeMaxDynamicSharedMemorySize, mx);
+      const void* fns[4] = {reinterpret_cast<const void*>(k_round<bf16>), reinterpret_cast<const void*>(k_round<float>),
+                            reinterpret_cast<const void*>(k_round_merge<bf16>),
+                            reinterpret_cast<const void*>(k_round_merge<float>)};
+      for (const void* f : fns)
+        if (set_err == hipSuccess) set_err = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, mx);
     });
     if (set_err != hipSuccess) return set_err;
   }
+  dim3 grid((unsigned)(rt.n_req * sh.nh * per));
   if (dtype == HYF_BF16)
-    hipLaunchKernelGGL(k_attn<bf16>, grid, dim3(256), lds, s, sh, a, rt);
+    hipLaunchKernelGGL(k_round<bf16>, grid, dim3(RT), lds, s, sh, a, rt);
   else
-    hipLaunchKernelGGL(k_attn<float>, grid, dim3(256), lds, s, sh, a, rt);
-  return hipGetLastError();
-}
-
-hipError_t launch_merge(int dtype, const Shape& sh, const RoundArgs& a, const ReqTable& rt, hipStream_t s) {
-  dim3 grid((unsigned)rt.n_req * sh.nh);
+    hipLaunchKernelGGL(k_round<float>, grid, dim3(RT), lds, s, sh, a, rt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (!a.do_draft) return a.do_commit ? launch_bump_counts(a.state_pool, sh, rt, s) : hipSuccess;
+  const size_t mlds = sizeof(float) * (size_t)a.n_split * RB * 2;
+  dim3 mgrid((unsigned)(rt.n_req * sh.nh));
   if (dtype == HYF_BF16)
-    hipLaunchKernelGGL(k_merge<bf16>, grid, dim3(256), 0, s, sh, a, rt);
+    hipLaunchKernelGGL(k_round_merge<bf16>, mgrid, dim3(RT), mlds, s, sh, a, rt);
   else
-    hipLaunchKernelGGL(k_merge<float>, grid, dim3(256), 0, s, sh, a, rt);
+    hipLaunchKernelGGL(k_round_merge<float>, mgrid, dim3(RT), mlds, s, sh, a, rt);
   return hipGetLastError();
 }
 
