@@ -119,7 +119,7 @@ int64_t time_blocks(int64_t rows, int32_t R) { return rows / HYF_TBLK + R + 1; }
 int64_t proj_ld(const Shape& s) { return (s.n_in + 3) / 4 * 4; }
 
 struct WsDraft {
-  uint64_t proj, mem, att_part, att_ml, o_in, end;
+  uint64_t proj, mem, att_part, att_ml, o_in, counters, end;
 };
 WsDraft ws_draft(const Shape& s, int dtype, int32_t R, int64_t rows) {
   WsDraft w;
@@ -135,6 +135,8 @@ WsDraft ws_draft(const Shape& s, int dtype, int32_t R, int64_t rows) {
   o += align_up((uint64_t)R * s.nh * ns * HYF_BLOCK * 2 * 4);
   w.o_in = o;
   o += align_up((uint64_t)R * HYF_BLOCK * s.dq * esize(dtype));
+  w.counters = o;
+  o += align_up((uint64_t)(R * s.nh + R) * 4);
   w.end = o;
   return w;
 }
@@ -312,13 +314,14 @@ int hyf_memory_commit(const hyf_config* cfg, const hyf_weights* w, void* state_p
   for (int i = 0; i < n_req; ++i) max_n = cu_rows[i + 1] - cu_rows[i] > max_n ? cu_rows[i + 1] - cu_rows[i] : max_n;
 
   if (max_n <= 16) {
-    // Round-sized commit: one weight pass over the k | v | B | dt rows, then the round kernel folds
-    // the rows into H (one read-modify-write) and appends them to the ring; count advances last.
+    // Round-sized commit: one weight pass over the k | v | B | dt rows, then one round kernel that
+    // folds the rows into H (one read-modify-write), appends them to the ring and advances count.
     const WsDraft L = ws_draft(s, dt, n_req, rows);
     float* proj = reinterpret_cast<float*>(wsb + L.proj);
+    int32_t* counters = reinterpret_cast<int32_t*>(wsb + L.counters);
     const int64_t ld = proj_ld(s);
     RowSrc xs{feats, feats, rows};
-    Epi e{proj + s.off_k, ld, 1, s.n_in, nullptr, 0, 0};
+    Epi e{proj + s.off_k, ld, 1, s.n_in, nullptr, 0, 0, counters, n_req * s.nh + n_req};
     hipError_t he = launch_linear(dt, xs, rows, s.d, static_cast<const char*>(w->w_in) + (int64_t)s.off_k * s.d * es,
                                   s.n_in - s.off_k, e, hs);
     if (he != hipSuccess) return HYF_EHIP;
@@ -330,6 +333,7 @@ int hyf_memory_commit(const hyf_config* cfg, const hyf_weights* w, void* state_p
     ra.a_log = w->a_log;
     ra.dt_bias = w->dt_bias;
     ra.d_skip = w->d_skip;
+    ra.counters = counters;
     ra.n_tiles = round_tiles(s);
     ra.n_split = 0;
     ra.do_commit = 1;
@@ -413,14 +417,15 @@ int hyf_draft_block(const hyf_config* cfg, const hyf_weights* w, void* state_poo
   const WsDraft L = ws_draft(s, dt, n_req, rows);
   float* proj = reinterpret_cast<float*>(wsb + L.proj);
 
-  // 1. one pass over w_in for [commit rows ; block rows]
+  // 1. one pass over w_in for [commit rows ; block rows] (it also clears the round's counters)
+  int32_t* counters = reinterpret_cast<int32_t*>(wsb + L.counters);
   const int64_t ld = proj_ld(s);
   RowSrc xs{rows > 0 ? commit_feats : block_in, block_in, rows};
-  Epi e{proj, ld, 1, s.n_in, nullptr, 0, 0};
+  Epi e{proj, ld, 1, s.n_in, nullptr, 0, 0, counters, n_req * s.nh + n_req};
   hipError_t he = launch_linear(dt, xs, rows + (int64_t)HYF_BLOCK * n_req, s.d, w->w_in, s.n_in, e, hs);
   if (he != hipSuccess) return HYF_EHIP;
 
-  // 2. the round kernels: commit + readout tiles and attention splits, then the merge per head
+  // 2. the round kernel: commit + readout tiles and attention splits, merged per head
   RoundArgs ra{};
   ra.proj = proj;
   ra.ld = ld;
@@ -433,6 +438,7 @@ int hyf_draft_block(const hyf_config* cfg, const hyf_weights* w, void* state_poo
   ra.att_part = reinterpret_cast<float*>(wsb + L.att_part);
   ra.att_ml = reinterpret_cast<float*>(wsb + L.att_ml);
   ra.o_in = wsb + L.o_in;
+  ra.counters = counters;
   ra.n_tiles = round_tiles(s);
   ra.n_split = n_att_split(s);
   ra.do_commit = rows > 0;
@@ -440,7 +446,7 @@ int hyf_draft_block(const hyf_config* cfg, const hyf_weights* w, void* state_poo
   if ((he = launch_round(dt, s, ra, rt, hs)) != hipSuccess) return HYF_EHIP;
   // 3. output projection
   RowSrc xo{ra.o_in, ra.o_in, (int64_t)HYF_BLOCK * n_req};
-  Epi eo{block_out, s.d, 0, s.d, nullptr, 0, 0};
+  Epi eo{block_out, s.d, 0, s.d, nullptr, 0, 0, nullptr, 0};
   return hip_status(launch_linear(dt, xo, (int64_t)HYF_BLOCK * n_req, s.dq, w->w_out, s.d, eo, hs));
 }
 

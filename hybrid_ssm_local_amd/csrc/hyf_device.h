@@ -95,6 +95,26 @@ template <> struct Mfma16<float> {
   }
 };
 
+// Wait until at most N vector-memory operations of this wave are outstanding (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt and lgkmcnt left at their no-wait maxima).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Direct global -> LDS loads (no registers): lane l's 16 (or 4) bytes land at lds_base + 16 l
+// (4 l).  lds_base must be the same for the whole wave; the data is there once this wave's
+// vector-memory count drains (vm_wait<0>) — other waves see it after a barrier.
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(src),
+                                   (void __attribute__((address_space(3)))*)(lds_base), 16, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(src),
+                                   (void __attribute__((address_space(3)))*)(lds_base), 4, 0, 0);
+}
+
 // 16-byte vector of storage elements.
 template <typename T> struct Vec16;
 template <> struct Vec16<bf16> {

@@ -13,7 +13,8 @@ namespace hyf {
 // at column (col - n_split) with row stride ld1.  With trans != 0 the output is written
 // time-blocked instead (rows m are tokens, blocks of HYF_TBLK; ld0 and ld1 are block strides):
 // out0 in the tiled layout of tile_off (storage dtype) or plain [f][HYF_TBLK] rows (fp32), out1
-// in plain rows.
+// in plain rows.  If zero is set, the launch also clears zero[0 .. n_zero) (the counters of the
+// kernel that consumes this output).
 struct Epi {
   void* out0;
   int64_t ld0;
@@ -22,6 +23,8 @@ struct Epi {
   float* out1;
   int64_t ld1;
   int32_t trans;
+  int32_t* zero;
+  int32_t n_zero;
 };
 
 // Rows of the projection input: rows m < M1 come from X1 (row stride K), the rest from X2.
@@ -72,13 +75,13 @@ struct RoundArgs {
   float* att_part;     // [n_req][nh][n_split][8][P]
   float* att_ml;       // [n_req][nh][n_split][8][2]
   void* o_in;          // [n_req*8][dq] storage dtype
+  int32_t* counters;   // [n_req*nh + n_req], zero on entry
   int32_t n_tiles;     // commit / readout tiles per (request, head)
   int32_t n_split;     // attention splits per (request, head), the last one holds the block keys
   int32_t do_commit;   // commit rows present
   int32_t do_draft;    // block rows present
 };
 int round_tiles(const Shape& sh);
-// k_round, then k_round_merge (draft) or the count update (commit only).
 hipError_t launch_round(int dtype, const Shape& sh, const RoundArgs& a, const ReqTable& rt, hipStream_t s);
 
 // Prefill ring append: the last m_i = min(n_i, W) rows of request i go to slots

@@ -53,7 +53,7 @@ k_proj_small(RowSrc xs, int M, int K, const T* __restrict__ W, int Nout, Epi epi
   constexpr int KE = Mfma16<T>::KE;
   constexpr int VN = Vec16<T>::n;
   constexpr int U = 4;                // MFMAs per slab
-  constexpr int LANE_K = U * KE;      // contiguous k values a lane covers per slab
+  constexpr int LANE_K = U * KE;      // k values a lane covers per slab
   constexpr int NV = LANE_K / VN;     // 16-byte loads per lane per slab and operand row
   constexpr int SLAB = 4 * LANE_K;    // k per slab
   typedef typename Vec16<T>::type V;
@@ -62,6 +62,8 @@ k_proj_small(RowSrc xs, int M, int K, const T* __restrict__ W, int Nout, Epi epi
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i = lane & 15, g = lane >> 4;
   const int f0 = blockIdx.x * 16;
+  if (epi.zero && blockIdx.x == 0 && blockIdx.y == 0)
+    for (int z = threadIdx.x; z < epi.n_zero; z += NW * 64) epi.zero[z] = 0;
   const int m_base = blockIdx.y * 16 * MT;
 
   const T* wrow = W + (int64_t)min(f0 + i, Nout - 1) * K;
@@ -78,17 +80,19 @@ k_proj_small(RowSrc xs, int M, int K, const T* __restrict__ W, int Nout, Epi epi
 
   // A wave takes slabs wave, wave + NW, ...; it loads SB of them before it multiplies, so a whole
   // row of weights is in flight at once (same order of MFMAs as one slab at a time).
-  constexpr int SB = MT == 1 ? 4 : (MT == 2 ? 2 : 1);
+  constexpr int SB = MT == 1 ? 3 : 1;  // at most 128 VGPRs: two 8-wave workgroups per CU
   const int nslab = (K + SLAB - 1) / SLAB;
   for (int s0 = wave; s0 < nslab; s0 += SB * NW) {
     V wv[SB][NV];
     V xv[SB][MT][NV];
 #pragma unroll
     for (int sb = 0; sb < SB; ++sb) {
-      const int kb = (s0 + sb * NW) * SLAB + g * LANE_K;
+      // load v of lane group g: k = slab start + 4 VN v + VN g, so the four groups read 64
+      // contiguous bytes of every row (MFMA u contracts the 4 VN k values of load u)
+      const int kb = (s0 + sb * NW) * SLAB + g * VN;
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
-        const int k = kb + v * VN;
+        const int k = kb + v * 4 * VN;
         const bool ok = k + VN <= K;
         wv[sb][v] = ok ? ld_vec<T>(wrow + k) : V{};
 #pragma unroll
@@ -171,6 +175,8 @@ k_gemm_bf16(RowSrc xs, int M, int K, const bf16* __restrict__ W, int Nout, Epi e
   const int i = lane & 15, g = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;
   const int n0 = blockIdx.x * GB_N, m0 = blockIdx.y * GB_M;
+  if (epi.zero && blockIdx.x == 0 && blockIdx.y == 0)
+    for (int z = threadIdx.x; z < epi.n_zero; z += 256) epi.zero[z] = 0;
 
   f32x4 acc[4][4];
 #pragma unroll

@@ -23,8 +23,7 @@ __device__ __forceinline__ T* ring_ptr(char* pool, const Shape& sh, int slot, ui
 }
 
 // ---------------------------------------------------------------------------------------------
-// One round in two launches.  k_round: workgroup roles per (request r, head h), in block-index
-// order:
+// One round, one launch.  Workgroup roles per (request r, head h), in block-index order:
 //   tiles  [0, n_tiles):   rows p0 .. p0 + rows_wg of H: fold the round's committed rows in (one
 //                          read-modify-write), memory readout of the block rows from the updated
 //                          rows, and (tile 0) the ring append of the committed (k, v);
@@ -32,14 +31,52 @@ __device__ __forceinline__ T* ring_ptr(char* pool, const Shape& sh, int slot, ui
 //                          over the block rows themselves), written as (max, sum, output) partials.
 // A split sees the ring as it is after this round's append without waiting for it: a slot that
 // the append overwrites is read from the projection instead (rounded to the storage dtype, as the
-// ring stores it).  k_round_merge then merges the splits per (r, h), adds the readout, writes the
-// output projection's input and advances the committed count.  (Merging inside k_round by its
-// last workgroup per head needs a device-scope release per workgroup, which on this chip writes
-// back the L2 and cost more than the extra launch.)
+// ring stores it).  The last workgroup of (r, h) to finish (a counter) merges the splits, adds the
+// readout and writes the output projection's input; the last head of a request advances the
+// request's committed count.  The counters are cleared by the round's input projection.
 
+// Staging: a job copies n chunks (16 or 4 bytes) from global memory, chunk i from src(i) to
+// dst + i chunks in LDS, with direct global -> LDS loads: no registers and no wait between
+// loads, so every job of a workgroup is one memory round trip.  A wave issues chunks
+// [64 k, 64 k + 64) for k = wave, wave + 4, ...; LDS regions are sized in whole 1 KiB (16-byte
+// jobs) or 256-byte (4-byte jobs) units so a wave's instruction stays inside its region.
+template <typename F>
+__device__ __forceinline__ void stage16(int n, void* dst, F src) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int base = wave * 64; base < n; base += RT)
+    if (base + lane < n) lds_dma16(src(base + lane), static_cast<char*>(dst) + 16 * base);
+}
+template <typename F>
+__device__ __forceinline__ void stage4(int n, void* dst, F src) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int base = wave * 64; base < n; base += RT)
+    if (base + lane < n) lds_dma4(src(base + lane), static_cast<char*>(dst) + 4 * base);
+}
+__host__ __device__ constexpr int up1k(int bytes) { return (bytes + 1023) / 1024 * 1024; }
+
+// Results another workgroup of the same launch merges are stored device-coherent (written through
+// to the level all XCDs share) and read the same way, so the hand-over needs no L2 write-back or
+// invalidation: the writer waits for its stores to complete before it counts itself in.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+constexpr int AUX_DEV = 16;  // cache policy of a device-coherent load (sc1)
+template <typename F>
+__device__ __forceinline__ void stage16_dev(int n, void* dst, F src) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int base = wave * 64; base < n; base += RT)
+    if (base + lane < n)
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(src(base + lane)),
+                                       (void __attribute__((address_space(3)))*)(static_cast<char*>(dst) + 16 * base),
+                                       16, 0, AUX_DEV);
+}
+
+// Tile LDS (bytes): B of the committed rows [RMAXC][N] f32 | C of the block rows [RB][N] f32 |
+// x (= v) of the committed rows [RMAXC][rows_wg] f32 | v of the block rows [RB][rows_wg] f32 |
+// weights [RMAXC + 4] | readout partials [RB][RT].
 template <typename T>
 __device__ __forceinline__ void round_tile(const Shape& sh, const RoundArgs& a, const ReqTable& rt, int r, int h,
-                                           int tile, float* smem) {
+                                           int tile, char* smem) {
   const int nh = sh.nh, P = sh.P, N = sh.N;
   const int tpr = N / 4;           // threads per H row (4 columns each)
   const int rows_wg = RT / tpr;    // H rows per tile
@@ -53,41 +90,27 @@ __device__ __forceinline__ void round_tile(const Shape& sh, const RoundArgs& a, 
   const int64_t crow0 = rt.row0[r];
   const int64_t brow0 = a.blk_row0 + (int64_t)r * RB;
   const int64_t ld = a.ld;
-  float* Bl = smem;                     // [RMAXC][N]  B of the committed rows
-  float* Cl = Bl + RMAXC * N;           // [RB][N]     C of the block rows
-  float* xv = Cl + RB * N;              // [RMAXC][rows_wg] x (= v) of the committed rows
-  float* vb = xv + RMAXC * rows_wg;     // [RB][rows_wg]    v of the block rows
-  float* wl = vb + RB * rows_wg;        // [RMAXC] weights, then the total decay
-  float* red = wl + RMAXC + 4;          // [RB][RT]
+  float* Bl = reinterpret_cast<float*>(smem);
+  float* Cl = reinterpret_cast<float*>(smem + up1k(RMAXC * N * 4));
+  float* xv = reinterpret_cast<float*>(reinterpret_cast<char*>(Cl) + up1k(RB * N * 4));
+  float* vb = reinterpret_cast<float*>(reinterpret_cast<char*>(xv) + up1k(RMAXC * rows_wg * 4));
+  float* wl = reinterpret_cast<float*>(reinterpret_cast<char*>(vb) + up1k(RB * rows_wg * 4));
+  float* red = wl + RMAXC + 4;
 
   // every load first (one round trip), then the arithmetic
   float* Hh = h_ptr(a.state_pool, sh, slot, h);
   f32x4 hv = f32x4{0.f, 0.f, 0.f, 0.f};
   if (active) hv = *reinterpret_cast<const f32x4*>(Hh + (int64_t)p * N + 4 * c4);
-  for (int idx = t; idx < nrows * tpr; idx += RT) {
-    const int tt = idx / tpr, c = idx % tpr;
-    *reinterpret_cast<f32x4*>(Bl + tt * N + 4 * c) =
-        *reinterpret_cast<const f32x4*>(a.proj + (crow0 + tt) * ld + sh.off_b + grp * N + 4 * c);
+  const float raw = t < nrows ? a.proj[(crow0 + t) * ld + sh.off_dt + h] : 0.f;
+  stage16(nrows * tpr, Bl, [&](int i) { return a.proj + (crow0 + i / tpr) * ld + sh.off_b + grp * N + 4 * (i % tpr); });
+  stage4(nrows * rows_wg, xv, [&](int i) { return a.proj + (crow0 + i / rows_wg) * ld + sh.off_v + h * P + p0 + i % rows_wg; });
+  if (a.do_draft) {
+    stage16(RB * tpr, Cl, [&](int i) { return a.proj + (brow0 + i / tpr) * ld + sh.off_c + grp * N + 4 * (i % tpr); });
+    stage4(RB * rows_wg, vb, [&](int i) { return a.proj + (brow0 + i / rows_wg) * ld + sh.off_v + h * P + p0 + i % rows_wg; });
   }
-  if (a.do_draft)
-    for (int idx = t; idx < RB * tpr; idx += RT) {
-      const int j = idx / tpr, c = idx % tpr;
-      *reinterpret_cast<f32x4*>(Cl + j * N + 4 * c) =
-          *reinterpret_cast<const f32x4*>(a.proj + (brow0 + j) * ld + sh.off_c + grp * N + 4 * c);
-    }
-  for (int idx = t; idx < nrows * rows_wg; idx += RT) {
-    const int tt = idx / rows_wg, pp = p0 + idx % rows_wg;
-    xv[idx] = pp < P ? a.proj[(crow0 + tt) * ld + sh.off_v + h * P + pp] : 0.f;
-  }
-  if (a.do_draft)
-    for (int idx = t; idx < RB * rows_wg; idx += RT) {
-      const int j = idx / rows_wg, pp = p0 + idx % rows_wg;
-      vb[idx] = pp < P ? a.proj[(brow0 + j) * ld + sh.off_v + h * P + pp] : 0.f;
-    }
   if (t < 64) {
     // weights relative to the last committed row: w_t = dt_t exp(sum_{tau > t} dt_tau A), and
     // the decay exp(sum_t dt_t A) of the old state; lane t < nrows holds row t
-    const float raw = t < nrows ? a.proj[(crow0 + t) * ld + sh.off_dt + h] : 0.f;
     const float A = -expf(a.a_log[h]);
     const float dt = t < nrows ? softplus_f(raw + a.dt_bias[h]) : 0.f;
     const float ell = dt * A;
@@ -100,6 +123,7 @@ __device__ __forceinline__ void round_tile(const Shape& sh, const RoundArgs& a, 
     if (t < nrows) wl[t] = dt * expf(inc - ell);
     if (t == 0) wl[RMAXC] = expf(inc);
   }
+  vm_wait<0>();
   __syncthreads();
 
   if (active && nrows > 0) {
@@ -115,12 +139,12 @@ __device__ __forceinline__ void round_tile(const Shape& sh, const RoundArgs& a, 
   if (a.do_draft) {
 #pragma unroll
     for (int j = 0; j < RB; ++j) {
-      float s = 0.f;
+      float sum = 0.f;
       if (active) {
         const f32x4 c = *reinterpret_cast<const f32x4*>(Cl + j * N + 4 * c4);
-        s = hv[0] * c[0] + hv[1] * c[1] + hv[2] * c[2] + hv[3] * c[3];
+        sum = hv[0] * c[0] + hv[1] * c[1] + hv[2] * c[2] + hv[3] * c[3];
       }
-      red[j * RT + t] = s;
+      red[j * RT + t] = sum;
     }
     __syncthreads();
     const float D = a.d_skip[h];
@@ -128,9 +152,9 @@ __device__ __forceinline__ void round_tile(const Shape& sh, const RoundArgs& a, 
       const int j = idx / rows_wg, pr = idx % rows_wg;
       const int pp = p0 + pr;
       if (pp >= P) continue;
-      float s = 0.f;
-      for (int c = 0; c < tpr; ++c) s += red[j * RT + pr * tpr + c];
-      a.mem[(((int64_t)r * RB + j) * nh + h) * P + pp] = s + D * vb[idx];
+      float sum = 0.f;
+      for (int c = 0; c < tpr; ++c) sum += red[j * RT + pr * tpr + c];
+      st_dev(a.mem + (((int64_t)r * RB + j) * nh + h) * P + pp, sum + D * vb[idx]);
     }
   }
 
@@ -150,177 +174,273 @@ __device__ __forceinline__ void round_tile(const Shape& sh, const RoundArgs& a, 
   }
 }
 
+// Four consecutive elements (8-byte aligned for bf16, 16-byte for fp32) as fp32.
+__device__ __forceinline__ f32x4 ld4f(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ f32x4 ld4f(const bf16* p) {
+  typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+  const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+  return f32x4{static_cast<float>(v[0]), static_cast<float>(v[1]), static_cast<float>(v[2]), static_cast<float>(v[3])};
+}
+
+// Scores and outputs of one split on fp32 MFMAs (16x16x4): keys from K (row stride P, up to 64
+// rows), values from V, queries qs [RB][P] f32.  Wave w computes S^T for keys 16 w .. 16 w + 15
+// against the 8 queries (padded to 16 columns); lane (li, lg) supplies, for instruction j of a
+// group of four, dimension p0 + 4 lg + j of key 16 w + li and of query li, so one 4-element load
+// of each operand feeds four instructions.  Softmax over the 64 keys meets in LDS; the
+// probabilities go to LDS and a second set of MFMAs forms P . V with wave w on the 16-column
+// tiles w, w + 4, ... of the output.  Keys at or past nk are masked (their rows may hold
+// anything: their scores are discarded and their values are multiplied by nothing).
+template <typename KT>
+__device__ __forceinline__ void attn_split(const Shape& sh, int nk, bool blk, const float* qs, const KT* K,
+                                           const KT* V, float* pl, float* red, float* op, float* ml) {
+  const int P = sh.P, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const float scale = rsqrtf((float)P);
+  // ---- scores S^T[key][q]
+  f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int krow = 16 * wave + li;
+  if (16 * wave < nk) {
+#pragma unroll 4
+    for (int p0 = 0; p0 < P; p0 += 16) {
+      const f32x4 kv = ld4f(K + krow * P + p0 + 4 * lg);
+      f32x4 qv = *reinterpret_cast<const f32x4*>(qs + li * P + p0 + 4 * lg);  // rows >= RB: masked
+      if (li >= RB) qv = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s = Mfma16<float>::mma(kv[j], qv[j], s);
+    }
+  }
+  // lane (li, lg) register rr: key 16 w + 4 lg + rr, query li
+  float e[4];
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int key = 16 * wave + 4 * lg + rr;
+    bool ok = key < nk && li < RB;
+    if (blk && !sh.cross && key != li) ok = false;
+    e[rr] = ok ? s[rr] * scale : -INFINITY;
+    mloc = fmaxf(mloc, e[rr]);
+  }
+  mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+  mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+  if (lg == 0) red[wave * 16 + li] = mloc;
+  __syncthreads();
+  float m = -INFINITY;
+#pragma unroll
+  for (int w2 = 0; w2 < 4; ++w2) m = fmaxf(m, red[w2 * 16 + li]);
+  float lsum = 0.f;
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    e[rr] = e[rr] == -INFINITY ? 0.f : expf(e[rr] - m);
+    lsum += e[rr];
+    pl[li * ATT_KS + 16 * wave + 4 * lg + rr] = e[rr];
+  }
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  if (lg == 0) red[64 + wave * 16 + li] = lsum;
+  __syncthreads();
+  if (wave == 0 && lg == 0 && li < RB) {
+    st_dev(ml + 2 * li, m);
+    st_dev(ml + 2 * li + 1, red[64 + li] + red[64 + 16 + li] + red[64 + 32 + li] + red[64 + 48 + li]);
+  }
+  // ---- O[q][p] = sum_key pl[q][key] V[key][p]
+  const int nks = (nk + 3) / 4 * 4;
+  for (int pt = wave; pt * 16 < P; pt += 4) {
+    f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+    for (int k0 = 0; k0 < nks; k0 += 16) {
+      const f32x4 pa = *reinterpret_cast<const f32x4*>(pl + li * ATT_KS + k0 + 4 * lg);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int key = k0 + 4 * lg + j;
+        const float vv = key < nk ? to_f32(V[key * P + pt * 16 + li]) : 0.f;
+        o = Mfma16<float>::mma(pa[j], vv, o);
+      }
+    }
+    // lane (li, lg) register rr: query 4 lg + rr, column pt * 16 + li
+    if (lg < 2)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) st_dev(op + (4 * lg + rr) * P + pt * 16 + li, o[rr]);
+  }
+}
+
+// Attention LDS (bytes): ring K, V of the split [ATT_KS][P] storage dtype | q [RB][P] f32 |
+// k, v of the round's committed rows (or of the block rows) [RB][P] f32 each | probabilities
+// [16][ATT_KS] | softmax scratch [128].
 template <typename T>
 __device__ __forceinline__ void round_attn(const Shape& sh, const RoundArgs& a, const ReqTable& rt, int r, int h,
-                                           int sp, float* smem) {
+                                           int sp, char* smem) {
   constexpr int VN = Vec16<T>::n;
-  typedef typename Vec16<T>::type Vv;
   const int nh = sh.nh, P = sh.P, W = sh.W;
-  const int PK = P + 1;  // key rows padded so consecutive keys fall in different banks
-  float* qs = smem;                   // [RB][P]
-  float* ks = qs + RB * P;            // [ATT_KS][P + 1]
-  float* vs = ks + ATT_KS * PK;       // [ATT_KS][P]
-  float* pl = vs + ATT_KS * P;        // [RB][ATT_KS]
+  T* kst = reinterpret_cast<T*>(smem);
+  T* vst = reinterpret_cast<T*>(smem + up1k(ATT_KS * P * (int)sizeof(T)));
+  float* qs = reinterpret_cast<float*>(reinterpret_cast<char*>(vst) + up1k(ATT_KS * P * (int)sizeof(T)));
+  float* nkf = reinterpret_cast<float*>(reinterpret_cast<char*>(qs) + up1k(RB * P * 4));
+  float* nvf = reinterpret_cast<float*>(reinterpret_cast<char*>(nkf) + up1k(RB * P * 4));
+  float* pl = reinterpret_cast<float*>(reinterpret_cast<char*>(nvf) + up1k(RB * P * 4));
+  float* red = pl + 16 * ATT_KS;
+  __shared__ int64_t s_count;
   const int slot = rt.slot[r];
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x;
   const int64_t ld = a.ld;
   const int64_t brow0 = a.blk_row0 + (int64_t)r * RB;
   const bool blk = sp == a.n_split - 1;
   const int nrows = a.do_commit ? rt.row0[r + 1] - rt.row0[r] : 0;
   const int64_t crow0 = rt.row0[r];
+  const int k0 = sp * ATT_KS;
+  const int P4 = P / 4;
 
-  const float scale = rsqrtf((float)P);
-  for (int idx = t; idx < RB * P / 4; idx += RT) {
-    const int j = 4 * idx / P, pp = 4 * idx % P;
-    *reinterpret_cast<f32x4*>(qs + j * P + pp) =
-        *reinterpret_cast<const f32x4*>(a.proj + (brow0 + j) * ld + sh.off_q + h * P + pp) * scale;
-  }
-  int nk;
+  // Every load is independent of the committed count, so all go out together: the count, q, the
+  // split's ring slots (always inside the ring), and the k, v of the round's committed rows (they
+  // replace the slots this round's append overwrites) or of the block rows.
+  if (!blk && t == 0) s_count = *count_ptr(a.state_pool, sh, slot);
+  stage16(RB * P4, qs, [&](int i) { return a.proj + (brow0 + i / P4) * ld + sh.off_q + h * P + 4 * (i % P4); });
   if (blk) {
-    nk = RB;
-    for (int idx = t; idx < RB * P / 4; idx += RT) {
-      const int j = 4 * idx / P, pp = 4 * idx % P;
-      const f32x4 kk = *reinterpret_cast<const f32x4*>(a.proj + (brow0 + j) * ld + sh.off_k + h * P + pp);
-      const f32x4 vv = *reinterpret_cast<const f32x4*>(a.proj + (brow0 + j) * ld + sh.off_v + h * P + pp);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ks[j * PK + pp + e] = kk[e];
-      *reinterpret_cast<f32x4*>(vs + j * P + pp) = vv;
-    }
+    stage16(RB * P4, nkf, [&](int i) { return a.proj + (brow0 + i / P4) * ld + sh.off_k + h * P + 4 * (i % P4); });
+    stage16(RB * P4, nvf, [&](int i) { return a.proj + (brow0 + i / P4) * ld + sh.off_v + h * P + 4 * (i % P4); });
   } else {
-    // ring slots k0 .. k0 + nk - 1 of the window after this round's append
-    const int64_t count = *count_ptr(a.state_pool, sh, slot);
-    const int64_t tot = count + nrows;
-    const int valid = (int)(tot < W ? tot : W);
-    const int k0 = sp * ATT_KS;
-    nk = valid - k0;
-    nk = nk < 0 ? 0 : (nk > ATT_KS ? ATT_KS : nk);
-    const int m = nrows < W ? nrows : W;             // rows of this round that land in the ring
-    const int lead = (int)((count + nrows - m) % W);  // slot of the first of them
-    const T* K = ring_ptr<T>(a.state_pool, sh, slot, sh.st_k, h);
-    const T* V = ring_ptr<T>(a.state_pool, sh, slot, sh.st_v, h);
-    const int CH = P / VN;  // 16-byte chunks per key row
-    for (int idx = t; idx < nk * CH; idx += RT) {
-      const int key = idx / CH, c = idx % CH;
-      const int s = k0 + key;
-      const int jn = (s - lead + W) % W;  // index among the landing rows, if this slot is one
-      float kf[VN], vf[VN];
-      if (jn < m) {
-        const int64_t row = crow0 + (nrows - m) + jn;
-#pragma unroll
-        for (int e = 0; e < VN; ++e) {
-          kf[e] = to_f32(from_f32<T>(a.proj[row * ld + sh.off_k + h * P + c * VN + e]));
-          vf[e] = to_f32(from_f32<T>(a.proj[row * ld + sh.off_v + h * P + c * VN + e]));
-        }
-      } else {
-        const Vv kv = *reinterpret_cast<const Vv*>(K + (int64_t)s * P + c * VN);
-        const Vv vv = *reinterpret_cast<const Vv*>(V + (int64_t)s * P + c * VN);
-#pragma unroll
-        for (int e = 0; e < VN; ++e) {
-          kf[e] = to_f32(kv[e]);
-          vf[e] = to_f32(vv[e]);
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < VN; ++e) {
-        ks[key * PK + c * VN + e] = kf[e];
-        vs[key * P + c * VN + e] = vf[e];
-      }
-    }
+    const int nslots = W - k0 < ATT_KS ? W - k0 : ATT_KS;
+    const T* K = ring_ptr<T>(a.state_pool, sh, slot, sh.st_k, h) + (int64_t)k0 * P;
+    const T* V = ring_ptr<T>(a.state_pool, sh, slot, sh.st_v, h) + (int64_t)k0 * P;
+    stage16(nslots * P / VN, kst, [&](int i) { return K + i * VN; });
+    stage16(nslots * P / VN, vst, [&](int i) { return V + i * VN; });
+    stage16(nrows * P4, nkf, [&](int i) { return a.proj + (crow0 + i / P4) * ld + sh.off_k + h * P + 4 * (i % P4); });
+    stage16(nrows * P4, nvf, [&](int i) { return a.proj + (crow0 + i / P4) * ld + sh.off_v + h * P + 4 * (i % P4); });
   }
+  vm_wait<0>();
+  __syncthreads();
+
   float* op = a.att_part + ((((int64_t)r * nh + h) * a.n_split + sp) * RB) * P;
   float* ml = a.att_ml + ((((int64_t)r * nh + h) * a.n_split + sp) * RB) * 2;
+  if (blk) {
+    attn_split(sh, RB, true, qs, nkf, nvf, pl, red, op, ml);
+    return;
+  }
+  const int64_t count = s_count;
+  const int64_t tot = count + nrows;
+  const int valid = (int)(tot < W ? tot : W);
+  int nk = valid - k0;
+  nk = nk < 0 ? 0 : (nk > ATT_KS ? ATT_KS : nk);
   if (nk == 0) {
-    for (int idx = t; idx < RB * P; idx += RT) op[idx] = 0.f;
+    for (int idx = t; idx < RB * P; idx += RT) st_dev(op + idx, 0.f);
     if (t < RB) {
-      ml[2 * t] = -INFINITY;
-      ml[2 * t + 1] = 0.f;
+      st_dev(ml + 2 * t, -INFINITY);
+      st_dev(ml + 2 * t + 1, 0.f);
     }
     return;
   }
-  __syncthreads();
-
-  // scores: lane = key, wave w handles block rows w and w + 4
-  const int key = lane;
-  float sc[2];
-#pragma unroll
-  for (int q2 = 0; q2 < 2; ++q2) {
-    const int j = wave + 4 * q2;
-    float acc = 0.f;
-    if (key < nk)
-      for (int pp = 0; pp < P; ++pp) acc += qs[j * P + pp] * ks[key * PK + pp];
-    bool ok = key < nk;
-    if (blk && !sh.cross && key != j) ok = false;
-    sc[q2] = ok ? acc : -INFINITY;
-  }
-#pragma unroll
-  for (int q2 = 0; q2 < 2; ++q2) {
-    const int j = wave + 4 * q2;
-    const float mx = wave_max(sc[q2]);
-    const float e = sc[q2] == -INFINITY ? 0.f : expf(sc[q2] - mx);
-    const float l = wave_sum(e);
-    pl[j * ATT_KS + key] = e;
-    if (lane == 0) {
-      ml[2 * j] = mx;
-      ml[2 * j + 1] = l;
+  if (nrows > 0) {
+    // the slots this round's append overwrites take its rows, rounded as the ring stores them:
+    // slot (count + j) mod W holds row j for the last m = min(nrows, W) rows
+    const int m = nrows < W ? nrows : W;
+    const int lead = (int)((count + nrows - m) % W);
+    for (int idx = t; idx < m * P; idx += RT) {
+      const int jn = idx / P, pp = idx % P;
+      const int key = (lead + jn) % W - k0;
+      if (key >= 0 && key < nk) {
+        kst[key * P + pp] = from_f32<T>(nkf[(nrows - m + jn) * P + pp]);
+        vst[key * P + pp] = from_f32<T>(nvf[(nrows - m + jn) * P + pp]);
+      }
     }
+    __syncthreads();
   }
-  __syncthreads();
-  for (int idx = t; idx < RB * P; idx += RT) {
-    const int j = idx / P, pp = idx % P;
-    float acc = 0.f;
-    for (int k2 = 0; k2 < nk; ++k2) acc += pl[j * ATT_KS + k2] * vs[k2 * P + pp];
-    op[idx] = acc;
-  }
+  attn_split(sh, nk, false, qs, kst, vst, pl, red, op, ml);
 }
 
+// Merge of one (request, head): the partials of MCH splits at a time are staged in LDS together
+// with the (max, sum) pairs and the readout (one round trip); per (split, row) factors
+// exp(max_s - max) are formed once, in parallel, then every output sums its splits.
+// Merge LDS (bytes): (max, sum) [ns][RB][2] | factors [ns][RB] | row maxima and sums [2 RB] |
+// readout [RB][P] | partials [MCH][RB][P].
+constexpr int MCH = 16;
 template <typename T>
-__device__ __forceinline__ void round_merge(const Shape& sh, const RoundArgs& a, int r, int h, float* smem) {
+__device__ __forceinline__ void round_merge(const Shape& sh, const RoundArgs& a, int r, int h, char* smem) {
   const int nh = sh.nh, P = sh.P, t = threadIdx.x;
   const int ns = a.n_split;
+  const int P4 = P / 4;
   const float* ml = a.att_ml + (((int64_t)r * nh + h) * ns) * RB * 2;
   const float* op = a.att_part + (((int64_t)r * nh + h) * ns) * RB * P;
-  float* sml = smem;  // [ns][RB][2]
-  for (int idx = t; idx < ns * RB * 2; idx += RT) sml[idx] = ml[idx];
-  __syncthreads();
-  T* out = static_cast<T*>(a.o_in);
-  for (int idx = t; idx < RB * P; idx += RT) {
-    const int j = idx / P, pp = idx % P;
-    float m = -INFINITY;
-    for (int s = 0; s < ns; ++s) m = fmaxf(m, sml[(s * RB + j) * 2]);
-    float l = 0.f, o = 0.f;
-#pragma unroll 4
-    for (int s = 0; s < ns; ++s) {
-      const float ms = sml[(s * RB + j) * 2];
-      const float f = ms == -INFINITY ? 0.f : expf(ms - m);
-      l += f * sml[(s * RB + j) * 2 + 1];
-      o += f * op[((int64_t)s * RB + j) * P + pp];
+  float* sml = reinterpret_cast<float*>(smem);
+  float* fac = reinterpret_cast<float*>(smem + up1k(ns * RB * 2 * 4));
+  float* rowm = reinterpret_cast<float*>(reinterpret_cast<char*>(fac) + up1k(ns * RB * 4));
+  float* memv = rowm + 256;
+  float* sop = reinterpret_cast<float*>(reinterpret_cast<char*>(memv) + up1k(RB * P * 4));
+  constexpr int EPT = 8;  // outputs per thread: RB * P <= 8 * RT for P <= 256
+  float acc[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) acc[e] = 0.f;
+  stage16_dev(ns * RB * 2 / 4, sml, [&](int i) { return ml + 4 * i; });
+  stage16_dev(RB * P4, memv, [&](int i) { return a.mem + (((int64_t)r * RB + i / P4) * nh + h) * P + 4 * (i % P4); });
+  for (int s0 = 0; s0 < ns; s0 += MCH) {
+    const int nc = ns - s0 < MCH ? ns - s0 : MCH;
+    stage16_dev(nc * RB * P4, sop, [&](int i) { return op + (int64_t)s0 * RB * P + 4 * i; });
+    vm_wait<0>();
+    __syncthreads();
+    if (s0 == 0) {
+      if (t < RB) {
+        float m = -INFINITY;
+        for (int s = 0; s < ns; ++s) m = fmaxf(m, sml[(s * RB + t) * 2]);
+        rowm[t] = m;
+      }
+      __syncthreads();
+      for (int i = t; i < ns * RB; i += RT) {
+        const float ms = sml[2 * i];
+        fac[i] = ms == -INFINITY ? 0.f : expf(ms - rowm[i % RB]);
+      }
+      __syncthreads();
+      if (t < RB) {
+        float l = 0.f;
+        for (int s = 0; s < ns; ++s) l += fac[s * RB + t] * sml[(s * RB + t) * 2 + 1];
+        rowm[RB + t] = l;
+      }
     }
-    const float mem = a.mem[(((int64_t)r * RB + j) * nh + h) * P + pp];
-    out[((int64_t)r * RB + j) * sh.dq + h * P + pp] = from_f32<T>(o / l + mem);
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int idx = t + e * RT;
+      if (idx >= RB * P) continue;
+      const int j = idx / P;
+      float sum = 0.f;
+#pragma unroll 4
+      for (int s = 0; s < nc; ++s) sum += fac[(s0 + s) * RB + j] * sop[s * RB * P + idx];
+      acc[e] += sum;
+    }
+    __syncthreads();  // sop is refilled by the next chunk; rowm sums are complete
+  }
+  T* out = static_cast<T*>(a.o_in);
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int idx = t + e * RT;
+    if (idx >= RB * P) continue;
+    const int j = idx / P, pp = idx % P;
+    out[((int64_t)r * RB + j) * sh.dq + h * P + pp] = from_f32<T>(acc[e] / rowm[RB + j] + memv[idx]);
   }
 }
 
 template <typename T>
 __global__ void __launch_bounds__(RT) k_round(Shape sh, RoundArgs a, ReqTable rt) {
-  extern __shared__ __attribute__((aligned(16))) float dsm[];
+  extern __shared__ __attribute__((aligned(16))) char dsm[];
+  __shared__ int s_last;
+  const int nh = sh.nh;
   const int per = a.n_tiles + a.n_split;
   const int rh = blockIdx.x / per, role = blockIdx.x % per;
-  const int r = rh / sh.nh, h = rh % sh.nh;
+  const int r = rh / nh, h = rh % nh;
   if (role < a.n_tiles)
     round_tile<T>(sh, a, rt, r, h, role, dsm);
   else
     round_attn<T>(sh, a, rt, r, h, role - a.n_tiles, dsm);
-}
 
-// Per (request, head): merge the attention splits, add the readout, write the output
-// projection's input; head 0 then advances the request's committed count (every reader of the
-// count ran in the previous launch).
-template <typename T>
-__global__ void __launch_bounds__(RT) k_round_merge(Shape sh, RoundArgs a, ReqTable rt) {
-  extern __shared__ __attribute__((aligned(16))) float dsm[];
-  const int r = blockIdx.x / sh.nh, h = blockIdx.x % sh.nh;
-  round_merge<T>(sh, a, r, h, dsm);
-  if (h == 0 && threadIdx.x == 0 && a.do_commit)
+  // count this workgroup in once its stores are complete; the last one of (r, h) merges
+  vm_wait<0>();
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(a.counters + rh, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == per - 1;
+  __syncthreads();
+  if (!s_last) return;
+  if (a.do_draft) round_merge<T>(sh, a, r, h, dsm);
+  if (!a.do_commit) return;
+  // the last (r, h) of the request to finish advances its committed count: every workgroup of the
+  // request has read the count by then
+  if (threadIdx.x == 0 &&
+      __hip_atomic_fetch_add(a.counters + rt.n_req * nh + r, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nh - 1)
     *count_ptr(a.state_pool, sh, rt.slot[r]) += rt.row0[r + 1] - rt.row0[r];
 }
 
@@ -374,18 +494,21 @@ __global__ void k_reset_states(char* pool, Shape sh, ReqTable rt) {
 int round_rows_per_tile(const Shape& sh) { return RT / (sh.N / 4); }
 int round_tiles(const Shape& sh) { return (sh.P + round_rows_per_tile(sh) - 1) / round_rows_per_tile(sh); }
 
-size_t round_lds_bytes(const Shape& sh, int n_split) {
-  const size_t rw = round_rows_per_tile(sh);
-  const size_t tile = sizeof(float) * ((size_t)(RMAXC + RB) * sh.N + (RMAXC + RB) * rw + RMAXC + 4 + RB * RT);
-  const size_t attn = sizeof(float) * ((size_t)RB * sh.P + (size_t)ATT_KS * (sh.P + 1) + (size_t)ATT_KS * sh.P + RB * ATT_KS);
-  const size_t merge = sizeof(float) * (size_t)n_split * RB * 2;
+size_t round_lds_bytes(const Shape& sh, int esz, int n_split) {
+  const int rw = round_rows_per_tile(sh);
+  const size_t tile = (size_t)up1k(RMAXC * sh.N * 4) + up1k(RB * sh.N * 4) + up1k(RMAXC * rw * 4) + up1k(RB * rw * 4) +
+                      4 * (RMAXC + 4 + RB * RT);
+  const size_t attn = (size_t)2 * up1k(ATT_KS * sh.P * esz) + 3 * up1k(RB * sh.P * 4) + 4 * (16 * ATT_KS + 128);
+  const size_t merge = n_split ? (size_t)up1k(n_split * RB * 2 * 4) + up1k(n_split * RB * 4) + 4 * 256 +
+                                     up1k(RB * sh.P * 4) + up1k(MCH * RB * sh.P * 4)
+                               : 0;
   size_t m = tile > attn ? tile : attn;
   return m > merge ? m : merge;
 }
 
 hipError_t launch_round(int dtype, const Shape& sh, const RoundArgs& a, const ReqTable& rt, hipStream_t s) {
   const int per = a.n_tiles + a.n_split;
-  const size_t lds = round_lds_bytes(sh, a.n_split);
+  const size_t lds = round_lds_bytes(sh, dtype == HYF_BF16 ? 2 : 4, a.do_draft ? a.n_split : 0);
   if (lds > 65536) {
     // Above 64 KiB of dynamic LDS the kernel has to opt in (gfx950 has 160 KiB per workgroup).
     // Done once per process with the largest size any shape needs, so later calls (possibly under
@@ -394,11 +517,11 @@ hipError_t launch_round(int dtype, const Shape& sh, const RoundArgs& a, const Re
     static hipError_t set_err = hipSuccess;
     std::call_once(once, [] {
       const int mx = 160 * 1024;
-      const void* fns[4] = {reinterpret_cast<const void*>(k_round<bf16>), reinterpret_cast<const void*>(k_round<float>),
-                            reinterpret_cast<const void*>(k_round_merge<bf16>),
-                            reinterpret_cast<const void*>(k_round_merge<float>)};
-      for (const void* f : fns)
-        if (set_err == hipSuccess) set_err = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, mx);
+      set_err = hipFuncSetAttribute(reinterpret_cast<const void*>(k_round<bf16>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, mx);
+      if (set_err == hipSuccess)
+        set_err = hipFuncSetAttribute(reinterpret_cast<const void*>(k_round<float>),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, mx);
     });
     if (set_err != hipSuccess) return set_err;
   }
@@ -407,15 +530,6 @@ hipError_t launch_round(int dtype, const Shape& sh, const RoundArgs& a, const Re
     hipLaunchKernelGGL(k_round<bf16>, grid, dim3(RT), lds, s, sh, a, rt);
   else
     hipLaunchKernelGGL(k_round<float>, grid, dim3(RT), lds, s, sh, a, rt);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (!a.do_draft) return a.do_commit ? launch_bump_counts(a.state_pool, sh, rt, s) : hipSuccess;
-  const size_t mlds = sizeof(float) * (size_t)a.n_split * RB * 2;
-  dim3 mgrid((unsigned)(rt.n_req * sh.nh));
-  if (dtype == HYF_BF16)
-    hipLaunchKernelGGL(k_round_merge<bf16>, mgrid, dim3(RT), mlds, s, sh, a, rt);
-  else
-    hipLaunchKernelGGL(k_round_merge<float>, mgrid, dim3(RT), mlds, s, sh, a, rt);
   return hipGetLastError();
 }
 
