@@ -137,24 +137,37 @@ __device__ __forceinline__ void round_tile(const Shape& sh, const RoundArgs& a, 
   }
 
   if (a.do_draft) {
+    float sum[RB];
 #pragma unroll
     for (int j = 0; j < RB; ++j) {
-      float sum = 0.f;
+      sum[j] = 0.f;
       if (active) {
         const f32x4 c = *reinterpret_cast<const f32x4*>(Cl + j * N + 4 * c4);
-        sum = hv[0] * c[0] + hv[1] * c[1] + hv[2] * c[2] + hv[3] * c[3];
+        sum[j] = hv[0] * c[0] + hv[1] * c[1] + hv[2] * c[2] + hv[3] * c[3];
       }
-      red[j * RT + t] = sum;
     }
-    __syncthreads();
     const float D = a.d_skip[h];
-    for (int idx = t; idx < RB * rows_wg; idx += RT) {
-      const int j = idx / rows_wg, pr = idx % rows_wg;
-      const int pp = p0 + pr;
-      if (pp >= P) continue;
-      float sum = 0.f;
-      for (int c = 0; c < tpr; ++c) sum += red[j * RT + pr * tpr + c];
-      st_dev(a.mem + (((int64_t)r * RB + j) * nh + h) * P + pp, sum + D * vb[idx]);
+    if ((tpr & (tpr - 1)) == 0) {
+      // the tpr threads of a row are consecutive lanes of one wave: xor-shuffle reduction
+      for (int o = tpr / 2; o >= 1; o >>= 1)
+#pragma unroll
+        for (int j = 0; j < RB; ++j) sum[j] += __shfl_xor(sum[j], o, 64);
+      if (active && c4 == 0)
+#pragma unroll
+        for (int j = 0; j < RB; ++j)
+          st_dev(a.mem + (((int64_t)r * RB + j) * nh + h) * P + p, sum[j] + D * vb[j * rows_wg + prow]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < RB; ++j) red[j * RT + t] = sum[j];
+      __syncthreads();
+      for (int idx = t; idx < RB * rows_wg; idx += RT) {
+        const int j = idx / rows_wg, pr = idx % rows_wg;
+        const int pp = p0 + pr;
+        if (pp >= P) continue;
+        float acc = 0.f;
+        for (int c = 0; c < tpr; ++c) acc += red[j * RT + pr * tpr + c];
+        st_dev(a.mem + (((int64_t)r * RB + j) * nh + h) * P + pp, acc + D * vb[idx]);
+      }
     }
   }
 
