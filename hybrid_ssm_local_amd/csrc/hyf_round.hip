@@ -529,7 +529,7 @@ hipError_t launch_round(int dtype, const Shape& sh, const RoundArgs& a, const Re
     static std::once_flag once;
     static hipError_t set_err = hipSuccess;
     std::call_once(once, [] {
-      const int mx = 160 * 1024;
+      const int mx = 160 * 1024 - 256;  // leaves room for the kernel's few bytes of static LDS
       set_err = hipFuncSetAttribute(reinterpret_cast<const void*>(k_round<bf16>),
                                     hipFuncAttributeMaxDynamicSharedMemorySize, mx);
       if (set_err == hipSuccess)
