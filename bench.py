@@ -44,6 +44,11 @@ def parse():
     p.add_argument("--kernel-reps", type=int, default=60)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--profile", action="store_true", help="short run for a profiler (2 steps, few reps)")
+    p.add_argument("--pmc-probe", action="store_true",
+                   help="only the measured kernels (plus a copy of known size), for rocprofv3 --pmc runs")
+    p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                   help="turn two rocprofv3 --pmc databases (FETCH_SIZE, WRITE_SIZE) of --pmc-probe runs "
+                        "into profiles/pmc_traffic.json")
     return p.parse_args()
 
 
@@ -123,19 +128,20 @@ class Episode:
 
 
 def time_calls(torch, fn, reps):
-    """Per-call HIP events on the current stream; returns mean milliseconds per call."""
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    """Mean milliseconds per call: HIP events on the current stream around `reps` back-to-back calls
+    (the same launches a rocprofv3 kernel trace of this loop averages)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    e0.record()
     for i in range(reps):
-        ev[i][0].record()
         fn(i)
-        ev[i][1].record()
+    e1.record()
     torch.cuda.synchronize()
-    ms = [a.elapsed_time(b) for a, b in ev]
-    return sum(ms) / len(ms), sorted(ms)[len(ms) // 2]
+    ms = e0.elapsed_time(e1) / reps
+    return ms, ms
 
 
-def kernel_loops(torch, hf, I, ep, reps):
+def kernel_loops(torch, hf, I, ep, reps, with_gemm=True):
     sh = ep.shape
     d, nh, P, N = sh.d_model, sh.n_heads, sh.head_dim, sh.d_state
     cfg = ep.cfg
@@ -176,6 +182,8 @@ def kernel_loops(torch, hf, I, ep, reps):
     sbytes = T * (nh * P * 2 + sh.gn * 2 + nh * 4) + 2 * nh * P * N * 4
     out["scan"] = dict(mean_us=mean_ms * 1e3, median_us=med_ms * 1e3, bytes=sbytes,
                        gbs=sbytes / (mean_ms * 1e-3) / 1e9, feats_per_s=T / (mean_ms * 1e-3))
+    if not with_gemm:
+        return out
     # 3. prefill projection GEMM (v | B | dt columns over the whole prefix)
     nvbd = sh.dq + sh.gn + nh
     g = torch.empty((T, nvbd), dtype=torch.bfloat16, device="cuda")
@@ -194,8 +202,99 @@ def kernel_loops(torch, hf, I, ep, reps):
     return out
 
 
-def cpu_baseline(I, ep):
-    """The float64 oracle on a bounded slice of the same workload (4096-row prefix + 128 rounds)."""
+# ---- HBM traffic from hardware counters -------------------------------------------------------
+# rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of a --pmc-probe run are scaled by
+# what the same counters read for a plain device copy of COPY_BYTES (read COPY_BYTES, write
+# COPY_BYTES).  The figures stay valid only for the kernel sources they were taken from.
+COPY_BYTES = 256 << 20
+PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+PMC_KERNELS = {  # key -> (kernel name prefix in the profile, source file)
+    "proj": ("_ZN3hyf12k_proj_small", "hybrid_ssm_local_amd/csrc/hyf_proj.hip"),
+    "scan": ("void hyf::k_ssd_seg", "hybrid_ssm_local_amd/csrc/hyf_scan.hip"),
+}
+
+
+def source_digest(rel):
+    import hashlib
+
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def pmc_probe(torch, hf, I, reps=6):
+    """The W_in projection of a round, the 8192-token scan, and a copy of known size."""
+    src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    ep = Episode(torch, hf, I)
+    kernel_loops(torch, hf, I, ep, reps, with_gemm=False)
+    torch.cuda.synchronize()
+
+
+def pmc_summary(fetch_db, write_db):
+    import sqlite3
+
+    def dispatches(db, counter):
+        con = sqlite3.connect(db)
+        rows = con.execute("select dispatch_id, kernel_name, sum(value) from counters_collection "
+                           "where counter_name = ? group by dispatch_id", (counter,)).fetchall()
+        return [(k, v) for _, k, v in rows]
+
+    def per_kernel(rows):
+        agg = {}
+        for k, v in rows:
+            agg.setdefault(k, []).append(v)
+        return {k: sum(v) / len(v) for k, v in agg.items()}
+
+    fd, wd = dispatches(fetch_db, "FETCH_SIZE"), dispatches(write_db, "WRITE_SIZE")
+    fetch, write = per_kernel(fd), per_kernel(wd)
+    # the copy of COPY_BYTES is the largest copy dispatch of the run
+    copy_f = max(v for k, v in fd if "copyBuffer" in k)
+    copy_w = max(v for k, v in wd if "copyBuffer" in k)
+    scale_f, scale_w = COPY_BYTES / (copy_f * 1024), COPY_BYTES / (copy_w * 1024)
+    out = {"copy_bytes": COPY_BYTES, "copy_fetch_kib": copy_f, "copy_write_kib": copy_w,
+           "fetch_scale": scale_f, "write_scale": scale_w, "kernels": {}}
+    for key, (prefix, src) in PMC_KERNELS.items():
+        names = [k for k in fetch if k.startswith(prefix)]
+        if not names:
+            continue
+        k = names[0]
+        f_kib, w_kib = fetch[k], write.get(k, 0.0)
+        out["kernels"][key] = {"kernel": k, "source": src, "source_sha256": source_digest(src),
+                               "fetch_kib": f_kib, "write_kib": w_kib,
+                               "traffic_bytes": f_kib * 1024 * scale_f + w_kib * 1024 * scale_w}
+    with open(PMC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    lines = ["# HBM traffic of the measured kernels (rocprofv3 counters)", "",
+             "Commands (repository root, one MI355X; each counter in a run of its own):", "", "```",
+             "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc/f -o f -- python3 bench.py --pmc-probe",
+             "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc/w -o w -- python3 bench.py --pmc-probe",
+             "python3 bench.py --pmc-summary gpurun_out/pmc/f/f_results.db gpurun_out/pmc/w/w_results.db", "```", "",
+             f"Calibration: a device copy of {COPY_BYTES >> 20} MiB reads FETCH_SIZE {copy_f:.0f} KiB and "
+             f"WRITE_SIZE {copy_w:.0f} KiB, so measured KiB are scaled by {scale_f:.3f} (fetch) and "
+             f"{scale_w:.3f} (write).", "",
+             "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes per launch |", "|---|---:|---:|---:|"]
+    for key, k in out["kernels"].items():
+        lines.append(f"| `{k['kernel'][:60]}` | {k['fetch_kib']:.0f} | {k['write_kib']:.0f} | {k['traffic_bytes']:.0f} |")
+    with open(PMC_FILE.replace(".json", ".md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps(out, indent=1))
+
+
+def pmc_traffic(key):
+    """Measured HBM bytes per launch of a kernel, or None if absent or taken from other sources."""
+    try:
+        with open(PMC_FILE) as f:
+            k = json.load(f)["kernels"][key]
+    except (OSError, KeyError, ValueError):
+        return None
+    return k["traffic_bytes"] if k["source_sha256"] == source_digest(k["source"]) else None
+
+
+def cpu_baseline(I, ep, min_seconds=10.0):
+    """The float64 oracle on the host cores: whole episodes of the same workload (reset, 8192-feature
+    prefix commit, 256 rounds), repeated until at least min_seconds of CPU work."""
     import numpy as np
 
     from oracle import hyflash_oracle as O
@@ -210,26 +309,35 @@ def cpu_baseline(I, ep):
     wl = I.WORKLOADS[WORKLOAD]
     w = {k: np.asarray(v, np.float64) for k, v in ep.host_w.items()}
     rng = I.rng_streams(wl["seed"] + 1000)
-    n_pre, n_rounds = 4096, 128
-    pre = I.make_rows(rng[1], n_pre, sh.d_model, wl["feat_scale"], sh.dtype)
-    t0 = time.perf_counter()
-    st, _ = O.commit(sh, w, O.new_state(sh), pre)
-    t_commit = time.perf_counter() - t0
-    acc = I.acceptance_lengths(rng[4], n_rounds)
-    t0 = time.perf_counter()
-    for a in acc:
-        cf = I.make_rows(rng[2], int(a), sh.d_model, wl["feat_scale"], sh.dtype)
-        blk = I.make_rows(rng[3], 8, sh.d_model, wl["block_scale"], sh.dtype)
-        st, _ = O.round_step(sh, w, st, cf, blk)
-    t_rounds = time.perf_counter() - t0
-    return {"value": n_rounds / t_rounds, "unit": "draft blocks/s per layer", "cores": cores, "kind": "oracle",
-            "sample": f"float64 NumPy oracle: {n_pre}-feature prefix commit, then {n_rounds} rounds "
-                      f"(acceptance 1-8) of the same Qwen3-4B-shaped layer",
-            "commit_feats_per_s": n_pre / t_commit, "seconds": t_commit + t_rounds}
+    n_pre, n_rounds = ep.T, ep.R
+    t_commit = t_rounds = 0.0
+    episodes = 0
+    while episodes == 0 or t_commit + t_rounds < min_seconds:
+        pre = I.make_rows(rng[1], n_pre, sh.d_model, wl["feat_scale"], sh.dtype)
+        acc = I.acceptance_lengths(rng[4], n_rounds)
+        commits = [I.make_rows(rng[2], int(a), sh.d_model, wl["feat_scale"], sh.dtype) for a in acc]
+        blocks = [I.make_rows(rng[3], 8, sh.d_model, wl["block_scale"], sh.dtype) for _ in acc]
+        t0 = time.perf_counter()
+        st, _ = O.commit(sh, w, O.new_state(sh), pre)
+        t1 = time.perf_counter()
+        for cf, blk in zip(commits, blocks):
+            st, _ = O.round_step(sh, w, st, cf, blk)
+        t2 = time.perf_counter()
+        t_commit += t1 - t0
+        t_rounds += t2 - t1
+        episodes += 1
+    return {"value": episodes * n_rounds / (t_commit + t_rounds), "unit": "draft blocks/s per layer", "cores": cores,
+            "kind": "oracle",
+            "sample": f"float64 NumPy oracle: {episodes} whole episodes of the benchmark workload (reset, "
+                      f"{n_pre}-feature prefix commit, {n_rounds} rounds with 1-8 accepted features)",
+            "commit_feats_per_s": episodes * n_pre / t_commit, "seconds": t_commit + t_rounds}
 
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
@@ -245,6 +353,9 @@ def main():
 
     if not torch.cuda.is_available():
         raise RuntimeError("bench.py needs a GPU")
+    if args.pmc_probe:
+        pmc_probe(torch, hf, I)
+        return
     log("building episode inputs")
     ep = Episode(torch, hf, I)
     stream = torch.cuda.current_stream().cuda_stream
@@ -321,10 +432,10 @@ def main():
         "commit_scan": {"value": scan["feats_per_s"], "unit": "committed feats/s", "T": ep.T,
                         "avg_us": scan["mean_us"],
                         "roofline": {"bound": "hbm", "achieved": scan["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                     "frac": scan["gbs"] / HBM_PEAK_GBS, "traffic": None,
+                                     "frac": scan["gbs"] / HBM_PEAK_GBS, "traffic": pmc_traffic("scan"),
                                      "bytes_per_launch": scan["bytes"]}},
         "roofline": {"bound": "hbm", "achieved": proj["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": proj["gbs"] / HBM_PEAK_GBS, "traffic": None,
+                     "frac": proj["gbs"] / HBM_PEAK_GBS, "traffic": pmc_traffic("proj"),
                      "kernel": "k_proj_small<bf16,8,1>: input projection of a round (12 rows x w_in)",
                      "bytes_per_launch": proj["bytes"], "avg_us": proj["mean_us"]},
         "gemm_roofline": {"bound": "mfma", "achieved": gemm["tflops"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
