@@ -11,7 +11,7 @@ namespace {
 
 constexpr uint64_t ALIGN = 256;
 constexpr int SCAN_TARGET_WGS = 256;         // scan workgroups the segment split aims for (one per CU)
-constexpr int64_t SCAN_MIN_SEG_TOKENS = 2048;  // shortest segment the split makes
+constexpr int64_t SCAN_MIN_SEG_TOKENS = 1024;  // shortest segment the split makes
 
 uint64_t align_up(uint64_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 int esize(int dtype) { return dtype == HYF_BF16 ? 2 : 4; }
@@ -82,7 +82,7 @@ int n_att_split(const Shape& s) { return (s.W + 63) / 64 + 1; }
 // weights for.
 int64_t scan_seg_target(const Shape& s) {
   const int64_t per_seg = scan_items_per_seg(s);
-  const int64_t t = (SCAN_TARGET_WGS + per_seg - 1) / per_seg;
+  const int64_t t = SCAN_TARGET_WGS / per_seg;
   return t < 1 ? 1 : t;
 }
 int64_t scan_cap_chunks(const Shape& s, int dtype) {
@@ -93,12 +93,19 @@ int64_t scan_cap_chunks(const Shape& s, int dtype) {
 // multiple of HYF_TBLK / L when the chunk is shorter than a block (chunk lengths are powers of 2).
 int64_t scan_cps_unit(const Shape& s) { return s.L >= HYF_TBLK ? 1 : HYF_TBLK / s.L; }
 int32_t scan_chunks_per_seg(const Shape& s, int dtype, int64_t total_chunks) {
-  const int64_t seg_target = scan_seg_target(s);
+  // One workgroup per CU at a time: the segment count fills whole waves of SCAN_TARGET_WGS
+  // workgroups, as many waves as the longest segment LDS allows forces.
   const int64_t unit = scan_cps_unit(s);
-  int64_t cps = (total_chunks + seg_target - 1) / seg_target;
+  const int64_t cap = scan_cap_chunks(s, dtype) / unit * unit;
+  const int64_t per_seg = scan_items_per_seg(s);
+  const int64_t need = (total_chunks + cap - 1) / cap;  // segments the cap alone requires
+  const int64_t waves = (need * per_seg + SCAN_TARGET_WGS - 1) / SCAN_TARGET_WGS;
+  int64_t target = waves * SCAN_TARGET_WGS / per_seg;
+  if (target < need) target = need;
+  if (target < 1) target = 1;
+  int64_t cps = (total_chunks + target - 1) / target;
   const int64_t min_cps = SCAN_MIN_SEG_TOKENS / s.L;
   if (cps < min_cps) cps = min_cps;
-  const int64_t cap = scan_cap_chunks(s, dtype) / unit * unit;
   cps = (cps + unit - 1) / unit * unit;
   if (cps > cap) cps = cap;
   return (int32_t)(cps < unit ? unit : cps);
@@ -109,7 +116,7 @@ int64_t scan_max_segs(const Shape& s, int dtype, int32_t n_req, int64_t rows) {
   const int64_t unit = s.L >= HYF_TBLK ? 1 : HYF_TBLK / s.L;
   int64_t cap = scan_cap_chunks(s, dtype) / unit * unit;
   if (cap < unit) cap = unit;
-  return scan_seg_target(s) + 2 * (int64_t)n_req + rows / (cap * s.L) + 1;
+  return scan_seg_target(s) + 2 * (int64_t)n_req + rows / (cap * s.L) + 3;
 }
 // Blocks of the time-blocked buffers for `rows` tokens over R requests (each request starts a block).
 int64_t time_blocks(int64_t rows, int32_t R) { return rows / HYF_TBLK + R + 1; }
