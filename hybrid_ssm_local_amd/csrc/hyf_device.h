@@ -54,8 +54,10 @@ template <> __device__ __forceinline__ float from_f32<float>(float v) { return v
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return static_cast<bf16>(v); }
 
 __device__ __forceinline__ float softplus_f(float z) {
-  // log(1 + e^z) without overflow: max(z, 0) + log1p(exp(-|z|)).
-  return fmaxf(z, 0.f) + log1pf(expf(-fabsf(z)));
+  // log(1 + e^z) without overflow: max(z, 0) + log(1 + e^-|z|), on the hardware exp2/log2 (their
+  // error, a few 1e-7 relative, is far inside every tolerance the results are held to; where
+  // e^-|z| drops below fp32's epsilon the result is max(z, 0) to within that epsilon)
+  return fmaxf(z, 0.f) + __logf(1.f + __expf(-fabsf(z)));
 }
 
 // 64-lane wave reductions (all lanes get the result).
@@ -113,6 +115,21 @@ __device__ __forceinline__ void lds_dma16(const void* src, void* lds_base) {
 __device__ __forceinline__ void lds_dma4(const void* src, void* lds_base) {
   __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(src),
                                    (void __attribute__((address_space(3)))*)(lds_base), 4, 0, 0);
+}
+
+// A staging job of n 16-byte chunks, chunk i from global src(i) to LDS dst + 16 i, by a workgroup
+// of THREADS threads with direct global -> LDS loads: no registers and no wait between loads, so
+// all jobs a workgroup issues before its vm_wait<0>() + barrier cost one memory round trip.  A
+// wave issues chunks [64 k, 64 k + 64) for k = wave, wave + THREADS / 64, ...; lanes past n are
+// masked off.  aux: cache policy bits of the loads.
+template <int THREADS, int AUX = 0, typename F>
+__device__ __forceinline__ void lds_stage16(int n, void* dst, F src) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int base = wave * 64; base < n; base += THREADS)
+    if (base + lane < n)
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(src(base + lane)),
+                                       (void __attribute__((address_space(3)))*)(static_cast<char*>(dst) + 16 * base),
+                                       16, 0, AUX);
 }
 
 // 16-byte vector of storage elements.

@@ -42,9 +42,7 @@ __device__ __forceinline__ T* ring_ptr(char* pool, const Shape& sh, int slot, ui
 // jobs) or 256-byte (4-byte jobs) units so a wave's instruction stays inside its region.
 template <typename F>
 __device__ __forceinline__ void stage16(int n, void* dst, F src) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int base = wave * 64; base < n; base += RT)
-    if (base + lane < n) lds_dma16(src(base + lane), static_cast<char*>(dst) + 16 * base);
+  lds_stage16<RT>(n, dst, src);
 }
 template <typename F>
 __device__ __forceinline__ void stage4(int n, void* dst, F src) {
@@ -63,12 +61,7 @@ __device__ __forceinline__ void st_dev(float* p, float v) {
 constexpr int AUX_DEV = 16;  // cache policy of a device-coherent load (sc1)
 template <typename F>
 __device__ __forceinline__ void stage16_dev(int n, void* dst, F src) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int base = wave * 64; base < n; base += RT)
-    if (base + lane < n)
-      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(src(base + lane)),
-                                       (void __attribute__((address_space(3)))*)(static_cast<char*>(dst) + 16 * base),
-                                       16, 0, AUX_DEV);
+  lds_stage16<RT, AUX_DEV>(n, dst, src);
 }
 
 // Tile LDS (bytes): B of the committed rows [RMAXC][N] f32 | C of the block rows [RB][N] f32 |

@@ -90,36 +90,35 @@ k_ssd_seg(Shape sh, ScanArgs a, ReqTable rt, int npb, int nnb, int n_items, int 
   // block boundary)
   const int64_t blk0 = rt.blk0[r] + s_begin / TB;
 
-  // ---- pre-pass: the per-token weights dt_t exp(suf_t) into LDS.  Thread t owns the run of RUN
-  // consecutive tokens from t RUN (RUN = 4 run4 with run4 odd, so 16-byte LDS accesses of
-  // neighbouring threads fall in different banks).  Forward over the run: raw steps (in batches
-  // of 8 x 4 tokens, all loads of a batch in flight together) -> dt, kept in LDS, and the run's
-  // log-decay total.  A wave scan and a workgroup scan of the run totals give each run the
-  // log-decay of all later tokens; backward over the run, each token's weight replaces its dt.
-  // Tokens past the segment end (up to the end of its last macro-step) get dt = 0, weight 0.
+  // ---- pre-pass: the per-token weights dt_t exp(suf_t) into LDS.  The segment's raw steps go to
+  // LDS in one direct copy (a block's 128 steps of head h are 512 contiguous bytes).  Thread t
+  // owns the run of RUN consecutive tokens from t RUN (RUN = 4 run4 with run4 odd, so 16-byte LDS
+  // accesses of neighbouring threads fall in different banks).  Forward over the run: dt (kept in
+  // LDS in place of the raw step) and the run's log-decay total.  A wave scan and a workgroup
+  // scan of the run totals give each run the log-decay of all later tokens; backward over the
+  // run, each token's weight replaces its dt.  Tokens past the segment end (up to the end of its
+  // last macro-step) get dt = 0, weight 0.
   const int wlen = (len + MS - 1) / MS * MS;
+  const int nblk_dt = (len + TB - 1) / TB;
+  lds_stage16<SG_THREADS>(nblk_dt * (TB / 4), wt, [&](int i) {
+    return a.dt + (blk0 + i / (TB / 4)) * a.dblk + (int64_t)h * TB + 4 * (i % (TB / 4));
+  });
+  vm_wait<0>();
+  __syncthreads();
   const int run4 = ((len + 4 * SG_THREADS - 1) / (4 * SG_THREADS)) | 1;
   const int tk0 = t * 4 * run4;
   float run_tot = 0.f;
-  for (int c0 = 0; c0 < run4; c0 += 8) {
-    f32x4 raw[8];
+#pragma unroll 4
+  for (int c = 0; c < run4; ++c) {
+    const int tk = tk0 + 4 * c;
+    if (tk < wlen) {
+      f32x4 d = *reinterpret_cast<const f32x4*>(wt + tk);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int tk = min(tk0 + 4 * (c0 + i), (len - 1) & ~3);  // clamped: always a valid address
-      raw[i] = *reinterpret_cast<const f32x4*>(a.dt + (blk0 + tk / TB) * a.dblk + (int64_t)h * TB + tk % TB);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int tk = tk0 + 4 * (c0 + i);
-      if (c0 + i < run4 && tk < wlen) {
-        f32x4 d;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          d[e] = tk + e < len ? softplus_f(raw[i][e] + bias) : 0.f;
-          run_tot += d[e] * A;
-        }
-        *reinterpret_cast<f32x4*>(wt + tk) = d;
+      for (int e = 0; e < 4; ++e) {
+        d[e] = tk + e < len ? softplus_f(d[e] + bias) : 0.f;
+        run_tot += d[e] * A;
       }
+      *reinterpret_cast<f32x4*>(wt + tk) = d;
     }
   }
   // exclusive suffix over the runs: later lanes of this wave, then later waves
@@ -139,13 +138,14 @@ k_ssd_seg(Shape sh, ScanArgs a, ReqTable rt, int npb, int nnb, int n_items, int 
     if (w2 > wave) suf += red[w2];
     lam_seg += red[w2];
   }
+#pragma unroll 4
   for (int c = run4 - 1; c >= 0; --c) {
     const int tk = tk0 + 4 * c;
     if (tk < wlen) {
       f32x4 d = *reinterpret_cast<const f32x4*>(wt + tk);
 #pragma unroll
       for (int e = 3; e >= 0; --e) {
-        const float w = d[e] * expf(suf);
+        const float w = d[e] * __expf(suf);  // suf <= 0
         suf += d[e] * A;
         d[e] = w;
       }
