@@ -118,6 +118,13 @@ int64_t scan_max_segs(const Shape& s, int dtype, int32_t n_req, int64_t rows) {
   if (cap < unit) cap = unit;
   return scan_seg_target(s) + 2 * (int64_t)n_req + rows / (cap * s.L) + 3;
 }
+// y-mode segments are single blocks of HYF_TBLK tokens.
+int64_t scan_max_segs_y(int32_t n_req, int64_t rows) { return rows / HYF_TBLK + (int64_t)n_req + 1; }
+int64_t scan_segs_bound(const Shape& s, int dtype, int32_t n_req, int64_t rows, bool with_y) {
+  const int64_t a = scan_max_segs(s, dtype, n_req, rows);
+  const int64_t b = with_y ? scan_max_segs_y(n_req, rows) : 0;
+  return a > b ? a : b;
+}
 // Blocks of the time-blocked buffers for `rows` tokens over R requests (each request starts a block).
 int64_t time_blocks(int64_t rows, int32_t R) { return rows / HYF_TBLK + R + 1; }
 
@@ -149,13 +156,13 @@ WsDraft ws_draft(const Shape& s, int dtype, int32_t R, int64_t rows) {
 }
 
 struct WsCommit {
-  uint64_t vb, dt, kb, part, lam, end;
+  uint64_t vb, dt, kb, c, part, lam, end;
 };
-WsCommit ws_commit(const Shape& s, int dtype, int32_t R, int64_t rows) {
+WsCommit ws_commit(const Shape& s, int dtype, int32_t R, int64_t rows, bool with_y) {
   WsCommit w;
   uint64_t o = 0;
   const int64_t krows = rows < (int64_t)R * s.W ? rows : (int64_t)R * s.W;
-  const int64_t segs = scan_max_segs(s, dtype, R, rows);
+  const int64_t segs = scan_segs_bound(s, dtype, R, rows, with_y);
   const int64_t nblk = time_blocks(rows, R);
   w.vb = o;  // v | B time-blocked: [nblk][dq + gn][HYF_TBLK]
   o += align_up((uint64_t)nblk * (s.dq + s.gn) * HYF_TBLK * esize(dtype));
@@ -163,6 +170,8 @@ WsCommit ws_commit(const Shape& s, int dtype, int32_t R, int64_t rows) {
   o += align_up((uint64_t)nblk * s.nh * HYF_TBLK * 4);
   w.kb = o;
   o += align_up((uint64_t)krows * s.dq * esize(dtype));
+  w.c = o;  // y-mode: C time-blocked: [nblk][gn][HYF_TBLK]
+  if (with_y) o += align_up((uint64_t)nblk * s.gn * HYF_TBLK * esize(dtype));
   w.part = o;
   o += align_up((uint64_t)segs * s.nh * s.P * s.N * 4);
   w.lam = o;
@@ -201,20 +210,24 @@ int build_table(const Shape& s, int32_t pool_slots, const int32_t* slots, int32_
   return HYF_OK;
 }
 
-void fill_segments(const Shape& s, int dtype, ReqTable* rt, int32_t* cps_out, int32_t* total_out, int32_t* max_out) {
-  int64_t total_chunks = 0;
-  for (int i = 0; i < rt->n_req; ++i) total_chunks += (rt->row0[i + 1] - rt->row0[i] + s.L - 1) / s.L;
-  const int32_t cps = scan_chunks_per_seg(s, dtype, total_chunks);
+void fill_segments(const Shape& s, int dtype, ReqTable* rt, bool y_mode, int32_t* seg_tokens_out, int32_t* total_out,
+                   int32_t* max_out) {
+  int32_t seg_tokens = HYF_TBLK;
+  if (!y_mode) {
+    int64_t total_chunks = 0;
+    for (int i = 0; i < rt->n_req; ++i) total_chunks += (rt->row0[i + 1] - rt->row0[i] + s.L - 1) / s.L;
+    seg_tokens = scan_chunks_per_seg(s, dtype, total_chunks) * s.L;
+  }
   int32_t q = 0, mx = 0;
   for (int i = 0; i < rt->n_req; ++i) {
     rt->seg0[i] = q;
-    const int64_t ch = (rt->row0[i + 1] - rt->row0[i] + s.L - 1) / s.L;
-    const int32_t ns = (int32_t)((ch + cps - 1) / cps);
+    const int64_t n = rt->row0[i + 1] - rt->row0[i];
+    const int32_t ns = (int32_t)((n + seg_tokens - 1) / seg_tokens);
     q += ns;
     if (ns > mx) mx = ns;
   }
   rt->seg0[rt->n_req] = q;
-  *cps_out = cps;
+  *seg_tokens_out = seg_tokens;
   *total_out = q;
   *max_out = mx;
 }
@@ -269,18 +282,18 @@ size_t hyf_state_bytes(const hyf_config* cfg) {
   return (size_t)L.total;
 }
 
-size_t hyf_workspace_bytes(const hyf_config* cfg, int32_t max_requests, int64_t max_rows) {
+size_t hyf_workspace_bytes(const hyf_config* cfg, int32_t max_requests, int64_t max_rows, int32_t with_y) {
   if (check_cfg(cfg) != HYF_OK || max_requests < 1 || max_requests > HYF_MAX_REQUESTS || max_rows < 0) return 0;
   const Shape s = make_shape(cfg);
   const uint64_t a = ws_draft(s, cfg->dtype, max_requests, max_rows).end;
-  const uint64_t b = ws_commit(s, cfg->dtype, max_requests, max_rows).end;
+  const uint64_t b = ws_commit(s, cfg->dtype, max_requests, max_rows, with_y != 0).end;
   return (size_t)(a > b ? a : b);
 }
 
-size_t hyf_ssd_scan_workspace_bytes(const hyf_config* cfg, int64_t T) {
+size_t hyf_ssd_scan_workspace_bytes(const hyf_config* cfg, int64_t T, int32_t with_y) {
   if (check_cfg(cfg) != HYF_OK || T < 0) return 0;
   const Shape s = make_shape(cfg);
-  const int64_t segs = scan_max_segs(s, cfg->dtype, 1, T);
+  const int64_t segs = scan_segs_bound(s, cfg->dtype, 1, T, with_y != 0);
   return (size_t)(align_up((uint64_t)segs * s.nh * s.P * s.N * 4) + align_up((uint64_t)segs * s.nh * 4));
 }
 
@@ -303,14 +316,16 @@ int hyf_memory_commit(const hyf_config* cfg, const hyf_weights* w, void* state_p
   if (st != HYF_OK) return st;
   if ((st = check_weights(w)) != HYF_OK) return st;
   if (!state_pool || !aligned(state_pool, ALIGN) || pool_slots < 1 || !cu_rows) return HYF_EINVAL;
-  if (y_opt) return HYF_EUNSUPPORTED;
   const Shape s = make_shape(cfg);
+  if (y_opt && !scan_y_supported(s, esize(cfg->dtype))) return HYF_EUNSUPPORTED;
+  if (y_opt && !aligned(y_opt, 16)) return HYF_EINVAL;
   ReqTable rt;
   if ((st = build_table(s, pool_slots, slots, n_req, cu_rows, &rt)) != HYF_OK) return st;
   const int64_t rows = cu_rows[n_req];
   if (rows == 0) return HYF_OK;
   if (!feats || !aligned(feats, 16)) return HYF_EINVAL;
-  if (!ws || !aligned(ws, ALIGN) || ws_bytes < hyf_workspace_bytes(cfg, n_req, rows)) return HYF_EWORKSPACE;
+  if (!ws || !aligned(ws, ALIGN) || ws_bytes < hyf_workspace_bytes(cfg, n_req, rows, y_opt != nullptr))
+    return HYF_EWORKSPACE;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   char* wsb = static_cast<char*>(ws);
   char* pool = static_cast<char*>(state_pool);
@@ -320,7 +335,7 @@ int hyf_memory_commit(const hyf_config* cfg, const hyf_weights* w, void* state_p
   int64_t max_n = 0;
   for (int i = 0; i < n_req; ++i) max_n = cu_rows[i + 1] - cu_rows[i] > max_n ? cu_rows[i + 1] - cu_rows[i] : max_n;
 
-  if (max_n <= 16) {
+  if (max_n <= 16 && !y_opt) {
     // Round-sized commit: one weight pass over the k | v | B | dt rows, then one round kernel that
     // folds the rows into H (one read-modify-write), appends them to the ring and advances count.
     const WsDraft L = ws_draft(s, dt, n_req, rows);
@@ -348,10 +363,14 @@ int hyf_memory_commit(const hyf_config* cfg, const hyf_weights* w, void* state_p
     return hip_status(launch_round(dt, s, ra, rt, hs));
   }
 
-  // Prefill-sized commit: projection GEMMs -> ring append -> scan -> count.
-  // The scan's operands v, B and dt are written time-contiguous (feature-major, each request's
-  // tokens starting at a multiple of 8) so the scan streams them as plain 16-byte rows.
-  const WsCommit L = ws_commit(s, dt, n_req, rows);
+  // Prefill-sized commit (or any commit with per-token outputs): projection GEMMs -> ring append ->
+  // scan -> count.  The GEMM epilogues write the scan's operands time-blocked (each request's
+  // tokens start a block): v and B (and C for y) tiled for the scan's MFMA fragments, dt plain.
+  const bool with_y = y_opt != nullptr;
+  const WsCommit L = ws_commit(s, dt, n_req, rows, with_y);
+  char* cT = wsb + L.c;
+  const int64_t c_blk = (int64_t)s.gn * HYF_TBLK;
+  const char* w_c = static_cast<const char*>(w->w_in) + (int64_t)s.off_c * s.d * es;
   char* vbT = wsb + L.vb;
   float* dtT = reinterpret_cast<float*>(wsb + L.dt);
   char* kb = wsb + L.kb;
@@ -369,6 +388,10 @@ int hyf_memory_commit(const hyf_config* cfg, const hyf_weights* w, void* state_p
     RowSrc xs{src, src, n};
     Epi e{vbT + rt.blk0[i] * vb_blk * es, vb_blk, 0, nvb, dtT + rt.blk0[i] * dt_blk, dt_blk, 1};
     if ((he = launch_linear(dt, xs, n, s.d, w_vbd, nvb + s.nh, e, hs)) != hipSuccess) return HYF_EHIP;
+    if (with_y) {
+      Epi ec{cT + rt.blk0[i] * c_blk * es, c_blk, 0, s.gn, nullptr, 0, 1};
+      if ((he = launch_linear(dt, xs, n, s.d, w_c, s.gn, ec, hs)) != hipSuccess) return HYF_EHIP;
+    }
     // k only for the rows that stay in the window: the last min(n_i, W) of the request.
     const int64_t m = n < s.W ? n : s.W;
     const char* ksrc = src + (n - m) * (int64_t)s.d * es;
@@ -391,8 +414,13 @@ int hyf_memory_commit(const hyf_config* cfg, const hyf_weights* w, void* state_p
   sa.h_direct = nullptr;
   sa.part = reinterpret_cast<float*>(wsb + L.part);
   sa.lam = reinterpret_cast<float*>(wsb + L.lam);
+  sa.y_mode = with_y;
+  sa.C = cT;
+  sa.cblk = c_blk;
+  sa.y = y_opt;
+  sa.d_skip = w->d_skip;
   int32_t max_segs = 0;
-  fill_segments(s, dt, &rt, &sa.chunks_per_seg, &sa.total_segs, &max_segs);
+  fill_segments(s, dt, &rt, with_y, &sa.seg_tokens, &sa.total_segs, &max_segs);
   if ((he = launch_ssd_state(dt, s, sa, rt, max_segs, hs)) != hipSuccess) return HYF_EHIP;
   return hip_status(launch_bump_counts(pool, s, rt, hs));
 }
@@ -416,7 +444,7 @@ int hyf_draft_block(const hyf_config* cfg, const hyf_weights* w, void* state_poo
       if (cu_commit[i + 1] - cu_commit[i] > HYF_BLOCK) return HYF_ECAPACITY;
     if (rows > 0 && !aligned(commit_feats, 16)) return HYF_EINVAL;
   }
-  if (!ws || !aligned(ws, ALIGN) || ws_bytes < hyf_workspace_bytes(cfg, n_req, rows)) return HYF_EWORKSPACE;
+  if (!ws || !aligned(ws, ALIGN) || ws_bytes < hyf_workspace_bytes(cfg, n_req, rows, 0)) return HYF_EWORKSPACE;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   char* wsb = static_cast<char*>(ws);
   char* pool = static_cast<char*>(state_pool);
@@ -477,11 +505,13 @@ int hyf_ssd_scan(const hyf_config* cfg, const void* x, const void* B, const void
   if (T < 0 || T > ((int64_t)1 << 30)) return HYF_ECAPACITY;
   if (!a_log || !dt_bias || !d_skip || !H_inout || !aligned(H_inout, 16)) return HYF_EINVAL;
   if ((y_opt != nullptr) != (C_opt != nullptr)) return HYF_EINVAL;
-  if (y_opt) return HYF_EUNSUPPORTED;
+  const Shape s = make_shape(cfg);
+  if (y_opt && !scan_y_supported(s, esize(cfg->dtype))) return HYF_EUNSUPPORTED;
   if (T == 0) return HYF_OK;
   if (!x || !B || !dt_raw || !aligned(x, 16) || !aligned(B, 16) || !aligned(dt_raw, 16)) return HYF_EINVAL;
-  if (!ws || !aligned(ws, ALIGN) || ws_bytes < hyf_ssd_scan_workspace_bytes(cfg, T)) return HYF_EWORKSPACE;
-  const Shape s = make_shape(cfg);
+  if (y_opt && (!aligned(C_opt, 16) || !aligned(y_opt, 16))) return HYF_EINVAL;
+  if (!ws || !aligned(ws, ALIGN) || ws_bytes < hyf_ssd_scan_workspace_bytes(cfg, T, y_opt != nullptr))
+    return HYF_EWORKSPACE;
   ReqTable rt;
   memset(&rt, 0, sizeof(rt));
   rt.n_req = 1;
@@ -498,11 +528,16 @@ int hyf_ssd_scan(const hyf_config* cfg, const void* x, const void* B, const void
   sa.dt_bias = dt_bias;
   sa.state_pool = nullptr;
   sa.h_direct = H_inout;
-  const int64_t segs = scan_max_segs(s, cfg->dtype, 1, T);
+  const int64_t segs = scan_segs_bound(s, cfg->dtype, 1, T, y_opt != nullptr);
   sa.part = static_cast<float*>(ws);
   sa.lam = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((uint64_t)segs * s.nh * s.P * s.N * 4));
+  sa.y_mode = y_opt != nullptr;
+  sa.C = C_opt;
+  sa.cblk = (int64_t)s.gn * HYF_TBLK;
+  sa.y = y_opt;
+  sa.d_skip = d_skip;
   int32_t max_segs = 0;
-  fill_segments(s, cfg->dtype, &rt, &sa.chunks_per_seg, &sa.total_segs, &max_segs);
+  fill_segments(s, cfg->dtype, &rt, y_opt != nullptr, &sa.seg_tokens, &sa.total_segs, &max_segs);
   return hip_status(launch_ssd_state(cfg->dtype, s, sa, rt, max_segs, static_cast<hipStream_t>(stream)));
 }
 

@@ -39,8 +39,9 @@ struct RowSrc {
 hipError_t launch_linear(int dtype, RowSrc x, int64_t M, int K, const void* W, int Nout,
                          const Epi& epi, hipStream_t s);
 
-// Memory scan over segments (see hyf_scan.hip).  Inputs are time-blocked: element (feature f,
-// token t) of request i sits at [(blk0[i] + t / HYF_TBLK) * block_stride + f * HYF_TBLK + t % HYF_TBLK].
+// Memory scan over segments (see hyf_scan.hip).  Inputs are time-blocked: token t of request i
+// sits in block blk0[i] + t / HYF_TBLK (block stride *blk); x, B and C are tiled inside a block
+// (tile_off), dt is plain ([feature][HYF_TBLK]).
 struct ScanArgs {
   const void* x;      // x, feature h*P + p
   const void* B;      // B, feature g*N + n
@@ -52,11 +53,20 @@ struct ScanArgs {
   float* h_direct;    // single-request H (hyf_ssd_scan); overrides the pool when non-null
   float* part;        // [total_segs][nh][P][N] partial states
   float* lam;         // [total_segs][nh] segment log-decays
-  int32_t chunks_per_seg;
+  int32_t seg_tokens; // tokens per segment (a multiple of HYF_TBLK; the last one may be short)
   int32_t total_segs;
+  // per-token outputs (y-mode: segments of HYF_TBLK tokens; part then holds each segment's
+  // starting state): y [rows][nh][P] storage dtype, row = request row0 + token
+  int32_t y_mode;
+  const void* C;      // C, feature g*N + n, tiled like B
+  int64_t cblk;
+  void* y;
+  const float* d_skip;
 };
 // Longest segment (tokens) one scan workgroup takes: its per-token weights live in LDS.
 int64_t scan_max_seg_tokens(const Shape& sh, int esz);
+// Whether the y-mode kernel fits this shape (its segment's x, B, C live in LDS).
+bool scan_y_supported(const Shape& sh, int esz);
 // Scan workgroups per segment: heads x P-blocks x N-blocks.
 int64_t scan_items_per_seg(const Shape& sh);
 hipError_t launch_ssd_state(int dtype, const Shape& sh, const ScanArgs& a, const ReqTable& rt,

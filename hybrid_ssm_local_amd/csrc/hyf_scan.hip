@@ -80,7 +80,7 @@ k_ssd_seg(Shape sh, ScanArgs a, ReqTable rt, int npb, int nnb, int n_items, int 
   const int ls = q - rt.seg0[r];
   const int nseg = rt.seg0[r + 1] - rt.seg0[r];
   const int Tr = rt.row0[r + 1] - rt.row0[r];
-  const int seg_len = a.chunks_per_seg * sh.L;
+  const int seg_len = a.seg_tokens;
   const int s_begin = ls * seg_len;
   const int len = min(s_begin + seg_len, Tr) - s_begin;
   const int grp = h / (nh / sh.G);
@@ -313,7 +313,7 @@ k_ssd_seg(Shape sh, ScanArgs a, ReqTable rt, int npb, int nnb, int n_items, int 
   __syncthreads();
 
   float* dst;
-  if (nseg == 1) {
+  if (nseg == 1 && !a.y_mode) {
     dst = Hh;
   } else {
     dst = a.part + ((int64_t)q * nh + h) * P * N;
@@ -345,6 +345,108 @@ __global__ void __launch_bounds__(256) k_ssd_combine(Shape sh, ScanArgs a, ReqTa
                          : reinterpret_cast<float*>(a.state_pool + (int64_t)rt.slot[r] * sh.st_bytes + sh.st_h) +
                                (int64_t)h * PN;
   *reinterpret_cast<f32x4*>(Hh + e) = acc;
+}
+
+// y-mode fold: per (request, head), the state before every segment replaces that segment's
+// partial (segment 0 starts from H), and H becomes the state after the last segment.
+__global__ void __launch_bounds__(256) k_ssd_prefix(Shape sh, ScanArgs a, ReqTable rt) {
+  const int nh = sh.nh;
+  const int r = blockIdx.x / nh, h = blockIdx.x % nh;
+  const int s0 = rt.seg0[r], s1 = rt.seg0[r + 1];
+  if (s1 == s0) return;
+  const int64_t PN = (int64_t)sh.P * sh.N;
+  const int64_t e = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 4;
+  if (e >= PN) return;
+  float* Hh = a.h_direct ? a.h_direct + (int64_t)h * PN
+                         : reinterpret_cast<float*>(a.state_pool + (int64_t)rt.slot[r] * sh.st_bytes + sh.st_h) +
+                               (int64_t)h * PN;
+  f32x4* p0 = reinterpret_cast<f32x4*>(a.part + ((int64_t)s0 * nh + h) * PN + e);
+  f32x4 acc = *p0;  // segment 0's partial includes exp(lam_0) H
+  *p0 = *reinterpret_cast<const f32x4*>(Hh + e);
+  for (int s = s0 + 1; s < s1; ++s) {
+    const float d = expf(a.lam[(int64_t)s * nh + h]);
+    f32x4* ps = reinterpret_cast<f32x4*>(a.part + ((int64_t)s * nh + h) * PN + e);
+    const f32x4 p = *ps;
+    *ps = acc;
+    acc = acc * d + p;
+  }
+  *reinterpret_cast<f32x4*>(Hh + e) = acc;
+}
+
+// y-mode outputs: per (segment of HYF_TBLK tokens, head, block of up to 64 state rows), the
+// recurrence token by token from the segment's starting state, y_t = H_t . C_t + D x_t.  The
+// segment's x (this head), B and C go to LDS token-major; 16 threads share a state row, each with
+// N / 16 = NCH columns, and y_t of the row is their shuffle-reduced dot product.
+constexpr int YROWS = 64;
+template <typename T, int NCH>
+__global__ void __launch_bounds__(16 * YROWS) k_ssd_y(Shape sh, ScanArgs a, ReqTable rt, int npb) {
+  constexpr int VN = Vec16<T>::n;
+  typedef typename Vec16<T>::type V;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int nh = sh.nh, P = sh.P, N = sh.N;
+  const int pb = blockIdx.x % npb, h = (blockIdx.x / npb) % nh, q = blockIdx.x / (npb * nh);
+  const int r = find_request(rt, q);
+  const int ls = q - rt.seg0[r];
+  const int Tr = rt.row0[r + 1] - rt.row0[r];
+  const int s_begin = ls * TB;
+  const int len = min(TB, Tr - s_begin);
+  const int64_t blk = rt.blk0[r] + ls;  // y-mode segments are single blocks
+  const int grp = h / (nh / sh.G);
+  T* xs = reinterpret_cast<T*>(smem);   // [TB][P]
+  T* bs = xs + TB * P;                  // [TB][N]
+  T* cs = bs + TB * N;                  // [TB][N]
+  float* dts = reinterpret_cast<float*>(cs + TB * N);  // [TB] dt
+  float* dec = dts + TB;                               // [TB] exp(dt A)
+  const int t = threadIdx.x;
+  const int nt = blockDim.x;
+  // token-major staging from the tiled layout: a 16-byte chunk is VN consecutive tokens of one
+  // feature
+  auto stage = [&](const T* base, int64_t bstride, int f0, int F, T* dst) {
+    const int per = TB / VN;
+    for (int c = t; c < F * per; c += nt) {
+      const int f = c / per, tg = c % per;
+      const V v = *reinterpret_cast<const V*>(base + blk * bstride + tile_off<T>(f0 + f, tg * VN));
+#pragma unroll
+      for (int e = 0; e < VN; ++e) dst[(tg * VN + e) * F + f] = v[e];
+    }
+  };
+  stage(static_cast<const T*>(a.x), a.xblk, h * P, P, xs);
+  stage(static_cast<const T*>(a.B), a.bblk, grp * N, N, bs);
+  stage(static_cast<const T*>(a.C), a.cblk, grp * N, N, cs);
+  const float A = -expf(a.a_log[h]);
+  for (int u = t; u < TB; u += nt) {
+    const float d = u < len ? softplus_f(a.dt[blk * a.dblk + (int64_t)h * TB + u] + a.dt_bias[h]) : 0.f;
+    dts[u] = d;
+    dec[u] = expf(d * A);
+  }
+  __syncthreads();
+
+  const int c16 = t & 15;                 // column chunk of this thread
+  const int p = pb * YROWS + (t >> 4);    // state row of this thread
+  const bool active = p < P;
+  float Hr[NCH];
+  const float* Hs = a.part + ((int64_t)q * nh + h) * P * N;  // state before the segment
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) Hr[j] = active ? Hs[(int64_t)p * N + c16 * NCH + j] : 0.f;
+  const float D = a.d_skip[h];
+  T* y = static_cast<T*>(a.y) + ((int64_t)rt.row0[r] + s_begin) * nh * P + (int64_t)h * P + p;
+  for (int u = 0; u < len; ++u) {
+    const float xv = active ? to_f32(xs[u * P + p]) : 0.f;
+    const float w = dts[u] * xv, dk = dec[u];
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      Hr[j] = dk * Hr[j] + w * to_f32(bs[u * N + c16 * NCH + j]);
+      acc += Hr[j] * to_f32(cs[u * N + c16 * NCH + j]);
+    }
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    if (active && c16 == 0) y[(int64_t)u * nh * P] = from_f32<T>(acc + D * xv);
+  }
+}
+
+bool scan_y_supported(const Shape& sh, int esz) {
+  return (size_t)TB * (sh.P + 2 * sh.N) * esz + 2 * TB * sizeof(float) <= 160 * 1024 - 256;
 }
 
 // Workgroup geometry: an output block of PB16 x NB16 tiles of 16 x 16, the largest divisors of
@@ -398,7 +500,7 @@ static hipError_t launch_seg_t(const Shape& sh, const ScanArgs& a, const ReqTabl
   const SegGeo g = seg_geo(sh);
   const int n_items = (int)(a.total_segs * scan_items_per_seg(sh));
   const int per_xcd = (n_items + 7) / 8;
-  const size_t lds = scan_lds_bytes(sh, sizeof(T), (int64_t)a.chunks_per_seg * sh.L);
+  const size_t lds = scan_lds_bytes(sh, sizeof(T), a.seg_tokens);
   static std::once_flag once;
   static hipError_t set_err = hipSuccess;
   std::call_once(once, [] {
@@ -434,15 +536,59 @@ static hipError_t launch_seg(const Shape& sh, const ScanArgs& a, const ReqTable&
   return f ? f(sh, a, rt, s) : hipErrorInvalidValue;
 }
 
+template <typename T, int NCH>
+static hipError_t launch_y_t(const Shape& sh, const ScanArgs& a, const ReqTable& rt, hipStream_t s) {
+  const int npb = (sh.P + YROWS - 1) / YROWS;
+  const int rows = sh.P < YROWS ? sh.P : YROWS;
+  const size_t lds = (size_t)TB * (sh.P + 2 * sh.N) * sizeof(T) + 2 * TB * sizeof(float);
+  static std::once_flag once;
+  static hipError_t set_err = hipSuccess;
+  std::call_once(once, [] {
+    set_err = hipFuncSetAttribute(reinterpret_cast<const void*>(k_ssd_y<T, NCH>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 256);
+  });
+  if (set_err != hipSuccess) return set_err;
+  hipLaunchKernelGGL((k_ssd_y<T, NCH>), dim3(a.total_segs * sh.nh * npb), dim3(16 * rows), lds, s, sh, a, rt, npb);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_y(const Shape& sh, const ScanArgs& a, const ReqTable& rt, hipStream_t s) {
+  switch (sh.N / 16) {
+    case 1: return launch_y_t<T, 1>(sh, a, rt, s);
+    case 2: return launch_y_t<T, 2>(sh, a, rt, s);
+    case 3: return launch_y_t<T, 3>(sh, a, rt, s);
+    case 4: return launch_y_t<T, 4>(sh, a, rt, s);
+    case 5: return launch_y_t<T, 5>(sh, a, rt, s);
+    case 6: return launch_y_t<T, 6>(sh, a, rt, s);
+    case 7: return launch_y_t<T, 7>(sh, a, rt, s);
+    case 8: return launch_y_t<T, 8>(sh, a, rt, s);
+    case 9: return launch_y_t<T, 9>(sh, a, rt, s);
+    case 10: return launch_y_t<T, 10>(sh, a, rt, s);
+    case 11: return launch_y_t<T, 11>(sh, a, rt, s);
+    case 12: return launch_y_t<T, 12>(sh, a, rt, s);
+    case 13: return launch_y_t<T, 13>(sh, a, rt, s);
+    case 14: return launch_y_t<T, 14>(sh, a, rt, s);
+    case 15: return launch_y_t<T, 15>(sh, a, rt, s);
+    default: return launch_y_t<T, 16>(sh, a, rt, s);
+  }
+}
+
 hipError_t launch_ssd_state(int dtype, const Shape& sh, const ScanArgs& a, const ReqTable& rt,
                             int32_t max_segs_per_req, hipStream_t s) {
   if (a.total_segs <= 0) return hipSuccess;
   hipError_t e = dtype == HYF_BF16 ? launch_seg<bf16>(sh, a, rt, s) : launch_seg<float>(sh, a, rt, s);
-  if (e != hipSuccess || max_segs_per_req <= 1) return e;
+  if (e != hipSuccess) return e;
   const int64_t PN = (int64_t)sh.P * sh.N;
   dim3 grid((unsigned)rt.n_req * sh.nh, (unsigned)((PN / 4 + 255) / 256));
-  hipLaunchKernelGGL(k_ssd_combine, grid, dim3(256), 0, s, sh, a, rt);
-  return hipGetLastError();
+  if (!a.y_mode) {
+    if (max_segs_per_req <= 1) return hipSuccess;
+    hipLaunchKernelGGL(k_ssd_combine, grid, dim3(256), 0, s, sh, a, rt);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(k_ssd_prefix, grid, dim3(256), 0, s, sh, a, rt);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return dtype == HYF_BF16 ? launch_y<bf16>(sh, a, rt, s) : launch_y<float>(sh, a, rt, s);
 }
 
 }  // namespace hyf

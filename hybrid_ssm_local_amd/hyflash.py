@@ -57,8 +57,8 @@ _SIGS = {
     "hyf_n_in": (_i64, [_P(HyfConfig)]),
     "hyf_state_layout_get": (ctypes.c_int, [_P(HyfConfig), _P(HyfStateLayout)]),
     "hyf_state_bytes": (_sz, [_P(HyfConfig)]),
-    "hyf_workspace_bytes": (_sz, [_P(HyfConfig), _i32, _i64]),
-    "hyf_ssd_scan_workspace_bytes": (_sz, [_P(HyfConfig), _i64]),
+    "hyf_workspace_bytes": (_sz, [_P(HyfConfig), _i32, _i64, _i32]),
+    "hyf_ssd_scan_workspace_bytes": (_sz, [_P(HyfConfig), _i64, _i32]),
     "hyf_state_reset": (ctypes.c_int, [_P(HyfConfig), _vp, _i32, _vp, _i32, _vp]),
     "hyf_memory_commit": (ctypes.c_int, [_P(HyfConfig), _P(HyfWeights), _vp, _i32, _vp, _i32, _vp, _vp, _vp,
                                          _vp, _sz, _vp]),
@@ -163,12 +163,12 @@ def hyf_state_bytes(cfg: HyfConfig) -> int:
     return lib().hyf_state_bytes(ctypes.byref(cfg))
 
 
-def hyf_workspace_bytes(cfg: HyfConfig, max_requests: int, max_rows: int) -> int:
-    return lib().hyf_workspace_bytes(ctypes.byref(cfg), max_requests, max_rows)
+def hyf_workspace_bytes(cfg: HyfConfig, max_requests: int, max_rows: int, with_y: int = 0) -> int:
+    return lib().hyf_workspace_bytes(ctypes.byref(cfg), max_requests, max_rows, int(with_y))
 
 
-def hyf_ssd_scan_workspace_bytes(cfg: HyfConfig, T: int) -> int:
-    return lib().hyf_ssd_scan_workspace_bytes(ctypes.byref(cfg), T)
+def hyf_ssd_scan_workspace_bytes(cfg: HyfConfig, T: int, with_y: int = 0) -> int:
+    return lib().hyf_ssd_scan_workspace_bytes(ctypes.byref(cfg), T, int(with_y))
 
 
 def hyf_state_reset(cfg, pool, pool_slots, slots, n_req, stream=None) -> int:
@@ -260,7 +260,7 @@ class DrafterLayer:
     """Owns one layer's device weights, a state pool and a workspace; forwards to the C ABI."""
 
     def __init__(self, shape: LayerShape, weights: dict, pool_slots: int = 1, max_requests: int = 1,
-                 max_rows: int = 8, device: str = "cuda"):
+                 max_rows: int = 8, with_y: bool = False, device: str = "cuda"):
         import torch
 
         self.shape, self.device = shape, device
@@ -277,16 +277,18 @@ class DrafterLayer:
         self.state_bytes = hyf_state_bytes(self.cfg)
         self.layout = hyf_state_layout_get(self.cfg)
         self.pool = torch.zeros(pool_slots * self.state_bytes, dtype=torch.uint8, device=device)
-        self.ws_bytes = hyf_workspace_bytes(self.cfg, max_requests, max_rows)
+        self.ws_bytes = hyf_workspace_bytes(self.cfg, max_requests, max_rows, with_y)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
 
     def reset(self, slots=None, n_req=None, stream=None):
         n = n_req if n_req is not None else (len(slots) if slots is not None else self.pool_slots)
         check(hyf_state_reset(self.cfg, self.pool, self.pool_slots, slots, n, stream), "hyf_state_reset")
 
-    def commit(self, feats, cu_rows, slots=None, stream=None):
+    def commit(self, feats, cu_rows, slots=None, y=None, stream=None):
+        """Commit rows; y (optional, [rows][nh][P] storage dtype) receives the per-token outputs
+        (needs a layer built with with_y=True)."""
         n_req = len(cu_rows) - 1
-        check(hyf_memory_commit(self.cfg, self.w, self.pool, self.pool_slots, slots, n_req, feats, cu_rows, None,
+        check(hyf_memory_commit(self.cfg, self.w, self.pool, self.pool_slots, slots, n_req, feats, cu_rows, y,
                                 self.ws, self.ws_bytes, stream), "hyf_memory_commit")
 
     def draft(self, block_in, block_out, commit_feats=None, cu_commit=None, slots=None, stream=None):

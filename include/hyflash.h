@@ -113,8 +113,9 @@ size_t hyf_state_bytes(const hyf_config* cfg);
 
 /* Host only.  Workspace bytes that hyf_memory_commit and hyf_draft_block need for up to
  * max_requests requests and up to max_rows committed rows in one call (summed over the
- * requests).  0 on bad arguments. */
-size_t hyf_workspace_bytes(const hyf_config* cfg, int32_t max_requests, int64_t max_rows);
+ * requests); with_y != 0 sizes it for hyf_memory_commit with per-token outputs (y_opt), which
+ * keeps one P x N state per 128 committed rows.  0 on bad arguments. */
+size_t hyf_workspace_bytes(const hyf_config* cfg, int32_t max_requests, int64_t max_rows, int32_t with_y);
 
 /* Empties the named states: count = 0, H = 0, ring zeroed.
  * slots (host, nullable): pool index of each request; NULL means 0..n_req-1. */
@@ -131,9 +132,11 @@ int hyf_state_reset(const hyf_config* cfg, void* state_pool, int32_t pool_slots,
  * Any row count works (a prefill of a whole prefix, or the 1-8 rows of a round).
  * cu_rows (host): int64 [n_req + 1], cu_rows[0] = 0, non-decreasing.  Empty requests
  * are left bit-identical.
- * y_opt (nullable): [cu_rows[n_req]][nh][P] storage dtype, per-token memory outputs
- * y_t = H_t . C_t + D * v_t (H_t after token t).
- * ws: at least hyf_workspace_bytes(cfg, n_req, cu_rows[n_req]) bytes, 256-byte aligned. */
+ * y_opt (nullable, 16-byte aligned): [cu_rows[n_req]][nh][P] storage dtype, per-token memory
+ * outputs y_t = H_t . C_t + D * v_t (H_t after token t, C_t from w_in); HYF_EUNSUPPORTED when a
+ * 128-token block of x, B and C does not fit one workgroup's LDS (fp32 with P + 2N > 320).
+ * ws: at least hyf_workspace_bytes(cfg, n_req, cu_rows[n_req], y_opt != NULL) bytes, 256-byte
+ * aligned. */
 int hyf_memory_commit(const hyf_config* cfg, const hyf_weights* w, void* state_pool,
                       int32_t pool_slots, const int32_t* slots, int32_t n_req, const void* feats,
                       const int64_t* cu_commit, void* y_opt, void* ws, size_t ws_bytes,
@@ -151,7 +154,7 @@ int hyf_memory_commit(const hyf_config* cfg, const hyf_weights* w, void* state_p
  *   mem  = H . C_q + D * v   (H is read, never written);
  *   block_out [n_req][block][d_model] = concat_heads(attn + mem) . w_out^T.
  * Drafting never writes the state: with commit_feats == NULL the state pool is left bit-
- * identical.  ws: at least hyf_workspace_bytes(cfg, n_req, cu_commit[n_req]) bytes. */
+ * identical.  ws: at least hyf_workspace_bytes(cfg, n_req, cu_commit[n_req], 0) bytes. */
 int hyf_draft_block(const hyf_config* cfg, const hyf_weights* w, void* state_pool,
                     int32_t pool_slots, const int32_t* slots, int32_t n_req,
                     const void* commit_feats, const int64_t* cu_commit, const void* block_in,
@@ -167,8 +170,9 @@ int hyf_draft_block(const hyf_config* cfg, const hyf_weights* w, void* state_poo
 int hyf_linear(const hyf_config* cfg, const void* X, int64_t M, int32_t K, const void* W,
                int32_t Nout, void* out, int32_t out_f32, void* stream);
 
-/* Host only.  Workspace bytes hyf_ssd_scan needs for T tokens. */
-size_t hyf_ssd_scan_workspace_bytes(const hyf_config* cfg, int64_t T);
+/* Host only.  Workspace bytes hyf_ssd_scan needs for T tokens, with (with_y != 0) or without
+ * per-token outputs. */
+size_t hyf_ssd_scan_workspace_bytes(const hyf_config* cfg, int64_t T, int32_t with_y);
 
 /* The memory's scan on pre-projected inputs, one request (explainer "Jargon": Mamba-2 folds
  * each input into a fixed-size state with an input-dependent step size and a learned decay).
@@ -188,7 +192,8 @@ size_t hyf_ssd_scan_workspace_bytes(const hyf_config* cfg, int64_t T);
  * Entries of the last block past T are never read into the result (they may hold anything).
  * x, B and dt_raw 16-byte aligned.
  * H_inout [nh][P][N] fp32 holds the initial state on entry and the final state on exit.
- * y_opt [T][nh][P] storage dtype.  T = 0 is a no-op. */
+ * y_opt [T][nh][P] storage dtype, 16-byte aligned (HYF_EUNSUPPORTED as for hyf_memory_commit).
+ * ws: at least hyf_ssd_scan_workspace_bytes(cfg, T, y_opt != NULL) bytes.  T = 0 is a no-op. */
 int hyf_ssd_scan(const hyf_config* cfg, const void* x, const void* B, const void* C_opt,
                  const float* dt_raw, const float* a_log, const float* dt_bias,
                  const float* d_skip, float* H_inout, void* y_opt, int64_t T, void* ws,

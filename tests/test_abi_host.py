@@ -77,6 +77,28 @@ def test_workspace_grows_with_requests_and_rows():
     assert hf.hyf_workspace_bytes(cfg, 0, 8) == 0
     assert hf.hyf_workspace_bytes(cfg, hf.HYF_MAX_REQUESTS + 1, 8) == 0
     assert hf.hyf_ssd_scan_workspace_bytes(cfg, 8192) > 0
+    # per-token outputs keep one state per 128-token block
+    assert hf.hyf_workspace_bytes(cfg, 1, 8192, 1) >= b
+    assert hf.hyf_ssd_scan_workspace_bytes(cfg, 8192, 1) >= 64 * 32 * 80 * 128 * 4
+
+
+def test_per_token_outputs_beyond_lds_are_unsupported():
+    # fp32 with head_dim + 2 d_state > 320: a 128-token block of x, B and C exceeds one
+    # workgroup's LDS, so y is refused before any device work (the state-only scan still runs).
+    shape = I.LayerShape(d_model=256, n_heads=2, head_dim=128, d_state=128, window=16, chunk=64, dtype="f32")
+    cfg = hf.make_config(shape)
+    assert hf.hyf_config_check(cfg) == hf.HYF_OK
+    fake = 1 << 20
+    w = hf.HyfWeights(fake, fake, fake, fake, fake)
+    assert hf.hyf_ssd_scan(cfg, fake, fake, fake, fake, fake, fake, fake, fake, fake, 4, fake, 1 << 30, 0) == \
+        hf.HYF_EUNSUPPORTED
+    assert hf.hyf_memory_commit(cfg, w, fake, 1, None, 1, fake, [0, 4], fake, fake, 1 << 30, 0) == \
+        hf.HYF_EUNSUPPORTED
+    # bf16 of the same sizes fits
+    cfg_b = hf.make_config(I.LayerShape(d_model=256, n_heads=2, head_dim=128, d_state=128, window=16, chunk=64,
+                                        dtype="bf16"))
+    assert hf.hyf_ssd_scan(cfg_b, fake, fake, fake, fake, fake, fake, fake, fake, fake, 4, fake, 16, 0) == \
+        hf.HYF_EWORKSPACE
 
 
 def test_invalid_calls_fail_before_any_device_work():

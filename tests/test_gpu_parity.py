@@ -46,20 +46,26 @@ def small_shape(dtype, **kw):
 # ---------------------------------------------------------------- scan level
 
 
-def run_scan(shape, sc, T):
-    # Tokens past T in the last time block hold NaN: none may reach the state.
+def run_scan(shape, sc, T, with_y=False):
+    # Tokens past T in the last time block hold NaN: none may reach the state or y.
     cfg = hf.make_config(shape)
-    x = hf.to_device(hf.time_tiled(sc["x"], T, hf.elem_bytes(shape), np.nan), shape)
-    B = hf.to_device(hf.time_tiled(sc["B"], T, hf.elem_bytes(shape), np.nan), shape)
+    eb = hf.elem_bytes(shape)
+    x = hf.to_device(hf.time_tiled(sc["x"], T, eb, np.nan), shape)
+    B = hf.to_device(hf.time_tiled(sc["B"], T, eb, np.nan), shape)
+    C = hf.to_device(hf.time_tiled(sc["C"], T, eb, np.nan), shape) if with_y else None
     dt = torch.from_numpy(hf.time_blocked(sc["dt_raw"], T, np.nan)).to(DEV)
     a_log = torch.from_numpy(sc["a_log"]).to(DEV)
     dt_bias = torch.from_numpy(sc["dt_bias"]).to(DEV)
     d_skip = torch.from_numpy(sc["d_skip"]).to(DEV)
     H = torch.from_numpy(sc["H0"]).to(DEV).contiguous()
-    wsb = hf.hyf_ssd_scan_workspace_bytes(cfg, T)
+    y = torch.full((T, shape.n_heads, shape.head_dim), float("nan"), dtype=hf.torch_dtype(shape), device=DEV) \
+        if with_y else None
+    wsb = hf.hyf_ssd_scan_workspace_bytes(cfg, T, with_y)
     ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=DEV)
-    hf.check(hf.hyf_ssd_scan(cfg, x, B, None, dt, a_log, dt_bias, d_skip, H, None, T, ws, wsb), "hyf_ssd_scan")
+    hf.check(hf.hyf_ssd_scan(cfg, x, B, C, dt, a_log, dt_bias, d_skip, H, y, T, ws, wsb), "hyf_ssd_scan")
     torch.cuda.synchronize()
+    if with_y:
+        return H.cpu().numpy(), y.float().cpu().numpy()
     return H.cpu().numpy()
 
 
@@ -82,6 +88,33 @@ def test_scan_state_matches_the_sequential_recurrence(name, shape, Ts):
         ref, _ = O.ssd_sequential(sc["x"], sc["B"], None, sc["dt_raw"], sc["a_log"], sc["dt_bias"], sc["d_skip"],
                                   sc["H0"], shape.n_groups)
         assert_close(H, ref, shape.dtype, f"{name} T={T}")
+
+
+Y_CASES = [
+    ("tiny_fp32", I.TINY, [1, 127, 128, 129, 300]),
+    ("qwen_bf16", I.QWEN, [7, 200]),
+    ("phi4_bf16_L256", I.PHI4_LONG, [255, 300]),
+    ("odd_bf16", small_shape("bf16", n_heads=3, head_dim=48, d_state=80, n_groups=3, chunk=32), [1, 100]),
+    ("odd_fp32", small_shape("f32", n_heads=6, head_dim=32, d_state=48, n_groups=2, chunk=32), [37, 260]),
+]
+
+
+@pytest.mark.parametrize("name,shape,Ts", Y_CASES, ids=[c[0] for c in Y_CASES])
+def test_scan_per_token_outputs_match_the_sequential_recurrence(name, shape, Ts):
+    for T in Ts:
+        rng = I.rng_streams(1000 + T)[0]
+        sc = I.make_scan_inputs(shape, T, rng, with_c=True, h0_scale=0.5)
+        # C scaled by a power of two near 1/sqrt(N) (exact in the storage dtype), so that y is of
+        # order one like the layer's outputs, where the absolute bound means something
+        sc["C"] = sc["C"] * np.float32(2.0 ** -round(np.log2(np.sqrt(shape.d_state))))
+        say("hyf_ssd_scan y", name, "T", T)
+        H, y = run_scan(shape, sc, T, with_y=True)
+        refH, refy = O.ssd_sequential(sc["x"], sc["B"], sc["C"], sc["dt_raw"], sc["a_log"], sc["dt_bias"],
+                                      sc["d_skip"], sc["H0"], shape.n_groups)
+        assert_close(H, refH, shape.dtype, f"{name} T={T} H")
+        assert_close(y, refy, shape.dtype, f"{name} T={T} y")
+        # the y-mode state equals the state-only scan's
+        assert_close(H, run_scan(shape, sc, T), shape.dtype, f"{name} T={T} H vs state-only")
 
 
 def test_scan_full_size_qwen_prefix_sampled_heads():
@@ -205,6 +238,40 @@ def test_rounds_match_the_oracle(name, shape):
     say("hyf_memory_commit small", name)
     pr.commit([pr.rows(5)])
     pr.check_state(what=f"{name} small commit")
+
+
+Y_LAYER_SHAPES = [
+    ("tiny_fp32", I.TINY),
+    ("small_bf16", small_shape("bf16", window=40)),
+    ("odd_bf16", small_shape("bf16", n_heads=5, head_dim=48, d_state=32, n_groups=5, window=20, chunk=32)),
+]
+
+
+@pytest.mark.parametrize("name,shape", Y_LAYER_SHAPES, ids=[c[0] for c in Y_LAYER_SHAPES])
+def test_commit_per_token_outputs_match_the_oracle(name, shape):
+    # Ragged multi-request commits with y; rows of one request never leak into another's y, and the
+    # state they leave is the one the oracle's commit leaves.
+    pr = Pair(shape, seed=61, pool_slots=4, max_requests=4, max_rows=700)
+    pr.gpu = hf.DrafterLayer(shape, pr.w, pool_slots=4, max_requests=4, max_rows=700, with_y=True)
+    pr.gpu.reset()
+    for step, lens in enumerate(([200, 0, 129, 1], [5, 300, 8, 128])):
+        feats = [pr.rows(n) for n in lens]
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+        y = torch.full((int(cu[-1]), shape.n_heads, shape.head_dim), float("nan"), dtype=hf.torch_dtype(shape),
+                       device=DEV)
+        say("hyf_memory_commit y", name, "lens", lens)
+        pr.gpu.commit(hf.to_device(np.concatenate(feats), shape), cu, y=y)
+        torch.cuda.synchronize()
+        got = y.float().cpu().numpy()
+        for i, f in enumerate(feats):
+            pr.ost[i], ref = O.commit(shape, pr.wo, pr.ost[i], f, want_y=True)
+            assert_close(got[cu[i]:cu[i + 1]], ref, shape.dtype, f"{name} step {step} request {i} y")
+        for i in range(4):
+            pr.check_state(slot=i, what=f"{name} step {step} request {i}")
+    # a round afterwards sees the same memory as the oracle
+    say("hyf_draft_block after y commits", name)
+    g, o = pr.draft([pr.rows(8, 3) for _ in range(4)], commits=[pr.rows(a) for a in (0, 3, 8, 1)])
+    assert_close(g, o, shape.dtype, f"{name} round after y")
 
 
 def test_qwen_full_size_prefill_and_rounds():
