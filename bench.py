@@ -209,7 +209,7 @@ def kernel_loops(torch, hf, I, ep, reps, with_gemm=True):
 COPY_BYTES = 256 << 20
 PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 PMC_KERNELS = {  # key -> (kernel name prefix in the profile, source file)
-    "proj": ("_ZN3hyf12k_proj_small", "hybrid_ssm_local_amd/csrc/hyf_proj.hip"),
+    "proj": ("_ZN3hyf13k_proj_stream", "hybrid_ssm_local_amd/csrc/hyf_proj.hip"),
     "scan": ("void hyf::k_ssd_seg", "hybrid_ssm_local_amd/csrc/hyf_scan.hip"),
 }
 
@@ -436,7 +436,7 @@ def main():
                                      "bytes_per_launch": scan["bytes"]}},
         "roofline": {"bound": "hbm", "achieved": proj["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": proj["gbs"] / HBM_PEAK_GBS, "traffic": pmc_traffic("proj"),
-                     "kernel": "k_proj_small<bf16,8,1>: input projection of a round (12 rows x w_in)",
+                     "kernel": "k_proj_stream<8,1>: input projection of a round (12 rows x w_in)",
                      "bytes_per_launch": proj["bytes"], "avg_us": proj["mean_us"]},
         "gemm_roofline": {"bound": "mfma", "achieved": gemm["tflops"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                           "frac": gemm["tflops"] / BF16_PEAK_TFLOPS,

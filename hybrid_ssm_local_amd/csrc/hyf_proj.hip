@@ -1,12 +1,15 @@
 // Projections of the drafter layer: out[m][f] = sum_k X[m][k] * W[f][k].
 //
-// Two kernels, chosen by the number of rows M:
-//  * k_proj_small (M <= 64): the batch-1 round.  The layer's weights are read from HBM exactly
-//    once; every 16 output features are one workgroup whose waves split K into slabs and
-//    reduce their partial tiles through LDS in a fixed order (deterministic).  MFMA 16x16
-//    tiles: W is the A operand (16 features), X^T the B operand (16 rows per tile).
+// Kernels, chosen by the number of rows M:
+//  * k_proj_stream (bf16) and k_proj_small (fp32), M <= 64: the batch-1 round.  The layer's
+//    weights are read from HBM exactly once; every 16 output features are one workgroup whose
+//    waves split K into slabs and reduce their partial tiles through LDS in a fixed order
+//    (deterministic).  MFMA 16x16 tiles: W is the A operand (16 features), X^T the B operand
+//    (16 rows per tile).
 //  * k_gemm_bf16 (large M): prefill and batched rounds.  128x128 macro tiles, K step 64,
 //    double-buffered LDS, 4 waves of 64x64 each built from 16x16x32 bf16 MFMAs.
+#include <mutex>
+
 #include "hyf_launch.h"
 
 namespace hyf {
@@ -132,6 +135,111 @@ k_proj_small(RowSrc xs, int M, int K, const T* __restrict__ W, int Nout, Epi epi
     const int f = f0 + fl;
     const int m = m_base + mt * 16 + ml;
     if (f < Nout && m < M) epi_store<T>(epi, m, f, v);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// bf16, M <= 64: the same K split and MFMA order as k_proj_small (bit-identical results), but the
+// weight rows and the x rows of a slab reach LDS by direct loads: one instruction moves 4 rows x
+// 256 contiguous bytes (the register path moves 16 rows x 64 bytes per instruction, which costs
+// the address unit twice as many cycles per byte).  Slot (r, p) of a 16-row x 256-byte tile holds
+// the row's 16-byte chunk p ^ r, so the fragment reads of 16 lanes (16 rows, one chunk) fall in 16
+// different bank groups.  Each wave owns its LDS region, so only its own load count is waited on.
+constexpr int PS_SLAB = 128;  // k per slab: 256 bytes of a row
+
+__device__ __forceinline__ void lgkm_wait0() {
+  // lgkmcnt(0), vmcnt and expcnt at their no-wait maxima
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+}
+
+template <int NW, int MT>
+__global__ void __launch_bounds__(NW * 64)
+k_proj_stream(RowSrc xs, int M, int K, const bf16* __restrict__ W, int Nout, Epi epi) {
+  constexpr int XT = MT < 2 ? MT : 2;  // x tiles staged at once
+  constexpr int PASSES = (MT + XT - 1) / XT;
+  constexpr int PER = 4096 * (1 + XT);  // LDS bytes per wave: the weight tile and XT x tiles
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = lane & 15, g = lane >> 4;
+  const int p = lane & 15, r4 = lane >> 4;  // the lane's slot in a direct-load instruction
+  const int f0 = blockIdx.x * 16;
+  if (epi.zero && blockIdx.x == 0 && blockIdx.y == 0)
+    for (int z = threadIdx.x; z < epi.n_zero; z += NW * 64) epi.zero[z] = 0;
+  const int m_base = blockIdx.y * 16 * MT;
+  char* wl = smem + wave * PER;
+  char* xl = wl + 4096;
+
+  f32x4 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nslab = (K + PS_SLAB - 1) / PS_SLAB;
+  for (int s = wave; s < nslab; s += NW) {
+    const int kb = s * PS_SLAB;
+    lgkm_wait0();  // the previous slab's fragment reads are done before its regions are refilled
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 4 * j + r4;
+      const int k = kb + ((p ^ r) << 3);
+      if (k < K) lds_dma16(W + (int64_t)min(f0 + r, Nout - 1) * K + k, wl + j * 1024);
+    }
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+      if (ps > 0) lgkm_wait0();
+#pragma unroll
+      for (int xt = 0; xt < XT; ++xt) {
+        const int mt = ps * XT + xt;
+        if (mt < MT) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int r = 4 * j + r4;
+            const int m = m_base + mt * 16 + r;
+            const int k = kb + ((p ^ r) << 3);
+            // rows past M stay unloaded: they only feed output columns that are never stored
+            if (m < M && k < K)
+              lds_dma16(static_cast<const bf16*>(row_ptr(xs, m, K, 2)) + k, xl + xt * 4096 + j * 1024);
+          }
+        }
+      }
+      vm_wait<0>();
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        // MFMA u contracts k = kb + 32 u + 8 g .. + 7 (chunk g + 4 u), as k_proj_small does; chunks
+        // past K are zero on both operands
+        const int c = g + 4 * u;
+        const bool ok = kb + c * 8 < K;
+        const int o = i * 256 + ((c ^ i) << 4);
+        const bf16x8 a = ok ? *reinterpret_cast<const bf16x8*>(wl + o) : bf16x8{};
+#pragma unroll
+        for (int xt = 0; xt < XT; ++xt) {
+          const int mt = ps * XT + xt;
+          if (mt < MT) {
+            const bf16x8 b = ok ? *reinterpret_cast<const bf16x8*>(xl + xt * 4096 + o) : bf16x8{};
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[mt], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+
+  // Cross-wave reduction in a fixed order (the LDS regions are free once every wave is here).
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);  // [NW][MT][4][64]
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[((wave * MT + mt) * 4 + r) * 64 + lane] = acc[mt][r];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < MT * 256; idx += NW * 64) {
+    const int mt = idx >> 8, rem = idx & 255;
+    const int fl = rem & 15, ml = rem >> 4;
+    const int src_lane = (fl >> 2) * 16 + ml, r = fl & 3;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) v += red[((w * MT + mt) * 4 + r) * 64 + src_lane];
+    const int f = f0 + fl;
+    const int m = m_base + mt * 16 + ml;
+    if (f < Nout && m < M) epi_store<bf16>(epi, m, f, v);
   }
 }
 
@@ -280,13 +388,45 @@ static hipError_t launch_small_nw(RowSrc x, int M, int K, const T* W, int Nout, 
   return hipGetLastError();
 }
 
+template <int NW, int MT>
+static hipError_t launch_stream_t(RowSrc x, int M, int K, const bf16* W, int Nout, const Epi& epi, hipStream_t s) {
+  constexpr int XT = MT < 2 ? MT : 2;
+  const size_t lds = (size_t)NW * 4096 * (1 + XT);
+  static std::once_flag once;
+  static hipError_t set_err = hipSuccess;
+  std::call_once(once, [] {
+    set_err = hipFuncSetAttribute(reinterpret_cast<const void*>(k_proj_stream<NW, MT>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 256);
+  });
+  if (set_err != hipSuccess) return set_err;
+  dim3 grid((Nout + 15) / 16, (M + 16 * MT - 1) / (16 * MT));
+  hipLaunchKernelGGL((k_proj_stream<NW, MT>), grid, dim3(NW * 64), lds, s, x, M, K, W, Nout, epi);
+  return hipGetLastError();
+}
+
+template <int NW>
+static hipError_t launch_stream_nw(RowSrc x, int M, int K, const bf16* W, int Nout, const Epi& epi, hipStream_t s) {
+  const int mt = (M + 15) / 16;
+  switch (mt >= 4 ? 4 : mt) {
+    case 1: return launch_stream_t<NW, 1>(x, M, K, W, Nout, epi, s);
+    case 2: return launch_stream_t<NW, 2>(x, M, K, W, Nout, epi, s);
+    case 3: return launch_stream_t<NW, 3>(x, M, K, W, Nout, epi, s);
+    default: return launch_stream_t<NW, 4>(x, M, K, W, Nout, epi, s);
+  }
+}
+
 template <typename T>
 static hipError_t launch_small(RowSrc x, int M, int K, const T* W, int Nout, const Epi& epi, hipStream_t s) {
   // The split of K over waves depends on K alone, so an output element is reduced in the same
   // order whatever rows and columns share the launch (a fused round and a standalone commit give
   // bit-identical projections).  Long rows use 8 waves to keep more loads in flight.
-  if (K >= 2048) return launch_small_nw<T, 8>(x, M, K, W, Nout, epi, s);
-  return launch_small_nw<T, 4>(x, M, K, W, Nout, epi, s);
+  if constexpr (sizeof(T) == 2) {
+    if (K >= 2048) return launch_stream_nw<8>(x, M, K, W, Nout, epi, s);
+    return launch_stream_nw<4>(x, M, K, W, Nout, epi, s);
+  } else {
+    if (K >= 2048) return launch_small_nw<T, 8>(x, M, K, W, Nout, epi, s);
+    return launch_small_nw<T, 4>(x, M, K, W, Nout, epi, s);
+  }
 }
 
 hipError_t launch_linear(int dtype, RowSrc x, int64_t M, int K, const void* W, int Nout, const Epi& epi,

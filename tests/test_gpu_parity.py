@@ -151,6 +151,56 @@ def test_scan_zero_length_is_a_noop():
     assert np.array_equal(H.cpu().numpy(), sc["H0"])
 
 
+# ---------------------------------------------------------------- projection level
+
+LINEAR_CASES = [  # (dtype, K, Nout, Ms): K tails past a 128-wide slab, M across 16-row tiles
+    ("bf16", 144, 7, [1, 16, 17, 40, 64, 65, 200]),
+    ("bf16", 2560, 300, [1, 12, 16, 33, 64, 130]),
+    ("bf16", 5120, 40, [8, 49]),
+    ("f32", 256, 100, [1, 20, 64, 65]),
+]
+
+
+@pytest.mark.parametrize("dtype,K,Nout,Ms", LINEAR_CASES, ids=[f"{c[0]}_K{c[1]}" for c in LINEAR_CASES])
+def test_linear_matches_the_oracle(dtype, K, Nout, Ms):
+    shape = small_shape(dtype)
+    cfg = hf.make_config(shape)
+    rng = I.rng_streams(K + Nout)
+    Wt = I.make_rows(rng[0], Nout, K, 1.0 / np.sqrt(K), dtype)
+    Wd = hf.to_device(Wt, shape)
+    for M in Ms:
+        X = I.make_rows(rng[1], M, K, 1.0, dtype)
+        Xd = hf.to_device(X, shape)
+        ref = O.project(X, Wt)
+        for out_f32 in (1, 0):
+            out = torch.full((M, Nout), float("nan"), device=DEV,
+                             dtype=torch.float32 if out_f32 else hf.torch_dtype(shape))
+            say("hyf_linear", dtype, "M", M, "K", K, "N", Nout, "f32 out" if out_f32 else "storage out")
+            hf.check(hf.hyf_linear(cfg, Xd, M, K, Wd, Nout, out, out_f32), "hyf_linear")
+            torch.cuda.synchronize()
+            assert_close(out.float().cpu().numpy(), ref, dtype, f"linear M={M} K={K} out_f32={out_f32}")
+
+
+def test_linear_rows_do_not_depend_on_the_batch():
+    # A row's projection is bit-identical whatever other rows share the call (M <= 64): the K split
+    # over waves depends on K alone.
+    shape = I.QWEN
+    cfg = hf.make_config(shape)
+    rng = I.rng_streams(77)
+    K, Nout = shape.d_model, 200
+    Wd = hf.to_device(I.make_rows(rng[0], Nout, K, 1.0 / np.sqrt(K), "bf16"), shape)
+    X = hf.to_device(I.make_rows(rng[1], 64, K, 1.0, "bf16"), shape)
+    outs = {}
+    for M in (64, 33, 16, 5, 1):
+        out = torch.empty(M, Nout, device=DEV, dtype=torch.float32)
+        say("hyf_linear batch independence M", M)
+        hf.check(hf.hyf_linear(cfg, X, M, K, Wd, Nout, out, 1), "hyf_linear")
+        torch.cuda.synchronize()
+        outs[M] = out.cpu()
+    for M in (33, 16, 5, 1):
+        assert torch.equal(outs[M], outs[64][:M]), M
+
+
 # ---------------------------------------------------------------- layer level
 
 
