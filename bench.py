@@ -208,9 +208,9 @@ def kernel_loops(torch, hf, I, ep, reps, with_gemm=True):
 # COPY_BYTES).  The figures stay valid only for the kernel sources they were taken from.
 COPY_BYTES = 256 << 20
 PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
-PMC_KERNELS = {  # key -> (kernel name prefix in the profile, source file)
-    "proj": ("_ZN3hyf13k_proj_stream", "hybrid_ssm_local_amd/csrc/hyf_proj.hip"),
-    "scan": ("void hyf::k_ssd_seg", "hybrid_ssm_local_amd/csrc/hyf_scan.hip"),
+PMC_KERNELS = {  # key -> (kernel name as it appears in the profile, mangled or not; source file)
+    "proj": ("k_proj_stream", "hybrid_ssm_local_amd/csrc/hyf_proj.hip"),
+    "scan": ("k_ssd_seg", "hybrid_ssm_local_amd/csrc/hyf_scan.hip"),
 }
 
 
@@ -256,7 +256,7 @@ def pmc_summary(fetch_db, write_db):
     out = {"copy_bytes": COPY_BYTES, "copy_fetch_kib": copy_f, "copy_write_kib": copy_w,
            "fetch_scale": scale_f, "write_scale": scale_w, "kernels": {}}
     for key, (prefix, src) in PMC_KERNELS.items():
-        names = [k for k in fetch if k.startswith(prefix)]
+        names = [k for k in fetch if prefix in k]
         if not names:
             continue
         k = names[0]
