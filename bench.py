@@ -184,6 +184,23 @@ def kernel_loops(torch, hf, I, ep, reps, with_gemm=True):
                        gbs=sbytes / (mean_ms * 1e-3) / 1e9, feats_per_s=T / (mean_ms * 1e-3))
     if not with_gemm:
         return out
+    # 2b. the same scan with per-token outputs y (C in, y out)
+    sc_c = I.make_scan_inputs(sh, T, I.rng_streams(101)[0], with_c=True, h0_scale=0.0)
+    CT = hf.to_device(hf.time_tiled(sc_c["C"], T, hf.elem_bytes(sh)), sh)
+    y = torch.empty((T, nh, P), dtype=torch.bfloat16, device="cuda")
+    wsy = hf.hyf_ssd_scan_workspace_bytes(cfg, T, 1)
+    wy = torch.empty(wsy, dtype=torch.uint8, device="cuda")
+
+    def scan_y(i):
+        c = scan_in[i % N_COPIES]
+        st[0] |= hf.hyf_ssd_scan(cfg, c["x"], c["B"], CT, c["dt"], ep.a_log, ep.dt_bias, ep.d_skip, c["H"],
+                                 y, T, wy, wsy)
+
+    scan_y(0)
+    mean_ms, med_ms = time_calls(torch, scan_y, max(4, reps // 4))
+    ybytes = sbytes + T * (sh.gn * 2 + nh * P * 2)
+    out["scan_y"] = dict(mean_us=mean_ms * 1e3, median_us=med_ms * 1e3, bytes=ybytes,
+                         gbs=ybytes / (mean_ms * 1e-3) / 1e9, feats_per_s=T / (mean_ms * 1e-3))
     # 3. prefill projection GEMM (v | B | dt columns over the whole prefix)
     nvbd = sh.dq + sh.gn + nh
     g = torch.empty((T, nvbd), dtype=torch.bfloat16, device="cuda")
@@ -434,6 +451,11 @@ def main():
                         "roofline": {"bound": "hbm", "achieved": scan["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                      "frac": scan["gbs"] / HBM_PEAK_GBS, "traffic": pmc_traffic("scan"),
                                      "bytes_per_launch": scan["bytes"]}},
+        "commit_scan_y": {"value": kl["scan_y"]["feats_per_s"], "unit": "committed feats/s", "T": ep.T,
+                          "avg_us": kl["scan_y"]["mean_us"],
+                          "roofline": {"bound": "hbm", "achieved": kl["scan_y"]["gbs"], "peak": HBM_PEAK_GBS,
+                                       "unit": "GB/s", "frac": kl["scan_y"]["gbs"] / HBM_PEAK_GBS, "traffic": None,
+                                       "bytes_per_launch": kl["scan_y"]["bytes"]}},
         "roofline": {"bound": "hbm", "achieved": proj["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": proj["gbs"] / HBM_PEAK_GBS, "traffic": pmc_traffic("proj"),
                      "kernel": "k_proj_stream<8,1>: input projection of a round (12 rows x w_in)",

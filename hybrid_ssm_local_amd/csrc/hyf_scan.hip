@@ -373,18 +373,23 @@ __global__ void __launch_bounds__(256) k_ssd_prefix(Shape sh, ScanArgs a, ReqTab
   *reinterpret_cast<f32x4*>(Hh + e) = acc;
 }
 
-// y-mode outputs: per (segment of HYF_TBLK tokens, head, block of up to 64 state rows), the
-// recurrence token by token from the segment's starting state, y_t = H_t . C_t + D x_t.  The
-// segment's x (this head), B and C go to LDS token-major; 16 threads share a state row, each with
-// N / 16 = NCH columns, and y_t of the row is their shuffle-reduced dot product.
-constexpr int YROWS = 64;
-template <typename T, int NCH>
-__global__ void __launch_bounds__(16 * YROWS) k_ssd_y(Shape sh, ScanArgs a, ReqTable rt, int npb) {
+// y-mode outputs, the chunked form of the recurrence: per (block of TB tokens, head), with H0 the
+// state before the block, a_s = dt_s A and cum_t = a_0 + ... + a_t,
+//   y_t = sum_{s <= t} exp(cum_t - cum_s) dt_s (C_t . B_s) x_s + exp(cum_t) H0 C_t + D x_t.
+// The block's x (this head), B and C are staged in LDS in their tiled layout (three contiguous
+// copies); every product runs on fp32 16x16x4 MFMAs with operands gathered element-wise from LDS
+// (exact products of the stored values):
+//   G^T[s][t] = sum_n B[s][n] C[t][n] for a 16 x 16 (s, t) tile, whose output register r of lane
+//   (li, lg) is G[t0 + li][s0 + 4 lg + r]: masked and scaled into M[t][s], it is already the A
+//   operand of Y += M X (instruction j contracts s0 + 4 lg + j);
+//   the state term sum_n C[t][n] H0[p][n] with H0 read from global memory, four columns a load.
+// Wave w takes the output row tiles w and 7 - w (the causal sums then cost each wave the same).
+template <typename T, int MAXT>
+__global__ void __launch_bounds__(256) k_ssd_y(Shape sh, ScanArgs a, ReqTable rt) {
   constexpr int VN = Vec16<T>::n;
-  typedef typename Vec16<T>::type V;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int nh = sh.nh, P = sh.P, N = sh.N;
-  const int pb = blockIdx.x % npb, h = (blockIdx.x / npb) % nh, q = blockIdx.x / (npb * nh);
+  const int h = blockIdx.x % nh, q = blockIdx.x / nh;
   const int r = find_request(rt, q);
   const int ls = q - rt.seg0[r];
   const int Tr = rt.row0[r + 1] - rt.row0[r];
@@ -392,56 +397,130 @@ __global__ void __launch_bounds__(16 * YROWS) k_ssd_y(Shape sh, ScanArgs a, ReqT
   const int len = min(TB, Tr - s_begin);
   const int64_t blk = rt.blk0[r] + ls;  // y-mode segments are single blocks
   const int grp = h / (nh / sh.G);
-  T* xs = reinterpret_cast<T*>(smem);   // [TB][P]
-  T* bs = xs + TB * P;                  // [TB][N]
-  T* cs = bs + TB * N;                  // [TB][N]
-  float* dts = reinterpret_cast<float*>(cs + TB * N);  // [TB] dt
-  float* dec = dts + TB;                               // [TB] exp(dt A)
-  const int t = threadIdx.x;
-  const int nt = blockDim.x;
-  // token-major staging from the tiled layout: a 16-byte chunk is VN consecutive tokens of one
-  // feature
-  auto stage = [&](const T* base, int64_t bstride, int f0, int F, T* dst) {
-    const int per = TB / VN;
-    for (int c = t; c < F * per; c += nt) {
-      const int f = c / per, tg = c % per;
-      const V v = *reinterpret_cast<const V*>(base + blk * bstride + tile_off<T>(f0 + f, tg * VN));
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int li = lane & 15, lg = lane >> 4;
+  T* xs = reinterpret_cast<T*>(smem);  // tiled [P][TB]
+  T* bs = xs + P * TB;                 // tiled [N][TB]
+  T* cs = bs + N * TB;                 // tiled [N][TB]
+  float* dts = reinterpret_cast<float*>(cs + N * TB);  // [TB] raw steps, then dt
+  float* cum = dts + TB;                               // [TB]
+  // the 16-feature groups of a block are contiguous: features f0 .. f0 + F of a block start at
+  // element f0 TB of it
+  const T* gx = static_cast<const T*>(a.x) + blk * a.xblk + (int64_t)h * P * TB;
+  const T* gb = static_cast<const T*>(a.B) + blk * a.bblk + (int64_t)grp * N * TB;
+  const T* gc = static_cast<const T*>(a.C) + blk * a.cblk + (int64_t)grp * N * TB;
+  const float* gd = a.dt + blk * a.dblk + (int64_t)h * TB;
+  lds_stage16<256>(P * TB / VN, xs, [&](int i) { return gx + (int64_t)i * VN; });
+  lds_stage16<256>(N * TB / VN, bs, [&](int i) { return gb + (int64_t)i * VN; });
+  lds_stage16<256>(N * TB / VN, cs, [&](int i) { return gc + (int64_t)i * VN; });
+  lds_stage16<256>(TB / 4, dts, [&](int i) { return gd + 4 * i; });
+  vm_wait<0>();
+  __syncthreads();
+  if (wave == 0) {
+    // dt and the inclusive prefix of a = dt A (tokens past len: dt = 0)
+    const float A = -expf(a.a_log[h]), bias = a.dt_bias[h];
+    const int u0 = 2 * lane;
+    const float d0 = u0 < len ? softplus_f(dts[u0] + bias) : 0.f;
+    const float d1 = u0 + 1 < len ? softplus_f(dts[u0 + 1] + bias) : 0.f;
+    const float a0 = d0 * A, a1 = d1 * A;
+    float inc = a0 + a1;
 #pragma unroll
-      for (int e = 0; e < VN; ++e) dst[(tg * VN + e) * F + f] = v[e];
+    for (int o = 1; o < 64; o <<= 1) {
+      const float v = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += v;
     }
-  };
-  stage(static_cast<const T*>(a.x), a.xblk, h * P, P, xs);
-  stage(static_cast<const T*>(a.B), a.bblk, grp * N, N, bs);
-  stage(static_cast<const T*>(a.C), a.cblk, grp * N, N, cs);
-  const float A = -expf(a.a_log[h]);
-  for (int u = t; u < TB; u += nt) {
-    const float d = u < len ? softplus_f(a.dt[blk * a.dblk + (int64_t)h * TB + u] + a.dt_bias[h]) : 0.f;
-    dts[u] = d;
-    dec[u] = expf(d * A);
+    const float ex = inc - (a0 + a1);
+    cum[u0] = ex + a0;
+    cum[u0 + 1] = inc;
+    dts[u0] = d0;
+    dts[u0 + 1] = d1;
   }
   __syncthreads();
 
-  const int c16 = t & 15;                 // column chunk of this thread
-  const int p = pb * YROWS + (t >> 4);    // state row of this thread
-  const bool active = p < P;
-  float Hr[NCH];
-  const float* Hs = a.part + ((int64_t)q * nh + h) * P * N;  // state before the segment
-#pragma unroll
-  for (int j = 0; j < NCH; ++j) Hr[j] = active ? Hs[(int64_t)p * N + c16 * NCH + j] : 0.f;
+  const int ntp = P / 16;
   const float D = a.d_skip[h];
-  T* y = static_cast<T*>(a.y) + ((int64_t)rt.row0[r] + s_begin) * nh * P + (int64_t)h * P + p;
-  for (int u = 0; u < len; ++u) {
-    const float xv = active ? to_f32(xs[u * P + p]) : 0.f;
-    const float w = dts[u] * xv, dk = dec[u];
-    float acc = 0.f;
+  const float* H0 = a.part + ((int64_t)q * nh + h) * P * N;  // state before the block
+  T* yout = static_cast<T*>(a.y) + ((int64_t)rt.row0[r] + s_begin) * nh * P + (int64_t)h * P;
+  for (int pass = 0; pass < 2; ++pass) {
+    const int tt = pass ? TB / 16 - 1 - wave : wave;
+    const int t0 = 16 * tt;
+    if (t0 >= len) continue;
+    f32x4 y[MAXT], yi[MAXT];
 #pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      Hr[j] = dk * Hr[j] + w * to_f32(bs[u * N + c16 * NCH + j]);
-      acc += Hr[j] * to_f32(cs[u * N + c16 * NCH + j]);
+    for (int i = 0; i < MAXT; ++i) y[i] = yi[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int st = 0; st <= tt && 16 * st < len; ++st) {
+      const int s0 = 16 * st;
+      // four independent chains over n (reads of a group of 64 columns issue together)
+      f32x4 g4[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) g4[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int n0 = 0; n0 < N; n0 += 64) {
+        float bv[4][4], cv[4][4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int n = min(n0 + 16 * k + 4 * lg + j, N - 1);
+            bv[k][j] = to_f32(bs[tile_off<T>(n, s0 + li)]);
+            cv[k][j] = to_f32(cs[tile_off<T>(n, t0 + li)]);
+          }
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (n0 + 16 * k < N)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) g4[k] = Mfma16<float>::mma(bv[k][j], cv[k][j], g4[k]);
+      }
+      const f32x4 g = (g4[0] + g4[1]) + (g4[2] + g4[3]);
+      float mv[4];
+      const int tq = t0 + li;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int sq = s0 + 4 * lg + rr;
+        mv[rr] = sq <= tq && sq < len ? g[rr] * expf(cum[tq] - cum[sq]) * dts[sq] : 0.f;
+      }
+#pragma unroll
+      for (int pt = 0; pt < MAXT; ++pt) {
+        if (pt < ntp) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int sq = s0 + 4 * lg + j;
+            const float xv = sq < len ? to_f32(xs[tile_off<T>(16 * pt + li, sq)]) : 0.f;
+            y[pt] = Mfma16<float>::mma(mv[j], xv, y[pt]);
+          }
+        }
+      }
     }
+    // state term: yi[t][p] = sum_n C[t][n] H0[p][n]
+#pragma unroll 4
+    for (int n0 = 0; n0 < N; n0 += 16) {
+      float cv[4];
 #pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
-    if (active && c16 == 0) y[(int64_t)u * nh * P] = from_f32<T>(acc + D * xv);
+      for (int j = 0; j < 4; ++j) cv[j] = to_f32(cs[tile_off<T>(n0 + 4 * lg + j, t0 + li)]);
+#pragma unroll
+      for (int pt = 0; pt < MAXT; ++pt) {
+        if (pt < ntp) {
+          const f32x4 hv = *reinterpret_cast<const f32x4*>(H0 + (int64_t)(16 * pt + li) * N + n0 + 4 * lg);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) yi[pt] = Mfma16<float>::mma(cv[j], hv[j], yi[pt]);
+        }
+      }
+    }
+    // lane (li, lg) register rr: token t0 + 4 lg + rr, column 16 pt + li
+#pragma unroll
+    for (int pt = 0; pt < MAXT; ++pt) {
+      if (pt < ntp) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int tq = t0 + 4 * lg + rr;
+          if (tq < len) {
+            const int p = 16 * pt + li;
+            const float v = y[pt][rr] + expf(cum[tq]) * yi[pt][rr] + D * to_f32(xs[tile_off<T>(p, tq)]);
+            yout[(int64_t)tq * nh * P + p] = from_f32<T>(v);
+          }
+        }
+      }
+    }
   }
 }
 
@@ -536,42 +615,23 @@ static hipError_t launch_seg(const Shape& sh, const ScanArgs& a, const ReqTable&
   return f ? f(sh, a, rt, s) : hipErrorInvalidValue;
 }
 
-template <typename T, int NCH>
+template <typename T, int MAXT>
 static hipError_t launch_y_t(const Shape& sh, const ScanArgs& a, const ReqTable& rt, hipStream_t s) {
-  const int npb = (sh.P + YROWS - 1) / YROWS;
-  const int rows = sh.P < YROWS ? sh.P : YROWS;
   const size_t lds = (size_t)TB * (sh.P + 2 * sh.N) * sizeof(T) + 2 * TB * sizeof(float);
   static std::once_flag once;
   static hipError_t set_err = hipSuccess;
   std::call_once(once, [] {
-    set_err = hipFuncSetAttribute(reinterpret_cast<const void*>(k_ssd_y<T, NCH>),
+    set_err = hipFuncSetAttribute(reinterpret_cast<const void*>(k_ssd_y<T, MAXT>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 256);
   });
   if (set_err != hipSuccess) return set_err;
-  hipLaunchKernelGGL((k_ssd_y<T, NCH>), dim3(a.total_segs * sh.nh * npb), dim3(16 * rows), lds, s, sh, a, rt, npb);
+  hipLaunchKernelGGL((k_ssd_y<T, MAXT>), dim3(a.total_segs * sh.nh), dim3(256), lds, s, sh, a, rt);
   return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t launch_y(const Shape& sh, const ScanArgs& a, const ReqTable& rt, hipStream_t s) {
-  switch (sh.N / 16) {
-    case 1: return launch_y_t<T, 1>(sh, a, rt, s);
-    case 2: return launch_y_t<T, 2>(sh, a, rt, s);
-    case 3: return launch_y_t<T, 3>(sh, a, rt, s);
-    case 4: return launch_y_t<T, 4>(sh, a, rt, s);
-    case 5: return launch_y_t<T, 5>(sh, a, rt, s);
-    case 6: return launch_y_t<T, 6>(sh, a, rt, s);
-    case 7: return launch_y_t<T, 7>(sh, a, rt, s);
-    case 8: return launch_y_t<T, 8>(sh, a, rt, s);
-    case 9: return launch_y_t<T, 9>(sh, a, rt, s);
-    case 10: return launch_y_t<T, 10>(sh, a, rt, s);
-    case 11: return launch_y_t<T, 11>(sh, a, rt, s);
-    case 12: return launch_y_t<T, 12>(sh, a, rt, s);
-    case 13: return launch_y_t<T, 13>(sh, a, rt, s);
-    case 14: return launch_y_t<T, 14>(sh, a, rt, s);
-    case 15: return launch_y_t<T, 15>(sh, a, rt, s);
-    default: return launch_y_t<T, 16>(sh, a, rt, s);
-  }
+  return sh.P > 128 ? launch_y_t<T, 16>(sh, a, rt, s) : launch_y_t<T, 8>(sh, a, rt, s);
 }
 
 hipError_t launch_ssd_state(int dtype, const Shape& sh, const ScanArgs& a, const ReqTable& rt,
