@@ -38,6 +38,7 @@ class LayerShape:
     chunk: int = 64
     dtype: str = BF16
     cross_slot: int = 1
+    memory: str = "mamba2"  # or "gdn": the gated delta-rule memory
 
     @property
     def dq(self) -> int:
@@ -48,12 +49,17 @@ class LayerShape:
         return self.n_groups * self.d_state
 
     # Row groups of the packed input projection, in storage order:
-    # q | C | k | v | B | dt  (each row is one output feature of length d_model).
+    # q | C | k | v | B | dt  (each row is one output feature of length d_model);
+    # the gated delta-rule memory has the two gates in place of dt: ... | B | alpha | beta.
     @property
     def in_groups(self):
         dq, gn, nh = self.dq, self.gn, self.n_heads
-        names = ("q", "C", "k", "v", "B", "dt")
-        sizes = (dq, gn, dq, dq, gn, nh)
+        if self.memory == "gdn":
+            names = ("q", "C", "k", "v", "B", "alpha", "beta")
+            sizes = (dq, gn, dq, dq, gn, nh, nh)
+        else:
+            names = ("q", "C", "k", "v", "B", "dt")
+            sizes = (dq, gn, dq, dq, gn, nh)
         out, off = {}, 0
         for n, s in zip(names, sizes):
             out[n] = (off, off + s)
@@ -62,7 +68,7 @@ class LayerShape:
 
     @property
     def n_in(self) -> int:
-        return 3 * self.dq + 2 * self.gn + self.n_heads
+        return 3 * self.dq + 2 * self.gn + (2 if self.memory == "gdn" else 1) * self.n_heads
 
     def replace(self, **kw) -> "LayerShape":
         return dataclasses.replace(self, **kw)
@@ -122,6 +128,11 @@ def make_weights(shape: LayerShape, rng, d_random: bool = False) -> dict:
     w_out = to_storage(xavier(rng, d, shape.dq), shape.dtype)
     a_log = rng.uniform(math.log(1.0), math.log(16.0), size=shape.n_heads).astype(np.float32)
     dt_bias = np.full(shape.n_heads, -2.0, dtype=np.float32)
+    if shape.memory == "gdn":
+        # gate biases: dt_bias carries the retention gate's (alpha = sigmoid(2..5): 0.88-0.99),
+        # a_log the write gate's (beta = sigmoid(0) = 0.5 at a zero projection)
+        dt_bias = rng.uniform(2.0, 5.0, size=shape.n_heads).astype(np.float32)
+        a_log = np.zeros(shape.n_heads, dtype=np.float32)
     if d_random:
         d_skip = rng.standard_normal(shape.n_heads, dtype=np.float32)
     else:

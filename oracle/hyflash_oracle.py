@@ -162,6 +162,47 @@ def ssd_chunked(x, B, C, dt_raw, a_log, dt_bias, d_skip, H0, chunk: int, n_group
 
 
 # ----------------------------------------------------------------------------
+# the gated delta-rule memory (the memory the pages swap in for Mamba-2)
+
+
+def sigmoid(z):
+    """1 / (1 + e^-z), evaluated as e^z / (1 + e^z) for z < 0 so that neither branch overflows and
+    small values keep their relative precision."""
+    z = np.asarray(z, dtype=F64)
+    e = np.exp(-np.abs(z))
+    return np.where(z >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+
+
+def l2_normalize(a, eps: float = 1e-6):
+    """a / sqrt(|a|^2 + eps) along the last axis."""
+    a = np.asarray(a, dtype=F64)
+    return a / np.sqrt(np.sum(a * a, axis=-1, keepdims=True) + eps)
+
+
+def gdn_sequential(x, B, alpha_raw, beta_raw, b_alpha, b_beta, H0, n_groups: int = 1):
+    """The gated delta rule, one token at a time.
+
+    HyFlash explainer, "That is HyFlash" and FAQ (a fixed-size memory of the committed history);
+    HyFlash paper, the memory ablation (Gated DeltaNet-2 in place of Mamba-2).  Per head, with the
+    key k = B_t normalized to unit length, the value x_t (the value projection), the retention gate
+    a = sigmoid(alpha_raw + b_alpha) and the write gate b = sigmoid(beta_raw + b_beta):
+        H <- a * H (I - b k k^T) + b * x_t k^T        (H is [P][N]: value rows, key columns)
+    x [T][nh][P], B [T][G*N], alpha_raw and beta_raw [T][nh], H0 [nh][P][N].  Returns H_T.
+    """
+    x = np.asarray(x, F64)
+    T, nh, P = x.shape
+    k = l2_normalize(per_head(B, nh, n_groups))                  # [T][nh][N]
+    a = sigmoid(np.asarray(alpha_raw, F64) + np.asarray(b_alpha, F64)[None, :])
+    b = sigmoid(np.asarray(beta_raw, F64) + np.asarray(b_beta, F64)[None, :])
+    H = np.array(H0, dtype=F64, copy=True)
+    for t in range(T):
+        Hk = np.einsum("hpn,hn->hp", H, k[t])                    # H k
+        H = a[t][:, None, None] * (H - b[t][:, None, None] * Hk[:, :, None] * k[t][:, None, :]) \
+            + b[t][:, None, None] * x[t][:, :, None] * k[t][:, None, :]
+    return H
+
+
+# ----------------------------------------------------------------------------
 # the layer: projections, ring, attention, readout, output projection
 
 
@@ -225,8 +266,14 @@ def commit(shape, wts: dict, st: dict, feats, want_y: bool = False):
     if feats.shape[0] == 0:
         return st, (np.zeros((0, shape.n_heads, shape.head_dim)) if want_y else None)
     pr = split_projection(project(feats, wts["w_in"]), shape)
-    H, y = ssd_sequential(pr["v"], pr["B"], pr["C"] if want_y else None, pr["dt"],
-                          wts["a_log"], wts["dt_bias"], wts["d_skip"], st["H"], shape.n_groups)
+    if shape.memory == "gdn":
+        if want_y:
+            raise ValueError("per-token outputs are defined for the Mamba-2 memory only")
+        H, y = gdn_sequential(pr["v"], pr["B"], pr["alpha"], pr["beta"], wts["dt_bias"], wts["a_log"], st["H"],
+                              shape.n_groups), None
+    else:
+        H, y = ssd_sequential(pr["v"], pr["B"], pr["C"] if want_y else None, pr["dt"],
+                              wts["a_log"], wts["dt_bias"], wts["d_skip"], st["H"], shape.n_groups)
     st["H"] = H
     ring_append(shape, st, pr["k"], pr["v"])
     return st, y
@@ -273,7 +320,8 @@ def draft(shape, wts: dict, st: dict, block_in):
     pr = split_projection(project(x, wts["w_in"]), shape)
     k_ctx, v_ctx = ring_window(shape, st)
     attn = block_attention(pr["q"], k_ctx, v_ctx, pr["k"], pr["v"], shape.cross_slot)
-    mem = memory_readout(st["H"], pr["C"], pr["v"], wts["d_skip"], shape.n_groups)
+    Cq = l2_normalize(pr["C"].reshape(nb, shape.n_groups, -1)).reshape(nb, -1) if shape.memory == "gdn" else pr["C"]
+    mem = memory_readout(st["H"], Cq, pr["v"], wts["d_skip"], shape.n_groups)
     o = (attn + mem).reshape(nb, shape.dq)
     return project(o, wts["w_out"])
 

@@ -385,3 +385,99 @@ def test_fp32_state_size_matches_the_pages():
     kv = 40 * 2 * 10 * 128 * 2 * 32768
     assert kv == g["target_kv_GiB_at_32k"] * 2**30
     assert round(kv / (g["drafter_context_MiB"] * 2**20)) == g["target_over_drafter_ratio"]
+
+
+# ---------------------------------------------------------------- gated delta-rule memory
+
+
+def _gdn_inputs(T, nh=3, P=5, N=6, seed=0):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((T, nh, P)), rng.standard_normal((T, N)), rng.standard_normal((T, nh)),
+            rng.standard_normal((T, nh)), rng.uniform(1, 3, nh), rng.standard_normal(nh),
+            rng.standard_normal((nh, P, N)))
+
+
+def test_gdn_gates_and_key_normalization_match_library_routines():
+    import scipy.special
+
+    z = np.linspace(-40, 40, 81)
+    assert np.allclose(O.sigmoid(z), scipy.special.expit(z), rtol=1e-14, atol=1e-300)
+    a = np.random.default_rng(1).standard_normal((7, 9))
+    n = np.linalg.norm(a, axis=-1, keepdims=True)
+    assert np.allclose(O.l2_normalize(a, eps=0.0), a / n, rtol=1e-14)
+    assert np.allclose(O.l2_normalize(a), a / np.sqrt(n * n + 1e-6), rtol=1e-14)
+
+
+def test_gdn_with_a_closed_write_gate_is_pure_decay():
+    # beta = sigmoid(-60) ~ 1e-26: H_T = prod_t alpha_t * H0 per head (closed form)
+    x, B, ar, _, ba, _, H0 = _gdn_inputs(9)
+    br = np.full_like(ar, -60.0)
+    H = O.gdn_sequential(x, B, ar, br, ba, np.zeros(3), H0)
+    decay = np.prod(O.sigmoid(ar + ba[None, :]), axis=0)
+    assert _rel(H, decay[:, None, None] * H0) < 1e-14
+
+
+def test_gdn_delta_write_recalls_the_written_value():
+    # alpha = beta = 1 (gates saturated): after writing (k, v), H k = v up to the key normalization
+    # epsilon (|k|^2 = |B|^2 / (|B|^2 + 1e-6))
+    x, B, _, _, _, _, H0 = _gdn_inputs(1, N=16)
+    big = np.full((1, 3), 60.0)
+    H = O.gdn_sequential(x, B, big, big, np.zeros(3), np.zeros(3), H0)
+    k = B[0] / np.sqrt(B[0] @ B[0] + 1e-6)
+    assert np.max(np.abs(np.einsum("hpn,n->hp", H, k) - x[0])) < 1e-6
+
+
+def test_gdn_orthogonal_keys_are_all_recalled():
+    # unit-gated writes of orthogonal keys (scaled basis vectors) into an empty state store each
+    # value under its own key: H e_t = v_t for every written t
+    T, N = 5, 8
+    x = np.random.default_rng(3).standard_normal((T, 2, 4))
+    B = np.zeros((T, N))
+    for t in range(T):
+        B[t, (3 * t) % N] = 2.0 + t
+    big = np.full((T, 2), 60.0)
+    H = O.gdn_sequential(x, B, big, big, np.zeros(2), np.zeros(2), np.zeros((2, 4, N)))
+    for t in range(T):
+        e = np.zeros(N)
+        e[(3 * t) % N] = 1.0
+        assert np.max(np.abs(np.einsum("hpn,n->hp", H, e) - x[t])) < 1e-6
+
+
+def test_gdn_matches_the_product_form_brute_force():
+    # H_T = H0 M_1 ... M_T + sum_t b_t x_t k_t^T M_{t+1} ... M_T with M_t = a_t (I - b_t k_t k_t^T),
+    # evaluated with explicit N x N matrix products (another order of operations)
+    for T in (1, 2, 7, 16):
+        x, B, ar, br, ba, bb, H0 = _gdn_inputs(T, seed=T)
+        got = O.gdn_sequential(x, B, ar, br, ba, bb, H0)
+        N = B.shape[1]
+        for h in range(3):
+            k = B / np.sqrt(np.sum(B * B, axis=1, keepdims=True) + 1e-6)
+            a = 1.0 / (1.0 + np.exp(-(ar[:, h] + ba[h])))
+            b = 1.0 / (1.0 + np.exp(-(br[:, h] + bb[h])))
+            M = [a[t] * (np.eye(N) - b[t] * np.outer(k[t], k[t])) for t in range(T)]
+            tail = [np.eye(N)] * (T + 1)
+            for t in range(T - 1, -1, -1):
+                tail[t] = M[t] @ tail[t + 1]
+            ref = H0[h] @ tail[0]
+            for t in range(T):
+                ref = ref + b[t] * np.outer(x[t, h], k[t]) @ tail[t + 1]
+            assert _rel(got[h], ref) < 1e-12, (T, h)
+
+
+def test_gdn_layer_commit_splits_and_reads_normalized_queries():
+    # Committing rows in two calls equals one call; a draft on an empty GDN state with D = 0 and no
+    # window is the block attention alone (the readout of H = 0 vanishes).
+    shape = I.TINY.replace(memory="gdn", d_model=64, n_heads=2, head_dim=16, d_state=16, window=8)
+    w = {k: np.asarray(v, np.float64) for k, v in I.make_weights(shape, I.rng_streams(7)[0]).items()}
+    feats = I.make_rows(I.rng_streams(8)[1], 11, shape.d_model, 1.0, shape.dtype)
+    st1, _ = O.commit(shape, w, O.new_state(shape), feats)
+    st2, _ = O.commit(shape, w, O.new_state(shape), feats[:4])
+    st2, _ = O.commit(shape, w, st2, feats[4:])
+    assert _rel(st2["H"], st1["H"]) < 1e-12
+    w0 = dict(w, d_skip=np.zeros(shape.n_heads))
+    blk = I.make_rows(I.rng_streams(9)[3], 8, shape.d_model, 1.0, shape.dtype)
+    out = O.draft(shape, w0, O.new_state(shape), blk)
+    pr = O.split_projection(O.project(blk, w0["w_in"]), shape)
+    att = O.block_attention(pr["q"], np.zeros((0, 2, 16)), np.zeros((0, 2, 16)), pr["k"], pr["v"])
+    assert _rel(out, O.project(att.reshape(8, -1), w0["w_out"])) < 1e-12
+    assert shape.n_in == 3 * 32 + 2 * 16 + 2 * 2 and shape.in_groups["beta"] == (shape.n_in - 2, shape.n_in)
