@@ -59,9 +59,9 @@ def log(*a):
 class Episode:
     """Device-resident inputs of one step and the precomputed C-ABI arguments."""
 
-    def __init__(self, torch, hf, I):
+    def __init__(self, torch, hf, I, memory="mamba2"):
         wl = I.WORKLOADS[WORKLOAD]
-        self.shape = sh = wl["shape"]
+        self.shape = sh = wl["shape"].replace(memory=memory)
         self.T, self.R = wl["prefix"], wl["rounds"]
         d = sh.d_model
         rng = I.rng_streams(wl["seed"])
@@ -415,6 +415,23 @@ def main():
     torch.cuda.synchronize()
     graph_ms = e0.elapsed_time(e1) / args.steps
 
+    # ---- the same episode with the gated delta-rule memory in place of Mamba-2 (eager steps)
+    log("gated delta-rule episode")
+    del g
+    ep_g = Episode(torch, hf, I, memory="gdn")
+    ep_g.step(stream)
+    gevs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(3)]
+    for k in range(3):
+        ep_g.step(stream, gevs[k])
+    torch.cuda.synchronize()
+    g_pre = sum(e[0].elapsed_time(e[1]) for e in gevs) / 3
+    g_rnd = sum(e[1].elapsed_time(e[2]) for e in gevs) / 3
+    gdn = {"prefill_commit_us": 1e3 * g_pre, "commit_feats_per_s": ep_g.T / (g_pre * 1e-3),
+           "round_us": 1e3 * g_rnd / ep_g.R, "draft_blocks_per_s": ep_g.R / (g_rnd * 1e-3),
+           "note": "eager steps of the same workload with memory = gated delta rule; the prefix commit runs "
+                   "the rule one token at a time"}
+    del ep_g
+
     log("kernel loops")
     kl = kernel_loops(torch, hf, I, ep, args.kernel_reps)
     cpu = None if args.no_cpu else cpu_baseline(I, ep)
@@ -463,6 +480,7 @@ def main():
         "gemm_roofline": {"bound": "mfma", "achieved": gemm["tflops"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                           "frac": gemm["tflops"] / BF16_PEAK_TFLOPS,
                           "kernel": "k_gemm_bf16: prefill projection 8192 x 2560 x 2720", "avg_us": gemm["mean_us"]},
+        "gated_delta_rule": gdn,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

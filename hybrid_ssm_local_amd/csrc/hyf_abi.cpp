@@ -20,8 +20,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 int check_cfg(const hyf_config* c) {
   if (!c) return HYF_EINVAL;
   if (c->dtype != HYF_F32 && c->dtype != HYF_BF16) return HYF_EDTYPE;
-  if (c->memory == HYF_MEM_GDN) return HYF_EUNSUPPORTED;
-  if (c->memory != HYF_MEM_MAMBA2) return HYF_EINVAL;
+  if (c->memory != HYF_MEM_MAMBA2 && c->memory != HYF_MEM_GDN) return HYF_EINVAL;
   if (c->reserved != 0) return HYF_EINVAL;
   if (c->cross_slot != 0 && c->cross_slot != 1) return HYF_EINVAL;
   if (c->d_model < 16 || c->d_model > 65536 || c->d_model % 16) return HYF_ESHAPE;
@@ -64,7 +63,9 @@ Shape make_shape(const hyf_config* c) {
   s.off_v = s.off_k + s.dq;
   s.off_b = s.off_v + s.dq;
   s.off_dt = s.off_b + s.gn;
-  s.n_in = s.off_dt + s.nh;
+  s.gdn = c->memory == HYF_MEM_GDN;
+  s.off_beta = s.off_dt + s.nh;
+  s.n_in = s.off_dt + (s.gdn ? 2 : 1) * s.nh;
   hyf_state_layout L;
   fill_layout(c, &L);
   s.st_bytes = L.total;
@@ -166,8 +167,8 @@ WsCommit ws_commit(const Shape& s, int dtype, int32_t R, int64_t rows, bool with
   const int64_t nblk = time_blocks(rows, R);
   w.vb = o;  // v | B time-blocked: [nblk][dq + gn][HYF_TBLK]
   o += align_up((uint64_t)nblk * (s.dq + s.gn) * HYF_TBLK * esize(dtype));
-  w.dt = o;  // raw step time-blocked: [nblk][nh][HYF_TBLK] fp32
-  o += align_up((uint64_t)nblk * s.nh * HYF_TBLK * 4);
+  w.dt = o;  // raw step (or the two raw gates) time-blocked: [nblk][nh or 2 nh][HYF_TBLK] fp32
+  o += align_up((uint64_t)nblk * (s.gdn ? 2 : 1) * s.nh * HYF_TBLK * 4);
   w.kb = o;
   o += align_up((uint64_t)krows * s.dq * esize(dtype));
   w.c = o;  // y-mode: C time-blocked: [nblk][gn][HYF_TBLK]
@@ -317,7 +318,7 @@ int hyf_memory_commit(const hyf_config* cfg, const hyf_weights* w, void* state_p
   if ((st = check_weights(w)) != HYF_OK) return st;
   if (!state_pool || !aligned(state_pool, ALIGN) || pool_slots < 1 || !cu_rows) return HYF_EINVAL;
   const Shape s = make_shape(cfg);
-  if (y_opt && !scan_y_supported(s, esize(cfg->dtype))) return HYF_EUNSUPPORTED;
+  if (y_opt && (s.gdn || !scan_y_supported(s, esize(cfg->dtype)))) return HYF_EUNSUPPORTED;
   if (y_opt && !aligned(y_opt, 16)) return HYF_EINVAL;
   ReqTable rt;
   if ((st = build_table(s, pool_slots, slots, n_req, cu_rows, &rt)) != HYF_OK) return st;
@@ -335,6 +336,7 @@ int hyf_memory_commit(const hyf_config* cfg, const hyf_weights* w, void* state_p
   int64_t max_n = 0;
   for (int i = 0; i < n_req; ++i) max_n = cu_rows[i + 1] - cu_rows[i] > max_n ? cu_rows[i + 1] - cu_rows[i] : max_n;
 
+  if (s.gdn && max_n > 16 && !gdn_supported(s)) return HYF_EUNSUPPORTED;
   if (max_n <= 16 && !y_opt) {
     // Round-sized commit: one weight pass over the k | v | B | dt rows, then one round kernel that
     // folds the rows into H (one read-modify-write), appends them to the ring and advances count.
@@ -376,7 +378,8 @@ int hyf_memory_commit(const hyf_config* cfg, const hyf_weights* w, void* state_p
   char* kb = wsb + L.kb;
   const int nvb = s.dq + s.gn;
   const int64_t vb_blk = (int64_t)nvb * HYF_TBLK;  // block strides (elements) of v | B and of dt
-  const int64_t dt_blk = (int64_t)s.nh * HYF_TBLK;
+  const int ndt = (s.gdn ? 2 : 1) * s.nh;  // raw step, or the two raw gates
+  const int64_t dt_blk = (int64_t)ndt * HYF_TBLK;
   const char* w_vbd = static_cast<const char*>(w->w_in) + (int64_t)s.off_v * s.d * es;
   const char* w_k = static_cast<const char*>(w->w_in) + (int64_t)s.off_k * s.d * es;
   hipError_t he;
@@ -387,7 +390,7 @@ int hyf_memory_commit(const hyf_config* cfg, const hyf_weights* w, void* state_p
     const char* src = static_cast<const char*>(feats) + cu_rows[i] * (int64_t)s.d * es;
     RowSrc xs{src, src, n};
     Epi e{vbT + rt.blk0[i] * vb_blk * es, vb_blk, 0, nvb, dtT + rt.blk0[i] * dt_blk, dt_blk, 1};
-    if ((he = launch_linear(dt, xs, n, s.d, w_vbd, nvb + s.nh, e, hs)) != hipSuccess) return HYF_EHIP;
+    if ((he = launch_linear(dt, xs, n, s.d, w_vbd, nvb + ndt, e, hs)) != hipSuccess) return HYF_EHIP;
     if (with_y) {
       Epi ec{cT + rt.blk0[i] * c_blk * es, c_blk, 0, s.gn, nullptr, 0, 1};
       if ((he = launch_linear(dt, xs, n, s.d, w_c, s.gn, ec, hs)) != hipSuccess) return HYF_EHIP;
@@ -419,9 +422,14 @@ int hyf_memory_commit(const hyf_config* cfg, const hyf_weights* w, void* state_p
   sa.cblk = c_blk;
   sa.y = y_opt;
   sa.d_skip = w->d_skip;
-  int32_t max_segs = 0;
-  fill_segments(s, dt, &rt, with_y, &sa.seg_tokens, &sa.total_segs, &max_segs);
-  if ((he = launch_ssd_state(dt, s, sa, rt, max_segs, hs)) != hipSuccess) return HYF_EHIP;
+  if (s.gdn) {
+    he = launch_gdn_commit(dt, s, sa, rt, hs);
+  } else {
+    int32_t max_segs = 0;
+    fill_segments(s, dt, &rt, with_y, &sa.seg_tokens, &sa.total_segs, &max_segs);
+    he = launch_ssd_state(dt, s, sa, rt, max_segs, hs);
+  }
+  if (he != hipSuccess) return HYF_EHIP;
   return hip_status(launch_bump_counts(pool, s, rt, hs));
 }
 
@@ -506,6 +514,7 @@ int hyf_ssd_scan(const hyf_config* cfg, const void* x, const void* B, const void
   if (!a_log || !dt_bias || !d_skip || !H_inout || !aligned(H_inout, 16)) return HYF_EINVAL;
   if ((y_opt != nullptr) != (C_opt != nullptr)) return HYF_EINVAL;
   const Shape s = make_shape(cfg);
+  if (s.gdn) return HYF_EUNSUPPORTED;  // the scan on pre-projected inputs is the Mamba-2 memory's
   if (y_opt && !scan_y_supported(s, esize(cfg->dtype))) return HYF_EUNSUPPORTED;
   if (T == 0) return HYF_OK;
   if (!x || !B || !dt_raw || !aligned(x, 16) || !aligned(B, 16) || !aligned(dt_raw, 16)) return HYF_EINVAL;

@@ -41,8 +41,9 @@ __host__ __device__ __forceinline__ int64_t tile_off(int64_t f, int t) {
 struct Shape {
   int32_t d, nh, P, N, G, W, L, cross;
   int32_t dq, gn, n_in;
+  int32_t gdn;  // 1: gated delta-rule memory (gates alpha at off_dt, beta at off_beta), 0: Mamba-2
   // w_in row offsets of each group
-  int32_t off_q, off_c, off_k, off_v, off_b, off_dt;
+  int32_t off_q, off_c, off_k, off_v, off_b, off_dt, off_beta;
   // state blob
   uint64_t st_bytes, st_h, st_k, st_v;
 };

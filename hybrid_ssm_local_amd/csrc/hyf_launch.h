@@ -92,6 +92,12 @@ struct RoundArgs {
   int32_t do_draft;    // block rows present
 };
 int round_tiles(const Shape& sh);
+
+// Gated delta-rule commit of whole prefixes (sh.gdn): x and B tiled as for the Mamba-2 scan, the raw
+// gates time-blocked in a.dt (alpha at feature h, beta at nh + h, block stride a.dblk); gate biases
+// in a.dt_bias (alpha) and a.a_log (beta); updates the state pool's H in place.
+bool gdn_supported(const Shape& sh);
+hipError_t launch_gdn_commit(int dtype, const Shape& sh, const ScanArgs& a, const ReqTable& rt, hipStream_t s);
 hipError_t launch_round(int dtype, const Shape& sh, const RoundArgs& a, const ReqTable& rt, hipStream_t s);
 
 // Prefill ring append: the last m_i = min(n_i, W) rows of request i go to slots

@@ -66,7 +66,13 @@ __device__ __forceinline__ void stage16_dev(int n, void* dst, F src) {
 
 // Tile LDS (bytes): B of the committed rows [RMAXC][N] f32 | C of the block rows [RB][N] f32 |
 // x (= v) of the committed rows [RMAXC][rows_wg] f32 | v of the block rows [RB][rows_wg] f32 |
-// weights [RMAXC + 4] | readout partials [RB][RT].
+// weights [RMAXC + 4] (gated delta rule: retention gates) | write gates [RMAXC] | inverse key norms
+// [RMAXC] | inverse query norms [RB] | readout partials [RB][RT].
+//
+// Gated delta-rule memory (sh.gdn): the committed rows are folded one at a time, each row of H
+// (tpr threads) forming H_p . k with a reduction over its threads, then
+// H_p <- alpha (H_p - beta (H_p . k) k) + beta x_p k, k the unit-normalized B row; the readout
+// uses the unit-normalized C rows.
 template <typename T>
 __device__ __forceinline__ void round_tile(const Shape& sh, const RoundArgs& a, const ReqTable& rt, int r, int h,
                                            int tile, char* smem) {
@@ -88,20 +94,29 @@ __device__ __forceinline__ void round_tile(const Shape& sh, const RoundArgs& a, 
   float* xv = reinterpret_cast<float*>(reinterpret_cast<char*>(Cl) + up1k(RB * N * 4));
   float* vb = reinterpret_cast<float*>(reinterpret_cast<char*>(xv) + up1k(RMAXC * rows_wg * 4));
   float* wl = reinterpret_cast<float*>(reinterpret_cast<char*>(vb) + up1k(RB * rows_wg * 4));
-  float* red = wl + RMAXC + 4;
+  float* ga = wl + RMAXC + 4;  // write gates (gated delta rule)
+  float* ik = ga + RMAXC;      // inverse key norms
+  float* iq = ik + RMAXC;      // inverse query norms
+  float* red = iq + RB;
 
   // every load first (one round trip), then the arithmetic
   float* Hh = h_ptr(a.state_pool, sh, slot, h);
   f32x4 hv = f32x4{0.f, 0.f, 0.f, 0.f};
   if (active) hv = *reinterpret_cast<const f32x4*>(Hh + (int64_t)p * N + 4 * c4);
   const float raw = t < nrows ? a.proj[(crow0 + t) * ld + sh.off_dt + h] : 0.f;
+  const float rawb = sh.gdn && t < nrows ? a.proj[(crow0 + t) * ld + sh.off_beta + h] : 0.f;
   stage16(nrows * tpr, Bl, [&](int i) { return a.proj + (crow0 + i / tpr) * ld + sh.off_b + grp * N + 4 * (i % tpr); });
   stage4(nrows * rows_wg, xv, [&](int i) { return a.proj + (crow0 + i / rows_wg) * ld + sh.off_v + h * P + p0 + i % rows_wg; });
   if (a.do_draft) {
     stage16(RB * tpr, Cl, [&](int i) { return a.proj + (brow0 + i / tpr) * ld + sh.off_c + grp * N + 4 * (i % tpr); });
     stage4(RB * rows_wg, vb, [&](int i) { return a.proj + (brow0 + i / rows_wg) * ld + sh.off_v + h * P + p0 + i % rows_wg; });
   }
-  if (t < 64) {
+  if (sh.gdn) {
+    if (t < nrows) {
+      wl[t] = 1.f / (1.f + __expf(-(raw + a.dt_bias[h])));  // retention gate (its bias in dt_bias)
+      ga[t] = 1.f / (1.f + __expf(-(rawb + a.a_log[h])));   // write gate (its bias in a_log)
+    }
+  } else if (t < 64) {
     // weights relative to the last committed row: w_t = dt_t exp(sum_{tau > t} dt_tau A), and
     // the decay exp(sum_t dt_t A) of the old state; lane t < nrows holds row t
     const float A = -expf(a.a_log[h]);
@@ -119,7 +134,41 @@ __device__ __forceinline__ void round_tile(const Shape& sh, const RoundArgs& a, 
   vm_wait<0>();
   __syncthreads();
 
-  if (active && nrows > 0) {
+  const bool pow2 = (tpr & (tpr - 1)) == 0;  // the tpr threads of a row are consecutive lanes of one wave
+  if (sh.gdn) {
+    // inverse norms of the committed rows' keys and the block rows' queries, one row per wave at a time
+    const int lane = t & 63, wave = t >> 6;
+    for (int j = wave; j < nrows + (a.do_draft ? RB : 0); j += RT / 64) {
+      const float* row = j < nrows ? Bl + j * N : Cl + (j - nrows) * N;
+      float ss = 0.f;
+      for (int n = lane; n < N; n += 64) ss += row[n] * row[n];
+      ss = wave_sum(ss);
+      if (lane == 0) {
+        if (j < nrows) ik[j] = rsqrtf(ss + 1e-6f);
+        else iq[j - nrows] = rsqrtf(ss + 1e-6f);
+      }
+    }
+    __syncthreads();
+    if (nrows > 0) {
+      for (int tt = 0; tt < nrows; ++tt) {
+        const f32x4 k = *reinterpret_cast<const f32x4*>(Bl + tt * N + 4 * c4) * ik[tt];
+        float d = hv[0] * k[0] + hv[1] * k[1] + hv[2] * k[2] + hv[3] * k[3];
+        if (pow2) {
+          for (int o = tpr / 2; o >= 1; o >>= 1) d += __shfl_xor(d, o, 64);
+        } else {
+          red[t] = d;
+          __syncthreads();
+          d = 0.f;
+          for (int c = 0; c < tpr; ++c) d += red[prow * tpr + c];
+          __syncthreads();
+        }
+        const float be = ga[tt];
+        const float xw = active ? be * xv[tt * rows_wg + prow] : 0.f;
+        hv = wl[tt] * (hv - (be * d) * k) + xw * k;
+      }
+      if (active) *reinterpret_cast<f32x4*>(Hh + (int64_t)p * N + 4 * c4) = hv;
+    }
+  } else if (active && nrows > 0) {
     hv *= wl[RMAXC];
     for (int tt = 0; tt < nrows; ++tt) {
       const float xw = xv[tt * rows_wg + prow] * wl[tt];
@@ -140,7 +189,7 @@ __device__ __forceinline__ void round_tile(const Shape& sh, const RoundArgs& a, 
       }
     }
     const float D = a.d_skip[h];
-    if ((tpr & (tpr - 1)) == 0) {
+    if (pow2) {
       // the tpr threads of a row are consecutive lanes of one wave: xor-shuffle reduction
       for (int o = tpr / 2; o >= 1; o >>= 1)
 #pragma unroll
@@ -148,7 +197,8 @@ __device__ __forceinline__ void round_tile(const Shape& sh, const RoundArgs& a, 
       if (active && c4 == 0)
 #pragma unroll
         for (int j = 0; j < RB; ++j)
-          st_dev(a.mem + (((int64_t)r * RB + j) * nh + h) * P + p, sum[j] + D * vb[j * rows_wg + prow]);
+          st_dev(a.mem + (((int64_t)r * RB + j) * nh + h) * P + p,
+                 sum[j] * (sh.gdn ? iq[j] : 1.f) + D * vb[j * rows_wg + prow]);
     } else {
 #pragma unroll
       for (int j = 0; j < RB; ++j) red[j * RT + t] = sum[j];
@@ -159,7 +209,7 @@ __device__ __forceinline__ void round_tile(const Shape& sh, const RoundArgs& a, 
         if (pp >= P) continue;
         float acc = 0.f;
         for (int c = 0; c < tpr; ++c) acc += red[j * RT + pr * tpr + c];
-        st_dev(a.mem + (((int64_t)r * RB + j) * nh + h) * P + pp, acc + D * vb[idx]);
+        st_dev(a.mem + (((int64_t)r * RB + j) * nh + h) * P + pp, acc * (sh.gdn ? iq[j] : 1.f) + D * vb[idx]);
       }
     }
   }
@@ -503,7 +553,7 @@ int round_tiles(const Shape& sh) { return (sh.P + round_rows_per_tile(sh) - 1) /
 size_t round_lds_bytes(const Shape& sh, int esz, int n_split) {
   const int rw = round_rows_per_tile(sh);
   const size_t tile = (size_t)up1k(RMAXC * sh.N * 4) + up1k(RB * sh.N * 4) + up1k(RMAXC * rw * 4) + up1k(RB * rw * 4) +
-                      4 * (RMAXC + 4 + RB * RT);
+                      4 * (3 * RMAXC + 4 + RB + RB * RT);
   const size_t attn = (size_t)2 * up1k(ATT_KS * sh.P * esz) + 3 * up1k(RB * sh.P * 4) + 4 * (16 * ATT_KS + 128);
   const size_t merge = n_split ? (size_t)up1k(n_split * RB * 2 * 4) + up1k(n_split * RB * 4) + 4 * 256 +
                                      up1k(RB * sh.P * 4) + up1k(MCH * RB * sh.P * 4)

@@ -100,7 +100,9 @@ def check(st: int, what: str = "libhyflash") -> None:
         raise HyfError(st, what)
 
 
-def make_config(shape: LayerShape, memory: int = HYF_MEM_MAMBA2) -> HyfConfig:
+def make_config(shape: LayerShape, memory: int | None = None) -> HyfConfig:
+    if memory is None:
+        memory = HYF_MEM_GDN if shape.memory == "gdn" else HYF_MEM_MAMBA2
     return HyfConfig(shape.d_model, shape.n_heads, shape.head_dim, shape.d_state, shape.n_groups, shape.window,
                      shape.block, shape.chunk, HYF_BF16 if shape.dtype == BF16 else HYF_F32, memory,
                      shape.cross_slot, 0)

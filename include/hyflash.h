@@ -70,7 +70,7 @@ typedef struct {
   int32_t block;      /* must be HYF_BLOCK                                             */
   int32_t chunk;      /* SSD chunk length L: a power of two, 16..1024                   */
   int32_t dtype;      /* hyf_dtype                                                      */
-  int32_t memory;     /* hyf_memory; only HYF_MEM_MAMBA2 is implemented                 */
+  int32_t memory;     /* hyf_memory (HYF_MEM_GDN: see hyf_weights)                      */
   int32_t cross_slot; /* 1: block rows attend to each other; 0: each only to itself     */
   int32_t reserved;   /* must be 0                                                      */
 } hyf_config;
@@ -79,7 +79,16 @@ typedef struct {
  * w_in rows come in groups, in this order:
  *   q [nh*P] | C [G*N] | k [nh*P] | v [nh*P] | B [G*N] | dt [nh]      (n_in rows in all)
  * The value projection v is also the memory's input x.  a_log, dt_bias and d_skip are
- * fp32 per head: A = -exp(a_log), dt = softplus(raw + dt_bias), D = d_skip. */
+ * fp32 per head: A = -exp(a_log), dt = softplus(raw + dt_bias), D = d_skip.
+ *
+ * memory = HYF_MEM_GDN, the gated delta-rule memory the HyFlash paper's memory ablation swaps in
+ * for Mamba-2 (Gated DeltaNet-2): w_in ends | B [G*N] | alpha [nh] | beta [nh], so n_in has nh
+ * more rows; per head and committed row, with k = B / sqrt(|B|^2 + 1e-6),
+ *   alpha = sigmoid(raw_alpha + dt_bias[h]),  beta = sigmoid(raw_beta + a_log[h]),
+ *   H <- alpha H (I - beta k k^T) + beta v k^T,
+ * and the readout uses C_q / sqrt(|C_q|^2 + 1e-6).  (dt_bias and a_log carry the two gate biases.)
+ * Per-token outputs (y_opt) and hyf_ssd_scan are Mamba-2 only (HYF_EUNSUPPORTED); a commit of more
+ * than 16 rows per request needs d_state <= 192 (HYF_EUNSUPPORTED otherwise). */
 typedef struct {
   const void* w_in;     /* [n_in][d_model], storage dtype, 16-byte aligned */
   const void* w_out;    /* [d_model][nh*P], storage dtype, 16-byte aligned */
@@ -132,6 +141,7 @@ int hyf_state_reset(const hyf_config* cfg, void* state_pool, int32_t pool_slots,
  * Any row count works (a prefill of a whole prefix, or the 1-8 rows of a round).
  * cu_rows (host): int64 [n_req + 1], cu_rows[0] = 0, non-decreasing.  Empty requests
  * are left bit-identical.
+ * With memory = HYF_MEM_GDN the fold is the gated delta rule of hyf_weights, row by row.
  * y_opt (nullable, 16-byte aligned): [cu_rows[n_req]][nh][P] storage dtype, per-token memory
  * outputs y_t = H_t . C_t + D * v_t (H_t after token t, C_t from w_in); HYF_EUNSUPPORTED when a
  * 128-token block of x, B and C does not fit one workgroup's LDS (fp32 with P + 2N > 320).

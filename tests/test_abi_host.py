@@ -42,7 +42,7 @@ def test_named_shapes_are_accepted(shape):
 @pytest.mark.parametrize("field,value,status", [
     ("head_dim", 72, hf.HYF_ESHAPE), ("head_dim", 0, hf.HYF_ESHAPE), ("d_state", 300, hf.HYF_ESHAPE),
     ("n_groups", 3, hf.HYF_ESHAPE), ("window", 0, hf.HYF_ESHAPE), ("block", 7, hf.HYF_ESHAPE),
-    ("chunk", 8, hf.HYF_ESHAPE), ("chunk", 48, hf.HYF_ESHAPE), ("dtype", 5, hf.HYF_EDTYPE), ("memory", hf.HYF_MEM_GDN, hf.HYF_EUNSUPPORTED),
+    ("chunk", 8, hf.HYF_ESHAPE), ("chunk", 48, hf.HYF_ESHAPE), ("dtype", 5, hf.HYF_EDTYPE), ("memory", 2, hf.HYF_EINVAL),
     ("cross_slot", 2, hf.HYF_EINVAL), ("reserved", 1, hf.HYF_EINVAL), ("d_model", 100, hf.HYF_ESHAPE),
 ])
 def test_bad_configs_are_rejected(field, value, status):
@@ -166,3 +166,20 @@ def test_time_tiled_layout_places_each_element_as_documented(elem_bytes):
             off = (((f // 16) * nj + tt // kt) * 64 + ((tt % kt) // vn) * 16 + f % 16) * vn + tt % vn
             assert out[(t // hf.HYF_TBLK) * F * hf.HYF_TBLK + off] == a[t, f]
     assert out.size == 3 * F * hf.HYF_TBLK and (out == -1.0).sum() == (3 * hf.HYF_TBLK - T) * F
+
+
+def test_gated_delta_rule_configs():
+    # the gated delta-rule memory adds a second gate row per head to w_in; its commit has no y, and
+    # the scan entry point on pre-projected inputs is the Mamba-2 memory's only
+    shape = I.QWEN.replace(memory="gdn")
+    cfg = hf.make_config(shape)
+    assert cfg.memory == hf.HYF_MEM_GDN and hf.hyf_config_check(cfg) == hf.HYF_OK
+    assert hf.hyf_n_in(cfg) == shape.n_in == 3 * shape.dq + 2 * shape.gn + 2 * shape.n_heads
+    assert hf.hyf_n_in(hf.make_config(I.QWEN)) == I.QWEN.n_in
+    assert hf.hyf_workspace_bytes(cfg, 1, 8192) > hf.hyf_workspace_bytes(hf.make_config(I.QWEN), 1, 8192)
+    fake = 1 << 20
+    w = hf.HyfWeights(fake, fake, fake, fake, fake)
+    assert hf.hyf_ssd_scan(cfg, fake, fake, None, fake, fake, fake, fake, fake, None, 4, fake, 1 << 30, 0) == \
+        hf.HYF_EUNSUPPORTED
+    assert hf.hyf_memory_commit(cfg, w, fake, 1, None, 1, fake, [0, 4], fake, fake, 1 << 30, 0) == \
+        hf.HYF_EUNSUPPORTED

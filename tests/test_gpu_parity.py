@@ -324,6 +324,54 @@ def test_commit_per_token_outputs_match_the_oracle(name, shape):
     assert_close(g, o, shape.dtype, f"{name} round after y")
 
 
+GDN_SHAPES = [
+    ("tiny_fp32", I.TINY.replace(memory="gdn")),
+    ("small_bf16", small_shape("bf16", window=40, memory="gdn")),
+    ("odd_bf16", small_shape("bf16", n_heads=5, head_dim=48, d_state=32, n_groups=5, window=20, chunk=32, memory="gdn")),
+    ("noncross_fp32", small_shape("f32", window=24, cross_slot=0, memory="gdn")),
+]
+
+
+@pytest.mark.parametrize("name,shape", GDN_SHAPES, ids=[c[0] for c in GDN_SHAPES])
+def test_gated_delta_rule_rounds_match_the_oracle(name, shape):
+    # prefill (the sequential prefix kernel), rounds (the round kernel's tiles), a small commit
+    pr = Pair(shape, seed=71, max_rows=400)
+    pr.gpu.reset()
+    say("gdn hyf_draft_block on an empty state", name)
+    g, o = pr.draft([pr.rows(8, 3)])
+    assert_close(g, o, shape.dtype, f"gdn {name} empty")
+    say("gdn hyf_memory_commit prefill 300", name)
+    pr.commit([pr.rows(300)])
+    pr.check_state(what=f"gdn {name} prefill")
+    acc_rng = pr.rng[4]
+    for rnd in range(8):
+        a = int(acc_rng.integers(1, 9))
+        say("gdn hyf_draft_block round", rnd, "a", a, name)
+        g, o = pr.draft([pr.rows(8, 3)], commits=[pr.rows(a)])
+        assert_close(g, o, shape.dtype, f"gdn {name} round {rnd}")
+    pr.check_state(what=f"gdn {name} after rounds")
+    say("gdn hyf_memory_commit small", name)
+    pr.commit([pr.rows(13)])
+    pr.check_state(what=f"gdn {name} small commit")
+
+
+def test_gated_delta_rule_qwen_prefill_batched_and_rounds():
+    # Qwen-shaped gated delta-rule layer: two requests with ragged prefixes (one of them spans
+    # several time blocks), then rounds over both
+    shape = I.QWEN.replace(memory="gdn")
+    pr = Pair(shape, seed=72, pool_slots=2, max_requests=2, max_rows=2100)
+    pr.gpu.reset()
+    say("gdn qwen prefill 1500 + 555")
+    pr.commit([pr.rows(1500), pr.rows(555)])
+    for s2 in (0, 1):
+        pr.check_state(slot=s2, what=f"gdn qwen prefill {s2}")
+    for rnd in range(3):
+        say("gdn qwen round", rnd)
+        g, o = pr.draft([pr.rows(8, 3), pr.rows(8, 3)], commits=[pr.rows(5), pr.rows(2)])
+        assert_close(g, o, "bf16", f"gdn qwen round {rnd}")
+    pr.check_state(slot=1, what="gdn qwen rounds")
+
+
 def test_qwen_full_size_prefill_and_rounds():
     # The 8192-row Qwen-shaped prefix and a few rounds, exactly as the benchmark launches them.
     shape = I.QWEN
