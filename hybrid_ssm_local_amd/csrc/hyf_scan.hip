@@ -532,7 +532,21 @@ __global__ void __launch_bounds__(256) k_ssd_y(Shape sh, ScanArgs a, ReqTable rt
 // H_p <- alpha (H_p - beta (H_p . k) k) + beta x_p k with k = B / sqrt(|B|^2 + 1e-6).
 // Gates: alpha = sigmoid(raw + dt_bias[h]), beta = sigmoid(raw' + a_log[h]) with the raw gates
 // time-blocked in a.dt (alpha at feature h, beta at feature nh + h).
-constexpr int GDN_ROWS = 64;
+constexpr int GDN_ROWS = 16;  // H rows per workgroup: many workgroups, so the whole chip shares the sequential work
+// Sum over the 16 lanes of a DPP row (lanes 16 i .. 16 i + 15), every lane getting the total: swaps
+// inside quads ([1,0,3,2], then [2,3,0,1]), then the mirrored half-row and the mirrored row.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);  // row_half_mirror
+  v += dpp<0x140>(v);  // row_mirror
+  return v;
+}
+
 template <typename T, int NCH>
 __global__ void __launch_bounds__(16 * GDN_ROWS) k_gdn_seq(Shape sh, ScanArgs a, ReqTable rt, int npb) {
   constexpr int VN = Vec16<T>::n;
@@ -587,25 +601,36 @@ __global__ void __launch_bounds__(16 * GDN_ROWS) k_gdn_seq(Shape sh, ScanArgs a,
       bg[u] = 1.f / (1.f + __expf(-(rb + bb)));
     }
     __syncthreads();
-    for (int u = t; u < TB; u += nt) {
+    // inverse key norms: 16 threads per token (a DPP row), tokens t / 16, t / 16 + nt / 16, ...
+    for (int u = t >> 4; u < TB; u += nt >> 4) {
       float ss = 0.f;
-      for (int n = 0; n < N; ++n) ss += ks[u * N + n] * ks[u * N + n];
-      iv[u] = rsqrtf(ss + 1e-6f);
+      for (int n = c16; n < N; n += 16) ss += ks[u * N + n] * ks[u * N + n];
+      ss = row16_sum(ss);
+      if (c16 == 0) iv[u] = rsqrtf(ss + 1e-6f);
     }
     __syncthreads();
+    // the next token's operands are read while the current one updates the row
+    float kn[NCH], inv_n = iv[0], al_n = ag[0], be_n = bg[0], x_n = xs[prow];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) kn[j] = ks[c16 * NCH + j];
     for (int u = 0; u < len; ++u) {
-      const float inv = iv[u];
       float kv[NCH];
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) kv[j] = kn[j] * inv_n;
+      const float al = al_n, be = be_n, xu = x_n;
+      if (u + 1 < TB) {
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) kn[j] = ks[(u + 1) * N + c16 * NCH + j];
+        inv_n = iv[u + 1];
+        al_n = ag[u + 1];
+        be_n = bg[u + 1];
+        x_n = xs[(u + 1) * GDN_ROWS + prow];
+      }
       float d = 0.f;
 #pragma unroll
-      for (int j = 0; j < NCH; ++j) {
-        kv[j] = ks[u * N + c16 * NCH + j] * inv;
-        d += Hr[j] * kv[j];
-      }
-#pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) d += __shfl_xor(d, o, 64);
-      const float al = ag[u], be = bg[u];
-      const float xw = active ? be * xs[u * GDN_ROWS + prow] : 0.f;
+      for (int j = 0; j < NCH; ++j) d += Hr[j] * kv[j];
+      d = row16_sum(d);
+      const float xw = active ? be * xu : 0.f;
       const float bd = be * d;
 #pragma unroll
       for (int j = 0; j < NCH; ++j) Hr[j] = al * (Hr[j] - bd * kv[j]) + xw * kv[j];
