@@ -479,7 +479,7 @@ def main():
                      "bytes_per_launch": proj["bytes"], "avg_us": proj["mean_us"]},
         "gemm_roofline": {"bound": "mfma", "achieved": gemm["tflops"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                           "frac": gemm["tflops"] / BF16_PEAK_TFLOPS,
-                          "kernel": "k_gemm_bf16: prefill projection 8192 x 2560 x 2720", "avg_us": gemm["mean_us"]},
+                          "kernel": "k_gemm_bf16_256: prefill projection 8192 x 2560 x 2720", "avg_us": gemm["mean_us"]},
         "gated_delta_rule": gdn,
         "cpu_baseline": cpu,
     }

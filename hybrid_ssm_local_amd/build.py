@@ -17,7 +17,9 @@ INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libhyflash.so")
 
-SOURCES = ["hyf_abi.cpp", "hyf_proj.hip", "hyf_scan.hip", "hyf_round.hip"]
+SOURCES = ["hyf_abi.cpp", "hyf_proj.hip", "hyf_gemm.hip", "hyf_scan.hip", "hyf_round.hip"]
+# Per-source extra flags.  The large GEMM keeps its MFMA accumulators in the unified VGPR file.
+EXTRA = {"hyf_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # Packed fp32 instructions stay disabled: hipcc would otherwise form them from float2/float4 code.
@@ -27,7 +29,7 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, 
 
 def _compile(src: str) -> str:
     obj = os.path.join(LIBDIR, "obj", os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr[-8000:]}")

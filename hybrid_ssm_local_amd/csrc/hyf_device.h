@@ -106,6 +106,10 @@ __device__ __forceinline__ void vm_wait() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Wait until this wave's LDS (and scalar-memory) operations are done: lgkmcnt(0), vmcnt and
+// expcnt at their no-wait maxima.
+__device__ __forceinline__ void lgkm_wait0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+
 // Direct global -> LDS loads (no registers): lane l's 16 (or 4) bytes land at lds_base + 16 l
 // (4 l).  lds_base must be the same for the whole wave; the data is there once this wave's
 // vector-memory count drains (vm_wait<0>) — other waves see it after a barrier.

@@ -1,0 +1,249 @@
+// bf16 GEMM for K a multiple of 64 on 256x128 tiles (the prefill projections and batched rounds).
+//
+// Built in its own translation unit with MFMA accumulators in the unified VGPR file
+// (-mllvm -amdgpu-mfma-vgpr-form): with accumulation registers the register allocator rotated the
+// 128 accumulator registers through copies on every K step.
+#include <mutex>
+
+#include "hyf_launch.h"
+
+namespace hyf {
+
+// bf16 GEMM for K a multiple of 64: 256x128 macro tiles (rows x features), K step 64, three LDS
+// stages filled by direct global -> LDS copies, one workgroup per CU (4 waves, one per SIMD).
+// Wave (wm, wn) owns the 128 x 64 block of rows wm*128.., features wn*64.. (32 accumulator tiles).
+//
+// Why this shape: per K step the workgroup does 2*256*128*64 flops against 48 KiB staged and
+// 96 KiB of fragment reads from LDS, so a CU at the MFMA rate needs about 47 B/clk from L2 and
+// 140 B/clk of LDS; a 128x128 tile with 64x64 per wave needs 64 B/clk from L2 per workgroup pair
+// and more LDS traffic per flop.  Three stages keep two K steps of loads in flight while one
+// computes, which covers the L2/HBM latency with a single wave per SIMD.
+//
+// LDS operand layout (both operands are K-contiguous rows): row r of a stage is 128 bytes = 8
+// chunks of 16 bytes; logical chunk c sits at position c ^ (r & 7), so the 16 lanes of an MFMA
+// fragment load (16 rows, one chunk) hit 8 distinct 16-byte bank groups per 8 lanes.  A direct
+// copy writes lane l's 16 bytes at base + 16 l, so lane l of a copy covering rows r0 .. r0 + 7
+// (r0 a multiple of 8) fetches row r0 + l / 8, logical chunk (l % 8) ^ (l / 8).
+constexpr int G2_M = 256, G2_N = 128, G2_K = 64, G2_ST = 3;
+constexpr int G2_STAGE = (G2_M + G2_N) * G2_K * 2;  // bytes per stage (48 KiB)
+constexpr int G2_LDS = G2_ST * G2_STAGE;            // 144 KiB
+constexpr int G2_GROUP = 4;                         // M tiles per group in the tile order
+
+template <typename TO>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+k_gemm_bf16_256(RowSrc xs, int M, int K, const bf16* __restrict__ W, int Nout, Epi epi, int tm, int tn,
+                int per_xcd) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  // Tile order: workgroup b runs on XCD b % 8; each XCD takes a contiguous range of tiles, walked
+  // in groups of G2_GROUP row tiles column by column, so the workgroups an XCD runs together
+  // share row and weight slabs in its L2.
+  const int tile = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (tile >= tm * tn) return;
+  const int grp = tile / (G2_GROUP * tn), in_grp = tile % (G2_GROUP * tn);
+  const int gm = min(G2_GROUP, tm - grp * G2_GROUP);
+  const int mi = grp * G2_GROUP + in_grp % gm, ni = in_grp / gm;
+  const int m0 = mi * G2_M, n0 = ni * G2_N;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int i = lane & 15, g = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
+  if (epi.zero && tile == 0)
+    for (int z = t; z < epi.n_zero; z += 256) epi.zero[z] = 0;
+
+  // Source rows of this lane's copies: A copy j covers rows 8 (wave + 4 j) .. + 7 (j < 8), B copy
+  // j rows 8 (wave + 4 j) .. + 7 (j < 4); rows past M or Nout repeat the last one (never stored).
+  const int lr = lane >> 3, lc = (lane & 7) ^ lr;  // row within the copy, logical chunk
+  const char* asrc[8];
+  const char* bsrc[4];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int m = min(m0 + 8 * (wave + 4 * j) + lr, M - 1);
+    asrc[j] = static_cast<const char*>(row_ptr(xs, m, K, 2)) + 16 * lc;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int f = min(n0 + 8 * (wave + 4 * j) + lr, Nout - 1);
+    bsrc[j] = reinterpret_cast<const char*>(W + (int64_t)f * K) + 16 * lc;
+  }
+  auto issue = [&](int kt) __attribute__((always_inline)) {
+    char* st = smem + (kt % G2_ST) * G2_STAGE;
+    const int64_t kb = (int64_t)kt * G2_K * 2;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) lds_dma16(asrc[j] + kb, st + (wave + 4 * j) * 1024);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lds_dma16(bsrc[j] + kb, st + G2_M * 128 + (wave + 4 * j) * 1024);
+  };
+
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = K / G2_K;
+  issue(0);
+  if (nk > 1) issue(1);
+  // fragment offsets: row r (r & 7 == i & 7), logical chunk c = 4 ks + g at position c ^ (i & 7)
+  const int arow = (wm * 128 + i) * 128, brow = G2_M * 128 + (wn * 64 + i) * 128;
+  auto frags = [&](const char* st, int ks, bf16x8 (&fa)[8], bf16x8 (&fb)[4]) __attribute__((always_inline)) {
+    const int co = ((4 * ks + g) ^ (i & 7)) * 16;
+#pragma unroll
+    for (int a = 0; a < 8; ++a) fa[a] = *reinterpret_cast<const bf16x8*>(st + arow + a * 16 * 128 + co);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) fb[b] = *reinterpret_cast<const bf16x8*>(st + brow + b * 16 * 128 + co);
+  };
+  auto mma = [&](const bf16x8 (&fa)[8], const bf16x8 (&fb)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
+  };
+  // Software pipeline over half-steps (32 k values).  Fragments of the next half-step are read
+  // while the current half-step's 32 MFMAs run; before a new batch of 12 fragment reads the
+  // previous batch is waited on (it has had a whole MFMA batch to land), so at most 12 LDS reads
+  // are ever outstanding.  The barrier of stage kt + 1 sits between the two half-steps of stage kt:
+  // once every wave passes it, stage kt + 1 is in LDS and all reads of stage kt are done, so the
+  // copies of stage kt + 3 can refill stage kt's buffer.  The barrier is the bare instruction: a
+  // __syncthreads() fence would also wait for the copies still in flight.
+  auto barrier = [&]() __attribute__((always_inline)) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  bf16x8 fa0[8], fb0[4], fa1[8], fb1[4];
+  if (nk > 1)
+    vm_wait<12>();
+  else
+    vm_wait<0>();
+  barrier();
+  if (nk > 2) issue(2);
+  frags(smem, 0, fa0, fb0);
+  // stage kt: its first half-step's fragments are in fa0/fb0 (read during the previous MFMAs)
+  auto first_half = [&](int kt) __attribute__((always_inline)) {
+    lgkm_wait0();
+    frags(smem + (kt % G2_ST) * G2_STAGE, 1, fa1, fb1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(fa0, fb0);
+    __builtin_amdgcn_sched_barrier(0);
+    lgkm_wait0();
+  };
+  for (int kt = 0; kt + 1 < nk; ++kt) {
+    first_half(kt);
+    // stage kt + 1 landed once at most the copies of stage kt + 2 (issued one barrier ago) remain;
+    // every wave's reads of stage kt are done, so the copies of stage kt + 3 may refill its buffer
+    if (kt + 2 < nk)
+      vm_wait<12>();
+    else
+      vm_wait<0>();
+    barrier();
+    if (kt + 3 < nk) issue(kt + 3);
+    frags(smem + ((kt + 1) % G2_ST) * G2_STAGE, 0, fa0, fb0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(fa1, fb1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  first_half(nk - 1);
+  mma(fa1, fb1);
+  __syncthreads();  // the stages are dead: the epilogue reuses LDS
+
+  if (epi.trans) {
+    // Time-blocked output: a 256-row tile spans two blocks (m0 is a multiple of 256).  The fp32
+    // tile is staged as [f][m] (pitch CP floats); each item then writes 8 tokens of one feature:
+    // one 16-byte chunk of the tiled layout (out0), or two 16-byte runs of a plain row (out1).
+    constexpr int CP = G2_M + 4;
+    float* ct = reinterpret_cast<float*>(smem);
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ct[(wn * 64 + b * 16 + i) * CP + wm * 128 + a * 16 + 4 * g + r] = acc[a][b][r];
+    __syncthreads();
+    for (int it = t; it < G2_N * (G2_M / 8); it += 256) {
+      const int fl = it % G2_N, m8 = (it / G2_N) * 8;
+      const int f = n0 + fl;
+      const int64_t m = (int64_t)m0 + m8;
+      if (f >= Nout || m >= M) continue;
+      const float* src = ct + fl * CP + m8;
+      if (m + 8 <= M) {
+        const int64_t blk = m / HYF_TBLK;
+        const int off = (int)(m % HYF_TBLK);
+        if (f < epi.n_split && !epi.out0_f32) {
+          bf16x8 v;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = static_cast<bf16>(src[e]);
+          *reinterpret_cast<bf16x8*>(static_cast<bf16*>(epi.out0) + blk * epi.ld0 + tile_off<bf16>(f, off)) = v;
+        } else {
+          float* dst = f < epi.n_split ? static_cast<float*>(epi.out0) + blk * epi.ld0 + (int64_t)f * HYF_TBLK + off
+                                       : epi.out1 + blk * epi.ld1 + (int64_t)(f - epi.n_split) * HYF_TBLK + off;
+          *reinterpret_cast<f32x4*>(dst) = f32x4{src[0], src[1], src[2], src[3]};
+          *reinterpret_cast<f32x4*>(dst + 4) = f32x4{src[4], src[5], src[6], src[7]};
+        }
+      } else {
+        for (int e = 0; m + e < M; ++e) epi_store<TO>(epi, m + e, f, src[e]);
+      }
+    }
+    return;
+  }
+  // Row-major output: the fp32 tile is staged as [m][f] (pitch RP floats); each item then writes 8
+  // features of one row, as one or two 16-byte stores where the destination allows it.
+  constexpr int RP = G2_N + 4;
+  float* ct = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ct[(wm * 128 + a * 16 + 4 * g + r) * RP + wn * 64 + b * 16 + i] = acc[a][b][r];
+  __syncthreads();
+  for (int it = t; it < G2_M * (G2_N / 8); it += 256) {
+    const int ml = it / (G2_N / 8), f8 = (it % (G2_N / 8)) * 8;
+    const int64_t m = (int64_t)m0 + ml;
+    const int f = n0 + f8;
+    if (m >= M || f >= Nout) continue;
+    const float* src = ct + ml * RP + f8;
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(src), hi = *reinterpret_cast<const f32x4*>(src + 4);
+    if (f + 8 <= Nout && (f + 8 <= epi.n_split || f >= epi.n_split)) {
+      if (f < epi.n_split && !epi.out0_f32) {
+        bf16* dst = static_cast<bf16*>(epi.out0) + m * epi.ld0 + f;
+        if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+          bf16x8 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[e] = static_cast<bf16>(lo[e]);
+            v[4 + e] = static_cast<bf16>(hi[e]);
+          }
+          *reinterpret_cast<bf16x8*>(dst) = v;
+          continue;
+        }
+      } else {
+        float* dst = f < epi.n_split ? static_cast<float*>(epi.out0) + m * epi.ld0 + f
+                                     : epi.out1 + m * epi.ld1 + (f - epi.n_split);
+        if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+          *reinterpret_cast<f32x4*>(dst) = lo;
+          *reinterpret_cast<f32x4*>(dst + 4) = hi;
+          continue;
+        }
+      }
+    }
+    for (int e = 0; e < 8 && f + e < Nout; ++e) epi_store<TO>(epi, m, f + e, src[e]);
+  }
+}
+
+hipError_t launch_gemm256(RowSrc x, int M, int K, const bf16* W, int Nout, const Epi& epi, hipStream_t s) {
+  static std::once_flag once;
+  static hipError_t set_err = hipSuccess;
+  std::call_once(once, [] {
+    set_err = hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm_bf16_256<bf16>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, G2_LDS);
+  });
+  if (set_err != hipSuccess) return set_err;
+  const int tm = (M + G2_M - 1) / G2_M, tn = (Nout + G2_N - 1) / G2_N;
+  const int per_xcd = (tm * tn + 7) / 8;
+  hipLaunchKernelGGL((k_gemm_bf16_256<bf16>), dim3(8 * per_xcd), dim3(256), G2_LDS, s, x, M, K, W, Nout, epi, tm, tn,
+                     per_xcd);
+  return hipGetLastError();
+}
+
+}  // namespace hyf

@@ -34,10 +34,43 @@ struct RowSrc {
   int64_t M1;
 };
 
+// Store of output element (row m, feature f) through an epilogue description.
+template <typename T>
+__device__ __forceinline__ void epi_store(const Epi& e, int64_t m, int f, float v) {
+  if (e.trans) {
+    const int64_t blk = m / HYF_TBLK, off = m % HYF_TBLK;
+    if (f < e.n_split) {
+      // out0: the tiled layout of the storage dtype (or plain [f][HYF_TBLK] for fp32 output)
+      if (e.out0_f32)
+        static_cast<float*>(e.out0)[blk * e.ld0 + (int64_t)f * HYF_TBLK + off] = v;
+      else
+        static_cast<T*>(e.out0)[blk * e.ld0 + tile_off<T>(f, (int)off)] = from_f32<T>(v);
+    } else {
+      e.out1[blk * e.ld1 + (int64_t)(f - e.n_split) * HYF_TBLK + off] = v;
+    }
+    return;
+  }
+  if (f < e.n_split) {
+    if (e.out0_f32)
+      static_cast<float*>(e.out0)[m * e.ld0 + f] = v;
+    else
+      static_cast<T*>(e.out0)[m * e.ld0 + f] = from_f32<T>(v);
+  } else {
+    e.out1[m * e.ld1 + (f - e.n_split)] = v;
+  }
+}
+
+__device__ __forceinline__ const void* row_ptr(const RowSrc& xs, int64_t m, int K, int esz) {
+  if (m < xs.M1) return static_cast<const char*>(xs.X1) + m * (int64_t)K * esz;
+  return static_cast<const char*>(xs.X2) + (m - xs.M1) * (int64_t)K * esz;
+}
+
 // out[m][f] = sum_k X[m][k] * W[f][k]   for m < M, f < Nout (W is [Nout][K], row-major).
 // Picks the weight-streaming kernel (small M) or the tiled MFMA GEMM (large M).
 hipError_t launch_linear(int dtype, RowSrc x, int64_t M, int K, const void* W, int Nout,
                          const Epi& epi, hipStream_t s);
+// The 256x128-tile bf16 GEMM (hyf_gemm.hip); K must be a multiple of 64.
+hipError_t launch_gemm256(RowSrc x, int M, int K, const bf16* W, int Nout, const Epi& epi, hipStream_t s);
 
 // Memory scan over segments (see hyf_scan.hip).  Inputs are time-blocked: token t of request i
 // sits in block blk0[i] + t / HYF_TBLK (block stride *blk); x, B and C are tiled inside a block

@@ -6,8 +6,11 @@
 //    waves split K into slabs and reduce their partial tiles through LDS in a fixed order
 //    (deterministic).  MFMA 16x16 tiles: W is the A operand (16 features), X^T the B operand
 //    (16 rows per tile).
-//  * k_gemm_bf16 (large M): prefill and batched rounds.  128x128 macro tiles, K step 64,
-//    double-buffered LDS, 4 waves of 64x64 each built from 16x16x32 bf16 MFMAs.
+//  * k_gemm_bf16_256 (large M, K a multiple of 64): prefill and batched rounds.  256x128 macro
+//    tiles, three LDS stages filled by direct global -> LDS copies, 4 waves of 128x64 each built
+//    from 16x16x32 bf16 MFMAs.
+//  * k_gemm_bf16 (large M, other K): 128x128 macro tiles, K step 64, register-staged
+//    double-buffered LDS, 4 waves of 64x64.
 #include <mutex>
 
 #include "hyf_launch.h"
@@ -17,36 +20,6 @@ namespace hyf {
 template <typename T>
 __device__ __forceinline__ typename Vec16<T>::type ld_vec(const T* p) {
   return *reinterpret_cast<const typename Vec16<T>::type*>(p);
-}
-
-template <typename T>
-__device__ __forceinline__ void epi_store(const Epi& e, int64_t m, int f, float v) {
-  if (e.trans) {
-    const int64_t blk = m / HYF_TBLK, off = m % HYF_TBLK;
-    if (f < e.n_split) {
-      // out0: the tiled layout of the storage dtype (or plain [f][HYF_TBLK] for fp32 output)
-      if (e.out0_f32)
-        static_cast<float*>(e.out0)[blk * e.ld0 + (int64_t)f * HYF_TBLK + off] = v;
-      else
-        static_cast<T*>(e.out0)[blk * e.ld0 + tile_off<T>(f, (int)off)] = from_f32<T>(v);
-    } else {
-      e.out1[blk * e.ld1 + (int64_t)(f - e.n_split) * HYF_TBLK + off] = v;
-    }
-    return;
-  }
-  if (f < e.n_split) {
-    if (e.out0_f32)
-      static_cast<float*>(e.out0)[m * e.ld0 + f] = v;
-    else
-      static_cast<T*>(e.out0)[m * e.ld0 + f] = from_f32<T>(v);
-  } else {
-    e.out1[m * e.ld1 + (f - e.n_split)] = v;
-  }
-}
-
-__device__ __forceinline__ const void* row_ptr(const RowSrc& xs, int64_t m, int K, int esz) {
-  if (m < xs.M1) return static_cast<const char*>(xs.X1) + m * (int64_t)K * esz;
-  return static_cast<const char*>(xs.X2) + (m - xs.M1) * (int64_t)K * esz;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -146,11 +119,6 @@ k_proj_small(RowSrc xs, int M, int K, const T* __restrict__ W, int Nout, Epi epi
 // the row's 16-byte chunk p ^ r, so the fragment reads of 16 lanes (16 rows, one chunk) fall in 16
 // different bank groups.  Each wave owns its LDS region, so only its own load count is waited on.
 constexpr int PS_SLAB = 128;  // k per slab: 256 bytes of a row
-
-__device__ __forceinline__ void lgkm_wait0() {
-  // lgkmcnt(0), vmcnt and expcnt at their no-wait maxima
-  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
-}
 
 template <int NW, int MT>
 __global__ void __launch_bounds__(NW * 64)
@@ -434,6 +402,7 @@ hipError_t launch_linear(int dtype, RowSrc x, int64_t M, int K, const void* W, i
   if (M <= 0 || Nout <= 0) return hipSuccess;
   if (dtype == HYF_BF16) {
     if (M <= 64 && !epi.trans) return launch_small<bf16>(x, (int)M, K, static_cast<const bf16*>(W), Nout, epi, s);
+    if (K % 64 == 0) return launch_gemm256(x, (int)M, K, static_cast<const bf16*>(W), Nout, epi, s);
     dim3 grid((Nout + GB_N - 1) / GB_N, (unsigned)((M + GB_M - 1) / GB_M));
     hipLaunchKernelGGL((k_gemm_bf16<bf16>), grid, dim3(256), 0, s, x, (int)M, K, static_cast<const bf16*>(W),
                        Nout, epi);

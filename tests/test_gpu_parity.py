@@ -157,6 +157,12 @@ LINEAR_CASES = [  # (dtype, K, Nout, Ms): K tails past a 128-wide slab, M across
     ("bf16", 144, 7, [1, 16, 17, 40, 64, 65, 200]),
     ("bf16", 2560, 300, [1, 12, 16, 33, 64, 130]),
     ("bf16", 5120, 40, [8, 49]),
+    # the 256x128-tile GEMM (K a multiple of 64, M > 64): one, two and three K steps (the
+    # three-stage pipeline's edges), ragged row and feature tiles
+    ("bf16", 64, 130, [65, 257]),
+    ("bf16", 128, 129, [100]),
+    ("bf16", 192, 256, [300]),
+    ("bf16", 256, 2720, [1000]),
     ("f32", 256, 100, [1, 20, 64, 65]),
 ]
 
