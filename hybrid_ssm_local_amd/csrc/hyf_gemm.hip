@@ -10,14 +10,15 @@
 namespace hyf {
 
 // bf16 GEMM for K a multiple of 64: 256x128 macro tiles (rows x features), K step 64, three LDS
-// stages filled by direct global -> LDS copies, one workgroup per CU (4 waves, one per SIMD).
-// Wave (wm, wn) owns the 128 x 64 block of rows wm*128.., features wn*64.. (32 accumulator tiles).
+// stages filled by direct global -> LDS copies, one workgroup per CU.  With NW waves the waves
+// form an (NW/2) x 2 grid: wave (wm, wn) owns rows wm*RW .. + RW - 1 (RW = 512 / NW) and features
+// wn*64 .. + 63.  The library runs NW = 8 (two waves per SIMD, 64 x 64 per wave): one wave's
+// MFMAs then cover the other's LDS reads, barrier and copy waits.  Measured at 8192 x 2560 x 2720:
+// 117 us with 8 waves against 145 us with 4 waves of 128 x 64 (one per SIMD).
 //
-// Why this shape: per K step the workgroup does 2*256*128*64 flops against 48 KiB staged and
-// 96 KiB of fragment reads from LDS, so a CU at the MFMA rate needs about 47 B/clk from L2 and
-// 140 B/clk of LDS; a 128x128 tile with 64x64 per wave needs 64 B/clk from L2 per workgroup pair
-// and more LDS traffic per flop.  Three stages keep two K steps of loads in flight while one
-// computes, which covers the L2/HBM latency with a single wave per SIMD.
+// Per K step the workgroup does 2*256*128*64 flops against 48 KiB staged, so a CU at the MFMA
+// rate needs about 47 B/clk from L2 (a 128x128 tile would need 64 B/clk per pair of workgroups).
+// Three stages keep two K steps of copies in flight while one computes.
 //
 // LDS operand layout (both operands are K-contiguous rows): row r of a stage is 128 bytes = 8
 // chunks of 16 bytes; logical chunk c sits at position c ^ (r & 7), so the 16 lanes of an MFMA
@@ -28,9 +29,10 @@ constexpr int G2_M = 256, G2_N = 128, G2_K = 64, G2_ST = 3;
 constexpr int G2_STAGE = (G2_M + G2_N) * G2_K * 2;  // bytes per stage (48 KiB)
 constexpr int G2_LDS = G2_ST * G2_STAGE;            // 144 KiB
 constexpr int G2_GROUP = 4;                         // M tiles per group in the tile order
+constexpr int G2_NW = 8;                            // waves per workgroup (two per SIMD)
 
-template <typename TO>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <typename TO, int NW>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 k_gemm_bf16_256(RowSrc xs, int M, int K, const bf16* __restrict__ W, int Nout, Epi epi, int tm, int tn,
                 int per_xcd) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -46,37 +48,42 @@ k_gemm_bf16_256(RowSrc xs, int M, int K, const bf16* __restrict__ W, int Nout, E
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int i = lane & 15, g = lane >> 4;
+  constexpr int NT = 64 * NW;             // threads
+  constexpr int RW = G2_M / (NW / 2);     // rows per wave (128 or 64)
+  constexpr int AT = RW / 16;             // row tiles per wave
+  constexpr int CA = G2_M / 8 / NW, CB = G2_N / 8 / NW;  // copies per stage and thread
   const int wm = wave >> 1, wn = wave & 1;
   if (epi.zero && tile == 0)
-    for (int z = t; z < epi.n_zero; z += 256) epi.zero[z] = 0;
+    for (int z = t; z < epi.n_zero; z += NT) epi.zero[z] = 0;
 
-  // Source rows of this lane's copies: A copy j covers rows 8 (wave + 4 j) .. + 7 (j < 8), B copy
-  // j rows 8 (wave + 4 j) .. + 7 (j < 4); rows past M or Nout repeat the last one (never stored).
+  // Source rows of this lane's copies: A copy j covers rows 8 (wave + NW j) .. + 7 (j < CA), B
+  // copy j rows 8 (wave + NW j) .. + 7 (j < CB); rows past M or Nout repeat the last one (never
+  // stored).
   const int lr = lane >> 3, lc = (lane & 7) ^ lr;  // row within the copy, logical chunk
-  const char* asrc[8];
-  const char* bsrc[4];
+  const char* asrc[CA];
+  const char* bsrc[CB];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int m = min(m0 + 8 * (wave + 4 * j) + lr, M - 1);
+  for (int j = 0; j < CA; ++j) {
+    const int m = min(m0 + 8 * (wave + NW * j) + lr, M - 1);
     asrc[j] = static_cast<const char*>(row_ptr(xs, m, K, 2)) + 16 * lc;
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int f = min(n0 + 8 * (wave + 4 * j) + lr, Nout - 1);
+  for (int j = 0; j < CB; ++j) {
+    const int f = min(n0 + 8 * (wave + NW * j) + lr, Nout - 1);
     bsrc[j] = reinterpret_cast<const char*>(W + (int64_t)f * K) + 16 * lc;
   }
   auto issue = [&](int kt) __attribute__((always_inline)) {
     char* st = smem + (kt % G2_ST) * G2_STAGE;
     const int64_t kb = (int64_t)kt * G2_K * 2;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) lds_dma16(asrc[j] + kb, st + (wave + 4 * j) * 1024);
+    for (int j = 0; j < CA; ++j) lds_dma16(asrc[j] + kb, st + (wave + NW * j) * 1024);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) lds_dma16(bsrc[j] + kb, st + G2_M * 128 + (wave + 4 * j) * 1024);
+    for (int j = 0; j < CB; ++j) lds_dma16(bsrc[j] + kb, st + G2_M * 128 + (wave + NW * j) * 1024);
   };
 
-  f32x4 acc[8][4];
+  f32x4 acc[AT][4];
 #pragma unroll
-  for (int a = 0; a < 8; ++a)
+  for (int a = 0; a < AT; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -84,17 +91,17 @@ k_gemm_bf16_256(RowSrc xs, int M, int K, const bf16* __restrict__ W, int Nout, E
   issue(0);
   if (nk > 1) issue(1);
   // fragment offsets: row r (r & 7 == i & 7), logical chunk c = 4 ks + g at position c ^ (i & 7)
-  const int arow = (wm * 128 + i) * 128, brow = G2_M * 128 + (wn * 64 + i) * 128;
-  auto frags = [&](const char* st, int ks, bf16x8 (&fa)[8], bf16x8 (&fb)[4]) __attribute__((always_inline)) {
+  const int arow = (wm * RW + i) * 128, brow = G2_M * 128 + (wn * 64 + i) * 128;
+  auto frags = [&](const char* st, int ks, bf16x8 (&fa)[AT], bf16x8 (&fb)[4]) __attribute__((always_inline)) {
     const int co = ((4 * ks + g) ^ (i & 7)) * 16;
 #pragma unroll
-    for (int a = 0; a < 8; ++a) fa[a] = *reinterpret_cast<const bf16x8*>(st + arow + a * 16 * 128 + co);
+    for (int a = 0; a < AT; ++a) fa[a] = *reinterpret_cast<const bf16x8*>(st + arow + a * 16 * 128 + co);
 #pragma unroll
     for (int b = 0; b < 4; ++b) fb[b] = *reinterpret_cast<const bf16x8*>(st + brow + b * 16 * 128 + co);
   };
-  auto mma = [&](const bf16x8 (&fa)[8], const bf16x8 (&fb)[4]) __attribute__((always_inline)) {
+  auto mma = [&](const bf16x8 (&fa)[AT], const bf16x8 (&fb)[4]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int a = 0; a < 8; ++a)
+    for (int a = 0; a < AT; ++a)
 #pragma unroll
       for (int b = 0; b < 4; ++b)
         acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
@@ -111,9 +118,9 @@ k_gemm_bf16_256(RowSrc xs, int M, int K, const bf16* __restrict__ W, int Nout, E
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  bf16x8 fa0[8], fb0[4], fa1[8], fb1[4];
+  bf16x8 fa0[AT], fb0[4], fa1[AT], fb1[4];
   if (nk > 1)
-    vm_wait<12>();
+    vm_wait<CA + CB>();
   else
     vm_wait<0>();
   barrier();
@@ -133,7 +140,7 @@ k_gemm_bf16_256(RowSrc xs, int M, int K, const bf16* __restrict__ W, int Nout, E
     // stage kt + 1 landed once at most the copies of stage kt + 2 (issued one barrier ago) remain;
     // every wave's reads of stage kt are done, so the copies of stage kt + 3 may refill its buffer
     if (kt + 2 < nk)
-      vm_wait<12>();
+      vm_wait<CA + CB>();
     else
       vm_wait<0>();
     barrier();
@@ -154,13 +161,13 @@ k_gemm_bf16_256(RowSrc xs, int M, int K, const bf16* __restrict__ W, int Nout, E
     constexpr int CP = G2_M + 4;
     float* ct = reinterpret_cast<float*>(smem);
 #pragma unroll
-    for (int a = 0; a < 8; ++a)
+    for (int a = 0; a < AT; ++a)
 #pragma unroll
       for (int b = 0; b < 4; ++b)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ct[(wn * 64 + b * 16 + i) * CP + wm * 128 + a * 16 + 4 * g + r] = acc[a][b][r];
+        for (int r = 0; r < 4; ++r) ct[(wn * 64 + b * 16 + i) * CP + wm * RW + a * 16 + 4 * g + r] = acc[a][b][r];
     __syncthreads();
-    for (int it = t; it < G2_N * (G2_M / 8); it += 256) {
+    for (int it = t; it < G2_N * (G2_M / 8); it += NT) {
       const int fl = it % G2_N, m8 = (it / G2_N) * 8;
       const int f = n0 + fl;
       const int64_t m = (int64_t)m0 + m8;
@@ -191,13 +198,13 @@ k_gemm_bf16_256(RowSrc xs, int M, int K, const bf16* __restrict__ W, int Nout, E
   constexpr int RP = G2_N + 4;
   float* ct = reinterpret_cast<float*>(smem);
 #pragma unroll
-  for (int a = 0; a < 8; ++a)
+  for (int a = 0; a < AT; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ct[(wm * 128 + a * 16 + 4 * g + r) * RP + wn * 64 + b * 16 + i] = acc[a][b][r];
+      for (int r = 0; r < 4; ++r) ct[(wm * RW + a * 16 + 4 * g + r) * RP + wn * 64 + b * 16 + i] = acc[a][b][r];
   __syncthreads();
-  for (int it = t; it < G2_M * (G2_N / 8); it += 256) {
+  for (int it = t; it < G2_M * (G2_N / 8); it += NT) {
     const int ml = it / (G2_N / 8), f8 = (it % (G2_N / 8)) * 8;
     const int64_t m = (int64_t)m0 + ml;
     const int f = n0 + f8;
@@ -235,13 +242,13 @@ hipError_t launch_gemm256(RowSrc x, int M, int K, const bf16* W, int Nout, const
   static std::once_flag once;
   static hipError_t set_err = hipSuccess;
   std::call_once(once, [] {
-    set_err = hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm_bf16_256<bf16>),
+    set_err = hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm_bf16_256<bf16, G2_NW>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, G2_LDS);
   });
   if (set_err != hipSuccess) return set_err;
   const int tm = (M + G2_M - 1) / G2_M, tn = (Nout + G2_N - 1) / G2_N;
   const int per_xcd = (tm * tn + 7) / 8;
-  hipLaunchKernelGGL((k_gemm_bf16_256<bf16>), dim3(8 * per_xcd), dim3(256), G2_LDS, s, x, M, K, W, Nout, epi, tm, tn,
+  hipLaunchKernelGGL((k_gemm_bf16_256<bf16, G2_NW>), dim3(8 * per_xcd), dim3(64 * G2_NW), G2_LDS, s, x, M, K, W, Nout, epi, tm, tn,
                      per_xcd);
   return hipGetLastError();
 }

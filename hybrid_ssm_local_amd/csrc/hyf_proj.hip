@@ -6,9 +6,9 @@
 //    waves split K into slabs and reduce their partial tiles through LDS in a fixed order
 //    (deterministic).  MFMA 16x16 tiles: W is the A operand (16 features), X^T the B operand
 //    (16 rows per tile).
-//  * k_gemm_bf16_256 (large M, K a multiple of 64): prefill and batched rounds.  256x128 macro
-//    tiles, three LDS stages filled by direct global -> LDS copies, 4 waves of 128x64 each built
-//    from 16x16x32 bf16 MFMAs.
+//  * k_gemm_bf16_256 (large M, K a multiple of 64; hyf_gemm.hip): prefill and batched rounds.
+//    256x128 macro tiles, three LDS stages filled by direct global -> LDS copies, 8 waves of 64x64
+//    each built from 16x16x32 bf16 MFMAs.
 //  * k_gemm_bf16 (large M, other K): 128x128 macro tiles, K step 64, register-staged
 //    double-buffered LDS, 4 waves of 64x64.
 #include <mutex>
