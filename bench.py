@@ -49,6 +49,9 @@ def parse():
     p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                    help="turn two rocprofv3 --pmc databases (FETCH_SIZE, WRITE_SIZE) of --pmc-probe runs "
                         "into profiles/pmc_traffic.json")
+    p.add_argument("--stats-summary", metavar="DIR",
+                   help="turn the csv output of a rocprofv3 --kernel-trace --stats run of --profile (output "
+                        "prefix 'bench') into profiles/qwen3_4b_episode_kernel_stats.md")
     return p.parse_args()
 
 
@@ -141,7 +144,29 @@ def time_calls(torch, fn, reps):
     return ms, ms
 
 
-def kernel_loops(torch, hf, I, ep, reps, with_gemm=True):
+def scan_y_loop(torch, hf, I, ep, reps, scan_in, sbytes, st, out):
+    """The commit scan with per-token outputs y (C in, y out), on the kernel loop's scan inputs."""
+    sh, cfg, T = ep.shape, ep.cfg, ep.T
+    nh, P = sh.n_heads, sh.head_dim
+    sc_c = I.make_scan_inputs(sh, T, I.rng_streams(101)[0], with_c=True, h0_scale=0.0)
+    CT = hf.to_device(hf.time_tiled(sc_c["C"], T, hf.elem_bytes(sh)), sh)
+    y = torch.empty((T, nh, P), dtype=torch.bfloat16, device="cuda")
+    wsy = hf.hyf_ssd_scan_workspace_bytes(cfg, T, 1)
+    wy = torch.empty(wsy, dtype=torch.uint8, device="cuda")
+
+    def scan_y(i):
+        c = scan_in[i % N_COPIES]
+        st[0] |= hf.hyf_ssd_scan(cfg, c["x"], c["B"], CT, c["dt"], ep.a_log, ep.dt_bias, ep.d_skip, c["H"],
+                                 y, T, wy, wsy)
+
+    scan_y(0)
+    mean_ms, med_ms = time_calls(torch, scan_y, max(4, reps // 4))
+    ybytes = sbytes + T * (sh.gn * 2 + nh * P * 2)
+    out["scan_y"] = dict(mean_us=mean_ms * 1e3, median_us=med_ms * 1e3, bytes=ybytes,
+                         gbs=ybytes / (mean_ms * 1e-3) / 1e9, feats_per_s=T / (mean_ms * 1e-3))
+
+
+def kernel_loops(torch, hf, I, ep, reps, with_gemm=True, with_y=True):
     sh = ep.shape
     d, nh, P, N = sh.d_model, sh.n_heads, sh.head_dim, sh.d_state
     cfg = ep.cfg
@@ -184,23 +209,8 @@ def kernel_loops(torch, hf, I, ep, reps, with_gemm=True):
                        gbs=sbytes / (mean_ms * 1e-3) / 1e9, feats_per_s=T / (mean_ms * 1e-3))
     if not with_gemm:
         return out
-    # 2b. the same scan with per-token outputs y (C in, y out)
-    sc_c = I.make_scan_inputs(sh, T, I.rng_streams(101)[0], with_c=True, h0_scale=0.0)
-    CT = hf.to_device(hf.time_tiled(sc_c["C"], T, hf.elem_bytes(sh)), sh)
-    y = torch.empty((T, nh, P), dtype=torch.bfloat16, device="cuda")
-    wsy = hf.hyf_ssd_scan_workspace_bytes(cfg, T, 1)
-    wy = torch.empty(wsy, dtype=torch.uint8, device="cuda")
-
-    def scan_y(i):
-        c = scan_in[i % N_COPIES]
-        st[0] |= hf.hyf_ssd_scan(cfg, c["x"], c["B"], CT, c["dt"], ep.a_log, ep.dt_bias, ep.d_skip, c["H"],
-                                 y, T, wy, wsy)
-
-    scan_y(0)
-    mean_ms, med_ms = time_calls(torch, scan_y, max(4, reps // 4))
-    ybytes = sbytes + T * (sh.gn * 2 + nh * P * 2)
-    out["scan_y"] = dict(mean_us=mean_ms * 1e3, median_us=med_ms * 1e3, bytes=ybytes,
-                         gbs=ybytes / (mean_ms * 1e-3) / 1e9, feats_per_s=T / (mean_ms * 1e-3))
+    if with_y:
+        scan_y_loop(torch, hf, I, ep, reps, scan_in, sbytes, st, out)
     # 3. prefill projection GEMM (v | B | dt columns over the whole prefix)
     nvbd = sh.dq + sh.gn + nh
     g = torch.empty((T, nvbd), dtype=torch.bfloat16, device="cuda")
@@ -212,7 +222,8 @@ def kernel_loops(torch, hf, I, ep, reps, with_gemm=True):
     gemm(0)
     mean_ms, med_ms = time_calls(torch, gemm, max(4, reps // 6))
     flops = 2.0 * T * d * nvbd
-    out["gemm"] = dict(mean_us=mean_ms * 1e3, median_us=med_ms * 1e3, flops=flops,
+    gbytes = (T * d + nvbd * d + T * nvbd) * 2  # rows, weights and outputs (bf16), each once
+    out["gemm"] = dict(mean_us=mean_ms * 1e3, median_us=med_ms * 1e3, flops=flops, bytes=gbytes,
                        tflops=flops / (mean_ms * 1e-3) / 1e12)
     if st[0]:
         raise RuntimeError("kernel loop call failed")
@@ -228,6 +239,7 @@ PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 PMC_KERNELS = {  # key -> (kernel name as it appears in the profile, mangled or not; source file)
     "proj": ("k_proj_stream", "hybrid_ssm_local_amd/csrc/hyf_proj.hip"),
     "scan": ("k_ssd_seg", "hybrid_ssm_local_amd/csrc/hyf_scan.hip"),
+    "gemm": ("k_gemm_bf16_256", "hybrid_ssm_local_amd/csrc/hyf_gemm.hip"),
 }
 
 
@@ -239,13 +251,13 @@ def source_digest(rel):
 
 
 def pmc_probe(torch, hf, I, reps=6):
-    """The W_in projection of a round, the 8192-token scan, and a copy of known size."""
+    """The W_in projection of a round, the 8192-token scan, the prefill GEMM and a copy of known size."""
     src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda").normal_()
     dst = torch.empty_like(src)
     for _ in range(3):
         dst.copy_(src)
     ep = Episode(torch, hf, I)
-    kernel_loops(torch, hf, I, ep, reps, with_gemm=False)
+    kernel_loops(torch, hf, I, ep, reps, with_gemm=True, with_y=False)
     torch.cuda.synchronize()
 
 
@@ -297,6 +309,53 @@ def pmc_summary(fetch_db, write_db):
     with open(PMC_FILE.replace(".json", ".md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print(json.dumps(out, indent=1))
+
+
+def stats_summary(d):
+    """Kernel statistics of a profiled --profile run: per kernel, per launch shape, and the launches
+    of the kernel loops (every dispatch after the episodes' last round kernel)."""
+    import csv
+
+    stats = list(csv.DictReader(open(os.path.join(d, "bench_kernel_stats.csv"))))
+    trace = list(csv.DictReader(open(os.path.join(d, "bench_kernel_trace.csv"))))
+    trace.sort(key=lambda r: int(r["Start_Timestamp"]))
+    dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    short = lambda n: n if len(n) <= 110 else n[:107] + "..."
+    lines = ["# Qwen3-4B-shaped drafter layer episode (8192-feature prefix commit + 256 rounds), bench.py --profile",
+             "", "Command (from the repository root, on one MI355X):", "", "```",
+             "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_bench -o bench -- "
+             "python3 bench.py --profile",
+             "python3 bench.py --stats-summary gpurun_out/prof_bench", "```", "",
+             "The run holds the Mamba-2 episode, the gated delta-rule episode, then bench.py's kernel loops.", "",
+             "rocprofv3 kernel statistics (durations in microseconds):", "",
+             "| kernel | calls | total us | average us | % |", "|---|---:|---:|---:|---:|"]
+    for r in stats:
+        lines.append(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e3:.1f} | "
+                     f"{float(r['AverageNs']) / 1e3:.3f} | {float(r['Percentage']):.2f} |")
+    shapes = {}
+    for r in trace:
+        key = (r["Kernel_Name"], int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]),
+               int(r["Workgroup_Size_X"]))
+        shapes.setdefault(key, []).append(dur(r))
+    lines += ["", "By launch shape (grid = threads in all dimensions; durations in microseconds):", "",
+              "| kernel | grid | workgroup | calls | average us |", "|---|---:|---:|---:|---:|"]
+    for (k, g, w), v in sorted(shapes.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{short(k)}` | {g} | {w} | {len(v)} | {sum(v) / len(v):.3f} |")
+    last_round = max((i for i, r in enumerate(trace) if "k_round" in r["Kernel_Name"]), default=-1)
+    loops = {}
+    for r in trace[last_round + 1:]:
+        key = (r["Kernel_Name"], int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]))
+        loops.setdefault(key, []).append(dur(r))
+    lines += ["", "Launches of bench.py's kernel loops (every dispatch after the episodes' last round kernel; "
+              "these are the launches its roofline figures time):", "",
+              "| kernel | grid | calls | average us | min us |", "|---|---:|---:|---:|---:|"]
+    for (k, g), v in loops.items():
+        if "hyf" in k:
+            lines.append(f"| `{short(k)}` | {g} | {len(v)} | {sum(v) / len(v):.3f} | {min(v):.3f} |")
+    out = os.path.join(ROOT, "profiles", "qwen3_4b_episode_kernel_stats.md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out)
 
 
 def pmc_traffic(key):
@@ -354,6 +413,9 @@ def main():
     args = parse()
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary)
+        return
+    if args.stats_summary:
+        stats_summary(args.stats_summary)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -479,7 +541,8 @@ def main():
                      "bytes_per_launch": proj["bytes"], "avg_us": proj["mean_us"]},
         "gemm_roofline": {"bound": "mfma", "achieved": gemm["tflops"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                           "frac": gemm["tflops"] / BF16_PEAK_TFLOPS,
-                          "kernel": "k_gemm_bf16_256: prefill projection 8192 x 2560 x 2720", "avg_us": gemm["mean_us"]},
+                          "kernel": "k_gemm_bf16_256: prefill projection 8192 x 2560 x 2720", "avg_us": gemm["mean_us"],
+                          "traffic": pmc_traffic("gemm"), "algorithmic_bytes": gemm["bytes"]},
         "gated_delta_rule": gdn,
         "cpu_baseline": cpu,
     }
