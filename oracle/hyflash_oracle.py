@@ -202,6 +202,41 @@ def gdn_sequential(x, B, alpha_raw, beta_raw, b_alpha, b_beta, H0, n_groups: int
     return H
 
 
+def gdn_chunked(x, B, alpha_raw, beta_raw, b_alpha, b_beta, H0, chunk: int, n_groups: int = 1):
+    """The gated delta rule over chunks of `chunk` tokens: the same H_T as gdn_sequential.
+
+    The pages print only the rule's name; this chunked form is derived from the rule above.  Within a
+    chunk (H0 the state before it, g = log a, G its running sum, gamma = exp(G)) the rule unrolls to
+        H_t = gamma_t H0 + sum_{s <= t} exp(G_t - G_s) u_s k_s^T,
+        u_t = b_t (x_t - gamma_t H0 k_t - sum_{s < t} exp(G_t - G_s) (k_s . k_t) u_s),
+    so with A the strictly lower part of b_t exp(G_t - G_s) (k_t . k_s), U = X - Y H0^T where
+    (I + A) X = diag(b) V and (I + A) Y = diag(b gamma) K, and the chunk ends at
+        H = gamma_last H0 + (X - Y H0^T)^T diag(exp(G_last - G_s)) K.
+    """
+    x = np.asarray(x, F64)
+    T, nh, P = x.shape
+    k = l2_normalize(per_head(B, nh, n_groups))                  # [T][nh][N]
+    a = sigmoid(np.asarray(alpha_raw, F64) + np.asarray(b_alpha, F64)[None, :])
+    b = sigmoid(np.asarray(beta_raw, F64) + np.asarray(b_beta, F64)[None, :])
+    H = np.array(H0, dtype=F64, copy=True)
+    for c0 in range(0, T, chunk):
+        c1 = min(c0 + chunk, T)
+        L = c1 - c0
+        for h in range(nh):
+            K = k[c0:c1, h]                                      # [L][N]
+            V = x[c0:c1, h]                                      # [L][P]
+            bb = b[c0:c1, h]
+            G = np.cumsum(np.log(a[c0:c1, h]))
+            decay = np.exp(np.minimum(G[:, None] - G[None, :], 0.0))
+            A = np.tril(bb[:, None] * decay * (K @ K.T), -1)
+            M = np.eye(L) + A
+            X = np.linalg.solve(M, bb[:, None] * V)
+            Y = np.linalg.solve(M, (bb * np.exp(G))[:, None] * K)
+            Kd = np.exp(G[-1] - G)[:, None] * K
+            H[h] = np.exp(G[-1]) * H[h] + (X - Y @ H[h].T).T @ Kd
+    return H
+
+
 # ----------------------------------------------------------------------------
 # the layer: projections, ring, attention, readout, output projection
 

@@ -481,3 +481,21 @@ def test_gdn_layer_commit_splits_and_reads_normalized_queries():
     att = O.block_attention(pr["q"], np.zeros((0, 2, 16)), np.zeros((0, 2, 16)), pr["k"], pr["v"])
     assert _rel(out, O.project(att.reshape(8, -1), w0["w_out"])) < 1e-12
     assert shape.n_in == 3 * 32 + 2 * 16 + 2 * 2 and shape.in_groups["beta"] == (shape.n_in - 2, shape.n_in)
+
+
+def test_gdn_chunked_equals_the_sequential_rule():
+    # The chunked form (per-chunk triangular solves, then one update per chunk) against the rule
+    # applied token by token, for chunk lengths from 1 to longer than the sequence, ragged tails,
+    # and gates from near-closed to near-open.
+    rng = np.random.default_rng(7)
+    T, nh, P, N = 37, 2, 3, 5
+    x = rng.standard_normal((T, nh, P))
+    B = rng.standard_normal((T, N))
+    ar = rng.standard_normal((T, nh)) * 3.0
+    br = rng.standard_normal((T, nh)) * 3.0
+    ba, bb = np.array([2.0, -1.0]), np.array([0.0, 1.5])
+    H0 = rng.standard_normal((nh, P, N))
+    ref = O.gdn_sequential(x, B, ar, br, ba, bb, H0)
+    for chunk in (1, 2, 4, 16, 64):
+        got = O.gdn_chunked(x, B, ar, br, ba, bb, H0, chunk)
+        assert np.max(np.abs(got - ref)) <= 1e-10 * max(1.0, np.max(np.abs(ref))), chunk
