@@ -174,7 +174,14 @@ WsCommit ws_commit(const Shape& s, int dtype, int32_t R, int64_t rows, bool with
   w.c = o;  // y-mode: C time-blocked: [nblk][gn][HYF_TBLK]
   if (with_y) o += align_up((uint64_t)nblk * s.gn * HYF_TBLK * esize(dtype));
   w.part = o;
-  o += align_up((uint64_t)segs * s.nh * s.P * s.N * 4);
+  uint64_t part_bytes = (uint64_t)segs * s.nh * s.P * s.N * 4;
+  if (s.gdn && gdn_chunked_supported(s, esize(dtype))) {
+    // per (chunk of GDN_CHUNK tokens, head) records of the chunked gated delta rule
+    const uint64_t chunks = (uint64_t)(rows / GDN_CHUNK + R + 1);
+    const uint64_t g = chunks * s.nh * (uint64_t)gdn_chunk_record_floats(s) * 4;
+    if (g > part_bytes) part_bytes = g;
+  }
+  o += align_up(part_bytes);
   w.lam = o;
   o += align_up((uint64_t)segs * s.nh * 4);
   w.end = o;
@@ -423,6 +430,13 @@ int hyf_memory_commit(const hyf_config* cfg, const hyf_weights* w, void* state_p
   sa.y = y_opt;
   sa.d_skip = w->d_skip;
   if (s.gdn) {
+    // chunk offsets of the chunked form (unused by the token-by-token kernel)
+    int32_t q = 0;
+    for (int i = 0; i < rt.n_req; ++i) {
+      rt.seg0[i] = q;
+      q += (int32_t)((rt.row0[i + 1] - rt.row0[i] + GDN_CHUNK - 1) / GDN_CHUNK);
+    }
+    rt.seg0[rt.n_req] = q;
     he = launch_gdn_commit(dt, s, sa, rt, hs);
   } else {
     int32_t max_segs = 0;

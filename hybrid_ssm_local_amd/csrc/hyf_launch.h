@@ -130,6 +130,12 @@ int round_tiles(const Shape& sh);
 // gates time-blocked in a.dt (alpha at feature h, beta at nh + h, block stride a.dblk); gate biases
 // in a.dt_bias (alpha) and a.a_log (beta); updates the state pool's H in place.
 bool gdn_supported(const Shape& sh);
+// The chunked form (chunks of 64 tokens: per-chunk solves, then a chain over chunks) runs when the
+// shape allows it; it then needs rt.seg0 to hold each request's first chunk and a.part to hold
+// gdn_chunk_record_floats(sh) floats per (chunk, head).
+bool gdn_chunked_supported(const Shape& sh, int esz);
+int64_t gdn_chunk_record_floats(const Shape& sh);
+constexpr int GDN_CHUNK = 64;
 hipError_t launch_gdn_commit(int dtype, const Shape& sh, const ScanArgs& a, const ReqTable& rt, hipStream_t s);
 hipError_t launch_round(int dtype, const Shape& sh, const RoundArgs& a, const ReqTable& rt, hipStream_t s);
 
