@@ -491,7 +491,7 @@ def main():
     gdn = {"prefill_commit_us": 1e3 * g_pre, "commit_feats_per_s": ep_g.T / (g_pre * 1e-3),
            "round_us": 1e3 * g_rnd / ep_g.R, "draft_blocks_per_s": ep_g.R / (g_rnd * 1e-3),
            "note": "eager steps of the same workload with memory = gated delta rule; the prefix commit runs "
-                   "the rule one token at a time"}
+                   "the chunked form (per-chunk solves, then one state update per 64-token chunk)"}
     del ep_g
 
     log("kernel loops")
