@@ -166,6 +166,38 @@ def scan_y_loop(torch, hf, I, ep, reps, scan_in, sbytes, st, out):
                          gbs=ybytes / (mean_ms * 1e-3) / 1e9, feats_per_s=T / (mean_ms * 1e-3))
 
 
+def scan_long_loop(torch, hf, I, ep, reps, st, out, T=131072):
+    """The state-only commit scan over a 131072-token prefix at the layer's shape (the long-context
+    prefill length), x, B, dt_raw ~ N(0, 1) drawn on the device from a fixed seed; two copies
+    (each larger than the last-level cache) alternate."""
+    sh, cfg = ep.shape, ep.cfg
+    nh, P, N = sh.n_heads, sh.head_dim, sh.d_state
+    nb = (T + 127) // 128
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(T)
+    copies = []
+    for _ in range(2):
+        copies.append(dict(
+            x=torch.randn(nb * nh * P * 128, generator=gen, device="cuda").to(torch.bfloat16),
+            B=torch.randn(nb * sh.gn * 128, generator=gen, device="cuda").to(torch.bfloat16),
+            dt=torch.randn(nb * nh * 128, generator=gen, device="cuda"),
+            H=torch.zeros((nh, P, N), device="cuda")))
+    wsb = hf.hyf_ssd_scan_workspace_bytes(cfg, T)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+
+    def scan(i):
+        c = copies[i % 2]
+        st[0] |= hf.hyf_ssd_scan(cfg, c["x"], c["B"], None, c["dt"], ep.a_log, ep.dt_bias, ep.d_skip, c["H"],
+                                 None, T, ws, wsb)
+
+    scan(0)
+    mean_ms, med_ms = time_calls(torch, scan, max(4, reps // 6))
+    sbytes = T * (nh * P * 2 + sh.gn * 2 + nh * 4) + 2 * nh * P * N * 4
+    out["scan_long"] = dict(T=T, mean_us=mean_ms * 1e3, median_us=med_ms * 1e3, bytes=sbytes,
+                            gbs=sbytes / (mean_ms * 1e-3) / 1e9, feats_per_s=T / (mean_ms * 1e-3))
+    del copies, ws
+
+
 def kernel_loops(torch, hf, I, ep, reps, with_gemm=True, with_y=True):
     sh = ep.shape
     d, nh, P, N = sh.d_model, sh.n_heads, sh.head_dim, sh.d_state
@@ -211,6 +243,7 @@ def kernel_loops(torch, hf, I, ep, reps, with_gemm=True, with_y=True):
         return out
     if with_y:
         scan_y_loop(torch, hf, I, ep, reps, scan_in, sbytes, st, out)
+        scan_long_loop(torch, hf, I, ep, reps, st, out)
     # 3. prefill projection GEMM (v | B | dt columns over the whole prefix)
     nvbd = sh.dq + sh.gn + nh
     g = torch.empty((T, nvbd), dtype=torch.bfloat16, device="cuda")
@@ -530,6 +563,12 @@ def main():
                         "roofline": {"bound": "hbm", "achieved": scan["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                      "frac": scan["gbs"] / HBM_PEAK_GBS, "traffic": pmc_traffic("scan"),
                                      "bytes_per_launch": scan["bytes"]}},
+        "commit_scan_long": {"value": kl["scan_long"]["feats_per_s"], "unit": "committed feats/s",
+                             "T": kl["scan_long"]["T"], "avg_us": kl["scan_long"]["mean_us"],
+                             "roofline": {"bound": "hbm", "achieved": kl["scan_long"]["gbs"], "peak": HBM_PEAK_GBS,
+                                          "unit": "GB/s", "frac": kl["scan_long"]["gbs"] / HBM_PEAK_GBS,
+                                          "traffic": None, "bytes_per_launch": kl["scan_long"]["bytes"]},
+                             "note": "the same scan over a 131072-token prefix at the same layer shape"},
         "commit_scan_y": {"value": kl["scan_y"]["feats_per_s"], "unit": "committed feats/s", "T": ep.T,
                           "avg_us": kl["scan_y"]["mean_us"],
                           "roofline": {"bound": "hbm", "achieved": kl["scan_y"]["gbs"], "peak": HBM_PEAK_GBS,
