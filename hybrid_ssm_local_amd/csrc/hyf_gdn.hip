@@ -385,17 +385,36 @@ __global__ void __launch_bounds__(256) k_gdn_chunk(Shape sh, ScanArgs a, ReqTabl
 
 // The chain: per (request, head, rows p0 .. p0 + 15 of H), chunk after chunk,
 //   S^T = H_rows Y^T (16 x GC),  Z^T = X^T - S^T,  H_rows <- gam_C H_rows + Z^T Kd   (16 x N),
-// on fp32 16x16x4 MFMAs.  Wave w computes S^T columns 16 w .. + 15 and H columns of tiles
-// w, w + 4, ... .  Y goes from the record straight into MFMA operand registers (one 16-byte load
-// per four k values, two chunks ahead); X rows, kd and the chunk's key tiles go to a ring of
-// GDN_ST LDS stages, GDN_ST - 1 chunks ahead.
+// on fp32 16x16x4 MFMAs, 8 waves (two per SIMD, so one wave's MFMAs cover the other's waits).
+// S^T: wave w computes token tile w % 4 over half the k range (w / 4) and leaves a partial in
+// LDS; H: wave w computes column tiles w, w + 8, ..., reading Z^T = X^T - S^T_0 - S^T_1 as its A
+// operand.  Y goes from the record straight into MFMA operand registers (one 16-byte load per four
+// k values, two chunks ahead); X rows, kd and the chunk's key tiles go to a ring of GDN_ST LDS
+// stages, GDN_ST - 1 chunks ahead.
 constexpr int GDN_ST = 4;
 constexpr int GDN_YMAX = 16;  // N / 16 at most (N <= 256)
+constexpr int GDN_CW = 8;     // waves of the chain
+
+// Wait until at most n vector-memory operations are outstanding, n rounded down to one of a few
+// immediates (waiting for more than needed is always correct).
+__device__ __forceinline__ void vm_wait_le(int n) {
+  if (n >= 32) vm_wait<32>();
+  else if (n >= 24) vm_wait<24>();
+  else if (n >= 16) vm_wait<16>();
+  else if (n >= 12) vm_wait<12>();
+  else if (n >= 8) vm_wait<8>();
+  else if (n >= 6) vm_wait<6>();
+  else if (n >= 4) vm_wait<4>();
+  else if (n >= 3) vm_wait<3>();
+  else if (n >= 2) vm_wait<2>();
+  else if (n >= 1) vm_wait<1>();
+  else vm_wait<0>();
+}
 
 template <typename T, int NQ>
-__global__ void __launch_bounds__(256) k_gdn_chain(Shape sh, ScanArgs a, ReqTable rt, int npb) {
+__global__ void __launch_bounds__(64 * GDN_CW) k_gdn_chain(Shape sh, ScanArgs a, ReqTable rt, int npb) {
   constexpr int VN = 16 / (int)sizeof(T), KT = 4 * VN;
-  constexpr int N = NQ * 16;
+  constexpr int N = NQ * 16, NQ2 = NQ / 2, NT = 64 * GDN_CW;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int nh = sh.nh, P = sh.P;
   const int pb = blockIdx.x % npb, h = (blockIdx.x / npb) % nh, r = blockIdx.x / (npb * nh);
@@ -406,68 +425,60 @@ __global__ void __launch_bounds__(256) k_gdn_chain(Shape sh, ScanArgs a, ReqTabl
   const int grp = h / (nh / sh.G);
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int ts = wave & 3, kh = wave >> 2;  // S^T token tile and k half of this wave
   const int i = lane & 15, g = lane >> 4;
-  constexpr int HP = N + 4;
+  constexpr int HP = N + 4, SP = GC + 4;
   const int64_t recf = gdn_rec_floats(N, P);
-  // LDS: H rows [16][HP] | Z^T [16][GC + 4] | GDN_ST stages of { X rows [GC][16] | kd [GC] + gam_C
-  // (4 spare) | key tiles }
+  // LDS: H rows [16][HP] | S^T partials [2][16][SP] | GDN_ST stages of { X rows [GC][16] | kd [GC] +
+  // gam_C (4 spare) | key tiles }
   float* Hs = reinterpret_cast<float*>(smem);
-  float* Zs = Hs + 16 * HP;
+  float* Sp = Hs + 16 * HP;
   constexpr int xbytes = GC * 16 * 4, kbytes = (GC + 4) * 4, bbytes = GC * N * (int)sizeof(T);
   constexpr int stage_bytes = xbytes + kbytes + bbytes;
-  char* stage0 = reinterpret_cast<char*>(Zs + 16 * (GC + 4));
+  char* stage0 = reinterpret_cast<char*>(Sp + 2 * 16 * SP);
   float* Hg = reinterpret_cast<float*>(a.state_pool + (int64_t)rt.slot[r] * sh.st_bytes + sh.st_h) +
               ((int64_t)h * P + p0) * N;
-  for (int idx = t; idx < 16 * N; idx += 256) Hs[(idx / N) * HP + idx % N] = Hg[idx];
+  for (int idx = t; idx < 16 * N; idx += NT) Hs[(idx / N) * HP + idx % N] = Hg[idx];
 
   auto rec_of = [&](int c) { return a.part + ((int64_t)(rt.seg0[r] + c) * nh + h) * recf; };
+  constexpr int NBC = N / 16 * (GC / KT) * 64;  // 16-byte chunks of a chunk's key tiles
   auto issue = [&](int c) {
     char* st = stage0 + (c % GDN_ST) * stage_bytes;
     const float* rec = rec_of(c);
-    lds_stage16<256>(GC * 4, st, [&](int k) { return rec + (int64_t)GC * N + (int64_t)(k >> 2) * P + p0 + 4 * (k & 3); });
-    lds_stage16<256>((GC + 4) / 4, st + xbytes, [&](int k) { return rec + (int64_t)GC * (N + P) + 4 * k; });
+    lds_stage16<NT>(GC * 4, st, [&](int k) { return rec + (int64_t)GC * N + (int64_t)(k >> 2) * P + p0 + 4 * (k & 3); });
+    lds_stage16<NT>((GC + 4) / 4, st + xbytes, [&](int k) { return rec + (int64_t)GC * (N + P) + 4 * k; });
     // key tiles of the chunk: tile (fg, jr) is 64 contiguous 16-byte chunks
     const int64_t t0 = (int64_t)c * GC;
     const T* bsrc = static_cast<const T*>(a.B) + (rt.blk0[r] + t0 / TB) * a.bblk;
     const int toff = (int)(t0 % TB);
-    lds_stage16<256>(N / 16 * (GC / KT) * 64, st + xbytes + kbytes, [&](int k) {
+    lds_stage16<NT>(NBC, st + xbytes + kbytes, [&](int k) {
       const int tile = k >> 6, fg = tile / (GC / KT), jr = tile % (GC / KT);
       return bsrc + tile_off<T>((int64_t)grp * N + 16 * fg, toff + jr * KT) + (k & 63) * VN;
     });
   };
-  // Y operands of wave w: rows 16 w .. + 15, lane (i, g) k values 4 j + g, j = 4 jq .. 4 jq + 3
-  auto load_y = [&](int c, f32x4 (&y)[NQ]) {
-    const f32x4* src = reinterpret_cast<const f32x4*>(rec_of(c)) + (int64_t)wave * NQ * 64 + lane;
+  // copies one stage costs this wave (lds_stage16 issues one per 64-chunk group it owns)
+  auto copies = [&](int n) { return n > 64 * wave ? (n - 64 * wave + NT - 1) / NT : 0; };
+  const int dw = copies(GC * 4) + copies((GC + 4) / 4) + copies(NBC);
+  // Y operands of wave w: rows 16 ts .. + 15, k values 16 jq + 4 jr + g for jq in its half
+  auto load_y = [&](int c, f32x4 (&y)[NQ2]) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(rec_of(c)) + ((int64_t)ts * NQ + kh * NQ2) * 64 + lane;
 #pragma unroll
-    for (int jq = 0; jq < NQ; ++jq) y[jq] = src[jq * 64];
+    for (int jq = 0; jq < NQ2; ++jq) y[jq] = src[jq * 64];
   };
-  // copies of the first GDN_ST - 1 stages, then the Y operands of the first two chunks
   for (int c = 0; c < GDN_ST - 1 && c < nc; ++c) issue(c);
-  f32x4 y0[NQ], y1[NQ], y2[NQ];
+  f32x4 y0[NQ2], y1[NQ2], y2[NQ2];
   load_y(0, y0);
   if (nc > 1) load_y(1, y1);
-  // Loads complete in order.  Iteration c needs stage c and Y of chunk c; the loads issued after
-  // them are those of iteration c - 1 (stage c + 2: DW copies, Y of chunk c + 1: NQ loads), or, at
-  // c = 0, Y of chunk 1.  DW = X rows (1) + kd (wave 0: 1) + key tiles (NQ 16 / KT).
-  constexpr int DW = 1 + NQ * 16 / KT;
   for (int c = 0; c < nc; ++c) {
-    if (c == 0) {
-      if (nc > 1)
-        vm_wait<NQ>();
-      else
-        vm_wait<0>();
-    } else if (c + 2 < nc) {
-      if (wave == 0)
-        vm_wait<DW + 1 + NQ>();
-      else
-        vm_wait<DW + NQ>();
-    } else if (c + 1 < nc) {
-      vm_wait<NQ>();
-    } else {
-      vm_wait<0>();
-    }
-    // stage c and Y of chunk c are in, H rows of the previous chunk are written; the barrier is
-    // the bare instruction (a __syncthreads() fence would wait for the loads still in flight)
+    // Loads complete in order.  Iteration c needs stage c and Y of chunk c; issued after them are
+    // the loads of iteration c - 1 (stage c + 2: dw copies, Y of chunk c + 1: NQ2 loads), or, at
+    // c = 0, Y of chunk 1.
+    if (c == 0)
+      vm_wait_le(nc > 1 ? NQ2 : 0);
+    else
+      vm_wait_le((c + 2 < nc ? dw : 0) + (c + 1 < nc ? NQ2 : 0));
+    // stage c and Y of chunk c are in, H rows of the previous chunk are written; the barrier is the
+    // bare instruction (a __syncthreads() fence would wait for the loads still in flight)
     lgkm_wait0();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -477,39 +488,35 @@ __global__ void __launch_bounds__(256) k_gdn_chain(Shape sh, ScanArgs a, ReqTabl
     const float* Xs = reinterpret_cast<const float*>(st);
     const float* kd = reinterpret_cast<const float*>(st + xbytes);
     const T* Bs = reinterpret_cast<const T*>(st + xbytes + kbytes);
-    // S^T tile: rows i of H, tokens 16 w + i (B operand: Y[16 w + i][4 j + g])
+    // partial S^T tile: rows i of H, tokens 16 ts + i, k values of half kh (four chains, one per jr)
     {
-      // four independent accumulation chains (one per jr), summed at the end
       f32x4 ac[4];
 #pragma unroll
       for (int jr = 0; jr < 4; ++jr) ac[jr] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int jq = 0; jq < NQ; ++jq)
+      for (int jq = 0; jq < NQ2; ++jq)
 #pragma unroll
         for (int jr = 0; jr < 4; ++jr)
-          ac[jr] = __builtin_amdgcn_mfma_f32_16x16x4f32(Hs[i * HP + 16 * jq + 4 * jr + g], y0[jq][jr], ac[jr], 0, 0, 0);
+          ac[jr] = __builtin_amdgcn_mfma_f32_16x16x4f32(Hs[i * HP + 16 * (kh * NQ2 + jq) + 4 * jr + g], y0[jq][jr],
+                                                       ac[jr], 0, 0, 0);
       const f32x4 acc = (ac[0] + ac[1]) + (ac[2] + ac[3]);
-      // lane holds S^T[4 g + rr][16 w + i]
-      const int s = 16 * wave + i;
+      // lane holds the partial of S^T[4 g + rr][16 ts + i]
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int row = 4 * g + rr;
-        Zs[row * (GC + 4) + s] = Xs[s * 16 + row] - acc[rr];
-      }
+      for (int rr = 0; rr < 4; ++rr) Sp[(kh * 16 + 4 * g + rr) * SP + 16 * ts + i] = acc[rr];
     }
     lgkm_wait0();
     __builtin_amdgcn_s_barrier();
-    // H columns 16 nt .. + 15: gam_C H + Z^T Kd (B operand: kd_s B[s][16 nt + i], s = 4 j + g; the
-    // keys past the request's end hold anything, so they are selected away, not multiplied by 0)
+    // H columns 16 nt .. + 15: gam_C H + Z^T Kd, A operand Z^T[i][s] = X[s][i] - S^T_0[i][s] -
+    // S^T_1[i][s], B operand kd_s B[s][16 nt + i] (s = 4 j + g; the keys past the request's end hold
+    // anything, so they are selected away, not multiplied by 0)
     const float gam = kd[GC];
     const int len = min(GC, n_r - c * GC);
-    // the wave's NQ / 4 column tiles, two accumulation chains each (even and odd j)
-    constexpr int TPW = (NQ + 3) / 4;
+    constexpr int TPW = (NQ + GDN_CW - 1) / GDN_CW;
     {
       f32x4 ae[TPW], ao[TPW];
 #pragma unroll
       for (int k = 0; k < TPW; ++k) {
-        const int nt = min(wave + 4 * k, NQ - 1);  // a wave past the last tile repeats it, unstored
+        const int nt = min(wave + GDN_CW * k, NQ - 1);  // a wave past the last tile repeats it, unstored
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) ae[k][rr] = gam * Hs[(4 * g + rr) * HP + 16 * nt + i];
         ao[k] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -517,11 +524,11 @@ __global__ void __launch_bounds__(256) k_gdn_chain(Shape sh, ScanArgs a, ReqTabl
 #pragma unroll
       for (int j = 0; j < GC / 4; ++j) {
         const int s = 4 * j + g;
-        const float z = Zs[i * (GC + 4) + s];
+        const float z = Xs[s * 16 + i] - Sp[i * SP + s] - Sp[(16 + i) * SP + s];
         const float ks = s < len ? kd[s] : 0.f;
 #pragma unroll
         for (int k = 0; k < TPW; ++k) {
-          const float bv = to_f32(Bs[chunk_tile_idx<T>(16 * min(wave + 4 * k, NQ - 1) + i, s)]);
+          const float bv = to_f32(Bs[chunk_tile_idx<T>(16 * min(wave + GDN_CW * k, NQ - 1) + i, s)]);
           const float b = s < len ? ks * bv : 0.f;
           if (j & 1)
             ao[k] = __builtin_amdgcn_mfma_f32_16x16x4f32(z, b, ao[k], 0, 0, 0);
@@ -529,9 +536,10 @@ __global__ void __launch_bounds__(256) k_gdn_chain(Shape sh, ScanArgs a, ReqTabl
             ae[k] = __builtin_amdgcn_mfma_f32_16x16x4f32(z, b, ae[k], 0, 0, 0);
         }
       }
+      // (every wave read all of H before the S^T barrier; after it a wave reads only its own tiles)
 #pragma unroll
       for (int k = 0; k < TPW; ++k) {
-        const int nt = wave + 4 * k;
+        const int nt = wave + GDN_CW * k;
         if (nt >= NQ) continue;
         const f32x4 acc = ae[k] + ao[k];
 #pragma unroll
@@ -539,13 +547,13 @@ __global__ void __launch_bounds__(256) k_gdn_chain(Shape sh, ScanArgs a, ReqTabl
       }
     }
 #pragma unroll
-    for (int jq = 0; jq < NQ; ++jq) {
+    for (int jq = 0; jq < NQ2; ++jq) {
       y0[jq] = y1[jq];
       y1[jq] = y2[jq];
     }
   }
   __syncthreads();
-  for (int idx = t; idx < 16 * N; idx += 256) Hg[idx] = Hs[(idx / N) * HP + idx % N];
+  for (int idx = t; idx < 16 * N; idx += NT) Hg[idx] = Hs[(idx / N) * HP + idx % N];
 }
 
 static size_t gdn_chunk_lds(const Shape& sh) {
@@ -553,7 +561,7 @@ static size_t gdn_chunk_lds(const Shape& sh) {
 }
 static size_t gdn_chain_lds(const Shape& sh, int esz) {
   const size_t stage = GC * 16 * 4 + (GC + 4) * 4 + (size_t)GC * sh.N * esz;
-  return sizeof(float) * (16 * (size_t)(sh.N + 4) + 16 * (GC + 4)) + GDN_ST * stage;
+  return sizeof(float) * (16 * (size_t)(sh.N + 4) + 2 * 16 * (GC + 4)) + GDN_ST * stage;
 }
 
 bool gdn_chunked_supported(const Shape& sh, int esz) {
@@ -591,14 +599,14 @@ static hipError_t launch_gdn_chunked_t(const Shape& sh, const ScanArgs& a, const
   const dim3 grid((unsigned)(rt.n_req * sh.nh * npb));
   const size_t lds = gdn_chain_lds(sh, sizeof(T));
   switch (sh.N / 16) {
-    case 2: hipLaunchKernelGGL((k_gdn_chain<T, 2>), grid, dim3(256), lds, s, sh, a, rt, npb); break;
-    case 4: hipLaunchKernelGGL((k_gdn_chain<T, 4>), grid, dim3(256), lds, s, sh, a, rt, npb); break;
-    case 6: hipLaunchKernelGGL((k_gdn_chain<T, 6>), grid, dim3(256), lds, s, sh, a, rt, npb); break;
-    case 8: hipLaunchKernelGGL((k_gdn_chain<T, 8>), grid, dim3(256), lds, s, sh, a, rt, npb); break;
-    case 10: hipLaunchKernelGGL((k_gdn_chain<T, 10>), grid, dim3(256), lds, s, sh, a, rt, npb); break;
-    case 12: hipLaunchKernelGGL((k_gdn_chain<T, 12>), grid, dim3(256), lds, s, sh, a, rt, npb); break;
-    case 14: hipLaunchKernelGGL((k_gdn_chain<T, 14>), grid, dim3(256), lds, s, sh, a, rt, npb); break;
-    default: hipLaunchKernelGGL((k_gdn_chain<T, 16>), grid, dim3(256), lds, s, sh, a, rt, npb); break;
+    case 2: hipLaunchKernelGGL((k_gdn_chain<T, 2>), grid, dim3(64 * GDN_CW), lds, s, sh, a, rt, npb); break;
+    case 4: hipLaunchKernelGGL((k_gdn_chain<T, 4>), grid, dim3(64 * GDN_CW), lds, s, sh, a, rt, npb); break;
+    case 6: hipLaunchKernelGGL((k_gdn_chain<T, 6>), grid, dim3(64 * GDN_CW), lds, s, sh, a, rt, npb); break;
+    case 8: hipLaunchKernelGGL((k_gdn_chain<T, 8>), grid, dim3(64 * GDN_CW), lds, s, sh, a, rt, npb); break;
+    case 10: hipLaunchKernelGGL((k_gdn_chain<T, 10>), grid, dim3(64 * GDN_CW), lds, s, sh, a, rt, npb); break;
+    case 12: hipLaunchKernelGGL((k_gdn_chain<T, 12>), grid, dim3(64 * GDN_CW), lds, s, sh, a, rt, npb); break;
+    case 14: hipLaunchKernelGGL((k_gdn_chain<T, 14>), grid, dim3(64 * GDN_CW), lds, s, sh, a, rt, npb); break;
+    default: hipLaunchKernelGGL((k_gdn_chain<T, 16>), grid, dim3(64 * GDN_CW), lds, s, sh, a, rt, npb); break;
   }
   return hipGetLastError();
 }
