@@ -368,16 +368,24 @@ __global__ void __launch_bounds__(256) k_gdn_chunk(Shape sh, ScanArgs a, ReqTabl
 #pragma unroll
       for (int tt = 0; tt < 16; ++tt) colp[(16 * b + tt) * pitch] = acc[tt];
     }
-    if (isy) {
-      // Y in the chain's MFMA operand order: element (s, n) at ((s / 16) (N / 16) + n / 16) 256 +
-      // (s % 16 + 16 (n % 4)) 4 + (n % 16) / 4, so a lane's four k values are one 16-byte load
-      const int jq = col >> 4, g4 = col & 3, jr = (col >> 2) & 3;
-      for (int u = 0; u < GC; ++u)
-        rec[(((u >> 4) * (N >> 4) + jq) * 64 + (u & 15) + 16 * g4) * 4 + jr] = colp[u * pitch];
-    } else {
-      float* dst = rec + (int64_t)GC * N + (col - N);
-      for (int u = 0; u < GC; ++u) dst[(int64_t)u * P] = colp[u * pitch];
-    }
+  }
+  __syncthreads();
+  // the solved columns to the record in 16-byte stores: Y in the chain's MFMA operand order (element
+  // (s, n) at ((s / 16) (N / 16) + n / 16) 256 + (s % 16 + 16 (n % 4)) 4 + (n % 16) / 4, so a chain
+  // lane's four k values are one 16-byte load), X row-major
+  for (int q4 = t; q4 < GC * N / 4; q4 += 256) {
+    const int lf = q4 & 63, bq = q4 >> 6;
+    const int sidx = (bq / (N >> 4)) * 16 + (lf & 15);
+    const int n0 = (bq % (N >> 4)) * 16 + (lf >> 4);
+    f32x4 v;
+#pragma unroll
+    for (int jr = 0; jr < 4; ++jr) v[jr] = Kt[sidx * KP + n0 + 4 * jr];
+    *reinterpret_cast<f32x4*>(rec + 4 * (int64_t)q4) = v;
+  }
+  for (int q4 = t; q4 < GC * P / 4; q4 += 256) {
+    const int sidx = q4 / (P / 4), c4 = q4 % (P / 4);
+    *reinterpret_cast<f32x4*>(rec + (int64_t)GC * N + (int64_t)sidx * P + 4 * c4) =
+        *reinterpret_cast<const f32x4*>(Vt + sidx * VP + 4 * c4);
   }
   if (t < GC) rec[(int64_t)GC * (N + P) + t] = t < len ? __expf(Gs[GC - 1] - Gs[t]) * iv[t] : 0.f;
   if (t == 0) rec[(int64_t)GC * (N + P) + GC] = __expf(Gs[GC - 1]);
