@@ -239,7 +239,10 @@ __global__ void __launch_bounds__(256) k_gdn_chunk(Shape sh, ScanArgs a, ReqTabl
       const int c = min(c0 + k * 256 + t, n16 - 1);
       const bool isb = c < N * (GC / VN);
       const int cc = isb ? c : c - N * (GC / VN);
-      const int f = cc / (GC / VN), tv = (cc % (GC / VN)) * VN;  // feature, first token
+      const int nf = isb ? N : P;
+      // feature, first token: consecutive threads take consecutive features (contiguous chunks of a
+      // tile, and different LDS banks when spread token-major)
+      const int f = cc % nf, tv = (cc / nf) * VN;
       vv[k] = isb ? *reinterpret_cast<const V*>(bb + tile_off<T>((int64_t)grp * N + f, toff + tv))
                   : *reinterpret_cast<const V*>(xb + tile_off<T>((int64_t)h * P + f, toff + tv));
     }
@@ -249,7 +252,8 @@ __global__ void __launch_bounds__(256) k_gdn_chunk(Shape sh, ScanArgs a, ReqTabl
       if (c >= n16) continue;
       const bool isb = c < N * (GC / VN);
       const int cc = isb ? c : c - N * (GC / VN);
-      const int f = cc / (GC / VN), tv = (cc % (GC / VN)) * VN;
+      const int nf = isb ? N : P;
+      const int f = cc % nf, tv = (cc / nf) * VN;
 #pragma unroll
       for (int e = 0; e < VN; ++e) {
         const float x = tv + e < len ? to_f32(vv[k][e]) : 0.f;
