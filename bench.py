@@ -243,7 +243,6 @@ def kernel_loops(torch, hf, I, ep, reps, with_gemm=True, with_y=True):
         return out
     if with_y:
         scan_y_loop(torch, hf, I, ep, reps, scan_in, sbytes, st, out)
-        scan_long_loop(torch, hf, I, ep, reps, st, out)
     # 3. prefill projection GEMM (v | B | dt columns over the whole prefix)
     nvbd = sh.dq + sh.gn + nh
     g = torch.empty((T, nvbd), dtype=torch.bfloat16, device="cuda")
@@ -258,6 +257,9 @@ def kernel_loops(torch, hf, I, ep, reps, with_gemm=True, with_y=True):
     gbytes = (T * d + nvbd * d + T * nvbd) * 2  # rows, weights and outputs (bf16), each once
     out["gemm"] = dict(mean_us=mean_ms * 1e3, median_us=med_ms * 1e3, flops=flops, bytes=gbytes,
                        tflops=flops / (mean_ms * 1e-3) / 1e12)
+    if with_y:
+        # last: its two 0.7 GB input copies are the largest allocation of the run
+        scan_long_loop(torch, hf, I, ep, reps, st, out)
     if st[0]:
         raise RuntimeError("kernel loop call failed")
     return out
@@ -375,16 +377,25 @@ def stats_summary(d):
     for (k, g, w), v in sorted(shapes.items(), key=lambda kv: -sum(kv[1])):
         lines.append(f"| `{short(k)}` | {g} | {w} | {len(v)} | {sum(v) / len(v):.3f} |")
     last_round = max((i for i, r in enumerate(trace) if "k_round" in r["Kernel_Name"]), default=-1)
+    # the kernel loops run, in order: the round's input projection, the 8192-token scan, the y-mode
+    # scan (k_ssd_y), the prefill GEMM, then the 131072-token scan (after the GEMM)
     loops = {}
+    seen_gemm = False
     for r in trace[last_round + 1:]:
-        key = (r["Kernel_Name"], int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]))
+        k = r["Kernel_Name"]
+        seen_gemm |= "k_gemm_bf16_256" in k
+        if "k_ssd_seg" in k or "k_ssd_combine" in k:
+            k = k + (" [131072-token scan]" if seen_gemm else "")
+        key = (k, int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]))
         loops.setdefault(key, []).append(dur(r))
     lines += ["", "Launches of bench.py's kernel loops (every dispatch after the episodes' last round kernel; "
               "these are the launches its roofline figures time):", "",
               "| kernel | grid | calls | average us | min us |", "|---|---:|---:|---:|---:|"]
     for (k, g), v in loops.items():
         if "hyf" in k:
-            lines.append(f"| `{short(k)}` | {g} | {len(v)} | {sum(v) / len(v):.3f} | {min(v):.3f} |")
+            tag = " [131072-token scan]"
+            name = f"`{short(k[:-len(tag)])}`{tag}" if k.endswith(tag) else f"`{short(k)}`"
+            lines.append(f"| {name} | {g} | {len(v)} | {sum(v) / len(v):.3f} | {min(v):.3f} |")
     out = os.path.join(ROOT, "profiles", "qwen3_4b_episode_kernel_stats.md")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
