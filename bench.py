@@ -144,6 +144,70 @@ def time_calls(torch, fn, reps):
     return ms, ms
 
 
+def batched_serving(torch, hf, I, rounds=16):
+    """Batched serving on one GPU at the Qwen3-4B layer shape: 64 requests with prefixes of
+    U{2048..16384} committed features (per-request states and rings in one pool), then rounds in
+    which every request commits 1-8 accepted features and drafts its block, all 64 in one call.
+    Weights Xavier-normal from the workload's seed; features ~ N(0, 1)/sqrt(d) drawn on the device
+    from a fixed seed (about 0.6 M prefix rows do not fit a quick host draw)."""
+    import numpy as np
+
+    wl = I.WORKLOADS["qwen3_4b_batched64"]
+    sh, R = wl["shape"], wl["requests"]
+    d, nh, P, N, W = sh.d_model, sh.n_heads, sh.head_dim, sh.d_state, sh.window
+    rng = I.rng_streams(wl["seed"])
+    w = I.make_weights(sh, rng[0])
+    lo, hi = wl["prefix_range"]
+    lens = rng[1].integers(lo, hi + 1, size=R)
+    acc = rng[4].integers(1, 9, size=(rounds, R))
+    cfg = hf.make_config(sh)
+    w_in, w_out = hf.to_device(w["w_in"], sh), hf.to_device(w["w_out"], sh)
+    a_log = hf.to_device(w["a_log"], sh, storage=False)
+    dt_bias = hf.to_device(w["dt_bias"], sh, storage=False)
+    d_skip = hf.to_device(w["d_skip"], sh, storage=False)
+    wts = hf.HyfWeights(w_in.data_ptr(), w_out.data_ptr(), a_log.data_ptr(), dt_bias.data_ptr(), d_skip.data_ptr())
+    T = int(lens.sum())
+    pool = torch.zeros(R * hf.hyf_state_bytes(cfg), dtype=torch.uint8, device="cuda")
+    wsb = hf.hyf_workspace_bytes(cfg, R, T)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(wl["seed"])
+    scale = wl["feat_scale"]
+    prefix = (torch.randn(T, d, generator=gen, device="cuda") * scale).to(torch.bfloat16)
+    commits = (torch.randn(int(acc.sum()), d, generator=gen, device="cuda") * scale).to(torch.bfloat16)
+    blocks = (torch.randn(rounds, R * 8, d, generator=gen, device="cuda") * wl["block_scale"]).to(torch.bfloat16)
+    out = torch.empty(R * 8, d, dtype=torch.bfloat16, device="cuda")
+    cu_pre = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    st = hf.hyf_state_reset(cfg, pool, R, None, R)
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    e[0].record()
+    st |= hf.hyf_memory_commit(cfg, wts, pool, R, None, R, prefix, cu_pre, None, ws, wsb)
+    e[1].record()
+    off = 0
+    for i in range(rounds):
+        cu = np.concatenate([[0], np.cumsum(acc[i])]).astype(np.int64)
+        cptr = commits.data_ptr() + off * d * 2
+        off += int(acc[i].sum())
+        st |= hf.hyf_draft_block(cfg, wts, pool, R, None, R, cptr, cu, blocks[i], out, ws, wsb)
+    e[2].record()
+    torch.cuda.synchronize()
+    if st:
+        raise RuntimeError(f"batched serving call failed (status bits {st})")
+    pre_ms, rnd_ms = e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])
+    round_us = 1e3 * rnd_ms / rounds
+    # bytes of one round, each counted once: the full windows (K and V), H read and written, the
+    # weights, the committed and block rows in, the block rows out
+    a_mean = float(acc.mean())
+    rbytes = (R * nh * W * P * 2 * 2 + 2 * R * nh * P * N * 4 + (sh.n_in + d) * d * 2
+              + R * (a_mean + 8) * d * 2 + R * 8 * d * 2)
+    return {"requests": R, "prefix_rows": T, "rounds": rounds, "prefill_commit_us": 1e3 * pre_ms,
+            "round_us": round_us, "draft_blocks_per_s": R * rounds / (rnd_ms * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": rbytes / (round_us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": rbytes / (round_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                         "bytes_per_round": rbytes},
+            "note": "eager rounds, 64 requests per call; blocks/s counts every request's block"}
+
+
 def scan_y_loop(torch, hf, I, ep, reps, scan_in, sbytes, st, out):
     """The commit scan with per-token outputs y (C in, y out), on the kernel loop's scan inputs."""
     sh, cfg, T = ep.shape, ep.cfg, ep.T
@@ -538,6 +602,9 @@ def main():
                    "the chunked form (per-chunk solves, then one state update per 64-token chunk)"}
     del ep_g
 
+    log("batched serving")
+    batched = batched_serving(torch, hf, I)
+    torch.cuda.empty_cache()
     log("kernel loops")
     kl = kernel_loops(torch, hf, I, ep, args.kernel_reps)
     cpu = None if args.no_cpu else cpu_baseline(I, ep)
@@ -594,6 +661,7 @@ def main():
                           "kernel": "k_gemm_bf16_256: prefill projection 8192 x 2560 x 2720", "avg_us": gemm["mean_us"],
                           "traffic": pmc_traffic("gemm"), "algorithmic_bytes": gemm["bytes"]},
         "gated_delta_rule": gdn,
+        "batched_serving": batched,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
