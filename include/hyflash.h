@@ -141,7 +141,10 @@ int hyf_state_reset(const hyf_config* cfg, void* state_pool, int32_t pool_slots,
  * Any row count works (a prefill of a whole prefix, or the 1-8 rows of a round).
  * cu_rows (host): int64 [n_req + 1], cu_rows[0] = 0, non-decreasing.  Empty requests
  * are left bit-identical.
- * With memory = HYF_MEM_GDN the fold is the gated delta rule of hyf_weights, row by row.
+ * With memory = HYF_MEM_GDN the fold is the gated delta rule of hyf_weights, the same result as
+ * row by row (computed, for more than 16 rows, in chunks of 64 tokens: per-chunk triangular
+ * solves, then one state update per chunk; the workspace then holds (N + P + 1) * 64 + 4 floats
+ * per chunk and head, which hyf_workspace_bytes includes); y_opt is HYF_EUNSUPPORTED.
  * y_opt (nullable, 16-byte aligned): [cu_rows[n_req]][nh][P] storage dtype, per-token memory
  * outputs y_t = H_t . C_t + D * v_t (H_t after token t, C_t from w_in); HYF_EUNSUPPORTED when a
  * 128-token block of x, B and C does not fit one workgroup's LDS (fp32 with P + 2N > 320).
