@@ -406,7 +406,8 @@ __device__ __forceinline__ void round_attn(const Shape& sh, const RoundArgs& a, 
 // with the (max, sum) pairs and the readout (one round trip); per (split, row) factors
 // exp(max_s - max) are formed once, in parallel, then every output sums its splits.
 // Merge LDS (bytes): (max, sum) [ns][RB][2] | factors [ns][RB] | row maxima and sums [2 RB] |
-// readout [RB][P] | partials [MCH][RB][P].
+// readout [RB][P] | partials [min(MCH, ns)][RB][P] (sized for the splits there are: with 9 splits
+// the kernel's LDS stays at the attention's 34 KiB, four workgroups per CU instead of three).
 constexpr int MCH = 16;
 template <typename T>
 __device__ __forceinline__ void round_merge(const Shape& sh, const RoundArgs& a, int r, int h, char* smem) {
@@ -556,7 +557,7 @@ size_t round_lds_bytes(const Shape& sh, int esz, int n_split) {
                       4 * (3 * RMAXC + 4 + RB + RB * RT);
   const size_t attn = (size_t)2 * up1k(ATT_KS * sh.P * esz) + 3 * up1k(RB * sh.P * 4) + 4 * (16 * ATT_KS + 128);
   const size_t merge = n_split ? (size_t)up1k(n_split * RB * 2 * 4) + up1k(n_split * RB * 4) + 4 * 256 +
-                                     up1k(RB * sh.P * 4) + up1k(MCH * RB * sh.P * 4)
+                                     up1k(RB * sh.P * 4) + up1k((n_split < MCH ? n_split : MCH) * RB * sh.P * 4)
                                : 0;
   size_t m = tile > attn ? tile : attn;
   return m > merge ? m : merge;
