@@ -361,6 +361,23 @@ def test_gated_delta_rule_rounds_match_the_oracle(name, shape):
     pr.check_state(what=f"gdn {name} small commit")
 
 
+def test_gated_delta_rule_chunk_edges_in_one_call():
+    # The chunked prefix commit over requests whose lengths sit on and around its 64-token chunks
+    # and 128-token blocks (one call, eight requests), then a second prefill on top of each state.
+    shape = small_shape("bf16", window=40, memory="gdn")
+    lens = [17, 63, 64, 65, 127, 128, 129, 200]
+    pr = Pair(shape, seed=73, pool_slots=8, max_requests=8, max_rows=2 * sum(lens))
+    pr.gpu.reset()
+    say("gdn chunk edges prefill", lens)
+    pr.commit([pr.rows(n) for n in lens])
+    for i in range(8):
+        pr.check_state(slot=i, what=f"gdn chunk edges request {i} ({lens[i]} rows)")
+    say("gdn chunk edges second prefill")
+    pr.commit([pr.rows(n) for n in reversed(lens)])
+    for i in range(8):
+        pr.check_state(slot=i, what=f"gdn chunk edges request {i} second prefill")
+
+
 def test_gated_delta_rule_qwen_prefill_batched_and_rounds():
     # Qwen-shaped gated delta-rule layer: two requests with ragged prefixes (one of them spans
     # several time blocks), then rounds over both
