@@ -378,6 +378,26 @@ def test_gated_delta_rule_chunk_edges_in_one_call():
         pr.check_state(slot=i, what=f"gdn chunk edges request {i} second prefill")
 
 
+def test_gated_delta_rule_rounds_of_sixteen_requests():
+    # Sixteen Qwen-shaped requests with ragged chunked prefixes, then rounds in which every request
+    # commits its own number of accepted rows (512 (request, head) pairs per round kernel).
+    shape = I.QWEN.replace(memory="gdn")
+    R = 16
+    pr = Pair(shape, seed=74, pool_slots=R, max_requests=R, max_rows=64 * R)
+    pr.gpu.reset()
+    lens = [17 + 3 * i for i in range(R)]
+    say("gdn sixteen requests prefill", lens)
+    pr.commit([pr.rows(n) for n in lens])
+    acc_rng = pr.rng[4]
+    for rnd in range(2):
+        acc = [int(a) for a in acc_rng.integers(1, 9, size=R)]
+        say("gdn sixteen requests round", rnd, acc)
+        g, o = pr.draft([pr.rows(8, 3) for _ in range(R)], commits=[pr.rows(a) for a in acc])
+        assert_close(g, o, "bf16", f"gdn sixteen requests round {rnd}")
+    for i in (0, 7, 15):
+        pr.check_state(slot=i, what=f"gdn sixteen requests state {i}")
+
+
 def test_gated_delta_rule_qwen_prefill_batched_and_rounds():
     # Qwen-shaped gated delta-rule layer: two requests with ragged prefixes (one of them spans
     # several time blocks), then rounds over both
