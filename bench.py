@@ -396,9 +396,9 @@ def pmc_summary(fetch_db, write_db):
         json.dump(out, f, indent=1)
     lines = ["# HBM traffic of the measured kernels (rocprofv3 counters)", "",
              "Commands (repository root, one MI355X; each counter in a run of its own):", "", "```",
-             "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc/f -o f -- python3 bench.py --pmc-probe",
-             "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc/w -o w -- python3 bench.py --pmc-probe",
-             "python3 bench.py --pmc-summary gpurun_out/pmc/f/f_results.db gpurun_out/pmc/w/w_results.db", "```", "",
+             "rocprofv3 --pmc FETCH_SIZE -d out/pmc/f -o f -- python3 bench.py --pmc-probe",
+             "rocprofv3 --pmc WRITE_SIZE -d out/pmc/w -o w -- python3 bench.py --pmc-probe",
+             "python3 bench.py --pmc-summary out/pmc/f/f_results.db out/pmc/w/w_results.db", "```", "",
              f"Calibration: a device copy of {COPY_BYTES >> 20} MiB reads FETCH_SIZE {copy_f:.0f} KiB and "
              f"WRITE_SIZE {copy_w:.0f} KiB, so measured KiB are scaled by {scale_f:.3f} (fetch) and "
              f"{scale_w:.3f} (write).", "",
@@ -422,9 +422,9 @@ def stats_summary(d):
     short = lambda n: n if len(n) <= 110 else n[:107] + "..."
     lines = ["# Qwen3-4B-shaped drafter layer episode (8192-feature prefix commit + 256 rounds), bench.py --profile",
              "", "Command (from the repository root, on one MI355X):", "", "```",
-             "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_bench -o bench -- "
+             "rocprofv3 --kernel-trace --stats --output-format csv -d out/prof_bench -o bench -- "
              "python3 bench.py --profile",
-             "python3 bench.py --stats-summary gpurun_out/prof_bench", "```", "",
+             "python3 bench.py --stats-summary out/prof_bench", "```", "",
              "The run holds the Mamba-2 episode, the gated delta-rule episode, then bench.py's kernel loops.", "",
              "rocprofv3 kernel statistics (durations in microseconds):", "",
              "| kernel | calls | total us | average us | % |", "|---|---:|---:|---:|---:|"]
@@ -527,7 +527,7 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
         sys.exit(2)
     if args.profile:

@@ -52,7 +52,7 @@ typedef enum {
   HYF_ECAPACITY = 3,    /* too many requests or rows, slot outside the pool          */
   HYF_EDTYPE = 4,       /* unknown dtype                                             */
   HYF_EWORKSPACE = 5,   /* ws_bytes smaller than the size the matching query returns */
-  HYF_EUNSUPPORTED = 6, /* a mode this build does not implement                      */
+  HYF_EUNSUPPORTED = 6, /* a mode the library does not implement                     */
   HYF_EHIP = 7          /* a HIP launch failed                                       */
 } hyf_status;
 
@@ -108,7 +108,7 @@ typedef struct {
 int hyf_abi_version(void);
 const char* hyf_status_str(int status);
 
-/* Host only.  HYF_OK if cfg describes a shape this build runs. */
+/* Host only.  HYF_OK if cfg describes a shape the library runs. */
 int hyf_config_check(const hyf_config* cfg);
 
 /* Host only.  Size of the input projection's output (n_in above); 0 on a bad cfg. */
