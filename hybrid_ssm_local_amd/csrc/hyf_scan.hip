@@ -385,7 +385,7 @@ __global__ void __launch_bounds__(256) k_ssd_prefix(Shape sh, ScanArgs a, ReqTab
 //   the state term sum_n C[t][n] H0[p][n] with H0 read from global memory, four columns a load.
 // Wave w takes the output row tiles w and 7 - w (the causal sums then cost each wave the same).
 template <typename T, int MAXT>
-__global__ void __launch_bounds__(256) k_ssd_y(Shape sh, ScanArgs a, ReqTable rt) {
+__global__ void __launch_bounds__(256) k_ssd_y(Shape sh, ScanArgs a, ReqTable rt, int h0_lds) {
   constexpr int VN = Vec16<T>::n;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int nh = sh.nh, P = sh.P, N = sh.N;
@@ -415,6 +415,16 @@ __global__ void __launch_bounds__(256) k_ssd_y(Shape sh, ScanArgs a, ReqTable rt
   lds_stage16<256>(N * TB / VN, bs, [&](int i) { return gb + (int64_t)i * VN; });
   lds_stage16<256>(N * TB / VN, cs, [&](int i) { return gc + (int64_t)i * VN; });
   lds_stage16<256>(TB / 4, dts, [&](int i) { return gd + 4 * i; });
+  // the state before the block, when it fits: [P][N] fp32, 16-byte chunk c of row p at position
+  // c ^ (p & 7) (the 16 rows of an MFMA operand load fall in 8 different bank groups)
+  float* h0s = cum + TB;
+  const float* H0 = a.part + ((int64_t)q * nh + h) * P * N;  // state before the block
+  const int cpr = N / 4;
+  if (h0_lds)
+    lds_stage16<256>(P * cpr, h0s, [&](int i) {
+      const int p = i / cpr, pc = i % cpr;
+      return H0 + (int64_t)p * N + 4 * (pc ^ (p & 7));
+    });
   vm_wait<0>();
   __syncthreads();
   if (wave == 0) {
@@ -440,7 +450,6 @@ __global__ void __launch_bounds__(256) k_ssd_y(Shape sh, ScanArgs a, ReqTable rt
 
   const int ntp = P / 16;
   const float D = a.d_skip[h];
-  const float* H0 = a.part + ((int64_t)q * nh + h) * P * N;  // state before the block
   T* yout = static_cast<T*>(a.y) + ((int64_t)rt.row0[r] + s_begin) * nh * P + (int64_t)h * P;
   for (int pass = 0; pass < 2; ++pass) {
     const int tt = pass ? TB / 16 - 1 - wave : wave;
@@ -500,7 +509,9 @@ __global__ void __launch_bounds__(256) k_ssd_y(Shape sh, ScanArgs a, ReqTable rt
 #pragma unroll
       for (int pt = 0; pt < MAXT; ++pt) {
         if (pt < ntp) {
-          const f32x4 hv = *reinterpret_cast<const f32x4*>(H0 + (int64_t)(16 * pt + li) * N + n0 + 4 * lg);
+          const int p = 16 * pt + li;
+          const f32x4 hv = h0_lds ? *reinterpret_cast<const f32x4*>(h0s + p * N + 4 * (((n0 >> 2) + lg) ^ (li & 7)))
+                                  : *reinterpret_cast<const f32x4*>(H0 + (int64_t)p * N + n0 + 4 * lg);
 #pragma unroll
           for (int j = 0; j < 4; ++j) yi[pt] = Mfma16<float>::mma(cv[j], hv[j], yi[pt]);
         }
@@ -617,7 +628,11 @@ static hipError_t launch_seg(const Shape& sh, const ScanArgs& a, const ReqTable&
 
 template <typename T, int MAXT>
 static hipError_t launch_y_t(const Shape& sh, const ScanArgs& a, const ReqTable& rt, hipStream_t s) {
-  const size_t lds = (size_t)TB * (sh.P + 2 * sh.N) * sizeof(T) + 2 * TB * sizeof(float);
+  size_t lds = (size_t)TB * (sh.P + 2 * sh.N) * sizeof(T) + 2 * TB * sizeof(float);
+  // the block's starting state goes to LDS too when it fits (N a multiple of 32 for its swizzle)
+  const size_t h0b = (size_t)sh.P * sh.N * sizeof(float);
+  const int h0_lds = sh.N % 32 == 0 && lds + h0b <= 160 * 1024 - 256 ? 1 : 0;
+  if (h0_lds) lds += h0b;
   static std::once_flag once;
   static hipError_t set_err = hipSuccess;
   std::call_once(once, [] {
@@ -625,7 +640,7 @@ static hipError_t launch_y_t(const Shape& sh, const ScanArgs& a, const ReqTable&
                                   hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 256);
   });
   if (set_err != hipSuccess) return set_err;
-  hipLaunchKernelGGL((k_ssd_y<T, MAXT>), dim3(a.total_segs * sh.nh), dim3(256), lds, s, sh, a, rt);
+  hipLaunchKernelGGL((k_ssd_y<T, MAXT>), dim3(a.total_segs * sh.nh), dim3(256), lds, s, sh, a, rt, h0_lds);
   return hipGetLastError();
 }
 
