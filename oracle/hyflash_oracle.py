@@ -37,6 +37,9 @@ notes of the repository):
 * Ring slot of committed row c (0-based over the request's life) is c mod W.
 * Stored values (ring K/V) are rounded to the storage dtype; everything else
   stays float64.
+* 4-bit weights (the pages name GPTQ, no format): group-wise symmetric
+  round-to-nearest, 128 k per group, scale max|w|/7 in float32, two codes per
+  byte (lower k in the low nibble); see quantize_w4.
 
 Parity is pinned for every function below by tests that compare against
 closed forms, library routines or brute force (see tests/test_oracle_pins.py).
@@ -372,3 +375,52 @@ def draft_two_layer(shape, wts1: dict, wts2: dict, st1: dict, st2: dict, block_i
     o1 = draft(shape, wts1, st1, block_in)
     x2 = np.asarray(block_in, F64) + round_storage(o1, shape.dtype)
     return o1, draft(shape, wts2, st2, x2)
+
+
+# ---------------------------------------------------------------------------------------------
+# Weight-only 4-bit projections (paper page, Figures & tables: the BF16 vs INT4 speedup table;
+# explainer, "Where it earns its keep": the drafter's weights quantized to 4 bits).  The pages
+# name GPTQ but give no format; the reading taken here is group-wise symmetric round-to-nearest
+# (calibration needs data, so none is done):
+#   groups of W4_GROUP consecutive k of one output row f share a scale s = max|w| / 7;
+#   q = round(w / s) (half away from zero), in -7 .. 7 (0 where s = 0); the dequantized weight is
+#   q * s;  stored as the nibble q + 8, two per byte along k, the lower k in the low nibble.
+# ---------------------------------------------------------------------------------------------
+W4_GROUP = 128
+
+
+def quantize_w4(W, group: int = W4_GROUP):
+    """Round-to-nearest 4-bit codes of W [Nout][K] (K a multiple of group): returns
+    (packed uint8 [Nout][K/2], scales float32 [Nout][K/group]).  The scales are rounded to
+    float32 first, and the codes are taken against the rounded scale, so that codes and
+    scales describe the dequantized weight exactly."""
+    W = np.asarray(W, dtype=np.float64)
+    n_out, K = W.shape
+    assert K % group == 0
+    Wg = W.reshape(n_out, K // group, group)
+    s = (np.abs(Wg).max(axis=2) / 7.0).astype(np.float32)
+    s64 = s.astype(np.float64)[:, :, None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(s64 > 0, Wg / np.where(s64 > 0, s64, 1.0), 0.0)
+    q = np.sign(r) * np.floor(np.abs(r) + 0.5)  # half away from zero
+    q = np.clip(q, -7, 7).astype(np.int64).reshape(n_out, K)
+    nib = (q + 8).astype(np.uint8)
+    packed = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    return packed, s
+
+
+def dequantize_w4(packed, scales, group: int = W4_GROUP):
+    """The weights that 4-bit codes and their scales stand for: [Nout][K] float64."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    n_out, half = packed.shape
+    K = 2 * half
+    q = np.empty((n_out, K), dtype=np.int64)
+    q[:, 0::2] = (packed & 15).astype(np.int64) - 8
+    q[:, 1::2] = (packed >> 4).astype(np.int64) - 8
+    s = np.repeat(np.asarray(scales, dtype=np.float64), group, axis=1)
+    return q * s
+
+
+def linear_w4(X, packed, scales, group: int = W4_GROUP):
+    """out[m][f] = sum_k X[m][k] * Wdq[f][k] with Wdq the dequantized weights, in float64."""
+    return np.asarray(X, dtype=np.float64) @ dequantize_w4(packed, scales, group).T

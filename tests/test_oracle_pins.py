@@ -499,3 +499,51 @@ def test_gdn_chunked_equals_the_sequential_rule():
     for chunk in (1, 2, 4, 16, 64):
         got = O.gdn_chunked(x, B, ar, br, ba, bb, H0, chunk)
         assert np.max(np.abs(got - ref)) <= 1e-10 * max(1.0, np.max(np.abs(ref))), chunk
+
+
+# --- 4-bit weight-only projections (group-wise symmetric round-to-nearest) -------------------
+
+def test_w4_packing_worked_by_hand():
+    """One 128-wide group with max |w| = 7, so the scale is exactly 1: codes 7, -7, round(0.5) =
+    1 and round(-2.5) = -3 (half away from zero) become the nibbles 15, 1, 9 and 5, the lower k
+    in the low nibble: bytes 0x1F and 0x59; every zero weight is the nibble pair 0x88."""
+    W = np.zeros((1, 128))
+    W[0, :4] = [7.0, -7.0, 0.5, -2.5]
+    packed, scales = O.quantize_w4(W)
+    assert scales.dtype == np.float32 and scales.shape == (1, 1) and scales[0, 0] == 1.0
+    assert packed.dtype == np.uint8 and packed.shape == (1, 64)
+    assert packed[0, 0] == 0x1F and packed[0, 1] == 0x59
+    assert np.all(packed[0, 2:] == 0x88)
+    dq = O.dequantize_w4(packed, scales)
+    assert np.array_equal(dq[0, :4], [7.0, -7.0, 1.0, -3.0]) and np.all(dq[0, 4:] == 0)
+
+
+def test_w4_weights_on_the_grid_come_back_exactly():
+    """Weights that already are integer multiples (-7..7, a 7 in every group) of a power-of-two
+    scale quantize to themselves, and the 4-bit projection then equals the plain matrix product."""
+    rng = np.random.default_rng(11)
+    n_out, K = 9, 384
+    q = rng.integers(-7, 8, size=(n_out, K))
+    q[:, ::128] = 7 * np.where(rng.random((n_out, K // 128)) < 0.5, -1, 1)
+    s = 2.0 ** rng.integers(-8, 2, size=(n_out, K // 128))
+    W = q * np.repeat(s, 128, axis=1)
+    packed, scales = O.quantize_w4(W)
+    assert np.array_equal(scales.astype(np.float64), s)
+    assert np.array_equal(O.dequantize_w4(packed, scales), W)
+    X = rng.standard_normal((5, K))
+    np.testing.assert_allclose(O.linear_w4(X, packed, scales), np.matmul(X, W.T), rtol=0, atol=1e-12)
+
+
+def test_w4_round_to_nearest_error_bound_and_zero_groups():
+    """Each dequantized weight lies within half a step of the original (the round-to-nearest
+    bound, plus float32 rounding of the scale); an all-zero group has scale 0 and code 8."""
+    rng = np.random.default_rng(12)
+    W = rng.standard_normal((7, 256)) * rng.random((7, 1))
+    W[3, 128:] = 0.0
+    packed, scales = O.quantize_w4(W)
+    dq = O.dequantize_w4(packed, scales)
+    step = np.repeat(scales.astype(np.float64), 128, axis=1)
+    assert np.all(np.abs(dq - W) <= 0.5 * step * (1 + 1e-6) + 1e-30)
+    assert scales[3, 1] == 0 and np.all(packed[3, 64:] == 0x88)
+    nib = np.concatenate([packed & 15, packed >> 4], axis=1)
+    assert nib.min() >= 1 and nib.max() <= 15
