@@ -519,6 +519,20 @@ int hyf_linear(const hyf_config* cfg, const void* X, int64_t M, int32_t K, const
   return hip_status(launch_linear(cfg->dtype, xs, M, K, W, Nout, e, static_cast<hipStream_t>(stream)));
 }
 
+int hyf_linear_w4(const hyf_config* cfg, const void* X, int64_t M, int32_t K, const void* Wq, const float* scales,
+                  int32_t Nout, void* out, int32_t out_f32, void* stream) {
+  const int st = check_cfg(cfg);
+  if (st != HYF_OK) return st;
+  if (cfg->dtype != HYF_BF16) return HYF_EUNSUPPORTED;
+  if (M < 0 || M > (int64_t)64 * 65535 || K < 128 || K % 128 || Nout < 1 || Nout > (1 << 24)) return HYF_ESHAPE;
+  if (M == 0) return HYF_OK;
+  if (!X || !Wq || !scales || !out || !aligned(X, 16) || !aligned(Wq, 16) || !aligned(scales, 4) ||
+      !aligned(out, out_f32 ? 4 : 2))
+    return HYF_EINVAL;
+  return hip_status(launch_linear_w4(static_cast<const bf16*>(X), M, K, static_cast<const uint8_t*>(Wq), scales,
+                                     Nout, out, out_f32 != 0, static_cast<hipStream_t>(stream)));
+}
+
 int hyf_ssd_scan(const hyf_config* cfg, const void* x, const void* B, const void* C_opt, const float* dt_raw,
                  const float* a_log, const float* dt_bias, const float* d_skip, float* H_inout, void* y_opt, int64_t T,
                  void* ws, size_t ws_bytes, void* stream) {

@@ -69,6 +69,9 @@ __device__ __forceinline__ const void* row_ptr(const RowSrc& xs, int64_t m, int 
 // Picks the weight-streaming kernel (small M) or the tiled MFMA GEMM (large M).
 hipError_t launch_linear(int dtype, RowSrc x, int64_t M, int K, const void* W, int Nout,
                          const Epi& epi, hipStream_t s);
+// Weight-only 4-bit projection (hyf_w4.hip); K a multiple of 128.
+hipError_t launch_linear_w4(const bf16* X, int64_t M, int K, const uint8_t* Wq, const float* S, int Nout,
+                            void* out, bool out_f32, hipStream_t s);
 // The 256x128-tile bf16 GEMM (hyf_gemm.hip); K must be a multiple of 64.
 hipError_t launch_gemm256(RowSrc x, int M, int K, const bf16* W, int Nout, const Epi& epi, hipStream_t s);
 

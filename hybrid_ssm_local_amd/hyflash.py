@@ -65,6 +65,7 @@ _SIGS = {
     "hyf_draft_block": (ctypes.c_int, [_P(HyfConfig), _P(HyfWeights), _vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp,
                                        _vp, _sz, _vp]),
     "hyf_linear": (ctypes.c_int, [_P(HyfConfig), _vp, _i64, _i32, _vp, _i32, _vp, _i32, _vp]),
+    "hyf_linear_w4": (ctypes.c_int, [_P(HyfConfig), _vp, _i64, _i32, _vp, _vp, _i32, _vp, _i32, _vp]),
     "hyf_ssd_scan": (ctypes.c_int, [_P(HyfConfig), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _sz,
                                     _vp]),
 }
@@ -197,6 +198,11 @@ def hyf_draft_block(cfg, w: HyfWeights, pool, pool_slots, slots, n_req, commit_f
 
 def hyf_linear(cfg, X, M, K, W, Nout, out, out_f32, stream=None) -> int:
     return lib().hyf_linear(ctypes.byref(cfg), _ptr(X), M, K, _ptr(W), Nout, _ptr(out), out_f32, _stream(stream))
+
+
+def hyf_linear_w4(cfg, X, M, K, Wq, scales, Nout, out, out_f32, stream=None) -> int:
+    return lib().hyf_linear_w4(ctypes.byref(cfg), _ptr(X), M, K, _ptr(Wq), _ptr(scales), Nout, _ptr(out), out_f32,
+                               _stream(stream))
 
 
 def hyf_ssd_scan(cfg, x, B, C, dt_raw, a_log, dt_bias, d_skip, H, y, T, ws, ws_bytes, stream=None) -> int:

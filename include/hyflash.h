@@ -183,6 +183,18 @@ int hyf_draft_block(const hyf_config* cfg, const hyf_weights* w, void* state_poo
 int hyf_linear(const hyf_config* cfg, const void* X, int64_t M, int32_t K, const void* W,
                int32_t Nout, void* out, int32_t out_f32, void* stream);
 
+/* Weight-only 4-bit projection (paper page, Figures & tables: a 4-bit drafter keeps the bf16
+ * drafter's acceptance; explainer, "Where it earns its keep": the drafter's weights in 4 bits):
+ *   out[m][f] = sum_k X[m][k] * (code(f, k) - 8) * scales[f][k / 128]      m < M, f < Nout
+ * X [M][K] bf16 (cfg->dtype must be HYF_BF16, else HYF_EUNSUPPORTED), 16-byte aligned.
+ * Wq [Nout][K/2] bytes, 16-byte aligned: codes 0..15, two per byte along k, the lower k in the
+ * low nibble.  scales [Nout][K/128] fp32, 4-byte aligned.  K a multiple of 128, 1 <= Nout <=
+ * 2^24, 0 <= M <= 64 * 65535 (HYF_ESHAPE otherwise).  out [M][Nout] is fp32 when out_f32 != 0,
+ * else bf16.  All device pointers, owned by the caller; M = 0 is a no-op.  The weights are
+ * streamed once per 64 rows of X, so the call suits round-sized M (up to 64 rows). */
+int hyf_linear_w4(const hyf_config* cfg, const void* X, int64_t M, int32_t K, const void* Wq,
+                  const float* scales, int32_t Nout, void* out, int32_t out_f32, void* stream);
+
 /* Host only.  Workspace bytes hyf_ssd_scan needs for T tokens, with (with_y != 0) or without
  * per-token outputs. */
 size_t hyf_ssd_scan_workspace_bytes(const hyf_config* cfg, int64_t T, int32_t with_y);

@@ -183,3 +183,21 @@ def test_gated_delta_rule_configs():
         hf.HYF_EUNSUPPORTED
     assert hf.hyf_memory_commit(cfg, w, fake, 1, None, 1, fake, [0, 4], fake, fake, 1 << 30, 0) == \
         hf.HYF_EUNSUPPORTED
+
+
+def test_four_bit_projection_rejects_bad_calls_before_device_work():
+    fake = 1 << 20  # never dereferenced: validation fails first
+    cfg = hf.make_config(I.QWEN)
+    assert cfg.dtype == hf.HYF_BF16
+    ok = (fake, 12, 2560, fake, fake, 7968, fake, 1, 0)
+    # K not a multiple of 128, no rows of weights, too many rows
+    assert hf.hyf_linear_w4(cfg, fake, 12, 2560 + 64, fake, fake, 7968, fake, 1, 0) == hf.HYF_ESHAPE
+    assert hf.hyf_linear_w4(cfg, fake, 12, 2560, fake, fake, 0, fake, 1, 0) == hf.HYF_ESHAPE
+    assert hf.hyf_linear_w4(cfg, fake, 64 * 65535 + 1, 2560, fake, fake, 7968, fake, 1, 0) == hf.HYF_ESHAPE
+    # misaligned codes, null scales
+    assert hf.hyf_linear_w4(cfg, fake, 12, 2560, fake + 8, fake, 7968, fake, 1, 0) == hf.HYF_EINVAL
+    assert hf.hyf_linear_w4(cfg, fake, 12, 2560, fake, None, 7968, fake, 1, 0) == hf.HYF_EINVAL
+    # no rows: nothing to do
+    assert hf.hyf_linear_w4(cfg, fake, 0, *ok[2:]) == hf.HYF_OK
+    # the activations must be bf16
+    assert hf.hyf_linear_w4(hf.make_config(I.TINY), *ok) == hf.HYF_EUNSUPPORTED

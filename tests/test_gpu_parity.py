@@ -207,6 +207,62 @@ def test_linear_rows_do_not_depend_on_the_batch():
         assert torch.equal(outs[M], outs[64][:M]), M
 
 
+W4_CASES = [  # (K, Nout, Ms): one 128-wide group; fewer groups than waves; 17 groups (a ragged
+    # split over 8 waves); the round projections of the Qwen3-4B-shaped layer (12 rows x w_in,
+    # 8 rows x w_out); rows across 16-row tiles and past the 64-row slab of one workgroup;
+    # more feature tiles than CUs
+    (128, 17, [1, 16, 17, 64, 65, 130]),
+    (384, 100, [3, 33]),
+    (2176, 48, [40]),
+    (2560, 7968, [12]),
+    (2560, 2560, [8]),
+    (256, 4129, [20, 5]),  # 259 feature tiles: two per workgroup, the last one past Nout
+]
+
+
+@pytest.mark.parametrize("K,Nout,Ms", W4_CASES, ids=[f"K{c[0]}_N{c[1]}" for c in W4_CASES])
+def test_four_bit_linear_matches_the_oracle(K, Nout, Ms):
+    """Every code 0..15 appears (random bytes), one group has scale 0; the codes are exact in the
+    kernel, so fp32 output differs from the oracle by fp32 accumulation only."""
+    shape = I.QWEN
+    cfg = hf.make_config(shape)
+    rng = I.rng_streams(K * 7 + Nout)
+    packed = rng[0].integers(0, 256, size=(Nout, K // 2), dtype=np.uint8)
+    scales = (np.abs(rng[0].standard_normal((Nout, K // 128))) / (7.0 * np.sqrt(K))).astype(np.float32)
+    scales[Nout // 2, (K // 128) // 2] = 0.0
+    Wq = torch.from_numpy(packed).to(DEV)
+    Sd = torch.from_numpy(scales).to(DEV)
+    for M in Ms:
+        X = I.make_rows(rng[1], M, K, 1.0, "bf16")
+        Xd = hf.to_device(X, shape)
+        ref = O.linear_w4(X, packed, scales)
+        for out_f32 in (1, 0):
+            out = torch.full((M, Nout), float("nan"), device=DEV, dtype=torch.float32 if out_f32 else torch.bfloat16)
+            say("hyf_linear_w4 M", M, "K", K, "N", Nout, "f32 out" if out_f32 else "bf16 out")
+            hf.check(hf.hyf_linear_w4(cfg, Xd, M, K, Wq, Sd, Nout, out, out_f32), "hyf_linear_w4")
+            torch.cuda.synchronize()
+            assert_close(out.float().cpu().numpy(), ref, "f32" if out_f32 else "bf16",
+                         f"linear_w4 M={M} K={K} N={Nout} out_f32={out_f32}")
+
+
+def test_four_bit_linear_of_quantized_xavier_weights():
+    """Weights quantized by the oracle's round-to-nearest rule: the 4-bit projection of the w_in
+    shape against the oracle's product of the same codes."""
+    shape = I.QWEN
+    cfg = hf.make_config(shape)
+    rng = I.rng_streams(4242)
+    K, Nout, M = shape.d_model, 1024, 12
+    W = I.make_rows(rng[0], Nout, K, 1.0 / np.sqrt(K), "f32")
+    packed, scales = O.quantize_w4(W)
+    X = I.make_rows(rng[1], M, K, 1.0, "bf16")
+    out = torch.empty(M, Nout, device=DEV, dtype=torch.float32)
+    say("hyf_linear_w4 quantized weights M", M, "K", K, "N", Nout)
+    hf.check(hf.hyf_linear_w4(cfg, hf.to_device(X, shape), M, K, torch.from_numpy(packed).to(DEV),
+                              torch.from_numpy(scales).to(DEV), Nout, out, 1), "hyf_linear_w4")
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), O.linear_w4(X, packed, scales), "f32", "linear_w4 quantized")
+
+
 # ---------------------------------------------------------------- layer level
 
 
