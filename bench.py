@@ -144,6 +144,70 @@ def time_calls(torch, fn, reps):
     return ms, ms
 
 
+def time_graph(torch, fn, reps, replays=3):
+    """Mean milliseconds per call of `reps` calls captured in one HIP graph, replayed `replays`
+    times between HIP events (for calls shorter than a host-side launch)."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(reps):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (replays * reps)
+
+
+def w4_round_projections(torch, hf, I, ep, reps=96):
+    """The round's two projections (12 rows x w_in, 8 rows x w_out) with 4-bit weights
+    (hyf_linear_w4) beside the bf16 ones (hyf_linear), each timed in a captured graph over enough
+    rotated weight copies to exceed the 256 MB last-level cache.  Codes are random bytes, scales
+    N(0,1)-sized; the timing does not depend on their values."""
+    sh, cfg = ep.shape, ep.cfg
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4)
+    st = [0]
+    res = {}
+    for name, M, K, N in (("w_in", 12, sh.d_model, sh.n_in), ("w_out", 8, sh.dq, sh.d_model)):
+        X = torch.randn((M, K), device="cuda", generator=gen).to(torch.bfloat16)
+        y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        w4_bytes = N * K // 2 + N * (K // 128) * 4
+        n4 = max(2, math.ceil(320e6 / w4_bytes))
+        codes = [torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device="cuda", generator=gen)
+                 for _ in range(n4)]
+        scales = [torch.rand((N, K // 128), device="cuda", generator=gen) / (7.0 * math.sqrt(K)) for _ in range(n4)]
+
+        def w4(i):
+            st[0] |= hf.hyf_linear_w4(cfg, X, M, K, codes[i % n4], scales[i % n4], N, y, 1)
+
+        w4(0)
+        us4 = 1e3 * time_graph(torch, w4, n4 * max(1, reps // n4))
+        del codes, scales
+        nb = max(2, math.ceil(320e6 / (N * K * 2)))
+        wb = [torch.randn((N, K), device="cuda", generator=gen).to(torch.bfloat16) for _ in range(nb)]
+
+        def b16(i):
+            st[0] |= hf.hyf_linear(cfg, X, M, K, wb[i % nb], N, y, 1)
+
+        b16(0)
+        usb = 1e3 * time_graph(torch, b16, nb * max(1, reps // nb))
+        del wb
+        byt = w4_bytes + M * K * 2 + M * N * 4
+        res[name] = {"rows": M, "K": K, "N": N, "w4_us": us4, "bf16_us": usb, "speedup": usb / us4,
+                     "bytes_per_launch": byt, "achieved_gbs": byt / (us4 * 1e-6) / 1e9,
+                     "frac": byt / (us4 * 1e-6) / 1e9 / HBM_PEAK_GBS}
+    if st[0]:
+        raise RuntimeError(f"projection call failed: status {st[0]}")
+    torch.cuda.empty_cache()
+    res["note"] = ("weight-only 4-bit codes (128-wide groups, fp32 scales) against bf16 weights, "
+                   "graph-timed; the layer entry points still take bf16 weights")
+    return res
+
+
 def batched_serving(torch, hf, I, rounds=16):
     """Batched serving on one GPU at the Qwen3-4B layer shape: 64 requests with prefixes of
     U{2048..16384} committed features (per-request states and rings in one pool), then rounds in
@@ -607,6 +671,8 @@ def main():
     torch.cuda.empty_cache()
     log("kernel loops")
     kl = kernel_loops(torch, hf, I, ep, args.kernel_reps)
+    log("4-bit projections")
+    w4 = w4_round_projections(torch, hf, I, ep)
     cpu = None if args.no_cpu else cpu_baseline(I, ep)
 
     sh = ep.shape
@@ -662,6 +728,7 @@ def main():
                           "traffic": pmc_traffic("gemm"), "algorithmic_bytes": gemm["bytes"]},
         "gated_delta_rule": gdn,
         "batched_serving": batched,
+        "w4a16_round_projections": w4,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
