@@ -263,6 +263,35 @@ def test_four_bit_linear_of_quantized_xavier_weights():
     assert_close(out.cpu().numpy(), O.linear_w4(X, packed, scales), "f32", "linear_w4 quantized")
 
 
+def test_four_bit_linear_replays_in_a_graph():
+    """One call captured in a HIP graph, replayed three times with new rows written eagerly
+    between the replays: every replay matches the eager call on the same rows."""
+    shape = I.QWEN
+    cfg = hf.make_config(shape)
+    rng = I.rng_streams(515)
+    K, Nout, M = 512, 300, 12
+    packed = torch.from_numpy(rng[0].integers(0, 256, size=(Nout, K // 2), dtype=np.uint8)).to(DEV)
+    scales = torch.from_numpy((np.abs(rng[0].standard_normal((Nout, K // 128))) * 0.02).astype(np.float32)).to(DEV)
+    X = torch.zeros(M, K, device=DEV, dtype=torch.bfloat16)
+    out = torch.zeros(M, Nout, device=DEV, dtype=torch.float32)
+    say("hyf_linear_w4 graph capture")
+    hf.check(hf.hyf_linear_w4(cfg, X, M, K, packed, scales, Nout, out, 1), "hyf_linear_w4")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        hf.check(hf.hyf_linear_w4(cfg, X, M, K, packed, scales, Nout, out, 1), "hyf_linear_w4")
+    for rep in range(3):
+        Xn = hf.to_device(I.make_rows(rng[1], M, K, 1.0, "bf16"), shape)
+        X.copy_(Xn)
+        eager = torch.empty_like(out)
+        hf.check(hf.hyf_linear_w4(cfg, Xn, M, K, packed, scales, Nout, eager, 1), "hyf_linear_w4")
+        torch.cuda.synchronize()
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), rep
+
+
 # ---------------------------------------------------------------- layer level
 
 
