@@ -217,6 +217,7 @@ W4_CASES = [  # (K, Nout, Ms): one 128-wide group; fewer groups than waves; 17 g
     (2560, 7968, [12]),
     (2560, 2560, [8]),
     (256, 4129, [20, 5]),  # 259 feature tiles: two per workgroup, the last one past Nout
+    (5120, 4200, [8, 20]),  # 40 groups: a wave loops over several batches of in-flight groups
 ]
 
 
