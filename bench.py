@@ -199,7 +199,8 @@ def w4_round_projections(torch, hf, I, ep, reps=96):
         byt = w4_bytes + M * K * 2 + M * N * 4
         res[name] = {"rows": M, "K": K, "N": N, "w4_us": us4, "bf16_us": usb, "speedup": usb / us4,
                      "bytes_per_launch": byt, "achieved_gbs": byt / (us4 * 1e-6) / 1e9,
-                     "frac": byt / (us4 * 1e-6) / 1e9 / HBM_PEAK_GBS}
+                     "frac": byt / (us4 * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                     "traffic": pmc_traffic("w4") if name == "w_in" else None}
     if st[0]:
         raise RuntimeError(f"projection call failed: status {st[0]}")
     torch.cuda.empty_cache()
@@ -403,6 +404,7 @@ PMC_KERNELS = {  # key -> (kernel name as it appears in the profile, mangled or 
     "proj": ("k_proj_stream", "hybrid_ssm_local_amd/csrc/hyf_proj.hip"),
     "scan": ("k_ssd_seg", "hybrid_ssm_local_amd/csrc/hyf_scan.hip"),
     "gemm": ("k_gemm_bf16_256", "hybrid_ssm_local_amd/csrc/hyf_gemm.hip"),
+    "w4": ("k_linear_w4", "hybrid_ssm_local_amd/csrc/hyf_w4.hip"),
 }
 
 
@@ -414,14 +416,29 @@ def source_digest(rel):
 
 
 def pmc_probe(torch, hf, I, reps=6):
-    """The W_in projection of a round, the 8192-token scan, the prefill GEMM and a copy of known size."""
+    """The W_in projection of a round (bf16 and 4-bit weights), the 8192-token scan, the prefill GEMM and a
+    copy of known size."""
     src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda").normal_()
     dst = torch.empty_like(src)
     for _ in range(3):
         dst.copy_(src)
     ep = Episode(torch, hf, I)
     kernel_loops(torch, hf, I, ep, reps, with_gemm=True, with_y=False)
+    # the 4-bit w_in projection of a round, eager calls on fresh weight copies
+    sh, cfg = ep.shape, ep.cfg
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4)
+    M, K, N = 12, sh.d_model, sh.n_in
+    X = torch.randn((M, K), device="cuda", generator=gen).to(torch.bfloat16)
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    st = 0
+    for _ in range(reps):
+        codes = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device="cuda", generator=gen)
+        scales = torch.rand((N, K // 128), device="cuda", generator=gen) / (7.0 * math.sqrt(K))
+        st |= hf.hyf_linear_w4(cfg, X, M, K, codes, scales, N, y, 1)
     torch.cuda.synchronize()
+    if st:
+        raise RuntimeError(f"hyf_linear_w4 failed: status {st}")
 
 
 def pmc_summary(fetch_db, write_db):
