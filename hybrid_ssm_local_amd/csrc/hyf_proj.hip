@@ -211,6 +211,84 @@ k_proj_stream(RowSrc xs, int M, int K, const bf16* __restrict__ W, int Nout, Epi
   }
 }
 
+// One 16-row tile of X with a grid of at most one workgroup per CU (w_out of a round): the same
+// slabs, waves and MFMA order as k_proj_stream<NW, 1> (so the same bits), with two LDS buffers per
+// wave: the next slab's direct loads are in flight while the current slab's MFMAs run.  Every slab
+// issues exactly 8 loads (addresses past M or K are clamped to valid ones; such chunks feed only
+// zeroed fragments or output columns that are never stored), so waiting until at most 8 loads
+// are outstanding means the current slab has landed.
+template <int NW>
+__global__ void __launch_bounds__(NW * 64)
+k_proj_stream2(RowSrc xs, int M, int K, const bf16* __restrict__ W, int Nout, Epi epi) {
+  constexpr int PER = 8192;  // LDS bytes per wave and buffer: the weight tile and one x tile
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = lane & 15, g = lane >> 4;
+  const int p = lane & 15, r4 = lane >> 4;
+  const int f0 = blockIdx.x * 16;
+  if (epi.zero && blockIdx.x == 0 && blockIdx.y == 0)
+    for (int z = threadIdx.x; z < epi.n_zero; z += NW * 64) epi.zero[z] = 0;
+  const int m_base = blockIdx.y * 16;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nslab = (K + PS_SLAB - 1) / PS_SLAB;
+  auto issue = [&](int sl, int buf) {
+    char* wl = smem + (wave * 2 + buf) * PER;
+    char* xl = wl + 4096;
+    const int kb = sl * PS_SLAB;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 4 * j + r4;
+      const int k = min(kb + ((p ^ r) << 3), K - 8);
+      lds_dma16(W + (int64_t)min(f0 + r, Nout - 1) * K + k, wl + j * 1024);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 4 * j + r4;
+      const int m = min(m_base + r, M - 1);
+      const int k = min(kb + ((p ^ r) << 3), K - 8);
+      lds_dma16(static_cast<const bf16*>(row_ptr(xs, m, K, 2)) + k, xl + j * 1024);
+    }
+  };
+  if (wave < nslab) issue(wave, 0);
+  int it = 0;
+  for (int sl = wave; sl < nslab; sl += NW, ++it) {
+    if (sl + NW < nslab) {
+      lgkm_wait0();  // the fragment reads of the buffer about to be refilled are done
+      issue(sl + NW, (it + 1) & 1);
+      vm_wait<8>();
+    } else {
+      vm_wait<0>();
+    }
+    const char* wl = smem + (wave * 2 + (it & 1)) * PER;
+    const char* xl = wl + 4096;
+    const int kb = sl * PS_SLAB;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = g + 4 * u;
+      const bool ok = kb + c * 8 < K;
+      const int o = i * 256 + ((c ^ i) << 4);
+      const bf16x8 a = ok ? *reinterpret_cast<const bf16x8*>(wl + o) : bf16x8{};
+      const bf16x8 b = ok ? *reinterpret_cast<const bf16x8*>(xl + o) : bf16x8{};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+    }
+  }
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);  // [NW][4][64]
+#pragma unroll
+  for (int r = 0; r < 4; ++r) red[(wave * 4 + r) * 64 + lane] = acc[r];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < 256; idx += NW * 64) {
+    const int fl = idx & 15, ml = idx >> 4;
+    const int src_lane = (fl >> 2) * 16 + ml, r = fl & 3;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) v += red[(w * 4 + r) * 64 + src_lane];
+    const int f = f0 + fl;
+    const int m = m_base + ml;
+    if (f < Nout && m < M) epi_store<bf16>(epi, m, f, v);
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // bf16 GEMM, 128x128 macro tile, K step 64.
 constexpr int GB_M = 128, GB_N = 128, GB_K = 64, GB_LD = GB_K + 8;  // LDS row pitch (elements)
@@ -373,8 +451,25 @@ static hipError_t launch_stream_t(RowSrc x, int M, int K, const bf16* W, int Nou
 }
 
 template <int NW>
+static hipError_t launch_stream2(RowSrc x, int M, int K, const bf16* W, int Nout, const Epi& epi, hipStream_t s) {
+  const size_t lds = (size_t)NW * 2 * 8192;
+  static std::once_flag once;
+  static hipError_t set_err = hipSuccess;
+  std::call_once(once, [] {
+    set_err = hipFuncSetAttribute(reinterpret_cast<const void*>(k_proj_stream2<NW>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 256);
+  });
+  if (set_err != hipSuccess) return set_err;
+  hipLaunchKernelGGL((k_proj_stream2<NW>), dim3((Nout + 15) / 16, 1), dim3(NW * 64), lds, s, x, M, K, W, Nout, epi);
+  return hipGetLastError();
+}
+
+template <int NW>
 static hipError_t launch_stream_nw(RowSrc x, int M, int K, const bf16* W, int Nout, const Epi& epi, hipStream_t s) {
   const int mt = (M + 15) / 16;
+  // One row tile on at most 256 workgroups (one per CU): the double-buffered kernel (the same
+  // results); larger grids keep more workgroups per CU in flight with the single buffer instead.
+  if (NW == 8 && mt == 1 && Nout <= 4096) return launch_stream2<NW>(x, M, K, W, Nout, epi, s);
   switch (mt >= 4 ? 4 : mt) {
     case 1: return launch_stream_t<NW, 1>(x, M, K, W, Nout, epi, s);
     case 2: return launch_stream_t<NW, 2>(x, M, K, W, Nout, epi, s);
