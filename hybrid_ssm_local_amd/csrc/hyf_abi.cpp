@@ -248,6 +248,75 @@ int check_weights(const hyf_weights* w) {
   return HYF_OK;
 }
 
+
+// Host checks of a draft call (everything but the workspace); fills the request table and the
+// number of commit rows.
+int draft_check(const hyf_config* cfg, const hyf_weights* w, void* state_pool, int32_t pool_slots,
+                const int32_t* slots, int32_t n_req, const void* commit_feats, const int64_t* cu_commit,
+                const void* block_in, void* block_out, ReqTable* rt, int64_t* rows_out) {
+  int st = check_cfg(cfg);
+  if (st != HYF_OK) return st;
+  if ((st = check_weights(w)) != HYF_OK) return st;
+  if (!state_pool || !aligned(state_pool, ALIGN) || pool_slots < 1) return HYF_EINVAL;
+  if (!block_in || !block_out || !aligned(block_in, 16) || !aligned(block_out, 16)) return HYF_EINVAL;
+  if ((commit_feats == nullptr) != (cu_commit == nullptr)) return HYF_EINVAL;
+  const Shape s = make_shape(cfg);
+  if ((st = build_table(s, pool_slots, slots, n_req, cu_commit, rt)) != HYF_OK) return st;
+  int64_t rows = 0;
+  if (cu_commit) {
+    rows = cu_commit[n_req];
+    for (int i = 0; i < n_req; ++i)
+      if (cu_commit[i + 1] - cu_commit[i] > HYF_BLOCK) return HYF_ECAPACITY;
+    if (rows > 0 && !aligned(commit_feats, 16)) return HYF_EINVAL;
+  }
+  *rows_out = rows;
+  return HYF_OK;
+}
+
+// The launches of a draft call, after every check has passed: ws holds at least
+// hyf_workspace_bytes(cfg, n_req, rows, 0) bytes, 256-byte aligned.
+int draft_run(const hyf_config* cfg, const hyf_weights* w, void* state_pool, const ReqTable& rt, int64_t rows,
+              const void* commit_feats, const void* block_in, void* block_out, char* wsb, hipStream_t hs) {
+  const Shape s = make_shape(cfg);
+  const int n_req = rt.n_req;
+  char* pool = static_cast<char*>(state_pool);
+  const int dt = cfg->dtype;
+  const WsDraft L = ws_draft(s, dt, n_req, rows);
+  float* proj = reinterpret_cast<float*>(wsb + L.proj);
+
+  // 1. one pass over w_in for [commit rows ; block rows] (it also clears the round's counters)
+  int32_t* counters = reinterpret_cast<int32_t*>(wsb + L.counters);
+  const int64_t ld = proj_ld(s);
+  RowSrc xs{rows > 0 ? commit_feats : block_in, block_in, rows};
+  Epi e{proj, ld, 1, s.n_in, nullptr, 0, 0, counters, n_req * s.nh + n_req};
+  hipError_t he = launch_linear(dt, xs, rows + (int64_t)HYF_BLOCK * n_req, s.d, w->w_in, s.n_in, e, hs);
+  if (he != hipSuccess) return HYF_EHIP;
+
+  // 2. the round kernel: commit + readout tiles and attention splits, merged per head
+  RoundArgs ra{};
+  ra.proj = proj;
+  ra.ld = ld;
+  ra.blk_row0 = rows;
+  ra.state_pool = pool;
+  ra.a_log = w->a_log;
+  ra.dt_bias = w->dt_bias;
+  ra.d_skip = w->d_skip;
+  ra.mem = reinterpret_cast<float*>(wsb + L.mem);
+  ra.att_part = reinterpret_cast<float*>(wsb + L.att_part);
+  ra.att_ml = reinterpret_cast<float*>(wsb + L.att_ml);
+  ra.o_in = wsb + L.o_in;
+  ra.counters = counters;
+  ra.n_tiles = round_tiles(s);
+  ra.n_split = n_att_split(s);
+  ra.do_commit = rows > 0;
+  ra.do_draft = 1;
+  if ((he = launch_round(dt, s, ra, rt, hs)) != hipSuccess) return HYF_EHIP;
+  // 3. output projection
+  RowSrc xo{ra.o_in, ra.o_in, (int64_t)HYF_BLOCK * n_req};
+  Epi eo{block_out, s.d, 0, s.d, nullptr, 0, 0, nullptr, 0};
+  return hip_status(launch_linear(dt, xo, (int64_t)HYF_BLOCK * n_req, s.dq, w->w_out, s.d, eo, hs));
+}
+
 }  // namespace
 
 extern "C" {
@@ -343,7 +412,9 @@ int hyf_memory_commit(const hyf_config* cfg, const hyf_weights* w, void* state_p
   int64_t max_n = 0;
   for (int i = 0; i < n_req; ++i) max_n = cu_rows[i + 1] - cu_rows[i] > max_n ? cu_rows[i + 1] - cu_rows[i] : max_n;
 
-  if (s.gdn && max_n > 16 && !gdn_supported(s)) return HYF_EUNSUPPORTED;
+  // a gated delta-rule prefix takes the chunked kernels when they fit the shape, else the
+  // token-by-token one; refused only when neither fits
+  if (s.gdn && max_n > 16 && !gdn_supported(s) && !gdn_chunked_supported(s, es)) return HYF_EUNSUPPORTED;
   if (max_n <= 16 && !y_opt) {
     // Round-sized commit: one weight pass over the k | v | B | dt rows, then one round kernel that
     // folds the rows into H (one read-modify-write), appends them to the ring and advances count.
@@ -450,61 +521,14 @@ int hyf_memory_commit(const hyf_config* cfg, const hyf_weights* w, void* state_p
 int hyf_draft_block(const hyf_config* cfg, const hyf_weights* w, void* state_pool, int32_t pool_slots,
                     const int32_t* slots, int32_t n_req, const void* commit_feats, const int64_t* cu_commit,
                     const void* block_in, void* block_out, void* ws, size_t ws_bytes, void* stream) {
-  int st = check_cfg(cfg);
-  if (st != HYF_OK) return st;
-  if ((st = check_weights(w)) != HYF_OK) return st;
-  if (!state_pool || !aligned(state_pool, ALIGN) || pool_slots < 1) return HYF_EINVAL;
-  if (!block_in || !block_out || !aligned(block_in, 16) || !aligned(block_out, 16)) return HYF_EINVAL;
-  if ((commit_feats == nullptr) != (cu_commit == nullptr)) return HYF_EINVAL;
-  const Shape s = make_shape(cfg);
   ReqTable rt;
-  if ((st = build_table(s, pool_slots, slots, n_req, cu_commit, &rt)) != HYF_OK) return st;
   int64_t rows = 0;
-  if (cu_commit) {
-    rows = cu_commit[n_req];
-    for (int i = 0; i < n_req; ++i)
-      if (cu_commit[i + 1] - cu_commit[i] > HYF_BLOCK) return HYF_ECAPACITY;
-    if (rows > 0 && !aligned(commit_feats, 16)) return HYF_EINVAL;
-  }
+  int st = draft_check(cfg, w, state_pool, pool_slots, slots, n_req, commit_feats, cu_commit, block_in, block_out,
+                       &rt, &rows);
+  if (st != HYF_OK) return st;
   if (!ws || !aligned(ws, ALIGN) || ws_bytes < hyf_workspace_bytes(cfg, n_req, rows, 0)) return HYF_EWORKSPACE;
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  char* wsb = static_cast<char*>(ws);
-  char* pool = static_cast<char*>(state_pool);
-  const int dt = cfg->dtype;
-  const WsDraft L = ws_draft(s, dt, n_req, rows);
-  float* proj = reinterpret_cast<float*>(wsb + L.proj);
-
-  // 1. one pass over w_in for [commit rows ; block rows] (it also clears the round's counters)
-  int32_t* counters = reinterpret_cast<int32_t*>(wsb + L.counters);
-  const int64_t ld = proj_ld(s);
-  RowSrc xs{rows > 0 ? commit_feats : block_in, block_in, rows};
-  Epi e{proj, ld, 1, s.n_in, nullptr, 0, 0, counters, n_req * s.nh + n_req};
-  hipError_t he = launch_linear(dt, xs, rows + (int64_t)HYF_BLOCK * n_req, s.d, w->w_in, s.n_in, e, hs);
-  if (he != hipSuccess) return HYF_EHIP;
-
-  // 2. the round kernel: commit + readout tiles and attention splits, merged per head
-  RoundArgs ra{};
-  ra.proj = proj;
-  ra.ld = ld;
-  ra.blk_row0 = rows;
-  ra.state_pool = pool;
-  ra.a_log = w->a_log;
-  ra.dt_bias = w->dt_bias;
-  ra.d_skip = w->d_skip;
-  ra.mem = reinterpret_cast<float*>(wsb + L.mem);
-  ra.att_part = reinterpret_cast<float*>(wsb + L.att_part);
-  ra.att_ml = reinterpret_cast<float*>(wsb + L.att_ml);
-  ra.o_in = wsb + L.o_in;
-  ra.counters = counters;
-  ra.n_tiles = round_tiles(s);
-  ra.n_split = n_att_split(s);
-  ra.do_commit = rows > 0;
-  ra.do_draft = 1;
-  if ((he = launch_round(dt, s, ra, rt, hs)) != hipSuccess) return HYF_EHIP;
-  // 3. output projection
-  RowSrc xo{ra.o_in, ra.o_in, (int64_t)HYF_BLOCK * n_req};
-  Epi eo{block_out, s.d, 0, s.d, nullptr, 0, 0, nullptr, 0};
-  return hip_status(launch_linear(dt, xo, (int64_t)HYF_BLOCK * n_req, s.dq, w->w_out, s.d, eo, hs));
+  return draft_run(cfg, w, state_pool, rt, rows, commit_feats, block_in, block_out, static_cast<char*>(ws),
+                   static_cast<hipStream_t>(stream));
 }
 
 int hyf_linear(const hyf_config* cfg, const void* X, int64_t M, int32_t K, const void* W, int32_t Nout, void* out,

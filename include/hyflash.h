@@ -88,7 +88,7 @@ typedef struct {
  *   H <- alpha H (I - beta k k^T) + beta v k^T,
  * and the readout uses C_q / sqrt(|C_q|^2 + 1e-6).  (dt_bias and a_log carry the two gate biases.)
  * Per-token outputs (y_opt) and hyf_ssd_scan are Mamba-2 only (HYF_EUNSUPPORTED); a commit of more
- * than 16 rows per request needs d_state <= 192 (HYF_EUNSUPPORTED otherwise). */
+ * than 16 rows per request needs d_state <= 192, or d_state 224 in bf16 (HYF_EUNSUPPORTED otherwise). */
 typedef struct {
   const void* w_in;     /* [n_in][d_model], storage dtype, 16-byte aligned */
   const void* w_out;    /* [d_model][nh*P], storage dtype, 16-byte aligned */

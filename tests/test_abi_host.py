@@ -201,3 +201,4 @@ def test_four_bit_projection_rejects_bad_calls_before_device_work():
     assert hf.hyf_linear_w4(cfg, fake, 0, *ok[2:]) == hf.HYF_OK
     # the activations must be bf16
     assert hf.hyf_linear_w4(hf.make_config(I.TINY), *ok) == hf.HYF_EUNSUPPORTED
+

@@ -157,6 +157,9 @@ LINEAR_CASES = [  # (dtype, K, Nout, Ms): K tails past a 128-wide slab, M across
     ("bf16", 144, 7, [1, 16, 17, 40, 64, 65, 200]),
     ("bf16", 2560, 300, [1, 12, 16, 33, 64, 130]),
     ("bf16", 5120, 40, [8, 49]),
+    # K past the last 128-wide slab on the double-buffered kernel (one 16-row tile, K >= 2048):
+    # its loads past K are clamped and zeroed
+    ("bf16", 2184, 300, [1, 8, 16]),
     # the 256x128-tile GEMM (K a multiple of 64, M > 64): one, two and three K steps (the
     # three-stage pipeline's edges), ragged row and feature tiles
     ("bf16", 64, 130, [65, 257]),
@@ -187,19 +190,21 @@ def test_linear_matches_the_oracle(dtype, K, Nout, Ms):
             assert_close(out.float().cpu().numpy(), ref, dtype, f"linear M={M} K={K} out_f32={out_f32}")
 
 
-def test_linear_rows_do_not_depend_on_the_batch():
+@pytest.mark.parametrize("K", [2560, 2184])
+def test_linear_rows_do_not_depend_on_the_batch(K):
     # A row's projection is bit-identical whatever other rows share the call (M <= 64): the K split
-    # over waves depends on K alone.
+    # over waves depends on K alone, so the double-buffered one-tile kernel (M <= 16) and the
+    # single-buffered one give the same bits, also for a K that ends inside a 128-wide slab.
     shape = I.QWEN
     cfg = hf.make_config(shape)
     rng = I.rng_streams(77)
-    K, Nout = shape.d_model, 200
+    Nout = 200
     Wd = hf.to_device(I.make_rows(rng[0], Nout, K, 1.0 / np.sqrt(K), "bf16"), shape)
     X = hf.to_device(I.make_rows(rng[1], 64, K, 1.0, "bf16"), shape)
     outs = {}
     for M in (64, 33, 16, 5, 1):
         out = torch.empty(M, Nout, device=DEV, dtype=torch.float32)
-        say("hyf_linear batch independence M", M)
+        say("hyf_linear batch independence K", K, "M", M)
         hf.check(hf.hyf_linear(cfg, X, M, K, Wd, Nout, out, 1), "hyf_linear")
         torch.cuda.synchronize()
         outs[M] = out.cpu()
@@ -462,6 +467,24 @@ def test_gated_delta_rule_chunk_edges_in_one_call():
     pr.commit([pr.rows(n) for n in reversed(lens)])
     for i in range(8):
         pr.check_state(slot=i, what=f"gdn chunk edges request {i} second prefill")
+
+
+def test_gated_delta_rule_prefix_with_d_state_224():
+    # bf16 d_state 224 is taken by the chunked prefix kernels only (the token-by-token one keeps at
+    # most 192 state columns per row): a prefill, rounds on top, and a second prefill.
+    shape = small_shape("bf16", head_dim=64, d_state=224, window=40, memory="gdn")
+    pr = Pair(shape, seed=75, max_rows=400)
+    pr.gpu.reset()
+    say("gdn d_state 224 prefill 300")
+    pr.commit([pr.rows(300)])
+    pr.check_state(what="gdn N224 prefill")
+    for rnd in range(3):
+        say("gdn d_state 224 round", rnd)
+        g, o = pr.draft([pr.rows(8, 3)], commits=[pr.rows(2 + 3 * rnd)])
+        assert_close(g, o, "bf16", f"gdn N224 round {rnd}")
+    say("gdn d_state 224 second prefill 130")
+    pr.commit([pr.rows(130)])
+    pr.check_state(what="gdn N224 second prefill")
 
 
 def test_gated_delta_rule_rounds_of_sixteen_requests():
