@@ -3,6 +3,8 @@
 // (other than HYF_EHIP) leaves device memory untouched.
 #include <string.h>
 
+#include <mutex>
+
 #include "hyf_launch.h"
 
 using namespace hyf;
@@ -317,6 +319,33 @@ int draft_run(const hyf_config* cfg, const hyf_weights* w, void* state_pool, con
   return hip_status(launch_linear(dt, xo, (int64_t)HYF_BLOCK * n_req, s.dq, w->w_out, s.d, eo, hs));
 }
 
+// ---- the allocation-free draft call's scratch --------------------------------------------------
+// One array per GPU, in the library's code object: each device that loads the library holds its own
+// copy until the process ends.  Host code never uses the array's name as an address (on the host it
+// names a stand-in, not device memory): the device address comes from hipGetSymbolAddress, taken
+// once per device with that device current, and is kept per device.  Every call on one device
+// shares its array, so overlapping calls on one device race.
+static __device__ __align__(256) unsigned char scratch[HYF_NOALLOC_SCRATCH_BYTES];
+
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[NOALLOC_MAX_DEVICES] = {};
+
+int noalloc_scratch(char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return HYF_EHIP;
+  if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) return HYF_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return HYF_EHIP;
+    if (!aligned(p, ALIGN)) return HYF_EHIP;
+    g_scratch_ptr[dev] = static_cast<char*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return HYF_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -528,6 +557,23 @@ int hyf_draft_block(const hyf_config* cfg, const hyf_weights* w, void* state_poo
   if (st != HYF_OK) return st;
   if (!ws || !aligned(ws, ALIGN) || ws_bytes < hyf_workspace_bytes(cfg, n_req, rows, 0)) return HYF_EWORKSPACE;
   return draft_run(cfg, w, state_pool, rt, rows, commit_feats, block_in, block_out, static_cast<char*>(ws),
+                   static_cast<hipStream_t>(stream));
+}
+
+int hyf_draft_block_noalloc(const hyf_config* cfg, const hyf_weights* w, void* state_pool, int32_t pool_slots,
+                            const int32_t* slots, int32_t n_req, const void* commit_feats, const int64_t* cu_commit,
+                            const void* block_in, void* block_out, void* stream) {
+  ReqTable rt;
+  int64_t rows = 0;
+  int st = draft_check(cfg, w, state_pool, pool_slots, slots, n_req, commit_feats, cu_commit, block_in, block_out,
+                       &rt, &rows);
+  if (st != HYF_OK) return st;
+  // a draft call uses only the draft part of the workspace hyf_workspace_bytes sizes
+  if (ws_draft(make_shape(cfg), cfg->dtype, n_req, rows).end > (uint64_t)HYF_NOALLOC_SCRATCH_BYTES)
+    return HYF_ECAPACITY;
+  char* ws = nullptr;
+  if ((st = noalloc_scratch(&ws)) != HYF_OK) return st;
+  return draft_run(cfg, w, state_pool, rt, rows, commit_feats, block_in, block_out, ws,
                    static_cast<hipStream_t>(stream));
 }
 

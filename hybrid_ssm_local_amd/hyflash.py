@@ -24,6 +24,7 @@ HYF_F32, HYF_BF16 = 0, 1
 HYF_MEM_MAMBA2, HYF_MEM_GDN = 0, 1
 HYF_BLOCK = 8
 HYF_MAX_REQUESTS = 128
+HYF_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class HyfConfig(ctypes.Structure):
@@ -64,6 +65,8 @@ _SIGS = {
                                          _vp, _sz, _vp]),
     "hyf_draft_block": (ctypes.c_int, [_P(HyfConfig), _P(HyfWeights), _vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp,
                                        _vp, _sz, _vp]),
+    "hyf_draft_block_noalloc": (ctypes.c_int, [_P(HyfConfig), _P(HyfWeights), _vp, _i32, _vp, _i32, _vp, _vp, _vp,
+                                               _vp, _vp]),
     "hyf_linear": (ctypes.c_int, [_P(HyfConfig), _vp, _i64, _i32, _vp, _i32, _vp, _i32, _vp]),
     "hyf_linear_w4": (ctypes.c_int, [_P(HyfConfig), _vp, _i64, _i32, _vp, _vp, _i32, _vp, _i32, _vp]),
     "hyf_ssd_scan": (ctypes.c_int, [_P(HyfConfig), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _sz,
@@ -194,6 +197,14 @@ def hyf_draft_block(cfg, w: HyfWeights, pool, pool_slots, slots, n_req, commit_f
     return lib().hyf_draft_block(ctypes.byref(cfg), ctypes.byref(w), _ptr(pool), pool_slots, sp, n_req,
                                  _ptr(commit_feats), cp, _ptr(block_in), _ptr(block_out), _ptr(ws), ws_bytes,
                                  _stream(stream))
+
+
+def hyf_draft_block_noalloc(cfg, w: HyfWeights, pool, pool_slots, slots, n_req, commit_feats, cu_commit, block_in,
+                            block_out, stream=None) -> int:
+    _s, sp = _host_i32(slots)
+    _c, cp = _host_i64(cu_commit)
+    return lib().hyf_draft_block_noalloc(ctypes.byref(cfg), ctypes.byref(w), _ptr(pool), pool_slots, sp, n_req,
+                                         _ptr(commit_feats), cp, _ptr(block_in), _ptr(block_out), _stream(stream))
 
 
 def hyf_linear(cfg, X, M, K, W, Nout, out, out_f32, stream=None) -> int:

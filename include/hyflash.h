@@ -14,7 +14,8 @@
  * Conventions shared by every call
  *   - Pointers are DEVICE pointers unless marked (host).  The caller owns all memory:
  *     weights, the state pool, inputs, outputs and the workspace.  The library never
- *     allocates or frees device memory and keeps no mutable global state.
+ *     allocates or frees device memory and keeps no mutable global state (one exception:
+ *     hyf_draft_block_noalloc's per-GPU scratch array, see there).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls only
  *     enqueue work on it and return without synchronizing.
  *   - Every call returns an hyf_status.  All conditions that can be checked on the
@@ -172,6 +173,24 @@ int hyf_draft_block(const hyf_config* cfg, const hyf_weights* w, void* state_poo
                     int32_t pool_slots, const int32_t* slots, int32_t n_req,
                     const void* commit_feats, const int64_t* cu_commit, const void* block_in,
                     void* block_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Size of the device array hyf_draft_block_noalloc uses in place of a workspace (16 MiB). */
+#define HYF_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* hyf_draft_block without a workspace argument, for callers that cannot allocate device memory
+ * (code that runs under HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ * Same arguments, checks, kernels and results as hyf_draft_block (bit for bit); the workspace is a
+ * device array of HYF_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held from the first
+ * call on that GPU (with it current) until the process ends.  The call allocates and frees
+ * nothing.  Calls whose draft workspace would exceed the array (it grows with n_req and the
+ * commit rows; one request of a layer up to d_model 5120 with 40 heads of 128 fits, at the
+ * Qwen3-4B-shaped layer about ten) return HYF_ECAPACITY before any device work.  Every call on one GPU shares that GPU's array, so calls that overlap
+ * on one GPU (other streams, other threads) race: the caller orders them.  The stream must belong
+ * to the current device. */
+int hyf_draft_block_noalloc(const hyf_config* cfg, const hyf_weights* w, void* state_pool,
+                            int32_t pool_slots, const int32_t* slots, int32_t n_req,
+                            const void* commit_feats, const int64_t* cu_commit,
+                            const void* block_in, void* block_out, void* stream);
 
 /* The projection building block of the layer (explainer, "That is HyFlash": each layer
  * projects committed features and block rows; the draft step ends in an output projection):

@@ -202,3 +202,19 @@ def test_four_bit_projection_rejects_bad_calls_before_device_work():
     # the activations must be bf16
     assert hf.hyf_linear_w4(hf.make_config(I.TINY), *ok) == hf.HYF_EUNSUPPORTED
 
+
+def test_allocation_free_draft_rejects_bad_and_oversized_calls_before_device_work():
+    # The same host checks as hyf_draft_block, and HYF_ECAPACITY when the call's workspace would
+    # not fit the library's scratch array (64 Qwen3-4B-shaped requests), all before any HIP call.
+    cfg = hf.make_config(I.QWEN)
+    fake = 1 << 20
+    w = hf.HyfWeights(fake, fake, fake, fake, fake)
+    R = 64
+    assert hf.hyf_workspace_bytes(cfg, R, 8 * R) > hf.HYF_NOALLOC_SCRATCH_BYTES
+    cu = list(range(0, 8 * R + 1, 8))
+    assert hf.hyf_draft_block_noalloc(cfg, w, fake, R, None, R, fake, cu, fake, fake, 0) == hf.HYF_ECAPACITY
+    assert hf.hyf_draft_block_noalloc(cfg, w, fake, 1, None, 1, fake, [0, 9], fake, fake, 0) == hf.HYF_ECAPACITY
+    assert hf.hyf_draft_block_noalloc(cfg, w, fake, 1, None, 1, fake, None, fake, fake, 0) == hf.HYF_EINVAL
+    assert hf.hyf_draft_block_noalloc(cfg, w, fake + 8, 1, None, 1, None, None, fake, fake, 0) == hf.HYF_EINVAL
+    bad_w = hf.HyfWeights(None, fake, fake, fake, fake)
+    assert hf.hyf_draft_block_noalloc(cfg, bad_w, fake, 1, None, 1, None, None, fake, fake, 0) == hf.HYF_EINVAL
