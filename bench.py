@@ -1,18 +1,27 @@
 #!/usr/bin/env python3
 """Throughput of the HyFlash drafter-layer hot path on one MI355X.
 
-A step is one episode of the Qwen3-4B-shaped drafter layer (bf16, d_model 2560, 32 heads x 80,
-d_state 128, chunk 64, window 512, block 7 + anchor, batch 1): reset the request's state, commit
-an 8192-feature prefix (projection GEMM, ring append, chunked scan), then 256 verification
-rounds, each committing 1-8 accepted features and drafting one block (hyf_draft_block).
-All inputs are synthetic and resident in HBM before the timed region.
+Headline step: batched serving on one GPU, the largest single-GPU workload.  The Qwen3-4B-shaped
+drafter layer (bf16, d_model 2560, 32 heads x 80, d_state 128, chunk 64, window 512, block 7 +
+anchor) serves 64 requests with per-request states and rings.  A step resets the 64 states,
+commits their prefixes (U{2048..16384} features each, one hyf_memory_commit call), then runs 128
+verification rounds; in each round every request commits its 1-8 accepted features and drafts its
+block, all 64 in one hyf_draft_block call.  `value` = draft blocks/s over whole steps (prefill
+included), summed over the requests.  Inputs are seeded synthetic arrays (NumPy PCG64 streams,
+seed 3), resident in HBM before the timed region.
 
-Printed: one JSON line.  `value` = draft blocks/s per layer over whole steps (prefill included).
-Kernel-level loops time the dominant kernel (the weight-streaming input projection of a round),
-the commit scan on pre-projected inputs and the prefill projection GEMM, each with HIP events on
-the stream the kernels run on.  Six copies of the weights and of the scan inputs are rotated so
-that the working set exceeds the 256 MB last-level cache and the figures are HBM figures.
-The CPU oracle is timed on a bounded sample of the same workload on the host cores.
+`roofline` is the round's dominant kernel, k_round at this shape: algorithmic bytes per launch
+(ring windows, H read and written, the append, the projection columns it reads, its output)
+over its average duration, measured with HIP events as a graph of the 128 rounds minus a graph
+of the same rounds' two projections (the same kernels and launch shapes, run through hyf_linear).
+`round` is the whole round against its algorithmic bytes.
+
+Sub-objects: the batch-1 Qwen3-4B-shaped episode (8192-feature prefix, 256 rounds; eight
+requests' episodes interleaved and seven weight copies rotated so the figures are HBM figures),
+the Phi-4-shaped two-layer drafter (32768-feature prefix, 512 rounds), the long-context
+Phi-4-shaped layer (131072-feature prefix, chunk 256, 128 rounds; Mamba-2 and the gated delta
+rule), kernel loops (commit scan, prefill GEMM, round projections, 4-bit projections), and the
+CPU oracle's rate on a bounded sample of the headline workload.
 """
 
 from __future__ import annotations
@@ -32,8 +41,10 @@ if ROOT not in sys.path:
 METRIC = "committed feats/s (SSD commit scan) + draft blocks/s per layer; % roofline"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
-N_COPIES = 6                 # 6 x 54 MB of weights > 256 MB last-level cache
-WORKLOAD = "qwen3_4b_bf16"
+W_COPIES = 7                 # 7 x 54 MB of Qwen-shaped weights > 256 MB last-level cache
+SCAN_COPIES = 6              # 6 x 46 MB of scan inputs
+EPISODES = 8                 # interleaved batch-1 episodes (8 states of 6.6 MB)
+HEADLINE = "qwen3_4b_batched64"
 
 
 def parse():
@@ -43,15 +54,15 @@ def parse():
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--kernel-reps", type=int, default=60)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
-    p.add_argument("--profile", action="store_true", help="short run for a profiler (2 steps, few reps)")
+    p.add_argument("--profile", action="store_true", help="short run for a profiler (few steps and reps)")
     p.add_argument("--pmc-probe", action="store_true",
                    help="only the measured kernels (plus a copy of known size), for rocprofv3 --pmc runs")
     p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                    help="turn two rocprofv3 --pmc databases (FETCH_SIZE, WRITE_SIZE) of --pmc-probe runs "
-                        "into profiles/pmc_traffic.json")
+                        "into profiles/pmc_traffic.json and .md")
     p.add_argument("--stats-summary", metavar="DIR",
                    help="turn the csv output of a rocprofv3 --kernel-trace --stats run of --profile (output "
-                        "prefix 'bench') into profiles/qwen3_4b_episode_kernel_stats.md")
+                        "prefix 'bench') into profiles/bench_kernel_stats.md")
     return p.parse_args()
 
 
@@ -59,80 +70,112 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-class Episode:
-    """Device-resident inputs of one step and the precomputed C-ABI arguments."""
+# ---- inputs --------------------------------------------------------------------------------------
 
-    def __init__(self, torch, hf, I, memory="mamba2"):
-        wl = I.WORKLOADS[WORKLOAD]
-        self.shape = sh = wl["shape"].replace(memory=memory)
-        self.T, self.R = wl["prefix"], wl["rounds"]
-        d = sh.d_model
-        rng = I.rng_streams(wl["seed"])
-        w = I.make_weights(sh, rng[0])
-        prefix = I.make_rows(rng[1], self.T, d, wl["feat_scale"], sh.dtype)
-        self.acc = I.acceptance_lengths(rng[4], self.R)
-        commits = I.make_rows(rng[2], int(self.acc.sum()), d, wl["feat_scale"], sh.dtype)
-        blocks = I.make_rows(rng[3], self.R * 8, d, wl["block_scale"], sh.dtype)
-        self.host_w = w
 
-        self.cfg = hf.make_config(sh)
-        dev = "cuda"
-        self.w_in = [hf.to_device(w["w_in"], sh, dev) for _ in range(N_COPIES)]
-        self.w_out = [hf.to_device(w["w_out"], sh, dev) for _ in range(N_COPIES)]
-        self.a_log = hf.to_device(w["a_log"], sh, dev, storage=False)
-        self.dt_bias = hf.to_device(w["dt_bias"], sh, dev, storage=False)
-        self.d_skip = hf.to_device(w["d_skip"], sh, dev, storage=False)
-        self.wts = [hf.HyfWeights(self.w_in[i].data_ptr(), self.w_out[i].data_ptr(), self.a_log.data_ptr(),
-                                  self.dt_bias.data_ptr(), self.d_skip.data_ptr()) for i in range(N_COPIES)]
-        self.state_bytes = hf.hyf_state_bytes(self.cfg)
-        self.pool = torch.zeros(self.state_bytes, dtype=torch.uint8, device=dev)
-        self.ws_bytes = hf.hyf_workspace_bytes(self.cfg, 1, self.T)
-        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
-        self.prefix = hf.to_device(prefix, sh, dev)
-        self.commits = hf.to_device(commits, sh, dev)
-        self.blocks = hf.to_device(blocks, sh, dev)
-        self.out = torch.empty_like(self.blocks)
+def device_rows(torch, rng, n, d, scale, chunk=65536):
+    """n x d rows ~ N(0, 1) * scale drawn on the host from `rng` (float32, in chunks), cast to bf16
+    (round to nearest even) and placed on the device."""
+    import numpy as np
 
-        es = 2
-        self.cu_pre = (ctypes.c_int64 * 2)(0, self.T)
-        self.cu = [(ctypes.c_int64 * 2)(0, int(a)) for a in self.acc]
-        offs = [0]
-        for a in self.acc:
-            offs.append(offs[-1] + int(a))
-        cb, bb, ob = self.commits.data_ptr(), self.blocks.data_ptr(), self.out.data_ptr()
-        self.c_ptr = [ctypes.c_void_p(cb + offs[i] * d * es) for i in range(self.R)]
-        self.b_ptr = [ctypes.c_void_p(bb + i * 8 * d * es) for i in range(self.R)]
-        self.o_ptr = [ctypes.c_void_p(ob + i * 8 * d * es) for i in range(self.R)]
-        self.lib = hf.lib()
-        self.cfg_ref = ctypes.byref(self.cfg)
-        self.w_ref = [ctypes.byref(x) for x in self.wts]
-        self.pool_p = ctypes.c_void_p(self.pool.data_ptr())
-        self.ws_p = ctypes.c_void_p(self.ws.data_ptr())
-        self.pre_p = ctypes.c_void_p(self.prefix.data_ptr())
-        self.copy = 0
+    out = torch.empty((max(n, 1), d), dtype=torch.bfloat16, device="cuda")
+    for i in range(0, n, chunk):
+        m = min(chunk, n - i)
+        a = rng.standard_normal((m, d), dtype=np.float32) * np.float32(scale)
+        out[i:i + m].copy_(torch.from_numpy(a).to(torch.bfloat16))
+    return out
 
-    def step(self, stream, events=None):
-        L, s = self.lib, ctypes.c_void_p(stream)
-        if events:
-            events[0].record()
-        st = L.hyf_state_reset(self.cfg_ref, self.pool_p, 1, None, 1, s)
-        st |= L.hyf_memory_commit(self.cfg_ref, self.w_ref[self.copy], self.pool_p, 1, None, 1, self.pre_p,
-                                  self.cu_pre, None, self.ws_p, self.ws_bytes, s)
-        if events:
-            events[1].record()
-        for i in range(self.R):
-            self.copy = (self.copy + 1) % N_COPIES
-            st |= L.hyf_draft_block(self.cfg_ref, self.w_ref[self.copy], self.pool_p, 1, None, 1, self.c_ptr[i],
-                                    self.cu[i], self.b_ptr[i], self.o_ptr[i], self.ws_p, self.ws_bytes, s)
-        if events:
-            events[2].record()
-        if st:
-            raise RuntimeError(f"libhyflash call failed (status bits {st})")
+
+class Calls:
+    """Prebuilt C-ABI arguments (ctypes) so that a step's host side is a loop of library calls."""
+
+    def __init__(self, hf, cfg, weights):
+        self.L = hf.lib()
+        self.cfg = cfg
+        self.cfg_ref = ctypes.byref(cfg)
+        self.w = weights if isinstance(weights, list) else [weights]
+        self.w_ref = [ctypes.byref(x) for x in self.w]
+
+    @staticmethod
+    def i64(vals):
+        return (ctypes.c_int64 * len(vals))(*[int(v) for v in vals])
+
+
+def weights_struct(hf, w_in, w_out, a_log, dt_bias, d_skip):
+    return hf.HyfWeights(w_in.data_ptr(), w_out.data_ptr(), a_log.data_ptr(), dt_bias.data_ptr(), d_skip.data_ptr())
+
+
+def layer_weights(torch, hf, I, shape, rng, copies=1):
+    w = I.make_weights(shape, rng)
+    w_in = [hf.to_device(w["w_in"], shape) for _ in range(copies)]
+    w_out = [hf.to_device(w["w_out"], shape) for _ in range(copies)]
+    vec = [hf.to_device(w[k], shape, storage=False) for k in ("a_log", "dt_bias", "d_skip")]
+    structs = [weights_struct(hf, w_in[i], w_out[i], *vec) for i in range(copies)]
+    return w, dict(w_in=w_in, w_out=w_out, vec=vec, structs=structs)
+
+
+# ---- algorithmic bytes ---------------------------------------------------------------------------
+
+
+def kround_bytes(sh, R, rows, windows):
+    """Bytes the round kernel must move once: each request's ring window (K and V of `windows[i]`
+    slots) read, H read and written, the committed rows' k and v appended to the ring, the fp32
+    projection columns it consumes (q, C, k, v of the block rows; k, v, B, step of the committed
+    rows) and its bf16 output (the output projection's input)."""
+    es = 2
+    nh, P, N = sh.n_heads, sh.head_dim, sh.d_state
+    ring = sum(windows) * nh * P * 2 * es
+    h = 2 * R * nh * P * N * 4
+    append = rows * nh * P * 2 * es
+    proj = (8 * R * (3 * sh.dq + sh.gn) + rows * (2 * sh.dq + sh.gn + sh.n_heads)) * 4
+    out = 8 * R * sh.dq * es
+    return ring + h + append + proj + out
+
+
+def round_bytes(sh, R, rows, windows):
+    """Bytes a whole round must move once: w_in and w_out, the committed and block rows in, the
+    block rows out, the ring windows read, the append, H read and written."""
+    es = 2
+    nh, P, N, d = sh.n_heads, sh.head_dim, sh.d_state, sh.d_model
+    weights = (sh.n_in + sh.dq) * d * es
+    rows_io = (rows + 8 * R + 8 * R) * d * es
+    ring = sum(windows) * nh * P * 2 * es
+    return weights + rows_io + ring + rows * nh * P * 2 * es + 2 * R * nh * P * N * 4
+
+
+def scan_bytes(sh, T):
+    return T * (sh.n_heads * sh.head_dim * 2 + sh.gn * 2 + sh.n_heads * 4) + 2 * sh.n_heads * sh.head_dim * sh.d_state * 4
+
+
+# ---- timing --------------------------------------------------------------------------------------
+
+
+def time_graph(torch, fn, reps, replays=3, stream=None):
+    """Mean microseconds per call of `reps` calls captured in one HIP graph, replayed `replays`
+    times between HIP events recorded on the replay stream."""
+    g = torch.cuda.CUDAGraph()
+    s = stream or torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        fn(0)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        for i in range(reps):
+            fn(i)
+    with torch.cuda.stream(s):
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(replays):
+            g.replay()
+        e1.record(s)
+    torch.cuda.synchronize()
+    del g
+    return 1e3 * e0.elapsed_time(e1) / (replays * reps)
 
 
 def time_calls(torch, fn, reps):
-    """Mean milliseconds per call: HIP events on the current stream around `reps` back-to-back calls
-    (the same launches a rocprofv3 kernel trace of this loop averages)."""
+    """Mean microseconds per call: HIP events on the current stream around `reps` back-to-back calls."""
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
@@ -140,258 +183,471 @@ def time_calls(torch, fn, reps):
         fn(i)
     e1.record()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
-    return ms, ms
+    return 1e3 * e0.elapsed_time(e1) / reps
 
 
-def time_graph(torch, fn, reps, replays=3):
-    """Mean milliseconds per call of `reps` calls captured in one HIP graph, replayed `replays`
-    times between HIP events (for calls shorter than a host-side launch)."""
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for i in range(reps):
-            fn(i)
-    g.replay()
+def run_steps(torch, step, steps, warmup):
+    """Eager steps on torch's current stream; events around the prefill and the rounds of each."""
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(warmup):
+        step(stream)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(replays):
-        g.replay()
-    e1.record()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / (replays * reps)
+    w0 = time.perf_counter()
+    for k in range(steps):
+        step(stream, evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    step_ms = [e[0].elapsed_time(e[2]) for e in evs]
+    pre_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    rnd_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    mean = lambda v: sum(v) / len(v)
+    return dict(step_ms=mean(step_ms), prefill_ms=mean(pre_ms), rounds_ms=mean(rnd_ms), wall_s=wall)
 
 
-def w4_round_projections(torch, hf, I, ep, reps=96):
+def hbm(bytes_, us):
+    gbs = bytes_ / (us * 1e-6) / 1e9
+    return {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS}
+
+
+# ---- workloads -----------------------------------------------------------------------------------
+
+
+class Batched:
+    """Batched serving: 64 Qwen3-4B-shaped requests, prefixes U{2048..16384}, 128 rounds."""
+
+    def __init__(self, torch, hf, I, name=HEADLINE):
+        import numpy as np
+
+        wl = I.WORKLOADS[name]
+        self.shape = sh = wl["shape"]
+        self.R = R = wl["requests"]
+        self.rounds = wl["rounds"]
+        d = sh.d_model
+        rng = I.rng_streams(wl["seed"])
+        self.host_w, self.wd = layer_weights(torch, hf, I, sh, rng[0])
+        lo, hi = wl["prefix_range"]
+        self.lens = rng[4].integers(lo, hi + 1, size=R)
+        self.acc = rng[4].integers(1, 9, size=(self.rounds, R))
+        self.T = int(self.lens.sum())
+        log(f"batched: drawing {self.T} prefix rows")
+        self.prefix = device_rows(torch, rng[1], self.T, d, wl["feat_scale"])
+        self.commits = device_rows(torch, rng[2], int(self.acc.sum()), d, wl["feat_scale"])
+        self.blocks = device_rows(torch, rng[3], self.rounds * R * 8, d, wl["block_scale"])
+        self.out = torch.empty((R * 8, d), dtype=torch.bfloat16, device="cuda")
+        self.cfg = hf.make_config(sh)
+        self.c = Calls(hf, self.cfg, self.wd["structs"])
+        self.state_bytes = hf.hyf_state_bytes(self.cfg)
+        self.pool = torch.zeros(R * self.state_bytes, dtype=torch.uint8, device="cuda")
+        self.ws_bytes = hf.hyf_workspace_bytes(self.cfg, R, self.T)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
+        self.cu_pre = Calls.i64(np.concatenate([[0], np.cumsum(self.lens)]))
+        self.cu = [Calls.i64(np.concatenate([[0], np.cumsum(a)])) for a in self.acc]
+        offs = np.concatenate([[0], np.cumsum(self.acc.sum(axis=1))])
+        es = 2
+        self.c_ptr = [ctypes.c_void_p(self.commits.data_ptr() + int(offs[i]) * d * es) for i in range(self.rounds)]
+        self.b_ptr = [ctypes.c_void_p(self.blocks.data_ptr() + i * R * 8 * d * es) for i in range(self.rounds)]
+        self.pool_p, self.ws_p = ctypes.c_void_p(self.pool.data_ptr()), ctypes.c_void_p(self.ws.data_ptr())
+        self.pre_p, self.out_p = ctypes.c_void_p(self.prefix.data_ptr()), ctypes.c_void_p(self.out.data_ptr())
+        self.windows = [min(int(n), sh.window) for n in self.lens]
+
+    def reset_and_prefill(self, s):
+        L, c = self.c.L, self.c
+        st = L.hyf_state_reset(c.cfg_ref, self.pool_p, self.R, None, self.R, s)
+        st |= L.hyf_memory_commit(c.cfg_ref, c.w_ref[0], self.pool_p, self.R, None, self.R, self.pre_p, self.cu_pre,
+                                  None, self.ws_p, self.ws_bytes, s)
+        return st
+
+    def round(self, i, s):
+        c = self.c
+        return c.L.hyf_draft_block(c.cfg_ref, c.w_ref[0], self.pool_p, self.R, None, self.R, self.c_ptr[i], self.cu[i],
+                                   self.b_ptr[i], self.out_p, self.ws_p, self.ws_bytes, s)
+
+    def step(self, stream, ev=None):
+        s = ctypes.c_void_p(stream)
+        if ev:
+            ev[0].record()
+        st = self.reset_and_prefill(s)
+        if ev:
+            ev[1].record()
+        for i in range(self.rounds):
+            st |= self.round(i, s)
+        if ev:
+            ev[2].record()
+        if st:
+            raise RuntimeError(f"libhyflash call failed (status bits {st})")
+
+    def round_kernel(self, torch, hf, nr=None):
+        """Per-round microseconds of the rounds (graph) and of their two projections alone (graph of
+        hyf_linear calls with the same shapes), and the round kernel's share (the difference)."""
+        import numpy as np
+
+        nr = nr or self.rounds
+        sh, R, d = self.shape, self.R, self.shape.d_model
+        st = [0]
+        stream = torch.cuda.Stream()
+
+        def rounds(i):
+            st[0] |= self.round(i % self.rounds, ctypes.c_void_p(stream.cuda_stream))
+
+        t_round = time_graph(torch, rounds, nr, stream=stream)
+        M = [int(self.acc[i % self.rounds].sum()) + 8 * R for i in range(nr)]
+        y = torch.empty((max(M), sh.n_in), dtype=torch.float32, device="cuda")
+        xo = torch.empty((8 * R, sh.dq), dtype=torch.bfloat16, device="cuda").normal_()
+        xin = torch.empty((max(M), d), dtype=torch.bfloat16, device="cuda").normal_()
+
+        def projs(i):
+            s = stream.cuda_stream
+            st[0] |= hf.hyf_linear(self.cfg, xin, M[i], d, self.wd["w_in"][0], sh.n_in, y, 1, s)
+            st[0] |= hf.hyf_linear(self.cfg, xo, 8 * R, sh.dq, self.wd["w_out"][0], d, self.out, 0, s)
+
+        t_proj = time_graph(torch, projs, nr, stream=stream)
+        if st[0]:
+            raise RuntimeError(f"round kernel timing failed (status bits {st[0]})")
+        rows = float(np.mean(self.acc[:nr].sum(axis=1)))
+        return t_round, t_proj, rows
+
+
+class EpisodesB1:
+    """The batch-1 Qwen3-4B-shaped episode (8192-feature prefix commit, 256 rounds), EPISODES
+    requests' episodes interleaved (each call is batch 1, on its own state) with W_COPIES weight
+    copies rotated call by call, so weights and states come from HBM."""
+
+    def __init__(self, torch, hf, I, name="qwen3_4b_bf16", memory="mamba2"):
+        import numpy as np
+
+        wl = I.WORKLOADS[name]
+        self.shape = sh = wl["shape"].replace(memory=memory)
+        self.T, self.rounds = wl["prefix"], wl["rounds"]
+        d = sh.d_model
+        rng = I.rng_streams(wl["seed"])
+        self.host_w, self.wd = layer_weights(torch, hf, I, sh, rng[0], copies=W_COPIES)
+        self.prefix = device_rows(torch, rng[1], self.T, d, wl["feat_scale"])
+        self.acc = rng[4].integers(1, 9, size=self.rounds)
+        self.commits = device_rows(torch, rng[2], int(self.acc.sum()), d, wl["feat_scale"])
+        self.blocks = device_rows(torch, rng[3], self.rounds * 8, d, wl["block_scale"])
+        self.out = torch.empty((8, d), dtype=torch.bfloat16, device="cuda")
+        self.cfg = hf.make_config(sh)
+        self.c = Calls(hf, self.cfg, self.wd["structs"])
+        self.state_bytes = hf.hyf_state_bytes(self.cfg)
+        self.pool = torch.zeros(EPISODES * self.state_bytes, dtype=torch.uint8, device="cuda")
+        self.ws_bytes = hf.hyf_workspace_bytes(self.cfg, 1, self.T)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
+        self.cu_pre = Calls.i64([0, self.T])
+        self.cu = [Calls.i64([0, a]) for a in self.acc]
+        offs = np.concatenate([[0], np.cumsum(self.acc)])
+        es = 2
+        self.c_ptr = [ctypes.c_void_p(self.commits.data_ptr() + int(offs[i]) * d * es) for i in range(self.rounds)]
+        self.b_ptr = [ctypes.c_void_p(self.blocks.data_ptr() + i * 8 * d * es) for i in range(self.rounds)]
+        self.slots = [(ctypes.c_int32 * 1)(e) for e in range(EPISODES)]
+        self.pool_p, self.ws_p = ctypes.c_void_p(self.pool.data_ptr()), ctypes.c_void_p(self.ws.data_ptr())
+        self.pre_p, self.out_p = ctypes.c_void_p(self.prefix.data_ptr()), ctypes.c_void_p(self.out.data_ptr())
+        self.k = 0
+
+    def round(self, e, i, s):
+        c = self.c
+        self.k = (self.k + 1) % W_COPIES
+        return c.L.hyf_draft_block(c.cfg_ref, c.w_ref[self.k], self.pool_p, EPISODES, self.slots[e], 1, self.c_ptr[i],
+                                   self.cu[i], self.b_ptr[i], self.out_p, self.ws_p, self.ws_bytes, s)
+
+    def step(self, stream, ev=None):
+        L, c = self.c.L, self.c
+        s = ctypes.c_void_p(stream)
+        if ev:
+            ev[0].record()
+        st = L.hyf_state_reset(c.cfg_ref, self.pool_p, EPISODES, None, EPISODES, s)
+        for e in range(EPISODES):
+            self.k = (self.k + 1) % W_COPIES
+            st |= L.hyf_memory_commit(c.cfg_ref, c.w_ref[self.k], self.pool_p, EPISODES, self.slots[e], 1, self.pre_p,
+                                      self.cu_pre, None, self.ws_p, self.ws_bytes, s)
+        if ev:
+            ev[1].record()
+        for i in range(self.rounds):
+            for e in range(EPISODES):
+                st |= self.round(e, i, s)
+        if ev:
+            ev[2].record()
+        if st:
+            raise RuntimeError(f"libhyflash call failed (status bits {st})")
+
+    def round_kernel(self, torch, hf, nr=64):
+        """As Batched.round_kernel, for batch-1 rounds over the interleaved states."""
+        sh, d = self.shape, self.shape.d_model
+        st = [0]
+        stream = torch.cuda.Stream()
+
+        def rounds(i):
+            st[0] |= self.round(i % EPISODES, (i // EPISODES) % self.rounds, ctypes.c_void_p(stream.cuda_stream))
+
+        t_round = time_graph(torch, rounds, nr, stream=stream)
+        M = [int(self.acc[(i // EPISODES) % self.rounds]) + 8 for i in range(nr)]
+        y = torch.empty((16, sh.n_in), dtype=torch.float32, device="cuda")
+        xo = torch.empty((8, sh.dq), dtype=torch.bfloat16, device="cuda").normal_()
+        xin = torch.empty((16, d), dtype=torch.bfloat16, device="cuda").normal_()
+        kk = [0]
+
+        def projs(i):
+            s = stream.cuda_stream
+            kk[0] = (kk[0] + 1) % W_COPIES
+            st[0] |= hf.hyf_linear(self.cfg, xin, M[i], d, self.wd["w_in"][kk[0]], sh.n_in, y, 1, s)
+            st[0] |= hf.hyf_linear(self.cfg, xo, 8, sh.dq, self.wd["w_out"][kk[0]], d, self.out, 0, s)
+
+        t_proj = time_graph(torch, projs, nr, stream=stream)
+        if st[0]:
+            raise RuntimeError(f"round kernel timing failed (status bits {st[0]})")
+        rows = sum(M) / len(M) - 8
+        return t_round, t_proj, rows
+
+
+class TwoLayerPhi4:
+    """The Phi-4-shaped two-layer drafter: both layers commit the 32768-feature prefix, then 512
+    rounds; in each, both layers commit the round's accepted features, layer 1 drafts the block and
+    layer 2 drafts from block_in + layer 1's output (the residual add between the two calls is the
+    caller's, in torch: the layer ends at its output projection)."""
+
+    def __init__(self, torch, hf, I, name="phi4_bf16_2layer"):
+        import numpy as np
+
+        wl = I.WORKLOADS[name]
+        self.shape = sh = wl["shape"]
+        self.T, self.rounds = wl["prefix"], wl["rounds"]
+        d = sh.d_model
+        rng = I.rng_streams(wl["seed"])
+        self.layers = [layer_weights(torch, hf, I, sh, rng[0])[1], layer_weights(torch, hf, I, sh, rng[5])[1]]
+        self.prefix = device_rows(torch, rng[1], self.T, d, wl["feat_scale"])
+        self.acc = rng[4].integers(1, 9, size=self.rounds)
+        self.commits = device_rows(torch, rng[2], int(self.acc.sum()), d, wl["feat_scale"])
+        self.blocks = device_rows(torch, rng[3], self.rounds * 8, d, wl["block_scale"])
+        self.o1 = torch.empty((8, d), dtype=torch.bfloat16, device="cuda")
+        self.x2 = torch.empty((8, d), dtype=torch.bfloat16, device="cuda")
+        self.o2 = torch.empty((8, d), dtype=torch.bfloat16, device="cuda")
+        self.cfg = hf.make_config(sh)
+        self.c = Calls(hf, self.cfg, [x["structs"][0] for x in self.layers])
+        self.state_bytes = hf.hyf_state_bytes(self.cfg)
+        self.pool = torch.zeros(2 * self.state_bytes, dtype=torch.uint8, device="cuda")
+        self.ws_bytes = hf.hyf_workspace_bytes(self.cfg, 1, self.T)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
+        self.cu_pre = Calls.i64([0, self.T])
+        self.cu = [Calls.i64([0, a]) for a in self.acc]
+        offs = np.concatenate([[0], np.cumsum(self.acc)])
+        es = 2
+        self.c_ptr = [ctypes.c_void_p(self.commits.data_ptr() + int(offs[i]) * d * es) for i in range(self.rounds)]
+        self.b = [self.blocks[8 * i: 8 * i + 8] for i in range(self.rounds)]
+        self.slots = [(ctypes.c_int32 * 1)(e) for e in range(2)]
+        self.pool_p, self.ws_p = ctypes.c_void_p(self.pool.data_ptr()), ctypes.c_void_p(self.ws.data_ptr())
+        self.pre_p = ctypes.c_void_p(self.prefix.data_ptr())
+        self.p = [ctypes.c_void_p(t.data_ptr()) for t in (self.o1, self.x2, self.o2)]
+
+    def step(self, stream, ev=None):
+        L, c = self.c.L, self.c
+        s = ctypes.c_void_p(stream)
+        if ev:
+            ev[0].record()
+        st = L.hyf_state_reset(c.cfg_ref, self.pool_p, 2, None, 2, s)
+        for li in range(2):
+            st |= L.hyf_memory_commit(c.cfg_ref, c.w_ref[li], self.pool_p, 2, self.slots[li], 1, self.pre_p,
+                                      self.cu_pre, None, self.ws_p, self.ws_bytes, s)
+        if ev:
+            ev[1].record()
+        for i in range(self.rounds):
+            bp = ctypes.c_void_p(self.b[i].data_ptr())
+            st |= L.hyf_draft_block(c.cfg_ref, c.w_ref[0], self.pool_p, 2, self.slots[0], 1, self.c_ptr[i], self.cu[i],
+                                    bp, self.p[0], self.ws_p, self.ws_bytes, s)
+            self.x2.copy_(self.b[i])
+            self.x2.add_(self.o1)
+            st |= L.hyf_draft_block(c.cfg_ref, c.w_ref[1], self.pool_p, 2, self.slots[1], 1, self.c_ptr[i], self.cu[i],
+                                    self.p[1], self.p[2], self.ws_p, self.ws_bytes, s)
+        if ev:
+            ev[2].record()
+        if st:
+            raise RuntimeError(f"libhyflash call failed (status bits {st})")
+
+
+class LongPhi4:
+    """The long-context Phi-4-shaped layer: chunk 256, a 131072-feature prefix commit, 128 rounds."""
+
+    def __init__(self, torch, hf, I, memory="mamba2", name="phi4_long131k", prefix_dev=None):
+        import numpy as np
+
+        wl = I.WORKLOADS[name]
+        self.shape = sh = wl["shape"].replace(memory=memory)
+        self.T, self.rounds = wl["prefix"], wl["rounds"]
+        d = sh.d_model
+        rng = I.rng_streams(wl["seed"])
+        self.host_w, self.wd = layer_weights(torch, hf, I, sh, rng[0])
+        self.prefix = prefix_dev if prefix_dev is not None else device_rows(torch, rng[1], self.T, d, wl["feat_scale"])
+        self.acc = rng[4].integers(1, 9, size=self.rounds)
+        self.commits = device_rows(torch, rng[2], int(self.acc.sum()), d, wl["feat_scale"])
+        self.blocks = device_rows(torch, rng[3], self.rounds * 8, d, wl["block_scale"])
+        self.out = torch.empty((8, d), dtype=torch.bfloat16, device="cuda")
+        self.cfg = hf.make_config(sh)
+        self.c = Calls(hf, self.cfg, self.wd["structs"])
+        self.state_bytes = hf.hyf_state_bytes(self.cfg)
+        self.pool = torch.zeros(self.state_bytes, dtype=torch.uint8, device="cuda")
+        self.ws_bytes = hf.hyf_workspace_bytes(self.cfg, 1, self.T)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
+        self.cu_pre = Calls.i64([0, self.T])
+        self.cu = [Calls.i64([0, a]) for a in self.acc]
+        offs = np.concatenate([[0], np.cumsum(self.acc)])
+        es = 2
+        self.c_ptr = [ctypes.c_void_p(self.commits.data_ptr() + int(offs[i]) * d * es) for i in range(self.rounds)]
+        self.b_ptr = [ctypes.c_void_p(self.blocks.data_ptr() + i * 8 * d * es) for i in range(self.rounds)]
+        self.pool_p, self.ws_p = ctypes.c_void_p(self.pool.data_ptr()), ctypes.c_void_p(self.ws.data_ptr())
+        self.pre_p, self.out_p = ctypes.c_void_p(self.prefix.data_ptr()), ctypes.c_void_p(self.out.data_ptr())
+
+    def step(self, stream, ev=None):
+        L, c = self.c.L, self.c
+        s = ctypes.c_void_p(stream)
+        if ev:
+            ev[0].record()
+        st = L.hyf_state_reset(c.cfg_ref, self.pool_p, 1, None, 1, s)
+        st |= L.hyf_memory_commit(c.cfg_ref, c.w_ref[0], self.pool_p, 1, None, 1, self.pre_p, self.cu_pre, None,
+                                  self.ws_p, self.ws_bytes, s)
+        if ev:
+            ev[1].record()
+        for i in range(self.rounds):
+            st |= c.L.hyf_draft_block(c.cfg_ref, c.w_ref[0], self.pool_p, 1, None, 1, self.c_ptr[i], self.cu[i],
+                                      self.b_ptr[i], self.out_p, self.ws_p, self.ws_bytes, s)
+        if ev:
+            ev[2].record()
+        if st:
+            raise RuntimeError(f"libhyflash call failed (status bits {st})")
+
+
+# ---- kernel loops --------------------------------------------------------------------------------
+
+
+def scan_loop(torch, hf, I, shape, T, copies, reps, seed):
+    """hyf_ssd_scan (state only) on pre-projected, time-blocked inputs x, B, dt_raw ~ N(0, 1),
+    `copies` copies rotated; returns mean microseconds per call and the algorithmic bytes."""
+    nh, P, N = shape.n_heads, shape.head_dim, shape.d_state
+    cfg = hf.make_config(shape)
+    nb = (T + 127) // 128
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    cp = [dict(x=torch.randn(nb * nh * P * 128, generator=gen, device="cuda").to(torch.bfloat16),
+               B=torch.randn(nb * shape.gn * 128, generator=gen, device="cuda").to(torch.bfloat16),
+               dt=torch.randn(nb * nh * 128, generator=gen, device="cuda"),
+               H=torch.zeros((nh, P, N), device="cuda")) for _ in range(copies)]
+    a_log = torch.rand(nh, generator=gen, device="cuda") * math.log(16.0)
+    dt_bias = torch.full((nh,), -2.0, device="cuda")
+    d_skip = torch.ones(nh, device="cuda")
+    wsb = hf.hyf_ssd_scan_workspace_bytes(cfg, T)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    st = [0]
+
+    def scan(i):
+        c = cp[i % copies]
+        st[0] |= hf.hyf_ssd_scan(cfg, c["x"], c["B"], None, c["dt"], a_log, dt_bias, d_skip, c["H"], None, T, ws, wsb)
+
+    scan(0)
+    us = time_calls(torch, scan, reps)
+    if st[0]:
+        raise RuntimeError("scan loop failed")
+    del cp, ws
+    torch.cuda.empty_cache()
+    return us, scan_bytes(shape, T)
+
+
+def scan_y_loop(torch, hf, I, shape, T, reps):
+    """hyf_ssd_scan with per-token outputs (C in, y out)."""
+    nh, P, N = shape.n_heads, shape.head_dim, shape.d_state
+    cfg = hf.make_config(shape)
+    sc = I.make_scan_inputs(shape, T, I.rng_streams(101)[0], with_c=True, h0_scale=0.0)
+    eb = hf.elem_bytes(shape)
+    x = hf.to_device(hf.time_tiled(sc["x"], T, eb), shape)
+    B = hf.to_device(hf.time_tiled(sc["B"], T, eb), shape)
+    C = hf.to_device(hf.time_tiled(sc["C"], T, eb), shape)
+    dt = torch.from_numpy(hf.time_blocked(sc["dt_raw"], T)).cuda()
+    v = [torch.from_numpy(sc[k]).cuda() for k in ("a_log", "dt_bias", "d_skip")]
+    H = torch.zeros((nh, P, N), device="cuda")
+    y = torch.empty((T, nh, P), dtype=torch.bfloat16, device="cuda")
+    wsb = hf.hyf_ssd_scan_workspace_bytes(cfg, T, 1)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    st = [0]
+
+    def scan(i):
+        st[0] |= hf.hyf_ssd_scan(cfg, x, B, C, dt, *v, H, y, T, ws, wsb)
+
+    scan(0)
+    us = time_calls(torch, scan, reps)
+    if st[0]:
+        raise RuntimeError("y-mode scan loop failed")
+    return us, scan_bytes(shape, T) + T * (shape.gn * 2 + nh * P * 2)
+
+
+def gemm_loop(torch, hf, shape, M, reps, copies=2):
+    """The prefill projection GEMM of v | B | dt over M rows (hyf_linear, tiled time-blocked output
+    is not needed here: plain bf16 output), `copies` weight copies rotated."""
+    d = shape.d_model
+    nout = shape.dq + shape.gn + shape.n_heads
+    cfg = hf.make_config(shape)
+    X = torch.empty((M, d), dtype=torch.bfloat16, device="cuda").normal_()
+    W = [torch.empty((nout, d), dtype=torch.bfloat16, device="cuda").normal_() for _ in range(copies)]
+    out = torch.empty((M, nout), dtype=torch.bfloat16, device="cuda")
+    st = [0]
+
+    def gemm(i):
+        st[0] |= hf.hyf_linear(cfg, X, M, d, W[i % copies], nout, out, 0)
+
+    gemm(0)
+    us = time_calls(torch, gemm, reps)
+    if st[0]:
+        raise RuntimeError("gemm loop failed")
+    flops = 2.0 * M * d * nout
+    tf = flops / (us * 1e-6) / 1e12
+    return {"M": M, "K": d, "N": nout, "avg_us": us, "tflops": tf,
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tf / BF16_PEAK_TFLOPS}}
+
+
+def proj_loop(torch, hf, shape, M, K, N, reps):
+    """A round projection (M rows, hyf_linear, fp32 output) with W_COPIES weight copies rotated."""
+    cfg = hf.make_config(shape)
+    X = torch.empty((M, K), dtype=torch.bfloat16, device="cuda").normal_()
+    W = [torch.empty((N, K), dtype=torch.bfloat16, device="cuda").normal_() for _ in range(W_COPIES)]
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    st = [0]
+
+    def proj(i):
+        st[0] |= hf.hyf_linear(cfg, X, M, K, W[i % W_COPIES], N, y, 1)
+
+    proj(0)
+    us = time_graph(torch, proj, W_COPIES * max(1, reps // W_COPIES))
+    if st[0]:
+        raise RuntimeError("projection loop failed")
+    b = N * K * 2 + M * K * 2 + M * N * 4
+    return {"rows": M, "K": K, "N": N, "avg_us": us, "bytes_per_launch": b, **hbm(b, us)}
+
+
+def w4_projections(torch, hf, shape, reps=96):
     """The round's two projections (12 rows x w_in, 8 rows x w_out) with 4-bit weights
-    (hyf_linear_w4) beside the bf16 ones (hyf_linear), each timed in a captured graph over enough
-    rotated weight copies to exceed the 256 MB last-level cache.  Codes are random bytes, scales
-    N(0,1)-sized; the timing does not depend on their values."""
-    sh, cfg = ep.shape, ep.cfg
+    (hyf_linear_w4) beside the bf16 ones, each graph-timed over rotated weight copies."""
+    cfg = hf.make_config(shape)
     gen = torch.Generator(device="cuda")
     gen.manual_seed(4)
     st = [0]
     res = {}
-    for name, M, K, N in (("w_in", 12, sh.d_model, sh.n_in), ("w_out", 8, sh.dq, sh.d_model)):
+    for name, M, K, N in (("w_in", 12, shape.d_model, shape.n_in), ("w_out", 8, shape.dq, shape.d_model)):
         X = torch.randn((M, K), device="cuda", generator=gen).to(torch.bfloat16)
         y = torch.empty((M, N), dtype=torch.float32, device="cuda")
-        w4_bytes = N * K // 2 + N * (K // 128) * 4
-        n4 = max(2, math.ceil(320e6 / w4_bytes))
-        codes = [torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device="cuda", generator=gen)
-                 for _ in range(n4)]
+        w4b = N * K // 2 + N * (K // 128) * 4
+        n4 = max(2, math.ceil(320e6 / w4b))
+        codes = [torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device="cuda", generator=gen) for _ in range(n4)]
         scales = [torch.rand((N, K // 128), device="cuda", generator=gen) / (7.0 * math.sqrt(K)) for _ in range(n4)]
 
         def w4(i):
             st[0] |= hf.hyf_linear_w4(cfg, X, M, K, codes[i % n4], scales[i % n4], N, y, 1)
 
-        w4(0)
-        us4 = 1e3 * time_graph(torch, w4, n4 * max(1, reps // n4))
+        us4 = time_graph(torch, w4, n4 * max(1, reps // n4))
         del codes, scales
-        nb = max(2, math.ceil(320e6 / (N * K * 2)))
-        wb = [torch.randn((N, K), device="cuda", generator=gen).to(torch.bfloat16) for _ in range(nb)]
-
-        def b16(i):
-            st[0] |= hf.hyf_linear(cfg, X, M, K, wb[i % nb], N, y, 1)
-
-        b16(0)
-        usb = 1e3 * time_graph(torch, b16, nb * max(1, reps // nb))
-        del wb
-        byt = w4_bytes + M * K * 2 + M * N * 4
-        res[name] = {"rows": M, "K": K, "N": N, "w4_us": us4, "bf16_us": usb, "speedup": usb / us4,
-                     "bytes_per_launch": byt, "achieved_gbs": byt / (us4 * 1e-6) / 1e9,
-                     "frac": byt / (us4 * 1e-6) / 1e9 / HBM_PEAK_GBS,
-                     "traffic": pmc_traffic("w4") if name == "w_in" else None}
+        byt = w4b + M * K * 2 + M * N * 4
+        res[name] = {"rows": M, "K": K, "N": N, "w4_us": us4, "bytes_per_launch": byt, **hbm(byt, us4)}
     if st[0]:
         raise RuntimeError(f"projection call failed: status {st[0]}")
     torch.cuda.empty_cache()
-    res["note"] = ("weight-only 4-bit codes (128-wide groups, fp32 scales) against bf16 weights, "
-                   "graph-timed; the layer entry points still take bf16 weights")
     return res
-
-
-def batched_serving(torch, hf, I, rounds=16):
-    """Batched serving on one GPU at the Qwen3-4B layer shape: 64 requests with prefixes of
-    U{2048..16384} committed features (per-request states and rings in one pool), then rounds in
-    which every request commits 1-8 accepted features and drafts its block, all 64 in one call.
-    Weights Xavier-normal from the workload's seed; features ~ N(0, 1)/sqrt(d) drawn on the device
-    from a fixed seed (about 0.6 M prefix rows do not fit a quick host draw)."""
-    import numpy as np
-
-    wl = I.WORKLOADS["qwen3_4b_batched64"]
-    sh, R = wl["shape"], wl["requests"]
-    d, nh, P, N, W = sh.d_model, sh.n_heads, sh.head_dim, sh.d_state, sh.window
-    rng = I.rng_streams(wl["seed"])
-    w = I.make_weights(sh, rng[0])
-    lo, hi = wl["prefix_range"]
-    lens = rng[1].integers(lo, hi + 1, size=R)
-    acc = rng[4].integers(1, 9, size=(rounds, R))
-    cfg = hf.make_config(sh)
-    w_in, w_out = hf.to_device(w["w_in"], sh), hf.to_device(w["w_out"], sh)
-    a_log = hf.to_device(w["a_log"], sh, storage=False)
-    dt_bias = hf.to_device(w["dt_bias"], sh, storage=False)
-    d_skip = hf.to_device(w["d_skip"], sh, storage=False)
-    wts = hf.HyfWeights(w_in.data_ptr(), w_out.data_ptr(), a_log.data_ptr(), dt_bias.data_ptr(), d_skip.data_ptr())
-    T = int(lens.sum())
-    pool = torch.zeros(R * hf.hyf_state_bytes(cfg), dtype=torch.uint8, device="cuda")
-    wsb = hf.hyf_workspace_bytes(cfg, R, T)
-    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
-    gen = torch.Generator(device="cuda")
-    gen.manual_seed(wl["seed"])
-    scale = wl["feat_scale"]
-    prefix = (torch.randn(T, d, generator=gen, device="cuda") * scale).to(torch.bfloat16)
-    commits = (torch.randn(int(acc.sum()), d, generator=gen, device="cuda") * scale).to(torch.bfloat16)
-    blocks = (torch.randn(rounds, R * 8, d, generator=gen, device="cuda") * wl["block_scale"]).to(torch.bfloat16)
-    out = torch.empty(R * 8, d, dtype=torch.bfloat16, device="cuda")
-    cu_pre = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
-    st = hf.hyf_state_reset(cfg, pool, R, None, R)
-    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    e[0].record()
-    st |= hf.hyf_memory_commit(cfg, wts, pool, R, None, R, prefix, cu_pre, None, ws, wsb)
-    e[1].record()
-    off = 0
-    for i in range(rounds):
-        cu = np.concatenate([[0], np.cumsum(acc[i])]).astype(np.int64)
-        cptr = commits.data_ptr() + off * d * 2
-        off += int(acc[i].sum())
-        st |= hf.hyf_draft_block(cfg, wts, pool, R, None, R, cptr, cu, blocks[i], out, ws, wsb)
-    e[2].record()
-    torch.cuda.synchronize()
-    if st:
-        raise RuntimeError(f"batched serving call failed (status bits {st})")
-    pre_ms, rnd_ms = e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])
-    round_us = 1e3 * rnd_ms / rounds
-    # bytes of one round, each counted once: the full windows (K and V), H read and written, the
-    # weights, the committed and block rows in, the block rows out
-    a_mean = float(acc.mean())
-    rbytes = (R * nh * W * P * 2 * 2 + 2 * R * nh * P * N * 4 + (sh.n_in + d) * d * 2
-              + R * (a_mean + 8) * d * 2 + R * 8 * d * 2)
-    return {"requests": R, "prefix_rows": T, "rounds": rounds, "prefill_commit_us": 1e3 * pre_ms,
-            "round_us": round_us, "draft_blocks_per_s": R * rounds / (rnd_ms * 1e-3),
-            "roofline": {"bound": "hbm", "achieved": rbytes / (round_us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": rbytes / (round_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-                         "bytes_per_round": rbytes},
-            "note": "eager rounds, 64 requests per call; blocks/s counts every request's block"}
-
-
-def scan_y_loop(torch, hf, I, ep, reps, scan_in, sbytes, st, out):
-    """The commit scan with per-token outputs y (C in, y out), on the kernel loop's scan inputs."""
-    sh, cfg, T = ep.shape, ep.cfg, ep.T
-    nh, P = sh.n_heads, sh.head_dim
-    sc_c = I.make_scan_inputs(sh, T, I.rng_streams(101)[0], with_c=True, h0_scale=0.0)
-    CT = hf.to_device(hf.time_tiled(sc_c["C"], T, hf.elem_bytes(sh)), sh)
-    y = torch.empty((T, nh, P), dtype=torch.bfloat16, device="cuda")
-    wsy = hf.hyf_ssd_scan_workspace_bytes(cfg, T, 1)
-    wy = torch.empty(wsy, dtype=torch.uint8, device="cuda")
-
-    def scan_y(i):
-        c = scan_in[i % N_COPIES]
-        st[0] |= hf.hyf_ssd_scan(cfg, c["x"], c["B"], CT, c["dt"], ep.a_log, ep.dt_bias, ep.d_skip, c["H"],
-                                 y, T, wy, wsy)
-
-    scan_y(0)
-    mean_ms, med_ms = time_calls(torch, scan_y, max(4, reps // 4))
-    ybytes = sbytes + T * (sh.gn * 2 + nh * P * 2)
-    out["scan_y"] = dict(mean_us=mean_ms * 1e3, median_us=med_ms * 1e3, bytes=ybytes,
-                         gbs=ybytes / (mean_ms * 1e-3) / 1e9, feats_per_s=T / (mean_ms * 1e-3))
-
-
-def scan_long_loop(torch, hf, I, ep, reps, st, out, T=131072):
-    """The state-only commit scan over a 131072-token prefix at the layer's shape (the long-context
-    prefill length), x, B, dt_raw ~ N(0, 1) drawn on the device from a fixed seed; two copies
-    (each larger than the last-level cache) alternate."""
-    sh, cfg = ep.shape, ep.cfg
-    nh, P, N = sh.n_heads, sh.head_dim, sh.d_state
-    nb = (T + 127) // 128
-    gen = torch.Generator(device="cuda")
-    gen.manual_seed(T)
-    copies = []
-    for _ in range(2):
-        copies.append(dict(
-            x=torch.randn(nb * nh * P * 128, generator=gen, device="cuda").to(torch.bfloat16),
-            B=torch.randn(nb * sh.gn * 128, generator=gen, device="cuda").to(torch.bfloat16),
-            dt=torch.randn(nb * nh * 128, generator=gen, device="cuda"),
-            H=torch.zeros((nh, P, N), device="cuda")))
-    wsb = hf.hyf_ssd_scan_workspace_bytes(cfg, T)
-    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
-
-    def scan(i):
-        c = copies[i % 2]
-        st[0] |= hf.hyf_ssd_scan(cfg, c["x"], c["B"], None, c["dt"], ep.a_log, ep.dt_bias, ep.d_skip, c["H"],
-                                 None, T, ws, wsb)
-
-    scan(0)
-    mean_ms, med_ms = time_calls(torch, scan, max(4, reps // 6))
-    sbytes = T * (nh * P * 2 + sh.gn * 2 + nh * 4) + 2 * nh * P * N * 4
-    out["scan_long"] = dict(T=T, mean_us=mean_ms * 1e3, median_us=med_ms * 1e3, bytes=sbytes,
-                            gbs=sbytes / (mean_ms * 1e-3) / 1e9, feats_per_s=T / (mean_ms * 1e-3))
-    del copies, ws
-
-
-def kernel_loops(torch, hf, I, ep, reps, with_gemm=True, with_y=True):
-    sh = ep.shape
-    d, nh, P, N = sh.d_model, sh.n_heads, sh.head_dim, sh.d_state
-    cfg = ep.cfg
-    out = {}
-    # 1. input projection of a round: the weight-streaming kernel, 12 rows (a = 4 committed + 8 block)
-    M = 12
-    X = ep.blocks[:M]
-    y = torch.empty((M, sh.n_in), dtype=torch.float32, device="cuda")
-    st = [0]
-
-    def proj(i):
-        st[0] |= hf.hyf_linear(cfg, X, M, d, ep.w_in[i % N_COPIES], sh.n_in, y, 1)
-
-    proj(0)
-    mean_ms, med_ms = time_calls(torch, proj, reps)
-    bytes_ = sh.n_in * d * 2 + M * d * 2 + M * sh.n_in * 4
-    out["proj"] = dict(mean_us=mean_ms * 1e3, median_us=med_ms * 1e3, bytes=bytes_,
-                       gbs=bytes_ / (mean_ms * 1e-3) / 1e9)
-    # 2. commit scan on pre-projected inputs (x, B, dt_raw), T = prefix, rotated copies
-    T = ep.T
-    sc = I.make_scan_inputs(sh, T, I.rng_streams(100)[0], with_c=False, h0_scale=0.0)
-    # time-blocked operands, the layout the prefill GEMM hands the scan
-    xT = hf.to_device(hf.time_tiled(sc["x"], T, hf.elem_bytes(sh)), sh)
-    BT = hf.to_device(hf.time_tiled(sc["B"], T, hf.elem_bytes(sh)), sh)
-    dtT = torch.from_numpy(hf.time_blocked(sc["dt_raw"], T)).cuda()
-    scan_in = [dict(x=xT.clone(), B=BT.clone(), dt=dtT.clone(), H=torch.zeros((nh, P, N), device="cuda"))
-               for _ in range(N_COPIES)]
-    wsb = hf.hyf_ssd_scan_workspace_bytes(cfg, T)
-    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
-
-    def scan(i):
-        c = scan_in[i % N_COPIES]
-        st[0] |= hf.hyf_ssd_scan(cfg, c["x"], c["B"], None, c["dt"], ep.a_log, ep.dt_bias, ep.d_skip, c["H"],
-                                 None, T, ws, wsb)
-
-    scan(0)
-    mean_ms, med_ms = time_calls(torch, scan, reps)
-    sbytes = T * (nh * P * 2 + sh.gn * 2 + nh * 4) + 2 * nh * P * N * 4
-    out["scan"] = dict(mean_us=mean_ms * 1e3, median_us=med_ms * 1e3, bytes=sbytes,
-                       gbs=sbytes / (mean_ms * 1e-3) / 1e9, feats_per_s=T / (mean_ms * 1e-3))
-    if not with_gemm:
-        return out
-    if with_y:
-        scan_y_loop(torch, hf, I, ep, reps, scan_in, sbytes, st, out)
-    # 3. prefill projection GEMM (v | B | dt columns over the whole prefix)
-    nvbd = sh.dq + sh.gn + nh
-    g = torch.empty((T, nvbd), dtype=torch.bfloat16, device="cuda")
-    off = (sh.in_groups["v"][0]) * d * 2
-
-    def gemm(i):
-        st[0] |= hf.hyf_linear(cfg, ep.prefix, T, d, ep.w_in[i % N_COPIES].data_ptr() + off, nvbd, g, 0)
-
-    gemm(0)
-    mean_ms, med_ms = time_calls(torch, gemm, max(4, reps // 6))
-    flops = 2.0 * T * d * nvbd
-    gbytes = (T * d + nvbd * d + T * nvbd) * 2  # rows, weights and outputs (bf16), each once
-    out["gemm"] = dict(mean_us=mean_ms * 1e3, median_us=med_ms * 1e3, flops=flops, bytes=gbytes,
-                       tflops=flops / (mean_ms * 1e-3) / 1e12)
-    if with_y:
-        # last: its two 0.7 GB input copies are the largest allocation of the run
-        scan_long_loop(torch, hf, I, ep, reps, st, out)
-    if st[0]:
-        raise RuntimeError("kernel loop call failed")
-    return out
 
 
 # ---- HBM traffic from hardware counters -------------------------------------------------------
@@ -400,11 +656,13 @@ def kernel_loops(torch, hf, I, ep, reps, with_gemm=True, with_y=True):
 # COPY_BYTES).  The figures stay valid only for the kernel sources they were taken from.
 COPY_BYTES = 256 << 20
 PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
-PMC_KERNELS = {  # key -> (kernel name as it appears in the profile, mangled or not; source file)
-    "proj": ("k_proj_stream", "hybrid_ssm_local_amd/csrc/hyf_proj.hip"),
-    "scan": ("k_ssd_seg", "hybrid_ssm_local_amd/csrc/hyf_scan.hip"),
-    "gemm": ("k_gemm_bf16_256", "hybrid_ssm_local_amd/csrc/hyf_gemm.hip"),
-    "w4": ("k_linear_w4", "hybrid_ssm_local_amd/csrc/hyf_w4.hip"),
+PMC_KERNELS = {  # key -> (kernel name substring, source file, launch shape the probe runs)
+    "round": ("k_round", "hybrid_ssm_local_amd/csrc/hyf_round.hip", "64 Qwen3-4B-shaped requests, full windows"),
+    "scan_seg": ("k_ssd_seg", "hybrid_ssm_local_amd/csrc/hyf_scan.hip", "8192 tokens, Qwen3-4B shape"),
+    "scan_combine": ("k_ssd_combine", "hybrid_ssm_local_amd/csrc/hyf_scan.hip", "8192 tokens, Qwen3-4B shape"),
+    "gemm": ("k_gemm_bf16_256", "hybrid_ssm_local_amd/csrc/hyf_gemm.hip", "8192 x 2560 x 2720"),
+    "proj": ("k_proj_stream<8, 1>", "hybrid_ssm_local_amd/csrc/hyf_proj.hip", "12 rows x w_in (2560 x 7968)"),
+    "w4": ("k_linear_w4", "hybrid_ssm_local_amd/csrc/hyf_w4.hip", "12 rows x 4-bit w_in"),
 }
 
 
@@ -415,30 +673,49 @@ def source_digest(rel):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def pmc_probe(torch, hf, I, reps=6):
-    """The W_in projection of a round (bf16 and 4-bit weights), the 8192-token scan, the prefill GEMM and a
-    copy of known size."""
+def pmc_probe(torch, hf, I, reps=4):
+    """The measured kernels in a fixed order, each at one launch shape: a copy of known size; the
+    round kernel at the batched shape (64 requests, windows filled by earlier rounds); the 8192-token
+    scan; the 8192 x 2560 x 2720 GEMM; the 12-row w_in projection (bf16, then 4-bit)."""
+    import numpy as np
+
     src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda").normal_()
     dst = torch.empty_like(src)
     for _ in range(3):
         dst.copy_(src)
-    ep = Episode(torch, hf, I)
-    kernel_loops(torch, hf, I, ep, reps, with_gemm=True, with_y=False)
-    # the 4-bit w_in projection of a round, eager calls on fresh weight copies
-    sh, cfg = ep.shape, ep.cfg
+    torch.cuda.synchronize()
+    del src, dst
+    sh = I.QWEN
+    R, d = 64, sh.d_model
+    rng = I.rng_streams(3)
+    _, wd = layer_weights(torch, hf, I, sh, rng[0])
+    cfg = hf.make_config(sh)
+    pool = torch.zeros(R * hf.hyf_state_bytes(cfg), dtype=torch.uint8, device="cuda")
+    wsb = hf.hyf_workspace_bytes(cfg, R, 8 * R)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    rows = (torch.randn((8 * R, d), device="cuda") / math.sqrt(d)).to(torch.bfloat16)
+    out = torch.empty_like(rows)
+    cu = np.arange(0, 8 * R + 1, 8, dtype=np.int64)
+    st = hf.hyf_state_reset(cfg, pool, R, None, R)
+    for _ in range(sh.window // 8 + reps):  # 64 rounds fill the windows, then `reps` more
+        st |= hf.hyf_draft_block(cfg, wd["structs"][0], pool, R, None, R, rows, cu, rows, out, ws, wsb)
+    torch.cuda.synchronize()
+    del pool, ws
+    scan_loop(torch, hf, I, sh, 8192, 2, reps, 100)
+    gemm_loop(torch, hf, sh, 8192, reps)
+    proj_loop(torch, hf, sh, 12, d, sh.n_in, W_COPIES)
     gen = torch.Generator(device="cuda")
     gen.manual_seed(4)
-    M, K, N = 12, sh.d_model, sh.n_in
+    M, K, N = 12, d, sh.n_in
     X = torch.randn((M, K), device="cuda", generator=gen).to(torch.bfloat16)
     y = torch.empty((M, N), dtype=torch.float32, device="cuda")
-    st = 0
     for _ in range(reps):
         codes = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device="cuda", generator=gen)
         scales = torch.rand((N, K // 128), device="cuda", generator=gen) / (7.0 * math.sqrt(K))
         st |= hf.hyf_linear_w4(cfg, X, M, K, codes, scales, N, y, 1)
     torch.cuda.synchronize()
     if st:
-        raise RuntimeError(f"hyf_linear_w4 failed: status {st}")
+        raise RuntimeError(f"pmc probe call failed: status {st}")
 
 
 def pmc_summary(fetch_db, write_db):
@@ -446,33 +723,43 @@ def pmc_summary(fetch_db, write_db):
 
     def dispatches(db, counter):
         con = sqlite3.connect(db)
-        rows = con.execute("select dispatch_id, kernel_name, sum(value) from counters_collection "
-                           "where counter_name = ? group by dispatch_id", (counter,)).fetchall()
-        return [(k, v) for _, k, v in rows]
-
-    def per_kernel(rows):
-        agg = {}
-        for k, v in rows:
-            agg.setdefault(k, []).append(v)
-        return {k: sum(v) / len(v) for k, v in agg.items()}
+        rows = con.execute("select dispatch_id, kernel_name, grid_size, sum(value) from counters_collection "
+                           "where counter_name = ? group by dispatch_id order by dispatch_id", (counter,)).fetchall()
+        return [(k, g, v) for _, k, g, v in rows]
 
     fd, wd = dispatches(fetch_db, "FETCH_SIZE"), dispatches(write_db, "WRITE_SIZE")
-    fetch, write = per_kernel(fd), per_kernel(wd)
-    # the copy of COPY_BYTES is the largest copy dispatch of the run
-    copy_f = max(v for k, v in fd if "copyBuffer" in k)
-    copy_w = max(v for k, v in wd if "copyBuffer" in k)
+    copy_f = max(v for k, g, v in fd if "copyBuffer" in k)
+    copy_w = max(v for k, g, v in wd if "copyBuffer" in k)
     scale_f, scale_w = COPY_BYTES / (copy_f * 1024), COPY_BYTES / (copy_w * 1024)
     out = {"copy_bytes": COPY_BYTES, "copy_fetch_kib": copy_f, "copy_write_kib": copy_w,
            "fetch_scale": scale_f, "write_scale": scale_w, "kernels": {}}
-    for key, (prefix, src) in PMC_KERNELS.items():
-        names = [k for k in fetch if prefix in k]
-        if not names:
+
+    def pick(rows, sub, grid=None):
+        # dispatches of the kernel; for the GEMM the probe's 8192-row launch (the largest grid)
+        m = [(g, v) for k, g, v in rows if sub in k]
+        if not m:
+            return None, None
+        if sub.startswith("k_gemm"):
+            gmax = max(g for g, _ in m)
+            m = [(g, v) for g, v in m if g == gmax]
+        else:
+            # the most frequent launch shape of this kernel in the probe
+            gs = {}
+            for g, _ in m:
+                gs[g] = gs.get(g, 0) + 1
+            gsel = max(gs, key=gs.get)
+            m = [(g, v) for g, v in m if g == gsel]
+        return m[0][0], sum(v for _, v in m) / len(m)
+
+    for key, (sub, src, what) in PMC_KERNELS.items():
+        g, f_kib = pick(fd, sub)
+        if g is None:
             continue
-        k = names[0]
-        f_kib, w_kib = fetch[k], write.get(k, 0.0)
-        out["kernels"][key] = {"kernel": k, "source": src, "source_sha256": source_digest(src),
-                               "fetch_kib": f_kib, "write_kib": w_kib,
-                               "traffic_bytes": f_kib * 1024 * scale_f + w_kib * 1024 * scale_w}
+        _, w_kib = pick(wd, sub)
+        name = next(k for k, gg, v in fd if sub in k)
+        out["kernels"][key] = {"kernel": name, "grid": g, "shape": what, "source": src,
+                               "source_sha256": source_digest(src), "fetch_kib": f_kib, "write_kib": w_kib or 0.0,
+                               "traffic_bytes": f_kib * 1024 * scale_f + (w_kib or 0.0) * 1024 * scale_w}
     with open(PMC_FILE, "w") as f:
         json.dump(out, f, indent=1)
     lines = ["# HBM traffic of the measured kernels (rocprofv3 counters)", "",
@@ -483,68 +770,14 @@ def pmc_summary(fetch_db, write_db):
              f"Calibration: a device copy of {COPY_BYTES >> 20} MiB reads FETCH_SIZE {copy_f:.0f} KiB and "
              f"WRITE_SIZE {copy_w:.0f} KiB, so measured KiB are scaled by {scale_f:.3f} (fetch) and "
              f"{scale_w:.3f} (write).", "",
-             "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes per launch |", "|---|---:|---:|---:|"]
+             "| key | kernel | launch shape | grid (threads) | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes per launch |",
+             "|---|---|---|---:|---:|---:|---:|"]
     for key, k in out["kernels"].items():
-        lines.append(f"| `{k['kernel'][:60]}` | {k['fetch_kib']:.0f} | {k['write_kib']:.0f} | {k['traffic_bytes']:.0f} |")
+        lines.append(f"| {key} | `{k['kernel'][:60]}` | {k['shape']} | {k['grid']} | {k['fetch_kib']:.0f} | "
+                     f"{k['write_kib']:.0f} | {k['traffic_bytes']:.0f} |")
     with open(PMC_FILE.replace(".json", ".md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print(json.dumps(out, indent=1))
-
-
-def stats_summary(d):
-    """Kernel statistics of a profiled --profile run: per kernel, per launch shape, and the launches
-    of the kernel loops (every dispatch after the episodes' last round kernel)."""
-    import csv
-
-    stats = list(csv.DictReader(open(os.path.join(d, "bench_kernel_stats.csv"))))
-    trace = list(csv.DictReader(open(os.path.join(d, "bench_kernel_trace.csv"))))
-    trace.sort(key=lambda r: int(r["Start_Timestamp"]))
-    dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-    short = lambda n: n if len(n) <= 110 else n[:107] + "..."
-    lines = ["# Qwen3-4B-shaped drafter layer episode (8192-feature prefix commit + 256 rounds), bench.py --profile",
-             "", "Command (from the repository root, on one MI355X):", "", "```",
-             "rocprofv3 --kernel-trace --stats --output-format csv -d out/prof_bench -o bench -- "
-             "python3 bench.py --profile",
-             "python3 bench.py --stats-summary out/prof_bench", "```", "",
-             "The run holds the Mamba-2 episode, the gated delta-rule episode, then bench.py's kernel loops.", "",
-             "rocprofv3 kernel statistics (durations in microseconds):", "",
-             "| kernel | calls | total us | average us | % |", "|---|---:|---:|---:|---:|"]
-    for r in stats:
-        lines.append(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e3:.1f} | "
-                     f"{float(r['AverageNs']) / 1e3:.3f} | {float(r['Percentage']):.2f} |")
-    shapes = {}
-    for r in trace:
-        key = (r["Kernel_Name"], int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]),
-               int(r["Workgroup_Size_X"]))
-        shapes.setdefault(key, []).append(dur(r))
-    lines += ["", "By launch shape (grid = threads in all dimensions; durations in microseconds):", "",
-              "| kernel | grid | workgroup | calls | average us |", "|---|---:|---:|---:|---:|"]
-    for (k, g, w), v in sorted(shapes.items(), key=lambda kv: -sum(kv[1])):
-        lines.append(f"| `{short(k)}` | {g} | {w} | {len(v)} | {sum(v) / len(v):.3f} |")
-    last_round = max((i for i, r in enumerate(trace) if "k_round" in r["Kernel_Name"]), default=-1)
-    # the kernel loops run, in order: the round's input projection, the 8192-token scan, the y-mode
-    # scan (k_ssd_y), the prefill GEMM, then the 131072-token scan (after the GEMM)
-    loops = {}
-    seen_gemm = False
-    for r in trace[last_round + 1:]:
-        k = r["Kernel_Name"]
-        seen_gemm |= "k_gemm_bf16_256" in k
-        if "k_ssd_seg" in k or "k_ssd_combine" in k:
-            k = k + (" [131072-token scan]" if seen_gemm else "")
-        key = (k, int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]))
-        loops.setdefault(key, []).append(dur(r))
-    lines += ["", "Launches of bench.py's kernel loops (every dispatch after the episodes' last round kernel; "
-              "these are the launches its roofline figures time):", "",
-              "| kernel | grid | calls | average us | min us |", "|---|---:|---:|---:|---:|"]
-    for (k, g), v in loops.items():
-        if "hyf" in k:
-            tag = " [131072-token scan]"
-            name = f"`{short(k[:-len(tag)])}`{tag}" if k.endswith(tag) else f"`{short(k)}`"
-            lines.append(f"| {name} | {g} | {len(v)} | {sum(v) / len(v):.3f} | {min(v):.3f} |")
-    out = os.path.join(ROOT, "profiles", "qwen3_4b_episode_kernel_stats.md")
-    with open(out, "w") as f:
-        f.write("\n".join(lines) + "\n")
-    print(out)
 
 
 def pmc_traffic(key):
@@ -557,9 +790,70 @@ def pmc_traffic(key):
     return k["traffic_bytes"] if k["source_sha256"] == source_digest(k["source"]) else None
 
 
-def cpu_baseline(I, ep, min_seconds=10.0):
-    """The float64 oracle on the host cores: whole episodes of the same workload (reset, 8192-feature
-    prefix commit, 256 rounds), repeated until at least min_seconds of CPU work."""
+def stats_summary(d):
+    """Kernel statistics of a profiled --profile run: per kernel, and per (kernel, launch shape) in
+    the order the shapes first ran, so each workload's launches can be read off separately."""
+    import csv
+
+    stats = list(csv.DictReader(open(os.path.join(d, "bench_kernel_stats.csv"))))
+    trace = list(csv.DictReader(open(os.path.join(d, "bench_kernel_trace.csv"))))
+    trace.sort(key=lambda r: int(r["Start_Timestamp"]))
+    dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    short = lambda n: n if len(n) <= 100 else n[:97] + "..."
+    lines = ["# bench.py --profile: kernel statistics", "",
+             "Command (from the repository root, on one MI355X):", "", "```",
+             "rocprofv3 --kernel-trace --stats --output-format csv -d out/prof_bench -o bench -- "
+             "python3 bench.py --profile",
+             "python3 bench.py --stats-summary out/prof_bench", "```", "",
+             "The run holds, in order: the batched 64-request serving steps (headline) and their round-kernel "
+             "graphs, the batch-1 Qwen3-4B-shaped episodes, the Phi-4-shaped two-layer steps, the long-context "
+             "Phi-4-shaped steps (Mamba-2, then the gated delta rule), then bench.py's kernel loops.", "",
+             "rocprofv3 kernel statistics (durations in microseconds):", "",
+             "| kernel | calls | total us | average us | % |", "|---|---:|---:|---:|---:|"]
+    for r in stats:
+        lines.append(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e3:.1f} | "
+                     f"{float(r['AverageNs']) / 1e3:.3f} | {float(r['Percentage']):.2f} |")
+    shapes, order = {}, []
+    for r in trace:
+        key = (r["Kernel_Name"], int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]),
+               int(r["Workgroup_Size_X"]))
+        if key not in shapes:
+            shapes[key] = []
+            order.append(key)
+        shapes[key].append(dur(r))
+    lines += ["", "By launch shape, in order of first launch (grid = threads in all dimensions; microseconds):", "",
+              "| kernel | grid | workgroup | calls | average us | min us |", "|---|---:|---:|---:|---:|---:|"]
+    for key in order:
+        k, g, w = key
+        v = shapes[key]
+        if "hyf" in k:
+            lines.append(f"| `{short(k)}` | {g} | {w} | {len(v)} | {sum(v) / len(v):.3f} | {min(v):.3f} |")
+    out = os.path.join(ROOT, "profiles", "bench_kernel_stats.md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out)
+
+
+# ---- CPU baseline --------------------------------------------------------------------------------
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(I, host_w, wl_name=HEADLINE, rounds_timed=32):
+    """The float64 oracle on the host cores, on a bounded sample of the headline workload: the
+    request of median prefix length commits its whole prefix, then `rounds_timed` of its rounds;
+    one request's episode (prefix + all its rounds) is scaled from those, and the rate is draft
+    blocks/s of that request's episode (requests are independent, so 64 of them take 64 times as
+    long).  cores = process CPU time / wall time of the timed work (the per-token loops are
+    single-threaded Python; only the projections use BLAS threads)."""
     import numpy as np
 
     from oracle import hyflash_oracle as O
@@ -567,35 +861,37 @@ def cpu_baseline(I, ep, min_seconds=10.0):
     try:
         from threadpoolctl import threadpool_info
 
-        cores = max([x["num_threads"] for x in threadpool_info()] + [1])
+        allowed = max([x["num_threads"] for x in threadpool_info()] + [1])
     except Exception:
-        cores = 1
-    sh = ep.shape
-    wl = I.WORKLOADS[WORKLOAD]
-    w = {k: np.asarray(v, np.float64) for k, v in ep.host_w.items()}
+        allowed = 1
+    wl = I.WORKLOADS[wl_name]
+    sh = wl["shape"]
     rng = I.rng_streams(wl["seed"] + 1000)
-    n_pre, n_rounds = ep.T, ep.R
-    t_commit = t_rounds = 0.0
-    episodes = 0
-    while episodes == 0 or t_commit + t_rounds < min_seconds:
-        pre = I.make_rows(rng[1], n_pre, sh.d_model, wl["feat_scale"], sh.dtype)
-        acc = I.acceptance_lengths(rng[4], n_rounds)
-        commits = [I.make_rows(rng[2], int(a), sh.d_model, wl["feat_scale"], sh.dtype) for a in acc]
-        blocks = [I.make_rows(rng[3], 8, sh.d_model, wl["block_scale"], sh.dtype) for _ in acc]
-        t0 = time.perf_counter()
-        st, _ = O.commit(sh, w, O.new_state(sh), pre)
-        t1 = time.perf_counter()
-        for cf, blk in zip(commits, blocks):
-            st, _ = O.round_step(sh, w, st, cf, blk)
-        t2 = time.perf_counter()
-        t_commit += t1 - t0
-        t_rounds += t2 - t1
-        episodes += 1
-    return {"value": episodes * n_rounds / (t_commit + t_rounds), "unit": "draft blocks/s per layer", "cores": cores,
-            "kind": "oracle",
-            "sample": f"float64 NumPy oracle: {episodes} whole episodes of the benchmark workload (reset, "
-                      f"{n_pre}-feature prefix commit, {n_rounds} rounds with 1-8 accepted features)",
-            "commit_feats_per_s": episodes * n_pre / t_commit, "seconds": t_commit + t_rounds}
+    lo, hi = wl["prefix_range"]
+    n_pre = (lo + hi) // 2
+    w = {k: np.asarray(v, np.float64) for k, v in host_w.items()}
+    pre = I.make_rows(rng[1], n_pre, sh.d_model, wl["feat_scale"], sh.dtype)
+    acc = I.acceptance_lengths(rng[4], rounds_timed)
+    commits = [I.make_rows(rng[2], int(a), sh.d_model, wl["feat_scale"], sh.dtype) for a in acc]
+    blocks = [I.make_rows(rng[3], 8, sh.d_model, wl["block_scale"], sh.dtype) for _ in acc]
+    c0, t0 = time.process_time(), time.perf_counter()
+    st, _ = O.commit(sh, w, O.new_state(sh), pre)
+    t1 = time.perf_counter()
+    for cf, blk in zip(commits, blocks):
+        st, _ = O.round_step(sh, w, st, cf, blk)
+    t2 = time.perf_counter()
+    cpu = time.process_time() - c0
+    episode_s = (t1 - t0) + (t2 - t1) * wl["rounds"] / rounds_timed
+    return {"value": wl["rounds"] / episode_s, "unit": "draft blocks/s (headline workload)",
+            "cores": max(1, round(cpu / (t2 - t0))), "kind": "oracle",
+            "sample": f"float64 NumPy oracle, one request of the batched workload: a {n_pre}-feature prefix commit "
+                      f"(the median prefix) and {rounds_timed} of its {wl['rounds']} rounds, scaled to the request's "
+                      f"whole episode; requests are independent, so the rate is the workload's",
+            "cpu_model": cpu_model(), "threads_allowed": allowed, "seconds": t2 - t0,
+            "commit_feats_per_s": n_pre / (t1 - t0), "round_ms": 1e3 * (t2 - t1) / rounds_timed}
+
+
+# ---- main ----------------------------------------------------------------------------------------
 
 
 def main():
@@ -611,8 +907,10 @@ def main():
         print(f"bench.py measures one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
         sys.exit(2)
+    sub_steps = 3
     if args.profile:
-        args.steps, args.warmup, args.kernel_reps, args.no_cpu = 2, 1, 12, True
+        args.steps, args.warmup, args.kernel_reps, args.no_cpu = 2, 1, 8, True
+        sub_steps = 1
 
     import torch
 
@@ -624,127 +922,141 @@ def main():
     if args.pmc_probe:
         pmc_probe(torch, hf, I)
         return
-    log("building episode inputs")
-    ep = Episode(torch, hf, I)
-    stream = torch.cuda.current_stream().cuda_stream
 
-    # ---- eager steps
-    log("warmup", args.warmup)
-    for _ in range(args.warmup):
-        ep.step(stream)
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    log("timed eager steps", args.steps)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    for k in range(args.steps):
-        ep.step(stream, evs[k])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    step_ms = [e[0].elapsed_time(e[2]) for e in evs]
-    pre_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    rnd_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    eager_ms = sum(step_ms) / len(step_ms)
-
-    # ---- the same step replayed from a captured HIP graph (no host launch cost per kernel)
-    log("graph capture")
-    g = torch.cuda.CUDAGraph()
-    cs = torch.cuda.Stream()
-    with torch.cuda.stream(cs):
-        ep.step(cs.cuda_stream)
-    torch.cuda.synchronize()
-    with torch.cuda.graph(g, stream=cs):
-        ep.step(cs.cuda_stream)
-    for _ in range(max(1, args.warmup)):
-        g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    graph_ms = e0.elapsed_time(e1) / args.steps
-
-    # ---- the same episode with the gated delta-rule memory in place of Mamba-2 (eager steps)
-    log("gated delta-rule episode")
-    del g
-    ep_g = Episode(torch, hf, I, memory="gdn")
-    ep_g.step(stream)
-    gevs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(3)]
-    for k in range(3):
-        ep_g.step(stream, gevs[k])
-    torch.cuda.synchronize()
-    g_pre = sum(e[0].elapsed_time(e[1]) for e in gevs) / 3
-    g_rnd = sum(e[1].elapsed_time(e[2]) for e in gevs) / 3
-    gdn = {"prefill_commit_us": 1e3 * g_pre, "commit_feats_per_s": ep_g.T / (g_pre * 1e-3),
-           "round_us": 1e3 * g_rnd / ep_g.R, "draft_blocks_per_s": ep_g.R / (g_rnd * 1e-3),
-           "note": "eager steps of the same workload with memory = gated delta rule; the prefix commit runs "
-                   "the chunked form (per-chunk solves, then one state update per 64-token chunk)"}
-    del ep_g
-
-    log("batched serving")
-    batched = batched_serving(torch, hf, I)
+    # ---- headline: batched serving, 64 requests, whole steps
+    log("headline: building the batched workload")
+    bt = Batched(torch, hf, I)
+    log("headline: eager steps", args.warmup, "+", args.steps)
+    head = run_steps(torch, bt.step, args.steps, args.warmup)
+    log("headline: round-kernel graphs")
+    t_round, t_proj, rows = bt.round_kernel(torch, hf)
+    sh, R = bt.shape, bt.R
+    kb = kround_bytes(sh, R, rows, bt.windows)
+    rb = round_bytes(sh, R, rows, bt.windows)
+    t_k = t_round - t_proj
+    blocks = R * bt.rounds
+    head_obj = {"host_w": bt.host_w, "T": bt.T}
+    del bt
     torch.cuda.empty_cache()
-    log("kernel loops")
-    kl = kernel_loops(torch, hf, I, ep, args.kernel_reps)
-    log("4-bit projections")
-    w4 = w4_round_projections(torch, hf, I, ep)
-    cpu = None if args.no_cpu else cpu_baseline(I, ep)
 
-    sh = ep.shape
-    R = ep.R
-    proj, scan, gemm = kl["proj"], kl["scan"], kl["gemm"]
+    # ---- batch-1 Qwen3-4B-shaped episodes
+    log("batch-1 episodes")
+    ep = EpisodesB1(torch, hf, I)
+    b1 = run_steps(torch, ep.step, sub_steps, 1)
+    b1_round, b1_proj, b1_rows = ep.round_kernel(torch, hf)
+    b1_win = [ep.shape.window]
+    b1_kb = kround_bytes(ep.shape, 1, b1_rows, b1_win)
+    b1_rb = round_bytes(ep.shape, 1, b1_rows, b1_win)
+    b1_blocks = EPISODES * ep.rounds
+    qwen_b1 = {
+        "workload": "Qwen3-4B-shaped layer, batch 1: 8192-feature prefix commit, then 256 rounds (1-8 accepted "
+                    f"features each); {EPISODES} requests' episodes interleaved call by call, {W_COPIES} weight copies "
+                    "rotated",
+        "value": b1_blocks / (b1["step_ms"] * 1e-3), "unit": "draft blocks/s per layer (batch 1)",
+        "ms_per_step": b1["step_ms"], "prefill_commit_us": 1e3 * b1["prefill_ms"] / EPISODES,
+        "round_us": 1e3 * b1["rounds_ms"] / b1_blocks,
+        "round_graph_us": b1_round, "round": {"bytes_per_round": b1_rb, **hbm(b1_rb, b1_round)},
+        "round_kernel": {"kernel": "k_round (1 request x 32 heads)", "avg_us": b1_round - b1_proj,
+                         "bytes_per_launch": b1_kb, **hbm(b1_kb, b1_round - b1_proj),
+                         "projections_graph_us": b1_proj},
+    }
+    del ep
+    torch.cuda.empty_cache()
+
+    # ---- Phi-4-shaped two-layer drafter
+    log("phi-4 two-layer")
+    tl = TwoLayerPhi4(torch, hf, I)
+    p3 = run_steps(torch, tl.step, sub_steps, 1)
+    phi4_2l = {"workload": "Phi-4-shaped two-layer drafter: both layers commit a 32768-feature prefix, then 512 rounds "
+                           "(each: both layers commit 1-8 accepted features; layer 2 drafts from block_in + layer 1's "
+                           "output)",
+               "value": tl.rounds / (p3["step_ms"] * 1e-3), "unit": "two-layer draft rounds/s (batch 1)",
+               "ms_per_step": p3["step_ms"], "prefill_commit_us": 1e3 * p3["prefill_ms"] / 2,
+               "round_us": 1e3 * p3["rounds_ms"] / tl.rounds,
+               "per_layer_blocks_per_s": 2 * tl.rounds / (p3["rounds_ms"] * 1e-3)}
+    del tl
+    torch.cuda.empty_cache()
+
+    # ---- long-context Phi-4-shaped layer, both memories
+    long5 = {}
+    prefix = None
+    for memory in ("mamba2", "gdn"):
+        log("phi-4 long context", memory)
+        lp = LongPhi4(torch, hf, I, memory=memory, prefix_dev=prefix)
+        prefix = lp.prefix
+        p5 = run_steps(torch, lp.step, sub_steps, 1)
+        long5[memory] = {"value": lp.rounds / (p5["step_ms"] * 1e-3), "unit": "draft blocks/s per layer (batch 1)",
+                         "ms_per_step": p5["step_ms"], "prefill_commit_us": 1e3 * p5["prefill_ms"],
+                         "commit_feats_per_s": lp.T / (p5["prefill_ms"] * 1e-3),
+                         "round_us": 1e3 * p5["rounds_ms"] / lp.rounds}
+        del lp
+        torch.cuda.empty_cache()
+    long5["workload"] = ("Phi-4-shaped layer, chunk 256: 131072-feature prefix commit, then 128 rounds; Mamba-2 and "
+                         "the gated delta rule")
+    del prefix
+    torch.cuda.empty_cache()
+
+    # ---- kernel loops
+    log("kernel loops")
+    reps = args.kernel_reps
+    s_us, s_b = scan_loop(torch, hf, I, I.QWEN, 8192, SCAN_COPIES, reps, 100)
+    sl_us, sl_b = scan_loop(torch, hf, I, I.PHI4_LONG, 131072, 2, max(4, reps // 6), 131072)
+    sq_us, sq_b = scan_loop(torch, hf, I, I.QWEN, 131072, 2, max(4, reps // 6), 131073)
+    sy_us, sy_b = scan_y_loop(torch, hf, I, I.QWEN, 8192, max(4, reps // 6))
+    g2 = gemm_loop(torch, hf, I.QWEN, 8192, max(4, reps // 6))
+    g3 = gemm_loop(torch, hf, I.PHI4, 32768, max(4, reps // 12))
+    pj = proj_loop(torch, hf, I.QWEN, 12, I.QWEN.d_model, I.QWEN.n_in, reps)
+    w4 = w4_projections(torch, hf, I.QWEN)
+    g2["traffic"] = pmc_traffic("gemm")
+    pj["traffic"] = pmc_traffic("proj")
+    cpu = None if args.no_cpu else cpu_baseline(I, head_obj["host_w"])
+
     res = {
         "metric": METRIC,
-        "value": R / (eager_ms * 1e-3),
-        "unit": "draft blocks/s per layer",
+        "value": blocks / (head["step_ms"] * 1e-3),
+        "unit": "draft blocks/s (64 requests, one layer)",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": eager_ms,
-        "wall_s": wall,
+        "ms_per_step": head["step_ms"],
+        "wall_s": head["wall_s"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1)/sqrt(d) features, Xavier-normal weights)",
-        "config": {"workload": "Qwen3-4B-shaped HyFlash drafter layer: prefix commit of 8192 features, then "
-                               "256 rounds of commit (1-8 accepted) + draft block, batch 1",
+        "data": "synthetic (seeded NumPy PCG64: N(0,1)/sqrt(d) features and block rows, Xavier-normal weights)",
+        "config": {"workload": "batched serving on one GPU: Qwen3-4B-shaped HyFlash drafter layer, 64 requests with "
+                               "prefixes U{2048..16384} committed in one call, then 128 rounds of commit (1-8 "
+                               "accepted per request) + draft block for all 64",
                    "d_model": sh.d_model, "n_heads": sh.n_heads, "head_dim": sh.head_dim, "d_state": sh.d_state,
-                   "chunk": sh.chunk, "window": sh.window, "block": sh.block, "prefix": ep.T, "rounds": R,
-                   "committed_rows": int(ep.acc.sum()), "parallelism": "single GPU"},
-        "breakdown": {"prefill_commit_us": 1e3 * sum(pre_ms) / len(pre_ms),
-                      "rounds_us": 1e3 * sum(rnd_ms) / len(rnd_ms),
-                      "round_us": 1e3 * sum(rnd_ms) / len(rnd_ms) / R,
-                      "graph_replay_ms_per_step": graph_ms,
-                      "graph_blocks_per_s": R / (graph_ms * 1e-3)},
-        "commit_scan": {"value": scan["feats_per_s"], "unit": "committed feats/s", "T": ep.T,
-                        "avg_us": scan["mean_us"],
-                        "roofline": {"bound": "hbm", "achieved": scan["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                     "frac": scan["gbs"] / HBM_PEAK_GBS, "traffic": pmc_traffic("scan"),
-                                     "bytes_per_launch": scan["bytes"]}},
-        "commit_scan_long": {"value": kl["scan_long"]["feats_per_s"], "unit": "committed feats/s",
-                             "T": kl["scan_long"]["T"], "avg_us": kl["scan_long"]["mean_us"],
-                             "roofline": {"bound": "hbm", "achieved": kl["scan_long"]["gbs"], "peak": HBM_PEAK_GBS,
-                                          "unit": "GB/s", "frac": kl["scan_long"]["gbs"] / HBM_PEAK_GBS,
-                                          "traffic": None, "bytes_per_launch": kl["scan_long"]["bytes"]},
-                             "note": "the same scan over a 131072-token prefix at the same layer shape"},
-        "commit_scan_y": {"value": kl["scan_y"]["feats_per_s"], "unit": "committed feats/s", "T": ep.T,
-                          "avg_us": kl["scan_y"]["mean_us"],
-                          "roofline": {"bound": "hbm", "achieved": kl["scan_y"]["gbs"], "peak": HBM_PEAK_GBS,
-                                       "unit": "GB/s", "frac": kl["scan_y"]["gbs"] / HBM_PEAK_GBS, "traffic": None,
-                                       "bytes_per_launch": kl["scan_y"]["bytes"]}},
-        "roofline": {"bound": "hbm", "achieved": proj["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": proj["gbs"] / HBM_PEAK_GBS, "traffic": pmc_traffic("proj"),
-                     "kernel": "k_proj_stream<8,1>: input projection of a round (12 rows x w_in)",
-                     "bytes_per_launch": proj["bytes"], "avg_us": proj["mean_us"]},
-        "gemm_roofline": {"bound": "mfma", "achieved": gemm["tflops"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                          "frac": gemm["tflops"] / BF16_PEAK_TFLOPS,
-                          "kernel": "k_gemm_bf16_256: prefill projection 8192 x 2560 x 2720", "avg_us": gemm["mean_us"],
-                          "traffic": pmc_traffic("gemm"), "algorithmic_bytes": gemm["bytes"]},
-        "gated_delta_rule": gdn,
-        "batched_serving": batched,
+                   "chunk": sh.chunk, "window": sh.window, "block": sh.block, "requests": R, "rounds": 128,
+                   "prefix_rows": head_obj["T"], "parallelism": "single GPU"},
+        "breakdown": {"prefill_commit_us": 1e3 * head["prefill_ms"], "rounds_us": 1e3 * head["rounds_ms"],
+                      "round_us": 1e3 * head["rounds_ms"] / 128, "round_graph_us": t_round,
+                      "projections_graph_us": t_proj},
+        "roofline": {**hbm(kb, t_k), "traffic": pmc_traffic("round"),
+                     "kernel": "k_round<bf16>: commit, readout, attention and merge of 64 requests x 32 heads",
+                     "bytes_per_launch": kb, "avg_us": t_k,
+                     "method": "graph of the 128 rounds minus a graph of their two projections (same kernels and "
+                               "shapes through hyf_linear), per round"},
+        "round": {"bytes_per_round": rb, "avg_us": t_round, **hbm(rb, t_round)},
+        "qwen3_4b_batch1": qwen_b1,
+        "phi4_two_layer": phi4_2l,
+        "phi4_long131k": long5,
+        "commit_scan": {"value": 8192 / (s_us * 1e-6), "unit": "committed feats/s", "T": 8192, "shape": "Qwen3-4B",
+                        "avg_us": s_us, "roofline": {**hbm(s_b, s_us), "traffic": pmc_traffic("scan_seg"),
+                                                     "bytes_per_launch": s_b}},
+        "commit_scan_phi4_131k": {"value": 131072 / (sl_us * 1e-6), "unit": "committed feats/s", "T": 131072,
+                                  "shape": "Phi-4, chunk 256", "avg_us": sl_us,
+                                  "roofline": {**hbm(sl_b, sl_us), "traffic": None, "bytes_per_launch": sl_b}},
+        "commit_scan_qwen_131k": {"value": 131072 / (sq_us * 1e-6), "unit": "committed feats/s", "T": 131072,
+                                  "shape": "Qwen3-4B", "avg_us": sq_us,
+                                  "roofline": {**hbm(sq_b, sq_us), "traffic": None, "bytes_per_launch": sq_b}},
+        "commit_scan_y": {"value": 8192 / (sy_us * 1e-6), "unit": "committed feats/s", "T": 8192, "avg_us": sy_us,
+                          "roofline": {**hbm(sy_b, sy_us), "traffic": None, "bytes_per_launch": sy_b}},
+        "gemm_qwen_8192": g2,
+        "gemm_phi4_32768": g3,
+        "round_projection_w_in": pj,
         "w4a16_round_projections": w4,
         "cpu_baseline": cpu,
     }

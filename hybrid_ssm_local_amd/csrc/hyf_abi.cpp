@@ -77,7 +77,6 @@ Shape make_shape(const hyf_config* c) {
   return s;
 }
 
-int n_att_split(const Shape& s) { return (s.W + 63) / 64 + 1; }
 
 // Segment policy of the scan: whole chunks per segment, the same count for every request, about
 // SCAN_TARGET_WGS workgroups in all, segments no shorter than SCAN_MIN_SEG_TOKENS (each segment
@@ -140,7 +139,7 @@ struct WsDraft {
 };
 WsDraft ws_draft(const Shape& s, int dtype, int32_t R, int64_t rows) {
   WsDraft w;
-  const int ns = n_att_split(s);
+  const int ns = round_max_splits(s);
   uint64_t o = 0;
   w.proj = o;
   o += align_up((uint64_t)(rows + (int64_t)HYF_BLOCK * R) * proj_ld(s) * 4);
@@ -308,10 +307,9 @@ int draft_run(const hyf_config* cfg, const hyf_weights* w, void* state_pool, con
   ra.att_ml = reinterpret_cast<float*>(wsb + L.att_ml);
   ra.o_in = wsb + L.o_in;
   ra.counters = counters;
-  ra.n_tiles = round_tiles(s);
-  ra.n_split = n_att_split(s);
   ra.do_commit = rows > 0;
   ra.do_draft = 1;
+  round_layout(s, n_req, esize(dt), &ra);
   if ((he = launch_round(dt, s, ra, rt, hs)) != hipSuccess) return HYF_EHIP;
   // 3. output projection
   RowSrc xo{ra.o_in, ra.o_in, (int64_t)HYF_BLOCK * n_req};
@@ -465,10 +463,10 @@ int hyf_memory_commit(const hyf_config* cfg, const hyf_weights* w, void* state_p
     ra.dt_bias = w->dt_bias;
     ra.d_skip = w->d_skip;
     ra.counters = counters;
-    ra.n_tiles = round_tiles(s);
-    ra.n_split = 0;
     ra.do_commit = 1;
     ra.do_draft = 0;
+    round_layout(s, n_req, es, &ra);
+    ra.n_split = 0;
     return hip_status(launch_round(dt, s, ra, rt, hs));
   }
 

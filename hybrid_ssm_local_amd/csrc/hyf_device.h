@@ -73,6 +73,31 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// The same reductions without LDS traffic: DPP moves inside each 16-lane row (swaps inside quads,
+// the mirrored half-row, the mirrored row), then the four row results read as scalars.  The result
+// is uniform (every lane gets it).
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float lane_f(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+__device__ __forceinline__ float wave_sum64(float v) {
+  v += dpp_row<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_row<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_row<0x141>(v);  // row_half_mirror
+  v += dpp_row<0x140>(v);  // row_mirror
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+}
+__device__ __forceinline__ float wave_max64(float v) {
+  v = fmaxf(v, dpp_row<0xB1>(v));
+  v = fmaxf(v, dpp_row<0x4E>(v));
+  v = fmaxf(v, dpp_row<0x141>(v));
+  v = fmaxf(v, dpp_row<0x140>(v));
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
+}
+
 // ---------------------------------------------------------------------------------------------
 // MFMA 16x16 tiles.  Layouts (checked on gfx950):
 //   bf16 16x16x32: lane l supplies A[l%16][8*(l/16) .. +7] and B[8*(l/16) .. +7][l%16];

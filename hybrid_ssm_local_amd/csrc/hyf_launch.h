@@ -126,8 +126,13 @@ struct RoundArgs {
   int32_t n_split;     // attention splits per (request, head), the last one holds the block keys
   int32_t do_commit;   // commit rows present
   int32_t do_draft;    // block rows present
+  int32_t tile_rows;   // rows of H per commit / readout tile
+  int32_t ks;          // ring slots per attention split
 };
-int round_tiles(const Shape& sh);
+// Fills n_tiles, tile_rows, ks and n_split of a round over n_req requests (esz: storage bytes).
+void round_layout(const Shape& sh, int n_req, int esz, RoundArgs* a);
+// The most attention splits any layout uses (the workspace is sized for it).
+int round_max_splits(const Shape& sh);
 
 // Gated delta-rule commit of whole prefixes (sh.gdn): x and B tiled as for the Mamba-2 scan, the raw
 // gates time-blocked in a.dt (alpha at feature h, beta at nh + h, block stride a.dblk); gate biases

@@ -8,7 +8,8 @@ namespace hyf {
 
 constexpr int RB = HYF_BLOCK;   // block rows
 constexpr int RMAXC = 16;       // largest per-request commit a round kernel folds in
-constexpr int ATT_KS = 64;      // keys per attention split
+constexpr int KS_MIN = 64;      // fewest keys per attention split (the workspace is sized for it)
+constexpr int WIDE_PASSES = 16; // most row passes of one commit / readout tile (wide layout)
 constexpr int RT = 256;         // threads per round workgroup
 
 __device__ __forceinline__ int64_t* count_ptr(char* pool, const Shape& sh, int slot) {
@@ -24,16 +25,26 @@ __device__ __forceinline__ T* ring_ptr(char* pool, const Shape& sh, int slot, ui
 
 // ---------------------------------------------------------------------------------------------
 // One round, one launch.  Workgroup roles per (request r, head h), in block-index order:
-//   tiles  [0, n_tiles):   rows p0 .. p0 + rows_wg of H: fold the round's committed rows in (one
+//   tiles  [0, n_tiles):   rows p0 .. p0 + tile_rows of H: fold the round's committed rows in (one
 //                          read-modify-write), memory readout of the block rows from the updated
 //                          rows, and (tile 0) the ring append of the committed (k, v);
-//   splits [n_tiles, +n_split): attention of the 8 block rows over 64 ring slots (the last split:
+//   splits [n_tiles, +n_split): attention of the 8 block rows over ks ring slots (the last split:
 //                          over the block rows themselves), written as (max, sum, output) partials.
+// The layout (ks, tile_rows) is chosen per launch (round_layout).
 // A split sees the ring as it is after this round's append without waiting for it: a slot that
 // the append overwrites is read from the projection instead (rounded to the storage dtype, as the
 // ring stores it).  The last workgroup of (r, h) to finish (a counter) merges the splits, adds the
 // readout and writes the output projection's input; the last head of a request advances the
 // request's committed count.  The counters are cleared by the round's input projection.
+//
+// Memory ordering of the hand-over: every partial result a workgroup leaves for the merge (the
+// attention partials, the (max, sum) pairs, the readout) is written with device-scope stores that
+// bypass the non-coherent per-XCD caches (st_dev), and the writer waits for all of its stores to be
+// acknowledged (vm_wait<0>) before the barrier after which one thread increments the (r, h) counter.
+// The workgroup that sees the counter reach its final value therefore runs after every store of the
+// other workgroups of (r, h) has reached the device-coherent level, and it reads the partials with
+// device-coherent loads (sc1), so it cannot see stale copies.  The atomic itself needs no fence: the
+// order comes from the completed stores before it, not from the atomic's own ordering.
 
 // Staging: a job copies n chunks (16 or 4 bytes) from global memory, chunk i from src(i) to
 // dst + i chunks in LDS, with direct global -> LDS loads: no registers and no wait between
@@ -65,24 +76,31 @@ __device__ __forceinline__ void stage16_dev(int n, void* dst, F src) {
 }
 
 // Tile LDS (bytes): B of the committed rows [RMAXC][N] f32 | C of the block rows [RB][N] f32 |
-// x (= v) of the committed rows [RMAXC][rows_wg] f32 | v of the block rows [RB][rows_wg] f32 |
+// x (= v) of the committed rows [RMAXC][tile_rows] f32 | v of the block rows [RB][tile_rows] f32 |
 // weights [RMAXC + 4] (gated delta rule: retention gates) | write gates [RMAXC] | inverse key norms
 // [RMAXC] | inverse query norms [RB] | readout partials [RB][RT].
+//
+// A tile's threads hold tpr = N / 4 threads per row of H (4 columns each), rows_wg = RT / tpr rows
+// at a time; a tile of tile_rows rows takes tile_rows / rows_wg passes, every pass's row of H in
+// registers, all of them loaded before any arithmetic.  Several passes need tpr a power of two (the
+// row reductions are lane shuffles); otherwise a tile is one pass.
 //
 // Gated delta-rule memory (sh.gdn): the committed rows are folded one at a time, each row of H
 // (tpr threads) forming H_p . k with a reduction over its threads, then
 // H_p <- alpha (H_p - beta (H_p . k) k) + beta x_p k, k the unit-normalized B row; the readout
 // uses the unit-normalized C rows.
-template <typename T>
+template <typename T, int TMAXG>
 __device__ __forceinline__ void round_tile(const Shape& sh, const RoundArgs& a, const ReqTable& rt, int r, int h,
                                            int tile, char* smem) {
   const int nh = sh.nh, P = sh.P, N = sh.N;
   const int tpr = N / 4;           // threads per H row (4 columns each)
-  const int rows_wg = RT / tpr;    // H rows per tile
+  const int rows_wg = RT / tpr;    // H rows per pass
+  const int trows = a.tile_rows;   // H rows per tile: a multiple of rows_wg, at most TMAXG passes (host-checked)
+  const int npass = trows / rows_wg;
   const int t = threadIdx.x;
   const int prow = t / tpr, c4 = t % tpr;
-  const int p0 = tile * rows_wg, p = p0 + prow;
-  const bool active = prow < rows_wg && p < P;
+  const int p0 = tile * trows;
+  const bool lane_ok = prow < rows_wg;
   const int slot = rt.slot[r];
   const int grp = h / (nh / sh.G);
   const int nrows = a.do_commit ? rt.row0[r + 1] - rt.row0[r] : 0;
@@ -92,8 +110,8 @@ __device__ __forceinline__ void round_tile(const Shape& sh, const RoundArgs& a, 
   float* Bl = reinterpret_cast<float*>(smem);
   float* Cl = reinterpret_cast<float*>(smem + up1k(RMAXC * N * 4));
   float* xv = reinterpret_cast<float*>(reinterpret_cast<char*>(Cl) + up1k(RB * N * 4));
-  float* vb = reinterpret_cast<float*>(reinterpret_cast<char*>(xv) + up1k(RMAXC * rows_wg * 4));
-  float* wl = reinterpret_cast<float*>(reinterpret_cast<char*>(vb) + up1k(RB * rows_wg * 4));
+  float* vb = reinterpret_cast<float*>(reinterpret_cast<char*>(xv) + up1k(RMAXC * trows * 4));
+  float* wl = reinterpret_cast<float*>(reinterpret_cast<char*>(vb) + up1k(RB * trows * 4));
   float* ga = wl + RMAXC + 4;  // write gates (gated delta rule)
   float* ik = ga + RMAXC;      // inverse key norms
   float* iq = ik + RMAXC;      // inverse query norms
@@ -101,15 +119,22 @@ __device__ __forceinline__ void round_tile(const Shape& sh, const RoundArgs& a, 
 
   // every load first (one round trip), then the arithmetic
   float* Hh = h_ptr(a.state_pool, sh, slot, h);
-  f32x4 hv = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (active) hv = *reinterpret_cast<const f32x4*>(Hh + (int64_t)p * N + 4 * c4);
+  f32x4 hv[TMAXG];
+#pragma unroll
+  for (int i = 0; i < TMAXG; ++i) {
+    hv[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int p = p0 + prow + i * rows_wg;
+    if (i < npass && lane_ok && p < P) hv[i] = *reinterpret_cast<const f32x4*>(Hh + (int64_t)p * N + 4 * c4);
+  }
   const float raw = t < nrows ? a.proj[(crow0 + t) * ld + sh.off_dt + h] : 0.f;
   const float rawb = sh.gdn && t < nrows ? a.proj[(crow0 + t) * ld + sh.off_beta + h] : 0.f;
+  // column of tile row i (rows past the head's last row read its last row; their values go unused)
+  auto tcol = [&](int i) { return p0 + i < P ? p0 + i : P - 1; };
   stage16(nrows * tpr, Bl, [&](int i) { return a.proj + (crow0 + i / tpr) * ld + sh.off_b + grp * N + 4 * (i % tpr); });
-  stage4(nrows * rows_wg, xv, [&](int i) { return a.proj + (crow0 + i / rows_wg) * ld + sh.off_v + h * P + p0 + i % rows_wg; });
+  stage4(nrows * trows, xv, [&](int i) { return a.proj + (crow0 + i / trows) * ld + sh.off_v + h * P + tcol(i % trows); });
   if (a.do_draft) {
     stage16(RB * tpr, Cl, [&](int i) { return a.proj + (brow0 + i / tpr) * ld + sh.off_c + grp * N + 4 * (i % tpr); });
-    stage4(RB * rows_wg, vb, [&](int i) { return a.proj + (brow0 + i / rows_wg) * ld + sh.off_v + h * P + p0 + i % rows_wg; });
+    stage4(RB * trows, vb, [&](int i) { return a.proj + (brow0 + i / trows) * ld + sh.off_v + h * P + tcol(i % trows); });
   }
   if (sh.gdn) {
     if (t < nrows) {
@@ -152,54 +177,125 @@ __device__ __forceinline__ void round_tile(const Shape& sh, const RoundArgs& a, 
     if (nrows > 0) {
       for (int tt = 0; tt < nrows; ++tt) {
         const f32x4 k = *reinterpret_cast<const f32x4*>(Bl + tt * N + 4 * c4) * ik[tt];
-        float d = hv[0] * k[0] + hv[1] * k[1] + hv[2] * k[2] + hv[3] * k[3];
+        const float be = ga[tt];
         if (pow2) {
-          for (int o = tpr / 2; o >= 1; o >>= 1) d += __shfl_xor(d, o, 64);
+#pragma unroll
+          for (int i = 0; i < TMAXG; ++i) {
+            if (i < npass) {
+              float d = hv[i][0] * k[0] + hv[i][1] * k[1] + hv[i][2] * k[2] + hv[i][3] * k[3];
+              for (int o = tpr / 2; o >= 1; o >>= 1) d += __shfl_xor(d, o, 64);
+              const int pr = prow + i * rows_wg;
+              const float xw = lane_ok && p0 + pr < P ? be * xv[tt * trows + pr] : 0.f;
+              hv[i] = wl[tt] * (hv[i] - (be * d) * k) + xw * k;
+            }
+          }
         } else {
+          // one pass (the host keeps tile_rows = rows_wg here)
+          float d = hv[0][0] * k[0] + hv[0][1] * k[1] + hv[0][2] * k[2] + hv[0][3] * k[3];
           red[t] = d;
           __syncthreads();
           d = 0.f;
-          for (int c = 0; c < tpr; ++c) d += red[prow * tpr + c];
+          if (lane_ok)
+            for (int c = 0; c < tpr; ++c) d += red[prow * tpr + c];
           __syncthreads();
+          const float xw = lane_ok && p0 + prow < P ? be * xv[tt * trows + prow] : 0.f;
+          hv[0] = wl[tt] * (hv[0] - (be * d) * k) + xw * k;
         }
-        const float be = ga[tt];
-        const float xw = active ? be * xv[tt * rows_wg + prow] : 0.f;
-        hv = wl[tt] * (hv - (be * d) * k) + xw * k;
       }
-      if (active) *reinterpret_cast<f32x4*>(Hh + (int64_t)p * N + 4 * c4) = hv;
     }
-  } else if (active && nrows > 0) {
-    hv *= wl[RMAXC];
+  } else if (nrows > 0) {
+    const float dec = wl[RMAXC];
+#pragma unroll
+    for (int i = 0; i < TMAXG; ++i)
+      if (i < npass) hv[i] *= dec;
     for (int tt = 0; tt < nrows; ++tt) {
-      const float xw = xv[tt * rows_wg + prow] * wl[tt];
       const f32x4 b = *reinterpret_cast<const f32x4*>(Bl + tt * N + 4 * c4);
-      hv += xw * b;
+      const float w = wl[tt];
+#pragma unroll
+      for (int i = 0; i < TMAXG; ++i) {
+        if (i < npass) {
+          const int pr = prow + i * rows_wg;
+          const float xw = lane_ok && p0 + pr < P ? xv[tt * trows + pr] * w : 0.f;
+          hv[i] += xw * b;
+        }
+      }
     }
-    *reinterpret_cast<f32x4*>(Hh + (int64_t)p * N + 4 * c4) = hv;
+  }
+  if (nrows > 0) {
+#pragma unroll
+    for (int i = 0; i < TMAXG; ++i) {
+      const int p = p0 + prow + i * rows_wg;
+      if (i < npass && lane_ok && p < P) *reinterpret_cast<f32x4*>(Hh + (int64_t)p * N + 4 * c4) = hv[i];
+    }
   }
 
   if (a.do_draft) {
-    float sum[RB];
-#pragma unroll
-    for (int j = 0; j < RB; ++j) {
-      sum[j] = 0.f;
-      if (active) {
-        const f32x4 c = *reinterpret_cast<const f32x4*>(Cl + j * N + 4 * c4);
-        sum[j] = hv[0] * c[0] + hv[1] * c[1] + hv[2] * c[2] + hv[3] * c[3];
-      }
-    }
     const float D = a.d_skip[h];
     if (pow2) {
-      // the tpr threads of a row are consecutive lanes of one wave: xor-shuffle reduction
-      for (int o = tpr / 2; o >= 1; o >>= 1)
 #pragma unroll
-        for (int j = 0; j < RB; ++j) sum[j] += __shfl_xor(sum[j], o, 64);
-      if (active && c4 == 0)
+      for (int i = 0; i < TMAXG; ++i) {
+        if (i >= npass) continue;
+        float sum[RB];
 #pragma unroll
-        for (int j = 0; j < RB; ++j)
-          st_dev(a.mem + (((int64_t)r * RB + j) * nh + h) * P + p,
-                 sum[j] * (sh.gdn ? iq[j] : 1.f) + D * vb[j * rows_wg + prow]);
+        for (int j = 0; j < RB; ++j) {
+          const f32x4 c = *reinterpret_cast<const f32x4*>(Cl + j * N + 4 * c4);
+          sum[j] = hv[i][0] * c[0] + hv[i][1] * c[1] + hv[i][2] * c[2] + hv[i][3] * c[3];
+        }
+        // the tpr threads of a row are consecutive lanes of one wave.  With tpr >= 8 the 8 sums are
+        // reduced by halving: at offsets tpr/2, tpr/4, tpr/8 a lane keeps half of its sums (the upper
+        // half if its offset bit is set) and adds its partner's copies of them, so after three steps
+        // lane c4 holds one sum, of block row j = (c4 / (tpr / 8)) mod 8, and the offsets below
+        // tpr/8 finish it (9 shuffles for tpr = 32 instead of 40).
+        const int pr = prow + i * rows_wg;
+        if (tpr >= 8) {
+          {
+            const int o = tpr >> 1;
+            const bool hi = (c4 & o) != 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const float send = hi ? sum[k] : sum[k + 4], keep = hi ? sum[k + 4] : sum[k];
+              sum[k] = keep + __shfl_xor(send, o, 64);
+            }
+          }
+          {
+            const int o = tpr >> 2;
+            const bool hi = (c4 & o) != 0;
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+              const float send = hi ? sum[k] : sum[k + 2], keep = hi ? sum[k + 2] : sum[k];
+              sum[k] = keep + __shfl_xor(send, o, 64);
+            }
+          }
+          {
+            const int o = tpr >> 3;
+            const bool hi = (c4 & o) != 0;
+            const float send = hi ? sum[0] : sum[1], keep = hi ? sum[1] : sum[0];
+            sum[0] = keep + __shfl_xor(send, o, 64);
+          }
+          for (int o = tpr >> 4; o >= 1; o >>= 1) sum[0] += __shfl_xor(sum[0], o, 64);
+          const int sub = tpr >> 3;
+          const int j = (c4 / sub) & 7;
+          if (lane_ok && c4 % sub == 0 && p0 + pr < P)
+            st_dev(a.mem + (((int64_t)r * RB + j) * nh + h) * P + p0 + pr,
+                   sum[0] * (sh.gdn ? iq[j] : 1.f) + D * vb[j * trows + pr]);
+        } else {
+          for (int o = tpr / 2; o >= 1; o >>= 1)
+#pragma unroll
+            for (int j = 0; j < RB; ++j) sum[j] += __shfl_xor(sum[j], o, 64);
+          if (lane_ok && c4 == 0 && p0 + pr < P)
+#pragma unroll
+            for (int j = 0; j < RB; ++j)
+              st_dev(a.mem + (((int64_t)r * RB + j) * nh + h) * P + p0 + pr,
+                     sum[j] * (sh.gdn ? iq[j] : 1.f) + D * vb[j * trows + pr]);
+        }
+      }
     } else {
+      float sum[RB];
+#pragma unroll
+      for (int j = 0; j < RB; ++j) {
+        const f32x4 c = *reinterpret_cast<const f32x4*>(Cl + j * N + 4 * c4);
+        sum[j] = lane_ok ? hv[0][0] * c[0] + hv[0][1] * c[1] + hv[0][2] * c[2] + hv[0][3] * c[3] : 0.f;
+      }
 #pragma unroll
       for (int j = 0; j < RB; ++j) red[j * RT + t] = sum[j];
       __syncthreads();
@@ -209,7 +305,8 @@ __device__ __forceinline__ void round_tile(const Shape& sh, const RoundArgs& a, 
         if (pp >= P) continue;
         float acc = 0.f;
         for (int c = 0; c < tpr; ++c) acc += red[j * RT + pr * tpr + c];
-        st_dev(a.mem + (((int64_t)r * RB + j) * nh + h) * P + pp, acc * (sh.gdn ? iq[j] : 1.f) + D * vb[idx]);
+        st_dev(a.mem + (((int64_t)r * RB + j) * nh + h) * P + pp,
+               acc * (sh.gdn ? iq[j] : 1.f) + D * vb[j * trows + pr]);
       }
     }
   }
@@ -221,120 +318,165 @@ __device__ __forceinline__ void round_tile(const Shape& sh, const RoundArgs& a, 
     const int first = nrows > W ? nrows - W : 0;
     T* K = ring_ptr<T>(a.state_pool, sh, slot, sh.st_k, h);
     T* V = ring_ptr<T>(a.state_pool, sh, slot, sh.st_v, h);
-    for (int idx = t; idx < (nrows - first) * P; idx += RT) {
-      const int tt = first + idx / P, pp = idx % P;
-      const int64_t s = (count + tt) % W;
-      K[s * P + pp] = from_f32<T>(a.proj[(crow0 + tt) * ld + sh.off_k + h * P + pp]);
-      V[s * P + pp] = from_f32<T>(a.proj[(crow0 + tt) * ld + sh.off_v + h * P + pp]);
-    }
-  }
-}
-
-// Four consecutive elements (8-byte aligned for bf16, 16-byte for fp32) as fp32.
-__device__ __forceinline__ f32x4 ld4f(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
-__device__ __forceinline__ f32x4 ld4f(const bf16* p) {
-  typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
-  const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
-  return f32x4{static_cast<float>(v[0]), static_cast<float>(v[1]), static_cast<float>(v[2]), static_cast<float>(v[3])};
-}
-
-// Scores and outputs of one split on fp32 MFMAs (16x16x4): keys from K (row stride P, up to 64
-// rows), values from V, queries qs [RB][P] f32.  Wave w computes S^T for keys 16 w .. 16 w + 15
-// against the 8 queries (padded to 16 columns); lane (li, lg) supplies, for instruction j of a
-// group of four, dimension p0 + 4 lg + j of key 16 w + li and of query li, so one 4-element load
-// of each operand feeds four instructions.  Softmax over the 64 keys meets in LDS; the
-// probabilities go to LDS and a second set of MFMAs forms P . V with wave w on the 16-column
-// tiles w, w + 4, ... of the output.  Keys at or past nk are masked (their rows may hold
-// anything: their scores are discarded and their values are multiplied by nothing).
-template <typename KT>
-__device__ __forceinline__ void attn_split(const Shape& sh, int nk, bool blk, const float* qs, const KT* K,
-                                           const KT* V, float* pl, float* red, float* op, float* ml) {
-  const int P = sh.P, t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int li = lane & 15, lg = lane >> 4;
-  const float scale = rsqrtf((float)P);
-  // ---- scores S^T[key][q]
-  f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int krow = 16 * wave + li;
-  if (16 * wave < nk) {
-#pragma unroll 4
-    for (int p0 = 0; p0 < P; p0 += 16) {
-      const f32x4 kv = ld4f(K + krow * P + p0 + 4 * lg);
-      f32x4 qv = *reinterpret_cast<const f32x4*>(qs + li * P + p0 + 4 * lg);  // rows >= RB: masked
-      if (li >= RB) qv = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) s = Mfma16<float>::mma(kv[j], qv[j], s);
-    }
-  }
-  // lane (li, lg) register rr: key 16 w + 4 lg + rr, query li
-  float e[4];
-  float mloc = -INFINITY;
-#pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    const int key = 16 * wave + 4 * lg + rr;
-    bool ok = key < nk && li < RB;
-    if (blk && !sh.cross && key != li) ok = false;
-    e[rr] = ok ? s[rr] * scale : -INFINITY;
-    mloc = fmaxf(mloc, e[rr]);
-  }
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-  if (lg == 0) red[wave * 16 + li] = mloc;
-  __syncthreads();
-  float m = -INFINITY;
-#pragma unroll
-  for (int w2 = 0; w2 < 4; ++w2) m = fmaxf(m, red[w2 * 16 + li]);
-  float lsum = 0.f;
-#pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    e[rr] = e[rr] == -INFINITY ? 0.f : expf(e[rr] - m);
-    lsum += e[rr];
-    pl[li * ATT_KS + 16 * wave + 4 * lg + rr] = e[rr];
-  }
-  lsum += __shfl_xor(lsum, 16, 64);
-  lsum += __shfl_xor(lsum, 32, 64);
-  if (lg == 0) red[64 + wave * 16 + li] = lsum;
-  __syncthreads();
-  if (wave == 0 && lg == 0 && li < RB) {
-    st_dev(ml + 2 * li, m);
-    st_dev(ml + 2 * li + 1, red[64 + li] + red[64 + 16 + li] + red[64 + 32 + li] + red[64 + 48 + li]);
-  }
-  // ---- O[q][p] = sum_key pl[q][key] V[key][p]
-  const int nks = (nk + 3) / 4 * 4;
-  for (int pt = wave; pt * 16 < P; pt += 4) {
-    f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-    for (int k0 = 0; k0 < nks; k0 += 16) {
-      const f32x4 pa = *reinterpret_cast<const f32x4*>(pl + li * ATT_KS + k0 + 4 * lg);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = k0 + 4 * lg + j;
-        const float vv = key < nk ? to_f32(V[key * P + pt * 16 + li]) : 0.f;
-        o = Mfma16<float>::mma(pa[j], vv, o);
+    for (int tt = first; tt < nrows; ++tt) {
+      const int64_t s = (count + tt) % W;  // uniform
+      for (int pp = t; pp < P; pp += RT) {
+        K[s * P + pp] = from_f32<T>(a.proj[(crow0 + tt) * ld + sh.off_k + h * P + pp]);
+        V[s * P + pp] = from_f32<T>(a.proj[(crow0 + tt) * ld + sh.off_v + h * P + pp]);
       }
     }
-    // lane (li, lg) register rr: query 4 lg + rr, column pt * 16 + li
-    if (lg < 2)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) st_dev(op + (4 * lg + rr) * P + pt * 16 + li, o[rr]);
   }
 }
 
-// Attention LDS (bytes): ring K, V of the split [ATT_KS][P] storage dtype | q [RB][P] f32 |
-// k, v of the round's committed rows (or of the block rows) [RB][P] f32 each | probabilities
-// [16][ATT_KS] | softmax scratch [128].
+// Eight consecutive elements (16-byte aligned) as fp32, and two as fp32 (4-byte aligned bf16,
+// 8-byte aligned fp32).
+__device__ __forceinline__ void ld8f(const float* p, float* o) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[i] = a[i];
+    o[4 + i] = b[i];
+  }
+}
+__device__ __forceinline__ void ld8f(const bf16* p, float* o) {
+  const bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = static_cast<float>(v[i]);
+}
+__device__ __forceinline__ void ld2f(const float* p, float& x, float& y) {
+  typedef __attribute__((ext_vector_type(2))) float f32x2;
+  const f32x2 v = *reinterpret_cast<const f32x2*>(p);
+  x = v[0];
+  y = v[1];
+}
+__device__ __forceinline__ void ld2f(const bf16* p, float& x, float& y) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  const bf16x2 v = *reinterpret_cast<const bf16x2*>(p);
+  x = static_cast<float>(v[0]);
+  y = static_cast<float>(v[1]);
+}
+
+// Attention of the 8 block rows over nk keys (at most ks) of one split, on the vector ALUs: wave w
+// owns queries 2w and 2w + 1 (fp32, qs [RB][P]); lane l scores keys l, l + 64, ... against both
+// (dot products over P with the key row read from LDS, 8 elements at a time; the query rows are
+// read by every lane at once, a broadcast), so the softmax of a query is a reduction inside one
+// wave.  The probabilities go to the wave's two rows of pl ([RB][ks + 4]); then lane l forms
+// output columns 2l, 2l + 1 (and 2l + 128, 2l + 129 when P > 128) of both queries, key by key.
+// Keys at or past nk are masked (their rows may hold anything; they are never read).
+template <typename KT>
+__device__ __forceinline__ void attn_split(const Shape& sh, int nk, int ks, bool blk, const float* qs, const KT* K,
+                                           const KT* V, float* pl, float* red, float* op, float* ml) {
+  (void)red;
+  const int P = sh.P, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int q0 = 2 * wave, q1 = q0 + 1;
+  const float scale = rsqrtf((float)P);
+  const int pls = ks + 4;
+  float m0 = -INFINITY, m1 = -INFINITY;
+  // ---- scores of this lane's keys
+  for (int key = lane; key < ks; key += 64) {
+    float s0 = -INFINITY, s1 = -INFINITY;
+    if (key < nk) {
+      const KT* kr = K + key * P;
+      float a0 = 0.f, a1 = 0.f;
+#pragma unroll 2
+      for (int p0 = 0; p0 < P; p0 += 8) {
+        float kv[8], qa[8], qb[8];
+        ld8f(kr + p0, kv);
+        ld8f(qs + q0 * P + p0, qa);
+        ld8f(qs + q1 * P + p0, qb);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          a0 = fmaf(kv[i], qa[i], a0);
+          a1 = fmaf(kv[i], qb[i], a1);
+        }
+      }
+      s0 = a0 * scale;
+      s1 = a1 * scale;
+      if (blk && !sh.cross) {  // block keys: each row sees only itself
+        if (key != q0) s0 = -INFINITY;
+        if (key != q1) s1 = -INFINITY;
+      }
+    }
+    pl[q0 * pls + key] = s0;
+    pl[q1 * pls + key] = s1;
+    m0 = fmaxf(m0, s0);
+    m1 = fmaxf(m1, s1);
+  }
+  m0 = wave_max64(m0);
+  m1 = wave_max64(m1);
+  float l0 = 0.f, l1 = 0.f;
+  for (int key = lane; key < ks; key += 64) {
+    const float e0 = pl[q0 * pls + key], e1 = pl[q1 * pls + key];
+    const float p0 = e0 == -INFINITY ? 0.f : __expf(e0 - m0);
+    const float p1 = e1 == -INFINITY ? 0.f : __expf(e1 - m1);
+    pl[q0 * pls + key] = p0;
+    pl[q1 * pls + key] = p1;
+    l0 += p0;
+    l1 += p1;
+  }
+  l0 = wave_sum64(l0);
+  l1 = wave_sum64(l1);
+  if (lane == 0) {
+    st_dev(ml + 2 * q0, m0);
+    st_dev(ml + 2 * q0 + 1, l0);
+    st_dev(ml + 2 * q1, m1);
+    st_dev(ml + 2 * q1 + 1, l1);
+  }
+  // the wave's probability rows are read by all of its lanes below
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // ---- O[q][p] = sum_key p[q][key] V[key][p], four keys per step
+  const float* pr0 = pl + q0 * pls;
+  const float* pr1 = pl + q1 * pls;
+  for (int c = 2 * lane; c < P; c += 128) {
+    float o00 = 0.f, o01 = 0.f, o10 = 0.f, o11 = 0.f;
+    const KT* vc = V + c;
+    int key = 0;
+    for (; key + 4 <= nk; key += 4) {
+      const f32x4 pa = *reinterpret_cast<const f32x4*>(pr0 + key);
+      const f32x4 pb = *reinterpret_cast<const f32x4*>(pr1 + key);
+      float vx[4], vy[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) ld2f(vc + (key + u) * P, vx[u], vy[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        o00 = fmaf(pa[u], vx[u], o00);
+        o01 = fmaf(pa[u], vy[u], o01);
+        o10 = fmaf(pb[u], vx[u], o10);
+        o11 = fmaf(pb[u], vy[u], o11);
+      }
+    }
+    for (; key < nk; ++key) {
+      float vx, vy;
+      ld2f(vc + key * P, vx, vy);
+      o00 = fmaf(pr0[key], vx, o00);
+      o01 = fmaf(pr0[key], vy, o01);
+      o10 = fmaf(pr1[key], vx, o10);
+      o11 = fmaf(pr1[key], vy, o11);
+    }
+    st_dev(op + q0 * P + c, o00);
+    st_dev(op + q0 * P + c + 1, o01);
+    st_dev(op + q1 * P + c, o10);
+    st_dev(op + q1 * P + c + 1, o11);
+  }
+}
+
+// Attention LDS (bytes): ring K, V of the split [ks][P] storage dtype (the block split: the block
+// rows' k, v [RB][P] f32 in the same places) | q [RB][P] f32 | probabilities [RB][ks + 4] |
+// scratch [128].
 template <typename T>
 __device__ __forceinline__ void round_attn(const Shape& sh, const RoundArgs& a, const ReqTable& rt, int r, int h,
                                            int sp, char* smem) {
   constexpr int VN = Vec16<T>::n;
-  const int nh = sh.nh, P = sh.P, W = sh.W;
+  constexpr int FIX = (RB * 256 + RT - 1) / RT;  // committed-row elements per thread (P <= 256)
+  const int nh = sh.nh, P = sh.P, W = sh.W, ks = a.ks;
+  const int kvb = up1k(ks * P * (int)sizeof(T)) > up1k(RB * P * 4) ? up1k(ks * P * (int)sizeof(T)) : up1k(RB * P * 4);
   T* kst = reinterpret_cast<T*>(smem);
-  T* vst = reinterpret_cast<T*>(smem + up1k(ATT_KS * P * (int)sizeof(T)));
-  float* qs = reinterpret_cast<float*>(reinterpret_cast<char*>(vst) + up1k(ATT_KS * P * (int)sizeof(T)));
-  float* nkf = reinterpret_cast<float*>(reinterpret_cast<char*>(qs) + up1k(RB * P * 4));
-  float* nvf = reinterpret_cast<float*>(reinterpret_cast<char*>(nkf) + up1k(RB * P * 4));
-  float* pl = reinterpret_cast<float*>(reinterpret_cast<char*>(nvf) + up1k(RB * P * 4));
-  float* red = pl + 16 * ATT_KS;
-  __shared__ int64_t s_count;
+  T* vst = reinterpret_cast<T*>(smem + kvb);
+  float* qs = reinterpret_cast<float*>(smem + 2 * kvb);
+  float* pl = reinterpret_cast<float*>(reinterpret_cast<char*>(qs) + up1k(RB * P * 4));
+  float* red = pl + RB * (ks + 4);
   const int slot = rt.slot[r];
   const int t = threadIdx.x;
   const int64_t ld = a.ld;
@@ -342,40 +484,52 @@ __device__ __forceinline__ void round_attn(const Shape& sh, const RoundArgs& a, 
   const bool blk = sp == a.n_split - 1;
   const int nrows = a.do_commit ? rt.row0[r + 1] - rt.row0[r] : 0;
   const int64_t crow0 = rt.row0[r];
-  const int k0 = sp * ATT_KS;
+  const int k0 = sp * ks;
   const int P4 = P / 4;
 
-  // Every load is independent of the committed count, so all go out together: the count, q, the
-  // split's ring slots (always inside the ring), and the k, v of the round's committed rows (they
-  // replace the slots this round's append overwrites) or of the block rows.
-  if (!blk && t == 0) s_count = *count_ptr(a.state_pool, sh, slot);
+  // Every load is independent of the committed count, so all go out together: q, the split's ring
+  // slots (always inside the ring) or the block rows' k, v, and (into registers) the k, v of the
+  // round's last committed rows, which replace the slots this round's append overwrites.
   stage16(RB * P4, qs, [&](int i) { return a.proj + (brow0 + i / P4) * ld + sh.off_q + h * P + 4 * (i % P4); });
+  const int m = nrows < W ? nrows : W;  // committed rows that land in the ring
+  float fk[FIX], fv[FIX];
   if (blk) {
-    stage16(RB * P4, nkf, [&](int i) { return a.proj + (brow0 + i / P4) * ld + sh.off_k + h * P + 4 * (i % P4); });
-    stage16(RB * P4, nvf, [&](int i) { return a.proj + (brow0 + i / P4) * ld + sh.off_v + h * P + 4 * (i % P4); });
+    float* bk = reinterpret_cast<float*>(kst);
+    float* bv = reinterpret_cast<float*>(vst);
+    stage16(RB * P4, bk, [&](int i) { return a.proj + (brow0 + i / P4) * ld + sh.off_k + h * P + 4 * (i % P4); });
+    stage16(RB * P4, bv, [&](int i) { return a.proj + (brow0 + i / P4) * ld + sh.off_v + h * P + 4 * (i % P4); });
   } else {
-    const int nslots = W - k0 < ATT_KS ? W - k0 : ATT_KS;
+    const int nslots = W - k0 < ks ? W - k0 : ks;
     const T* K = ring_ptr<T>(a.state_pool, sh, slot, sh.st_k, h) + (int64_t)k0 * P;
     const T* V = ring_ptr<T>(a.state_pool, sh, slot, sh.st_v, h) + (int64_t)k0 * P;
     stage16(nslots * P / VN, kst, [&](int i) { return K + i * VN; });
     stage16(nslots * P / VN, vst, [&](int i) { return V + i * VN; });
-    stage16(nrows * P4, nkf, [&](int i) { return a.proj + (crow0 + i / P4) * ld + sh.off_k + h * P + 4 * (i % P4); });
-    stage16(nrows * P4, nvf, [&](int i) { return a.proj + (crow0 + i / P4) * ld + sh.off_v + h * P + 4 * (i % P4); });
+#pragma unroll
+    for (int e = 0; e < FIX; ++e) {
+      const int idx = t + e * RT;
+      fk[e] = fv[e] = 0.f;
+      if (idx < m * P) {
+        const int64_t row = crow0 + nrows - m + idx / P;
+        fk[e] = a.proj[row * ld + sh.off_k + h * P + idx % P];
+        fv[e] = a.proj[row * ld + sh.off_v + h * P + idx % P];
+      }
+    }
   }
+  const int64_t count = blk ? 0 : *count_ptr(a.state_pool, sh, slot);
   vm_wait<0>();
   __syncthreads();
 
   float* op = a.att_part + ((((int64_t)r * nh + h) * a.n_split + sp) * RB) * P;
   float* ml = a.att_ml + ((((int64_t)r * nh + h) * a.n_split + sp) * RB) * 2;
   if (blk) {
-    attn_split(sh, RB, true, qs, nkf, nvf, pl, red, op, ml);
+    attn_split(sh, RB, ks, true, qs, reinterpret_cast<const float*>(kst), reinterpret_cast<const float*>(vst), pl,
+               red, op, ml);
     return;
   }
-  const int64_t count = s_count;
   const int64_t tot = count + nrows;
   const int valid = (int)(tot < W ? tot : W);
   int nk = valid - k0;
-  nk = nk < 0 ? 0 : (nk > ATT_KS ? ATT_KS : nk);
+  nk = nk < 0 ? 0 : (nk > ks ? ks : nk);
   if (nk == 0) {
     for (int idx = t; idx < RB * P; idx += RT) st_dev(op + idx, 0.f);
     if (t < RB) {
@@ -384,30 +538,33 @@ __device__ __forceinline__ void round_attn(const Shape& sh, const RoundArgs& a, 
     }
     return;
   }
-  if (nrows > 0) {
+  if (m > 0) {
     // the slots this round's append overwrites take its rows, rounded as the ring stores them:
-    // slot (count + j) mod W holds row j for the last m = min(nrows, W) rows
-    const int m = nrows < W ? nrows : W;
+    // slot (count + nrows - m + j) mod W holds committed row nrows - m + j
     const int lead = (int)((count + nrows - m) % W);
-    for (int idx = t; idx < m * P; idx += RT) {
-      const int jn = idx / P, pp = idx % P;
-      const int key = (lead + jn) % W - k0;
-      if (key >= 0 && key < nk) {
-        kst[key * P + pp] = from_f32<T>(nkf[(nrows - m + jn) * P + pp]);
-        vst[key * P + pp] = from_f32<T>(nvf[(nrows - m + jn) * P + pp]);
+#pragma unroll
+    for (int e = 0; e < FIX; ++e) {
+      const int idx = t + e * RT;
+      if (idx < m * P) {
+        int key = lead + idx / P;
+        if (key >= W) key -= W;
+        key -= k0;
+        if (key >= 0 && key < nk) {
+          kst[key * P + idx % P] = from_f32<T>(fk[e]);
+          vst[key * P + idx % P] = from_f32<T>(fv[e]);
+        }
       }
     }
     __syncthreads();
   }
-  attn_split(sh, nk, false, qs, kst, vst, pl, red, op, ml);
+  attn_split(sh, nk, ks, false, qs, kst, vst, pl, red, op, ml);
 }
 
 // Merge of one (request, head): the partials of MCH splits at a time are staged in LDS together
 // with the (max, sum) pairs and the readout (one round trip); per (split, row) factors
 // exp(max_s - max) are formed once, in parallel, then every output sums its splits.
 // Merge LDS (bytes): (max, sum) [ns][RB][2] | factors [ns][RB] | row maxima and sums [2 RB] |
-// readout [RB][P] | partials [min(MCH, ns)][RB][P] (sized for the splits there are: with 9 splits
-// the kernel's LDS stays at the attention's 34 KiB, four workgroups per CU instead of three).
+// readout [RB][P] | partials [min(MCH, ns)][RB][P] (sized for the splits there are).
 constexpr int MCH = 16;
 template <typename T>
 __device__ __forceinline__ void round_merge(const Shape& sh, const RoundArgs& a, int r, int h, char* smem) {
@@ -472,8 +629,8 @@ __device__ __forceinline__ void round_merge(const Shape& sh, const RoundArgs& a,
   }
 }
 
-template <typename T>
-__global__ void __launch_bounds__(RT) k_round(Shape sh, RoundArgs a, ReqTable rt) {
+template <typename T, int TMAXG>
+__device__ __forceinline__ void round_body(const Shape& sh, const RoundArgs& a, const ReqTable& rt) {
   extern __shared__ __attribute__((aligned(16))) char dsm[];
   __shared__ int s_last;
   const int nh = sh.nh;
@@ -481,7 +638,7 @@ __global__ void __launch_bounds__(RT) k_round(Shape sh, RoundArgs a, ReqTable rt
   const int rh = blockIdx.x / per, role = blockIdx.x % per;
   const int r = rh / nh, h = rh % nh;
   if (role < a.n_tiles)
-    round_tile<T>(sh, a, rt, r, h, role, dsm);
+    round_tile<T, TMAXG>(sh, a, rt, r, h, role, dsm);
   else
     round_attn<T>(sh, a, rt, r, h, role - a.n_tiles, dsm);
 
@@ -499,6 +656,18 @@ __global__ void __launch_bounds__(RT) k_round(Shape sh, RoundArgs a, ReqTable rt
   if (threadIdx.x == 0 &&
       __hip_atomic_fetch_add(a.counters + rt.n_req * nh + r, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nh - 1)
     *count_ptr(a.state_pool, sh, rt.slot[r]) += rt.row0[r + 1] - rt.row0[r];
+}
+
+// Tiles of one row pass (the narrow layout): the register budget keeps five workgroups on a CU.
+template <typename T, int TMAXG>
+__global__ void __launch_bounds__(RT) __attribute__((amdgpu_waves_per_eu(5))) k_round(Shape sh, RoundArgs a,
+                                                                                     ReqTable rt) {
+  round_body<T, TMAXG>(sh, a, rt);
+}
+// Tiles of up to WIDE_PASSES row passes (the wide layout).
+template <typename T, int TMAXG>
+__global__ void __launch_bounds__(RT) k_round_wide(Shape sh, RoundArgs a, ReqTable rt) {
+  round_body<T, TMAXG>(sh, a, rt);
 }
 
 template <typename T>
@@ -547,47 +716,89 @@ __global__ void k_reset_states(char* pool, Shape sh, ReqTable rt) {
     p[i] = 0u;
 }
 
-// Rows of H per commit tile and tiles per head.
-int round_rows_per_tile(const Shape& sh) { return RT / (sh.N / 4); }
-int round_tiles(const Shape& sh) { return (sh.P + round_rows_per_tile(sh) - 1) / round_rows_per_tile(sh); }
+// Layout of a round launch: rows of H per commit tile and keys per attention split.  The narrow
+// layout (tiles of one row pass, 64-key splits) spreads one head over ~20 small workgroups; it is
+// the faster one at every Qwen3-4B-shaped batch measured (64 requests: 300 us against 358 us for
+// the wide one).  The wide layout (tiles of up to WIDE_PASSES row passes, splits of up to 128 keys)
+// moves more bytes per workgroup and is taken for heads of 128 or more dimensions over many
+// (request, head) pairs, where it measured faster (16 Phi-4-shaped requests: 178 us against 193 us).
+constexpr int WIDE_MIN_PAIRS = 256;
+constexpr int WIDE_MIN_P = 128;
+constexpr int WIDE_KS = 128;
+static int attn_lds(const Shape& sh, int esz, int ks) {
+  // the block split keeps fp32 k, v rows where the ring splits keep ks ring slots
+  const int kv = up1k(ks * sh.P * esz) > up1k(RB * sh.P * 4) ? up1k(ks * sh.P * esz) : up1k(RB * sh.P * 4);
+  return 2 * kv + up1k(RB * sh.P * 4) + 4 * (RB * (ks + 4) + 128);
+}
+void round_layout(const Shape& sh, int n_req, int esz, RoundArgs* a) {
+  const int tpr = sh.N / 4;
+  const int rows_wg = RT / tpr;
+  const bool pow2 = (tpr & (tpr - 1)) == 0;
+  const bool wide = (int64_t)n_req * sh.nh >= WIDE_MIN_PAIRS && sh.P >= WIDE_MIN_P;
+  int passes = 1;
+  if (wide && pow2) {
+    passes = (sh.P + rows_wg - 1) / rows_wg;
+    if (passes > WIDE_PASSES) passes = WIDE_PASSES;
+  }
+  a->tile_rows = passes * rows_wg;
+  a->n_tiles = (sh.P + a->tile_rows - 1) / a->tile_rows;
+  int ks = KS_MIN;
+  if (wide) {
+    ks = WIDE_KS;
+    // no wider than the window needs, and LDS for at least two workgroups per CU
+    while (ks > KS_MIN && (ks / 2 >= sh.W || attn_lds(sh, esz, ks) > 80 * 1024)) ks /= 2;
+  }
+  a->ks = ks;
+  a->n_split = (sh.W + ks - 1) / ks + 1;
+}
+int round_max_splits(const Shape& sh) { return (sh.W + KS_MIN - 1) / KS_MIN + 1; }
 
-size_t round_lds_bytes(const Shape& sh, int esz, int n_split) {
-  const int rw = round_rows_per_tile(sh);
+size_t round_lds_bytes(const Shape& sh, int esz, const RoundArgs& a) {
+  const int rw = a.tile_rows;
   const size_t tile = (size_t)up1k(RMAXC * sh.N * 4) + up1k(RB * sh.N * 4) + up1k(RMAXC * rw * 4) + up1k(RB * rw * 4) +
                       4 * (3 * RMAXC + 4 + RB + RB * RT);
-  const size_t attn = (size_t)2 * up1k(ATT_KS * sh.P * esz) + 3 * up1k(RB * sh.P * 4) + 4 * (16 * ATT_KS + 128);
-  const size_t merge = n_split ? (size_t)up1k(n_split * RB * 2 * 4) + up1k(n_split * RB * 4) + 4 * 256 +
-                                     up1k(RB * sh.P * 4) + up1k((n_split < MCH ? n_split : MCH) * RB * sh.P * 4)
-                               : 0;
+  const size_t attn = a.n_split ? (size_t)attn_lds(sh, esz, a.ks) : 0;
+  const int ns = a.do_draft ? a.n_split : 0;
+  const size_t merge = ns ? (size_t)up1k(ns * RB * 2 * 4) + up1k(ns * RB * 4) + 4 * 256 + up1k(RB * sh.P * 4) +
+                                up1k((ns < MCH ? ns : MCH) * RB * sh.P * 4)
+                          : 0;
   size_t m = tile > attn ? tile : attn;
   return m > merge ? m : merge;
 }
 
-hipError_t launch_round(int dtype, const Shape& sh, const RoundArgs& a, const ReqTable& rt, hipStream_t s) {
-  const int per = a.n_tiles + a.n_split;
-  const size_t lds = round_lds_bytes(sh, dtype == HYF_BF16 ? 2 : 4, a.do_draft ? a.n_split : 0);
+template <typename T, int G>
+static hipError_t launch_round_t(const Shape& sh, const RoundArgs& a, const ReqTable& rt, size_t lds, hipStream_t s) {
+  void (*kern)(Shape, RoundArgs, ReqTable);
+  if constexpr (G == 1)
+    kern = k_round<T, G>;
+  else
+    kern = k_round_wide<T, G>;
   if (lds > 65536) {
     // Above 64 KiB of dynamic LDS the kernel has to opt in (gfx950 has 160 KiB per workgroup).
-    // Done once per process with the largest size any shape needs, so later calls (possibly under
-    // stream capture) launch only kernels.
+    // Done once per process and instantiation with the largest size any shape needs, so later calls
+    // (possibly under stream capture) launch only kernels.
     static std::once_flag once;
     static hipError_t set_err = hipSuccess;
-    std::call_once(once, [] {
-      const int mx = 160 * 1024 - 256;  // leaves room for the kernel's few bytes of static LDS
-      set_err = hipFuncSetAttribute(reinterpret_cast<const void*>(k_round<bf16>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, mx);
-      if (set_err == hipSuccess)
-        set_err = hipFuncSetAttribute(reinterpret_cast<const void*>(k_round<float>),
-                                      hipFuncAttributeMaxDynamicSharedMemorySize, mx);
+    std::call_once(once, [kern] {
+      set_err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    160 * 1024 - 256);
     });
     if (set_err != hipSuccess) return set_err;
   }
-  dim3 grid((unsigned)(rt.n_req * sh.nh * per));
-  if (dtype == HYF_BF16)
-    hipLaunchKernelGGL(k_round<bf16>, grid, dim3(RT), lds, s, sh, a, rt);
-  else
-    hipLaunchKernelGGL(k_round<float>, grid, dim3(RT), lds, s, sh, a, rt);
+  const int per = a.n_tiles + a.n_split;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(rt.n_req * sh.nh * per)), dim3(RT), lds, s, sh, a, rt);
   return hipGetLastError();
+}
+
+hipError_t launch_round(int dtype, const Shape& sh, const RoundArgs& a, const ReqTable& rt, hipStream_t s) {
+  const size_t lds = round_lds_bytes(sh, dtype == HYF_BF16 ? 2 : 4, a);
+  if (lds > 160 * 1024 - 256) return hipErrorInvalidValue;
+  const int rows_wg = RT / (sh.N / 4);
+  const bool wide = a.tile_rows > rows_wg;  // tiles of several row passes
+  if (wide && a.tile_rows > WIDE_PASSES * rows_wg) return hipErrorInvalidValue;
+  if (dtype == HYF_BF16)
+    return wide ? launch_round_t<bf16, WIDE_PASSES>(sh, a, rt, lds, s) : launch_round_t<bf16, 1>(sh, a, rt, lds, s);
+  return wide ? launch_round_t<float, WIDE_PASSES>(sh, a, rt, lds, s) : launch_round_t<float, 1>(sh, a, rt, lds, s);
 }
 
 hipError_t launch_ring_append(int dtype, const Shape& sh, char* pool, const ReqTable& rt, const void* k,

@@ -596,6 +596,40 @@ def test_split_invariance_of_commits():
         assert_close(H, ref, "f32", f"split {parts}")
 
 
+WIDE_SHAPES = [
+    ("tiny_fp32", I.TINY),
+    ("small_bf16_w40", small_shape("bf16", window=40)),
+    ("gdn_bf16", small_shape("bf16", window=100, memory="gdn")),
+    ("odd_bf16", small_shape("bf16", n_heads=5, head_dim=48, d_state=32, n_groups=5, window=20, chunk=32)),
+    ("noncross_fp32", small_shape("f32", window=24, cross_slot=0)),
+    # heads of 128 dimensions over 256 (request, head) pairs: the wide layout (whole-head tiles,
+    # 128-key splits)
+    ("wide_p128_bf16", small_shape("bf16", head_dim=128, window=300)),
+    ("wide_p128_gdn_fp32", small_shape("f32", head_dim=128, d_state=32, window=130, memory="gdn")),
+]
+
+
+@pytest.mark.parametrize("name,shape", WIDE_SHAPES, ids=[c[0] for c in WIDE_SHAPES])
+def test_rounds_of_many_requests_match_the_oracle(name, shape):
+    # 64 requests (256-320 (request, head) pairs) with ragged prefixes around the window, then
+    # rounds in which every request commits 0-8 rows; every request against the oracle.
+    R = 64
+    pr = Pair(shape, seed=81, pool_slots=R, max_requests=R, max_rows=300 * R)
+    pr.gpu.reset()
+    lens = [(37 * i) % 300 for i in range(R)]
+    say("wide layout prefill", name, "rows", sum(lens))
+    pr.commit([pr.rows(n) for n in lens])
+    acc_rng = pr.rng[4]
+    for rnd in range(3):
+        acc = [int(a) for a in acc_rng.integers(0, 9, size=R)]
+        say("wide layout round", rnd, name)
+        g, o = pr.draft([pr.rows(8, 3) for _ in range(R)], commits=[pr.rows(a) for a in acc])
+        for i in range(R):
+            assert_close(g[i], o[i], shape.dtype, f"{name} round {rnd} request {i}")
+    for i in (0, 13, 63):
+        pr.check_state(slot=i, what=f"{name} wide state {i}")
+
+
 def test_batched_requests_with_a_slot_table():
     shape = small_shape("bf16", window=48)
     R, pool = 5, 8
