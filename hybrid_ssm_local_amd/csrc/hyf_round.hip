@@ -10,6 +10,7 @@ constexpr int RB = HYF_BLOCK;   // block rows
 constexpr int RMAXC = 16;       // largest per-request commit a round kernel folds in
 constexpr int KS_MIN = 64;      // fewest keys per attention split (the workspace is sized for it)
 constexpr int WIDE_PASSES = 16; // most row passes of one commit / readout tile (wide layout)
+constexpr int MID_PASSES = 3;   // most row passes of a tile in the narrow layout
 constexpr int RT = 256;         // threads per round workgroup
 
 __device__ __forceinline__ int64_t* count_ptr(char* pool, const Shape& sh, int slot) {
@@ -658,7 +659,8 @@ __device__ __forceinline__ void round_body(const Shape& sh, const RoundArgs& a, 
     *count_ptr(a.state_pool, sh, rt.slot[r]) += rt.row0[r + 1] - rt.row0[r];
 }
 
-// Tiles of one row pass (the narrow layout): the register budget keeps five workgroups on a CU.
+// Tiles of up to MID_PASSES row passes (the narrow layout): the register budget keeps five
+// workgroups on a CU.
 template <typename T, int TMAXG>
 __global__ void __launch_bounds__(RT) __attribute__((amdgpu_waves_per_eu(5))) k_round(Shape sh, RoundArgs a,
                                                                                      ReqTable rt) {
@@ -734,11 +736,16 @@ void round_layout(const Shape& sh, int n_req, int esz, RoundArgs* a) {
   const int tpr = sh.N / 4;
   const int rows_wg = RT / tpr;
   const bool pow2 = (tpr & (tpr - 1)) == 0;
-  const bool wide = (int64_t)n_req * sh.nh >= WIDE_MIN_PAIRS && sh.P >= WIDE_MIN_P;
+  const bool many = (int64_t)n_req * sh.nh >= WIDE_MIN_PAIRS;
+  const bool wide = many && sh.P >= WIDE_MIN_P;
   int passes = 1;
+  const int need = (sh.P + rows_wg - 1) / rows_wg;  // row passes one head takes
   if (wide && pow2) {
-    passes = (sh.P + rows_wg - 1) / rows_wg;
-    if (passes > WIDE_PASSES) passes = WIDE_PASSES;
+    passes = need < WIDE_PASSES ? need : WIDE_PASSES;
+  } else if (many && pow2) {
+    // the narrow layout over many pairs: tiles of up to MID_PASSES passes, balanced over the head
+    const int tiles = (need + MID_PASSES - 1) / MID_PASSES;
+    passes = (need + tiles - 1) / tiles;
   }
   a->tile_rows = passes * rows_wg;
   a->n_tiles = (sh.P + a->tile_rows - 1) / a->tile_rows;
@@ -769,7 +776,7 @@ size_t round_lds_bytes(const Shape& sh, int esz, const RoundArgs& a) {
 template <typename T, int G>
 static hipError_t launch_round_t(const Shape& sh, const RoundArgs& a, const ReqTable& rt, size_t lds, hipStream_t s) {
   void (*kern)(Shape, RoundArgs, ReqTable);
-  if constexpr (G == 1)
+  if constexpr (G <= MID_PASSES)
     kern = k_round<T, G>;
   else
     kern = k_round_wide<T, G>;
@@ -794,11 +801,14 @@ hipError_t launch_round(int dtype, const Shape& sh, const RoundArgs& a, const Re
   const size_t lds = round_lds_bytes(sh, dtype == HYF_BF16 ? 2 : 4, a);
   if (lds > 160 * 1024 - 256) return hipErrorInvalidValue;
   const int rows_wg = RT / (sh.N / 4);
-  const bool wide = a.tile_rows > rows_wg;  // tiles of several row passes
+  const bool wide = a.tile_rows > MID_PASSES * rows_wg;  // tiles of more passes than the narrow kernel keeps
   if (wide && a.tile_rows > WIDE_PASSES * rows_wg) return hipErrorInvalidValue;
+  const bool one = a.tile_rows == rows_wg;  // tiles of one pass: the smallest register footprint
   if (dtype == HYF_BF16)
-    return wide ? launch_round_t<bf16, WIDE_PASSES>(sh, a, rt, lds, s) : launch_round_t<bf16, 1>(sh, a, rt, lds, s);
-  return wide ? launch_round_t<float, WIDE_PASSES>(sh, a, rt, lds, s) : launch_round_t<float, 1>(sh, a, rt, lds, s);
+    return wide ? launch_round_t<bf16, WIDE_PASSES>(sh, a, rt, lds, s)
+                : one ? launch_round_t<bf16, 1>(sh, a, rt, lds, s) : launch_round_t<bf16, MID_PASSES>(sh, a, rt, lds, s);
+  return wide ? launch_round_t<float, WIDE_PASSES>(sh, a, rt, lds, s)
+              : one ? launch_round_t<float, 1>(sh, a, rt, lds, s) : launch_round_t<float, MID_PASSES>(sh, a, rt, lds, s);
 }
 
 hipError_t launch_ring_append(int dtype, const Shape& sh, char* pool, const ReqTable& rt, const void* k,
