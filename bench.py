@@ -106,10 +106,22 @@ def weights_struct(hf, w_in, w_out, a_log, dt_bias, d_skip):
 
 
 def layer_weights(torch, hf, I, shape, rng, copies=1):
+    """Device weights of one layer (`copies` copies of the projection weights) and their C structs.
+    With 4-bit weights (shape.weights == "w4") the projections get random codes and scales: the
+    timing does not depend on their values."""
     w = I.make_weights(shape, rng)
+    vec = [hf.to_device(w[k], shape, storage=False) for k in ("a_log", "dt_bias", "d_skip")]
+    if shape.weights == "w4":
+        q = []
+        for _ in range(copies):
+            qi, si = I.random_w4(rng, shape.n_in, shape.d_model)
+            qo, so = I.random_w4(rng, shape.d_model, shape.dq)
+            q.append([torch.from_numpy(a).cuda() for a in (qi, si, qo, so)])
+        structs = [hf.HyfWeights(None, None, *[v.data_ptr() for v in vec], *[a.data_ptr() for a in q[i]])
+                   for i in range(copies)]
+        return w, dict(w_in=None, w_out=None, q=q, vec=vec, structs=structs)
     w_in = [hf.to_device(w["w_in"], shape) for _ in range(copies)]
     w_out = [hf.to_device(w["w_out"], shape) for _ in range(copies)]
-    vec = [hf.to_device(w[k], shape, storage=False) for k in ("a_log", "dt_bias", "d_skip")]
     structs = [weights_struct(hf, w_in[i], w_out[i], *vec) for i in range(copies)]
     return w, dict(w_in=w_in, w_out=w_out, vec=vec, structs=structs)
 
@@ -314,11 +326,11 @@ class EpisodesB1:
     requests' episodes interleaved (each call is batch 1, on its own state) with W_COPIES weight
     copies rotated call by call, so weights and states come from HBM."""
 
-    def __init__(self, torch, hf, I, name="qwen3_4b_bf16", memory="mamba2"):
+    def __init__(self, torch, hf, I, name="qwen3_4b_bf16", memory="mamba2", weights="dense"):
         import numpy as np
 
         wl = I.WORKLOADS[name]
-        self.shape = sh = wl["shape"].replace(memory=memory)
+        self.shape = sh = wl["shape"].replace(memory=memory, weights=weights)
         self.T, self.rounds = wl["prefix"], wl["rounds"]
         d = sh.d_model
         rng = I.rng_streams(wl["seed"])
@@ -390,8 +402,13 @@ class EpisodesB1:
         def projs(i):
             s = stream.cuda_stream
             kk[0] = (kk[0] + 1) % W_COPIES
-            st[0] |= hf.hyf_linear(self.cfg, xin, M[i], d, self.wd["w_in"][kk[0]], sh.n_in, y, 1, s)
-            st[0] |= hf.hyf_linear(self.cfg, xo, 8, sh.dq, self.wd["w_out"][kk[0]], d, self.out, 0, s)
+            if sh.weights == "w4":
+                qi, si, qo, so = self.wd["q"][kk[0]]
+                st[0] |= hf.hyf_linear_w4(self.cfg, xin, M[i], d, qi, si, sh.n_in, y, 1, s)
+                st[0] |= hf.hyf_linear_w4(self.cfg, xo, 8, sh.dq, qo, so, d, self.out, 0, s)
+            else:
+                st[0] |= hf.hyf_linear(self.cfg, xin, M[i], d, self.wd["w_in"][kk[0]], sh.n_in, y, 1, s)
+                st[0] |= hf.hyf_linear(self.cfg, xo, 8, sh.dq, self.wd["w_out"][kk[0]], d, self.out, 0, s)
 
         t_proj = time_graph(torch, projs, nr, stream=stream)
         if st[0]:
@@ -847,13 +864,14 @@ def cpu_model():
     return "unknown"
 
 
-def cpu_baseline(I, host_w, wl_name=HEADLINE, rounds_timed=32):
-    """The float64 oracle on the host cores, on a bounded sample of the headline workload: the
-    request of median prefix length commits its whole prefix, then `rounds_timed` of its rounds;
-    one request's episode (prefix + all its rounds) is scaled from those, and the rate is draft
-    blocks/s of that request's episode (requests are independent, so 64 of them take 64 times as
-    long).  cores = process CPU time / wall time of the timed work (the per-token loops are
-    single-threaded Python; only the projections use BLAS threads)."""
+def cpu_baseline(I, host_w, wl_name=HEADLINE, min_seconds=12.0):
+    """The float64 oracle on the host cores, on a bounded sample of the headline workload: whole
+    request episodes (the request's prefix commit, then all of its rounds, each committing 1-8
+    accepted features and drafting a block), request after request with prefix lengths drawn like
+    the workload's, until at least min_seconds of work.  The rate is draft blocks/s over those
+    episodes; requests are independent, so 64 of them take 64 times as long.  cores = process CPU
+    time / wall time of the timed work (the per-token loops are single-threaded Python; only the
+    projections use BLAS threads)."""
     import numpy as np
 
     from oracle import hyflash_oracle as O
@@ -868,27 +886,36 @@ def cpu_baseline(I, host_w, wl_name=HEADLINE, rounds_timed=32):
     sh = wl["shape"]
     rng = I.rng_streams(wl["seed"] + 1000)
     lo, hi = wl["prefix_range"]
-    n_pre = (lo + hi) // 2
     w = {k: np.asarray(v, np.float64) for k, v in host_w.items()}
-    pre = I.make_rows(rng[1], n_pre, sh.d_model, wl["feat_scale"], sh.dtype)
-    acc = I.acceptance_lengths(rng[4], rounds_timed)
-    commits = [I.make_rows(rng[2], int(a), sh.d_model, wl["feat_scale"], sh.dtype) for a in acc]
-    blocks = [I.make_rows(rng[3], 8, sh.d_model, wl["block_scale"], sh.dtype) for _ in acc]
-    c0, t0 = time.process_time(), time.perf_counter()
-    st, _ = O.commit(sh, w, O.new_state(sh), pre)
-    t1 = time.perf_counter()
-    for cf, blk in zip(commits, blocks):
-        st, _ = O.round_step(sh, w, st, cf, blk)
-    t2 = time.perf_counter()
-    cpu = time.process_time() - c0
-    episode_s = (t1 - t0) + (t2 - t1) * wl["rounds"] / rounds_timed
-    return {"value": wl["rounds"] / episode_s, "unit": "draft blocks/s (headline workload)",
-            "cores": max(1, round(cpu / (t2 - t0))), "kind": "oracle",
-            "sample": f"float64 NumPy oracle, one request of the batched workload: a {n_pre}-feature prefix commit "
-                      f"(the median prefix) and {rounds_timed} of its {wl['rounds']} rounds, scaled to the request's "
-                      f"whole episode; requests are independent, so the rate is the workload's",
-            "cpu_model": cpu_model(), "threads_allowed": allowed, "seconds": t2 - t0,
-            "commit_feats_per_s": n_pre / (t1 - t0), "round_ms": 1e3 * (t2 - t1) / rounds_timed}
+    t_commit = t_rounds = cpu = 0.0
+    feats = blocks = 0
+    lens = []
+    while t_commit + t_rounds < min_seconds:
+        n_pre = int(rng[4].integers(lo, hi + 1))
+        lens.append(n_pre)
+        pre = I.make_rows(rng[1], n_pre, sh.d_model, wl["feat_scale"], sh.dtype)
+        acc = I.acceptance_lengths(rng[4], wl["rounds"])
+        commits = [I.make_rows(rng[2], int(a), sh.d_model, wl["feat_scale"], sh.dtype) for a in acc]
+        blks = [I.make_rows(rng[3], 8, sh.d_model, wl["block_scale"], sh.dtype) for _ in acc]
+        c0, t0 = time.process_time(), time.perf_counter()
+        st, _ = O.commit(sh, w, O.new_state(sh), pre)
+        t1 = time.perf_counter()
+        for cf, blk in zip(commits, blks):
+            st, _ = O.round_step(sh, w, st, cf, blk)
+        t2 = time.perf_counter()
+        cpu += time.process_time() - c0
+        t_commit += t1 - t0
+        t_rounds += t2 - t1
+        feats += n_pre
+        blocks += len(acc)
+    wall = t_commit + t_rounds
+    return {"value": blocks / wall, "unit": "draft blocks/s (headline workload)",
+            "cores": max(1, round(cpu / wall)), "kind": "oracle",
+            "sample": f"float64 NumPy oracle: {len(lens)} whole request episodes of the batched workload (prefixes "
+                      f"{lens} features, then {wl['rounds']} rounds each); requests are independent, so the rate is "
+                      f"the workload's",
+            "cpu_model": cpu_model(), "threads_allowed": allowed, "seconds": wall,
+            "commit_feats_per_s": feats / t_commit, "round_ms": 1e3 * t_rounds / blocks}
 
 
 # ---- main ----------------------------------------------------------------------------------------
@@ -961,6 +988,23 @@ def main():
                          "projections_graph_us": b1_proj},
     }
     del ep
+    torch.cuda.empty_cache()
+    log("batch-1 episodes, 4-bit weights")
+    ep4 = EpisodesB1(torch, hf, I, weights="w4")
+    b4 = run_steps(torch, ep4.step, sub_steps, 1)
+    b4_round, b4_proj, b4_rows = ep4.round_kernel(torch, hf)
+    w4b = (ep4.shape.n_in * ep4.shape.d_model + ep4.shape.d_model * ep4.shape.dq) // 2 + \
+        (ep4.shape.n_in * ep4.shape.d_model + ep4.shape.d_model * ep4.shape.dq) // 128 * 4
+    b4_rb = b1_rb - (ep4.shape.n_in + ep4.shape.dq) * ep4.shape.d_model * 2 + w4b
+    qwen_b1_w4 = {
+        "workload": "as qwen3_4b_batch1, with the projections' weights as 4-bit codes (random) and fp32 scales",
+        "value": b1_blocks / (b4["step_ms"] * 1e-3), "unit": "draft blocks/s per layer (batch 1)",
+        "ms_per_step": b4["step_ms"], "prefill_commit_us": 1e3 * b4["prefill_ms"] / EPISODES,
+        "round_us": 1e3 * b4["rounds_ms"] / b1_blocks, "round_graph_us": b4_round,
+        "round": {"bytes_per_round": b4_rb, **hbm(b4_rb, b4_round)}, "projections_graph_us": b4_proj,
+        "speedup_vs_bf16_round": b1_round / b4_round,
+    }
+    del ep4
     torch.cuda.empty_cache()
 
     # ---- Phi-4-shaped two-layer drafter
@@ -1041,6 +1085,7 @@ def main():
                                "shapes through hyf_linear), per round"},
         "round": {"bytes_per_round": rb, "avg_us": t_round, **hbm(rb, t_round)},
         "qwen3_4b_batch1": qwen_b1,
+        "qwen3_4b_batch1_w4": qwen_b1_w4,
         "phi4_two_layer": phi4_2l,
         "phi4_long131k": long5,
         "commit_scan": {"value": 8192 / (s_us * 1e-6), "unit": "committed feats/s", "T": 8192, "shape": "Qwen3-4B",

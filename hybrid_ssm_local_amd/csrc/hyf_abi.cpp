@@ -23,7 +23,7 @@ int check_cfg(const hyf_config* c) {
   if (!c) return HYF_EINVAL;
   if (c->dtype != HYF_F32 && c->dtype != HYF_BF16) return HYF_EDTYPE;
   if (c->memory != HYF_MEM_MAMBA2 && c->memory != HYF_MEM_GDN) return HYF_EINVAL;
-  if (c->reserved != 0) return HYF_EINVAL;
+  if (c->weights != HYF_WEIGHTS_DENSE && c->weights != HYF_WEIGHTS_W4) return HYF_EINVAL;
   if (c->cross_slot != 0 && c->cross_slot != 1) return HYF_EINVAL;
   if (c->d_model < 16 || c->d_model > 65536 || c->d_model % 16) return HYF_ESHAPE;
   if (c->n_heads < 1 || c->n_heads > 1024) return HYF_ESHAPE;
@@ -34,6 +34,9 @@ int check_cfg(const hyf_config* c) {
   if (c->block != HYF_BLOCK) return HYF_ESHAPE;
   if (c->chunk < 16 || c->chunk > 1024 || (c->chunk & (c->chunk - 1))) return HYF_ESHAPE;
   if ((int64_t)c->n_heads * c->head_dim > 65536) return HYF_ESHAPE;
+  if (c->weights == HYF_WEIGHTS_W4 &&
+      (c->dtype != HYF_BF16 || c->d_model % 128 || ((int64_t)c->n_heads * c->head_dim) % 128))
+    return HYF_EUNSUPPORTED;
   return HYF_OK;
 }
 
@@ -66,6 +69,7 @@ Shape make_shape(const hyf_config* c) {
   s.off_b = s.off_v + s.dq;
   s.off_dt = s.off_b + s.gn;
   s.gdn = c->memory == HYF_MEM_GDN;
+  s.w4 = c->weights == HYF_WEIGHTS_W4;
   s.off_beta = s.off_dt + s.nh;
   s.n_in = s.off_dt + (s.gdn ? 2 : 1) * s.nh;
   hyf_state_layout L;
@@ -158,8 +162,11 @@ WsDraft ws_draft(const Shape& s, int dtype, int32_t R, int64_t rows) {
 }
 
 struct WsCommit {
-  uint64_t vb, dt, kb, c, part, lam, end;
+  uint64_t vb, dt, kb, c, part, lam, deq, end;
 };
+// First w_in row a prefill commit projects through (C for per-token outputs, else k): with 4-bit
+// weights the rows from there to n_in are expanded to bf16 in the workspace.
+int64_t prefill_row0(const Shape& s) { return s.off_c; }
 WsCommit ws_commit(const Shape& s, int dtype, int32_t R, int64_t rows, bool with_y) {
   WsCommit w;
   uint64_t o = 0;
@@ -185,6 +192,8 @@ WsCommit ws_commit(const Shape& s, int dtype, int32_t R, int64_t rows, bool with
   o += align_up(part_bytes);
   w.lam = o;
   o += align_up((uint64_t)segs * s.nh * 4);
+  w.deq = o;
+  if (s.w4) o += align_up((uint64_t)(s.n_in - prefill_row0(s)) * s.d * 2);
   w.end = o;
   return w;
 }
@@ -243,10 +252,33 @@ void fill_segments(const Shape& s, int dtype, ReqTable* rt, bool y_mode, int32_t
 
 int hip_status(hipError_t e) { return e == hipSuccess ? HYF_OK : HYF_EHIP; }
 
-int check_weights(const hyf_weights* w) {
-  if (!w || !w->w_in || !w->w_out || !w->a_log || !w->dt_bias || !w->d_skip) return HYF_EINVAL;
+int check_weights(const hyf_config* c, const hyf_weights* w) {
+  if (!w || !w->a_log || !w->dt_bias || !w->d_skip) return HYF_EINVAL;
+  if (c->weights == HYF_WEIGHTS_W4) {
+    if (!w->w_in_q || !w->w_in_s || !w->w_out_q || !w->w_out_s) return HYF_EINVAL;
+    if (!aligned(w->w_in_q, 16) || !aligned(w->w_out_q, 16) || !aligned(w->w_in_s, 4) || !aligned(w->w_out_s, 4))
+      return HYF_EINVAL;
+    return HYF_OK;
+  }
+  if (!w->w_in || !w->w_out) return HYF_EINVAL;
   if (!aligned(w->w_in, 16) || !aligned(w->w_out, 16)) return HYF_EINVAL;
   return HYF_OK;
+}
+
+// The layer's input projection restricted to w_in rows row0 .. row0 + n (dense or 4-bit weights).
+hipError_t project_in(const Shape& s, int dtype, const hyf_weights* w, int row0, int n, const RowSrc& xs, int64_t M,
+                      const Epi& e, hipStream_t hs) {
+  if (s.w4)
+    return launch_linear_w4_epi(xs, M, s.d, w->w_in_q + (int64_t)row0 * (s.d / 2),
+                                w->w_in_s + (int64_t)row0 * (s.d / 128), n, e, hs);
+  return launch_linear(dtype, xs, M, s.d, static_cast<const char*>(w->w_in) + (int64_t)row0 * s.d * esize(dtype), n,
+                       e, hs);
+}
+// The layer's output projection.
+hipError_t project_out(const Shape& s, int dtype, const hyf_weights* w, const RowSrc& xs, int64_t M, const Epi& e,
+                       hipStream_t hs) {
+  if (s.w4) return launch_linear_w4_epi(xs, M, s.dq, w->w_out_q, w->w_out_s, s.d, e, hs);
+  return launch_linear(dtype, xs, M, s.dq, w->w_out, s.d, e, hs);
 }
 
 
@@ -257,7 +289,7 @@ int draft_check(const hyf_config* cfg, const hyf_weights* w, void* state_pool, i
                 const void* block_in, void* block_out, ReqTable* rt, int64_t* rows_out) {
   int st = check_cfg(cfg);
   if (st != HYF_OK) return st;
-  if ((st = check_weights(w)) != HYF_OK) return st;
+  if ((st = check_weights(cfg, w)) != HYF_OK) return st;
   if (!state_pool || !aligned(state_pool, ALIGN) || pool_slots < 1) return HYF_EINVAL;
   if (!block_in || !block_out || !aligned(block_in, 16) || !aligned(block_out, 16)) return HYF_EINVAL;
   if ((commit_feats == nullptr) != (cu_commit == nullptr)) return HYF_EINVAL;
@@ -290,7 +322,7 @@ int draft_run(const hyf_config* cfg, const hyf_weights* w, void* state_pool, con
   const int64_t ld = proj_ld(s);
   RowSrc xs{rows > 0 ? commit_feats : block_in, block_in, rows};
   Epi e{proj, ld, 1, s.n_in, nullptr, 0, 0, counters, n_req * s.nh + n_req};
-  hipError_t he = launch_linear(dt, xs, rows + (int64_t)HYF_BLOCK * n_req, s.d, w->w_in, s.n_in, e, hs);
+  hipError_t he = project_in(s, dt, w, 0, s.n_in, xs, rows + (int64_t)HYF_BLOCK * n_req, e, hs);
   if (he != hipSuccess) return HYF_EHIP;
 
   // 2. the round kernel: commit + readout tiles and attention splits, merged per head
@@ -314,7 +346,7 @@ int draft_run(const hyf_config* cfg, const hyf_weights* w, void* state_pool, con
   // 3. output projection
   RowSrc xo{ra.o_in, ra.o_in, (int64_t)HYF_BLOCK * n_req};
   Epi eo{block_out, s.d, 0, s.d, nullptr, 0, 0, nullptr, 0};
-  return hip_status(launch_linear(dt, xo, (int64_t)HYF_BLOCK * n_req, s.dq, w->w_out, s.d, eo, hs));
+  return hip_status(project_out(s, dt, w, xo, (int64_t)HYF_BLOCK * n_req, eo, hs));
 }
 
 // ---- the allocation-free draft call's scratch --------------------------------------------------
@@ -389,7 +421,10 @@ size_t hyf_state_bytes(const hyf_config* cfg) {
 size_t hyf_workspace_bytes(const hyf_config* cfg, int32_t max_requests, int64_t max_rows, int32_t with_y) {
   if (check_cfg(cfg) != HYF_OK || max_requests < 1 || max_requests > HYF_MAX_REQUESTS || max_rows < 0) return 0;
   const Shape s = make_shape(cfg);
-  const uint64_t a = ws_draft(s, cfg->dtype, max_requests, max_rows).end;
+  // the draft-sized layout serves draft calls (at most HYF_BLOCK commit rows per request) and round-sized
+  // commits (at most RMAXC rows per request); longer commits take the commit layout
+  const int64_t round_rows = (int64_t)16 * max_requests;
+  const uint64_t a = ws_draft(s, cfg->dtype, max_requests, max_rows < round_rows ? max_rows : round_rows).end;
   const uint64_t b = ws_commit(s, cfg->dtype, max_requests, max_rows, with_y != 0).end;
   return (size_t)(a > b ? a : b);
 }
@@ -418,7 +453,7 @@ int hyf_memory_commit(const hyf_config* cfg, const hyf_weights* w, void* state_p
                       void* ws, size_t ws_bytes, void* stream) {
   int st = check_cfg(cfg);
   if (st != HYF_OK) return st;
-  if ((st = check_weights(w)) != HYF_OK) return st;
+  if ((st = check_weights(cfg, w)) != HYF_OK) return st;
   if (!state_pool || !aligned(state_pool, ALIGN) || pool_slots < 1 || !cu_rows) return HYF_EINVAL;
   const Shape s = make_shape(cfg);
   if (y_opt && (s.gdn || !scan_y_supported(s, esize(cfg->dtype)))) return HYF_EUNSUPPORTED;
@@ -451,8 +486,7 @@ int hyf_memory_commit(const hyf_config* cfg, const hyf_weights* w, void* state_p
     const int64_t ld = proj_ld(s);
     RowSrc xs{feats, feats, rows};
     Epi e{proj + s.off_k, ld, 1, s.n_in, nullptr, 0, 0, counters, n_req * s.nh + n_req};
-    hipError_t he = launch_linear(dt, xs, rows, s.d, static_cast<const char*>(w->w_in) + (int64_t)s.off_k * s.d * es,
-                                  s.n_in - s.off_k, e, hs);
+    hipError_t he = project_in(s, dt, w, s.off_k, s.n_in - s.off_k, xs, rows, e, hs);
     if (he != hipSuccess) return HYF_EHIP;
     RoundArgs ra{};
     ra.proj = proj;
@@ -477,7 +511,19 @@ int hyf_memory_commit(const hyf_config* cfg, const hyf_weights* w, void* state_p
   const WsCommit L = ws_commit(s, dt, n_req, rows, with_y);
   char* cT = wsb + L.c;
   const int64_t c_blk = (int64_t)s.gn * HYF_TBLK;
-  const char* w_c = static_cast<const char*>(w->w_in) + (int64_t)s.off_c * s.d * es;
+  hipError_t he;
+  // the w_in rows from prefill_row0 on, dense: the caller's, or (4-bit weights) expanded to bf16
+  const char* w_rows = static_cast<const char*>(w->w_in) + prefill_row0(s) * (int64_t)s.d * es;
+  if (s.w4) {
+    char* deq = wsb + L.deq;
+    const int64_t r0 = prefill_row0(s);
+    if ((he = launch_w4_dequant(w->w_in_q + r0 * (s.d / 2), w->w_in_s + r0 * (s.d / 128), (int)(s.n_in - r0), s.d,
+                                reinterpret_cast<bf16*>(deq), hs)) != hipSuccess)
+      return HYF_EHIP;
+    w_rows = deq;
+  }
+  auto w_row = [&](int r) { return w_rows + (int64_t)(r - prefill_row0(s)) * s.d * es; };
+  const char* w_c = w_row(s.off_c);
   char* vbT = wsb + L.vb;
   float* dtT = reinterpret_cast<float*>(wsb + L.dt);
   char* kb = wsb + L.kb;
@@ -485,9 +531,8 @@ int hyf_memory_commit(const hyf_config* cfg, const hyf_weights* w, void* state_p
   const int64_t vb_blk = (int64_t)nvb * HYF_TBLK;  // block strides (elements) of v | B and of dt
   const int ndt = (s.gdn ? 2 : 1) * s.nh;  // raw step, or the two raw gates
   const int64_t dt_blk = (int64_t)ndt * HYF_TBLK;
-  const char* w_vbd = static_cast<const char*>(w->w_in) + (int64_t)s.off_v * s.d * es;
-  const char* w_k = static_cast<const char*>(w->w_in) + (int64_t)s.off_k * s.d * es;
-  hipError_t he;
+  const char* w_vbd = w_row(s.off_v);
+  const char* w_k = w_row(s.off_k);
   int64_t krow = 0;
   for (int i = 0; i < n_req; ++i) {
     const int64_t n = cu_rows[i + 1] - cu_rows[i];

@@ -42,6 +42,7 @@ struct Shape {
   int32_t d, nh, P, N, G, W, L, cross;
   int32_t dq, gn, n_in;
   int32_t gdn;  // 1: gated delta-rule memory (gates alpha at off_dt, beta at off_beta), 0: Mamba-2
+  int32_t w4;   // 1: the projections' weights are 4-bit codes and scales
   // w_in row offsets of each group
   int32_t off_q, off_c, off_k, off_v, off_b, off_dt, off_beta;
   // state blob

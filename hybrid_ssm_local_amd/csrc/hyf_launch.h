@@ -72,6 +72,11 @@ hipError_t launch_linear(int dtype, RowSrc x, int64_t M, int K, const void* W, i
 // Weight-only 4-bit projection (hyf_w4.hip); K a multiple of 128.
 hipError_t launch_linear_w4(const bf16* X, int64_t M, int K, const uint8_t* Wq, const float* S, int Nout,
                             void* out, bool out_f32, hipStream_t s);
+// The same with rows from a RowSrc and the output through an epilogue description (not time-blocked).
+hipError_t launch_linear_w4_epi(const RowSrc& x, int64_t M, int K, const uint8_t* Wq, const float* S, int Nout,
+                                const Epi& epi, hipStream_t s);
+// bf16 values (code - 8) * scale of `rows` rows of 4-bit weights with K inputs each: out [rows][K].
+hipError_t launch_w4_dequant(const uint8_t* Wq, const float* S, int rows, int K, bf16* out, hipStream_t s);
 // The 256x128-tile bf16 GEMM (hyf_gemm.hip); K must be a multiple of 64.
 hipError_t launch_gemm256(RowSrc x, int M, int K, const bf16* W, int Nout, const Epi& epi, hipStream_t s);
 

@@ -47,12 +47,13 @@ __device__ __forceinline__ bf16x8 codes_frag(uint32_t w) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-template <typename TO, int MT, int FT>
+template <int MT, int FT>
 __global__ void __launch_bounds__(W4_NW * 64)
-k_linear_w4(const bf16* __restrict__ X, int M, int K, const uint8_t* __restrict__ Wq,
-            const float* __restrict__ S, int Nout, TO* __restrict__ out) {
+k_linear_w4(RowSrc xs, int M, int K, const uint8_t* __restrict__ Wq, const float* __restrict__ S, int Nout, Epi epi) {
   __shared__ float red[W4_NW * FT * MT * 256];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (epi.zero && blockIdx.x == 0 && blockIdx.y == 0)
+    for (int z = threadIdx.x; z < epi.n_zero; z += W4_NW * 64) epi.zero[z] = 0;
   const int i = lane & 15, g = lane >> 4;
   const int f0 = blockIdx.x * 16 * FT;  // FT tiles of 16 features, sharing the X fragments
   const int m0 = blockIdx.y * W4_MROWS;
@@ -72,7 +73,7 @@ k_linear_w4(const bf16* __restrict__ X, int M, int K, const uint8_t* __restrict_
   for (int t = 0; t < MT; ++t) {
     const int m = m0 + 16 * t + i;
     xok[t] = m < M;
-    xrow[t] = X + (int64_t)(xok[t] ? m : 0) * K + 32 * g;
+    xrow[t] = static_cast<const bf16*>(row_ptr(xs, xok[t] ? m : 0, K, 2)) + 32 * g;
   }
   const bf16x8 neg136 = __builtin_bit_cast(bf16x8, u32x4{0xc308c308u, 0xc308c308u, 0xc308c308u, 0xc308c308u});
   f32x4 acc[FT][MT];
@@ -145,43 +146,67 @@ k_linear_w4(const bf16* __restrict__ X, int M, int K, const uint8_t* __restrict_
 #pragma unroll
     for (int w = 0; w < W4_NW; ++w) v += red[(((w * FT + ft) * MT + tm) * 4 + r) * 64 + src_lane];
     const int f = f0 + 16 * ft + fl, m = m0 + 16 * tm + ml;
-    if (f < Nout && m < M) out[(int64_t)m * Nout + f] = from_f32<TO>(v);
+    if (f < Nout && m < M) epi_store<bf16>(epi, m, f, v);
   }
 }
 
-template <typename TO, int FT>
-void launch_w4_mt(int mt, dim3 grid, const bf16* X, int64_t M, int K, const uint8_t* Wq, const float* S, int Nout,
-                  TO* out, hipStream_t s) {
+template <int FT>
+void launch_w4_mt(int mt, dim3 grid, const RowSrc& x, int64_t M, int K, const uint8_t* Wq, const float* S, int Nout,
+                  const Epi& epi, hipStream_t s) {
   const dim3 block(W4_NW * 64);
   switch (mt) {
-    case 1: hipLaunchKernelGGL((k_linear_w4<TO, 1, FT>), grid, block, 0, s, X, (int)M, K, Wq, S, Nout, out); break;
-    case 2: hipLaunchKernelGGL((k_linear_w4<TO, 2, FT>), grid, block, 0, s, X, (int)M, K, Wq, S, Nout, out); break;
-    case 3: hipLaunchKernelGGL((k_linear_w4<TO, 3, FT>), grid, block, 0, s, X, (int)M, K, Wq, S, Nout, out); break;
-    default: hipLaunchKernelGGL((k_linear_w4<TO, 4, FT>), grid, block, 0, s, X, (int)M, K, Wq, S, Nout, out); break;
+    case 1: hipLaunchKernelGGL((k_linear_w4<1, FT>), grid, block, 0, s, x, (int)M, K, Wq, S, Nout, epi); break;
+    case 2: hipLaunchKernelGGL((k_linear_w4<2, FT>), grid, block, 0, s, x, (int)M, K, Wq, S, Nout, epi); break;
+    case 3: hipLaunchKernelGGL((k_linear_w4<3, FT>), grid, block, 0, s, x, (int)M, K, Wq, S, Nout, epi); break;
+    default: hipLaunchKernelGGL((k_linear_w4<4, FT>), grid, block, 0, s, x, (int)M, K, Wq, S, Nout, epi); break;
   }
 }
 
-template <typename TO>
-hipError_t launch_w4_typed(const bf16* X, int64_t M, int K, const uint8_t* Wq, const float* S, int Nout, TO* out,
-                           hipStream_t s) {
+// out[f][k] = bf16((code(f, k) - 8) * scale[f][k / 128]): one byte (two codes) per thread.
+__global__ void __launch_bounds__(256) k_w4_dequant(const uint8_t* __restrict__ Wq, const float* __restrict__ S,
+                                                    int64_t bytes, int K, bf16* __restrict__ out) {
+  const int half = K / 2, ng = K / W4_GROUP;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < bytes; i += (int64_t)gridDim.x * 256) {
+    const int64_t f = i / half;
+    const int j = (int)(i % half);
+    const uint32_t b = Wq[i];
+    const float sc = S[f * ng + (2 * j) / W4_GROUP];
+    out[f * K + 2 * j] = static_cast<bf16>((float)((int)(b & 15u) - 8) * sc);
+    out[f * K + 2 * j + 1] = static_cast<bf16>((float)((int)(b >> 4) - 8) * sc);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_linear_w4_epi(const RowSrc& x, int64_t M, int K, const uint8_t* Wq, const float* S, int Nout,
+                                const Epi& epi, hipStream_t s) {
+  if (M <= 0 || Nout <= 0) return hipSuccess;
+  if (epi.trans) return hipErrorInvalidValue;  // the time-blocked layout is the prefill GEMM's
   const int mt = (int)((M < W4_MROWS ? M : W4_MROWS) + 15) / 16;
   const int tiles = (Nout + 15) / 16;
   const unsigned gy = (unsigned)((M + W4_MROWS - 1) / W4_MROWS);
   // One workgroup fits a CU at this kernel's register count: past one workgroup per CU, two
   // feature tiles per workgroup keep the grid to one round (and share the X fragments).
   if (tiles > 256 && mt <= 2)
-    launch_w4_mt<TO, 2>(mt, dim3((tiles + 1) / 2, gy), X, M, K, Wq, S, Nout, out, s);
+    launch_w4_mt<2>(mt, dim3((tiles + 1) / 2, gy), x, M, K, Wq, S, Nout, epi, s);
   else
-    launch_w4_mt<TO, 1>(mt, dim3(tiles, gy), X, M, K, Wq, S, Nout, out, s);
+    launch_w4_mt<1>(mt, dim3(tiles, gy), x, M, K, Wq, S, Nout, epi, s);
   return hipGetLastError();
 }
 
-}  // namespace
-
 hipError_t launch_linear_w4(const bf16* X, int64_t M, int K, const uint8_t* Wq, const float* S, int Nout,
                             void* out, bool out_f32, hipStream_t s) {
-  if (out_f32) return launch_w4_typed<float>(X, M, K, Wq, S, Nout, static_cast<float*>(out), s);
-  return launch_w4_typed<bf16>(X, M, K, Wq, S, Nout, static_cast<bf16*>(out), s);
+  RowSrc xs{X, X, M};
+  Epi e{out, Nout, out_f32 ? 1 : 0, Nout, nullptr, 0, 0, nullptr, 0};
+  return launch_linear_w4_epi(xs, M, K, Wq, S, Nout, e, s);
+}
+
+hipError_t launch_w4_dequant(const uint8_t* Wq, const float* S, int rows, int K, bf16* out, hipStream_t s) {
+  const int64_t bytes = (int64_t)rows * (K / 2);
+  if (bytes <= 0) return hipSuccess;
+  const int64_t want = (bytes + 255) / 256;
+  hipLaunchKernelGGL(k_w4_dequant, dim3((unsigned)(want < 4096 ? want : 4096)), dim3(256), 0, s, Wq, S, bytes, K, out);
+  return hipGetLastError();
 }
 
 }  // namespace hyf

@@ -22,6 +22,7 @@ HEADER = os.path.join(os.path.dirname(_PKG), "include", "hyflash.h")
 HYF_OK, HYF_EINVAL, HYF_ESHAPE, HYF_ECAPACITY, HYF_EDTYPE, HYF_EWORKSPACE, HYF_EUNSUPPORTED, HYF_EHIP = range(8)
 HYF_F32, HYF_BF16 = 0, 1
 HYF_MEM_MAMBA2, HYF_MEM_GDN = 0, 1
+HYF_WEIGHTS_DENSE, HYF_WEIGHTS_W4 = 0, 1
 HYF_BLOCK = 8
 HYF_MAX_REQUESTS = 128
 HYF_NOALLOC_SCRATCH_BYTES = 16 << 20
@@ -30,12 +31,13 @@ HYF_NOALLOC_SCRATCH_BYTES = 16 << 20
 class HyfConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "d_model", "n_heads", "head_dim", "d_state", "n_groups", "window", "block", "chunk",
-        "dtype", "memory", "cross_slot", "reserved")]
+        "dtype", "memory", "cross_slot", "weights")]
 
 
 class HyfWeights(ctypes.Structure):
     _fields_ = [("w_in", ctypes.c_void_p), ("w_out", ctypes.c_void_p), ("a_log", ctypes.c_void_p),
-                ("dt_bias", ctypes.c_void_p), ("d_skip", ctypes.c_void_p)]
+                ("dt_bias", ctypes.c_void_p), ("d_skip", ctypes.c_void_p), ("w_in_q", ctypes.c_void_p),
+                ("w_in_s", ctypes.c_void_p), ("w_out_q", ctypes.c_void_p), ("w_out_s", ctypes.c_void_p)]
 
 
 class HyfStateLayout(ctypes.Structure):
@@ -109,7 +111,7 @@ def make_config(shape: LayerShape, memory: int | None = None) -> HyfConfig:
         memory = HYF_MEM_GDN if shape.memory == "gdn" else HYF_MEM_MAMBA2
     return HyfConfig(shape.d_model, shape.n_heads, shape.head_dim, shape.d_state, shape.n_groups, shape.window,
                      shape.block, shape.chunk, HYF_BF16 if shape.dtype == BF16 else HYF_F32, memory,
-                     shape.cross_slot, 0)
+                     shape.cross_slot, HYF_WEIGHTS_W4 if shape.weights == "w4" else HYF_WEIGHTS_DENSE)
 
 
 def _ptr(t):
@@ -285,13 +287,22 @@ class DrafterLayer:
         self.shape, self.device = shape, device
         self.cfg = make_config(shape)
         check(hyf_config_check(self.cfg), "hyf_config_check")
-        self.w_in = to_device(weights["w_in"], shape, device)
-        self.w_out = to_device(weights["w_out"], shape, device)
         self.a_log = to_device(weights["a_log"], shape, device, storage=False)
         self.dt_bias = to_device(weights["dt_bias"], shape, device, storage=False)
         self.d_skip = to_device(weights["d_skip"], shape, device, storage=False)
-        self.w = HyfWeights(self.w_in.data_ptr(), self.w_out.data_ptr(), self.a_log.data_ptr(),
-                            self.dt_bias.data_ptr(), self.d_skip.data_ptr())
+        if shape.weights == "w4":
+            # 4-bit weights: codes [out][in/2] uint8, scales [out][in/128] fp32
+            q = {k: torch.from_numpy(np.ascontiguousarray(weights[k])).to(device)
+                 for k in ("w_in_q", "w_in_s", "w_out_q", "w_out_s")}
+            self.w4 = q
+            self.w = HyfWeights(None, None, self.a_log.data_ptr(), self.dt_bias.data_ptr(), self.d_skip.data_ptr(),
+                                q["w_in_q"].data_ptr(), q["w_in_s"].data_ptr(), q["w_out_q"].data_ptr(),
+                                q["w_out_s"].data_ptr())
+        else:
+            self.w_in = to_device(weights["w_in"], shape, device)
+            self.w_out = to_device(weights["w_out"], shape, device)
+            self.w = HyfWeights(self.w_in.data_ptr(), self.w_out.data_ptr(), self.a_log.data_ptr(),
+                                self.dt_bias.data_ptr(), self.d_skip.data_ptr())
         self.pool_slots = pool_slots
         self.state_bytes = hyf_state_bytes(self.cfg)
         self.layout = hyf_state_layout_get(self.cfg)

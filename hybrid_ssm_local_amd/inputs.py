@@ -38,7 +38,8 @@ class LayerShape:
     chunk: int = 64
     dtype: str = BF16
     cross_slot: int = 1
-    memory: str = "mamba2"  # or "gdn": the gated delta-rule memory
+    memory: str = "mamba2"  # or "gdn": the gated delta-rule memory; "lastw": Mamba-2 over the window only
+    weights: str = "dense"  # or "w4": the projections' weights as 4-bit codes and scales
 
     @property
     def dq(self) -> int:
@@ -162,3 +163,12 @@ def make_scan_inputs(shape: LayerShape, T: int, rng, with_c: bool = True, h0_sca
     H0 = (rng.standard_normal((nh, P, shape.d_state), dtype=np.float32) * np.float32(h0_scale)
           if h0_scale else np.zeros((nh, P, shape.d_state), dtype=np.float32))
     return dict(x=x, B=B, C=C, dt_raw=dt_raw, a_log=a_log, dt_bias=dt_bias, d_skip=d_skip, H0=H0)
+
+
+def random_w4(rng, n_out: int, k: int):
+    """Random 4-bit codes and scales of an [n_out][k] weight (k a multiple of 128) for timing runs:
+    codes uniform 0..15 packed two per byte, scales 1 / (7 sqrt(k)) to 2 / (7 sqrt(k)).  Returns
+    (codes uint8 [n_out][k/2], scales float32 [n_out][k/128])."""
+    codes = rng.integers(0, 256, size=(n_out, k // 2), dtype=np.uint8)
+    scales = (rng.uniform(1.0, 2.0, size=(n_out, k // 128)) / (7.0 * math.sqrt(k))).astype(np.float32)
+    return codes, scales

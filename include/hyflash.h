@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define HYF_ABI_VERSION 1
+#define HYF_ABI_VERSION 2
 /* Requests per call (state slots touched by one commit or draft call). */
 #define HYF_MAX_REQUESTS 128
 /* Rows of the draft block: anchor + seven draft positions (explainer, "Jargon"). */
@@ -59,6 +59,10 @@ typedef enum {
 
 typedef enum { HYF_F32 = 0, HYF_BF16 = 1 } hyf_dtype;
 typedef enum { HYF_MEM_MAMBA2 = 0, HYF_MEM_GDN = 1 } hyf_memory;
+/* Weights of the layer's two projections: in the storage dtype, or 4-bit codes with fp32 scales
+ * (HyFlash paper page, Figures & tables: the BF16 vs INT4 table; explainer, "Where it earns its
+ * keep": the drafter's weights quantized to 4 bits keep the bf16 drafter's acceptance). */
+typedef enum { HYF_WEIGHTS_DENSE = 0, HYF_WEIGHTS_W4 = 1 } hyf_weight_format;
 
 /* Layer shape.  48 bytes, all int32. */
 typedef struct {
@@ -73,7 +77,8 @@ typedef struct {
   int32_t dtype;      /* hyf_dtype                                                      */
   int32_t memory;     /* hyf_memory (HYF_MEM_GDN: see hyf_weights)                      */
   int32_t cross_slot; /* 1: block rows attend to each other; 0: each only to itself     */
-  int32_t reserved;   /* must be 0                                                      */
+  int32_t weights;    /* hyf_weight_format; HYF_WEIGHTS_W4 needs HYF_BF16 and d_model and
+                         nh*head_dim multiples of 128 (HYF_EUNSUPPORTED otherwise)          */
 } hyf_config;
 
 /* Layer weights, nn.Linear layout ([out_features][in_features], row-major).
@@ -91,11 +96,19 @@ typedef struct {
  * Per-token outputs (y_opt) and hyf_ssd_scan are Mamba-2 only (HYF_EUNSUPPORTED); a commit of more
  * than 16 rows per request needs d_state <= 192, or d_state 224 in bf16 (HYF_EUNSUPPORTED otherwise). */
 typedef struct {
-  const void* w_in;     /* [n_in][d_model], storage dtype, 16-byte aligned */
-  const void* w_out;    /* [d_model][nh*P], storage dtype, 16-byte aligned */
+  const void* w_in;     /* [n_in][d_model], storage dtype, 16-byte aligned (dense weights)   */
+  const void* w_out;    /* [d_model][nh*P], storage dtype, 16-byte aligned (dense weights)   */
   const float* a_log;   /* [nh] */
   const float* dt_bias; /* [nh] */
   const float* d_skip;  /* [nh] */
+  /* 4-bit weights (cfg->weights = HYF_WEIGHTS_W4; w_in and w_out are then not read): the same
+   * matrices as codes 0..15 standing for (code - 8) * scale, two per byte along the input
+   * dimension (the lower index in the low nibble), one fp32 scale per 128 consecutive inputs of a
+   * row, as hyf_linear_w4 takes them.  Codes 16-byte aligned, scales 4-byte aligned. */
+  const uint8_t* w_in_q;  /* [n_in][d_model / 2]        */
+  const float* w_in_s;    /* [n_in][d_model / 128]      */
+  const uint8_t* w_out_q; /* [d_model][nh*P / 2]        */
+  const float* w_out_s;   /* [d_model][nh*P / 128]      */
 } hyf_weights;
 
 /* Byte offsets inside one request's state blob (each section 256-byte aligned):
@@ -131,6 +144,11 @@ size_t hyf_workspace_bytes(const hyf_config* cfg, int32_t max_requests, int64_t 
  * slots (host, nullable): pool index of each request; NULL means 0..n_req-1. */
 int hyf_state_reset(const hyf_config* cfg, void* state_pool, int32_t pool_slots,
                     const int32_t* slots, int32_t n_req, void* stream);
+
+/* With 4-bit weights a round's projections (hyf_draft_block, and hyf_memory_commit of at most 16
+ * rows per request) compute with the codes exactly (as hyf_linear_w4); a longer commit first
+ * expands the codes of the w_in rows it uses to bf16 values (code - 8) * scale in the workspace
+ * and runs the bf16 prefill GEMM on them. */
 
 /* Commit: the only writer of committed state (explainer, "That is HyFlash": after
  * verification only the newly committed features update the memory).

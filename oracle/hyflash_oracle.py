@@ -39,7 +39,8 @@ notes of the repository):
   stays float64.
 * 4-bit weights (the pages name GPTQ, no format): group-wise symmetric
   round-to-nearest, 128 k per group, scale max|w|/7 in float32, two codes per
-  byte (lower k in the low nibble); see quantize_w4.
+  byte (lower k in the low nibble); see quantize_w4.  A layer with 4-bit weights
+  projects through the dequantized weights (layer_projection).
 
 Parity is pinned for every function below by tests that compare against
 closed forms, library routines or brute force (see tests/test_oracle_pins.py).
@@ -261,27 +262,65 @@ def project(rows, w):
     return np.asarray(rows, F64) @ np.asarray(w, F64).T
 
 
+def layer_projection(rows, wts: dict, which: str):
+    """The layer's input ("in") or output ("out") projection: with 4-bit weights (the dict holds
+    w_<which>_q codes and w_<which>_s scales) the product of the dequantized weights (linear_w4),
+    else the dense weight w_<which>."""
+    if f"w_{which}_q" in wts:
+        return linear_w4(rows, wts[f"w_{which}_q"], wts[f"w_{which}_s"])
+    return project(rows, wts[f"w_{which}"])
+
+
 def new_state(shape) -> dict:
-    """Empty per-request state: nothing committed, H = 0, empty ring."""
+    """Empty per-request state: nothing committed, H = 0, empty ring.  The last-W memory also keeps,
+    per ring slot, the row's B (storage dtype) and raw step (fp32)."""
     nh, P, N, W = shape.n_heads, shape.head_dim, shape.d_state, shape.window
-    return dict(count=0, H=np.zeros((nh, P, N), F64),
-                K=np.zeros((nh, W, P), F64), V=np.zeros((nh, W, P), F64))
+    st = dict(count=0, H=np.zeros((nh, P, N), F64),
+              K=np.zeros((nh, W, P), F64), V=np.zeros((nh, W, P), F64))
+    if shape.memory == "lastw":
+        st["Bring"] = np.zeros((W, shape.gn), F64)
+        st["DTring"] = np.zeros((W, nh), F64)
+    return st
 
 
 def copy_state(st: dict) -> dict:
-    return dict(count=st["count"], H=st["H"].copy(), K=st["K"].copy(), V=st["V"].copy())
+    return {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in st.items()}
 
 
-def ring_append(shape, st: dict, k, v) -> None:
-    """Committed row c (0-based over the request) goes to slot c mod W; values stored rounded."""
+def ring_append(shape, st: dict, k, v, B=None, dt_raw=None) -> None:
+    """Committed row c (0-based over the request) goes to slot c mod W; values stored rounded (k, v
+    and B to the storage dtype, the raw step to fp32)."""
     W = shape.window
     kr = round_storage(k, shape.dtype)
     vr = round_storage(v, shape.dtype)
+    br = round_storage(B, shape.dtype) if B is not None else None
+    dr = round_storage(dt_raw, "f32") if dt_raw is not None else None
     for i in range(kr.shape[0]):
         slot = st["count"] % W
         st["K"][:, slot, :] = kr[i]
         st["V"][:, slot, :] = vr[i]
+        if br is not None:
+            st["Bring"][slot] = br[i]
+            st["DTring"][slot] = dr[i]
         st["count"] += 1
+
+
+def window_in_order(shape, st: dict):
+    """Ring slots of the last min(count, W) committed rows, oldest first."""
+    n = min(st["count"], shape.window)
+    return (st["count"] - n + np.arange(n)) % shape.window
+
+
+def lastw_state(shape, wts: dict, st: dict):
+    """The memory of the paper's last-W ablation ("SSM: last 512"): the Mamba-2 state of a scan
+    from H = 0 over only the last min(count, W) committed rows, in commit order, from the stored
+    (rounded) x = v, B and raw steps of the ring."""
+    slots = window_in_order(shape, st)
+    x = st["V"][:, slots, :].transpose(1, 0, 2)
+    H0 = np.zeros((shape.n_heads, shape.head_dim, shape.d_state), F64)
+    H, _ = ssd_sequential(x, st["Bring"][slots], None, st["DTring"][slots], wts["a_log"], wts["dt_bias"],
+                          wts["d_skip"], H0, shape.n_groups)
+    return H
 
 
 def ring_window(shape, st: dict):
@@ -303,7 +342,13 @@ def commit(shape, wts: dict, st: dict, feats, want_y: bool = False):
     feats = np.asarray(feats, F64)
     if feats.shape[0] == 0:
         return st, (np.zeros((0, shape.n_heads, shape.head_dim)) if want_y else None)
-    pr = split_projection(project(feats, wts["w_in"]), shape)
+    pr = split_projection(layer_projection(feats, wts, "in"), shape)
+    if shape.memory == "lastw":
+        # the last-W memory keeps no running state: the ring holds what its scan reads
+        if want_y:
+            raise ValueError("per-token outputs are defined for the Mamba-2 memory only")
+        ring_append(shape, st, pr["k"], pr["v"], pr["B"], pr["dt"])
+        return st, None
     if shape.memory == "gdn":
         if want_y:
             raise ValueError("per-token outputs are defined for the Mamba-2 memory only")
@@ -355,13 +400,14 @@ def draft(shape, wts: dict, st: dict, block_in):
     """
     x = np.asarray(block_in, F64)
     nb = x.shape[0]
-    pr = split_projection(project(x, wts["w_in"]), shape)
+    pr = split_projection(layer_projection(x, wts, "in"), shape)
     k_ctx, v_ctx = ring_window(shape, st)
     attn = block_attention(pr["q"], k_ctx, v_ctx, pr["k"], pr["v"], shape.cross_slot)
     Cq = l2_normalize(pr["C"].reshape(nb, shape.n_groups, -1)).reshape(nb, -1) if shape.memory == "gdn" else pr["C"]
-    mem = memory_readout(st["H"], Cq, pr["v"], wts["d_skip"], shape.n_groups)
+    H = lastw_state(shape, wts, st) if shape.memory == "lastw" else st["H"]
+    mem = memory_readout(H, Cq, pr["v"], wts["d_skip"], shape.n_groups)
     o = (attn + mem).reshape(nb, shape.dq)
-    return project(o, wts["w_out"])
+    return layer_projection(o, wts, "out")
 
 
 def round_step(shape, wts: dict, st: dict, commit_feats, block_in):

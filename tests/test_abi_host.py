@@ -23,12 +23,12 @@ def test_library_exports_every_declared_function():
     L = hf.lib()
     for n in names:
         assert getattr(L, n) is not None
-    assert hf.hyf_abi_version() == 1
+    assert hf.hyf_abi_version() == 2
 
 
 def test_struct_sizes_match_the_header():
     assert ctypes.sizeof(hf.HyfConfig) == 48
-    assert ctypes.sizeof(hf.HyfWeights) == 40
+    assert ctypes.sizeof(hf.HyfWeights) == 72  # nine pointers
     assert ctypes.sizeof(hf.HyfStateLayout) == 40
 
 
@@ -43,7 +43,7 @@ def test_named_shapes_are_accepted(shape):
     ("head_dim", 72, hf.HYF_ESHAPE), ("head_dim", 0, hf.HYF_ESHAPE), ("d_state", 300, hf.HYF_ESHAPE),
     ("n_groups", 3, hf.HYF_ESHAPE), ("window", 0, hf.HYF_ESHAPE), ("block", 7, hf.HYF_ESHAPE),
     ("chunk", 8, hf.HYF_ESHAPE), ("chunk", 48, hf.HYF_ESHAPE), ("dtype", 5, hf.HYF_EDTYPE), ("memory", 2, hf.HYF_EINVAL),
-    ("cross_slot", 2, hf.HYF_EINVAL), ("reserved", 1, hf.HYF_EINVAL), ("d_model", 100, hf.HYF_ESHAPE),
+    ("cross_slot", 2, hf.HYF_EINVAL), ("weights", 2, hf.HYF_EINVAL), ("d_model", 100, hf.HYF_ESHAPE),
 ])
 def test_bad_configs_are_rejected(field, value, status):
     cfg = hf.make_config(I.QWEN)
@@ -218,3 +218,26 @@ def test_allocation_free_draft_rejects_bad_and_oversized_calls_before_device_wor
     assert hf.hyf_draft_block_noalloc(cfg, w, fake + 8, 1, None, 1, None, None, fake, fake, 0) == hf.HYF_EINVAL
     bad_w = hf.HyfWeights(None, fake, fake, fake, fake)
     assert hf.hyf_draft_block_noalloc(cfg, bad_w, fake, 1, None, 1, None, None, fake, fake, 0) == hf.HYF_EINVAL
+
+
+def test_four_bit_layer_weights_config_and_checks():
+    # 4-bit projection weights need bf16 and d_model, nh*head_dim multiples of 128; the codes and
+    # scales are checked (not w_in / w_out) before any device work.
+    qwen = I.QWEN.replace(weights="w4")
+    assert hf.hyf_config_check(hf.make_config(qwen)) == hf.HYF_OK
+    assert hf.hyf_config_check(hf.make_config(I.TINY.replace(weights="w4"))) == hf.HYF_EUNSUPPORTED
+    odd = I.LayerShape(d_model=192, n_heads=3, head_dim=64, d_state=64, weights="w4")
+    assert hf.hyf_config_check(hf.make_config(odd)) == hf.HYF_EUNSUPPORTED
+    cfg = hf.make_config(qwen)
+    fake = 1 << 20
+    dense_only = hf.HyfWeights(fake, fake, fake, fake, fake)
+    assert hf.hyf_draft_block(cfg, dense_only, fake, 1, None, 1, None, None, fake, fake, fake, 1 << 30, 0) == \
+        hf.HYF_EINVAL
+    misaligned = hf.HyfWeights(None, None, fake, fake, fake, fake + 8, fake, fake, fake)
+    assert hf.hyf_draft_block(cfg, misaligned, fake, 1, None, 1, None, None, fake, fake, fake, 1 << 30, 0) == \
+        hf.HYF_EINVAL
+    # the prefill workspace holds the expanded w_in rows from C on
+    dense_ws = hf.hyf_workspace_bytes(hf.make_config(I.QWEN), 1, 8192)
+    w4_ws = hf.hyf_workspace_bytes(cfg, 1, 8192)
+    rows = qwen.n_in - qwen.in_groups["C"][0]
+    assert w4_ws >= dense_ws + rows * qwen.d_model * 2 - 256

@@ -524,6 +524,68 @@ def test_gated_delta_rule_qwen_prefill_batched_and_rounds():
     pr.check_state(slot=1, what="gdn qwen rounds")
 
 
+def w4_weights(shape, seed):
+    """Xavier weights of the shape, quantized with the oracle's round-to-nearest 4-bit format: the
+    GPU gets the codes and scales, the oracle the same codes and scales."""
+    w = I.make_weights(shape, I.rng_streams(seed)[0], d_random=True)
+    qi, si = O.quantize_w4(w["w_in"])
+    qo, so = O.quantize_w4(w["w_out"])
+    w.update(w_in_q=qi, w_in_s=si, w_out_q=qo, w_out_s=so)
+    return w
+
+
+W4_LAYER_SHAPES = [
+    ("small_bf16", small_shape("bf16", window=40, weights="w4")),
+    ("qwen_bf16", I.QWEN.replace(weights="w4")),
+    ("gdn_bf16", small_shape("bf16", window=40, memory="gdn", weights="w4")),
+]
+
+
+@pytest.mark.parametrize("name,shape", W4_LAYER_SHAPES, ids=[c[0] for c in W4_LAYER_SHAPES])
+def test_four_bit_layer_matches_the_oracle(name, shape):
+    # The layer with 4-bit projection weights: a prefill (codes expanded to bf16, then the GEMM), rounds
+    # (codes streamed by the 4-bit kernel), a round-sized commit, and a batched round of three requests.
+    w = w4_weights(shape, 41)
+    wo = {k: (np.asarray(v) if k.endswith("_q") else np.asarray(v, np.float64)) for k, v in w.items()
+          if k not in ("w_in", "w_out")}
+    layer = hf.DrafterLayer(shape, w, pool_slots=3, max_requests=3, max_rows=1000)
+    layer.reset()
+    rng = I.rng_streams(42)
+    sc = 1.0 / np.sqrt(shape.d_model)
+    rows = lambda n, st=1: I.make_rows(rng[st], n, shape.d_model, sc, shape.dtype)
+    ost = [O.new_state(shape) for _ in range(3)]
+    pre = [rows(n) for n in (300, 17, 600)]
+    say("w4 layer prefill", name)
+    layer.commit(hf.to_device(np.concatenate(pre), shape), np.concatenate([[0], np.cumsum([300, 17, 600])]))
+    for i in range(3):
+        ost[i], _ = O.commit(shape, wo, ost[i], pre[i])
+    torch.cuda.synchronize()
+    for i in range(3):
+        g = layer.state(i)
+        assert_close(g["H"].cpu().numpy(), ost[i]["H"], "bf16", f"w4 {name} prefill H {i}")
+    for rnd in range(3):
+        acc = [int(a) for a in rng[4].integers(1, 9, size=3)]
+        commits = [rows(a, 2) for a in acc]
+        blocks = [rows(8, 3) for _ in range(3)]
+        bi = hf.to_device(np.concatenate(blocks), shape)
+        bo = torch.empty_like(bi)
+        say("w4 layer round", rnd, name)
+        layer.draft(bi, bo, hf.to_device(np.concatenate(commits), shape), np.concatenate([[0], np.cumsum(acc)]))
+        torch.cuda.synchronize()
+        got = bo.float().cpu().numpy().reshape(3, 8, -1)
+        for i in range(3):
+            ost[i], ref = O.round_step(shape, wo, ost[i], commits[i], blocks[i])
+            assert_close(got[i], ref, "bf16", f"w4 {name} round {rnd} request {i}")
+    small = rows(5)
+    say("w4 layer small commit", name)
+    layer.commit(hf.to_device(small, shape), [0, 5], slots=[1])
+    ost[1], _ = O.commit(shape, wo, ost[1], small)
+    torch.cuda.synchronize()
+    g = layer.state(1)
+    assert int(g["count"].item()) == ost[1]["count"]
+    assert_close(g["H"].cpu().numpy(), ost[1]["H"], "bf16", f"w4 {name} small commit H")
+
+
 def test_qwen_full_size_prefill_and_rounds():
     # The 8192-row Qwen-shaped prefix and a few rounds, exactly as the benchmark launches them.
     shape = I.QWEN

@@ -231,3 +231,66 @@ def test_two_layers_chain_through_the_rounded_residual():
     # the rounding matters at this tolerance: without it layer 2 differs measurably
     ref2_unrounded = _expected_draft(shape, p2, w2["w_out"], w2["d_skip"], s2, k2, v2, x + ref1)
     assert _rel(ref2_unrounded, ref2) > 1e-6
+
+
+def test_four_bit_layer_equals_the_layer_of_its_dequantized_weights():
+    # A layer whose w_in and w_out are 4-bit codes computes exactly what the same layer computes
+    # with the dense weights the codes stand for (dequantize_w4, pinned on its own): commit and
+    # draft, state and output.
+    shape = I.LayerShape(d_model=256, n_heads=2, head_dim=128, d_state=16, window=6, dtype="bf16")
+    rng = np.random.default_rng(31)
+    parts, w_in, w_out = _parts(rng, shape)
+    qi, si = O.quantize_w4(w_in)
+    qo, so = O.quantize_w4(w_out)
+    base = dict(a_log=rng.uniform(0, 2, 2), dt_bias=np.full(2, -1.0), d_skip=rng.standard_normal(2))
+    w4 = dict(base, w_in_q=qi, w_in_s=si, w_out_q=qo, w_out_s=so)
+    dense = dict(base, w_in=O.dequantize_w4(qi, si), w_out=O.dequantize_w4(qo, so))
+    F = rng.standard_normal((9, 256)) / 16
+    x = rng.standard_normal((8, 256)) / 16
+    st4, _ = O.commit(shape, w4, O.new_state(shape), F)
+    std, _ = O.commit(shape, dense, O.new_state(shape), F)
+    assert np.array_equal(st4["H"], std["H"]) and np.array_equal(st4["K"], std["K"])
+    assert np.array_equal(O.draft(shape, w4, st4, x), O.draft(shape, dense, std, x))
+    # and the 4-bit layer is not the layer of the unquantized weights (the rounding is there)
+    undq = dict(base, w_in=w_in, w_out=w_out)
+    assert _rel(O.draft(shape, w4, st4, x), O.draft(shape, undq, O.commit(shape, undq, O.new_state(shape), F)[0], x)) > 1e-4
+
+
+@pytest.mark.parametrize("total", [5, 6, 17])
+def test_last_w_memory_is_the_scan_of_the_last_w_committed_rows(total):
+    # The last-W memory (the paper's "SSM: last 512" ablation) after `total` committed rows over a
+    # window of 6: its state equals the closed form of a scan from zero over exactly the last
+    # min(total, 6) rows in commit order, written here from the rows' own x = v, B and step
+    # projections (the sub-matrices) rounded as the ring stores them; the draft reads it with
+    # H . C_q + D v, and commit keeps no running state (H stays zero).
+    shape = I.LayerShape(d_model=24, n_heads=2, head_dim=4, d_state=3, window=6, dtype="bf16", memory="lastw")
+    rng = np.random.default_rng(60 + total)
+    parts, w_in, w_out = _parts(rng, shape)
+    a_log, dt_bias, D = rng.uniform(0, 1.5, 2), np.array([-1.0, 0.5]), rng.standard_normal(2)
+    wts = dict(w_in=w_in, w_out=w_out, a_log=a_log, dt_bias=dt_bias, d_skip=D)
+    F = rng.standard_normal((total, 24)) / 4
+    st, done = O.new_state(shape), 0
+    while done < total:
+        a = min(int(rng.integers(1, 5)), total - done)
+        st, _ = O.commit(shape, wts, st, F[done:done + a])
+        done += a
+    assert st["count"] == total and not np.any(st["H"])
+    bf = lambda z: torch.from_numpy(np.asarray(z, np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    last = F[max(total - 6, 0):]
+    x = bf(_lin(last, parts["v"])).reshape(len(last), 2, 4)
+    B = bf(_lin(last, parts["B"]))
+    raw = _lin(last, parts["dt"]).astype(np.float32).astype(np.float64)
+    dt = np.log1p(np.exp(raw + dt_bias))
+    ell = dt * -np.exp(a_log)
+    H = np.zeros((2, 4, 3))
+    for h in range(2):
+        for t in range(len(last)):
+            H[h] += math.exp(ell[t + 1:, h].sum()) * dt[t, h] * np.outer(x[t, h], B[t])
+    assert _rel(O.lastw_state(shape, wts, st), H) < 1e-12
+    # the draft reads that state
+    xb = rng.standard_normal((8, 24)) / 4
+    ref_st = dict(st, H=H)
+    hist = bf(_lin(F, parts["k"])).reshape(total, 2, 4), bf(_lin(F, parts["v"])).reshape(total, 2, 4)
+    lo = max(total - 6, 0)
+    ref = _expected_draft(shape, parts, w_out, D, ref_st, hist[0][lo:], hist[1][lo:], xb)
+    assert _rel(O.draft(shape, wts, st, xb), ref) < 1e-12
