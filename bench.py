@@ -1006,6 +1006,18 @@ def main():
     }
     del ep4
     torch.cuda.empty_cache()
+    log("batch-1 episodes, last-W memory")
+    epw = EpisodesB1(torch, hf, I, memory="lastw")
+    bw = run_steps(torch, epw.step, sub_steps, 1)
+    qwen_b1_lastw = {
+        "workload": "as qwen3_4b_batch1, with the memory restricted to the last W = 512 committed rows (each commit "
+                    "rescans the window into H; a round commits, then drafts)",
+        "value": b1_blocks / (bw["step_ms"] * 1e-3), "unit": "draft blocks/s per layer (batch 1)",
+        "ms_per_step": bw["step_ms"], "prefill_commit_us": 1e3 * bw["prefill_ms"] / EPISODES,
+        "round_us": 1e3 * bw["rounds_ms"] / b1_blocks,
+    }
+    del epw
+    torch.cuda.empty_cache()
 
     # ---- Phi-4-shaped two-layer drafter
     log("phi-4 two-layer")
@@ -1086,6 +1098,7 @@ def main():
         "round": {"bytes_per_round": rb, "avg_us": t_round, **hbm(rb, t_round)},
         "qwen3_4b_batch1": qwen_b1,
         "qwen3_4b_batch1_w4": qwen_b1_w4,
+        "qwen3_4b_batch1_lastw": qwen_b1_lastw,
         "phi4_two_layer": phi4_2l,
         "phi4_long131k": long5,
         "commit_scan": {"value": 8192 / (s_us * 1e-6), "unit": "committed feats/s", "T": 8192, "shape": "Qwen3-4B",

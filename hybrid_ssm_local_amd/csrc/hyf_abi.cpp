@@ -22,7 +22,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 int check_cfg(const hyf_config* c) {
   if (!c) return HYF_EINVAL;
   if (c->dtype != HYF_F32 && c->dtype != HYF_BF16) return HYF_EDTYPE;
-  if (c->memory != HYF_MEM_MAMBA2 && c->memory != HYF_MEM_GDN) return HYF_EINVAL;
+  if (c->memory != HYF_MEM_MAMBA2 && c->memory != HYF_MEM_GDN && c->memory != HYF_MEM_LASTW) return HYF_EINVAL;
   if (c->weights != HYF_WEIGHTS_DENSE && c->weights != HYF_WEIGHTS_W4) return HYF_EINVAL;
   if (c->cross_slot != 0 && c->cross_slot != 1) return HYF_EINVAL;
   if (c->d_model < 16 || c->d_model > 65536 || c->d_model % 16) return HYF_ESHAPE;
@@ -48,6 +48,12 @@ void fill_layout(const hyf_config* c, hyf_state_layout* L) {
   const uint64_t ring = align_up((uint64_t)c->n_heads * c->window * c->head_dim * es);
   L->v_off = L->k_off + ring;
   L->total = L->v_off + ring;
+  L->b_off = L->dt_off = 0;
+  if (c->memory == HYF_MEM_LASTW) {
+    L->b_off = L->total;
+    L->dt_off = L->b_off + align_up((uint64_t)c->window * c->n_groups * c->d_state * es);
+    L->total = L->dt_off + align_up((uint64_t)c->n_heads * c->window * 4);
+  }
 }
 
 Shape make_shape(const hyf_config* c) {
@@ -70,6 +76,7 @@ Shape make_shape(const hyf_config* c) {
   s.off_dt = s.off_b + s.gn;
   s.gdn = c->memory == HYF_MEM_GDN;
   s.w4 = c->weights == HYF_WEIGHTS_W4;
+  s.lastw = c->memory == HYF_MEM_LASTW;
   s.off_beta = s.off_dt + s.nh;
   s.n_in = s.off_dt + (s.gdn ? 2 : 1) * s.nh;
   hyf_state_layout L;
@@ -78,6 +85,8 @@ Shape make_shape(const hyf_config* c) {
   s.st_h = L.h_off;
   s.st_k = L.k_off;
   s.st_v = L.v_off;
+  s.st_b = L.b_off;
+  s.st_dt = L.dt_off;
   return s;
 }
 
@@ -138,8 +147,34 @@ int64_t time_blocks(int64_t rows, int32_t R) { return rows / HYF_TBLK + R + 1; }
 // group starts 16-byte aligned.
 int64_t proj_ld(const Shape& s) { return (s.n_in + 3) / 4 * 4; }
 
+// The last-W memory's rescan after a commit (appended to both workspace layouts): every request's
+// window as W rows (the first W - min(count, W) of them padding) in the scan's time-blocked
+// layout, and the scan's segment partials.
+struct WsLastw {
+  uint64_t vb, dt, part, lam, end;
+};
+int64_t lastw_blocks(const Shape& s) { return (s.W + HYF_TBLK - 1) / HYF_TBLK; }
+WsLastw ws_lastw(const Shape& s, int dtype, int32_t R, uint64_t base) {
+  WsLastw w{};
+  uint64_t o = base;
+  if (s.lastw) {
+    const int64_t nblk = (int64_t)R * lastw_blocks(s);
+    const int64_t segs = scan_segs_bound(s, dtype, R, (int64_t)R * s.W, false);
+    w.vb = o;
+    o += align_up((uint64_t)nblk * (s.dq + s.gn) * HYF_TBLK * esize(dtype));
+    w.dt = o;
+    o += align_up((uint64_t)nblk * s.nh * HYF_TBLK * 4);
+    w.part = o;
+    o += align_up((uint64_t)segs * s.nh * s.P * s.N * 4);
+    w.lam = o;
+    o += align_up((uint64_t)segs * s.nh * 4);
+  }
+  w.end = o;
+  return w;
+}
+
 struct WsDraft {
-  uint64_t proj, mem, att_part, att_ml, o_in, counters, end;
+  uint64_t proj, mem, att_part, att_ml, o_in, counters, lastw, end;
 };
 WsDraft ws_draft(const Shape& s, int dtype, int32_t R, int64_t rows) {
   WsDraft w;
@@ -157,12 +192,13 @@ WsDraft ws_draft(const Shape& s, int dtype, int32_t R, int64_t rows) {
   o += align_up((uint64_t)R * HYF_BLOCK * s.dq * esize(dtype));
   w.counters = o;
   o += align_up((uint64_t)(R * s.nh + R) * 4);
-  w.end = o;
+  w.lastw = o;
+  w.end = ws_lastw(s, dtype, R, o).end;
   return w;
 }
 
 struct WsCommit {
-  uint64_t vb, dt, kb, c, part, lam, deq, end;
+  uint64_t vb, dt, kb, c, part, lam, deq, lastw, end;
 };
 // First w_in row a prefill commit projects through (C for per-token outputs, else k): with 4-bit
 // weights the rows from there to n_in are expanded to bf16 in the workspace.
@@ -194,7 +230,8 @@ WsCommit ws_commit(const Shape& s, int dtype, int32_t R, int64_t rows, bool with
   o += align_up((uint64_t)segs * s.nh * 4);
   w.deq = o;
   if (s.w4) o += align_up((uint64_t)(s.n_in - prefill_row0(s)) * s.d * 2);
-  w.end = o;
+  w.lastw = o;
+  w.end = ws_lastw(s, dtype, R, o).end;
   return w;
 }
 
@@ -282,6 +319,76 @@ hipError_t project_out(const Shape& s, int dtype, const hyf_weights* w, const Ro
 }
 
 
+// The last-W memory after a commit (counts already advanced): every request's window as W rows in
+// commit order, padding first (x = 0, so the padding leaves the zero state as it is), into the
+// scan's time-blocked layout, H zeroed, then the Mamba-2 scan of those rows into H.
+int lastw_rescan(const Shape& s, int dt, const hyf_weights* w, char* pool, const ReqTable& rt_in, char* base,
+                 hipStream_t hs) {
+  const WsLastw L = ws_lastw(s, dt, rt_in.n_req, 0);
+  ReqTable rt = rt_in;
+  const int64_t bpr = lastw_blocks(s);
+  for (int i = 0; i <= rt.n_req; ++i) {
+    rt.row0[i] = (int32_t)((int64_t)i * s.W);
+    rt.blk0[i] = (int32_t)((int64_t)i * bpr);
+  }
+  const int64_t vb_blk = (int64_t)(s.dq + s.gn) * HYF_TBLK, dt_blk = (int64_t)s.nh * HYF_TBLK;
+  char* vb = base + L.vb;
+  float* dtb = reinterpret_cast<float*>(base + L.dt);
+  hipError_t he = launch_lastw_gather(dt, s, pool, rt, vb, vb_blk, dtb, dt_blk, hs);
+  if (he != hipSuccess) return HYF_EHIP;
+  ScanArgs sa{};
+  sa.x = vb;
+  sa.B = vb + (int64_t)s.dq * HYF_TBLK * esize(dt);
+  sa.dt = dtb;
+  sa.xblk = vb_blk;
+  sa.bblk = vb_blk;
+  sa.dblk = dt_blk;
+  sa.a_log = w->a_log;
+  sa.dt_bias = w->dt_bias;
+  sa.state_pool = pool;
+  sa.h_direct = nullptr;
+  sa.part = reinterpret_cast<float*>(base + L.part);
+  sa.lam = reinterpret_cast<float*>(base + L.lam);
+  sa.y_mode = 0;
+  sa.d_skip = w->d_skip;
+  int32_t max_segs = 0;
+  fill_segments(s, dt, &rt, false, &sa.seg_tokens, &sa.total_segs, &max_segs);
+  return hip_status(launch_ssd_state(dt, s, sa, rt, max_segs, hs));
+}
+
+// Round-sized commit (at most 16 rows per request): one weight pass over the k | v | B | dt rows,
+// then one round kernel that folds the rows into H (one read-modify-write), appends them to the
+// ring and advances count (the last-W memory: appends them with their B and steps, then rescans).
+int commit_round(const hyf_config* cfg, const hyf_weights* w, char* pool, const ReqTable& rt, int64_t rows,
+                 const void* feats, char* wsb, hipStream_t hs) {
+  const Shape s = make_shape(cfg);
+  const int dt = cfg->dtype, n_req = rt.n_req;
+  const WsDraft L = ws_draft(s, dt, n_req, rows);
+  float* proj = reinterpret_cast<float*>(wsb + L.proj);
+  int32_t* counters = reinterpret_cast<int32_t*>(wsb + L.counters);
+  const int64_t ld = proj_ld(s);
+  RowSrc xs{feats, feats, rows};
+  Epi e{proj + s.off_k, ld, 1, s.n_in, nullptr, 0, 0, counters, n_req * s.nh + n_req};
+  hipError_t he = project_in(s, dt, w, s.off_k, s.n_in - s.off_k, xs, rows, e, hs);
+  if (he != hipSuccess) return HYF_EHIP;
+  RoundArgs ra{};
+  ra.proj = proj;
+  ra.ld = ld;
+  ra.blk_row0 = rows;
+  ra.state_pool = pool;
+  ra.a_log = w->a_log;
+  ra.dt_bias = w->dt_bias;
+  ra.d_skip = w->d_skip;
+  ra.counters = counters;
+  ra.do_commit = 1;
+  ra.do_draft = 0;
+  round_layout(s, n_req, esize(dt), &ra);
+  ra.n_split = 0;
+  if ((he = launch_round(dt, s, ra, rt, hs)) != hipSuccess) return HYF_EHIP;
+  if (s.lastw) return lastw_rescan(s, dt, w, pool, rt, wsb + L.lastw, hs);
+  return HYF_OK;
+}
+
 // Host checks of a draft call (everything but the workspace); fills the request table and the
 // number of commit rows.
 int draft_check(const hyf_config* cfg, const hyf_weights* w, void* state_pool, int32_t pool_slots,
@@ -314,6 +421,12 @@ int draft_run(const hyf_config* cfg, const hyf_weights* w, void* state_pool, con
   const int n_req = rt.n_req;
   char* pool = static_cast<char*>(state_pool);
   const int dt = cfg->dtype;
+  if (s.lastw && rows > 0) {
+    // the window's scan has to follow the append: commit, then draft without commit rows
+    const int st = commit_round(cfg, w, pool, rt, rows, commit_feats, wsb, hs);
+    if (st != HYF_OK) return st;
+    rows = 0;
+  }
   const WsDraft L = ws_draft(s, dt, n_req, rows);
   float* proj = reinterpret_cast<float*>(wsb + L.proj);
 
@@ -456,7 +569,7 @@ int hyf_memory_commit(const hyf_config* cfg, const hyf_weights* w, void* state_p
   if ((st = check_weights(cfg, w)) != HYF_OK) return st;
   if (!state_pool || !aligned(state_pool, ALIGN) || pool_slots < 1 || !cu_rows) return HYF_EINVAL;
   const Shape s = make_shape(cfg);
-  if (y_opt && (s.gdn || !scan_y_supported(s, esize(cfg->dtype)))) return HYF_EUNSUPPORTED;
+  if (y_opt && (s.gdn || s.lastw || !scan_y_supported(s, esize(cfg->dtype)))) return HYF_EUNSUPPORTED;
   if (y_opt && !aligned(y_opt, 16)) return HYF_EINVAL;
   ReqTable rt;
   if ((st = build_table(s, pool_slots, slots, n_req, cu_rows, &rt)) != HYF_OK) return st;
@@ -477,32 +590,7 @@ int hyf_memory_commit(const hyf_config* cfg, const hyf_weights* w, void* state_p
   // a gated delta-rule prefix takes the chunked kernels when they fit the shape, else the
   // token-by-token one; refused only when neither fits
   if (s.gdn && max_n > 16 && !gdn_supported(s) && !gdn_chunked_supported(s, es)) return HYF_EUNSUPPORTED;
-  if (max_n <= 16 && !y_opt) {
-    // Round-sized commit: one weight pass over the k | v | B | dt rows, then one round kernel that
-    // folds the rows into H (one read-modify-write), appends them to the ring and advances count.
-    const WsDraft L = ws_draft(s, dt, n_req, rows);
-    float* proj = reinterpret_cast<float*>(wsb + L.proj);
-    int32_t* counters = reinterpret_cast<int32_t*>(wsb + L.counters);
-    const int64_t ld = proj_ld(s);
-    RowSrc xs{feats, feats, rows};
-    Epi e{proj + s.off_k, ld, 1, s.n_in, nullptr, 0, 0, counters, n_req * s.nh + n_req};
-    hipError_t he = project_in(s, dt, w, s.off_k, s.n_in - s.off_k, xs, rows, e, hs);
-    if (he != hipSuccess) return HYF_EHIP;
-    RoundArgs ra{};
-    ra.proj = proj;
-    ra.ld = ld;
-    ra.blk_row0 = rows;
-    ra.state_pool = pool;
-    ra.a_log = w->a_log;
-    ra.dt_bias = w->dt_bias;
-    ra.d_skip = w->d_skip;
-    ra.counters = counters;
-    ra.do_commit = 1;
-    ra.do_draft = 0;
-    round_layout(s, n_req, es, &ra);
-    ra.n_split = 0;
-    return hip_status(launch_round(dt, s, ra, rt, hs));
-  }
+  if (max_n <= 16 && !y_opt) return commit_round(cfg, w, pool, rt, rows, feats, wsb, hs);
 
   // Prefill-sized commit (or any commit with per-token outputs): projection GEMMs -> ring append ->
   // scan -> count.  The GEMM epilogues write the scan's operands time-blocked (each request's
@@ -553,7 +641,8 @@ int hyf_memory_commit(const hyf_config* cfg, const hyf_weights* w, void* state_p
     if ((he = launch_linear(dt, ks, m, s.d, w_k, s.dq, ek, hs)) != hipSuccess) return HYF_EHIP;
     krow += m;
   }
-  if ((he = launch_ring_append(dt, s, pool, rt, kb, s.dq, vbT, vb_blk, hs)) != hipSuccess) return HYF_EHIP;
+  if ((he = launch_ring_append(dt, s, pool, rt, kb, s.dq, vbT, vb_blk, dtT, dt_blk, hs)) != hipSuccess)
+    return HYF_EHIP;
   ScanArgs sa{};
   sa.x = vbT;
   sa.B = vbT + (int64_t)s.dq * HYF_TBLK * es;
@@ -572,6 +661,11 @@ int hyf_memory_commit(const hyf_config* cfg, const hyf_weights* w, void* state_p
   sa.cblk = c_blk;
   sa.y = y_opt;
   sa.d_skip = w->d_skip;
+  if (s.lastw) {
+    // the last-W memory keeps no running fold: the rings now hold the window; rescan it
+    if ((he = launch_bump_counts(pool, s, rt, hs)) != hipSuccess) return HYF_EHIP;
+    return lastw_rescan(s, dt, w, pool, rt, wsb + L.lastw, hs);
+  }
   if (s.gdn) {
     // chunk offsets of the chunked form (unused by the token-by-token kernel)
     int32_t q = 0;

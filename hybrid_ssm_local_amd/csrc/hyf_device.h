@@ -43,10 +43,11 @@ struct Shape {
   int32_t dq, gn, n_in;
   int32_t gdn;  // 1: gated delta-rule memory (gates alpha at off_dt, beta at off_beta), 0: Mamba-2
   int32_t w4;   // 1: the projections' weights are 4-bit codes and scales
+  int32_t lastw;  // 1: Mamba-2 over the last W committed rows (B and step rings in the state)
   // w_in row offsets of each group
   int32_t off_q, off_c, off_k, off_v, off_b, off_dt, off_beta;
   // state blob
-  uint64_t st_bytes, st_h, st_k, st_v;
+  uint64_t st_bytes, st_h, st_k, st_v, st_b, st_dt;
 };
 
 __device__ __forceinline__ float to_f32(float v) { return v; }

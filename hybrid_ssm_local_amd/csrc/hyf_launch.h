@@ -154,10 +154,18 @@ hipError_t launch_round(int dtype, const Shape& sh, const RoundArgs& a, const Re
 
 // Prefill ring append: the last m_i = min(n_i, W) rows of request i go to slots
 // (count + n_i - m_i + j) mod W.  k: token-major [sum m_i][ld_k] (the requests' last rows back to
-// back); v: time-blocked with block stride ld_v (feature h*P + p, token n_i - m_i + j).
+// back); v: time-blocked with block stride ld_v (feature h*P + p, token n_i - m_i + j); with the
+// last-W memory also B (feature dq + g*N + n of the same buffer) and the raw step (dtT, plain,
+// block stride ld_dt) into the B and step rings.
 hipError_t launch_ring_append(int dtype, const Shape& sh, char* pool, const ReqTable& rt,
                               const void* k, int64_t ld_k, const void* vT, int64_t ld_v,
-                              hipStream_t s);
+                              const float* dtT, int64_t ld_dt, hipStream_t s);
+// The last-W memory's rescan input: request i's window (rt.slot[i], its count already advanced) as
+// W rows in commit order, the first W - min(count, W) of them padding (x = 0, B = 0, step 0),
+// written time-blocked like the prefill's (x | B tiled with block stride ld_vb starting at block
+// rt.blk0[i]; raw steps plain with block stride ld_dt); H of each request zeroed.
+hipError_t launch_lastw_gather(int dtype, const Shape& sh, char* pool, const ReqTable& rt, void* vb, int64_t ld_vb,
+                               float* dtT, int64_t ld_dt, hipStream_t s);
 // count += rows committed, per request (the last launch of a commit).
 hipError_t launch_bump_counts(char* pool, const Shape& sh, const ReqTable& rt, hipStream_t s);
 // Zero fill (a kernel, not a memset, so graph replays stay correct).

@@ -204,7 +204,7 @@ __device__ __forceinline__ void round_tile(const Shape& sh, const RoundArgs& a, 
         }
       }
     }
-  } else if (nrows > 0) {
+  } else if (nrows > 0 && !sh.lastw) {
     const float dec = wl[RMAXC];
 #pragma unroll
     for (int i = 0; i < TMAXG; ++i)
@@ -222,7 +222,7 @@ __device__ __forceinline__ void round_tile(const Shape& sh, const RoundArgs& a, 
       }
     }
   }
-  if (nrows > 0) {
+  if (nrows > 0 && !sh.lastw) {
 #pragma unroll
     for (int i = 0; i < TMAXG; ++i) {
       const int p = p0 + prow + i * rows_wg;
@@ -324,6 +324,15 @@ __device__ __forceinline__ void round_tile(const Shape& sh, const RoundArgs& a, 
       for (int pp = t; pp < P; pp += RT) {
         K[s * P + pp] = from_f32<T>(a.proj[(crow0 + tt) * ld + sh.off_k + h * P + pp]);
         V[s * P + pp] = from_f32<T>(a.proj[(crow0 + tt) * ld + sh.off_v + h * P + pp]);
+      }
+      if (sh.lastw) {
+        // the B row (one head per group writes it) and the raw step of the row, for the rescan
+        char* blob = a.state_pool + (int64_t)slot * sh.st_bytes;
+        if (t == 0) reinterpret_cast<float*>(blob + sh.st_dt)[(int64_t)h * W + s] = a.proj[(crow0 + tt) * ld + sh.off_dt + h];
+        if (h % (nh / sh.G) == 0)
+          for (int n = t; n < N; n += RT)
+            reinterpret_cast<T*>(blob + sh.st_b)[s * sh.gn + grp * N + n] =
+                from_f32<T>(a.proj[(crow0 + tt) * ld + sh.off_b + grp * N + n]);
       }
     }
   }
@@ -674,7 +683,8 @@ __global__ void __launch_bounds__(RT) k_round_wide(Shape sh, RoundArgs a, ReqTab
 
 template <typename T>
 __global__ void __launch_bounds__(256) k_ring_append(Shape sh, char* pool, ReqTable rt, const T* __restrict__ k,
-                                                     int64_t ld_k, const T* __restrict__ vT, int64_t ld_v) {
+                                                     int64_t ld_k, const T* __restrict__ vT, int64_t ld_v,
+                                                     const float* __restrict__ dtT, int64_t ld_dt) {
   const int nh = sh.nh, P = sh.P, W = sh.W;
   const int r = blockIdx.x / nh, h = blockIdx.x % nh;
   const int64_t n = rt.row0[r + 1] - rt.row0[r];
@@ -698,6 +708,62 @@ __global__ void __launch_bounds__(256) k_ring_append(Shape sh, char* pool, ReqTa
     K[s * P + pp] = k[(krow + j) * ld_k + h * P + pp];
     V[s * P + pp] = vT[(rt.blk0[r] + tok / HYF_TBLK) * ld_v + tile_off<T>(h * P + pp, (int)(tok % HYF_TBLK))];
   }
+  if (!sh.lastw) return;
+  // the last-W memory's rings: the raw step of head h, and (one head per group) the group's B row
+  char* blob = pool + (int64_t)slot * sh.st_bytes;
+  float* DTr = reinterpret_cast<float*>(blob + sh.st_dt) + (int64_t)h * W;
+  T* Br = reinterpret_cast<T*>(blob + sh.st_b);
+  const int N = sh.N, grp = h / (sh.nh / sh.G);
+  for (int64_t j = (int64_t)blockIdx.y * 256 + threadIdx.x; j < m; j += (int64_t)gridDim.y * 256) {
+    const int64_t s = (count + n - m + j) % W, tok = n - m + j;
+    DTr[s] = dtT[(rt.blk0[r] + tok / HYF_TBLK) * ld_dt + (int64_t)h * HYF_TBLK + tok % HYF_TBLK];
+  }
+  if (h % (sh.nh / sh.G) != 0) return;
+  for (int64_t idx = (int64_t)blockIdx.y * 256 + threadIdx.x; idx < m * N; idx += (int64_t)gridDim.y * 256) {
+    const int64_t j = idx / N;
+    const int nn = (int)(idx % N);
+    const int64_t s = (count + n - m + j) % W, tok = n - m + j;
+    Br[s * sh.gn + grp * N + nn] =
+        vT[(rt.blk0[r] + tok / HYF_TBLK) * ld_v + tile_off<T>(sh.dq + grp * N + nn, (int)(tok % HYF_TBLK))];
+  }
+}
+
+// The last-W memory's rescan input, one workgroup per (request, head): x of head h (and, for one
+// head per group, the group's B) of the W window positions in commit order, padding first, into the
+// time-blocked layout; the raw steps of head h; H of head h zeroed.  Position j (0 .. W - 1) holds
+// the committed row in slot (count - W + j) mod W when j >= W - min(count, W), else padding.
+template <typename T>
+__global__ void __launch_bounds__(256) k_lastw_gather(Shape sh, char* pool, ReqTable rt, T* __restrict__ vb,
+                                                      int64_t ld_vb, float* __restrict__ dtT, int64_t ld_dt) {
+  const int nh = sh.nh, P = sh.P, N = sh.N, W = sh.W;
+  const int r = blockIdx.x / nh, h = blockIdx.x % nh;
+  const int slot = rt.slot[r];
+  char* blob = pool + (int64_t)slot * sh.st_bytes;
+  const int64_t count = *reinterpret_cast<const int64_t*>(blob);
+  const int64_t n = count < W ? count : W;
+  const int64_t pad = W - n;
+  const T* V = reinterpret_cast<const T*>(blob + sh.st_v) + (int64_t)h * W * P;
+  const T* Br = reinterpret_cast<const T*>(blob + sh.st_b);
+  const float* DTr = reinterpret_cast<const float*>(blob + sh.st_dt) + (int64_t)h * W;
+  const int grp = h / (nh / sh.G);
+  auto src_slot = [&](int64_t j) { return ((count - W + j) % W + W) % W; };
+  for (int64_t idx = threadIdx.x; idx < (int64_t)W * P; idx += 256) {
+    const int64_t j = idx / P;
+    const int p = (int)(idx % P);
+    const T v = j >= pad ? V[src_slot(j) * P + p] : from_f32<T>(0.f);
+    vb[(rt.blk0[r] + j / HYF_TBLK) * ld_vb + tile_off<T>(h * P + p, (int)(j % HYF_TBLK))] = v;
+  }
+  for (int64_t j = threadIdx.x; j < W; j += 256)
+    dtT[(rt.blk0[r] + j / HYF_TBLK) * ld_dt + (int64_t)h * HYF_TBLK + j % HYF_TBLK] = j >= pad ? DTr[src_slot(j)] : 0.f;
+  if (h % (nh / sh.G) == 0)
+    for (int64_t idx = threadIdx.x; idx < (int64_t)W * N; idx += 256) {
+      const int64_t j = idx / N;
+      const int nn = (int)(idx % N);
+      const T b = j >= pad ? Br[src_slot(j) * sh.gn + grp * N + nn] : from_f32<T>(0.f);
+      vb[(rt.blk0[r] + j / HYF_TBLK) * ld_vb + tile_off<T>(sh.dq + grp * N + nn, (int)(j % HYF_TBLK))] = b;
+    }
+  float* H = reinterpret_cast<float*>(blob + sh.st_h) + (int64_t)h * P * N;
+  for (int64_t i = threadIdx.x; i < (int64_t)P * N; i += 256) H[i] = 0.f;
 }
 
 __global__ void k_bump_counts(char* pool, Shape sh, ReqTable rt) {
@@ -812,15 +878,28 @@ hipError_t launch_round(int dtype, const Shape& sh, const RoundArgs& a, const Re
 }
 
 hipError_t launch_ring_append(int dtype, const Shape& sh, char* pool, const ReqTable& rt, const void* k,
-                              int64_t ld_k, const void* vT, int64_t ld_v, hipStream_t s) {
+                              int64_t ld_k, const void* vT, int64_t ld_v, const float* dtT, int64_t ld_dt,
+                              hipStream_t s) {
   const int64_t per = (int64_t)sh.W * sh.P;
   dim3 grid((unsigned)rt.n_req * sh.nh, (unsigned)((per + 255) / 256 < 16 ? (per + 255) / 256 : 16));
   if (dtype == HYF_BF16)
     hipLaunchKernelGGL(k_ring_append<bf16>, grid, dim3(256), 0, s, sh, pool, rt, static_cast<const bf16*>(k), ld_k,
-                       static_cast<const bf16*>(vT), ld_v);
+                       static_cast<const bf16*>(vT), ld_v, dtT, ld_dt);
   else
     hipLaunchKernelGGL(k_ring_append<float>, grid, dim3(256), 0, s, sh, pool, rt, static_cast<const float*>(k), ld_k,
-                       static_cast<const float*>(vT), ld_v);
+                       static_cast<const float*>(vT), ld_v, dtT, ld_dt);
+  return hipGetLastError();
+}
+
+hipError_t launch_lastw_gather(int dtype, const Shape& sh, char* pool, const ReqTable& rt, void* vb, int64_t ld_vb,
+                               float* dtT, int64_t ld_dt, hipStream_t s) {
+  dim3 grid((unsigned)(rt.n_req * sh.nh));
+  if (dtype == HYF_BF16)
+    hipLaunchKernelGGL(k_lastw_gather<bf16>, grid, dim3(256), 0, s, sh, pool, rt, static_cast<bf16*>(vb), ld_vb, dtT,
+                       ld_dt);
+  else
+    hipLaunchKernelGGL(k_lastw_gather<float>, grid, dim3(256), 0, s, sh, pool, rt, static_cast<float*>(vb), ld_vb,
+                       dtT, ld_dt);
   return hipGetLastError();
 }
 

@@ -21,7 +21,7 @@ HEADER = os.path.join(os.path.dirname(_PKG), "include", "hyflash.h")
 
 HYF_OK, HYF_EINVAL, HYF_ESHAPE, HYF_ECAPACITY, HYF_EDTYPE, HYF_EWORKSPACE, HYF_EUNSUPPORTED, HYF_EHIP = range(8)
 HYF_F32, HYF_BF16 = 0, 1
-HYF_MEM_MAMBA2, HYF_MEM_GDN = 0, 1
+HYF_MEM_MAMBA2, HYF_MEM_GDN, HYF_MEM_LASTW = 0, 1, 2
 HYF_WEIGHTS_DENSE, HYF_WEIGHTS_W4 = 0, 1
 HYF_BLOCK = 8
 HYF_MAX_REQUESTS = 128
@@ -41,7 +41,7 @@ class HyfWeights(ctypes.Structure):
 
 
 class HyfStateLayout(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_uint64) for n in ("count_off", "h_off", "k_off", "v_off", "total")]
+    _fields_ = [(n, ctypes.c_uint64) for n in ("count_off", "h_off", "k_off", "v_off", "total", "b_off", "dt_off")]
 
 
 class HyfError(RuntimeError):
@@ -108,7 +108,7 @@ def check(st: int, what: str = "libhyflash") -> None:
 
 def make_config(shape: LayerShape, memory: int | None = None) -> HyfConfig:
     if memory is None:
-        memory = HYF_MEM_GDN if shape.memory == "gdn" else HYF_MEM_MAMBA2
+        memory = {"gdn": HYF_MEM_GDN, "lastw": HYF_MEM_LASTW}.get(shape.memory, HYF_MEM_MAMBA2)
     return HyfConfig(shape.d_model, shape.n_heads, shape.head_dim, shape.d_state, shape.n_groups, shape.window,
                      shape.block, shape.chunk, HYF_BF16 if shape.dtype == BF16 else HYF_F32, memory,
                      shape.cross_slot, HYF_WEIGHTS_W4 if shape.weights == "w4" else HYF_WEIGHTS_DENSE)
@@ -339,4 +339,8 @@ class DrafterLayer:
         H = blob[L.h_off: L.h_off + nh * P * N * 4].view(torch.float32).view(nh, P, N)
         K = blob[L.k_off: L.k_off + nh * W * P * es].view(torch_dtype(sh)).view(nh, W, P)
         V = blob[L.v_off: L.v_off + nh * W * P * es].view(torch_dtype(sh)).view(nh, W, P)
-        return dict(count=count, H=H, K=K, V=V, blob=blob)
+        out = dict(count=count, H=H, K=K, V=V, blob=blob)
+        if L.b_off:
+            out["Bring"] = blob[L.b_off: L.b_off + W * sh.gn * es].view(torch_dtype(sh)).view(W, sh.gn)
+            out["DTring"] = blob[L.dt_off: L.dt_off + nh * W * 4].view(torch.float32).view(nh, W)
+        return out

@@ -58,7 +58,11 @@ typedef enum {
 } hyf_status;
 
 typedef enum { HYF_F32 = 0, HYF_BF16 = 1 } hyf_dtype;
-typedef enum { HYF_MEM_MAMBA2 = 0, HYF_MEM_GDN = 1 } hyf_memory;
+/* The recurrent memory: Mamba-2 over the whole committed history; the gated delta rule in its place
+ * (the paper's memory ablation, Gated DeltaNet-2); or Mamba-2 over the last W committed rows only
+ * (the paper's history ablation, "SSM: last 512": HyFlash paper page, Figures & tables, the
+ * ablation table; explainer, "That is HyFlash", the paragraph on the ablations). */
+typedef enum { HYF_MEM_MAMBA2 = 0, HYF_MEM_GDN = 1, HYF_MEM_LASTW = 2 } hyf_memory;
 /* Weights of the layer's two projections: in the storage dtype, or 4-bit codes with fp32 scales
  * (HyFlash paper page, Figures & tables: the BF16 vs INT4 table; explainer, "Where it earns its
  * keep": the drafter's weights quantized to 4 bits keep the bf16 drafter's acceptance). */
@@ -75,7 +79,8 @@ typedef struct {
   int32_t block;      /* must be HYF_BLOCK                                             */
   int32_t chunk;      /* SSD chunk length L: a power of two, 16..1024                   */
   int32_t dtype;      /* hyf_dtype                                                      */
-  int32_t memory;     /* hyf_memory (HYF_MEM_GDN: see hyf_weights)                      */
+  int32_t memory;     /* hyf_memory (HYF_MEM_GDN: see hyf_weights; HYF_MEM_LASTW: see the
+                         state layout and hyf_memory_commit)                              */
   int32_t cross_slot; /* 1: block rows attend to each other; 0: each only to itself     */
   int32_t weights;    /* hyf_weight_format; HYF_WEIGHTS_W4 needs HYF_BF16 and d_model and
                          nh*head_dim multiples of 128 (HYF_EUNSUPPORTED otherwise)          */
@@ -114,9 +119,12 @@ typedef struct {
 /* Byte offsets inside one request's state blob (each section 256-byte aligned):
  *   header: int64 committed count at offset 0 (the ring head is count mod W), rest 0
  *   H:      fp32 [nh][P][N]
- *   K, V:   storage dtype [nh][W][P]; committed row c of the request sits in slot c mod W */
+ *   K, V:   storage dtype [nh][W][P]; committed row c of the request sits in slot c mod W
+ *   B ring: storage dtype [W][G*N], the B row of the row in each slot      (HYF_MEM_LASTW only)
+ *   step ring: fp32 [nh][W], the raw step (before dt_bias) of each slot     (HYF_MEM_LASTW only)
+ * b_off and dt_off are 0 when the memory keeps no B and step rings. */
 typedef struct {
-  uint64_t count_off, h_off, k_off, v_off, total;
+  uint64_t count_off, h_off, k_off, v_off, total, b_off, dt_off;
 } hyf_state_layout;
 
 int hyf_abi_version(void);
@@ -144,6 +152,12 @@ size_t hyf_workspace_bytes(const hyf_config* cfg, int32_t max_requests, int64_t 
  * slots (host, nullable): pool index of each request; NULL means 0..n_req-1. */
 int hyf_state_reset(const hyf_config* cfg, void* state_pool, int32_t pool_slots,
                     const int32_t* slots, int32_t n_req, void* stream);
+
+/* With memory = HYF_MEM_LASTW a commit appends k, v, B and the raw step of its rows to the rings,
+ * then rebuilds H from zero as the Mamba-2 scan of the last min(count, W) committed rows in commit
+ * order (from the stored, rounded x = v, B and steps); drafting reads that H like any other.  A
+ * draft call with commit rows then runs the commit and the draft one after the other (no fused
+ * projection pass).  Per-token outputs (y_opt) are HYF_EUNSUPPORTED. */
 
 /* With 4-bit weights a round's projections (hyf_draft_block, and hyf_memory_commit of at most 16
  * rows per request) compute with the codes exactly (as hyf_linear_w4); a longer commit first

@@ -344,10 +344,11 @@ def commit(shape, wts: dict, st: dict, feats, want_y: bool = False):
         return st, (np.zeros((0, shape.n_heads, shape.head_dim)) if want_y else None)
     pr = split_projection(layer_projection(feats, wts, "in"), shape)
     if shape.memory == "lastw":
-        # the last-W memory keeps no running state: the ring holds what its scan reads
+        # the last-W memory: after the rows enter the ring, the state is the scan of the window
         if want_y:
             raise ValueError("per-token outputs are defined for the Mamba-2 memory only")
         ring_append(shape, st, pr["k"], pr["v"], pr["B"], pr["dt"])
+        st["H"] = lastw_state(shape, wts, st)
         return st, None
     if shape.memory == "gdn":
         if want_y:
@@ -404,8 +405,7 @@ def draft(shape, wts: dict, st: dict, block_in):
     k_ctx, v_ctx = ring_window(shape, st)
     attn = block_attention(pr["q"], k_ctx, v_ctx, pr["k"], pr["v"], shape.cross_slot)
     Cq = l2_normalize(pr["C"].reshape(nb, shape.n_groups, -1)).reshape(nb, -1) if shape.memory == "gdn" else pr["C"]
-    H = lastw_state(shape, wts, st) if shape.memory == "lastw" else st["H"]
-    mem = memory_readout(H, Cq, pr["v"], wts["d_skip"], shape.n_groups)
+    mem = memory_readout(st["H"], Cq, pr["v"], wts["d_skip"], shape.n_groups)
     o = (attn + mem).reshape(nb, shape.dq)
     return layer_projection(o, wts, "out")
 

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
 def test_struct_sizes_match_the_header():
     assert ctypes.sizeof(hf.HyfConfig) == 48
     assert ctypes.sizeof(hf.HyfWeights) == 72  # nine pointers
-    assert ctypes.sizeof(hf.HyfStateLayout) == 40
+    assert ctypes.sizeof(hf.HyfStateLayout) == 56
 
 
 @pytest.mark.parametrize("shape", [I.TINY, I.QWEN, I.PHI4, I.PHI4_LONG])
@@ -42,7 +42,7 @@ def test_named_shapes_are_accepted(shape):
 @pytest.mark.parametrize("field,value,status", [
     ("head_dim", 72, hf.HYF_ESHAPE), ("head_dim", 0, hf.HYF_ESHAPE), ("d_state", 300, hf.HYF_ESHAPE),
     ("n_groups", 3, hf.HYF_ESHAPE), ("window", 0, hf.HYF_ESHAPE), ("block", 7, hf.HYF_ESHAPE),
-    ("chunk", 8, hf.HYF_ESHAPE), ("chunk", 48, hf.HYF_ESHAPE), ("dtype", 5, hf.HYF_EDTYPE), ("memory", 2, hf.HYF_EINVAL),
+    ("chunk", 8, hf.HYF_ESHAPE), ("chunk", 48, hf.HYF_ESHAPE), ("dtype", 5, hf.HYF_EDTYPE), ("memory", 3, hf.HYF_EINVAL),
     ("cross_slot", 2, hf.HYF_EINVAL), ("weights", 2, hf.HYF_EINVAL), ("d_model", 100, hf.HYF_ESHAPE),
 ])
 def test_bad_configs_are_rejected(field, value, status):
@@ -241,3 +241,23 @@ def test_four_bit_layer_weights_config_and_checks():
     w4_ws = hf.hyf_workspace_bytes(cfg, 1, 8192)
     rows = qwen.n_in - qwen.in_groups["C"][0]
     assert w4_ws >= dense_ws + rows * qwen.d_model * 2 - 256
+
+
+def test_last_w_memory_layout_keeps_b_and_step_rings():
+    # The last-W memory's state blob adds a B ring [W][G*N] (storage dtype) and a raw-step ring
+    # [nh][W] (fp32) after the K and V rings; the other memories have none.
+    for shape in (I.QWEN, I.TINY):
+        lw = shape.replace(memory="lastw")
+        L0 = hf.hyf_state_layout_get(hf.make_config(shape))
+        L = hf.hyf_state_layout_get(hf.make_config(lw))
+        assert L0.b_off == 0 and L0.dt_off == 0
+        assert (L.h_off, L.k_off, L.v_off) == (L0.h_off, L0.k_off, L0.v_off)
+        es = 2 if shape.dtype == "bf16" else 4
+        assert L.b_off == L0.total and L.dt_off >= L.b_off + shape.window * shape.gn * es
+        assert L.total >= L.dt_off + shape.n_heads * shape.window * 4 and L.total % 256 == 0
+    # per-token outputs are Mamba-2 over the whole history only
+    cfg = hf.make_config(I.TINY.replace(memory="lastw"))
+    fake = 1 << 20
+    w = hf.HyfWeights(fake, fake, fake, fake, fake)
+    assert hf.hyf_memory_commit(cfg, w, fake, 1, None, 1, fake, [0, 4], fake, fake, 1 << 30, 0) == \
+        hf.HYF_EUNSUPPORTED

@@ -524,6 +524,44 @@ def test_gated_delta_rule_qwen_prefill_batched_and_rounds():
     pr.check_state(slot=1, what="gdn qwen rounds")
 
 
+LASTW_SHAPES = [
+    ("tiny_fp32", I.TINY.replace(memory="lastw")),
+    ("small_bf16", small_shape("bf16", window=40, memory="lastw")),
+    ("odd_bf16", small_shape("bf16", n_heads=5, head_dim=48, d_state=32, n_groups=5, window=20, chunk=32,
+                             memory="lastw")),
+]
+
+
+@pytest.mark.parametrize("name,shape", LASTW_SHAPES, ids=[c[0] for c in LASTW_SHAPES])
+def test_last_w_memory_matches_the_oracle(name, shape):
+    # The last-W memory: prefills longer and shorter than the window (the rescan pads the short
+    # windows), rounds that commit 0-8 rows per request (commit, rescan, then draft), a round-sized
+    # commit; states (H = the window's scan, rings with B and steps) and outputs against the oracle.
+    pr = Pair(shape, seed=91, pool_slots=3, max_requests=3, max_rows=700)
+    pr.gpu.reset()
+    lens = [300, 7, 0]
+    say("last-W prefill", name, lens)
+    pr.commit([pr.rows(n) for n in lens])
+    for i in range(2):
+        pr.check_state(slot=i, what=f"lastw {name} prefill {i}")
+    acc_rng = pr.rng[4]
+    for rnd in range(6):
+        acc = [int(a) for a in acc_rng.integers(0, 9, size=3)]
+        say("last-W round", rnd, name, acc)
+        g, o = pr.draft([pr.rows(8, 3) for _ in range(3)], commits=[pr.rows(a) for a in acc])
+        for i in range(3):
+            assert_close(g[i], o[i], shape.dtype, f"lastw {name} round {rnd} request {i}")
+    say("last-W small commit", name)
+    pr.commit([pr.rows(5)], slots=[2])
+    for i in range(3):
+        pr.check_state(slot=i, what=f"lastw {name} final {i}")
+        st, ost = pr.gpu.state(i), pr.ost[i]
+        n = min(ost["count"], shape.window)
+        slots = (ost["count"] - n + np.arange(n)) % shape.window
+        assert_close(st["Bring"].float().cpu().numpy()[slots], ost["Bring"][slots], shape.dtype, f"lastw B ring {i}")
+        assert_close(st["DTring"].cpu().numpy()[:, slots], ost["DTring"][slots].T, "f32", f"lastw step ring {i}")
+
+
 def w4_weights(shape, seed):
     """Xavier weights of the shape, quantized with the oracle's round-to-nearest 4-bit format: the
     GPU gets the codes and scales, the oracle the same codes and scales."""

@@ -261,8 +261,8 @@ def test_last_w_memory_is_the_scan_of_the_last_w_committed_rows(total):
     # The last-W memory (the paper's "SSM: last 512" ablation) after `total` committed rows over a
     # window of 6: its state equals the closed form of a scan from zero over exactly the last
     # min(total, 6) rows in commit order, written here from the rows' own x = v, B and step
-    # projections (the sub-matrices) rounded as the ring stores them; the draft reads it with
-    # H . C_q + D v, and commit keeps no running state (H stays zero).
+    # projections (the sub-matrices) rounded as the ring stores them; every commit leaves that
+    # state in H, and the draft reads it with H . C_q + D v.
     shape = I.LayerShape(d_model=24, n_heads=2, head_dim=4, d_state=3, window=6, dtype="bf16", memory="lastw")
     rng = np.random.default_rng(60 + total)
     parts, w_in, w_out = _parts(rng, shape)
@@ -274,7 +274,7 @@ def test_last_w_memory_is_the_scan_of_the_last_w_committed_rows(total):
         a = min(int(rng.integers(1, 5)), total - done)
         st, _ = O.commit(shape, wts, st, F[done:done + a])
         done += a
-    assert st["count"] == total and not np.any(st["H"])
+    assert st["count"] == total
     bf = lambda z: torch.from_numpy(np.asarray(z, np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
     last = F[max(total - 6, 0):]
     x = bf(_lin(last, parts["v"])).reshape(len(last), 2, 4)
@@ -287,6 +287,7 @@ def test_last_w_memory_is_the_scan_of_the_last_w_committed_rows(total):
         for t in range(len(last)):
             H[h] += math.exp(ell[t + 1:, h].sum()) * dt[t, h] * np.outer(x[t, h], B[t])
     assert _rel(O.lastw_state(shape, wts, st), H) < 1e-12
+    assert _rel(st["H"], H) < 1e-12
     # the draft reads that state
     xb = rng.standard_normal((8, 24)) / 4
     ref_st = dict(st, H=H)
