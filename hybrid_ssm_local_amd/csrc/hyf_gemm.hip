@@ -1,4 +1,4 @@
-// bf16 GEMM for K a multiple of 64 on 256x128 tiles (the prefill projections and batched rounds).
+// bf16 GEMM for K a multiple of 64 (the prefill projections and batched rounds).
 //
 // Built in its own translation unit with MFMA accumulators in the unified VGPR file
 // (-mllvm -amdgpu-mfma-vgpr-form): with accumulation registers the register allocator rotated the
@@ -9,32 +9,41 @@
 
 namespace hyf {
 
-// bf16 GEMM for K a multiple of 64: 256x128 macro tiles (rows x features), K step 64, three LDS
-// stages filled by direct global -> LDS copies, one workgroup per CU.  With NW waves the waves
-// form an (NW/2) x 2 grid: wave (wm, wn) owns rows wm*RW .. + RW - 1 (RW = 512 / NW) and features
-// wn*64 .. + 63.  The library runs NW = 8 (two waves per SIMD, 64 x 64 per wave): one wave's
-// MFMAs then cover the other's LDS reads, barrier and copy waits.  Measured at 8192 x 2560 x 2720:
-// 117 us with 8 waves against 145 us with 4 waves of 128 x 64 (one per SIMD).
+// bf16 GEMM for K a multiple of 64: BM x BN macro tiles (rows x features), K step 64, three LDS
+// stages filled by direct global -> LDS copies.  With NW waves the waves form an (NW/2) x 2 grid:
+// wave (wm, wn) owns rows wm*RW .. + RW - 1 (RW = 2 BM / NW) and features wn*BN/2 .. + BN/2 - 1.
+// Large products run 256 x 128 tiles with NW = 8 (two waves per SIMD, 64 x 64 per wave, one
+// workgroup per CU): one wave's MFMAs then cover the other's LDS reads, barrier and copy waits.
+// Measured at 8192 x 2560 x 2720: 117 us with 8 waves against 145 us with 4 waves of 128 x 64 (one
+// per SIMD).  Products of a few hundred rows (the batched rounds' projections) have too few such
+// tiles to fill 256 CUs and take smaller ones (several workgroups per CU).
 //
-// Per K step the workgroup does 2*256*128*64 flops against 48 KiB staged, so a CU at the MFMA
-// rate needs about 47 B/clk from L2 (a 128x128 tile would need 64 B/clk per pair of workgroups).
-// Three stages keep two K steps of copies in flight while one computes.
+// Per K step a 256 x 128 workgroup does 2*256*128*64 flops against 48 KiB staged, so a CU at the
+// MFMA rate needs about 47 B/clk from L2; smaller tiles need more bytes per flop.  Three stages keep
+// two K steps of copies in flight while one computes.
 //
 // LDS operand layout (both operands are K-contiguous rows): row r of a stage is 128 bytes = 8
 // chunks of 16 bytes; logical chunk c sits at position c ^ (r & 7), so the 16 lanes of an MFMA
 // fragment load (16 rows, one chunk) hit 8 distinct 16-byte bank groups per 8 lanes.  A direct
 // copy writes lane l's 16 bytes at base + 16 l, so lane l of a copy covering rows r0 .. r0 + 7
 // (r0 a multiple of 8) fetches row r0 + l / 8, logical chunk (l % 8) ^ (l / 8).
-constexpr int G2_M = 256, G2_N = 128, G2_K = 64, G2_ST = 3;
-constexpr int G2_STAGE = (G2_M + G2_N) * G2_K * 2;  // bytes per stage (48 KiB)
-constexpr int G2_LDS = G2_ST * G2_STAGE;            // 144 KiB
-constexpr int G2_GROUP = 4;                         // M tiles per group in the tile order
-constexpr int G2_NW = 8;                            // waves per workgroup (two per SIMD)
+constexpr int G2_K = 64, G2_ST = 3;
+constexpr int G2_GROUP = 4;  // M tiles per group in the tile order
+template <int BM, int BN>
+constexpr int g2_stage() { return (BM + BN) * G2_K * 2; }  // bytes per stage (48 KiB at 256 x 128)
+template <int BM, int BN>
+constexpr int g2_lds() {  // three stages; the epilogue's fp32 tile ([f][m] or [m][f]) reuses them
+  constexpr int st = G2_ST * g2_stage<BM, BN>(), tr = BN * (BM + 4) * 4, rm = BM * (BN + 4) * 4;
+  return st > tr ? (st > rm ? st : rm) : (tr > rm ? tr : rm);
+}
 
-template <typename TO, int NW>
-__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
-k_gemm_bf16_256(RowSrc xs, int M, int K, const bf16* __restrict__ W, int Nout, Epi epi, int tm, int tn,
-                int per_xcd) {
+template <typename TO, int BM, int BN, int NW, int WPE>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+k_gemm_bf16_tile(RowSrc xs, int M, int K, const bf16* __restrict__ W, int Nout, Epi epi, int tm, int tn,
+                 int per_xcd) {
+  constexpr int G2_M = BM, G2_N = BN, G2_STAGE = g2_stage<BM, BN>();
+  constexpr int BT = BN / 32;  // 16-feature tiles per wave
+  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0 && BN % 32 == 0 && (2 * BM / NW) % 16 == 0, "tile shape");
   extern __shared__ __attribute__((aligned(16))) char smem[];
   // Tile order: workgroup b runs on XCD b % 8; each XCD takes a contiguous range of tiles, walked
   // in groups of G2_GROUP row tiles column by column, so the workgroups an XCD runs together
@@ -49,7 +58,7 @@ k_gemm_bf16_256(RowSrc xs, int M, int K, const bf16* __restrict__ W, int Nout, E
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int i = lane & 15, g = lane >> 4;
   constexpr int NT = 64 * NW;             // threads
-  constexpr int RW = G2_M / (NW / 2);     // rows per wave (128 or 64)
+  constexpr int RW = G2_M / (NW / 2);     // rows per wave
   constexpr int AT = RW / 16;             // row tiles per wave
   constexpr int CA = G2_M / 8 / NW, CB = G2_N / 8 / NW;  // copies per stage and thread
   const int wm = wave >> 1, wn = wave & 1;
@@ -81,29 +90,29 @@ k_gemm_bf16_256(RowSrc xs, int M, int K, const bf16* __restrict__ W, int Nout, E
     for (int j = 0; j < CB; ++j) lds_dma16(bsrc[j] + kb, st + G2_M * 128 + (wave + NW * j) * 1024);
   };
 
-  f32x4 acc[AT][4];
+  f32x4 acc[AT][BT];
 #pragma unroll
   for (int a = 0; a < AT; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < BT; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nk = K / G2_K;
   issue(0);
   if (nk > 1) issue(1);
   // fragment offsets: row r (r & 7 == i & 7), logical chunk c = 4 ks + g at position c ^ (i & 7)
-  const int arow = (wm * RW + i) * 128, brow = G2_M * 128 + (wn * 64 + i) * 128;
-  auto frags = [&](const char* st, int ks, bf16x8 (&fa)[AT], bf16x8 (&fb)[4]) __attribute__((always_inline)) {
+  const int arow = (wm * RW + i) * 128, brow = G2_M * 128 + (wn * (BN / 2) + i) * 128;
+  auto frags = [&](const char* st, int ks, bf16x8 (&fa)[AT], bf16x8 (&fb)[BT]) __attribute__((always_inline)) {
     const int co = ((4 * ks + g) ^ (i & 7)) * 16;
 #pragma unroll
     for (int a = 0; a < AT; ++a) fa[a] = *reinterpret_cast<const bf16x8*>(st + arow + a * 16 * 128 + co);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) fb[b] = *reinterpret_cast<const bf16x8*>(st + brow + b * 16 * 128 + co);
+    for (int b = 0; b < BT; ++b) fb[b] = *reinterpret_cast<const bf16x8*>(st + brow + b * 16 * 128 + co);
   };
-  auto mma = [&](const bf16x8 (&fa)[AT], const bf16x8 (&fb)[4]) __attribute__((always_inline)) {
+  auto mma = [&](const bf16x8 (&fa)[AT], const bf16x8 (&fb)[BT]) __attribute__((always_inline)) {
 #pragma unroll
     for (int a = 0; a < AT; ++a)
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
+      for (int b = 0; b < BT; ++b)
         acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
   };
   // Software pipeline over half-steps (32 k values).  Fragments of the next half-step are read
@@ -118,7 +127,7 @@ k_gemm_bf16_256(RowSrc xs, int M, int K, const bf16* __restrict__ W, int Nout, E
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  bf16x8 fa0[AT], fb0[4], fa1[AT], fb1[4];
+  bf16x8 fa0[AT], fb0[BT], fa1[AT], fb1[BT];
   if (nk > 1)
     vm_wait<CA + CB>();
   else
@@ -155,17 +164,18 @@ k_gemm_bf16_256(RowSrc xs, int M, int K, const bf16* __restrict__ W, int Nout, E
   __syncthreads();  // the stages are dead: the epilogue reuses LDS
 
   if (epi.trans) {
-    // Time-blocked output: a 256-row tile spans two blocks (m0 is a multiple of 256).  The fp32
-    // tile is staged as [f][m] (pitch CP floats); each item then writes 8 tokens of one feature:
-    // one 16-byte chunk of the tiled layout (out0), or two 16-byte runs of a plain row (out1).
+    // Time-blocked output: m0 is a multiple of BM, so every run of 8 rows lies in one block.  The
+    // fp32 tile is staged as [f][m] (pitch CP floats); each item then writes 8 tokens of one
+    // feature: one 16-byte chunk of the tiled layout (out0), or two 16-byte runs of a plain row
+    // (out1).
     constexpr int CP = G2_M + 4;
     float* ct = reinterpret_cast<float*>(smem);
 #pragma unroll
     for (int a = 0; a < AT; ++a)
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
+      for (int b = 0; b < BT; ++b)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ct[(wn * 64 + b * 16 + i) * CP + wm * RW + a * 16 + 4 * g + r] = acc[a][b][r];
+        for (int r = 0; r < 4; ++r) ct[(wn * (BN / 2) + b * 16 + i) * CP + wm * RW + a * 16 + 4 * g + r] = acc[a][b][r];
     __syncthreads();
     for (int it = t; it < G2_N * (G2_M / 8); it += NT) {
       const int fl = it % G2_N, m8 = (it / G2_N) * 8;
@@ -200,9 +210,9 @@ k_gemm_bf16_256(RowSrc xs, int M, int K, const bf16* __restrict__ W, int Nout, E
 #pragma unroll
   for (int a = 0; a < AT; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < BT; ++b)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ct[(wm * RW + a * 16 + 4 * g + r) * RP + wn * 64 + b * 16 + i] = acc[a][b][r];
+      for (int r = 0; r < 4; ++r) ct[(wm * RW + a * 16 + 4 * g + r) * RP + wn * (BN / 2) + b * 16 + i] = acc[a][b][r];
   __syncthreads();
   for (int it = t; it < G2_M * (G2_N / 8); it += NT) {
     const int ml = it / (G2_N / 8), f8 = (it % (G2_N / 8)) * 8;
@@ -238,19 +248,34 @@ k_gemm_bf16_256(RowSrc xs, int M, int K, const bf16* __restrict__ W, int Nout, E
   }
 }
 
-hipError_t launch_gemm256(RowSrc x, int M, int K, const bf16* W, int Nout, const Epi& epi, hipStream_t s) {
+template <int BM, int BN, int NW, int WPE>
+static hipError_t launch_tile(RowSrc x, int M, int K, const bf16* W, int Nout, const Epi& epi, hipStream_t s) {
+  constexpr int lds = g2_lds<BM, BN>();
   static std::once_flag once;
   static hipError_t set_err = hipSuccess;
   std::call_once(once, [] {
-    set_err = hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm_bf16_256<bf16, G2_NW>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, G2_LDS);
+    set_err = hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm_bf16_tile<bf16, BM, BN, NW, WPE>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   });
   if (set_err != hipSuccess) return set_err;
-  const int tm = (M + G2_M - 1) / G2_M, tn = (Nout + G2_N - 1) / G2_N;
+  const int tm = (M + BM - 1) / BM, tn = (Nout + BN - 1) / BN;
   const int per_xcd = (tm * tn + 7) / 8;
-  hipLaunchKernelGGL((k_gemm_bf16_256<bf16, G2_NW>), dim3(8 * per_xcd), dim3(64 * G2_NW), G2_LDS, s, x, M, K, W, Nout, epi, tm, tn,
-                     per_xcd);
+  hipLaunchKernelGGL((k_gemm_bf16_tile<bf16, BM, BN, NW, WPE>), dim3(8 * per_xcd), dim3(64 * NW), lds, s, x, M, K, W,
+                     Nout, epi, tm, tn, per_xcd);
   return hipGetLastError();
+}
+
+// Tile choice, from measured products (bf16, K 2560-5120): 256 x 128 tiles (one workgroup of 8
+// waves per CU) once there are 192 or more of them; below that the largest of 128 x 128 (one per
+// CU), 128 x 64 (8 waves, two per CU) and 64 x 64 (4 waves, three per CU) that still gives 160 or
+// more workgroups, else 64 x 64.  At 512 x 2560 x 2560 this takes 17 us against 37.5 us for the
+// 40 large tiles; at 800 x 2560 x 7968 the 252 large tiles stay fastest (48.7 us).
+hipError_t launch_gemm256(RowSrc x, int M, int K, const bf16* W, int Nout, const Epi& epi, hipStream_t s) {
+  auto tiles = [&](int bm, int bn) { return (int64_t)((M + bm - 1) / bm) * ((Nout + bn - 1) / bn); };
+  if (tiles(256, 128) >= 192) return launch_tile<256, 128, 8, 2>(x, M, K, W, Nout, epi, s);
+  if (tiles(128, 128) >= 160) return launch_tile<128, 128, 8, 2>(x, M, K, W, Nout, epi, s);
+  if (tiles(128, 64) >= 160) return launch_tile<128, 64, 8, 4>(x, M, K, W, Nout, epi, s);
+  return launch_tile<64, 64, 4, 3>(x, M, K, W, Nout, epi, s);
 }
 
 }  // namespace hyf

@@ -728,42 +728,65 @@ __global__ void __launch_bounds__(256) k_ring_append(Shape sh, char* pool, ReqTa
   }
 }
 
-// The last-W memory's rescan input, one workgroup per (request, head): x of head h (and, for one
-// head per group, the group's B) of the W window positions in commit order, padding first, into the
-// time-blocked layout; the raw steps of head h; H of head h zeroed.  Position j (0 .. W - 1) holds
-// the committed row in slot (count - W + j) mod W when j >= W - min(count, W), else padding.
+// The last-W memory's rescan input.  Window position j (0 .. W - 1) holds the committed row in ring
+// slot (count - W + j) mod W when j >= W - min(count, W), else padding (zeros).  One workgroup per
+// (request, time block of the window, e) where e < nh is head e (its x rows, its raw steps, and a
+// share of its H, zeroed) and e = nh + g is group g's B rows.  Each thread writes whole 16-byte
+// chunks of the tiled layout (VN tokens of one feature, consecutive threads on consecutive
+// features, so the ring reads of a wave are contiguous rows and the writes fill 1 KiB tiles in
+// lane order); slot arithmetic stays 32-bit (count mod W taken once).
 template <typename T>
 __global__ void __launch_bounds__(256) k_lastw_gather(Shape sh, char* pool, ReqTable rt, T* __restrict__ vb,
-                                                      int64_t ld_vb, float* __restrict__ dtT, int64_t ld_dt) {
+                                                      int64_t ld_vb, float* __restrict__ dtT, int64_t ld_dt,
+                                                      int nblk) {
+  typedef typename Vec16<T>::type V;
+  constexpr int VN = Vec16<T>::n;
   const int nh = sh.nh, P = sh.P, N = sh.N, W = sh.W;
-  const int r = blockIdx.x / nh, h = blockIdx.x % nh;
-  const int slot = rt.slot[r];
-  char* blob = pool + (int64_t)slot * sh.st_bytes;
+  const int ne = nh + sh.G;
+  const int blk = (int)(blockIdx.x % nblk);
+  const int e = (int)((blockIdx.x / nblk) % ne);
+  const int r = (int)(blockIdx.x / (nblk * ne));
+  char* blob = pool + (int64_t)rt.slot[r] * sh.st_bytes;
   const int64_t count = *reinterpret_cast<const int64_t*>(blob);
-  const int64_t n = count < W ? count : W;
-  const int64_t pad = W - n;
-  const T* V = reinterpret_cast<const T*>(blob + sh.st_v) + (int64_t)h * W * P;
-  const T* Br = reinterpret_cast<const T*>(blob + sh.st_b);
-  const float* DTr = reinterpret_cast<const float*>(blob + sh.st_dt) + (int64_t)h * W;
-  const int grp = h / (nh / sh.G);
-  auto src_slot = [&](int64_t j) { return ((count - W + j) % W + W) % W; };
-  for (int64_t idx = threadIdx.x; idx < (int64_t)W * P; idx += 256) {
-    const int64_t j = idx / P;
-    const int p = (int)(idx % P);
-    const T v = j >= pad ? V[src_slot(j) * P + p] : from_f32<T>(0.f);
-    vb[(rt.blk0[r] + j / HYF_TBLK) * ld_vb + tile_off<T>(h * P + p, (int)(j % HYF_TBLK))] = v;
-  }
-  for (int64_t j = threadIdx.x; j < W; j += 256)
-    dtT[(rt.blk0[r] + j / HYF_TBLK) * ld_dt + (int64_t)h * HYF_TBLK + j % HYF_TBLK] = j >= pad ? DTr[src_slot(j)] : 0.f;
-  if (h % (nh / sh.G) == 0)
-    for (int64_t idx = threadIdx.x; idx < (int64_t)W * N; idx += 256) {
-      const int64_t j = idx / N;
-      const int nn = (int)(idx % N);
-      const T b = j >= pad ? Br[src_slot(j) * sh.gn + grp * N + nn] : from_f32<T>(0.f);
-      vb[(rt.blk0[r] + j / HYF_TBLK) * ld_vb + tile_off<T>(sh.dq + grp * N + nn, (int)(j % HYF_TBLK))] = b;
+  const int pad = count < W ? W - (int)count : 0;
+  const int c = (int)(count % W);
+  const int j0 = blk * HYF_TBLK;
+  const int jn = min(W - j0, HYF_TBLK);  // window positions in this block
+  T* dst = vb + (int64_t)(rt.blk0[r] + blk) * ld_vb;
+  auto ring_slot = [&](int j) {
+    const int q = c + j;
+    return q >= W ? q - W : q;
+  };
+  // rows: the ring of this head's x (pitch P) or of the group's B (pitch gn, offset g N)
+  const bool is_b = e >= nh;
+  const int nf = is_b ? N : P;
+  const int64_t f0 = is_b ? (int64_t)sh.dq + (int64_t)(e - nh) * N : (int64_t)e * P;
+  const T* src = is_b ? reinterpret_cast<const T*>(blob + sh.st_b) + (int64_t)(e - nh) * N
+                      : reinterpret_cast<const T*>(blob + sh.st_v) + (int64_t)e * W * P;
+  const int pitch = is_b ? sh.gn : P;
+  const int nch = nf * (HYF_TBLK / VN);
+  for (int i = threadIdx.x; i < nch; i += 256) {
+    const int f = i % nf, tc = i / nf;
+    V v;
+#pragma unroll
+    for (int u = 0; u < VN; ++u) {
+      const int jj = tc * VN + u, j = j0 + jj;
+      v[u] = jj < jn && j >= pad ? src[(int64_t)ring_slot(j) * pitch + f] : from_f32<T>(0.f);
     }
-  float* H = reinterpret_cast<float*>(blob + sh.st_h) + (int64_t)h * P * N;
-  for (int64_t i = threadIdx.x; i < (int64_t)P * N; i += 256) H[i] = 0.f;
+    *reinterpret_cast<V*>(dst + tile_off<T>(f0 + f, tc * VN)) = v;
+  }
+  if (is_b) return;
+  const int h = e;
+  const float* DTr = reinterpret_cast<const float*>(blob + sh.st_dt) + (int64_t)h * W;
+  for (int jj = threadIdx.x; jj < HYF_TBLK; jj += 256) {
+    const int j = j0 + jj;
+    dtT[(int64_t)(rt.blk0[r] + blk) * ld_dt + (int64_t)h * HYF_TBLK + jj] = jj < jn && j >= pad ? DTr[ring_slot(j)] : 0.f;
+  }
+  // this block's share of H (P N / 4 16-byte words over the nblk blocks of the head)
+  f32x4* H = reinterpret_cast<f32x4*>(blob + sh.st_h) + (int64_t)h * P * N / 4;
+  const int words = P * N / 4, share = (words + nblk - 1) / nblk;
+  const int w1 = min(words, (blk + 1) * share);
+  for (int i = blk * share + threadIdx.x; i < w1; i += 256) H[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 __global__ void k_bump_counts(char* pool, Shape sh, ReqTable rt) {
@@ -893,13 +916,14 @@ hipError_t launch_ring_append(int dtype, const Shape& sh, char* pool, const ReqT
 
 hipError_t launch_lastw_gather(int dtype, const Shape& sh, char* pool, const ReqTable& rt, void* vb, int64_t ld_vb,
                                float* dtT, int64_t ld_dt, hipStream_t s) {
-  dim3 grid((unsigned)(rt.n_req * sh.nh));
+  const int nblk = (sh.W + HYF_TBLK - 1) / HYF_TBLK;
+  dim3 grid((unsigned)(rt.n_req * (sh.nh + sh.G) * nblk));
   if (dtype == HYF_BF16)
     hipLaunchKernelGGL(k_lastw_gather<bf16>, grid, dim3(256), 0, s, sh, pool, rt, static_cast<bf16*>(vb), ld_vb, dtT,
-                       ld_dt);
+                       ld_dt, nblk);
   else
     hipLaunchKernelGGL(k_lastw_gather<float>, grid, dim3(256), 0, s, sh, pool, rt, static_cast<float*>(vb), ld_vb,
-                       dtT, ld_dt);
+                       dtT, ld_dt, nblk);
   return hipGetLastError();
 }
 

@@ -160,17 +160,23 @@ LINEAR_CASES = [  # (dtype, K, Nout, Ms): K tails past a 128-wide slab, M across
     # K past the last 128-wide slab on the double-buffered kernel (one 16-row tile, K >= 2048):
     # its loads past K are clamped and zeroed
     ("bf16", 2184, 300, [1, 8, 16]),
-    # the 256x128-tile GEMM (K a multiple of 64, M > 64): one, two and three K steps (the
-    # three-stage pipeline's edges), ragged row and feature tiles
+    # the MFMA GEMM (K a multiple of 64, M > 64), its tile chosen by the product's size.  64 x 64
+    # tiles: one, two and three K steps (the three-stage pipeline's edges), ragged row and feature
+    # tiles
     ("bf16", 64, 130, [65, 257]),
     ("bf16", 128, 129, [100]),
     ("bf16", 192, 256, [300]),
+    # 128 x 128 tiles (176 of them)
     ("bf16", 256, 2720, [1000]),
+    # 128 x 64 tiles (164), ragged rows and features
+    ("bf16", 128, 2600, [500]),
+    # 256 x 128 tiles (192), ragged features
+    ("bf16", 128, 3000, [2000]),
     ("f32", 256, 100, [1, 20, 64, 65]),
 ]
 
 
-@pytest.mark.parametrize("dtype,K,Nout,Ms", LINEAR_CASES, ids=[f"{c[0]}_K{c[1]}" for c in LINEAR_CASES])
+@pytest.mark.parametrize("dtype,K,Nout,Ms", LINEAR_CASES, ids=[f"{c[0]}_K{c[1]}_N{c[2]}" for c in LINEAR_CASES])
 def test_linear_matches_the_oracle(dtype, K, Nout, Ms):
     shape = small_shape(dtype)
     cfg = hf.make_config(shape)
