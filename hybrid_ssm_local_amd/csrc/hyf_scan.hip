@@ -103,6 +103,17 @@ k_ssd_seg(Shape sh, ScanArgs a, ReqTable rt, int npb, int nnb, int n_items, int 
   lds_stage16<SG_THREADS>(nblk_dt * (TB / 4), wt, [&](int i) {
     return a.dt + (blk0 + i / (TB / 4)) * a.dblk + (int64_t)h * TB + 4 * (i % (TB / 4));
   });
+  // The request's first segment starts from exp(lam_seg) H: this workgroup's block of H goes to LDS
+  // behind the weights (unpitched rows of NB) in the same round trip as the raw steps.
+  constexpr int PB = PB16 * 16, NB = NB16 * 16;
+  float* Hh = a.h_direct ? a.h_direct + (int64_t)h * P * N
+                         : reinterpret_cast<float*>(a.state_pool + (int64_t)rt.slot[r] * sh.st_bytes + sh.st_h) +
+                               (int64_t)h * P * N;
+  float* hs = wt + (seg_len + MS - 1) / MS * MS;
+  if (ls == 0)
+    lds_stage16<SG_THREADS>(PB * NB / 4, hs, [&](int i) {
+      return Hh + (int64_t)(p0 + i / (NB / 4)) * N + n0 + (i % (NB / 4)) * 4;
+    });
   vm_wait<0>();
   __syncthreads();
   const int run4 = ((len + 4 * SG_THREADS - 1) / (4 * SG_THREADS)) | 1;
@@ -154,22 +165,11 @@ k_ssd_seg(Shape sh, ScanArgs a, ReqTable rt, int npb, int nnb, int n_items, int 
   }
 
   // ---- accumulators.  Tile (pt, nt), lane (li, lg), register rr holds state row
-  // p0 + 16 pt + 4 lg + rr, column n0 + 16 nt + li (the MFMA output layout).  The request's first
-  // segment starts from exp(lam_seg) H: this workgroup's block of H is staged in LDS behind the
-  // weights (16-byte loads by every thread, row pitch RP) and wave 0 starts from it; every other
-  // accumulator starts at 0.
-  constexpr int PB = PB16 * 16, NB = NB16 * 16, RP = NB + 4;
-  float* Hh = a.h_direct ? a.h_direct + (int64_t)h * P * N
-                         : reinterpret_cast<float*>(a.state_pool + (int64_t)rt.slot[r] * sh.st_bytes + sh.st_h) +
-                               (int64_t)h * P * N;
-  float* hs = wt + (seg_len + MS - 1) / MS * MS;
-  if (ls == 0) {
-    for (int idx = t; idx < PB * NB / 4; idx += SG_THREADS) {
-      const int p = idx / (NB / 4), n = (idx % (NB / 4)) * 4;
-      *reinterpret_cast<f32x4*>(hs + p * RP + n) = *reinterpret_cast<const f32x4*>(Hh + (int64_t)(p0 + p) * N + n0 + n);
-    }
-  }
-  __syncthreads();  // weights (and the staged H) complete
+  // p0 + 16 pt + 4 lg + rr, column n0 + 16 nt + li (the MFMA output layout).  Wave 0 of the
+  // request's first segment starts from exp(lam_seg) H (staged above); every other accumulator
+  // starts at 0.
+  constexpr int RP = NB + 4;
+  __syncthreads();  // weights complete
   f32x4 acc[PB16][NB16];
 #pragma unroll
   for (int pt = 0; pt < PB16; ++pt)
@@ -182,7 +182,7 @@ k_ssd_seg(Shape sh, ScanArgs a, ReqTable rt, int npb, int nnb, int n_items, int 
 #pragma unroll
       for (int nt = 0; nt < NB16; ++nt)
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) acc[pt][nt][rr] = d0 * hs[(pt * 16 + 4 * lg + rr) * RP + nt * 16 + li];
+        for (int rr = 0; rr < 4; ++rr) acc[pt][nt][rr] = d0 * hs[(pt * 16 + 4 * lg + rr) * NB + nt * 16 + li];
   }
 
   // ---- operand loads.  With the tiled layout the 16-byte chunk lane l brings for an MFMA sits at
@@ -560,7 +560,8 @@ int64_t scan_items_per_seg(const Shape& sh) {
 }
 
 // LDS of one workgroup: the pre-pass scratch, one weight per token (whole macro-steps) and a
-// staged block of H (row pitch NB + 4); afterwards two row-major accumulator blocks.
+// staged block of H (unpitched rows); afterwards two row-major accumulator blocks (row pitch
+// NB + 4).
 static size_t scan_acc_block_bytes(const Shape& sh) {
   const SegGeo g = seg_geo(sh);
   return sizeof(float) * (16 * g.pb16) * (16 * g.nb16 + 4);
