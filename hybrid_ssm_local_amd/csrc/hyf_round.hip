@@ -645,7 +645,15 @@ __device__ __forceinline__ void round_body(const Shape& sh, const RoundArgs& a, 
   __shared__ int s_last;
   const int nh = sh.nh;
   const int per = a.n_tiles + a.n_split;
-  const int rh = blockIdx.x / per, role = blockIdx.x % per;
+  // Block b runs on XCD b % 8: each XCD takes a contiguous range of (request, head, role) items, so
+  // the workgroups of one (request, head) share its L2 (the block rows' q and C, read by every
+  // split and tile); 64 Qwen3-4B-shaped requests 248 -> 236 us.  Only speed depends on this
+  // placement: the hand-over to the merge is device-coherent wherever the workgroups run.  The
+  // grid is padded to a multiple of 8.
+  const int per_xcd = (int)(gridDim.x / 8);
+  const int item = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (item >= rt.n_req * nh * per) return;
+  const int rh = item / per, role = item % per;
   const int r = rh / nh, h = rh % nh;
   if (role < a.n_tiles)
     round_tile<T, TMAXG>(sh, a, rt, r, h, role, dsm);
@@ -882,7 +890,8 @@ static hipError_t launch_round_t(const Shape& sh, const RoundArgs& a, const ReqT
     if (set_err != hipSuccess) return set_err;
   }
   const int per = a.n_tiles + a.n_split;
-  hipLaunchKernelGGL(kern, dim3((unsigned)(rt.n_req * sh.nh * per)), dim3(RT), lds, s, sh, a, rt);
+  const unsigned items = (unsigned)(rt.n_req * sh.nh * per);
+  hipLaunchKernelGGL(kern, dim3((items + 7) / 8 * 8), dim3(RT), lds, s, sh, a, rt);
   return hipGetLastError();
 }
 
