@@ -622,7 +622,40 @@ int hyf_memory_commit(const hyf_config* cfg, const hyf_weights* w, void* state_p
   const char* w_vbd = w_row(s.off_v);
   const char* w_k = w_row(s.off_k);
   int64_t krow = 0;
-  for (int i = 0; i < n_req; ++i) {
+  if (dt == HYF_BF16 && s.d % 64 == 0) {
+    // bf16: one grouped GEMM launch over every request's rows for v | B | dt (and C), one for k
+    // (each request's last min(n_i, W) rows).  Each request's time-blocked output starts its own
+    // block, so its product rows start on a multiple of 8 (padding rows between requests); the k
+    // rows are row-major and packed.
+    RowGroups gv{}, gk{};
+    gv.n = gk.n = n_req;
+    gv.m0[0] = gk.m0[0] = 0;
+    for (int i = 0; i < n_req; ++i) {
+      const int64_t n = cu_rows[i + 1] - cu_rows[i];
+      const int64_t m = n < s.W ? n : s.W;
+      gv.m0[i + 1] = (int32_t)(gv.m0[i] + (n + 7) / 8 * 8);
+      gv.cnt[i] = (int32_t)n;
+      gv.src0[i] = (int32_t)cu_rows[i];
+      gv.blk0[i] = rt.blk0[i];
+      gk.m0[i + 1] = (int32_t)(gk.m0[i] + m);
+      gk.cnt[i] = (int32_t)m;
+      gk.src0[i] = (int32_t)(cu_rows[i + 1] - m);
+      gk.blk0[i] = 0;
+    }
+    const bf16* X = static_cast<const bf16*>(feats);
+    Epi e{vbT, vb_blk, 0, nvb, dtT, dt_blk, 1};
+    if ((he = launch_gemm_grouped(X, gv, s.d, reinterpret_cast<const bf16*>(w_vbd), nvb + ndt, e, hs)) != hipSuccess)
+      return HYF_EHIP;
+    if (with_y) {
+      Epi ec{cT, c_blk, 0, s.gn, nullptr, 0, 1};
+      if ((he = launch_gemm_grouped(X, gv, s.d, reinterpret_cast<const bf16*>(w_c), s.gn, ec, hs)) != hipSuccess)
+        return HYF_EHIP;
+    }
+    Epi ek{kb, s.dq, 0, s.dq, nullptr, 0, 0};
+    if ((he = launch_gemm_grouped(X, gk, s.d, reinterpret_cast<const bf16*>(w_k), s.dq, ek, hs)) != hipSuccess)
+      return HYF_EHIP;
+  }
+  for (int i = 0; i < n_req && !(dt == HYF_BF16 && s.d % 64 == 0); ++i) {
     const int64_t n = cu_rows[i + 1] - cu_rows[i];
     if (n == 0) continue;
     const char* src = static_cast<const char*>(feats) + cu_rows[i] * (int64_t)s.d * es;

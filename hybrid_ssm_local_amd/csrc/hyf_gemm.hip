@@ -4,6 +4,7 @@
 // (-mllvm -amdgpu-mfma-vgpr-form): with accumulation registers the register allocator rotated the
 // 128 accumulator registers through copies on every K step.
 #include <mutex>
+#include <type_traits>
 
 #include "hyf_launch.h"
 
@@ -37,10 +38,35 @@ constexpr int g2_lds() {  // three stages; the epilogue's fp32 tile ([f][m] or [
   return st > tr ? (st > rm ? st : rm) : (tr > rm ? tr : rm);
 }
 
-template <typename TO, int BM, int BN, int NW, int WPE>
+// A product of one group of rows (plain launches) carries no row table.
+struct NoGroups {};
+// Group of product row m (m < M): the last g with m0[g] <= m (empty groups are skipped over).
+__device__ __forceinline__ int group_of(const RowGroups& g, int m) {
+  int lo = 0, hi = g.n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (g.m0[mid] <= m) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+// Store of element (token off of time block blk, feature f) through a time-blocked epilogue.
+template <typename T>
+__device__ __forceinline__ void epi_store_blk(const Epi& e, int64_t blk, int off, int f, float v) {
+  if (f < e.n_split) {
+    if (e.out0_f32)
+      static_cast<float*>(e.out0)[blk * e.ld0 + (int64_t)f * HYF_TBLK + off] = v;
+    else
+      static_cast<T*>(e.out0)[blk * e.ld0 + tile_off<T>(f, off)] = from_f32<T>(v);
+  } else {
+    e.out1[blk * e.ld1 + (int64_t)(f - e.n_split) * HYF_TBLK + off] = v;
+  }
+}
+
+template <typename TO, int BM, int BN, int NW, int WPE, typename GRP>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 k_gemm_bf16_tile(RowSrc xs, int M, int K, const bf16* __restrict__ W, int Nout, Epi epi, int tm, int tn,
-                 int per_xcd) {
+                 int per_xcd, GRP rows) {
+  constexpr bool GR = std::is_same<GRP, RowGroups>::value;
   constexpr int G2_M = BM, G2_N = BN, G2_STAGE = g2_stage<BM, BN>();
   constexpr int BT = BN / 32;  // 16-feature tiles per wave
   static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0 && BN % 32 == 0 && (2 * BM / NW) % 16 == 0, "tile shape");
@@ -74,7 +100,13 @@ k_gemm_bf16_tile(RowSrc xs, int M, int K, const bf16* __restrict__ W, int Nout, 
 #pragma unroll
   for (int j = 0; j < CA; ++j) {
     const int m = min(m0 + 8 * (wave + NW * j) + lr, M - 1);
-    asrc[j] = static_cast<const char*>(row_ptr(xs, m, K, 2)) + 16 * lc;
+    if constexpr (GR) {
+      const int gi = group_of(rows, m);
+      const int loc = min(m - rows.m0[gi], rows.cnt[gi] - 1);  // padding rows repeat the group's last row
+      asrc[j] = static_cast<const char*>(xs.X1) + ((int64_t)rows.src0[gi] + loc) * K * 2 + 16 * lc;
+    } else {
+      asrc[j] = static_cast<const char*>(row_ptr(xs, m, K, 2)) + 16 * lc;
+    }
   }
 #pragma unroll
   for (int j = 0; j < CB; ++j) {
@@ -183,9 +215,19 @@ k_gemm_bf16_tile(RowSrc xs, int M, int K, const bf16* __restrict__ W, int Nout, 
       const int64_t m = (int64_t)m0 + m8;
       if (f >= Nout || m >= M) continue;
       const float* src = ct + fl * CP + m8;
-      if (m + 8 <= M) {
-        const int64_t blk = m / HYF_TBLK;
-        const int off = (int)(m % HYF_TBLK);
+      int64_t blk = m / HYF_TBLK;
+      int off = (int)(m % HYF_TBLK);
+      bool whole = m + 8 <= M;  // 8 tokens in one block, starting on a multiple of 8
+      int gi = 0, loc = 0;
+      if constexpr (GR) {
+        gi = group_of(rows, (int)m);
+        loc = (int)m - rows.m0[gi];
+        if (loc >= rows.cnt[gi]) continue;  // padding
+        blk = rows.blk0[gi] + loc / HYF_TBLK;
+        off = loc % HYF_TBLK;
+        whole = loc + 8 <= rows.cnt[gi] && off % 8 == 0;
+      }
+      if (whole) {
         if (f < epi.n_split && !epi.out0_f32) {
           bf16x8 v;
 #pragma unroll
@@ -197,8 +239,12 @@ k_gemm_bf16_tile(RowSrc xs, int M, int K, const bf16* __restrict__ W, int Nout, 
           *reinterpret_cast<f32x4*>(dst) = f32x4{src[0], src[1], src[2], src[3]};
           *reinterpret_cast<f32x4*>(dst + 4) = f32x4{src[4], src[5], src[6], src[7]};
         }
+      } else if constexpr (GR) {
+        // the group's last rows (m0[g] is a multiple of 8, so a run of 8 never spans two groups)
+        for (int e = 0; e < 8 && loc + e < rows.cnt[gi]; ++e)
+          epi_store_blk<TO>(epi, rows.blk0[gi] + (loc + e) / HYF_TBLK, (loc + e) % HYF_TBLK, f, src[e]);
       } else {
-        for (int e = 0; m + e < M; ++e) epi_store<TO>(epi, m + e, f, src[e]);
+        for (int e = 0; e < 8 && m + e < M; ++e) epi_store<TO>(epi, m + e, f, src[e]);
       }
     }
     return;
@@ -248,21 +294,32 @@ k_gemm_bf16_tile(RowSrc xs, int M, int K, const bf16* __restrict__ W, int Nout, 
   }
 }
 
-template <int BM, int BN, int NW, int WPE>
-static hipError_t launch_tile(RowSrc x, int M, int K, const bf16* W, int Nout, const Epi& epi, hipStream_t s) {
+template <int BM, int BN, int NW, int WPE, typename GRP>
+static hipError_t launch_tile(RowSrc x, int M, int K, const bf16* W, int Nout, const Epi& epi, const GRP& grp,
+                              hipStream_t s) {
   constexpr int lds = g2_lds<BM, BN>();
   static std::once_flag once;
   static hipError_t set_err = hipSuccess;
   std::call_once(once, [] {
-    set_err = hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm_bf16_tile<bf16, BM, BN, NW, WPE>),
+    set_err = hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm_bf16_tile<bf16, BM, BN, NW, WPE, GRP>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   });
   if (set_err != hipSuccess) return set_err;
   const int tm = (M + BM - 1) / BM, tn = (Nout + BN - 1) / BN;
   const int per_xcd = (tm * tn + 7) / 8;
-  hipLaunchKernelGGL((k_gemm_bf16_tile<bf16, BM, BN, NW, WPE>), dim3(8 * per_xcd), dim3(64 * NW), lds, s, x, M, K, W,
-                     Nout, epi, tm, tn, per_xcd);
+  hipLaunchKernelGGL((k_gemm_bf16_tile<bf16, BM, BN, NW, WPE, GRP>), dim3(8 * per_xcd), dim3(64 * NW), lds, s, x, M,
+                     K, W, Nout, epi, tm, tn, per_xcd, grp);
   return hipGetLastError();
+}
+
+template <typename GRP>
+static hipError_t launch_chosen(RowSrc x, int M, int K, const bf16* W, int Nout, const Epi& epi, const GRP& grp,
+                                hipStream_t s) {
+  auto tiles = [&](int bm, int bn) { return (int64_t)((M + bm - 1) / bm) * ((Nout + bn - 1) / bn); };
+  if (tiles(256, 128) >= 192) return launch_tile<256, 128, 8, 2>(x, M, K, W, Nout, epi, grp, s);
+  if (tiles(128, 128) >= 160) return launch_tile<128, 128, 8, 2>(x, M, K, W, Nout, epi, grp, s);
+  if (tiles(128, 64) >= 160) return launch_tile<128, 64, 8, 4>(x, M, K, W, Nout, epi, grp, s);
+  return launch_tile<64, 64, 4, 3>(x, M, K, W, Nout, epi, grp, s);
 }
 
 // Tile choice, from measured products (bf16, K 2560-5120): 256 x 128 tiles (one workgroup of 8
@@ -271,11 +328,15 @@ static hipError_t launch_tile(RowSrc x, int M, int K, const bf16* W, int Nout, c
 // more workgroups, else 64 x 64.  At 512 x 2560 x 2560 this takes 17 us against 37.5 us for the
 // 40 large tiles; at 800 x 2560 x 7968 the 252 large tiles stay fastest (48.7 us).
 hipError_t launch_gemm256(RowSrc x, int M, int K, const bf16* W, int Nout, const Epi& epi, hipStream_t s) {
-  auto tiles = [&](int bm, int bn) { return (int64_t)((M + bm - 1) / bm) * ((Nout + bn - 1) / bn); };
-  if (tiles(256, 128) >= 192) return launch_tile<256, 128, 8, 2>(x, M, K, W, Nout, epi, s);
-  if (tiles(128, 128) >= 160) return launch_tile<128, 128, 8, 2>(x, M, K, W, Nout, epi, s);
-  if (tiles(128, 64) >= 160) return launch_tile<128, 64, 8, 4>(x, M, K, W, Nout, epi, s);
-  return launch_tile<64, 64, 4, 3>(x, M, K, W, Nout, epi, s);
+  return launch_chosen(x, M, K, W, Nout, epi, NoGroups{}, s);
+}
+
+hipError_t launch_gemm_grouped(const bf16* X, const RowGroups& g, int K, const bf16* W, int Nout, const Epi& epi,
+                               hipStream_t s) {
+  const int M = g.m0[g.n];
+  if (M <= 0 || Nout <= 0) return hipSuccess;
+  if (K % 64 != 0 || g.n < 1) return hipErrorInvalidValue;
+  return launch_chosen(RowSrc{X, X, M}, M, K, W, Nout, epi, g, s);
 }
 
 }  // namespace hyf

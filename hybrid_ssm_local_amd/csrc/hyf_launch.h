@@ -77,8 +77,27 @@ hipError_t launch_linear_w4_epi(const RowSrc& x, int64_t M, int K, const uint8_t
                                 const Epi& epi, hipStream_t s);
 // bf16 values (code - 8) * scale of `rows` rows of 4-bit weights with K inputs each: out [rows][K].
 hipError_t launch_w4_dequant(const uint8_t* Wq, const float* S, int rows, int K, bf16* out, hipStream_t s);
-// The 256x128-tile bf16 GEMM (hyf_gemm.hip); K must be a multiple of 64.
+// The tiled bf16 GEMM (hyf_gemm.hip); K must be a multiple of 64.
 hipError_t launch_gemm256(RowSrc x, int M, int K, const bf16* W, int Nout, const Epi& epi, hipStream_t s);
+
+// Rows of a grouped product: one GEMM launch over the rows of several requests.  Product row m
+// belongs to the group g with m0[g] <= m < m0[g + 1]; its local index is l = m - m0[g], and only
+// l < cnt[g] is a row of the group (rows past cnt[g], up to the next group, are padding: computed
+// from the group's last row and never stored).  Row l reads input row src0[g] + l of X and, with a
+// time-blocked epilogue (epi.trans), writes token l of a sequence whose first block is blk0[g]
+// (in blocks of the epilogue's strides); a row-major epilogue writes product row m.  A time-blocked
+// product needs every m0[g] to be a multiple of 8.  Groups may be empty.
+struct RowGroups {
+  int32_t n;
+  int32_t m0[HYF_MAX_REQUESTS + 1];
+  int32_t cnt[HYF_MAX_REQUESTS];
+  int32_t src0[HYF_MAX_REQUESTS];
+  int32_t blk0[HYF_MAX_REQUESTS];
+};
+// out = X[rows of g] . W^T over all groups in one launch (bf16, K a multiple of 64, rows from X with
+// row stride K).
+hipError_t launch_gemm_grouped(const bf16* X, const RowGroups& g, int K, const bf16* W, int Nout, const Epi& epi,
+                               hipStream_t s);
 
 // Memory scan over segments (see hyf_scan.hip).  Inputs are time-blocked: token t of request i
 // sits in block blk0[i] + t / HYF_TBLK (block stride *blk); x, B and C are tiled inside a block
