@@ -559,7 +559,7 @@ def scan_loop(torch, hf, I, shape, T, copies, reps, seed):
         st[0] |= hf.hyf_ssd_scan(cfg, c["x"], c["B"], None, c["dt"], a_log, dt_bias, d_skip, c["H"], None, T, ws, wsb)
 
     scan(0)
-    us = time_calls(torch, scan, reps)
+    us = time_graph(torch, scan, copies * max(1, reps // copies))
     if st[0]:
         raise RuntimeError("scan loop failed")
     del cp, ws
@@ -614,9 +614,45 @@ def gemm_loop(torch, hf, shape, M, reps, copies=2):
         raise RuntimeError("gemm loop failed")
     flops = 2.0 * M * d * nout
     tf = flops / (us * 1e-6) / 1e12
-    return {"M": M, "K": d, "N": nout, "avg_us": us, "tflops": tf,
+    res = {"M": M, "K": d, "N": nout, "avg_us": us, "tflops": tf,
+           "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": tf / BF16_PEAK_TFLOPS}}
+    res["vendor_blas"] = vendor_gemm(torch, X, W, M, d, nout, reps)
+    return res
+
+
+def vendor_gemm(torch, X, W, M, K, N, reps):
+    """The same product through torch.matmul (ROCm's vendor BLAS), for context only."""
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    Wt = [w.t() for w in W]
+    torch.matmul(X, Wt[0], out=out)
+    us = time_calls(torch, lambda i: torch.matmul(X, Wt[i % len(Wt)], out=out), reps)
+    tf = 2.0 * M * K * N / (us * 1e-6) / 1e12
+    return {"what": "torch.matmul on the same operands (vendor BLAS), context only", "avg_us": us,
+            "tflops": tf, "frac": tf / BF16_PEAK_TFLOPS}
+
+
+def round_gemm_loop(torch, hf, shape, M, K, N, reps):
+    """A batched round's projection through the tiled GEMM (bf16 in, fp32 out as the round takes it),
+    W_COPIES weight copies rotated, and the vendor BLAS on the same shape for context."""
+    cfg = hf.make_config(shape)
+    X = torch.empty((M, K), dtype=torch.bfloat16, device="cuda").normal_()
+    W = [torch.empty((N, K), dtype=torch.bfloat16, device="cuda").normal_() for _ in range(W_COPIES)]
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    st = [0]
+
+    def proj(i):
+        st[0] |= hf.hyf_linear(cfg, X, M, K, W[i % W_COPIES], N, y, 1)
+
+    proj(0)
+    us = time_calls(torch, proj, reps)
+    if st[0]:
+        raise RuntimeError("round GEMM loop failed")
+    tf = 2.0 * M * K * N / (us * 1e-6) / 1e12
+    return {"M": M, "K": K, "N": N, "avg_us": us, "tflops": tf,
             "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": tf / BF16_PEAK_TFLOPS}}
+                         "frac": tf / BF16_PEAK_TFLOPS},
+            "vendor_blas": vendor_gemm(torch, X, W, M, K, N, reps)}
 
 
 def proj_loop(torch, hf, shape, M, K, N, reps):
@@ -677,7 +713,7 @@ PMC_KERNELS = {  # key -> (kernel name substring, source file, launch shape the 
     "round": ("k_round", "hybrid_ssm_local_amd/csrc/hyf_round.hip", "64 Qwen3-4B-shaped requests, full windows"),
     "scan_seg": ("k_ssd_seg", "hybrid_ssm_local_amd/csrc/hyf_scan.hip", "8192 tokens, Qwen3-4B shape"),
     "scan_combine": ("k_ssd_combine", "hybrid_ssm_local_amd/csrc/hyf_scan.hip", "8192 tokens, Qwen3-4B shape"),
-    "gemm": ("k_gemm_bf16_256", "hybrid_ssm_local_amd/csrc/hyf_gemm.hip", "8192 x 2560 x 2720"),
+    "gemm": ("k_gemm_bf16_tile", "hybrid_ssm_local_amd/csrc/hyf_gemm.hip", "8192 x 2560 x 2720"),
     "proj": ("k_proj_stream<8, 1>", "hybrid_ssm_local_amd/csrc/hyf_proj.hip", "12 rows x w_in (2560 x 7968)"),
     "w4": ("k_linear_w4", "hybrid_ssm_local_amd/csrc/hyf_w4.hip", "12 rows x 4-bit w_in"),
 }
@@ -805,6 +841,12 @@ def pmc_traffic(key):
     except (OSError, KeyError, ValueError):
         return None
     return k["traffic_bytes"] if k["source_sha256"] == source_digest(k["source"]) else None
+
+
+def scan_traffic():
+    """HBM bytes of one state-only scan call: the segment kernel plus the fold."""
+    seg, comb = pmc_traffic("scan_seg"), pmc_traffic("scan_combine")
+    return None if seg is None or comb is None else seg + comb
 
 
 def stats_summary(d):
@@ -1061,6 +1103,8 @@ def main():
     sy_us, sy_b = scan_y_loop(torch, hf, I, I.QWEN, 8192, max(4, reps // 6))
     g2 = gemm_loop(torch, hf, I.QWEN, 8192, max(4, reps // 6))
     g3 = gemm_loop(torch, hf, I.PHI4, 32768, max(4, reps // 12))
+    gr_in = round_gemm_loop(torch, hf, I.QWEN, 800, I.QWEN.d_model, I.QWEN.n_in, reps)
+    gr_out = round_gemm_loop(torch, hf, I.QWEN, 512, I.QWEN.dq, I.QWEN.d_model, reps)
     pj = proj_loop(torch, hf, I.QWEN, 12, I.QWEN.d_model, I.QWEN.n_in, reps)
     w4 = w4_projections(torch, hf, I.QWEN)
     g2["traffic"] = pmc_traffic("gemm")
@@ -1102,7 +1146,7 @@ def main():
         "phi4_two_layer": phi4_2l,
         "phi4_long131k": long5,
         "commit_scan": {"value": 8192 / (s_us * 1e-6), "unit": "committed feats/s", "T": 8192, "shape": "Qwen3-4B",
-                        "avg_us": s_us, "roofline": {**hbm(s_b, s_us), "traffic": pmc_traffic("scan_seg"),
+                        "avg_us": s_us, "roofline": {**hbm(s_b, s_us), "traffic": scan_traffic(),
                                                      "bytes_per_launch": s_b}},
         "commit_scan_phi4_131k": {"value": 131072 / (sl_us * 1e-6), "unit": "committed feats/s", "T": 131072,
                                   "shape": "Phi-4, chunk 256", "avg_us": sl_us,
@@ -1114,6 +1158,8 @@ def main():
                           "roofline": {**hbm(sy_b, sy_us), "traffic": None, "bytes_per_launch": sy_b}},
         "gemm_qwen_8192": g2,
         "gemm_phi4_32768": g3,
+        "gemm_batched_round_w_in": gr_in,
+        "gemm_batched_round_w_out": gr_out,
         "round_projection_w_in": pj,
         "w4a16_round_projections": w4,
         "cpu_baseline": cpu,
