@@ -880,13 +880,24 @@ def stats_summary(d):
             shapes[key] = []
             order.append(key)
         shapes[key].append(dur(r))
-    lines += ["", "By launch shape, in order of first launch (grid = threads in all dimensions; microseconds):", "",
+    lines += ["", "By launch shape, in order of first launch (grid = threads in all dimensions; microseconds).  "
+              "Launches of one shape whose durations differ by more than 3x (the same grid over different "
+              "work, e.g. the 8192- and 131072-token scans) are listed as separate duration classes:", "",
               "| kernel | grid | workgroup | calls | average us | min us |", "|---|---:|---:|---:|---:|---:|"]
     for key in order:
         k, g, w = key
-        v = shapes[key]
-        if "hyf" in k:
-            lines.append(f"| `{short(k)}` | {g} | {w} | {len(v)} | {sum(v) / len(v):.3f} | {min(v):.3f} |")
+        if "hyf" not in k:
+            continue
+        v = sorted(shapes[key])
+        classes, cur = [], [v[0]]
+        for x in v[1:]:
+            if x > 3.0 * cur[-1] and x > cur[-1] + 5.0:
+                classes.append(cur)
+                cur = []
+            cur.append(x)
+        classes.append(cur)
+        for c in classes:
+            lines.append(f"| `{short(k)}` | {g} | {w} | {len(c)} | {sum(c) / len(c):.3f} | {min(c):.3f} |")
     out = os.path.join(ROOT, "profiles", "bench_kernel_stats.md")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
