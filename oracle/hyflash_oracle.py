@@ -42,8 +42,17 @@ notes of the repository):
   byte (lower k in the low nibble); see quantize_w4.  A layer with 4-bit weights
   projects through the dequantized weights (layer_projection).
 
+* The full drafter block (explainer, "That is HyFlash": every layer of the
+  drafter holds the two branches; "Where it earns its keep": a drafter
+  backbone of a few milliseconds; the pages give no backbone beyond that):
+  the plainest pre-norm residual block around the two-branch layer,
+      h = x + Layer(RMSNorm(x) * g1),   out = h + MLP(RMSNorm(h) * g2),
+  RMSNorm(x) = x / sqrt(mean(x^2) + eps), MLP(z) = (silu(z Wg^T) * (z Wu^T)) Wd^T
+  (SwiGLU); the memory commits RMSNorm(feats) * g1, the layer's own input.
+
 Parity is pinned for every function below by tests that compare against
-closed forms, library routines or brute force (see tests/test_oracle_pins.py).
+closed forms, library routines or brute force (see tests/test_oracle_pins.py
+and tests/test_oracle_layer_pins.py).
 """
 
 from __future__ import annotations
@@ -470,3 +479,48 @@ def dequantize_w4(packed, scales, group: int = W4_GROUP):
 def linear_w4(X, packed, scales, group: int = W4_GROUP):
     """out[m][f] = sum_k X[m][k] * Wdq[f][k] with Wdq the dequantized weights, in float64."""
     return np.asarray(X, dtype=np.float64) @ dequantize_w4(packed, scales, group).T
+
+
+# ---------------------------------------------------------------------------------------------
+# The full drafter block: the two-branch layer between pre-norms and residuals, then a SwiGLU
+# MLP.  The pages fix the layer, not the backbone around it; this is the plainest pre-norm block.
+# bw holds norm1 [d], norm2 [d], w_gate [F][d], w_up [F][d], w_down [d][F] and eps.
+# ---------------------------------------------------------------------------------------------
+
+
+def rms_norm(x, g, eps: float):
+    """x / sqrt(mean over the row of x^2 + eps) * g, row by row."""
+    x = np.asarray(x, F64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * np.asarray(g, F64)
+
+
+def silu(z):
+    """z * sigmoid(z)."""
+    z = np.asarray(z, F64)
+    return z * sigmoid(z)
+
+
+def swiglu_mlp(z, w_gate, w_up, w_down):
+    """(silu(z Wg^T) * (z Wu^T)) Wd^T."""
+    z = np.asarray(z, F64)
+    a = silu(z @ np.asarray(w_gate, F64).T) * (z @ np.asarray(w_up, F64).T)
+    return a @ np.asarray(w_down, F64).T
+
+
+def block_commit(shape, wts: dict, bw: dict, st: dict, feats):
+    """The block's memory commit: the layer commits its own input, RMSNorm(feats) * g1."""
+    return commit(shape, wts, st, rms_norm(feats, bw["norm1"], bw["eps"]))
+
+
+def block_draft(shape, wts: dict, bw: dict, st: dict, block_in):
+    """One draft step of the full block; reads the state, never writes it.  Returns [nb][d]."""
+    x = np.asarray(block_in, F64)
+    h = x + draft(shape, wts, st, rms_norm(x, bw["norm1"], bw["eps"]))
+    return h + swiglu_mlp(rms_norm(h, bw["norm2"], bw["eps"]), bw["w_gate"], bw["w_up"], bw["w_down"])
+
+
+def block_round(shape, wts: dict, bw: dict, st: dict, commit_feats, block_in):
+    """One verification round of the full block: commit the accepted rows, then draft."""
+    st2, _ = block_commit(shape, wts, bw, st, commit_feats)
+    return st2, block_draft(shape, wts, bw, st2, block_in)

@@ -295,3 +295,105 @@ def test_last_w_memory_is_the_scan_of_the_last_w_committed_rows(total):
     lo = max(total - 6, 0)
     ref = _expected_draft(shape, parts, w_out, D, ref_st, hist[0][lo:], hist[1][lo:], xb)
     assert _rel(O.draft(shape, wts, st, xb), ref) < 1e-12
+
+
+# ---------------------------------------------------------------------------------------------
+# The full drafter block (pre-norm residual block around the layer, then a SwiGLU MLP).  The
+# expected values use torch's rms_norm and silu and the hand-built layer expectation above.
+
+
+def _t(a):
+    return torch.from_numpy(np.asarray(a, np.float64))
+
+
+def _rms(x, g, eps):
+    return torch.nn.functional.rms_norm(_t(x), (x.shape[-1],), weight=_t(g), eps=eps).numpy()
+
+
+def _swiglu(z, wg, wu, wd):
+    z = _t(z)
+    a = torch.nn.functional.silu(z @ _t(wg).T) * (z @ _t(wu).T)
+    return (a @ _t(wd).T).numpy()
+
+
+def test_rms_norm_and_silu_against_worked_values_and_torch():
+    # [3, 4]: mean square 12.5, so the row becomes [3, 4] / sqrt(12.5)
+    got = O.rms_norm(np.array([[3.0, 4.0]]), np.ones(2), 0.0)
+    assert np.allclose(got, [[3 / math.sqrt(12.5), 4 / math.sqrt(12.5)]], rtol=0, atol=1e-15)
+    rng = np.random.default_rng(3)
+    x, g = rng.standard_normal((5, 32)), rng.standard_normal(32)
+    assert _rel(O.rms_norm(x, g, 1e-6), _rms(x, g, 1e-6)) < 1e-13
+    # scale invariance with eps = 0, and unit root mean square with g = 1
+    assert _rel(O.rms_norm(7.5 * x, g, 0.0), O.rms_norm(x, g, 0.0)) < 1e-13
+    assert np.allclose(np.sqrt(np.mean(O.rms_norm(x, np.ones(32), 0.0) ** 2, axis=1)), 1.0, atol=1e-13)
+    z = rng.standard_normal(50) * 6
+    assert _rel(O.silu(z), torch.nn.functional.silu(_t(z)).numpy()) < 1e-13
+    assert O.silu(np.array([0.0]))[0] == 0.0
+
+
+def test_swiglu_mlp_against_torch():
+    rng = np.random.default_rng(4)
+    z = rng.standard_normal((6, 24))
+    wg, wu, wd = rng.standard_normal((40, 24)), rng.standard_normal((40, 24)), rng.standard_normal((24, 40))
+    assert _rel(O.swiglu_mlp(z, wg, wu, wd), _swiglu(z, wg, wu, wd)) < 1e-12
+    # the gate is the one under silu: swapping gate and up changes the result
+    assert _rel(O.swiglu_mlp(z, wu, wg, wd), _swiglu(z, wg, wu, wd)) > 1e-3
+
+
+def _block_case(seed, memory="mamba2"):
+    shape = I.LayerShape(d_model=24, n_heads=4, head_dim=8, d_state=6, window=6, dtype="f32", memory=memory)
+    rng = np.random.default_rng(seed)
+    parts, w_in, w_out = _parts(rng, shape)
+    d_skip = rng.standard_normal(shape.n_heads)
+    wts = dict(w_in=w_in, w_out=w_out, d_skip=d_skip, a_log=np.zeros(shape.n_heads),
+               dt_bias=np.zeros(shape.n_heads))
+    F = 40
+    bw = dict(norm1=1 + 0.3 * rng.standard_normal(24), norm2=1 + 0.3 * rng.standard_normal(24),
+              w_gate=rng.standard_normal((F, 24)) / 5, w_up=rng.standard_normal((F, 24)) / 5,
+              w_down=rng.standard_normal((24, F)) / 6, eps=1e-5)
+    st, wk, wv = _hand_state(rng, shape, 9)
+    return shape, parts, wts, bw, st, wk, wv, rng
+
+
+@pytest.mark.parametrize("memory", ["mamba2", "gdn"])
+def test_block_draft_wiring(memory):
+    # out = h + MLP(rms(h) g2) with h = x + Layer(rms(x) g1): the layer from the hand-built
+    # expectation, the norms and the MLP from torch.  A missing residual, the second norm taken of
+    # x instead of h, or the norms' weights swapped fails.
+    shape, parts, wts, bw, st, wk, wv, rng = _block_case(31, memory)
+    x = 3.0 * rng.standard_normal((8, 24))
+    h = x + _expected_draft(shape, parts, wts["w_out"], wts["d_skip"], st, wk, wv, _rms(x, bw["norm1"], bw["eps"]))
+    ref = h + _swiglu(_rms(h, bw["norm2"], bw["eps"]), bw["w_gate"], bw["w_up"], bw["w_down"])
+    got = O.block_draft(shape, wts, bw, st, x)
+    assert _rel(got, ref) < 1e-12
+    wrong = [h + _swiglu(_rms(x, bw["norm2"], bw["eps"]), bw["w_gate"], bw["w_up"], bw["w_down"]),
+             x + _swiglu(_rms(h, bw["norm2"], bw["eps"]), bw["w_gate"], bw["w_up"], bw["w_down"]),
+             h + _swiglu(_rms(h, bw["norm1"], bw["eps"]), bw["w_gate"], bw["w_up"], bw["w_down"])]
+    for w in wrong:
+        assert _rel(w, ref) > 1e-4
+
+
+def test_block_with_zero_output_weights_is_the_identity():
+    # With the layer's w_out and the MLP's w_down zero, both residual branches vanish.
+    shape, parts, wts, bw, st, _, _, rng = _block_case(32)
+    x = rng.standard_normal((8, 24))
+    out = O.block_draft(shape, dict(wts, w_out=np.zeros_like(wts["w_out"])), dict(bw, w_down=np.zeros((24, 40))), st, x)
+    assert np.array_equal(out, x)
+
+
+def test_block_commit_folds_the_normalized_features():
+    # The memory commits rms(feats) g1: with identity v / B / step rows of w_in (the closed-form
+    # layer above), H after the block's commit equals H after a plain commit of torch's normalized
+    # rows.
+    shape, w_in, rng = _identity_layer("mamba2")
+    d = shape.d_model
+    wts = dict(w_in=w_in, w_out=rng.standard_normal((d, shape.dq)), d_skip=np.zeros(2), a_log=np.zeros(2),
+               dt_bias=np.zeros(2))
+    bw = dict(norm1=1 + 0.2 * rng.standard_normal(d), norm2=np.ones(d), w_gate=np.zeros((8, d)),
+              w_up=np.zeros((8, d)), w_down=np.zeros((d, 8)), eps=1e-6)
+    feats = 2.0 * rng.standard_normal((7, d))
+    st_b, _ = O.block_commit(shape, wts, bw, O.new_state(shape), feats)
+    st_p, _ = O.commit(shape, wts, O.new_state(shape), _rms(feats, bw["norm1"], bw["eps"]))
+    assert _rel(st_b["H"], st_p["H"]) < 1e-12 and _rel(st_b["V"], st_p["V"]) < 1e-12
+    st_raw, _ = O.commit(shape, wts, O.new_state(shape), feats)
+    assert _rel(st_b["H"], st_raw["H"]) > 1e-3
