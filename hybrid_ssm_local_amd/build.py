@@ -17,7 +17,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libhyflash.so")
 
-SOURCES = ["hyf_abi.cpp", "hyf_proj.hip", "hyf_gemm.hip", "hyf_scan.hip", "hyf_gdn.hip", "hyf_round.hip", "hyf_w4.hip"]
+SOURCES = ["hyf_abi.cpp", "hyf_proj.hip", "hyf_gemm.hip", "hyf_scan.hip", "hyf_gdn.hip", "hyf_round.hip", "hyf_w4.hip",
+           "hyf_block.hip"]
 # Per-source extra flags.  The large GEMM keeps its MFMA accumulators in the unified VGPR file.
 EXTRA = {"hyf_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -818,4 +818,123 @@ int hyf_ssd_scan(const hyf_config* cfg, const void* x, const void* B, const void
   return hip_status(launch_ssd_state(cfg->dtype, s, sa, rt, max_segs, static_cast<hipStream_t>(stream)));
 }
 
+// ---- the full drafter block ----------------------------------------------------------------
+
+namespace {
+
+int check_block(const hyf_config* cfg, const hyf_block_weights* bw) {
+  if (!bw || !bw->norm1 || !bw->norm2 || !bw->w_gate_up || !bw->w_down) return HYF_EINVAL;
+  if (!aligned(bw->norm1, 16) || !aligned(bw->norm2, 16) || !aligned(bw->w_gate_up, 16) || !aligned(bw->w_down, 16))
+    return HYF_EINVAL;
+  if (bw->d_ff < 16 || bw->d_ff % 16 != 0 || !(bw->eps >= 0.f) || bw->eps > 1.f) return HYF_ESHAPE;
+  (void)cfg;
+  return HYF_OK;
+}
+
+// Block workspace: the layer's own workspace first, then the block's buffers for up to `rows`
+// committed rows and R blocks: normalized commit rows and block rows (storage dtype), the
+// layer's output (storage dtype), h (fp32), z (storage dtype), gate|up (fp32), the gated
+// product (storage dtype) and the down projection (fp32).
+struct WsBlock {
+  uint64_t inner, xc, xb, o, h, z, gu, a, y, end;
+};
+WsBlock ws_block(const hyf_config* cfg, const hyf_block_weights* bw, int32_t R, int64_t rows) {
+  WsBlock L{};
+  const uint64_t es = esize(cfg->dtype), d = cfg->d_model, F = bw->d_ff, nb = (uint64_t)HYF_BLOCK * R;
+  uint64_t o = align_up(hyf_workspace_bytes(cfg, R, rows, 0));
+  L.inner = 0;
+  L.xc = o; o += align_up((uint64_t)rows * d * es);
+  L.xb = o; o += align_up(nb * d * es);
+  L.o = o; o += align_up(nb * d * es);
+  L.h = o; o += align_up(nb * d * 4);
+  L.z = o; o += align_up(nb * d * es);
+  L.gu = o; o += align_up(nb * 2 * F * 4);
+  L.a = o; o += align_up(nb * F * es);
+  L.y = o; o += align_up(nb * d * 4);
+  L.end = o;
+  return L;
+}
+
+}  // namespace
+
+size_t hyf_block_workspace_bytes(const hyf_config* cfg, const hyf_block_weights* bw, int32_t max_requests,
+                                 int64_t max_rows) {
+  if (check_cfg(cfg) != HYF_OK || check_block(cfg, bw) != HYF_OK || max_requests < 1 ||
+      max_requests > HYF_MAX_REQUESTS || max_rows < 0)
+    return 0;
+  return (size_t)ws_block(cfg, bw, max_requests, max_rows).end;
+}
+
+int hyf_block_commit(const hyf_config* cfg, const hyf_weights* w, const hyf_block_weights* bw, void* state_pool,
+                     int32_t pool_slots, const int32_t* slots, int32_t n_req, const void* feats,
+                     const int64_t* cu_rows, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_cfg(cfg);
+  if (st != HYF_OK) return st;
+  if ((st = check_block(cfg, bw)) != HYF_OK) return st;
+  if (n_req < 0 || n_req > HYF_MAX_REQUESTS || !cu_rows) return HYF_EINVAL;
+  if (n_req == 0) return hyf_memory_commit(cfg, w, state_pool, pool_slots, slots, n_req, feats, cu_rows, nullptr, ws,
+                                           ws_bytes, stream);
+  const int64_t rows = cu_rows[n_req];
+  if (rows < 0) return HYF_EINVAL;
+  if (rows > 0 && (!feats || !aligned(feats, 16))) return HYF_EINVAL;
+  if (!ws || !aligned(ws, ALIGN) || ws_bytes < hyf_block_workspace_bytes(cfg, bw, n_req, rows)) return HYF_EWORKSPACE;
+  const WsBlock L = ws_block(cfg, bw, n_req, rows);
+  char* wsb = static_cast<char*>(ws);
+  // the layer's checks (weights, state, table) run before anything is launched
+  const Shape s = make_shape(cfg);
+  ReqTable rt;
+  if ((st = check_weights(cfg, w)) != HYF_OK) return st;
+  if (!state_pool || !aligned(state_pool, ALIGN) || pool_slots < 1) return HYF_EINVAL;
+  if ((st = build_table(s, pool_slots, slots, n_req, cu_rows, &rt)) != HYF_OK) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (launch_rmsnorm(cfg->dtype, feats, rows, cfg->d_model, bw->norm1, bw->eps, wsb + L.xc, hs) != hipSuccess)
+    return HYF_EHIP;
+  return hyf_memory_commit(cfg, w, state_pool, pool_slots, slots, n_req, rows > 0 ? wsb + L.xc : feats, cu_rows,
+                           nullptr, wsb + L.inner, hyf_workspace_bytes(cfg, n_req, rows, 0), stream);
+}
+
+int hyf_block_draft(const hyf_config* cfg, const hyf_weights* w, const hyf_block_weights* bw, void* state_pool,
+                    int32_t pool_slots, const int32_t* slots, int32_t n_req, const void* commit_feats,
+                    const int64_t* cu_commit, const void* block_in, void* block_out, void* ws, size_t ws_bytes,
+                    void* stream) {
+  ReqTable rt;
+  int64_t rows = 0;
+  int st = draft_check(cfg, w, state_pool, pool_slots, slots, n_req, commit_feats, cu_commit, block_in, block_out,
+                       &rt, &rows);
+  if (st != HYF_OK) return st;
+  if ((st = check_block(cfg, bw)) != HYF_OK) return st;
+  if (!ws || !aligned(ws, ALIGN) || ws_bytes < hyf_block_workspace_bytes(cfg, bw, n_req, rows)) return HYF_EWORKSPACE;
+  const int64_t nbytes_in = (int64_t)HYF_BLOCK * n_req * cfg->d_model * esize(cfg->dtype);
+  const char* bi = static_cast<const char*>(block_in);
+  const char* bo = static_cast<const char*>(block_out);
+  if (bi < bo + nbytes_in && bo < bi + nbytes_in) return HYF_EINVAL;  // block_out overlaps block_in
+  const WsBlock L = ws_block(cfg, bw, n_req, rows);
+  char* wsb = static_cast<char*>(ws);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const int dt = cfg->dtype, d = cfg->d_model, F = bw->d_ff;
+  const int64_t nb = (int64_t)HYF_BLOCK * n_req;
+  hipError_t he;
+  // the layer reads its own inputs: the normalized commit rows and block rows
+  if (rows > 0 && (he = launch_rmsnorm(dt, commit_feats, rows, d, bw->norm1, bw->eps, wsb + L.xc, hs)) != hipSuccess)
+    return HYF_EHIP;
+  if ((he = launch_rmsnorm(dt, block_in, nb, d, bw->norm1, bw->eps, wsb + L.xb, hs)) != hipSuccess) return HYF_EHIP;
+  if ((st = draft_run(cfg, w, state_pool, rt, rows, rows > 0 ? wsb + L.xc : nullptr, wsb + L.xb, wsb + L.o,
+                      wsb + L.inner, hs)) != HYF_OK)
+    return st;
+  // h = x + o, z = RMSNorm(h) norm2; gate|up = z w_gate_up^T; a = silu(gate) up; y = a w_down^T; out = h + y
+  float* h = reinterpret_cast<float*>(wsb + L.h);
+  float* gu = reinterpret_cast<float*>(wsb + L.gu);
+  float* y = reinterpret_cast<float*>(wsb + L.y);
+  if ((he = launch_resid_norm(dt, block_in, wsb + L.o, nb, d, bw->norm2, bw->eps, h, wsb + L.z, hs)) != hipSuccess)
+    return HYF_EHIP;
+  Epi e1{gu, 2 * (int64_t)F, 1, 2 * F, nullptr, 0, 0};
+  if ((he = launch_linear(dt, RowSrc{wsb + L.z, wsb + L.z, nb}, nb, d, bw->w_gate_up, 2 * F, e1, hs)) != hipSuccess)
+    return HYF_EHIP;
+  if ((he = launch_swiglu(dt, gu, nb, F, wsb + L.a, hs)) != hipSuccess) return HYF_EHIP;
+  Epi e2{y, (int64_t)d, 1, d, nullptr, 0, 0};
+  if ((he = launch_linear(dt, RowSrc{wsb + L.a, wsb + L.a, nb}, nb, F, bw->w_down, d, e2, hs)) != hipSuccess)
+    return HYF_EHIP;
+  return hip_status(launch_add_out(dt, h, y, nb * d, block_out, hs));
+}
+
 }  // extern "C"

@@ -80,6 +80,18 @@ hipError_t launch_w4_dequant(const uint8_t* Wq, const float* S, int rows, int K,
 // The tiled bf16 GEMM (hyf_gemm.hip); K must be a multiple of 64.
 hipError_t launch_gemm256(RowSrc x, int M, int K, const bf16* W, int Nout, const Epi& epi, hipStream_t s);
 
+// The full drafter block's row kernels (hyf_block.hip); rows of d (or F) elements, contiguous.
+// y = RMSNorm(x) * g (storage dtype in and out).
+hipError_t launch_rmsnorm(int dtype, const void* x, int64_t rows, int d, const float* g, float eps, void* y,
+                          hipStream_t s);
+// h = x + o (fp32) and z = RMSNorm(h) * g (storage dtype).
+hipError_t launch_resid_norm(int dtype, const void* x, const void* o, int64_t rows, int d, const float* g, float eps,
+                             float* h, void* z, hipStream_t s);
+// a[m][j] = silu(gu[m][j]) * gu[m][F + j] (gu fp32 [rows][2F], a storage dtype [rows][F]).
+hipError_t launch_swiglu(int dtype, const float* gu, int64_t rows, int F, void* a, hipStream_t s);
+// out = h + y over n elements (fp32 in, storage dtype out).
+hipError_t launch_add_out(int dtype, const float* h, const float* y, int64_t n, void* out, hipStream_t s);
+
 // Rows of a grouped product: one GEMM launch over the rows of several requests.  Product row m
 // belongs to the group g with m0[g] <= m < m0[g + 1]; its local index is l = m - m0[g], and only
 // l < cnt[g] is a row of the group (rows past cnt[g], up to the next group, are padding: computed

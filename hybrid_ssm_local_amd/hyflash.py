@@ -44,6 +44,11 @@ class HyfStateLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in ("count_off", "h_off", "k_off", "v_off", "total", "b_off", "dt_off")]
 
 
+class HyfBlockWeights(ctypes.Structure):
+    _fields_ = [("norm1", ctypes.c_void_p), ("norm2", ctypes.c_void_p), ("w_gate_up", ctypes.c_void_p),
+                ("w_down", ctypes.c_void_p), ("d_ff", ctypes.c_int32), ("eps", ctypes.c_float)]
+
+
 class HyfError(RuntimeError):
     def __init__(self, status: int, what: str = ""):
         super().__init__(f"{what}: status {status} ({status_str(status)})")
@@ -73,6 +78,11 @@ _SIGS = {
     "hyf_linear_w4": (ctypes.c_int, [_P(HyfConfig), _vp, _i64, _i32, _vp, _vp, _i32, _vp, _i32, _vp]),
     "hyf_ssd_scan": (ctypes.c_int, [_P(HyfConfig), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _sz,
                                     _vp]),
+    "hyf_block_workspace_bytes": (_sz, [_P(HyfConfig), _P(HyfBlockWeights), _i32, _i64]),
+    "hyf_block_commit": (ctypes.c_int, [_P(HyfConfig), _P(HyfWeights), _P(HyfBlockWeights), _vp, _i32, _vp, _i32,
+                                        _vp, _vp, _vp, _sz, _vp]),
+    "hyf_block_draft": (ctypes.c_int, [_P(HyfConfig), _P(HyfWeights), _P(HyfBlockWeights), _vp, _i32, _vp, _i32,
+                                       _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
 }
 
 
@@ -207,6 +217,27 @@ def hyf_draft_block_noalloc(cfg, w: HyfWeights, pool, pool_slots, slots, n_req, 
     _c, cp = _host_i64(cu_commit)
     return lib().hyf_draft_block_noalloc(ctypes.byref(cfg), ctypes.byref(w), _ptr(pool), pool_slots, sp, n_req,
                                          _ptr(commit_feats), cp, _ptr(block_in), _ptr(block_out), _stream(stream))
+
+
+def hyf_block_workspace_bytes(cfg, bw: HyfBlockWeights, max_requests: int, max_rows: int) -> int:
+    return lib().hyf_block_workspace_bytes(ctypes.byref(cfg), ctypes.byref(bw), max_requests, max_rows)
+
+
+def hyf_block_commit(cfg, w: HyfWeights, bw: HyfBlockWeights, pool, pool_slots, slots, n_req, feats, cu_rows, ws,
+                     ws_bytes, stream=None) -> int:
+    _s, sp = _host_i32(slots)
+    _c, cp = _host_i64(cu_rows)
+    return lib().hyf_block_commit(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(bw), _ptr(pool), pool_slots, sp,
+                                  n_req, _ptr(feats), cp, _ptr(ws), ws_bytes, _stream(stream))
+
+
+def hyf_block_draft(cfg, w: HyfWeights, bw: HyfBlockWeights, pool, pool_slots, slots, n_req, commit_feats,
+                    cu_commit, block_in, block_out, ws, ws_bytes, stream=None) -> int:
+    _s, sp = _host_i32(slots)
+    _c, cp = _host_i64(cu_commit)
+    return lib().hyf_block_draft(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(bw), _ptr(pool), pool_slots, sp,
+                                 n_req, _ptr(commit_feats), cp, _ptr(block_in), _ptr(block_out), _ptr(ws), ws_bytes,
+                                 _stream(stream))
 
 
 def hyf_linear(cfg, X, M, K, W, Nout, out, out_f32, stream=None) -> int:
@@ -344,3 +375,44 @@ class DrafterLayer:
             out["Bring"] = blob[L.b_off: L.b_off + W * sh.gn * es].view(torch_dtype(sh)).view(W, sh.gn)
             out["DTring"] = blob[L.dt_off: L.dt_off + nh * W * 4].view(torch.float32).view(nh, W)
         return out
+
+
+class DrafterBlock:
+    """The full drafter block around one layer: the layer's weights and state (a DrafterLayer)
+    plus the block's norms and MLP; forwards to hyf_block_commit / hyf_block_draft."""
+
+    def __init__(self, shape: LayerShape, weights: dict, block_weights: dict, pool_slots: int = 1,
+                 max_requests: int = 1, max_rows: int = 8, device: str = "cuda"):
+        import torch
+
+        self.layer = DrafterLayer(shape, weights, pool_slots, max_requests, max_rows, device=device)
+        self.shape = shape
+        bwt = block_weights
+        self.norm1 = torch.from_numpy(np.asarray(bwt["norm1"], np.float32)).to(device)
+        self.norm2 = torch.from_numpy(np.asarray(bwt["norm2"], np.float32)).to(device)
+        self.w_gate_up = to_device(np.concatenate([bwt["w_gate"], bwt["w_up"]], axis=0), shape, device)
+        self.w_down = to_device(bwt["w_down"], shape, device)
+        self.bw = HyfBlockWeights(self.norm1.data_ptr(), self.norm2.data_ptr(), self.w_gate_up.data_ptr(),
+                                  self.w_down.data_ptr(), int(np.asarray(bwt["w_gate"]).shape[0]), float(bwt["eps"]))
+        self.ws_bytes = hyf_block_workspace_bytes(self.layer.cfg, self.bw, max_requests, max_rows)
+        if self.ws_bytes == 0:
+            raise HyfError(1, "hyf_block_workspace_bytes")
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+
+    def reset(self, slots=None, n_req=None, stream=None):
+        self.layer.reset(slots, n_req, stream)
+
+    def commit(self, feats, cu_rows, slots=None, stream=None):
+        n_req = len(cu_rows) - 1
+        L = self.layer
+        check(hyf_block_commit(L.cfg, L.w, self.bw, L.pool, L.pool_slots, slots, n_req, feats, cu_rows, self.ws,
+                               self.ws_bytes, stream), "hyf_block_commit")
+
+    def draft(self, block_in, block_out, commit_feats=None, cu_commit=None, slots=None, stream=None):
+        n_req = block_in.shape[0] // HYF_BLOCK if block_in.dim() == 2 else block_in.shape[0]
+        L = self.layer
+        check(hyf_block_draft(L.cfg, L.w, self.bw, L.pool, L.pool_slots, slots, n_req, commit_feats, cu_commit,
+                              block_in, block_out, self.ws, self.ws_bytes, stream), "hyf_block_draft")
+
+    def state(self, slot: int = 0) -> dict:
+        return self.layer.state(slot)

@@ -141,6 +141,20 @@ def make_weights(shape: LayerShape, rng, d_random: bool = False) -> dict:
     return dict(w_in=w_in, w_out=w_out, a_log=a_log, dt_bias=dt_bias, d_skip=d_skip)
 
 
+def make_block_weights(shape: LayerShape, rng, d_ff: int | None = None) -> dict:
+    """The full block's own weights: the first RMSNorm's gains (1 + 0.1 N(0, 1)) / sqrt(d_model), so
+    the layer sees rows of root mean square 1 / sqrt(d_model) like the layer's own synthetic
+    features, the second's 1 + 0.1 N(0, 1) (float32), and the SwiGLU MLP's gate and up
+    [d_ff][d_model] and down [d_model][d_ff] Xavier-normal in the storage dtype.  d_ff defaults to
+    3 d_model."""
+    d = shape.d_model
+    F = 3 * d if d_ff is None else d_ff
+    return dict(norm1=((1 + 0.1 * rng.standard_normal(d)) / math.sqrt(d)).astype(np.float32),
+                norm2=(1 + 0.1 * rng.standard_normal(d)).astype(np.float32),
+                w_gate=to_storage(xavier(rng, F, d), shape.dtype), w_up=to_storage(xavier(rng, F, d), shape.dtype),
+                w_down=to_storage(xavier(rng, d, F), shape.dtype), eps=1e-6)
+
+
 def make_rows(rng, n: int, d: int, scale: float, dtype: str) -> np.ndarray:
     return to_storage(rng.standard_normal((n, d), dtype=np.float32) * np.float32(scale), dtype)
 

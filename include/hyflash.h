@@ -246,6 +246,49 @@ int hyf_linear(const hyf_config* cfg, const void* X, int64_t M, int32_t K, const
 int hyf_linear_w4(const hyf_config* cfg, const void* X, int64_t M, int32_t K, const void* Wq,
                   const float* scales, int32_t Nout, void* out, int32_t out_f32, void* stream);
 
+/* The full drafter block around the two-branch layer.  The pages fix the layer (explainer, "That
+ * is HyFlash": every drafter layer holds a local-attention branch and the recurrent memory) and a
+ * drafter backbone of a few milliseconds ("Where it earns its keep"), not the blocks around it;
+ * the plainest pre-norm residual block is:
+ *   h   = x + Layer(RMSNorm(x) * norm1)
+ *   out = h + (silu(z . w_gate^T) * (z . w_up^T)) . w_down^T,   z = RMSNorm(h) * norm2,
+ *   RMSNorm(x) = x / sqrt(mean over d_model of x^2 + eps),
+ * and the memory commits the layer's own input, RMSNorm(feats) * norm1.  Layer is the
+ * hyf_draft_block / hyf_memory_commit layer of hyf_weights.
+ * norm1, norm2 [d_model] fp32; w_gate_up [2 d_ff][d_model] storage dtype, the gate rows first
+ * (rows 0 .. d_ff - 1), then the up rows; w_down [d_model][d_ff] storage dtype; all 16-byte
+ * aligned device pointers owned by the caller.  d_ff >= 16, a multiple of 16 (HYF_ESHAPE
+ * otherwise); eps >= 0.  4-bit layer weights are allowed; the block's own weights are dense. */
+typedef struct {
+  const float* norm1;
+  const float* norm2;
+  const void* w_gate_up;
+  const void* w_down;
+  int32_t d_ff;
+  float eps;
+} hyf_block_weights;
+
+/* Host only.  Workspace bytes hyf_block_commit and hyf_block_draft need for up to max_requests
+ * requests and max_rows committed rows per call (0 for invalid arguments). */
+size_t hyf_block_workspace_bytes(const hyf_config* cfg, const hyf_block_weights* bw, int32_t max_requests,
+                                 int64_t max_rows);
+
+/* The block's commit: hyf_memory_commit of RMSNorm(feats) * norm1 (arguments as there, without
+ * per-token outputs).  ws: at least hyf_block_workspace_bytes(cfg, bw, n_req, cu_rows[n_req]). */
+int hyf_block_commit(const hyf_config* cfg, const hyf_weights* w, const hyf_block_weights* bw,
+                     void* state_pool, int32_t pool_slots, const int32_t* slots, int32_t n_req,
+                     const void* feats, const int64_t* cu_rows, void* ws, size_t ws_bytes, void* stream);
+
+/* One draft step of the block: with commit_feats not NULL, exactly hyf_block_commit of those rows
+ * first (at most `block` rows per request, as hyf_draft_block); then block_out
+ * [n_req][block][d_model] (storage dtype) = out above for block_in [n_req][block][d_model].
+ * Never writes the state when commit_feats is NULL.  block_out must not overlap block_in.
+ * ws: at least hyf_block_workspace_bytes(cfg, bw, n_req, cu_commit[n_req]) bytes. */
+int hyf_block_draft(const hyf_config* cfg, const hyf_weights* w, const hyf_block_weights* bw,
+                    void* state_pool, int32_t pool_slots, const int32_t* slots, int32_t n_req,
+                    const void* commit_feats, const int64_t* cu_commit, const void* block_in,
+                    void* block_out, void* ws, size_t ws_bytes, void* stream);
+
 /* Host only.  Workspace bytes hyf_ssd_scan needs for T tokens, with (with_y != 0) or without
  * per-token outputs. */
 size_t hyf_ssd_scan_workspace_bytes(const hyf_config* cfg, int64_t T, int32_t with_y);

@@ -30,6 +30,7 @@ def test_struct_sizes_match_the_header():
     assert ctypes.sizeof(hf.HyfConfig) == 48
     assert ctypes.sizeof(hf.HyfWeights) == 72  # nine pointers
     assert ctypes.sizeof(hf.HyfStateLayout) == 56
+    assert ctypes.sizeof(hf.HyfBlockWeights) == 40  # four pointers, d_ff, eps
 
 
 @pytest.mark.parametrize("shape", [I.TINY, I.QWEN, I.PHI4, I.PHI4_LONG])
@@ -261,3 +262,35 @@ def test_last_w_memory_layout_keeps_b_and_step_rings():
     w = hf.HyfWeights(fake, fake, fake, fake, fake)
     assert hf.hyf_memory_commit(cfg, w, fake, 1, None, 1, fake, [0, 4], fake, fake, 1 << 30, 0) == \
         hf.HYF_EUNSUPPORTED
+
+
+def test_full_block_checks_before_device_work():
+    # The block's own weights are checked (pointers, alignment, d_ff a multiple of 16 and at least
+    # 16, eps in [0, 1]), the workspace covers the layer's and the block's buffers, block_out may
+    # not overlap block_in; every rejection comes before any HIP call.
+    cfg = hf.make_config(I.QWEN)
+    fake = 1 << 20
+    w = hf.HyfWeights(fake, fake, fake, fake, fake)
+    bw = hf.HyfBlockWeights(fake, fake, fake, fake, 7680, 1e-6)
+    lay = hf.hyf_workspace_bytes(cfg, 1, 8)
+    blk = hf.hyf_block_workspace_bytes(cfg, bw, 1, 8)
+    # layer workspace + 8 commit rows and 8 block rows of x, the layer's output, h, z, gate|up, a, y
+    assert blk >= lay + (8 + 8 + 8) * 2560 * 2 + 8 * 2560 * 4 * 2 + 8 * 2560 * 2 + 8 * 2 * 7680 * 4 + 8 * 7680 * 2
+    assert hf.hyf_block_workspace_bytes(cfg, bw, 2, 8) > blk
+    for bad in (hf.HyfBlockWeights(fake, fake, fake, fake, 7688, 1e-6), hf.HyfBlockWeights(fake, fake, fake, fake, 0, 1e-6),
+                hf.HyfBlockWeights(fake, fake, fake, fake, 7680, -1.0)):
+        assert hf.hyf_block_workspace_bytes(cfg, bad, 1, 8) == 0
+        assert hf.hyf_block_draft(cfg, w, bad, fake, 1, None, 1, None, None, fake, 2 * fake, fake, blk, 0) == hf.HYF_ESHAPE
+    nul = hf.HyfBlockWeights(None, fake, fake, fake, 7680, 1e-6)
+    mis = hf.HyfBlockWeights(fake, fake, fake + 4, fake, 7680, 1e-6)
+    for bad in (nul, mis):
+        assert hf.hyf_block_draft(cfg, w, bad, fake, 1, None, 1, None, None, fake, 2 * fake, fake, blk, 0) == hf.HYF_EINVAL
+        assert hf.hyf_block_commit(cfg, w, bad, fake, 1, None, 1, fake, [0, 8], fake, blk, 0) == hf.HYF_EINVAL
+    # block_out overlapping block_in, a short workspace, too many commit rows
+    assert hf.hyf_block_draft(cfg, w, bw, fake, 1, None, 1, None, None, fake, fake + 4096, fake, blk, 0) == hf.HYF_EINVAL
+    blk0 = hf.hyf_block_workspace_bytes(cfg, bw, 1, 0)  # a draft without commit rows
+    assert hf.hyf_block_draft(cfg, w, bw, fake, 1, None, 1, None, None, fake, 2 * fake, fake, blk0 - 256, 0) == \
+        hf.HYF_EWORKSPACE
+    assert hf.hyf_block_draft(cfg, w, bw, fake, 1, None, 1, fake, [0, 9], fake, 2 * fake, fake, blk, 0) == \
+        hf.HYF_ECAPACITY
+    assert hf.hyf_block_commit(cfg, w, bw, fake, 1, None, 1, fake, [0, 8], fake, blk - 256, 0) == hf.HYF_EWORKSPACE
