@@ -383,6 +383,19 @@ class EpisodesB1:
         if st:
             raise RuntimeError(f"libhyflash call failed (status bits {st})")
 
+    def round_graph(self, torch, nr=64):
+        """Microseconds per round of `nr` rounds captured in one HIP graph (interleaved states)."""
+        st = [0]
+        stream = torch.cuda.Stream()
+
+        def rounds(i):
+            st[0] |= self.round(i % EPISODES, (i // EPISODES) % self.rounds, ctypes.c_void_p(stream.cuda_stream))
+
+        t = time_graph(torch, rounds, nr, stream=stream)
+        if st[0]:
+            raise RuntimeError("round graph failed")
+        return t
+
     def round_kernel(self, torch, hf, nr=64):
         """As Batched.round_kernel, for batch-1 rounds over the interleaved states."""
         sh, d = self.shape, self.shape.d_model
@@ -415,6 +428,56 @@ class EpisodesB1:
             raise RuntimeError(f"round kernel timing failed (status bits {st[0]})")
         rows = sum(M) / len(M) - 8
         return t_round, t_proj, rows
+
+
+class EpisodesBlockB1(EpisodesB1):
+    """The batch-1 episode of the full drafter block around the Qwen3-4B-shaped layer (pre-norms,
+    residuals, SwiGLU MLP of width 3 d_model): prefix commit through hyf_block_commit, rounds through
+    hyf_block_draft; layer and MLP weights rotated over W_COPIES copies."""
+
+    def __init__(self, torch, hf, I):
+        import numpy as np
+
+        super().__init__(torch, hf, I)
+        sh = self.shape
+        bw = I.make_block_weights(sh, I.rng_streams(77)[0])
+        self.F = bw["w_gate"].shape[0]
+        self.norms = [torch.from_numpy(bw[k]).cuda() for k in ("norm1", "norm2")]
+        gu = np.concatenate([bw["w_gate"], bw["w_up"]], axis=0)
+        self.mlp = [(hf.to_device(gu, sh), hf.to_device(bw["w_down"], sh)) for _ in range(W_COPIES)]
+        self.bws = [hf.HyfBlockWeights(self.norms[0].data_ptr(), self.norms[1].data_ptr(), g.data_ptr(),
+                                       dn.data_ptr(), self.F, float(bw["eps"])) for g, dn in self.mlp]
+        self.bw_ref = [ctypes.byref(b) for b in self.bws]
+        self.ws_bytes = hf.hyf_block_workspace_bytes(self.cfg, self.bws[0], 1, self.T)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
+        self.ws_p = ctypes.c_void_p(self.ws.data_ptr())
+
+    def round(self, e, i, s):
+        c = self.c
+        self.k = (self.k + 1) % W_COPIES
+        return c.L.hyf_block_draft(c.cfg_ref, c.w_ref[self.k], self.bw_ref[self.k], self.pool_p, EPISODES,
+                                   self.slots[e], 1, self.c_ptr[i], self.cu[i], self.b_ptr[i], self.out_p, self.ws_p,
+                                   self.ws_bytes, s)
+
+    def step(self, stream, ev=None):
+        L, c = self.c.L, self.c
+        s = ctypes.c_void_p(stream)
+        if ev:
+            ev[0].record()
+        st = L.hyf_state_reset(c.cfg_ref, self.pool_p, EPISODES, None, EPISODES, s)
+        for e in range(EPISODES):
+            self.k = (self.k + 1) % W_COPIES
+            st |= L.hyf_block_commit(c.cfg_ref, c.w_ref[self.k], self.bw_ref[self.k], self.pool_p, EPISODES,
+                                     self.slots[e], 1, self.pre_p, self.cu_pre, self.ws_p, self.ws_bytes, s)
+        if ev:
+            ev[1].record()
+        for i in range(self.rounds):
+            for e in range(EPISODES):
+                st |= self.round(e, i, s)
+        if ev:
+            ev[2].record()
+        if st:
+            raise RuntimeError(f"libhyflash call failed (status bits {st})")
 
 
 class TwoLayerPhi4:
@@ -1071,6 +1134,23 @@ def main():
     }
     del epw
     torch.cuda.empty_cache()
+    log("batch-1 episodes, full drafter block")
+    epb = EpisodesBlockB1(torch, hf, I)
+    bb = run_steps(torch, epb.step, sub_steps, 1)
+    bb_round = epb.round_graph(torch)
+    sh_b = epb.shape
+    mlp_b = 3 * epb.F * sh_b.d_model * 2
+    bb_rb = b1_rb + mlp_b  # the layer's round bytes plus the MLP's weights (the norms' rows are a few KB)
+    qwen_b1_block = {
+        "workload": "the full drafter block around the Qwen3-4B-shaped layer (pre-norm, layer, residual, pre-norm, "
+                    f"SwiGLU MLP of width {epb.F}, residual), batch 1, episodes as qwen3_4b_batch1",
+        "value": b1_blocks / (bb["step_ms"] * 1e-3), "unit": "draft blocks/s per block (batch 1)",
+        "ms_per_step": bb["step_ms"], "prefill_commit_us": 1e3 * bb["prefill_ms"] / EPISODES,
+        "round_us": 1e3 * bb["rounds_ms"] / b1_blocks, "round_graph_us": bb_round,
+        "round": {"bytes_per_round": bb_rb, **hbm(bb_rb, bb_round)},
+    }
+    del epb
+    torch.cuda.empty_cache()
 
     # ---- Phi-4-shaped two-layer drafter
     log("phi-4 two-layer")
@@ -1154,6 +1234,7 @@ def main():
         "qwen3_4b_batch1": qwen_b1,
         "qwen3_4b_batch1_w4": qwen_b1_w4,
         "qwen3_4b_batch1_lastw": qwen_b1_lastw,
+        "qwen3_4b_full_block_batch1": qwen_b1_block,
         "phi4_two_layer": phi4_2l,
         "phi4_long131k": long5,
         "commit_scan": {"value": 8192 / (s_us * 1e-6), "unit": "committed feats/s", "T": 8192, "shape": "Qwen3-4B",
