@@ -360,7 +360,7 @@ int lastw_rescan(const Shape& s, int dt, const hyf_weights* w, char* pool, const
 // then one round kernel that folds the rows into H (one read-modify-write), appends them to the
 // ring and advances count (the last-W memory: appends them with their B and steps, then rescans).
 int commit_round(const hyf_config* cfg, const hyf_weights* w, char* pool, const ReqTable& rt, int64_t rows,
-                 const void* feats, char* wsb, hipStream_t hs) {
+                 const void* feats, char* wsb, hipStream_t hs, const int32_t* dev_rows) {
   const Shape s = make_shape(cfg);
   const int dt = cfg->dtype, n_req = rt.n_req;
   const WsDraft L = ws_draft(s, dt, n_req, rows);
@@ -382,6 +382,7 @@ int commit_round(const hyf_config* cfg, const hyf_weights* w, char* pool, const 
   ra.counters = counters;
   ra.do_commit = 1;
   ra.do_draft = 0;
+  ra.dev_rows = dev_rows;
   round_layout(s, n_req, esize(dt), &ra);
   ra.n_split = 0;
   if ((he = launch_round(dt, s, ra, rt, hs)) != hipSuccess) return HYF_EHIP;
@@ -416,16 +417,18 @@ int draft_check(const hyf_config* cfg, const hyf_weights* w, void* state_pool, i
 // The launches of a draft call, after every check has passed: ws holds at least
 // hyf_workspace_bytes(cfg, n_req, rows, 0) bytes, 256-byte aligned.
 int draft_run(const hyf_config* cfg, const hyf_weights* w, void* state_pool, const ReqTable& rt, int64_t rows,
-              const void* commit_feats, const void* block_in, void* block_out, char* wsb, hipStream_t hs) {
+              const void* commit_feats, const void* block_in, void* block_out, char* wsb, hipStream_t hs,
+              const int32_t* dev_rows) {
   const Shape s = make_shape(cfg);
   const int n_req = rt.n_req;
   char* pool = static_cast<char*>(state_pool);
   const int dt = cfg->dtype;
   if (s.lastw && rows > 0) {
     // the window's scan has to follow the append: commit, then draft without commit rows
-    const int st = commit_round(cfg, w, pool, rt, rows, commit_feats, wsb, hs);
+    const int st = commit_round(cfg, w, pool, rt, rows, commit_feats, wsb, hs, dev_rows);
     if (st != HYF_OK) return st;
     rows = 0;
+    dev_rows = nullptr;
   }
   const WsDraft L = ws_draft(s, dt, n_req, rows);
   float* proj = reinterpret_cast<float*>(wsb + L.proj);
@@ -454,6 +457,7 @@ int draft_run(const hyf_config* cfg, const hyf_weights* w, void* state_pool, con
   ra.counters = counters;
   ra.do_commit = rows > 0;
   ra.do_draft = 1;
+  ra.dev_rows = dev_rows;
   round_layout(s, n_req, esize(dt), &ra);
   if ((he = launch_round(dt, s, ra, rt, hs)) != hipSuccess) return HYF_EHIP;
   // 3. output projection
@@ -590,7 +594,7 @@ int hyf_memory_commit(const hyf_config* cfg, const hyf_weights* w, void* state_p
   // a gated delta-rule prefix takes the chunked kernels when they fit the shape, else the
   // token-by-token one; refused only when neither fits
   if (s.gdn && max_n > 16 && !gdn_supported(s) && !gdn_chunked_supported(s, es)) return HYF_EUNSUPPORTED;
-  if (max_n <= 16 && !y_opt) return commit_round(cfg, w, pool, rt, rows, feats, wsb, hs);
+  if (max_n <= 16 && !y_opt) return commit_round(cfg, w, pool, rt, rows, feats, wsb, hs, nullptr);
 
   // Prefill-sized commit (or any commit with per-token outputs): projection GEMMs -> ring append ->
   // scan -> count.  The GEMM epilogues write the scan's operands time-blocked (each request's
@@ -727,7 +731,7 @@ int hyf_draft_block(const hyf_config* cfg, const hyf_weights* w, void* state_poo
   if (st != HYF_OK) return st;
   if (!ws || !aligned(ws, ALIGN) || ws_bytes < hyf_workspace_bytes(cfg, n_req, rows, 0)) return HYF_EWORKSPACE;
   return draft_run(cfg, w, state_pool, rt, rows, commit_feats, block_in, block_out, static_cast<char*>(ws),
-                   static_cast<hipStream_t>(stream));
+                   static_cast<hipStream_t>(stream), nullptr);
 }
 
 int hyf_draft_block_noalloc(const hyf_config* cfg, const hyf_weights* w, void* state_pool, int32_t pool_slots,
@@ -744,7 +748,27 @@ int hyf_draft_block_noalloc(const hyf_config* cfg, const hyf_weights* w, void* s
   char* ws = nullptr;
   if ((st = noalloc_scratch(&ws)) != HYF_OK) return st;
   return draft_run(cfg, w, state_pool, rt, rows, commit_feats, block_in, block_out, ws,
-                   static_cast<hipStream_t>(stream));
+                   static_cast<hipStream_t>(stream), nullptr);
+}
+
+int hyf_draft_block_dev(const hyf_config* cfg, const hyf_weights* w, void* state_pool, int32_t pool_slots,
+                        const int32_t* slots, int32_t n_req, const void* commit_feats, const int32_t* commit_rows,
+                        const void* block_in, void* block_out, void* ws, size_t ws_bytes, void* stream) {
+  // the host checks of hyf_draft_block with a table of HYF_BLOCK padded commit rows per request
+  // (their real counts come from commit_rows on the device)
+  if (n_req < 0 || n_req > HYF_MAX_REQUESTS) return HYF_EINVAL;
+  if ((commit_feats == nullptr) != (commit_rows == nullptr)) return HYF_EINVAL;
+  if (commit_rows && !aligned(commit_rows, 4)) return HYF_EINVAL;
+  int64_t cu[HYF_MAX_REQUESTS + 1];
+  for (int i = 0; i <= n_req; ++i) cu[i] = commit_feats ? (int64_t)HYF_BLOCK * i : 0;
+  ReqTable rt;
+  int64_t rows = 0;
+  int st = draft_check(cfg, w, state_pool, pool_slots, slots, n_req, commit_feats, commit_feats ? cu : nullptr,
+                       block_in, block_out, &rt, &rows);
+  if (st != HYF_OK) return st;
+  if (!ws || !aligned(ws, ALIGN) || ws_bytes < hyf_workspace_bytes(cfg, n_req, rows, 0)) return HYF_EWORKSPACE;
+  return draft_run(cfg, w, state_pool, rt, rows, commit_feats, block_in, block_out, static_cast<char*>(ws),
+                   static_cast<hipStream_t>(stream), rows > 0 ? commit_rows : nullptr);
 }
 
 int hyf_linear(const hyf_config* cfg, const void* X, int64_t M, int32_t K, const void* W, int32_t Nout, void* out,
@@ -919,7 +943,7 @@ int hyf_block_draft(const hyf_config* cfg, const hyf_weights* w, const hyf_block
     return HYF_EHIP;
   if ((he = launch_rmsnorm(dt, block_in, nb, d, bw->norm1, bw->eps, wsb + L.xb, hs)) != hipSuccess) return HYF_EHIP;
   if ((st = draft_run(cfg, w, state_pool, rt, rows, rows > 0 ? wsb + L.xc : nullptr, wsb + L.xb, wsb + L.o,
-                      wsb + L.inner, hs)) != HYF_OK)
+                      wsb + L.inner, hs, nullptr)) != HYF_OK)
     return st;
   // h = x + o, z = RMSNorm(h) norm2; gate|up = z w_gate_up^T; a = silu(gate) up; y = a w_down^T; out = h + y
   float* h = reinterpret_cast<float*>(wsb + L.h);

@@ -164,6 +164,9 @@ struct RoundArgs {
   int32_t do_draft;    // block rows present
   int32_t tile_rows;   // rows of H per commit / readout tile
   int32_t ks;          // ring slots per attention split
+  // nullable: committed rows of request r read from device memory (clamped to 0..HYF_BLOCK); its
+  // commit rows then sit at proj rows HYF_BLOCK r .. (a padded layout) instead of the table's row0
+  const int32_t* dev_rows;
 };
 // Fills n_tiles, tile_rows, ks and n_split of a round over n_req requests (esz: storage bytes).
 void round_layout(const Shape& sh, int n_req, int esz, RoundArgs* a);

@@ -24,6 +24,13 @@ __device__ __forceinline__ T* ring_ptr(char* pool, const Shape& sh, int slot, ui
   return reinterpret_cast<T*>(pool + (int64_t)slot * sh.st_bytes + off) + (int64_t)h * sh.W * sh.P;
 }
 
+// Committed rows of request r in this round: from the host table, or from device memory (clamped to
+// 0..RB) when the caller passes the counts on the device.
+__device__ __forceinline__ int commit_rows(const RoundArgs& a, const ReqTable& rt, int r) {
+  if (a.dev_rows) return min(max(a.dev_rows[r], 0), RB);
+  return rt.row0[r + 1] - rt.row0[r];
+}
+
 // ---------------------------------------------------------------------------------------------
 // One round, one launch.  Workgroup roles per (request r, head h), in block-index order:
 //   tiles  [0, n_tiles):   rows p0 .. p0 + tile_rows of H: fold the round's committed rows in (one
@@ -104,8 +111,8 @@ __device__ __forceinline__ void round_tile(const Shape& sh, const RoundArgs& a, 
   const bool lane_ok = prow < rows_wg;
   const int slot = rt.slot[r];
   const int grp = h / (nh / sh.G);
-  const int nrows = a.do_commit ? rt.row0[r + 1] - rt.row0[r] : 0;
-  const int64_t crow0 = rt.row0[r];
+  const int nrows = a.do_commit ? commit_rows(a, rt, r) : 0;
+  const int64_t crow0 = a.dev_rows ? (int64_t)RB * r : rt.row0[r];
   const int64_t brow0 = a.blk_row0 + (int64_t)r * RB;
   const int64_t ld = a.ld;
   float* Bl = reinterpret_cast<float*>(smem);
@@ -492,8 +499,8 @@ __device__ __forceinline__ void round_attn(const Shape& sh, const RoundArgs& a, 
   const int64_t ld = a.ld;
   const int64_t brow0 = a.blk_row0 + (int64_t)r * RB;
   const bool blk = sp == a.n_split - 1;
-  const int nrows = a.do_commit ? rt.row0[r + 1] - rt.row0[r] : 0;
-  const int64_t crow0 = rt.row0[r];
+  const int nrows = a.do_commit ? commit_rows(a, rt, r) : 0;
+  const int64_t crow0 = a.dev_rows ? (int64_t)RB * r : rt.row0[r];
   const int k0 = sp * ks;
   const int P4 = P / 4;
 
@@ -673,7 +680,7 @@ __device__ __forceinline__ void round_body(const Shape& sh, const RoundArgs& a, 
   // request has read the count by then
   if (threadIdx.x == 0 &&
       __hip_atomic_fetch_add(a.counters + rt.n_req * nh + r, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nh - 1)
-    *count_ptr(a.state_pool, sh, rt.slot[r]) += rt.row0[r + 1] - rt.row0[r];
+    *count_ptr(a.state_pool, sh, rt.slot[r]) += commit_rows(a, rt, r);
 }
 
 // Tiles of up to MID_PASSES row passes (the narrow layout): the register budget keeps five

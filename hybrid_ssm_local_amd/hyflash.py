@@ -78,6 +78,8 @@ _SIGS = {
     "hyf_linear_w4": (ctypes.c_int, [_P(HyfConfig), _vp, _i64, _i32, _vp, _vp, _i32, _vp, _i32, _vp]),
     "hyf_ssd_scan": (ctypes.c_int, [_P(HyfConfig), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _sz,
                                     _vp]),
+    "hyf_draft_block_dev": (ctypes.c_int, [_P(HyfConfig), _P(HyfWeights), _vp, _i32, _vp, _i32, _vp, _vp, _vp,
+                                           _vp, _vp, _sz, _vp]),
     "hyf_block_workspace_bytes": (_sz, [_P(HyfConfig), _P(HyfBlockWeights), _i32, _i64]),
     "hyf_block_commit": (ctypes.c_int, [_P(HyfConfig), _P(HyfWeights), _P(HyfBlockWeights), _vp, _i32, _vp, _i32,
                                         _vp, _vp, _vp, _sz, _vp]),
@@ -209,6 +211,15 @@ def hyf_draft_block(cfg, w: HyfWeights, pool, pool_slots, slots, n_req, commit_f
     return lib().hyf_draft_block(ctypes.byref(cfg), ctypes.byref(w), _ptr(pool), pool_slots, sp, n_req,
                                  _ptr(commit_feats), cp, _ptr(block_in), _ptr(block_out), _ptr(ws), ws_bytes,
                                  _stream(stream))
+
+
+def hyf_draft_block_dev(cfg, w: HyfWeights, pool, pool_slots, slots, n_req, commit_feats, commit_rows, block_in,
+                        block_out, ws, ws_bytes, stream=None) -> int:
+    """commit_feats [n_req*HYF_BLOCK][d] and commit_rows int32 [n_req] are device tensors (or None)."""
+    _s, sp = _host_i32(slots)
+    return lib().hyf_draft_block_dev(ctypes.byref(cfg), ctypes.byref(w), _ptr(pool), pool_slots, sp, n_req,
+                                     _ptr(commit_feats), _ptr(commit_rows), _ptr(block_in), _ptr(block_out), _ptr(ws),
+                                     ws_bytes, _stream(stream))
 
 
 def hyf_draft_block_noalloc(cfg, w: HyfWeights, pool, pool_slots, slots, n_req, commit_feats, cu_commit, block_in,

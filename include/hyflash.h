@@ -224,6 +224,22 @@ int hyf_draft_block_noalloc(const hyf_config* cfg, const hyf_weights* w, void* s
                             const void* commit_feats, const int64_t* cu_commit,
                             const void* block_in, void* block_out, void* stream);
 
+/* hyf_draft_block with the round's accepted-row counts on the device, for a serving loop whose
+ * verification step leaves them in GPU memory (explainer, "That is HyFlash": the accepted rows are
+ * committed before the next block is drafted): no host array depends on the counts, so one call
+ * has fixed launch shapes and can be captured in a graph once and replayed every round.
+ * commit_feats: [n_req][HYF_BLOCK][d_model] storage dtype, request i's committed row j at row
+ * i*HYF_BLOCK + j (rows past its count are projected and ignored; they may hold anything);
+ * commit_rows: device int32 [n_req], request i commits commit_rows[i] rows (values outside
+ * 0..HYF_BLOCK are clamped), read by the kernels when they run; both NULL for a pure draft.
+ * Results equal hyf_draft_block's for the same rows.  ws: at least
+ * hyf_workspace_bytes(cfg, n_req, HYF_BLOCK * n_req, 0) bytes. */
+int hyf_draft_block_dev(const hyf_config* cfg, const hyf_weights* w, void* state_pool,
+                        int32_t pool_slots, const int32_t* slots, int32_t n_req,
+                        const void* commit_feats, const int32_t* commit_rows,
+                        const void* block_in, void* block_out, void* ws, size_t ws_bytes,
+                        void* stream);
+
 /* The projection building block of the layer (explainer, "That is HyFlash": each layer
  * projects committed features and block rows; the draft step ends in an output projection):
  *   out[m][f] = sum_k X[m][k] * W[f][k]      m < M, f < Nout

@@ -838,3 +838,99 @@ def test_graph_replay_matches_eager():
         for o, r in zip(outs, ref_out):
             assert torch.equal(o, r)
         assert torch.equal(L.state()["blob"], ref_state)
+
+
+DEV_COUNT_SHAPES = [
+    ("tiny_fp32", I.TINY, 2),
+    ("small_bf16", small_shape("bf16", window=40), 3),
+    ("gdn_bf16", small_shape("bf16", window=24, memory="gdn"), 2),
+    ("lastw_bf16", small_shape("bf16", window=24, memory="lastw"), 2),
+    ("qwen", I.QWEN, 1),
+]
+
+
+def _padded_commits(shape, commits):
+    """[R*8][d] storage-dtype rows, request i's rows at i*8 .. (the rest of each slot NaN)."""
+    R = len(commits)
+    pad = np.full((R * hf.HYF_BLOCK, shape.d_model), np.nan, np.float32)
+    for i, c in enumerate(commits):
+        pad[i * hf.HYF_BLOCK: i * hf.HYF_BLOCK + len(c)] = c
+    return hf.to_device(pad, shape)
+
+
+@pytest.mark.parametrize("name,shape,R", DEV_COUNT_SHAPES, ids=[c[0] for c in DEV_COUNT_SHAPES])
+def test_device_counts_equal_the_host_table(name, shape, R):
+    # The same rounds through hyf_draft_block (host cu) and hyf_draft_block_dev (padded rows, counts
+    # on the device; the unused padding is NaN and must not leak): outputs and states bit for bit.
+    pr = Pair(shape, seed=111, pool_slots=R, max_requests=R, max_rows=200)
+    dev = hf.DrafterLayer(shape, pr.w, pool_slots=R, max_requests=R, max_rows=200)
+    pre = [pr.rows(n) for n in ([40, 9, 1][:R] if R > 1 else [60])]
+    cu = np.concatenate([[0], np.cumsum([len(p) for p in pre])]).astype(np.int64)
+    for L in (pr.gpu, dev):
+        L.reset()
+        L.commit(hf.to_device(np.concatenate(pre), shape), cu)
+    for rnd, a in enumerate(([3, 8, 0], [0, 1, 5], [8, 2, 7])):
+        a = a[:R]
+        commits = [pr.rows(n) for n in a]
+        blocks = hf.to_device(np.concatenate([pr.rows(8, 3) for _ in range(R)]), shape)
+        o_host, o_dev = torch.empty_like(blocks), torch.empty_like(blocks)
+        cu_r = np.concatenate([[0], np.cumsum(a)]).astype(np.int64)
+        cf = hf.to_device(np.concatenate(commits) if cu_r[-1] else np.zeros((1, shape.d_model), np.float32), shape)
+        say("hyf_draft_block host table", name, a)
+        pr.gpu.draft(blocks, o_host, cf, cu_r)
+        counts = torch.tensor(a, dtype=torch.int32, device=DEV)
+        say("hyf_draft_block_dev", name, a)
+        hf.check(hf.hyf_draft_block_dev(dev.cfg, dev.w, dev.pool, R, None, R, _padded_commits(shape, commits), counts,
+                                        blocks, o_dev, dev.ws, dev.ws_bytes), "hyf_draft_block_dev")
+        torch.cuda.synchronize()
+        assert torch.equal(o_host, o_dev), f"{name} round {rnd} outputs"
+        assert torch.equal(pr.gpu.pool, dev.pool), f"{name} round {rnd} states"
+
+
+def test_device_count_round_replays_in_a_graph():
+    # One hyf_draft_block_dev call captured once, replayed for four rounds whose rows and counts are
+    # written into its fixed buffers on the device between replays (eager copies, then a sync):
+    # every replay equals the eager host-table round on the same rows, outputs and state.
+    shape = small_shape("bf16", window=40)
+    R = 2
+    pr = Pair(shape, seed=112, pool_slots=R, max_requests=R, max_rows=200)
+    dev = hf.DrafterLayer(shape, pr.w, pool_slots=R, max_requests=R, max_rows=200)
+    pre = hf.to_device(np.concatenate([pr.rows(50), pr.rows(70)]), shape)
+    for L in (pr.gpu, dev):
+        L.reset()
+        L.commit(pre, np.array([0, 50, 120], np.int64))
+    torch.cuda.synchronize()
+    feats_buf = torch.zeros((R * hf.HYF_BLOCK, shape.d_model), dtype=hf.torch_dtype(shape), device=DEV)
+    counts_buf = torch.zeros(R, dtype=torch.int32, device=DEV)
+    block_buf = torch.zeros((R * hf.HYF_BLOCK, shape.d_model), dtype=hf.torch_dtype(shape), device=DEV)
+    out_buf = torch.empty_like(block_buf)
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    snap = dev.pool.clone()
+    say("graph: warm call and capture of hyf_draft_block_dev")
+    with torch.cuda.stream(cs):
+        hf.check(hf.hyf_draft_block_dev(dev.cfg, dev.w, dev.pool, R, None, R, feats_buf, counts_buf, block_buf,
+                                        out_buf, dev.ws, dev.ws_bytes, cs))
+    torch.cuda.synchronize()
+    dev.pool.copy_(snap)  # the warm call committed zero rows (counts 0) but restore anyway
+    with torch.cuda.graph(g, stream=cs):
+        hf.check(hf.hyf_draft_block_dev(dev.cfg, dev.w, dev.pool, R, None, R, feats_buf, counts_buf, block_buf,
+                                        out_buf, dev.ws, dev.ws_bytes, cs))
+    torch.cuda.synchronize()
+    for rnd, a in enumerate(([4, 1], [0, 8], [7, 3], [2, 0])):
+        commits = [pr.rows(n) for n in a]
+        blocks = hf.to_device(np.concatenate([pr.rows(8, 3) for _ in range(R)]), shape)
+        feats_buf.copy_(_padded_commits(shape, commits).nan_to_num(0.0))
+        counts_buf.copy_(torch.tensor(a, dtype=torch.int32))
+        block_buf.copy_(blocks)
+        torch.cuda.synchronize()
+        say("graph: replay round", rnd, a)
+        g.replay()
+        torch.cuda.synchronize()
+        cu_r = np.concatenate([[0], np.cumsum(a)]).astype(np.int64)
+        cf = hf.to_device(np.concatenate(commits) if cu_r[-1] else np.zeros((1, shape.d_model), np.float32), shape)
+        o_host = torch.empty_like(blocks)
+        pr.gpu.draft(blocks, o_host, cf, cu_r)
+        torch.cuda.synchronize()
+        assert torch.equal(out_buf, o_host), f"replay {rnd} outputs"
+        assert torch.equal(dev.pool, pr.gpu.pool), f"replay {rnd} states"
