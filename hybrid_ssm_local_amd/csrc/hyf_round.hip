@@ -10,7 +10,7 @@ constexpr int RB = HYF_BLOCK;   // block rows
 constexpr int RMAXC = 16;       // largest per-request commit a round kernel folds in
 constexpr int KS_MIN = 64;      // fewest keys per attention split (the workspace is sized for it)
 constexpr int WIDE_PASSES = 16; // most row passes of one commit / readout tile (wide layout)
-constexpr int MID_PASSES = 3;   // most row passes of a tile in the narrow layout
+constexpr int MID_PASSES = 2;   // most row passes of a tile in the narrow layout (3 spills at 80 VGPRs)
 constexpr int RT = 256;         // threads per round workgroup
 
 __device__ __forceinline__ int64_t* count_ptr(char* pool, const Shape& sh, int slot) {
@@ -693,9 +693,9 @@ __device__ __forceinline__ void round_body(const Shape& sh, const RoundArgs& a, 
     *count_ptr(a.state_pool, sh, rt.slot[r]) += commit_rows(a, rt, r);
 }
 
-// Tiles of up to MID_PASSES row passes (the narrow layout): the register budget (80 VGPRs, a few
-// spilled) and the LDS of the attention splits keep six workgroups on a CU (64 Qwen3-4B-shaped
-// requests: 227 against 233 us with five).
+// Tiles of up to MID_PASSES row passes (the narrow layout): the register budget (80 VGPRs) and
+// the LDS of the attention splits keep six workgroups on a CU (64 Qwen3-4B-shaped requests: 221
+// against 233 us with five workgroups and three-pass tiles).
 template <typename T, int TMAXG>
 __global__ void __launch_bounds__(RT) __attribute__((amdgpu_waves_per_eu(6))) k_round(Shape sh, RoundArgs a,
                                                                                      ReqTable rt) {
