@@ -10,31 +10,31 @@
 
 namespace hyf {
 
-// bf16 GEMM for K a multiple of 64: BM x BN macro tiles (rows x features), K step 64, three LDS
+// bf16 GEMM for K a multiple of 64: BM x BN macro tiles (rows x features), K step 64, ST LDS
 // stages filled by direct global -> LDS copies.  With NW waves the waves form an (NW/2) x 2 grid:
 // wave (wm, wn) owns rows wm*RW .. + RW - 1 (RW = 2 BM / NW) and features wn*BN/2 .. + BN/2 - 1.
-// Large products run 256 x 128 tiles with NW = 8 (two waves per SIMD, 64 x 64 per wave, one
-// workgroup per CU): one wave's MFMAs then cover the other's LDS reads, barrier and copy waits.
-// Measured at 8192 x 2560 x 2720: 117 us with 8 waves against 145 us with 4 waves of 128 x 64 (one
-// per SIMD).  Products of a few hundred rows (the batched rounds' projections) have too few such
-// tiles to fill 256 CUs and take smaller ones (several workgroups per CU).
+// Large products run 256 x 128 tiles with NW = 16 (four waves per SIMD, 32 x 64 per wave, one
+// workgroup per CU): the other waves' MFMAs then cover one wave's LDS reads, barrier and copy
+// waits.  Products of a few hundred rows (the batched rounds' projections) have too few such tiles
+// to fill 256 CUs and take smaller ones (several workgroups per CU).
 //
 // Per K step a 256 x 128 workgroup does 2*256*128*64 flops against 48 KiB staged, so a CU at the
 // MFMA rate needs about 47 B/clk from L2; smaller tiles need more bytes per flop.  Three stages keep
-// two K steps of copies in flight while one computes.
+// two K steps of copies in flight while one computes; two workgroups of two stages per CU do the
+// same.
 //
 // LDS operand layout (both operands are K-contiguous rows): row r of a stage is 128 bytes = 8
 // chunks of 16 bytes; logical chunk c sits at position c ^ (r & 7), so the 16 lanes of an MFMA
 // fragment load (16 rows, one chunk) hit 8 distinct 16-byte bank groups per 8 lanes.  A direct
 // copy writes lane l's 16 bytes at base + 16 l, so lane l of a copy covering rows r0 .. r0 + 7
 // (r0 a multiple of 8) fetches row r0 + l / 8, logical chunk (l % 8) ^ (l / 8).
-constexpr int G2_K = 64, G2_ST = 3;
+constexpr int G2_K = 64;
 constexpr int G2_GROUP = 4;  // M tiles per group in the tile order
 template <int BM, int BN>
 constexpr int g2_stage() { return (BM + BN) * G2_K * 2; }  // bytes per stage (48 KiB at 256 x 128)
-template <int BM, int BN>
-constexpr int g2_lds() {  // three stages; the epilogue's fp32 tile ([f][m] or [m][f]) reuses them
-  constexpr int st = G2_ST * g2_stage<BM, BN>(), tr = BN * (BM + 4) * 4, rm = BM * (BN + 4) * 4;
+template <int BM, int BN, int ST>
+constexpr int g2_lds() {  // ST stages; the epilogue's fp32 tile ([f][m] or [m][f]) reuses them
+  constexpr int st = ST * g2_stage<BM, BN>(), tr = BN * (BM + 4) * 4, rm = BM * (BN + 4) * 4;
   return st > tr ? (st > rm ? st : rm) : (tr > rm ? tr : rm);
 }
 
@@ -62,10 +62,21 @@ __device__ __forceinline__ void epi_store_blk(const Epi& e, int64_t blk, int off
   }
 }
 
-template <typename TO, int BM, int BN, int NW, int WPE, typename GRP>
+// Wait until at most n stages of this wave's copies (CP instructions each) are outstanding, n in
+// 0..ST-2 (a run-time count near the end of K; vm_wait needs an immediate).
+template <int CP, int ST>
+__device__ __forceinline__ void wait_stages(int n) {
+  if constexpr (ST >= 4) {
+    if (n >= 2) { vm_wait<2 * CP>(); return; }
+  }
+  if (n >= 1) vm_wait<CP>(); else vm_wait<0>();
+}
+
+template <typename TO, int BM, int BN, int NW, int WPE, typename GRP, int ST>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 k_gemm_bf16_tile(RowSrc xs, int M, int K, const bf16* __restrict__ W, int Nout, Epi epi, int tm, int tn,
                  int per_xcd, GRP rows) {
+  static_assert(ST >= 2 && ST <= 4, "stages");
   constexpr bool GR = std::is_same<GRP, RowGroups>::value;
   constexpr int G2_M = BM, G2_N = BN, G2_STAGE = g2_stage<BM, BN>();
   constexpr int BT = BN / 32;  // 16-feature tiles per wave
@@ -114,7 +125,7 @@ k_gemm_bf16_tile(RowSrc xs, int M, int K, const bf16* __restrict__ W, int Nout, 
     bsrc[j] = reinterpret_cast<const char*>(W + (int64_t)f * K) + 16 * lc;
   }
   auto issue = [&](int kt) __attribute__((always_inline)) {
-    char* st = smem + (kt % G2_ST) * G2_STAGE;
+    char* st = smem + (kt % ST) * G2_STAGE;
     const int64_t kb = (int64_t)kt * G2_K * 2;
 #pragma unroll
     for (int j = 0; j < CA; ++j) lds_dma16(asrc[j] + kb, st + (wave + NW * j) * 1024);
@@ -129,8 +140,9 @@ k_gemm_bf16_tile(RowSrc xs, int M, int K, const bf16* __restrict__ W, int Nout, 
     for (int b = 0; b < BT; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nk = K / G2_K;
-  issue(0);
-  if (nk > 1) issue(1);
+#pragma unroll
+  for (int k = 0; k < ST - 1; ++k)
+    if (k < nk) issue(k);
   // fragment offsets: row r (r & 7 == i & 7), logical chunk c = 4 ks + g at position c ^ (i & 7)
   const int arow = (wm * RW + i) * 128, brow = G2_M * 128 + (wn * (BN / 2) + i) * 128;
   auto frags = [&](const char* st, int ks, bf16x8 (&fa)[AT], bf16x8 (&fb)[BT]) __attribute__((always_inline)) {
@@ -148,29 +160,26 @@ k_gemm_bf16_tile(RowSrc xs, int M, int K, const bf16* __restrict__ W, int Nout, 
         acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
   };
   // Software pipeline over half-steps (32 k values).  Fragments of the next half-step are read
-  // while the current half-step's 32 MFMAs run; before a new batch of 12 fragment reads the
-  // previous batch is waited on (it has had a whole MFMA batch to land), so at most 12 LDS reads
-  // are ever outstanding.  The barrier of stage kt + 1 sits between the two half-steps of stage kt:
-  // once every wave passes it, stage kt + 1 is in LDS and all reads of stage kt are done, so the
-  // copies of stage kt + 3 can refill stage kt's buffer.  The barrier is the bare instruction: a
-  // __syncthreads() fence would also wait for the copies still in flight.
+  // while the current half-step's MFMAs run; before a new batch of fragment reads the previous
+  // batch is waited on (it has had a whole MFMA batch to land).  The barrier of stage kt + 1 sits
+  // between the two half-steps of stage kt: once every wave passes it, stage kt + 1 is in LDS and
+  // all reads of stage kt are done, so the copies of stage kt + ST can refill stage kt's buffer
+  // (ST - 2 stages stay in flight behind the one that landed).  The barrier is the bare
+  // instruction: a __syncthreads() fence would also wait for the copies still in flight.
   auto barrier = [&]() __attribute__((always_inline)) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
   bf16x8 fa0[AT], fb0[BT], fa1[AT], fb1[BT];
-  if (nk > 1)
-    vm_wait<CA + CB>();
-  else
-    vm_wait<0>();
+  wait_stages<CA + CB, ST>(min(ST - 2, nk - 1));  // stage 0 landed
   barrier();
-  if (nk > 2) issue(2);
+  if (ST - 1 < nk) issue(ST - 1);
   frags(smem, 0, fa0, fb0);
   // stage kt: its first half-step's fragments are in fa0/fb0 (read during the previous MFMAs)
   auto first_half = [&](int kt) __attribute__((always_inline)) {
     lgkm_wait0();
-    frags(smem + (kt % G2_ST) * G2_STAGE, 1, fa1, fb1);
+    frags(smem + (kt % ST) * G2_STAGE, 1, fa1, fb1);
     __builtin_amdgcn_sched_barrier(0);
     mma(fa0, fb0);
     __builtin_amdgcn_sched_barrier(0);
@@ -178,15 +187,12 @@ k_gemm_bf16_tile(RowSrc xs, int M, int K, const bf16* __restrict__ W, int Nout, 
   };
   for (int kt = 0; kt + 1 < nk; ++kt) {
     first_half(kt);
-    // stage kt + 1 landed once at most the copies of stage kt + 2 (issued one barrier ago) remain;
-    // every wave's reads of stage kt are done, so the copies of stage kt + 3 may refill its buffer
-    if (kt + 2 < nk)
-      vm_wait<CA + CB>();
-    else
-      vm_wait<0>();
+    // stage kt + 1 landed once at most the copies of the stages issued after it remain; every
+    // wave's reads of stage kt are done, so the copies of stage kt + ST may refill its buffer
+    wait_stages<CA + CB, ST>(min(ST - 2, nk - 2 - kt));
     barrier();
-    if (kt + 3 < nk) issue(kt + 3);
-    frags(smem + ((kt + 1) % G2_ST) * G2_STAGE, 0, fa0, fb0);
+    if (kt + ST < nk) issue(kt + ST);
+    frags(smem + ((kt + 1) % ST) * G2_STAGE, 0, fa0, fb0);
     __builtin_amdgcn_sched_barrier(0);
     mma(fa1, fb1);
     __builtin_amdgcn_sched_barrier(0);
@@ -294,21 +300,21 @@ k_gemm_bf16_tile(RowSrc xs, int M, int K, const bf16* __restrict__ W, int Nout, 
   }
 }
 
-template <int BM, int BN, int NW, int WPE, typename GRP>
+template <int BM, int BN, int NW, int WPE, typename GRP, int ST = 3>
 static hipError_t launch_tile(RowSrc x, int M, int K, const bf16* W, int Nout, const Epi& epi, const GRP& grp,
                               hipStream_t s) {
-  constexpr int lds = g2_lds<BM, BN>();
+  constexpr int lds = g2_lds<BM, BN, ST>();
   static std::once_flag once;
   static hipError_t set_err = hipSuccess;
   std::call_once(once, [] {
-    set_err = hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm_bf16_tile<bf16, BM, BN, NW, WPE, GRP>),
+    set_err = hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm_bf16_tile<bf16, BM, BN, NW, WPE, GRP, ST>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   });
   if (set_err != hipSuccess) return set_err;
   const int tm = (M + BM - 1) / BM, tn = (Nout + BN - 1) / BN;
   const int per_xcd = (tm * tn + 7) / 8;
-  hipLaunchKernelGGL((k_gemm_bf16_tile<bf16, BM, BN, NW, WPE, GRP>), dim3(8 * per_xcd), dim3(64 * NW), lds, s, x, M,
-                     K, W, Nout, epi, tm, tn, per_xcd, grp);
+  hipLaunchKernelGGL((k_gemm_bf16_tile<bf16, BM, BN, NW, WPE, GRP, ST>), dim3(8 * per_xcd), dim3(64 * NW), lds, s, x,
+                     M, K, W, Nout, epi, tm, tn, per_xcd, grp);
   return hipGetLastError();
 }
 
@@ -316,17 +322,22 @@ template <typename GRP>
 static hipError_t launch_chosen(RowSrc x, int M, int K, const bf16* W, int Nout, const Epi& epi, const GRP& grp,
                                 hipStream_t s) {
   auto tiles = [&](int bm, int bn) { return (int64_t)((M + bm - 1) / bm) * ((Nout + bn - 1) / bn); };
-  if (tiles(256, 128) >= 192) return launch_tile<256, 128, 8, 2>(x, M, K, W, Nout, epi, grp, s);
-  if (tiles(128, 128) >= 160) return launch_tile<128, 128, 8, 2>(x, M, K, W, Nout, epi, grp, s);
+  if (tiles(256, 128) >= 384) return launch_tile<256, 128, 16, 4, GRP, 3>(x, M, K, W, Nout, epi, grp, s);
+  if (tiles(128, 128) >= 160) return launch_tile<128, 128, 8, 4, GRP, 2>(x, M, K, W, Nout, epi, grp, s);
   if (tiles(128, 64) >= 160) return launch_tile<128, 64, 8, 4>(x, M, K, W, Nout, epi, grp, s);
   return launch_tile<64, 64, 4, 3>(x, M, K, W, Nout, epi, grp, s);
 }
 
-// Tile choice, from measured products (bf16, K 2560-5120): 256 x 128 tiles (one workgroup of 8
-// waves per CU) once there are 192 or more of them; below that the largest of 128 x 128 (one per
-// CU), 128 x 64 (8 waves, two per CU) and 64 x 64 (4 waves, three per CU) that still gives 160 or
-// more workgroups, else 64 x 64.  At 512 x 2560 x 2560 this takes 17 us against 37.5 us for the
-// 40 large tiles; at 800 x 2560 x 7968 the 252 large tiles stay fastest (48.7 us).
+// Tile choice, from measured products (bf16, K 2560-5120): 256 x 128 tiles (one workgroup of 16
+// waves per CU, three stages) once there are 384 or more of them; below that the largest of
+// 128 x 128 (8 waves, two stages, two workgroups per CU), 128 x 64 (8 waves, two per CU) and
+// 64 x 64 (4 waves, three per CU) that still gives 160 or more workgroups, else 64 x 64.  Two
+// resident workgroups of two stages each keep as many copies in flight per CU as one of three
+// and let one workgroup's MFMAs run through the other's barrier waits: 520 x 2560 x 7968 takes
+// 36 us against 47 us for one 128 x 128 workgroup of three stages per CU, and 800 x 2560 x 7968
+// 46 us against 51 us for 252 large tiles.  Sixteen waves on the large tile (each a 32 x 64 block)
+// beat eight (64 x 64 blocks) by 3-6% from 2048 x 2560 x 7968 up to 32768 x 5120 x 5288.  At
+// 512 x 2560 x 2560 the 64 x 64 tiles take 17 us against 28 us for the 80 128 x 128 tiles.
 hipError_t launch_gemm256(RowSrc x, int M, int K, const bf16* W, int Nout, const Epi& epi, hipStream_t s) {
   return launch_chosen(x, M, K, W, Nout, epi, NoGroups{}, s);
 }
