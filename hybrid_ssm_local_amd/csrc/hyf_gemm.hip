@@ -32,9 +32,14 @@ constexpr int G2_K = 64;
 constexpr int G2_GROUP = 4;  // M tiles per group in the tile order
 template <int BM, int BN>
 constexpr int g2_stage() { return (BM + BN) * G2_K * 2; }  // bytes per stage (48 KiB at 256 x 128)
+// The epilogue stages the fp32 tile ([f][m] or [m][f]) in the stages' LDS, in EH passes of BN / EH
+// features each: two passes when the whole tile would not fit in 160 KiB.
+template <int BM, int BN>
+constexpr int g2_epi_halves() { return BN * (BM + 4) * 4 > 160 * 1024 || BM * (BN + 4) * 4 > 160 * 1024 ? 2 : 1; }
 template <int BM, int BN, int ST>
-constexpr int g2_lds() {  // ST stages; the epilogue's fp32 tile ([f][m] or [m][f]) reuses them
-  constexpr int st = ST * g2_stage<BM, BN>(), tr = BN * (BM + 4) * 4, rm = BM * (BN + 4) * 4;
+constexpr int g2_lds() {
+  constexpr int EN = BN / g2_epi_halves<BM, BN>();
+  constexpr int st = ST * g2_stage<BM, BN>(), tr = EN * (BM + 4) * 4, rm = BM * (EN + 4) * 4;
   return st > tr ? (st > rm ? st : rm) : (tr > rm ? tr : rm);
 }
 
@@ -79,6 +84,7 @@ k_gemm_bf16_tile(RowSrc xs, int M, int K, const bf16* __restrict__ W, int Nout, 
   static_assert(ST >= 2 && ST <= 4, "stages");
   constexpr bool GR = std::is_same<GRP, RowGroups>::value;
   constexpr int G2_M = BM, G2_N = BN, G2_STAGE = g2_stage<BM, BN>();
+  constexpr int EH = g2_epi_halves<BM, BN>(), EN = BN / EH;  // epilogue passes, features per pass
   constexpr int BT = BN / 32;  // 16-feature tiles per wave
   static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0 && BN % 32 == 0 && (2 * BM / NW) % 16 == 0, "tile shape");
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -208,16 +214,21 @@ k_gemm_bf16_tile(RowSrc xs, int M, int K, const bf16* __restrict__ W, int Nout, 
     // (out1).
     constexpr int CP = G2_M + 4;
     float* ct = reinterpret_cast<float*>(smem);
+    for (int eh = 0; eh < EH; ++eh) {  // feature passes
+    if (eh > 0) __syncthreads();  // the previous pass's reads of ct are done
+    if (EH == 1 || wn == eh) {
 #pragma unroll
-    for (int a = 0; a < AT; ++a)
+      for (int a = 0; a < AT; ++a)
 #pragma unroll
-      for (int b = 0; b < BT; ++b)
+        for (int b = 0; b < BT; ++b)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ct[(wn * (BN / 2) + b * 16 + i) * CP + wm * RW + a * 16 + 4 * g + r] = acc[a][b][r];
+          for (int r = 0; r < 4; ++r)
+            ct[((EH == 1 ? wn * (BN / 2) : 0) + b * 16 + i) * CP + wm * RW + a * 16 + 4 * g + r] = acc[a][b][r];
+    }
     __syncthreads();
-    for (int it = t; it < G2_N * (G2_M / 8); it += NT) {
-      const int fl = it % G2_N, m8 = (it / G2_N) * 8;
-      const int f = n0 + fl;
+    for (int it = t; it < EN * (G2_M / 8); it += NT) {
+      const int fl = it % EN, m8 = (it / EN) * 8;
+      const int f = n0 + eh * EN + fl;
       const int64_t m = (int64_t)m0 + m8;
       if (f >= Nout || m >= M) continue;
       const float* src = ct + fl * CP + m8;
@@ -253,23 +264,29 @@ k_gemm_bf16_tile(RowSrc xs, int M, int K, const bf16* __restrict__ W, int Nout, 
         for (int e = 0; e < 8 && m + e < M; ++e) epi_store<TO>(epi, m + e, f, src[e]);
       }
     }
+    }
     return;
   }
   // Row-major output: the fp32 tile is staged as [m][f] (pitch RP floats); each item then writes 8
   // features of one row, as one or two 16-byte stores where the destination allows it.
-  constexpr int RP = G2_N + 4;
+  constexpr int RP = EN + 4;
   float* ct = reinterpret_cast<float*>(smem);
+  for (int eh = 0; eh < EH; ++eh) {  // feature passes
+  if (eh > 0) __syncthreads();  // the previous pass's reads of ct are done
+  if (EH == 1 || wn == eh) {
 #pragma unroll
-  for (int a = 0; a < AT; ++a)
+    for (int a = 0; a < AT; ++a)
 #pragma unroll
-    for (int b = 0; b < BT; ++b)
+      for (int b = 0; b < BT; ++b)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ct[(wm * RW + a * 16 + 4 * g + r) * RP + wn * (BN / 2) + b * 16 + i] = acc[a][b][r];
+        for (int r = 0; r < 4; ++r)
+          ct[(wm * RW + a * 16 + 4 * g + r) * RP + (EH == 1 ? wn * (BN / 2) : 0) + b * 16 + i] = acc[a][b][r];
+  }
   __syncthreads();
-  for (int it = t; it < G2_M * (G2_N / 8); it += NT) {
-    const int ml = it / (G2_N / 8), f8 = (it % (G2_N / 8)) * 8;
+  for (int it = t; it < G2_M * (EN / 8); it += NT) {
+    const int ml = it / (EN / 8), f8 = (it % (EN / 8)) * 8;
     const int64_t m = (int64_t)m0 + ml;
-    const int f = n0 + f8;
+    const int f = n0 + eh * EN + f8;
     if (m >= M || f >= Nout) continue;
     const float* src = ct + ml * RP + f8;
     const f32x4 lo = *reinterpret_cast<const f32x4*>(src), hi = *reinterpret_cast<const f32x4*>(src + 4);
@@ -298,6 +315,7 @@ k_gemm_bf16_tile(RowSrc xs, int M, int K, const bf16* __restrict__ W, int Nout, 
     }
     for (int e = 0; e < 8 && f + e < Nout; ++e) epi_store<TO>(epi, m, f + e, src[e]);
   }
+  }
 }
 
 template <int BM, int BN, int NW, int WPE, typename GRP, int ST = 3>
@@ -322,14 +340,23 @@ template <typename GRP>
 static hipError_t launch_chosen(RowSrc x, int M, int K, const bf16* W, int Nout, const Epi& epi, const GRP& grp,
                                 hipStream_t s) {
   auto tiles = [&](int bm, int bn) { return (int64_t)((M + bm - 1) / bm) * ((Nout + bn - 1) / bn); };
+  // fraction of the last wave of tiles (256 CUs, one large tile each) that is busy
+  auto fill = [&](int64_t n) { return (double)n / (double)(((n + 255) / 256) * 256); };
+  const int64_t t256 = tiles(256, 256);
+  if (t256 >= 256 && fill(t256) * 1.12 >= fill(tiles(256, 128)))
+    return launch_tile<256, 256, 8, 2, GRP, 2>(x, M, K, W, Nout, epi, grp, s);
   if (tiles(256, 128) >= 384) return launch_tile<256, 128, 16, 4, GRP, 3>(x, M, K, W, Nout, epi, grp, s);
   if (tiles(128, 128) >= 160) return launch_tile<128, 128, 8, 4, GRP, 2>(x, M, K, W, Nout, epi, grp, s);
   if (tiles(128, 64) >= 160) return launch_tile<128, 64, 8, 4>(x, M, K, W, Nout, epi, grp, s);
   return launch_tile<64, 64, 4, 3>(x, M, K, W, Nout, epi, grp, s);
 }
 
-// Tile choice, from measured products (bf16, K 2560-5120): 256 x 128 tiles (one workgroup of 16
-// waves per CU, three stages) once there are 384 or more of them; below that the largest of
+// Tile choice, from measured products (bf16, K 2560-5120): 256 x 256 tiles (8 waves of 64 x 128,
+// two stages, one workgroup per CU) where there are 256 or more of them and their last wave is not
+// much emptier than that of 256 x 128 tiles: about 10% faster than 256 x 128 at 2048 x 2560 x 7968,
+// 16384 x 2560 x 7968 and 32768 x 5120 x 5288, but not at 8192 x 2560 x 2720 (352 tiles, 1.4 waves).
+// Else 256 x 128 tiles (one workgroup of 16 waves per CU, three stages) once there are 384 or more
+// of them; below that the largest of
 // 128 x 128 (8 waves, two stages, two workgroups per CU), 128 x 64 (8 waves, two per CU) and
 // 64 x 64 (4 waves, three per CU) that still gives 160 or more workgroups, else 64 x 64.  Two
 // resident workgroups of two stages each keep as many copies in flight per CU as one of three

@@ -166,12 +166,17 @@ LINEAR_CASES = [  # (dtype, K, Nout, Ms): K tails past a 128-wide slab, M across
     ("bf16", 64, 130, [65, 257]),
     ("bf16", 128, 129, [100]),
     ("bf16", 192, 256, [300]),
-    # 128 x 128 tiles (176 of them)
+    # 128 x 128 tiles (176 of them, two stages)
     ("bf16", 256, 2720, [1000]),
     # 128 x 64 tiles (164), ragged rows and features
     ("bf16", 128, 2600, [500]),
-    # 256 x 128 tiles (192), ragged features
+    # 128 x 128 tiles (384), ragged features
     ("bf16", 128, 3000, [2000]),
+    # 256 x 128 tiles (423, 16 waves, three stages), ragged rows and features
+    ("bf16", 128, 6000, [2100]),
+    # 256 x 256 tiles (256, two stages; the epilogue in two feature passes), ragged rows and
+    # features, three K steps
+    ("bf16", 192, 4000, [4090]),
     ("f32", 256, 100, [1, 20, 64, 65]),
 ]
 
