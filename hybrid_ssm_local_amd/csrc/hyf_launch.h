@@ -145,6 +145,18 @@ hipError_t launch_ssd_state(int dtype, const Shape& sh, const ScanArgs& a, const
                             int32_t max_segs_per_req, hipStream_t s);
 
 // Round kernel (see hyf_round.hip).
+// Division of small non-negative indices by a divisor d >= 1 as one multiply-high: with
+// m = ceil(2^32 / d), floor(i / d) = mulhi(i, m) exactly whenever i d < 2^32 (0 <= m d - 2^32 < d);
+// d = 1 wraps m to 0 and is taken apart.  Built on the host, so kernels divide without a sequence.
+struct Div {
+  uint32_t m;
+  int32_t d;
+  Div() = default;
+  __host__ __device__ explicit Div(int d_) : m(0xFFFFFFFFu / (uint32_t)d_ + 1u), d(d_) {}
+  __device__ int q(int i) const { return m ? (int)__umulhi((uint32_t)i, m) : i; }
+  __device__ int r(int i) const { return i - q(i) * d; }
+};
+
 struct RoundArgs {
   const float* proj;   // [rows][ld] fp32: commit rows first (row0 table), then block rows
   int64_t ld;          // row stride of proj (n_in rounded up to a multiple of 4)
@@ -167,6 +179,8 @@ struct RoundArgs {
   // nullable: committed rows of request r read from device memory (clamped to 0..HYF_BLOCK); its
   // commit rows then sit at proj rows HYF_BLOCK r .. (a padded layout) instead of the table's row0
   const int32_t* dev_rows;
+  // set by launch_round: n_tiles + n_split, nh, P / 4, P, N / 4, tile_rows
+  Div d_per, d_nh, d_p4, d_p, d_tpr, d_tr;
 };
 // Fills n_tiles, tile_rows, ks and n_split of a round over n_req requests (esz: storage bytes).
 void round_layout(const Shape& sh, int n_req, int esz, RoundArgs* a);

@@ -71,6 +71,16 @@ __device__ __forceinline__ void stage4(int n, void* dst, F src) {
 }
 __host__ __device__ constexpr int up1k(int bytes) { return (bytes + 1023) / 1024 * 1024; }
 
+// count mod W for 0 <= count < 2^52 (one double division instead of a 64-bit integer division: the
+// rounded quotient is within one of the true one, and one step corrects the remainder).
+__device__ __forceinline__ int mod_w(int64_t count, int W) {
+  const int64_t q = (int64_t)((double)count / (double)W);
+  int64_t r = count - q * W;
+  if (r < 0) r += W;
+  else if (r >= W) r -= W;
+  return (int)r;
+}
+
 // Results another workgroup of the same launch merges are stored device-coherent (written through
 // to the level all XCDs share) and read the same way, so the hand-over needs no L2 write-back or
 // invalidation: the writer waits for its stores to complete before it counts itself in.
@@ -106,7 +116,9 @@ __device__ __forceinline__ void round_tile(const Shape& sh, const RoundArgs& a, 
   const int trows = a.tile_rows;   // H rows per tile: a multiple of rows_wg, at most TMAXG passes (host-checked)
   const int npass = trows / rows_wg;
   const int t = threadIdx.x;
-  const int prow = t / tpr, c4 = t % tpr;
+  const Div& dtpr = a.d_tpr;
+  const Div& dtr = a.d_tr;
+  const int prow = dtpr.q(t), c4 = t - prow * tpr;
   const int p0 = tile * trows;
   const bool lane_ok = prow < rows_wg;
   const int slot = rt.slot[r];
@@ -138,11 +150,17 @@ __device__ __forceinline__ void round_tile(const Shape& sh, const RoundArgs& a, 
   const float rawb = sh.gdn && t < nrows ? a.proj[(crow0 + t) * ld + sh.off_beta + h] : 0.f;
   // column of tile row i (rows past the head's last row read its last row; their values go unused)
   auto tcol = [&](int i) { return p0 + i < P ? p0 + i : P - 1; };
-  stage16(nrows * tpr, Bl, [&](int i) { return a.proj + (crow0 + i / tpr) * ld + sh.off_b + grp * N + 4 * (i % tpr); });
-  stage4(nrows * trows, xv, [&](int i) { return a.proj + (crow0 + i / trows) * ld + sh.off_v + h * P + tcol(i % trows); });
+  // row q of a staging job sits q ld floats past the job's first row (ld (RMAXC + RB) < 2^31 / 4)
+  const int ldi = (int)ld;
+  const float* cb = a.proj + crow0 * ld + sh.off_b + grp * N;
+  const float* cv = a.proj + crow0 * ld + sh.off_v + h * P;
+  stage16(nrows * tpr, Bl, [&](int i) { const int q = dtpr.q(i); return cb + (uint32_t)(q * ldi + 4 * (i - q * tpr)); });
+  stage4(nrows * trows, xv, [&](int i) { const int q = dtr.q(i); return cv + (uint32_t)(q * ldi + tcol(i - q * trows)); });
   if (a.do_draft) {
-    stage16(RB * tpr, Cl, [&](int i) { return a.proj + (brow0 + i / tpr) * ld + sh.off_c + grp * N + 4 * (i % tpr); });
-    stage4(RB * trows, vb, [&](int i) { return a.proj + (brow0 + i / trows) * ld + sh.off_v + h * P + tcol(i % trows); });
+    const float* bc = a.proj + brow0 * ld + sh.off_c + grp * N;
+    const float* bv = a.proj + brow0 * ld + sh.off_v + h * P;
+    stage16(RB * tpr, Cl, [&](int i) { const int q = dtpr.q(i); return bc + (uint32_t)(q * ldi + 4 * (i - q * tpr)); });
+    stage4(RB * trows, vb, [&](int i) { const int q = dtr.q(i); return bv + (uint32_t)(q * ldi + tcol(i - q * trows)); });
   }
   if (sh.gdn) {
     if (t < nrows) {
@@ -326,8 +344,10 @@ __device__ __forceinline__ void round_tile(const Shape& sh, const RoundArgs& a, 
     const int first = nrows > W ? nrows - W : 0;
     T* K = ring_ptr<T>(a.state_pool, sh, slot, sh.st_k, h);
     T* V = ring_ptr<T>(a.state_pool, sh, slot, sh.st_v, h);
+    const int cw = mod_w(count, W);
     for (int tt = first; tt < nrows; ++tt) {
-      const int64_t s = (count + tt) % W;  // uniform
+      int s = cw + tt;
+      while (s >= W) s -= W;  // uniform
       for (int pp = t; pp < P; pp += RT) {
         K[s * P + pp] = from_f32<T>(a.proj[(crow0 + tt) * ld + sh.off_k + h * P + pp]);
         V[s * P + pp] = from_f32<T>(a.proj[(crow0 + tt) * ld + sh.off_v + h * P + pp]);
@@ -479,6 +499,167 @@ __device__ __forceinline__ void attn_split(const Shape& sh, int nk, int ks, bool
   }
 }
 
+// Attention of the 8 block rows over nk keys (at most ks, ks a multiple of 16, at most 128) of a
+// bf16 ring split, on bf16 matrix cores (16x16x16, fp32 accumulation), near fp32 accuracy: the
+// fp32 queries and probabilities enter as two bf16 terms each (hi = bf16(x), lo = bf16(x - hi),
+// together within 2^-16 of x), the ring's keys and values are bf16 already, and every product of
+// bf16 operands is exact in fp32.
+//   scores:  wave w takes key tiles w, w + 4 (16 keys each): S^T = K Q^T, A = 16 keys x 16 dims
+//            of K (LDS), B = 16 dims x 16 queries (rows 8..15 repeat rows 0..7 and go unused);
+//            lane l ends with keys 16 kt + 4 (l / 16) + r (r = 0..3) of query l % 16 in registers.
+//   softmax: the split's maximum per query over the four waves (LDS), then p = exp(s - max).
+//   values:  those registers are already the A operand of O = P V (query l % 16, keys
+//            4 (l / 16) + r of the tile), B = V[keys][16 dims], four 2-byte LDS reads per lane;
+//            the waves' products (same maximum) are summed through LDS in wave order.
+// Ring rows past nk may hold anything: their scores are replaced (not multiplied) by -inf, and
+// their value rows are zeroed first, since a zero probability times a NaN would not be zero.
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+__device__ __forceinline__ short bf16_bits(float v) { return __builtin_bit_cast(short, static_cast<bf16>(v)); }
+__device__ __forceinline__ float bf16_val(short b) { return static_cast<float>(__builtin_bit_cast(bf16, b)); }
+
+__device__ __forceinline__ void attn_split_mfma(const Shape& sh, int nk, int ks, float* qs, const bf16* K, bf16* V,
+                                                float* red, float* op, float* ml) {
+  const int P = sh.P, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int li = lane & 15, g = lane >> 4;
+  const float scale = rsqrtf((float)P);
+  const int nkt = ks / 16, npc = P / 16;
+  // ---- queries -> (hi, lo) bf16 pairs in place: qh [RB][P] then ql [RB][P] over the fp32 rows
+  constexpr int QE = RB * 256 / RT;  // elements per thread (P <= 256)
+  float qv[QE];
+#pragma unroll
+  for (int e = 0; e < QE; ++e) qv[e] = t + e * RT < RB * P ? qs[t + e * RT] : 0.f;
+  // value rows past nk: zero (16-byte stores)
+  if (nk < ks) {
+    uint4* vz = reinterpret_cast<uint4*>(V + (int64_t)nk * P);
+    const int n16 = (ks - nk) * P / 8;
+    for (int i = t; i < n16; i += RT) vz[i] = uint4{0u, 0u, 0u, 0u};
+  }
+  __syncthreads();
+  short* qh = reinterpret_cast<short*>(qs);
+  short* ql = qh + RB * P;
+#pragma unroll
+  for (int e = 0; e < QE; ++e) {
+    const int i = t + e * RT;
+    if (i < RB * P) {
+      const short hb = bf16_bits(qv[e]);
+      qh[i] = hb;
+      ql[i] = bf16_bits(qv[e] - bf16_val(hb));
+    }
+  }
+  __syncthreads();
+
+  // ---- scores of this wave's key tiles
+  const short* kb = reinterpret_cast<const short*>(K);
+  const int qrow = (li & 7) * P;
+  f32x4 s[2];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int kt = wave + 4 * j;
+    s[j] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    if (kt < nkt && 16 * kt < nk) {  // uniform
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      const short* kr = kb + (16 * kt + li) * P + 4 * g;
+      for (int c = 0; c < npc; ++c) {
+        const s16x4 a = *reinterpret_cast<const s16x4*>(kr + 16 * c);
+        const s16x4 bh = *reinterpret_cast<const s16x4*>(qh + qrow + 16 * c + 4 * g);
+        const s16x4 bl = *reinterpret_cast<const s16x4*>(ql + qrow + 16 * c + 4 * g);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, bh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, bl, acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        s[j][r] = 16 * kt + 4 * g + r < nk ? acc[r] * scale : -INFINITY;
+        mx = fmaxf(mx, s[j][r]);
+      }
+    }
+  }
+  // ---- softmax over the split: maximum over the lanes of query li, then over the waves
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  if (g == 0) red[wave * 16 + li] = mx;
+  __syncthreads();
+  const float m = fmaxf(fmaxf(red[li], red[16 + li]), fmaxf(red[32 + li], red[48 + li]));
+  float lsum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      s[j][r] = s[j][r] == -INFINITY ? 0.f : __expf(s[j][r] - m);
+      lsum += s[j][r];
+    }
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  if (g == 0) red[64 + wave * 16 + li] = lsum;
+  // probabilities as (hi, lo) A operands
+  s16x4 ph[2], pl[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const short hb = bf16_bits(s[j][r]);
+      ph[j][r] = hb;
+      pl[j][r] = bf16_bits(s[j][r] - bf16_val(hb));
+    }
+
+  // ---- O = P V in groups of up to PG dimension tiles; the waves' sums meet in the K region
+  float* ob = reinterpret_cast<float*>(const_cast<bf16*>(K));  // [4][RB][16 PG]
+  const short* vb = reinterpret_cast<const short*>(V);
+  constexpr int PG = 4;  // 16 accumulator registers: the kernel keeps six workgroups per CU
+  for (int c0 = 0; c0 < npc; c0 += PG) {
+    const int nc = npc - c0 < PG ? npc - c0 : PG;
+    f32x4 o[PG];
+#pragma unroll
+    for (int c = 0; c < PG; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int kt = wave + 4 * j;
+      if (kt < nkt && 16 * kt < nk) {  // uniform
+        const short* vr = vb + (16 * kt + 4 * g) * P + 16 * c0 + li;
+#pragma unroll
+        for (int c = 0; c < PG; ++c) {
+          if (c < nc) {
+            s16x4 b;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) b[r] = vr[r * P + 16 * c];
+            o[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph[j], b, o[c], 0, 0, 0);
+            o[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl[j], b, o[c], 0, 0, 0);
+          }
+        }
+      }
+    }
+    if (c0 > 0) __syncthreads();  // the previous group's sums are read
+    // lane l holds O[4 g + r][16 (c0 + c) + li]; rows 0..7 are the queries (g < 2)
+    const int gw = 16 * nc;
+    if (g < 2) {
+#pragma unroll
+      for (int c = 0; c < PG; ++c)
+        if (c < nc)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ob[(wave * RB + 4 * g + r) * gw + 16 * c + li] = o[c][r];
+    }
+    __syncthreads();
+    // wave w sums dimension tile c = w of the group, in the same lane layout
+    if (g < 2) {
+      {
+        const int c = wave;
+        if (c < nc) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int o0 = (4 * g + r) * gw + 16 * c + li, wst = RB * gw;
+            st_dev(op + (4 * g + r) * P + 16 * (c0 + c) + li, ob[o0] + ob[wst + o0] + ob[2 * wst + o0] + ob[3 * wst + o0]);
+          }
+        }
+      }
+    }
+  }
+  if (t < RB) {
+    const float mq = fmaxf(fmaxf(red[t], red[16 + t]), fmaxf(red[32 + t], red[48 + t]));
+    st_dev(ml + 2 * t, mq);
+    st_dev(ml + 2 * t + 1, red[64 + t] + red[80 + t] + red[96 + t] + red[112 + t]);
+  }
+}
+
 // Attention LDS (bytes): ring K, V of the split [ks][P] storage dtype (the block split: the block
 // rows' k, v [RB][P] f32 in the same places) | q [RB][P] f32 | probabilities [RB][ks + 4] |
 // scratch [128].
@@ -507,28 +688,37 @@ __device__ __forceinline__ void round_attn(const Shape& sh, const RoundArgs& a, 
   // Every load is independent of the committed count, so all go out together: q, the split's ring
   // slots (always inside the ring) or the block rows' k, v, and (into registers) the k, v of the
   // round's last committed rows, which replace the slots this round's append overwrites.
-  stage16(RB * P4, qs, [&](int i) { return a.proj + (brow0 + i / P4) * ld + sh.off_q + h * P + 4 * (i % P4); });
+  const Div& dP4 = a.d_p4;
+  const Div& dP = a.d_p;
+  const int ldi = (int)ld;  // rows of one job lie q ld floats apart (ld (RMAXC + RB) < 2^31 / 4)
+  const float* bq = a.proj + brow0 * ld + h * P;
+  stage16(RB * P4, qs, [&](int i) { const int q = dP4.q(i); return bq + (uint32_t)(sh.off_q + q * ldi + 4 * (i - q * P4)); });
   const int m = nrows < W ? nrows : W;  // committed rows that land in the ring
+  // the committed rows' k, v in registers: thread t holds column pc of rows jr, jr + rpp, ...
+  const int rpp = dP.q(RT);  // rows per pass (P <= 256)
+  const int jr = dP.q(t), pc = t - jr * P;
   float fk[FIX], fv[FIX];
   if (blk) {
     float* bk = reinterpret_cast<float*>(kst);
     float* bv = reinterpret_cast<float*>(vst);
-    stage16(RB * P4, bk, [&](int i) { return a.proj + (brow0 + i / P4) * ld + sh.off_k + h * P + 4 * (i % P4); });
-    stage16(RB * P4, bv, [&](int i) { return a.proj + (brow0 + i / P4) * ld + sh.off_v + h * P + 4 * (i % P4); });
+    stage16(RB * P4, bk, [&](int i) { const int q = dP4.q(i); return bq + (uint32_t)(sh.off_k + q * ldi + 4 * (i - q * P4)); });
+    stage16(RB * P4, bv, [&](int i) { const int q = dP4.q(i); return bq + (uint32_t)(sh.off_v + q * ldi + 4 * (i - q * P4)); });
   } else {
     const int nslots = W - k0 < ks ? W - k0 : ks;
     const T* K = ring_ptr<T>(a.state_pool, sh, slot, sh.st_k, h) + (int64_t)k0 * P;
     const T* V = ring_ptr<T>(a.state_pool, sh, slot, sh.st_v, h) + (int64_t)k0 * P;
-    stage16(nslots * P / VN, kst, [&](int i) { return K + i * VN; });
-    stage16(nslots * P / VN, vst, [&](int i) { return V + i * VN; });
+    stage16(nslots * P / VN, kst, [&](int i) { return K + (uint32_t)(i * VN); });
+    stage16(nslots * P / VN, vst, [&](int i) { return V + (uint32_t)(i * VN); });
+    const float* ck = a.proj + (crow0 + nrows - m) * ld + h * P;
 #pragma unroll
     for (int e = 0; e < FIX; ++e) {
-      const int idx = t + e * RT;
       fk[e] = fv[e] = 0.f;
-      if (idx < m * P) {
-        const int64_t row = crow0 + nrows - m + idx / P;
-        fk[e] = a.proj[row * ld + sh.off_k + h * P + idx % P];
-        fv[e] = a.proj[row * ld + sh.off_v + h * P + idx % P];
+      if (e * rpp < m) {  // uniform
+        const int j = jr + e * rpp;
+        if (jr < rpp && j < m) {
+          fk[e] = ck[(uint32_t)(sh.off_k + j * ldi + pc)];
+          fv[e] = ck[(uint32_t)(sh.off_v + j * ldi + pc)];
+        }
       }
     }
   }
@@ -558,23 +748,27 @@ __device__ __forceinline__ void round_attn(const Shape& sh, const RoundArgs& a, 
   if (m > 0) {
     // the slots this round's append overwrites take its rows, rounded as the ring stores them:
     // slot (count + nrows - m + j) mod W holds committed row nrows - m + j
-    const int lead = (int)((count + nrows - m) % W);
+    int lead = mod_w(count, W) + nrows - m;
+    while (lead >= W) lead -= W;  // uniform, at most RB / W + 1 steps
 #pragma unroll
     for (int e = 0; e < FIX; ++e) {
-      const int idx = t + e * RT;
-      if (idx < m * P) {
-        int key = lead + idx / P;
+      const int j = jr + e * rpp;
+      if (e * rpp < m && jr < rpp && j < m) {
+        int key = lead + j;
         if (key >= W) key -= W;
         key -= k0;
         if (key >= 0 && key < nk) {
-          kst[key * P + idx % P] = from_f32<T>(fk[e]);
-          vst[key * P + idx % P] = from_f32<T>(fv[e]);
+          kst[key * P + pc] = from_f32<T>(fk[e]);
+          vst[key * P + pc] = from_f32<T>(fv[e]);
         }
       }
     }
     __syncthreads();
   }
-  attn_split(sh, nk, ks, false, qs, kst, vst, pl, red, op, ml);
+  if constexpr (sizeof(T) == 2)
+    attn_split_mfma(sh, nk, ks, qs, kst, vst, red, op, ml);
+  else
+    attn_split(sh, nk, ks, false, qs, kst, vst, pl, red, op, ml);
 }
 
 // Merge of one (request, head).  The (max, sum) pairs and the readout are staged in LDS, and each
@@ -601,14 +795,16 @@ __device__ __forceinline__ void round_merge(const Shape& sh, const RoundArgs& a,
   const __amdgpu_buffer_rsrc_t rop = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(op), 0,
                                                                        ns * RB * P * 4, 0x00020000);
   stage16_dev(ns * RB * 2 / 4, sml, [&](int i) { return ml + 4 * i; });
-  stage16_dev(RB * P4, memv, [&](int i) { return a.mem + (((int64_t)r * RB + i / P4) * nh + h) * P + 4 * (i % P4); });
+  const Div& dP4 = a.d_p4;
+  const float* mrow = a.mem + ((int64_t)r * RB * nh + h) * P;  // row j of the readout: j nh P floats further
+  stage16_dev(RB * P4, memv, [&](int i) { const int q = dP4.q(i); return mrow + (uint32_t)(q * nh * P + 4 * (i - q * P4)); });
   T* out = static_cast<T*>(a.o_in);
   bool first = true;  // uniform: the factors are formed after the first round trip
   for (int e = 0; e < MQ; ++e) {
     if (e * RT >= RB * P4) break;  // uniform
     const int q = t + e * RT;      // this thread's group of 4 outputs: row q / P4, columns 4 (q % P4) ..
     const bool mine = q < RB * P4;
-    const int j = mine ? q / P4 : 0;
+    const int j = mine ? dP4.q(q) : 0;
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < ns; s0 += MSPL) {
       const int nc = ns - s0 < MSPL ? ns - s0 : MSPL;
@@ -647,7 +843,7 @@ __device__ __forceinline__ void round_merge(const Shape& sh, const RoundArgs& a,
       }
     }
     if (mine) {
-      const int pp = 4 * (q % P4);
+      const int pp = 4 * (q - j * P4);
       const float inv = 1.f / rowm[RB + j];
 #pragma unroll
       for (int c = 0; c < 4; ++c)
@@ -670,8 +866,8 @@ __device__ __forceinline__ void round_body(const Shape& sh, const RoundArgs& a, 
   const int per_xcd = (int)(gridDim.x / 8);
   const int item = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
   if (item >= rt.n_req * nh * per) return;
-  const int rh = item / per, role = item % per;
-  const int r = rh / nh, h = rh % nh;
+  const int rh = a.d_per.q(item), role = item - rh * per;
+  const int r = a.d_nh.q(rh), h = rh - r * nh;
   if (role < a.n_tiles)
     round_tile<T, TMAXG>(sh, a, rt, r, h, role, dsm);
   else
@@ -690,6 +886,305 @@ __device__ __forceinline__ void round_body(const Shape& sh, const RoundArgs& a, 
   // request has read the count by then
   if (threadIdx.x == 0 &&
       __hip_atomic_fetch_add(a.counters + rt.n_req * nh + r, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nh - 1)
+    *count_ptr(a.state_pool, sh, rt.slot[r]) += commit_rows(a, rt, r);
+}
+
+// ---------------------------------------------------------------------------------------------
+// One round with one workgroup per (request, head) (bf16, draft rounds over many pairs): the
+// commit / readout of the whole head (round_tile over all P rows, ring append included), then the
+// attention of the 8 block rows over the ring window streamed through LDS in chunks of PK = 64
+// slots (the next chunk's direct loads in flight while the current one is multiplied), with a
+// running softmax per wave on bf16 matrix cores, then the block keys, and the output written
+// directly: no partial results, no merge.
+//   scores:  wave w takes slots 16 w .. 16 w + 15 of every chunk: S^T = K Q^T (A = 16 slots x 16
+//            dims of K, B = 16 dims x 16 queries as (hi, lo) bf16 pairs; rows 8..15 repeat 0..7);
+//            lane l holds slots 16 w + 4 (l / 16) + r (r = 0..3) of query l % 16.
+//   values:  O^T += V^T P^T (A = 16 dims x 16 slots of V, four 2-byte LDS reads per lane; B = those
+//            probabilities as (hi, lo) pairs), so lane l's accumulators are dimensions
+//            16 c + 4 (l / 16) + r of query l % 16, and the running maximum rescales them in place.
+//   The ring rows this round's append overwrites are read from the projection instead (rounded
+//   as the ring stores them), so a chunk's contents do not depend on whether the append's stores
+//   have landed.  Rows past the window's valid slots are masked: their scores replaced by -inf,
+//   their value rows zeroed.
+constexpr int PK = 64;  // ring slots per chunk: 16 per wave
+template <typename T>
+struct PairLds {  // byte offsets: [tile region | the waves' tile buffers] then q, fk, fv, bk, bv, scratch
+  int q, fk, fv, bk, bv, red, total;
+  __host__ __device__ PairLds(const Shape& sh, int tile_bytes) {
+    const int chunks = 4 * 3 * 2 * 16 * sh.P * (int)sizeof(T);  // per wave: three tiles of K and V
+    int o = up1k(tile_bytes > chunks ? tile_bytes : chunks);
+    const int rows = up1k(RB * sh.P * 4);
+    q = o; o += rows;
+    fk = o; o += rows;
+    fv = o; o += rows;
+    bk = o; o += rows;
+    bv = o; o += rows;
+    red = o; o += 4 * 256;
+    total = o;
+  }
+};
+
+template <typename T>
+__device__ __forceinline__ void pair_body(const Shape& sh, const RoundArgs& a, const ReqTable& rt, int r, int h,
+                                          char* smem, int tile_bytes) {
+  const int nh = sh.nh, P = sh.P, W = sh.W, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int li = lane & 15, g = lane >> 4;
+  const int P4 = P / 4, npc = P / 16;
+  const PairLds<T> L(sh, tile_bytes);
+  float* qs = reinterpret_cast<float*>(smem + L.q);
+  float* fk = reinterpret_cast<float*>(smem + L.fk);
+  float* fv = reinterpret_cast<float*>(smem + L.fv);
+  float* bk = reinterpret_cast<float*>(smem + L.bk);
+  float* bv = reinterpret_cast<float*>(smem + L.bv);
+  float* red = reinterpret_cast<float*>(smem + L.red);  // [4][16] maxima | [4][16] sums | [8][8] block scores | factors
+  const int slot = rt.slot[r];
+  const int nrows = a.do_commit ? commit_rows(a, rt, r) : 0;
+  const int m = nrows < W ? nrows : W;  // committed rows that land in the ring
+  const int64_t crow0 = a.dev_rows ? (int64_t)RB * r : rt.row0[r];
+  const int64_t brow0 = a.blk_row0 + (int64_t)r * RB;
+  const int ldi = (int)a.ld;
+  const Div& dP4 = a.d_p4;
+  // the attention's inputs go out with the commit tile's loads (its wait covers them)
+  const float* bq = a.proj + brow0 * a.ld + h * P;
+  const float* cq = a.proj + (crow0 + nrows - m) * a.ld + h * P;
+  stage16(RB * P4, qs, [&](int i) { const int q = dP4.q(i); return bq + (uint32_t)(sh.off_q + q * ldi + 4 * (i - q * P4)); });
+  stage16(RB * P4, bk, [&](int i) { const int q = dP4.q(i); return bq + (uint32_t)(sh.off_k + q * ldi + 4 * (i - q * P4)); });
+  stage16(RB * P4, bv, [&](int i) { const int q = dP4.q(i); return bq + (uint32_t)(sh.off_v + q * ldi + 4 * (i - q * P4)); });
+  stage16(m * P4, fk, [&](int i) { const int q = dP4.q(i); return cq + (uint32_t)(sh.off_k + q * ldi + 4 * (i - q * P4)); });
+  stage16(m * P4, fv, [&](int i) { const int q = dP4.q(i); return cq + (uint32_t)(sh.off_v + q * ldi + 4 * (i - q * P4)); });
+  const int64_t count = *count_ptr(a.state_pool, sh, slot);
+
+  round_tile<T, WIDE_PASSES>(sh, a, rt, r, h, 0, smem);  // its readout goes to a.mem (device scope)
+  __syncthreads();  // the tile region is free
+
+  // ---- block keys: wave 0, lane = 8 q + key, exact fp32 scores (before q turns into bf16 pairs)
+  const float scale = rsqrtf((float)P);
+  float* sb = red + 128;
+  if (wave == 0) {
+    const int q = lane >> 3, key = lane & 7;
+    float acc = 0.f;
+    for (int p = 0; p < P; p += 4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(qs + q * P + p);
+      const f32x4 y = *reinterpret_cast<const f32x4*>(bk + key * P + p);
+      acc = fmaf(x[0], y[0], acc);
+      acc = fmaf(x[1], y[1], acc);
+      acc = fmaf(x[2], y[2], acc);
+      acc = fmaf(x[3], y[3], acc);
+    }
+    sb[lane] = (!sh.cross && key != q) ? -INFINITY : acc * scale;
+  }
+  // ---- queries -> (hi, lo) bf16 pairs in place
+  constexpr int QE = RB * 256 / RT;
+  float qv[QE];
+#pragma unroll
+  for (int e = 0; e < QE; ++e) qv[e] = t + e * RT < RB * P ? qs[t + e * RT] : 0.f;
+  __syncthreads();
+  short* qh = reinterpret_cast<short*>(qs);
+  short* ql = qh + RB * P;
+#pragma unroll
+  for (int e = 0; e < QE; ++e) {
+    const int i = t + e * RT;
+    if (i < RB * P) {
+      const short hb = bf16_bits(qv[e]);
+      qh[i] = hb;
+      ql[i] = bf16_bits(qv[e] - bf16_val(hb));
+    }
+  }
+
+  // ---- the ring window after this round's append: wave w streams slots 64 c + 16 w .. + 15 of
+  // every chunk c through its own three LDS buffers (two tiles in flight while one is multiplied);
+  // a tile is NI = ceil(P / 32) direct loads per operand for every wave and chunk (addresses past
+  // the ring clamped to its rows), so the waits are fixed counts and the waves never meet.
+  const int64_t tot = count + nrows;
+  const int valid = (int)(tot < W ? tot : W);
+  const int nch = (valid + PK - 1) / PK;
+  int lead = mod_w(count, W) + nrows - m;  // slot of committed row nrows - m
+  while (lead >= W) lead -= W;
+  const T* Kr = ring_ptr<T>(a.state_pool, sh, slot, sh.st_k, h);
+  const T* Vr = ring_ptr<T>(a.state_pool, sh, slot, sh.st_v, h);
+  const int tb = 16 * P * (int)sizeof(T);  // bytes of one 16-slot tile of K or V
+  const int NI = (P + 31) / 32;            // 1 KiB loads per tile (2 P 16-byte pieces)
+  auto tbuf = [&](int c) { return smem + (wave * 3 + c % 3) * 2 * tb; };
+  auto issue = [&](int c) {
+    // rows of this wave's tile that lie inside the ring (at least one: a tile past the ring
+    // re-reads the ring's last row)
+    const int row0 = PK * c + 16 * wave < W ? PK * c + 16 * wave : W - 1;
+    const int avail = W - row0 < 16 ? W - row0 : 16;
+    const int lim = avail * P * (int)sizeof(T) - 16;  // last whole 16-byte piece of those rows
+    const char* ks = reinterpret_cast<const char*>(Kr + (int64_t)row0 * P);
+    const char* vs = reinterpret_cast<const char*>(Vr + (int64_t)row0 * P);
+    char* dk = tbuf(c);
+#pragma unroll 1
+    for (int n = 0; n < NI; ++n) {
+      // lanes past the tile's 2 P pieces stay idle (the last load keeps at least 32 lanes)
+      const int b = 1024 * n + 16 * lane;
+      if (b < tb) {
+        lds_dma16(ks + (uint32_t)(b < lim ? b : lim), dk + 1024 * n);
+        lds_dma16(vs + (uint32_t)(b < lim ? b : lim), dk + tb + 1024 * n);
+      }
+    }
+  };
+  auto wait_tiles = [&](int pending) {  // this wave's loads of `pending` later tiles may stay out
+    const int n = pending * 2 * NI;
+    if (n >= 16) vm_wait<16>();
+    else if (n >= 12) vm_wait<12>();
+    else if (n >= 8) vm_wait<8>();
+    else if (n >= 6) vm_wait<6>();
+    else if (n >= 4) vm_wait<4>();
+    else if (n >= 2) vm_wait<2>();
+    else vm_wait<0>();
+  };
+  const int qrow = (li & 7) * P;
+  float mrun = -INFINITY, lrun = 0.f;
+  f32x4 o[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  vm_wait<0>();     // the commit's stores are out of the count: only tile loads from here on
+  __syncthreads();  // the tile region is free; the q pairs are published
+  if (nch > 0) issue(0);
+  if (nch > 1) issue(1);
+  for (int c = 0; c < nch; ++c) {
+    if (c + 2 < nch) issue(c + 2);  // buffer (c + 2) % 3 held tile c - 1, done above
+    wait_tiles(nch - 1 - c < 2 ? nch - 1 - c : 2);
+    const int nv = valid - PK * c < PK ? valid - PK * c : PK;
+    const int nw = nv - 16 * wave < 16 ? nv - 16 * wave : 16;  // valid slots of this wave's tile
+    if (nw <= 0) continue;          // uniform per wave
+    T* kc = reinterpret_cast<T*>(tbuf(c));
+    T* vc = reinterpret_cast<T*>(tbuf(c) + tb);
+    // this round's committed rows replace the slots the append overwrites; value rows past the
+    // valid ones are zeroed (a zero probability times a NaN would not be zero)
+    for (int j = 0; j < m; ++j) {  // uniform
+      int sl = lead + j;
+      if (sl >= W) sl -= W;
+      sl -= PK * c + 16 * wave;
+      if (sl >= 0 && sl < nw)
+        for (int p = lane; p < P; p += 64) {
+          kc[sl * P + p] = from_f32<T>(fk[j * P + p]);
+          vc[sl * P + p] = from_f32<T>(fv[j * P + p]);
+        }
+    }
+    if (nw < 16)
+      for (int i2 = lane; i2 < (16 - nw) * P; i2 += 64) vc[nw * P + i2] = from_f32<T>(0.f);
+    // scores of slots PK c + 16 wave + 4 g + r for query li (the wave's own LDS writes are ordered
+    // before its reads)
+    const short* kr = reinterpret_cast<const short*>(kc) + li * P + 4 * g;
+    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int cc = 0; cc < npc; ++cc) {
+      const s16x4 ka = *reinterpret_cast<const s16x4*>(kr + 16 * cc);
+      const s16x4 qb = *reinterpret_cast<const s16x4*>(qh + qrow + 16 * cc + 4 * g);
+      const s16x4 qc = *reinterpret_cast<const s16x4*>(ql + qrow + 16 * cc + 4 * g);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ka, qb, sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ka, qc, sacc, 0, 0, 0);
+    }
+    float sv[4], cm = -INFINITY;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      sv[rr] = 4 * g + rr < nw ? sacc[rr] * scale : -INFINITY;
+      cm = fmaxf(cm, sv[rr]);
+    }
+    cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
+    cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+    const float mnew = fmaxf(mrun, cm);  // finite: the tile's first slot is valid
+    const float alpha = mrun == -INFINITY ? 0.f : __expf(mrun - mnew);
+    mrun = mnew;
+    s16x4 ph, pl;
+    float ps = 0.f;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const float pv = sv[rr] == -INFINITY ? 0.f : __expf(sv[rr] - mnew);
+      ps += pv;
+      const short hb = bf16_bits(pv);
+      ph[rr] = hb;
+      pl[rr] = bf16_bits(pv - bf16_val(hb));
+    }
+    lrun = lrun * alpha + ps;
+    const short* vr = reinterpret_cast<const short*>(vc) + 4 * g * P + li;
+#pragma unroll
+    for (int cc = 0; cc < 16; ++cc) {
+      if (cc < npc) {
+        s16x4 va;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) va[rr] = vr[rr * P + 16 * cc];
+        o[cc] *= alpha;
+        o[cc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph, o[cc], 0, 0, 0);
+        o[cc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl, o[cc], 0, 0, 0);
+      }
+    }
+  }
+  // ---- the waves' (max, sum, O) and the block keys
+  lrun += __shfl_xor(lrun, 16, 64);
+  lrun += __shfl_xor(lrun, 32, 64);
+  if (g == 0) {
+    red[wave * 16 + li] = mrun;
+    red[64 + wave * 16 + li] = lrun;
+  }
+  vm_wait<0>();     // this thread's readout stores (round_tile) are complete before the reads below
+  __syncthreads();  // every chunk read is done: the chunk region takes the waves' O
+  float* ob = reinterpret_cast<float*>(smem);  // [4][RB][P]
+  if (li < RB) {
+#pragma unroll
+    for (int cc = 0; cc < 16; ++cc)
+      if (cc < npc)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) ob[(wave * RB + li) * P + 16 * cc + 4 * g + rr] = o[cc][rr];
+  }
+  float* fac = red + 192;  // [RB][8]: wave factors 0..3, 1 / sum at 4
+  float* fbk = red + 128;  // block scores -> block factors in place
+  if (t < RB) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, red[w * 16 + t]);
+#pragma unroll
+    for (int k = 0; k < RB; ++k) M = fmaxf(M, sb[t * RB + k]);
+    float Ls = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = red[w * 16 + t];
+      const float f = mw == -INFINITY ? 0.f : __expf(mw - M);
+      fac[t * 8 + w] = f;
+      Ls += f * red[64 + w * 16 + t];
+    }
+#pragma unroll
+    for (int k = 0; k < RB; ++k) {
+      const float sk = sb[t * RB + k];
+      const float f = sk == -INFINITY ? 0.f : __expf(sk - M);
+      fbk[t * RB + k] = f;
+      Ls += f;
+    }
+    fac[t * 8 + 4] = 1.f / Ls;
+  }
+  __syncthreads();
+  T* out = static_cast<T*>(a.o_in);
+  const Div& dP = a.d_p;
+  for (int i = t; i < RB * P; i += RT) {
+    const int q = dP.q(i), p = i - q * P;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) v += fac[q * 8 + w] * ob[(w * RB + q) * P + p];
+#pragma unroll
+    for (int k = 0; k < RB; ++k) v += fbk[q * RB + k] * bv[k * P + p];
+    const float mem = __hip_atomic_load(a.mem + (((int64_t)r * RB + q) * nh + h) * P + p, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+    out[((int64_t)r * RB + q) * sh.dq + h * P + p] = from_f32<T>(v * fac[q * 8 + 4] + mem);
+  }
+}
+
+// One (request, head) per workgroup; the last head of a request to finish advances its count.
+template <typename T>
+__global__ void __launch_bounds__(RT) __attribute__((amdgpu_waves_per_eu(2))) k_round_pair(Shape sh, RoundArgs a,
+                                                                                           ReqTable rt, int tile_bytes) {
+  extern __shared__ __attribute__((aligned(16))) char dsm[];
+  const int per_xcd = (int)(gridDim.x / 8);
+  const int item = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (item >= rt.n_req * sh.nh) return;
+  const int r = a.d_nh.q(item), h = item - r * sh.nh;
+  pair_body<T>(sh, a, rt, r, h, dsm, tile_bytes);
+  if (!a.do_commit) return;
+  vm_wait<0>();
+  __syncthreads();
+  if (threadIdx.x == 0 &&
+      __hip_atomic_fetch_add(a.counters + rt.n_req * sh.nh + r, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+          sh.nh - 1)
     *count_ptr(a.state_pool, sh, rt.slot[r]) += commit_rows(a, rt, r);
 }
 
@@ -875,10 +1370,13 @@ void round_layout(const Shape& sh, int n_req, int esz, RoundArgs* a) {
 }
 int round_max_splits(const Shape& sh) { return (sh.W + KS_MIN - 1) / KS_MIN + 1; }
 
+static size_t tile_lds_bytes(const Shape& sh, int rw) {
+  return (size_t)up1k(RMAXC * sh.N * 4) + up1k(RB * sh.N * 4) + up1k(RMAXC * rw * 4) + up1k(RB * rw * 4) +
+         4 * (3 * RMAXC + 4 + RB + RB * RT);
+}
+
 size_t round_lds_bytes(const Shape& sh, int esz, const RoundArgs& a) {
-  const int rw = a.tile_rows;
-  const size_t tile = (size_t)up1k(RMAXC * sh.N * 4) + up1k(RB * sh.N * 4) + up1k(RMAXC * rw * 4) + up1k(RB * rw * 4) +
-                      4 * (3 * RMAXC + 4 + RB + RB * RT);
+  const size_t tile = tile_lds_bytes(sh, a.tile_rows);
   const size_t attn = a.n_split ? (size_t)attn_lds(sh, esz, a.ks) : 0;
   const int ns = a.do_draft ? a.n_split : 0;
   const size_t merge = ns ? (size_t)up1k(ns * RB * 2 * 4) + up1k(ns * RB * 4) + 4 * 256 + up1k(RB * sh.P * 4) : 0;
@@ -911,7 +1409,55 @@ static hipError_t launch_round_t(const Shape& sh, const RoundArgs& a, const ReqT
   return hipGetLastError();
 }
 
-hipError_t launch_round(int dtype, const Shape& sh, const RoundArgs& a, const ReqTable& rt, hipStream_t s) {
+// The per-(request, head) kernel takes bf16 draft rounds over many pairs whose whole head fits one
+// tile (power-of-two threads per row of H, at most WIDE_PASSES passes) with two workgroups per CU.
+constexpr int PAIR_MAX_LDS = 80 * 1024;
+static hipError_t launch_round_pair(const Shape& sh, const RoundArgs& a0, const ReqTable& rt, hipStream_t s,
+                                    bool* taken) {
+  *taken = false;
+  const int tpr = sh.N / 4, rows_wg = RT / tpr;
+  const int passes = (sh.P + rows_wg - 1) / rows_wg;
+  if (!a0.do_draft || rt.n_req * sh.nh < WIDE_MIN_PAIRS || (tpr & (tpr - 1)) != 0 || passes > WIDE_PASSES)
+    return hipSuccess;
+  RoundArgs a = a0;
+  a.tile_rows = passes * rows_wg;
+  a.n_tiles = 1;
+  const int tile_bytes = (int)tile_lds_bytes(sh, a.tile_rows);
+  const PairLds<bf16> L(sh, tile_bytes);
+  if (L.total > PAIR_MAX_LDS) return hipSuccess;
+  *taken = true;
+  a.d_per = Div(1);
+  a.d_nh = Div(sh.nh);
+  a.d_p4 = Div(sh.P / 4);
+  a.d_p = Div(sh.P);
+  a.d_tpr = Div(tpr);
+  a.d_tr = Div(a.tile_rows);
+  static std::once_flag once;
+  static hipError_t set_err = hipSuccess;
+  std::call_once(once, [] {
+    set_err = hipFuncSetAttribute(reinterpret_cast<const void*>(k_round_pair<bf16>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, PAIR_MAX_LDS);
+  });
+  if (set_err != hipSuccess) return set_err;
+  const unsigned items = (unsigned)(rt.n_req * sh.nh);
+  hipLaunchKernelGGL(k_round_pair<bf16>, dim3((items + 7) / 8 * 8), dim3(RT), (size_t)L.total, s, sh, a, rt,
+                     tile_bytes);
+  return hipGetLastError();
+}
+
+hipError_t launch_round(int dtype, const Shape& sh, const RoundArgs& a0, const ReqTable& rt, hipStream_t s) {
+  if (dtype == HYF_BF16) {
+    bool taken = false;
+    const hipError_t e = launch_round_pair(sh, a0, rt, s, &taken);
+    if (taken || e != hipSuccess) return e;
+  }
+  RoundArgs a = a0;
+  a.d_per = Div(a.n_tiles + a.n_split);
+  a.d_nh = Div(sh.nh);
+  a.d_p4 = Div(sh.P / 4);
+  a.d_p = Div(sh.P);
+  a.d_tpr = Div(sh.N / 4);
+  a.d_tr = Div(a.tile_rows);
   const size_t lds = round_lds_bytes(sh, dtype == HYF_BF16 ? 2 : 4, a);
   if (lds > 160 * 1024 - 256) return hipErrorInvalidValue;
   const int rows_wg = RT / (sh.N / 4);

@@ -713,6 +713,10 @@ WIDE_SHAPES = [
     ("gdn_bf16", small_shape("bf16", window=100, memory="gdn")),
     ("odd_bf16", small_shape("bf16", n_heads=5, head_dim=48, d_state=32, n_groups=5, window=20, chunk=32)),
     ("noncross_fp32", small_shape("f32", window=24, cross_slot=0)),
+    # bf16 draft rounds over 256+ (request, head) pairs take one workgroup per pair: block rows
+    # that see only themselves, the last-W memory, a window of one 64-slot chunk plus one slot
+    ("noncross_bf16", small_shape("bf16", window=65, cross_slot=0)),
+    ("lastw_bf16", small_shape("bf16", window=72, memory="lastw")),
     # heads of 128 dimensions over 256 (request, head) pairs: the wide layout (whole-head tiles,
     # 128-key splits)
     ("wide_p128_bf16", small_shape("bf16", head_dim=128, window=300)),
