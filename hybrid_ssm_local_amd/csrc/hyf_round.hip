@@ -908,29 +908,36 @@ __device__ __forceinline__ void round_body(const Shape& sh, const RoundArgs& a, 
 //   their value rows zeroed.
 constexpr int PK = 64;  // ring slots per chunk: 16 per wave
 template <typename T>
-struct PairLds {  // byte offsets: [tile region | the waves' tile buffers] then q, fk, fv, bk, bv, scratch
-  int q, fk, fv, bk, bv, red, total;
-  __host__ __device__ PairLds(const Shape& sh, int tile_bytes) {
+struct PairLds {  // byte offsets: [commit region | the waves' tile buffers] then q, fk, fv, bk, bv, memv, scratch
+  int q, fk, fv, bk, bv, memv, red, total;
+  __host__ __device__ PairLds(const Shape& sh, int commit_bytes, bool m2) {
     const int chunks = 4 * 3 * 2 * 16 * sh.P * (int)sizeof(T);  // per wave: three tiles of K and V
-    int o = up1k(tile_bytes > chunks ? tile_bytes : chunks);
+    int o = up1k(commit_bytes > chunks ? commit_bytes : chunks);
     const int rows = up1k(RB * sh.P * 4);
     q = o; o += rows;
     fk = o; o += rows;
     fv = o; o += rows;
     bk = o; o += rows;
     bv = o; o += rows;
+    memv = o; o += m2 ? rows : 0;
     red = o; o += 4 * 256;
     total = o;
   }
 };
+// Commit region of the Mamba-2 pair kernel: B of the committed rows [RB][N] | C of the block rows
+// [RB][N] | the waves' readout partials [4][P][RB], all fp32.
+__host__ __device__ constexpr int m2_commit_bytes(int P, int N) { return 2 * up1k(RB * N * 4) + up1k(4 * P * RB * 4); }
 
-template <typename T>
+// NPC: dimension tiles of a head (P = 16 NPC) fixed at compile time, or 0 (P from the shape).
+// M2: the Mamba-2 commit and readout on fp32 matrix cores (NBW column blocks of H per wave) instead
+// of round_tile (which also serves the gated delta rule and the last-W memory).
+template <typename T, int NPC, bool M2, int NBW>
 __device__ __forceinline__ void pair_body(const Shape& sh, const RoundArgs& a, const ReqTable& rt, int r, int h,
-                                          char* smem, int tile_bytes) {
-  const int nh = sh.nh, P = sh.P, W = sh.W, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+                                          char* smem, int commit_bytes) {
+  const int nh = sh.nh, P = NPC ? 16 * NPC : sh.P, W = sh.W, N = sh.N, t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int li = lane & 15, g = lane >> 4;
-  const int P4 = P / 4, npc = P / 16;
-  const PairLds<T> L(sh, tile_bytes);
+  const int P4 = P / 4, npc = NPC ? NPC : P / 16;
+  const PairLds<T> L(sh, commit_bytes, M2);
   float* qs = reinterpret_cast<float*>(smem + L.q);
   float* fk = reinterpret_cast<float*>(smem + L.fk);
   float* fv = reinterpret_cast<float*>(smem + L.fv);
@@ -953,9 +960,131 @@ __device__ __forceinline__ void pair_body(const Shape& sh, const RoundArgs& a, c
   stage16(m * P4, fk, [&](int i) { const int q = dP4.q(i); return cq + (uint32_t)(sh.off_k + q * ldi + 4 * (i - q * P4)); });
   stage16(m * P4, fv, [&](int i) { const int q = dP4.q(i); return cq + (uint32_t)(sh.off_v + q * ldi + 4 * (i - q * P4)); });
   const int64_t count = *count_ptr(a.state_pool, sh, slot);
-
-  round_tile<T, WIDE_PASSES>(sh, a, rt, r, h, 0, smem);  // its readout goes to a.mem (device scope)
-  __syncthreads();  // the tile region is free
+  float* memv = reinterpret_cast<float*>(smem + L.memv);  // [RB][P] readout (M2)
+  if constexpr (!M2) {
+    round_tile<T, WIDE_PASSES>(sh, a, rt, r, h, 0, smem);  // its readout goes to a.mem (device scope)
+  } else {
+    // ---- Mamba-2 commit and readout on fp32 matrix cores (16x16x4: exact products, fp32 sums).
+    // H^T is held in 16 x 16 blocks (state columns n x rows p of H) in the accumulator layout:
+    // lane (li, g) holds H[16 pb + li][16 nb + 4 g + r], r = 0..3, one 16-byte piece of a row of H,
+    // so a block loads and stores with one access per lane.  Wave w owns column blocks w, w + 4,
+    // ... of every row block.
+    //   commit:  H^T <- dec H^T + B^T (w x)  (A: lane holds B_t[16 nb + li] for row t = 4 s + g;
+    //            B: w_t x_t[16 pb + li]; two steps of four committed rows).
+    //   readout: Y^T[p][j] = sum_n H[p][n] C_j[n], four steps per block with A = the lane's
+    //            register r (row li, column 16 nb + 4 g + r) and B = C_li[16 nb + 4 g + r]; the waves'
+    //            partial sums over their columns meet in LDS.
+    const int NB = N / 16;
+    constexpr int PB = NPC;
+    float* Bl = reinterpret_cast<float*>(smem);
+    float* Cl = reinterpret_cast<float*>(smem + up1k(RB * N * 4));
+    float* part = reinterpret_cast<float*>(smem + 2 * up1k(RB * N * 4));  // [4][P][RB]
+    float* wl = red;  // weights of the committed rows, the old state's decay at RMAXC
+    const int grp = h / (nh / sh.G);
+    float* Hh = h_ptr(a.state_pool, sh, slot, h);
+    f32x4 hreg[PB][NBW];
+#pragma unroll
+    for (int pb = 0; pb < PB; ++pb)
+#pragma unroll
+      for (int b = 0; b < NBW; ++b) {
+        const int nb = wave + 4 * b;
+        hreg[pb][b] = nb < NB ? *reinterpret_cast<const f32x4*>(Hh + (16 * pb + li) * N + 16 * nb + 4 * g)
+                              : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    const int N4 = N / 4;
+    const float* cb = a.proj + crow0 * a.ld + sh.off_b + grp * N;
+    const float* bc = a.proj + brow0 * a.ld + sh.off_c + grp * N;
+    stage16(nrows * N4, Bl, [&](int i) { const int q = a.d_tpr.q(i); return cb + (uint32_t)(q * ldi + 4 * (i - q * N4)); });
+    stage16(RB * N4, Cl, [&](int i) { const int q = a.d_tpr.q(i); return bc + (uint32_t)(q * ldi + 4 * (i - q * N4)); });
+    const float raw = t < nrows ? a.proj[(crow0 + t) * a.ld + sh.off_dt + h] : 0.f;
+    vm_wait<0>();
+    __syncthreads();
+    if (t < 64) {
+      // w_t = dt_t exp(sum_{tau > t} dt_tau A) and the decay exp(sum_t dt_t A); lane t holds row t
+      const float A = -expf(a.a_log[h]);
+      const float dt = t < nrows ? softplus_f(raw + a.dt_bias[h]) : 0.f;
+      const float ell = dt * A;
+      float inc = ell;
+#pragma unroll
+      for (int o = 1; o < RMAXC; o <<= 1) {
+        const float v = __shfl_down(inc, o, 64);
+        if (t + o < RMAXC) inc += v;
+      }
+      if (t < nrows) wl[t] = dt * expf(inc - ell);
+      if (t == 0) wl[RMAXC] = expf(inc);
+    }
+    __syncthreads();
+    if (nrows > 0) {
+      const float dec = wl[RMAXC];
+      float bw[2][PB];  // w_t x_t[16 pb + li] for t = 4 s + g
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int tt = 4 * s2 + g;
+#pragma unroll
+        for (int pb = 0; pb < PB; ++pb) bw[s2][pb] = tt < nrows ? wl[tt] * fv[tt * P + 16 * pb + li] : 0.f;
+      }
+#pragma unroll
+      for (int b = 0; b < NBW; ++b) {
+        const int nb = wave + 4 * b;
+        if (nb < NB) {  // uniform
+          float ba[2];
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const int tt = 4 * s2 + g;
+            ba[s2] = tt < nrows ? Bl[tt * N + 16 * nb + li] : 0.f;
+          }
+#pragma unroll
+          for (int pb = 0; pb < PB; ++pb) {
+            f32x4 acc = hreg[pb][b] * dec;
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ba[0], bw[0][pb], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ba[1], bw[1][pb], acc, 0, 0, 0);
+            hreg[pb][b] = acc;
+            *reinterpret_cast<f32x4*>(Hh + (16 * pb + li) * N + 16 * nb + 4 * g) = acc;
+          }
+        }
+      }
+    }
+    // readout partials of this wave's columns
+#pragma unroll
+    for (int pb = 0; pb < PB; ++pb) {
+      f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int b = 0; b < NBW; ++b) {
+        const int nb = wave + 4 * b;
+        if (nb < NB) {
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            y = __builtin_amdgcn_mfma_f32_16x16x4f32(hreg[pb][b][rr], Cl[(li & 7) * N + 16 * nb + 4 * g + rr], y, 0, 0, 0);
+        }
+      }
+      // lane (li, g) holds Y^T[16 pb + 4 g + rr][li]; queries li < RB are the block rows
+      if (li < RB)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) part[(wave * P + 16 * pb + 4 * g + rr) * RB + li] = y[rr];
+    }
+    __syncthreads();
+    const float D = a.d_skip[h];
+    for (int i = t; i < RB * P; i += RT) {
+      const int j = i / P, p = i - j * P;  // P is a compile-time constant here
+      memv[i] = part[(0 * P + p) * RB + j] + part[(1 * P + p) * RB + j] + part[(2 * P + p) * RB + j] +
+                part[(3 * P + p) * RB + j] + D * bv[j * P + p];
+    }
+    // ring append of this round's rows (the last m), from the staged projection rows
+    if (nrows > 0) {
+      T* Kw = ring_ptr<T>(a.state_pool, sh, slot, sh.st_k, h);
+      T* Vw = ring_ptr<T>(a.state_pool, sh, slot, sh.st_v, h);
+      int s0 = mod_w(count, W) + nrows - m;
+      while (s0 >= W) s0 -= W;
+      for (int j = 0; j < m; ++j) {  // uniform
+        const int sl = s0 + j >= W ? s0 + j - W : s0 + j;
+        for (int p = t; p < P; p += RT) {
+          Kw[sl * P + p] = from_f32<T>(fk[j * P + p]);
+          Vw[sl * P + p] = from_f32<T>(fv[j * P + p]);
+        }
+      }
+    }
+  }
+  __syncthreads();  // the commit region is free
 
   // ---- block keys: wave 0, lane = 8 q + key, exact fp32 scores (before q turns into bf16 pairs)
   const float scale = rsqrtf((float)P);
@@ -1155,30 +1284,33 @@ __device__ __forceinline__ void pair_body(const Shape& sh, const RoundArgs& a, c
   }
   __syncthreads();
   T* out = static_cast<T*>(a.o_in);
-  const Div& dP = a.d_p;
   for (int i = t; i < RB * P; i += RT) {
-    const int q = dP.q(i), p = i - q * P;
+    const int q = NPC ? i / P : a.d_p.q(i), p = i - q * P;
     float v = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) v += fac[q * 8 + w] * ob[(w * RB + q) * P + p];
 #pragma unroll
     for (int k = 0; k < RB; ++k) v += fbk[q * RB + k] * bv[k * P + p];
-    const float mem = __hip_atomic_load(a.mem + (((int64_t)r * RB + q) * nh + h) * P + p, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT);
+    float mem;
+    if constexpr (M2)
+      mem = memv[i];
+    else
+      mem = __hip_atomic_load(a.mem + (((int64_t)r * RB + q) * nh + h) * P + p, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
     out[((int64_t)r * RB + q) * sh.dq + h * P + p] = from_f32<T>(v * fac[q * 8 + 4] + mem);
   }
 }
 
 // One (request, head) per workgroup; the last head of a request to finish advances its count.
-template <typename T>
+template <typename T, int NPC, bool M2, int NBW>
 __global__ void __launch_bounds__(RT) __attribute__((amdgpu_waves_per_eu(2))) k_round_pair(Shape sh, RoundArgs a,
-                                                                                           ReqTable rt, int tile_bytes) {
+                                                                                           ReqTable rt, int commit_bytes) {
   extern __shared__ __attribute__((aligned(16))) char dsm[];
   const int per_xcd = (int)(gridDim.x / 8);
   const int item = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
   if (item >= rt.n_req * sh.nh) return;
   const int r = a.d_nh.q(item), h = item - r * sh.nh;
-  pair_body<T>(sh, a, rt, r, h, dsm, tile_bytes);
+  pair_body<T, NPC, M2, NBW>(sh, a, rt, r, h, dsm, commit_bytes);
   if (!a.do_commit) return;
   vm_wait<0>();
   __syncthreads();
@@ -1409,21 +1541,46 @@ static hipError_t launch_round_t(const Shape& sh, const RoundArgs& a, const ReqT
   return hipGetLastError();
 }
 
-// The per-(request, head) kernel takes bf16 draft rounds over many pairs whose whole head fits one
-// tile (power-of-two threads per row of H, at most WIDE_PASSES passes) with two workgroups per CU.
+// The per-(request, head) kernels take bf16 draft rounds over many pairs with two workgroups per
+// CU: the Mamba-2 memory with heads of 48, 64 or 80 dimensions and up to 128 state columns on the
+// matrix-core commit; otherwise (gated delta rule, last-W memory, other heads) round_tile's commit
+// where its whole head fits one tile (power-of-two threads per row of H, at most WIDE_PASSES passes).
 constexpr int PAIR_MAX_LDS = 80 * 1024;
+template <int NPC, bool M2, int NBW>
+static hipError_t launch_pair_t(const Shape& sh, const RoundArgs& a, const ReqTable& rt, int commit_bytes,
+                                size_t lds, hipStream_t s) {
+  auto kern = k_round_pair<bf16, NPC, M2, NBW>;
+  static std::once_flag once;
+  static hipError_t set_err = hipSuccess;
+  std::call_once(once, [kern] {
+    set_err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  PAIR_MAX_LDS);
+  });
+  if (set_err != hipSuccess) return set_err;
+  const unsigned items = (unsigned)(rt.n_req * sh.nh);
+  hipLaunchKernelGGL(kern, dim3((items + 7) / 8 * 8), dim3(RT), lds, s, sh, a, rt, commit_bytes);
+  return hipGetLastError();
+}
+
 static hipError_t launch_round_pair(const Shape& sh, const RoundArgs& a0, const ReqTable& rt, hipStream_t s,
                                     bool* taken) {
   *taken = false;
+  if (!a0.do_draft || rt.n_req * sh.nh < WIDE_MIN_PAIRS || sh.W < RB) return hipSuccess;
   const int tpr = sh.N / 4, rows_wg = RT / tpr;
-  const int passes = (sh.P + rows_wg - 1) / rows_wg;
-  if (!a0.do_draft || rt.n_req * sh.nh < WIDE_MIN_PAIRS || (tpr & (tpr - 1)) != 0 || passes > WIDE_PASSES)
-    return hipSuccess;
+  const int npc = sh.P / 16, nb = sh.N / 16;
+  const bool m2 = !sh.gdn && !sh.lastw && npc >= 3 && npc <= 5 && nb <= 8;
   RoundArgs a = a0;
-  a.tile_rows = passes * rows_wg;
-  a.n_tiles = 1;
-  const int tile_bytes = (int)tile_lds_bytes(sh, a.tile_rows);
-  const PairLds<bf16> L(sh, tile_bytes);
+  int commit_bytes;
+  if (m2) {
+    commit_bytes = m2_commit_bytes(sh.P, sh.N);
+  } else {
+    const int passes = (sh.P + rows_wg - 1) / rows_wg;
+    if ((tpr & (tpr - 1)) != 0 || passes > WIDE_PASSES) return hipSuccess;
+    a.tile_rows = passes * rows_wg;
+    a.n_tiles = 1;
+    commit_bytes = (int)tile_lds_bytes(sh, a.tile_rows);
+  }
+  const PairLds<bf16> L(sh, commit_bytes, m2);
   if (L.total > PAIR_MAX_LDS) return hipSuccess;
   *taken = true;
   a.d_per = Div(1);
@@ -1431,18 +1588,18 @@ static hipError_t launch_round_pair(const Shape& sh, const RoundArgs& a0, const 
   a.d_p4 = Div(sh.P / 4);
   a.d_p = Div(sh.P);
   a.d_tpr = Div(tpr);
-  a.d_tr = Div(a.tile_rows);
-  static std::once_flag once;
-  static hipError_t set_err = hipSuccess;
-  std::call_once(once, [] {
-    set_err = hipFuncSetAttribute(reinterpret_cast<const void*>(k_round_pair<bf16>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, PAIR_MAX_LDS);
-  });
-  if (set_err != hipSuccess) return set_err;
-  const unsigned items = (unsigned)(rt.n_req * sh.nh);
-  hipLaunchKernelGGL(k_round_pair<bf16>, dim3((items + 7) / 8 * 8), dim3(RT), (size_t)L.total, s, sh, a, rt,
-                     tile_bytes);
-  return hipGetLastError();
+  a.d_tr = Div(a.tile_rows > 0 ? a.tile_rows : 1);
+  const size_t lds = (size_t)L.total;
+  if (!m2) return launch_pair_t<0, false, 1>(sh, a, rt, commit_bytes, lds, s);
+  const bool two = nb > 4;
+  switch (npc) {
+    case 3: return two ? launch_pair_t<3, true, 2>(sh, a, rt, commit_bytes, lds, s)
+                       : launch_pair_t<3, true, 1>(sh, a, rt, commit_bytes, lds, s);
+    case 4: return two ? launch_pair_t<4, true, 2>(sh, a, rt, commit_bytes, lds, s)
+                       : launch_pair_t<4, true, 1>(sh, a, rt, commit_bytes, lds, s);
+    default: return two ? launch_pair_t<5, true, 2>(sh, a, rt, commit_bytes, lds, s)
+                        : launch_pair_t<5, true, 1>(sh, a, rt, commit_bytes, lds, s);
+  }
 }
 
 hipError_t launch_round(int dtype, const Shape& sh, const RoundArgs& a0, const ReqTable& rt, hipStream_t s) {
