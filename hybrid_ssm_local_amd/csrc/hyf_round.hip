@@ -908,11 +908,13 @@ __device__ __forceinline__ void round_body(const Shape& sh, const RoundArgs& a, 
 //   their value rows zeroed.
 constexpr int PK = 64;  // ring slots per chunk: 16 per wave
 template <typename T>
-struct PairLds {  // byte offsets: [commit region | the waves' tile buffers] then q, fk, fv, bk, bv, memv, scratch
-  int q, fk, fv, bk, bv, memv, red, total;
+struct PairLds {  // byte offsets: [tile buffers 0, 1 | buffer 2 or the commit region] then q, fk, fv, bk, bv, memv, scratch
+  int commit, q, fk, fv, bk, bv, memv, red, total;
   __host__ __device__ PairLds(const Shape& sh, int commit_bytes, bool m2) {
-    const int chunks = 4 * 3 * 2 * 16 * sh.P * (int)sizeof(T);  // per wave: three tiles of K and V
-    int o = up1k(commit_bytes > chunks ? commit_bytes : chunks);
+    const int slot = 4 * 2 * 16 * sh.P * (int)sizeof(T);  // one tile of K and V for each of the four waves
+    commit = 2 * slot;  // buffers 0 and 1 fill while the commit runs
+    const int a = commit + (commit_bytes > slot ? commit_bytes : slot);
+    int o = up1k(a);
     const int rows = up1k(RB * sh.P * 4);
     q = o; o += rows;
     fk = o; o += rows;
@@ -961,8 +963,36 @@ __device__ __forceinline__ void pair_body(const Shape& sh, const RoundArgs& a, c
   stage16(m * P4, fv, [&](int i) { const int q = dP4.q(i); return cq + (uint32_t)(sh.off_v + q * ldi + 4 * (i - q * P4)); });
   const int64_t count = *count_ptr(a.state_pool, sh, slot);
   float* memv = reinterpret_cast<float*>(smem + L.memv);  // [RB][P] readout (M2)
+  // the first two ring tiles of every wave go out with these loads (see the attention below)
+  const T* Kr = ring_ptr<T>(a.state_pool, sh, slot, sh.st_k, h);
+  const T* Vr = ring_ptr<T>(a.state_pool, sh, slot, sh.st_v, h);
+  const int tb = 16 * P * (int)sizeof(T);  // bytes of one 16-slot tile of K or V
+  const int NI = (P + 31) / 32;            // 1 KiB loads per tile (2 P 16-byte pieces)
+  auto tbuf = [&](int c) { return smem + ((c % 3) * 4 + wave) * 2 * tb; };
+  auto issue = [&](int c) {
+    // rows of this wave's tile that lie inside the ring (at least one: a tile past the ring
+    // re-reads the ring's last row); the slots' validity is decided later, from the count
+    const int row0 = PK * c + 16 * wave < W ? PK * c + 16 * wave : W - 1;
+    const int avail = W - row0 < 16 ? W - row0 : 16;
+    const int lim = avail * P * (int)sizeof(T) - 16;  // last whole 16-byte piece of those rows
+    const char* ks = reinterpret_cast<const char*>(Kr + (int64_t)row0 * P);
+    const char* vs = reinterpret_cast<const char*>(Vr + (int64_t)row0 * P);
+    char* dk = tbuf(c);
+#pragma unroll 1
+    for (int n = 0; n < NI; ++n) {
+      // lanes past the tile's 2 P pieces stay idle (the last load keeps at least 32 lanes)
+      const int b = 1024 * n + 16 * lane;
+      if (b < tb) {
+        lds_dma16(ks + (uint32_t)(b < lim ? b : lim), dk + 1024 * n);
+        lds_dma16(vs + (uint32_t)(b < lim ? b : lim), dk + tb + 1024 * n);
+      }
+    }
+  };
+  issue(0);
+  issue(1);
+  char* creg = smem + L.commit;
   if constexpr (!M2) {
-    round_tile<T, WIDE_PASSES>(sh, a, rt, r, h, 0, smem);  // its readout goes to a.mem (device scope)
+    round_tile<T, WIDE_PASSES>(sh, a, rt, r, h, 0, creg);  // its readout goes to a.mem (device scope)
   } else {
     // ---- Mamba-2 commit and readout on fp32 matrix cores (16x16x4: exact products, fp32 sums).
     // H^T is held in 16 x 16 blocks (state columns n x rows p of H) in the accumulator layout:
@@ -976,9 +1006,9 @@ __device__ __forceinline__ void pair_body(const Shape& sh, const RoundArgs& a, c
     //            partial sums over their columns meet in LDS.
     const int NB = N / 16;
     constexpr int PB = NPC;
-    float* Bl = reinterpret_cast<float*>(smem);
-    float* Cl = reinterpret_cast<float*>(smem + up1k(RB * N * 4));
-    float* part = reinterpret_cast<float*>(smem + 2 * up1k(RB * N * 4));  // [4][P][RB]
+    float* Bl = reinterpret_cast<float*>(creg);
+    float* Cl = reinterpret_cast<float*>(creg + up1k(RB * N * 4));
+    float* part = reinterpret_cast<float*>(creg + 2 * up1k(RB * N * 4));  // [4][P][RB]
     float* wl = red;  // weights of the committed rows, the old state's decay at RMAXC
     const int grp = h / (nh / sh.G);
     float* Hh = h_ptr(a.state_pool, sh, slot, h);
@@ -1121,38 +1151,15 @@ __device__ __forceinline__ void pair_body(const Shape& sh, const RoundArgs& a, c
   }
 
   // ---- the ring window after this round's append: wave w streams slots 64 c + 16 w .. + 15 of
-  // every chunk c through its own three LDS buffers (two tiles in flight while one is multiplied);
-  // a tile is NI = ceil(P / 32) direct loads per operand for every wave and chunk (addresses past
-  // the ring clamped to its rows), so the waits are fixed counts and the waves never meet.
+  // every chunk c through three LDS buffers of its own (two tiles in flight while one is
+  // multiplied; tiles 0 and 1 went out with the commit's loads); a tile is NI = ceil(P / 32) direct
+  // loads per operand for every wave and chunk (addresses past the ring clamped to its rows), so
+  // the waits are fixed counts and the waves never meet.
   const int64_t tot = count + nrows;
   const int valid = (int)(tot < W ? tot : W);
   const int nch = (valid + PK - 1) / PK;
   int lead = mod_w(count, W) + nrows - m;  // slot of committed row nrows - m
   while (lead >= W) lead -= W;
-  const T* Kr = ring_ptr<T>(a.state_pool, sh, slot, sh.st_k, h);
-  const T* Vr = ring_ptr<T>(a.state_pool, sh, slot, sh.st_v, h);
-  const int tb = 16 * P * (int)sizeof(T);  // bytes of one 16-slot tile of K or V
-  const int NI = (P + 31) / 32;            // 1 KiB loads per tile (2 P 16-byte pieces)
-  auto tbuf = [&](int c) { return smem + (wave * 3 + c % 3) * 2 * tb; };
-  auto issue = [&](int c) {
-    // rows of this wave's tile that lie inside the ring (at least one: a tile past the ring
-    // re-reads the ring's last row)
-    const int row0 = PK * c + 16 * wave < W ? PK * c + 16 * wave : W - 1;
-    const int avail = W - row0 < 16 ? W - row0 : 16;
-    const int lim = avail * P * (int)sizeof(T) - 16;  // last whole 16-byte piece of those rows
-    const char* ks = reinterpret_cast<const char*>(Kr + (int64_t)row0 * P);
-    const char* vs = reinterpret_cast<const char*>(Vr + (int64_t)row0 * P);
-    char* dk = tbuf(c);
-#pragma unroll 1
-    for (int n = 0; n < NI; ++n) {
-      // lanes past the tile's 2 P pieces stay idle (the last load keeps at least 32 lanes)
-      const int b = 1024 * n + 16 * lane;
-      if (b < tb) {
-        lds_dma16(ks + (uint32_t)(b < lim ? b : lim), dk + 1024 * n);
-        lds_dma16(vs + (uint32_t)(b < lim ? b : lim), dk + tb + 1024 * n);
-      }
-    }
-  };
   auto wait_tiles = [&](int pending) {  // this wave's loads of `pending` later tiles may stay out
     const int n = pending * 2 * NI;
     if (n >= 16) vm_wait<16>();
@@ -1169,9 +1176,7 @@ __device__ __forceinline__ void pair_body(const Shape& sh, const RoundArgs& a, c
 #pragma unroll
   for (int c = 0; c < 16; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
   vm_wait<0>();     // the commit's stores are out of the count: only tile loads from here on
-  __syncthreads();  // the tile region is free; the q pairs are published
-  if (nch > 0) issue(0);
-  if (nch > 1) issue(1);
+  __syncthreads();  // the commit region (buffer 2) is free; the q pairs are published
   for (int c = 0; c < nch; ++c) {
     if (c + 2 < nch) issue(c + 2);  // buffer (c + 2) % 3 held tile c - 1, done above
     wait_tiles(nch - 1 - c < 2 ? nch - 1 - c : 2);
