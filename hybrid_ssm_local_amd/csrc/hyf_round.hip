@@ -911,9 +911,10 @@ template <typename T>
 struct PairLds {  // byte offsets: [tile buffers 0, 1 | buffer 2 or the commit region] then q, fk, fv, bk, bv, memv, scratch
   int commit, q, fk, fv, bk, bv, memv, red, total;
   __host__ __device__ PairLds(const Shape& sh, int commit_bytes, bool m2) {
+    // the Mamba-2 kernel keeps its ring tiles in registers; the other streams them through LDS
     const int slot = 4 * 2 * 16 * sh.P * (int)sizeof(T);  // one tile of K and V for each of the four waves
-    commit = 2 * slot;  // buffers 0 and 1 fill while the commit runs
-    const int a = commit + (commit_bytes > slot ? commit_bytes : slot);
+    commit = m2 ? 0 : 2 * slot;  // LDS buffers 0 and 1 fill while the commit runs
+    const int a = m2 ? commit_bytes : commit + (commit_bytes > slot ? commit_bytes : slot);
     int o = up1k(a);
     const int rows = up1k(RB * sh.P * 4);
     q = o; o += rows;
@@ -988,8 +989,10 @@ __device__ __forceinline__ void pair_body(const Shape& sh, const RoundArgs& a, c
       }
     }
   };
-  issue(0);
-  issue(1);
+  if constexpr (!M2) {
+    issue(0);
+    issue(1);
+  }
   char* creg = smem + L.commit;
   if constexpr (!M2) {
     round_tile<T, WIDE_PASSES>(sh, a, rt, r, h, 0, creg);  // its readout goes to a.mem (device scope)
@@ -1160,6 +1163,147 @@ __device__ __forceinline__ void pair_body(const Shape& sh, const RoundArgs& a, c
   const int nch = (valid + PK - 1) / PK;
   int lead = mod_w(count, W) + nrows - m;  // slot of committed row nrows - m
   while (lead >= W) lead -= W;
+  const int qrow = (li & 7) * P;
+  float mrun = -INFINITY, lrun = 0.f;
+  f32x4 o[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (M2) {
+    // Ring tiles straight into registers: lane (li, g) of wave w loads slot 64 c + 16 w + li,
+    // 16 bytes per 32 dimensions (dimensions 32 cc + 8 g .. + 7, the 16x16x32 operand layout) and
+    // 8 bytes for a last run of 16 (dimensions + 4 g .. + 3, 16x16x16).  K is the A operand of the
+    // scores as it stands; V goes through one exact product with a 0/1 matrix per 16 dimensions,
+    // D = V I, whose accumulator layout (lane: dimension li, slots 4 g .. 4 g + 3) is the A operand
+    // of O^T += V^T P^T.  Two tiles load while one is multiplied (three register sets, rotated by
+    // unrolling).
+    constexpr int NC = NPC / 2, TAIL = NPC % 2;  // 32-dimension runs, and a last run of 16
+    struct Tile {
+      bf16x8 k[NC], v[NC];
+      s16x4 kt, vt;
+    };
+    vm_wait<0>();     // the commit's stores are out
+    __syncthreads();  // the q pairs are published
+    bf16x8 idf[2];
+    s16x4 idt;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) idf[hh][e] = static_cast<bf16>(8 * g + e == 16 * hh + li ? 1.f : 0.f);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) idt[e] = bf16_bits(4 * g + e == li ? 1.f : 0.f);
+    const T* Kr2 = ring_ptr<T>(a.state_pool, sh, slot, sh.st_k, h);
+    const T* Vr2 = ring_ptr<T>(a.state_pool, sh, slot, sh.st_v, h);
+    auto load = [&](int c, Tile& d) __attribute__((always_inline)) {
+      int row = PK * c + 16 * wave + li;
+      row = row < W ? row : W - 1;  // rows past the ring re-read its last row (masked below)
+      const bf16* kp = reinterpret_cast<const bf16*>(Kr2) + row * P;
+      const bf16* vp = reinterpret_cast<const bf16*>(Vr2) + row * P;
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) {
+        d.k[cc] = *reinterpret_cast<const bf16x8*>(kp + 32 * cc + 8 * g);
+        d.v[cc] = *reinterpret_cast<const bf16x8*>(vp + 32 * cc + 8 * g);
+      }
+      if constexpr (TAIL) {
+        d.kt = *reinterpret_cast<const s16x4*>(kp + 32 * NC + 4 * g);
+        d.vt = *reinterpret_cast<const s16x4*>(vp + 32 * NC + 4 * g);
+      }
+    };
+    auto step = [&](int c, Tile& cur, Tile& nxt) __attribute__((always_inline)) {
+      if (c + 2 < nch) load(c + 2, nxt);
+      const int nv = valid - PK * c < PK ? valid - PK * c : PK;
+      const int nw = nv - 16 * wave < 16 ? nv - 16 * wave : 16;  // valid slots of this wave's tile
+      if (nw <= 0) return;                                       // uniform per wave
+      // this round's committed rows replace the slots the append overwrites; value rows past the
+      // valid ones are zeroed (a zero probability times a NaN would not be zero)
+      const int myslot = PK * c + 16 * wave + li;
+      for (int j = 0; j < m; ++j) {  // uniform
+        int sl = lead + j;
+        if (sl >= W) sl -= W;
+        if (sl == myslot) {
+          const float* fkr = fk + j * P;
+          const float* fvr = fv + j * P;
+#pragma unroll
+          for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              cur.k[cc][e] = static_cast<bf16>(fkr[32 * cc + 8 * g + e]);
+              cur.v[cc][e] = static_cast<bf16>(fvr[32 * cc + 8 * g + e]);
+            }
+          if constexpr (TAIL)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              cur.kt[e] = bf16_bits(fkr[32 * NC + 4 * g + e]);
+              cur.vt[e] = bf16_bits(fvr[32 * NC + 4 * g + e]);
+            }
+        }
+      }
+      if (li >= nw) {
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) cur.v[cc] = bf16x8{};
+        cur.vt = s16x4{0, 0, 0, 0};
+      }
+      f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) {
+        const bf16x8 qb = *reinterpret_cast<const bf16x8*>(qh + qrow + 32 * cc + 8 * g);
+        const bf16x8 qc = *reinterpret_cast<const bf16x8*>(ql + qrow + 32 * cc + 8 * g);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.k[cc], qb, sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.k[cc], qc, sacc, 0, 0, 0);
+      }
+      if constexpr (TAIL) {
+        const s16x4 qb = *reinterpret_cast<const s16x4*>(qh + qrow + 32 * NC + 4 * g);
+        const s16x4 qc = *reinterpret_cast<const s16x4*>(ql + qrow + 32 * NC + 4 * g);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(cur.kt, qb, sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(cur.kt, qc, sacc, 0, 0, 0);
+      }
+      float sv[4], cm = -INFINITY;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        sv[rr] = 4 * g + rr < nw ? sacc[rr] * scale : -INFINITY;
+        cm = fmaxf(cm, sv[rr]);
+      }
+      cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
+      cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+      const float mnew = fmaxf(mrun, cm);  // finite: the tile's first slot is valid
+      const float alpha = mrun == -INFINITY ? 0.f : __expf(mrun - mnew);
+      mrun = mnew;
+      s16x4 ph, pl;
+      float ps = 0.f;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const float pv = sv[rr] == -INFINITY ? 0.f : __expf(sv[rr] - mnew);
+        ps += pv;
+        const short hb = bf16_bits(pv);
+        ph[rr] = hb;
+        pl[rr] = bf16_bits(pv - bf16_val(hb));
+      }
+      lrun = lrun * alpha + ps;
+      auto pv_run = [&](int d, const f32x4& tr) __attribute__((always_inline)) {
+        s16x4 va;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) va[rr] = bf16_bits(tr[rr]);  // exact: the values are bf16
+        o[d] *= alpha;
+        o[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph, o[d], 0, 0, 0);
+        o[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl, o[d], 0, 0, 0);
+      };
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          pv_run(2 * cc + hh,
+                 __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.v[cc], idf[hh], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0));
+      if constexpr (TAIL)
+        pv_run(2 * NC, __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(cur.vt, idt, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0));
+    };
+    Tile t0, t1, t2;
+    if (nch > 0) load(0, t0);
+    if (nch > 1) load(1, t1);
+    for (int c = 0; c < nch; c += 3) {
+      step(c, t0, t2);
+      if (c + 1 < nch) step(c + 1, t1, t0);
+      if (c + 2 < nch) step(c + 2, t2, t1);
+    }
+  } else {
   auto wait_tiles = [&](int pending) {  // this wave's loads of `pending` later tiles may stay out
     const int n = pending * 2 * NI;
     if (n >= 16) vm_wait<16>();
@@ -1170,11 +1314,6 @@ __device__ __forceinline__ void pair_body(const Shape& sh, const RoundArgs& a, c
     else if (n >= 2) vm_wait<2>();
     else vm_wait<0>();
   };
-  const int qrow = (li & 7) * P;
-  float mrun = -INFINITY, lrun = 0.f;
-  f32x4 o[16];
-#pragma unroll
-  for (int c = 0; c < 16; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
   vm_wait<0>();     // the commit's stores are out of the count: only tile loads from here on
   __syncthreads();  // the commit region (buffer 2) is free; the q pairs are published
   for (int c = 0; c < nch; ++c) {
@@ -1245,6 +1384,7 @@ __device__ __forceinline__ void pair_body(const Shape& sh, const RoundArgs& a, c
       }
     }
   }
+  }
   // ---- the waves' (max, sum, O) and the block keys
   lrun += __shfl_xor(lrun, 16, 64);
   lrun += __shfl_xor(lrun, 32, 64);
@@ -1308,7 +1448,7 @@ __device__ __forceinline__ void pair_body(const Shape& sh, const RoundArgs& a, c
 
 // One (request, head) per workgroup; the last head of a request to finish advances its count.
 template <typename T, int NPC, bool M2, int NBW>
-__global__ void __launch_bounds__(RT) __attribute__((amdgpu_waves_per_eu(2))) k_round_pair(Shape sh, RoundArgs a,
+__global__ void __launch_bounds__(RT) __attribute__((amdgpu_waves_per_eu(M2 ? 3 : 2))) k_round_pair(Shape sh, RoundArgs a,
                                                                                            ReqTable rt, int commit_bytes) {
   extern __shared__ __attribute__((aligned(16))) char dsm[];
   const int per_xcd = (int)(gridDim.x / 8);
