@@ -849,6 +849,79 @@ def test_graph_replay_matches_eager():
         assert torch.equal(L.state()["blob"], ref_state)
 
 
+
+def test_qwen_rounds_of_eight_requests_match_the_oracle():
+    # 8 Qwen3-4B-shaped requests are 256 (request, head) pairs: one workgroup per pair with heads of
+    # 80 dimensions (two 32-dimension runs and a run of 16); prefixes on both sides of the window.
+    shape = I.QWEN
+    R = 8
+    pr = Pair(shape, seed=111, pool_slots=R, max_requests=R, max_rows=700 * R)
+    pr.gpu.reset()
+    lens = [700, 3, 512, 0, 130, 513, 64, 600]
+    say("qwen 8 requests prefill", lens)
+    pr.commit([pr.rows(n) for n in lens])
+    acc_rng = pr.rng[4]
+    for rnd in range(3):
+        acc = [int(a) for a in acc_rng.integers(0, 9, size=R)]
+        say("qwen 8 requests round", rnd, acc)
+        g, o = pr.draft([pr.rows(8, 3) for _ in range(R)], commits=[pr.rows(a) for a in acc])
+        for i in range(R):
+            assert_close(g[i], o[i], "bf16", f"qwen 8 requests round {rnd} request {i}")
+    for i in (0, 3, 5):
+        pr.check_state(slot=i, what=f"qwen 8 requests state {i}")
+
+
+def test_per_pair_rounds_are_deterministic_and_replay_in_a_graph():
+    # 64 requests of 4 heads (one workgroup per pair): two eager episodes agree bit for bit, and a
+    # captured episode replayed three times (with eager work in between) reproduces them.
+    shape = small_shape("bf16", window=70)
+    R = 64
+    pr = Pair(shape, seed=121, pool_slots=R, max_requests=R, max_rows=200 * R)
+    L = pr.gpu
+    lens = [(53 * i) % 200 for i in range(R)]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    feats = hf.to_device(np.concatenate([pr.rows(n) for n in lens]), shape)
+    rounds = []
+    for a in (np.arange(R) % 9, (np.arange(R) * 5) % 9):
+        cr = np.concatenate([[0], np.cumsum(a)]).astype(np.int64)
+        rounds.append((hf.to_device(pr.rows(int(cr[-1])), shape), cr, hf.to_device(pr.rows(8 * R, 3), shape)))
+    outs = [torch.empty_like(r[2]) for r in rounds]
+
+    def episode(stream):
+        hf.check(hf.hyf_state_reset(L.cfg, L.pool, R, None, R, stream))
+        hf.check(hf.hyf_memory_commit(L.cfg, L.w, L.pool, R, None, R, feats, cu, None, L.ws, L.ws_bytes, stream))
+        for (cf, cr, bi), bo in zip(rounds, outs):
+            hf.check(hf.hyf_draft_block(L.cfg, L.w, L.pool, R, None, R, cf, cr, bi, bo, L.ws, L.ws_bytes, stream))
+
+    ref = None
+    for run in range(2):
+        say("per-pair eager episode", run)
+        episode(None)
+        torch.cuda.synchronize()
+        got = ([o.clone() for o in outs], L.pool.clone())
+        if ref is None:
+            ref = got
+        else:
+            assert all(torch.equal(a, b) for a, b in zip(got[0], ref[0])) and torch.equal(got[1], ref[1])
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    with torch.cuda.stream(cs):
+        episode(cs)
+    torch.cuda.synchronize()
+    say("per-pair graph capture")
+    with torch.cuda.graph(g, stream=cs):
+        episode(cs)
+    for rep in range(3):
+        for o in outs:
+            o.zero_()
+        L.pool.zero_()
+        torch.cuda.synchronize()
+        say("per-pair graph replay", rep)
+        g.replay()
+        torch.cuda.synchronize()
+        assert all(torch.equal(a, b) for a, b in zip(outs, ref[0]))
+        assert torch.equal(L.pool, ref[1])
+
 DEV_COUNT_SHAPES = [
     ("tiny_fp32", I.TINY, 2),
     ("small_bf16", small_shape("bf16", window=40), 3),
