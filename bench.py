@@ -10,9 +10,9 @@ block, all 64 in one hyf_draft_block call.  `value` = draft blocks/s over whole 
 included), summed over the requests.  Inputs are seeded synthetic arrays (NumPy PCG64 streams,
 seed 3), resident in HBM before the timed region.
 
-`roofline` is the round's dominant kernel, k_round at this shape: algorithmic bytes per launch
-(ring windows, H read and written, the append, the projection columns it reads, its output)
-over its average duration, measured with HIP events as a graph of the 128 rounds minus a graph
+`roofline` is the round's dominant kernel at this shape, the round kernel with one workgroup per
+(request, head) (k_round_pair): algorithmic bytes per launch (ring windows, H read and written,
+the append, the projection columns it reads, its output) over its average duration, measured with HIP events as a graph of the 128 rounds minus a graph
 of the same rounds' two projections (the same kernels and launch shapes, run through hyf_linear).
 `round` is the whole round against its algorithmic bytes.
 
@@ -308,11 +308,16 @@ class Batched:
         y = torch.empty((max(M), sh.n_in), dtype=torch.float32, device="cuda")
         xo = torch.empty((8 * R, sh.dq), dtype=torch.bfloat16, device="cuda").normal_()
         xin = torch.empty((max(M), d), dtype=torch.bfloat16, device="cuda").normal_()
+        # In a round the round kernel streams its 531 MB between two rounds' projections, so their
+        # weights come from HBM; the projection-only graph rotates W_COPIES weight copies (more than
+        # the last-level cache holds) to price them the same way.
+        w_in = [torch.empty_like(self.wd["w_in"][0]).normal_() for _ in range(W_COPIES)]
+        w_out = [torch.empty_like(self.wd["w_out"][0]).normal_() for _ in range(W_COPIES)]
 
         def projs(i):
             s = stream.cuda_stream
-            st[0] |= hf.hyf_linear(self.cfg, xin, M[i], d, self.wd["w_in"][0], sh.n_in, y, 1, s)
-            st[0] |= hf.hyf_linear(self.cfg, xo, 8 * R, sh.dq, self.wd["w_out"][0], d, self.out, 0, s)
+            st[0] |= hf.hyf_linear(self.cfg, xin, M[i], d, w_in[i % W_COPIES], sh.n_in, y, 1, s)
+            st[0] |= hf.hyf_linear(self.cfg, xo, 8 * R, sh.dq, w_out[i % W_COPIES], d, self.out, 0, s)
 
         t_proj = time_graph(torch, projs, nr, stream=stream)
         if st[0]:
@@ -789,7 +794,10 @@ def source_digest(rel):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def pmc_probe(torch, hf, I, reps=4):
+PMC_REPS = 4  # launches of each measured shape at the end of its section of the PMC probe
+
+
+def pmc_probe(torch, hf, I, reps=PMC_REPS):
     """The measured kernels in a fixed order, each at one launch shape: a copy of known size; the
     round kernel at the batched shape (64 requests, windows filled by earlier rounds); the 8192-token
     scan; the 8192 x 2560 x 2720 GEMM; the 12-row w_in projection (bf16, then 4-bit)."""
@@ -850,29 +858,20 @@ def pmc_summary(fetch_db, write_db):
     out = {"copy_bytes": COPY_BYTES, "copy_fetch_kib": copy_f, "copy_write_kib": copy_w,
            "fetch_scale": scale_f, "write_scale": scale_w, "kernels": {}}
 
-    def pick(rows, sub, grid=None):
-        # dispatches of the kernel; for the GEMM the probe's 8192-row launch (the largest grid)
-        m = [(g, v) for k, g, v in rows if sub in k]
+    def pick(rows, sub):
+        # the kernel's last PMC_REPS dispatches: each section of the probe ends with PMC_REPS launches
+        # of its measured shape (the round kernel after the windows have filled, the GEMM after the
+        # rounds' own projection GEMMs)
+        m = [(k, g, v) for k, g, v in rows if sub in k][-PMC_REPS:]
         if not m:
-            return None, None
-        if sub.startswith("k_gemm"):
-            gmax = max(g for g, _ in m)
-            m = [(g, v) for g, v in m if g == gmax]
-        else:
-            # the most frequent launch shape of this kernel in the probe
-            gs = {}
-            for g, _ in m:
-                gs[g] = gs.get(g, 0) + 1
-            gsel = max(gs, key=gs.get)
-            m = [(g, v) for g, v in m if g == gsel]
-        return m[0][0], sum(v for _, v in m) / len(m)
+            return None, None, None
+        return m[-1][0], m[-1][1], sum(v for _, _, v in m) / len(m)
 
     for key, (sub, src, what) in PMC_KERNELS.items():
-        g, f_kib = pick(fd, sub)
+        name, g, f_kib = pick(fd, sub)
         if g is None:
             continue
-        _, w_kib = pick(wd, sub)
-        name = next(k for k, gg, v in fd if sub in k)
+        _, _, w_kib = pick(wd, sub)
         out["kernels"][key] = {"kernel": name, "grid": g, "shape": what, "source": src,
                                "source_sha256": source_digest(src), "fetch_kib": f_kib, "write_kib": w_kib or 0.0,
                                "traffic_bytes": f_kib * 1024 * scale_f + (w_kib or 0.0) * 1024 * scale_w}
@@ -1226,7 +1225,8 @@ def main():
                       "round_us": 1e3 * head["rounds_ms"] / 128, "round_graph_us": t_round,
                       "projections_graph_us": t_proj},
         "roofline": {**hbm(kb, t_k), "traffic": pmc_traffic("round"),
-                     "kernel": "k_round<bf16>: commit, readout, attention and merge of 64 requests x 32 heads",
+                     "kernel": "k_round_pair<bf16>: commit, readout and attention of 64 requests x 32 heads, one "
+                               "workgroup per (request, head)",
                      "bytes_per_launch": kb, "avg_us": t_k,
                      "method": "graph of the 128 rounds minus a graph of their two projections (same kernels and "
                                "shapes through hyf_linear), per round"},
