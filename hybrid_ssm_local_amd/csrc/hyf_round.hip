@@ -1174,8 +1174,9 @@ __device__ __forceinline__ void pair_body(const Shape& sh, const RoundArgs& a, c
     // 8 bytes for a last run of 16 (dimensions + 4 g .. + 3, 16x16x16).  K is the A operand of the
     // scores as it stands; V goes through one exact product with a 0/1 matrix per 16 dimensions,
     // D = V I, whose accumulator layout (lane: dimension li, slots 4 g .. 4 g + 3) is the A operand
-    // of O^T += V^T P^T.  Two tiles load while one is multiplied (three register sets, rotated by
-    // unrolling).
+    // of O^T += V^T P^T.  The next tile loads while one is multiplied (two register sets, rotated by
+    // unrolling): 118 VGPRs and four workgroups per CU measured faster than two tiles in flight
+    // with three per CU (119 against 127 us at 64 Qwen3-4B-shaped requests).
     constexpr int NC = NPC / 2, TAIL = NPC % 2;  // 32-dimension runs, and a last run of 16
     struct Tile {
       bf16x8 k[NC], v[NC];
@@ -1209,7 +1210,7 @@ __device__ __forceinline__ void pair_body(const Shape& sh, const RoundArgs& a, c
       }
     };
     auto step = [&](int c, Tile& cur, Tile& nxt) __attribute__((always_inline)) {
-      if (c + 2 < nch) load(c + 2, nxt);
+      if (c + 1 < nch) load(c + 1, nxt);
       const int nv = valid - PK * c < PK ? valid - PK * c : PK;
       const int nw = nv - 16 * wave < 16 ? nv - 16 * wave : 16;  // valid slots of this wave's tile
       if (nw <= 0) return;                                       // uniform per wave
@@ -1295,13 +1296,11 @@ __device__ __forceinline__ void pair_body(const Shape& sh, const RoundArgs& a, c
       if constexpr (TAIL)
         pv_run(2 * NC, __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(cur.vt, idt, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0));
     };
-    Tile t0, t1, t2;
+    Tile t0, t1;
     if (nch > 0) load(0, t0);
-    if (nch > 1) load(1, t1);
-    for (int c = 0; c < nch; c += 3) {
-      step(c, t0, t2);
+    for (int c = 0; c < nch; c += 2) {
+      step(c, t0, t1);
       if (c + 1 < nch) step(c + 1, t1, t0);
-      if (c + 2 < nch) step(c + 2, t2, t1);
     }
   } else {
   auto wait_tiles = [&](int pending) {  // this wave's loads of `pending` later tiles may stay out
@@ -1448,7 +1447,7 @@ __device__ __forceinline__ void pair_body(const Shape& sh, const RoundArgs& a, c
 
 // One (request, head) per workgroup; the last head of a request to finish advances its count.
 template <typename T, int NPC, bool M2, int NBW>
-__global__ void __launch_bounds__(RT) __attribute__((amdgpu_waves_per_eu(M2 ? 3 : 2))) k_round_pair(Shape sh, RoundArgs a,
+__global__ void __launch_bounds__(RT) __attribute__((amdgpu_waves_per_eu(M2 ? 4 : 2))) k_round_pair(Shape sh, RoundArgs a,
                                                                                            ReqTable rt, int commit_bytes) {
   extern __shared__ __attribute__((aligned(16))) char dsm[];
   const int per_xcd = (int)(gridDim.x / 8);
