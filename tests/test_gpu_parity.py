@@ -969,6 +969,36 @@ def test_device_counts_equal_the_host_table(name, shape, R):
         assert torch.equal(pr.gpu.pool, dev.pool), f"{name} round {rnd} states"
 
 
+
+def test_device_counts_equal_the_host_table_over_many_pairs():
+    # 64 requests of 4 heads (one workgroup per (request, head)): hyf_draft_block with the host
+    # table and hyf_draft_block_dev with padded rows and device counts agree bit for bit.
+    shape = small_shape("bf16", window=40)
+    R = 64
+    pr = Pair(shape, seed=113, pool_slots=R, max_requests=R, max_rows=120 * R)
+    dev = hf.DrafterLayer(shape, pr.w, pool_slots=R, max_requests=R, max_rows=120 * R)
+    lens = [(29 * i) % 120 for i in range(R)]
+    pre = np.concatenate([pr.rows(n) for n in lens])
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    for L in (pr.gpu, dev):
+        L.reset()
+        L.commit(hf.to_device(pre, shape), cu)
+    for rnd in range(3):
+        a = [int((7 * i + 3 * rnd) % 9) for i in range(R)]
+        commits = [pr.rows(n) for n in a]
+        blocks = hf.to_device(np.concatenate([pr.rows(8, 3) for _ in range(R)]), shape)
+        o_host, o_dev = torch.empty_like(blocks), torch.empty_like(blocks)
+        cu_r = np.concatenate([[0], np.cumsum(a)]).astype(np.int64)
+        say("hyf_draft_block host table, 64 requests", rnd)
+        pr.gpu.draft(blocks, o_host, hf.to_device(np.concatenate(commits), shape), cu_r)
+        counts = torch.tensor(a, dtype=torch.int32, device=DEV)
+        say("hyf_draft_block_dev, 64 requests", rnd)
+        hf.check(hf.hyf_draft_block_dev(dev.cfg, dev.w, dev.pool, R, None, R, _padded_commits(shape, commits), counts,
+                                        blocks, o_dev, dev.ws, dev.ws_bytes), "hyf_draft_block_dev")
+        torch.cuda.synchronize()
+        assert torch.equal(o_host, o_dev), f"round {rnd} outputs"
+        assert torch.equal(pr.gpu.pool, dev.pool), f"round {rnd} states"
+
 def test_device_count_round_replays_in_a_graph():
     # One hyf_draft_block_dev call captured once, replayed for four rounds whose rows and counts are
     # written into its fixed buffers on the device between replays (eager copies, then a sync):
