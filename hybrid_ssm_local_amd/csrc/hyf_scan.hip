@@ -535,6 +535,178 @@ __global__ void __launch_bounds__(256) k_ssd_y(Shape sh, ScanArgs a, ReqTable rt
   }
 }
 
+// y-mode outputs of a bf16 block on bf16 matrix cores (16x16x16, fp32 sums), the same chunked
+// form as k_ssd_y.  B and C of the block go to LDS in their tiled layout and are turned in place,
+// one 1 KiB tile (16 features x 32 tokens) per wave at a time, into token-major 16 x 16 blocks:
+// the tile is the A operand of a 16x16x32 product with a 0/1 matrix I_h (h: which 16 of its 32
+// tokens), D = A I_h, whose accumulator layout (lane (i, g): features 4 g .. + 3 of token i) is the
+// operand layout of a product contracting over features; written back as 512-byte halves of the
+// same tile, so the turn needs no other buffer.  Then per 16-token output tile t and input tile s:
+//   G^T[s][t] = sum_n B[s][n] C[t][n]      (A: B block of s, B: C block of t, exact bf16 products);
+//   its accumulator (lane (i, g): token t0 + i, tokens s0 + 4 g + r) masked and scaled into
+//   M[t][s] = exp(cum_t - cum_s) dt_s G[t][s] is the A operand of Y += M X, M entering as two bf16
+//   terms (hi, lo) and X as 8-byte pieces of the tiled x straight from global memory;
+//   the state term sum_n C[t][n] H0[p][n] with H0 (fp32, global) as two bf16 terms.
+// Inputs past the block's length hold anything: B and C there are zeroed before the turn (a product
+// with I_h sums every token of the run), their scores are replaced by 0 and their x pieces read as
+// 0.  Wave w takes output tiles w and 7 - w.
+template <int PB>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+k_ssd_y_mfma(Shape sh, ScanArgs a, ReqTable rt) {
+  typedef __attribute__((ext_vector_type(4))) short s16x4;
+  constexpr int NJ = TB / 32;  // 32-token runs of a block
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int nh = sh.nh, P = 16 * PB, N = sh.N, NFG = N / 16;
+  const int h = blockIdx.x % nh, q = blockIdx.x / nh;
+  const int r = find_request(rt, q);
+  const int ls = q - rt.seg0[r];
+  const int Tr = rt.row0[r + 1] - rt.row0[r];
+  const int s_begin = ls * TB;
+  const int len = min(TB, Tr - s_begin);
+  const int64_t blk = rt.blk0[r] + ls;  // y-mode segments are single blocks
+  const int grp = h / (nh / sh.G);
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int li = lane & 15, g = lane >> 4;
+  char* bs = smem;                   // B: NFG x NJ tiles of 1 KiB
+  char* cs = smem + NFG * NJ * 1024;  // C, the same
+  float* dts = reinterpret_cast<float*>(cs + NFG * NJ * 1024);  // [TB] raw steps, then dt
+  float* cum = dts + TB;                                         // [TB]
+  const bf16* gx = static_cast<const bf16*>(a.x) + blk * a.xblk + (int64_t)h * P * TB;
+  const bf16* gb = static_cast<const bf16*>(a.B) + blk * a.bblk + (int64_t)grp * N * TB;
+  const bf16* gc = static_cast<const bf16*>(a.C) + blk * a.cblk + (int64_t)grp * N * TB;
+  const float* gd = a.dt + blk * a.dblk + (int64_t)h * TB;
+  lds_stage16<256>(N * TB / 8, bs, [&](int i) { return gb + (int64_t)i * 8; });
+  lds_stage16<256>(N * TB / 8, cs, [&](int i) { return gc + (int64_t)i * 8; });
+  lds_stage16<256>(TB / 4, dts, [&](int i) { return gd + 4 * i; });
+  vm_wait<0>();
+  __syncthreads();
+  // ---- turn B and C token-major (each wave its own tiles, in place) and form dt and cum
+  {
+    bf16x8 id[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) id[hh][e] = static_cast<bf16>(8 * g + e == 16 * hh + li ? 1.f : 0.f);
+    for (int tile = wave; tile < 2 * NFG * NJ; tile += 4) {
+      char* tb = (tile < NFG * NJ ? bs : cs) + (tile % (NFG * NJ)) * 1024;
+      bf16x8 v = *reinterpret_cast<const bf16x8*>(tb + 16 * lane);
+      // tokens past the length may hold NaN or infinity, which a 0 of I_h would not cancel
+      const int tok = 32 * (tile % NJ) + 8 * g;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (tok + e >= len) v[e] = static_cast<bf16>(0.f);
+      f32x4 d[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        d[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, id[hh], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        s16x4 o;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) o[rr] = __builtin_bit_cast(short, static_cast<bf16>(d[hh][rr]));  // exact
+        *reinterpret_cast<s16x4*>(tb + 512 * hh + 8 * lane) = o;
+      }
+    }
+  }
+  if (wave == 0) {
+    // dt and the inclusive prefix of a = dt A (tokens past len: dt = 0)
+    const float A = -expf(a.a_log[h]), bias = a.dt_bias[h];
+    const int u0 = 2 * lane;
+    const float d0 = u0 < len ? softplus_f(dts[u0] + bias) : 0.f;
+    const float d1 = u0 + 1 < len ? softplus_f(dts[u0 + 1] + bias) : 0.f;
+    const float a0 = d0 * A, a1 = d1 * A;
+    float inc = a0 + a1;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float v = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += v;
+    }
+    const float ex = inc - (a0 + a1);
+    cum[u0] = ex + a0;
+    cum[u0 + 1] = inc;
+    dts[u0] = d0;
+    dts[u0 + 1] = d1;
+  }
+  __syncthreads();
+
+  // 16 x 16 token-major block (token tile tt, feature group fg) of B or C: lane (i, g) reads token
+  // 16 tt + i, features 16 fg + 4 g .. + 3
+  auto blk8 = [&](const char* base, int tt, int fg) {
+    return *reinterpret_cast<const s16x4*>(base + (fg * NJ + tt / 2) * 1024 + (tt % 2) * 512 + 8 * lane);
+  };
+  const float* H0 = a.part + ((int64_t)q * nh + h) * P * N;  // state before the block
+  const float D = a.d_skip[h];
+  bf16* yout = static_cast<bf16*>(a.y) + ((int64_t)rt.row0[r] + s_begin) * nh * P + (int64_t)h * P;
+  for (int pass = 0; pass < 2; ++pass) {
+    const int tt = pass ? TB / 16 - 1 - wave : wave;
+    const int t0 = 16 * tt;
+    if (t0 >= len) continue;  // uniform
+    f32x4 y[PB], ys[PB];
+#pragma unroll
+    for (int pt = 0; pt < PB; ++pt) y[pt] = ys[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const float ct = cum[t0 + li];
+    for (int st = 0; st <= tt && 16 * st < len; ++st) {
+      const int s0 = 16 * st;
+      f32x4 gt = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int fg = 0; fg < NFG; ++fg)
+        gt = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(blk8(bs, st, fg), blk8(cs, tt, fg), gt, 0, 0, 0);
+      // lane (li, g) register rr: G[t0 + li][s0 + 4 g + rr]
+      s16x4 mh, ml;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int sq = s0 + 4 * g + rr;
+        const float m = sq <= t0 + li && sq < len ? gt[rr] * expf(ct - cum[sq]) * dts[sq] : 0.f;
+        const bf16 hb = static_cast<bf16>(m);
+        mh[rr] = __builtin_bit_cast(short, hb);
+        ml[rr] = __builtin_bit_cast(short, static_cast<bf16>(m - static_cast<float>(hb)));
+      }
+      // X[s0 + 4 g .. + 3][16 pt + li]: half of a 16-byte chunk of the tiled x
+      const int tok = s0 + 4 * g;
+      const int64_t xo = ((tok / 32) * 64 + ((tok % 32) / 8) * 16 + li) * 8 + tok % 8;
+#pragma unroll
+      for (int pt = 0; pt < PB; ++pt) {
+        s16x4 xv = *reinterpret_cast<const s16x4*>(gx + (int64_t)pt * NJ * 64 * 8 + xo);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          if (tok + rr >= len) xv[rr] = 0;  // x past the block's length may hold anything
+        y[pt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(mh, xv, y[pt], 0, 0, 0);
+        y[pt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ml, xv, y[pt], 0, 0, 0);
+      }
+    }
+    // state term: ys[t][p] = sum_n C[t][n] H0[p][n], H0 as two bf16 terms
+    for (int fg = 0; fg < NFG; ++fg) {
+      const s16x4 cv = blk8(cs, tt, fg);
+#pragma unroll
+      for (int pt = 0; pt < PB; ++pt) {
+        const f32x4 hv = *reinterpret_cast<const f32x4*>(H0 + (int64_t)(16 * pt + li) * N + 16 * fg + 4 * g);
+        s16x4 hh, hl;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const bf16 hb = static_cast<bf16>(hv[rr]);
+          hh[rr] = __builtin_bit_cast(short, hb);
+          hl[rr] = __builtin_bit_cast(short, static_cast<bf16>(hv[rr] - static_cast<float>(hb)));
+        }
+        ys[pt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(cv, hh, ys[pt], 0, 0, 0);
+        ys[pt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(cv, hl, ys[pt], 0, 0, 0);
+      }
+    }
+    // lane (li, g) register rr: token t0 + 4 g + rr, column 16 pt + li
+#pragma unroll
+    for (int pt = 0; pt < PB; ++pt) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int tq = t0 + 4 * g + rr;
+        if (tq < len) {
+          const int p = 16 * pt + li;
+          const float v = y[pt][rr] + expf(cum[tq]) * ys[pt][rr] + D * to_f32(gx[tile_off<bf16>(p, tq)]);
+          yout[(int64_t)tq * nh * P + p] = from_f32<bf16>(v);
+        }
+      }
+    }
+  }
+}
+
 bool scan_y_supported(const Shape& sh, int esz) {
   return (size_t)TB * (sh.P + 2 * sh.N) * esz + 2 * TB * sizeof(float) <= 160 * 1024 - 256;
 }
@@ -645,8 +817,36 @@ static hipError_t launch_y_t(const Shape& sh, const ScanArgs& a, const ReqTable&
   return hipGetLastError();
 }
 
+template <int PB>
+static hipError_t launch_y_mfma_t(const Shape& sh, const ScanArgs& a, const ReqTable& rt, hipStream_t s) {
+  const size_t lds = (size_t)2 * sh.N * TB * 2 + 2 * TB * sizeof(float);
+  static std::once_flag once;
+  static hipError_t set_err = hipSuccess;
+  std::call_once(once, [] {
+    set_err = hipFuncSetAttribute(reinterpret_cast<const void*>(k_ssd_y_mfma<PB>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 256);
+  });
+  if (set_err != hipSuccess) return set_err;
+  hipLaunchKernelGGL(k_ssd_y_mfma<PB>, dim3(a.total_segs * sh.nh), dim3(256), lds, s, sh, a, rt);
+  return hipGetLastError();
+}
+
 template <typename T>
 static hipError_t launch_y(const Shape& sh, const ScanArgs& a, const ReqTable& rt, hipStream_t s) {
+  if constexpr (sizeof(T) == 2) {
+    // heads of up to 128 dimensions on the bf16 matrix cores
+    switch (sh.P / 16) {
+      case 1: return launch_y_mfma_t<1>(sh, a, rt, s);
+      case 2: return launch_y_mfma_t<2>(sh, a, rt, s);
+      case 3: return launch_y_mfma_t<3>(sh, a, rt, s);
+      case 4: return launch_y_mfma_t<4>(sh, a, rt, s);
+      case 5: return launch_y_mfma_t<5>(sh, a, rt, s);
+      case 6: return launch_y_mfma_t<6>(sh, a, rt, s);
+      case 7: return launch_y_mfma_t<7>(sh, a, rt, s);
+      case 8: return launch_y_mfma_t<8>(sh, a, rt, s);
+      default: break;
+    }
+  }
   return sh.P > 128 ? launch_y_t<T, 16>(sh, a, rt, s) : launch_y_t<T, 8>(sh, a, rt, s);
 }
 
