@@ -536,25 +536,27 @@ __global__ void __launch_bounds__(256) k_ssd_y(Shape sh, ScanArgs a, ReqTable rt
 }
 
 // y-mode outputs of a bf16 block on bf16 matrix cores (16x16x16, fp32 sums), the same chunked
-// form as k_ssd_y.  B and C of the block go to LDS in their tiled layout and are turned in place,
-// one 1 KiB tile (16 features x 32 tokens) per wave at a time, into token-major 16 x 16 blocks:
-// the tile is the A operand of a 16x16x32 product with a 0/1 matrix I_h (h: which 16 of its 32
-// tokens), D = A I_h, whose accumulator layout (lane (i, g): features 4 g .. + 3 of token i) is the
-// operand layout of a product contracting over features; written back as 512-byte halves of the
-// same tile, so the turn needs no other buffer.  Then per 16-token output tile t and input tile s:
+// form as k_ssd_y, with eight waves: wave w owns output tile w (tokens 16 w .. 16 w + 15).
+// B and C of the block go to LDS in their tiled layout and are turned in place, one 1 KiB tile (16
+// features x 32 tokens) at a time, into token-major 16 x 16 blocks: the tile is the A operand of a
+// 16x16x32 product with a 0/1 matrix I_h (h: which 16 of its 32 tokens), D = A I_h, whose
+// accumulator layout (lane (i, g): features 4 g .. + 3 of token i) is the operand layout of a
+// product contracting over features; written back as 512-byte halves of the same tile, so the
+// turn needs no other buffer.  Then per input tile s <= t:
 //   G^T[s][t] = sum_n B[s][n] C[t][n]      (A: B block of s, B: C block of t, exact bf16 products);
 //   its accumulator (lane (i, g): token t0 + i, tokens s0 + 4 g + r) masked and scaled into
 //   M[t][s] = exp(cum_t - cum_s) dt_s G[t][s] is the A operand of Y += M X, M entering as two bf16
-//   terms (hi, lo) and X as 8-byte pieces of the tiled x straight from global memory;
-//   the state term sum_n C[t][n] H0[p][n] with H0 (fp32, global) as two bf16 terms.
+//   terms (hi, lo) and X as 8-byte pieces of the tiled x read from global memory one step ahead;
+// and the state term sum_n C[t][n] H0[p][n], H0 (fp32, global, one feature group ahead up to 96
+// head dimensions) as two bf16 terms.  The x pieces of the diagonal step (s = t) are the x_t the skip term D x_t needs.
 // Inputs past the block's length hold anything: B and C there are zeroed before the turn (a product
-// with I_h sums every token of the run), their scores are replaced by 0 and their x pieces read as
-// 0.  Wave w takes output tiles w and 7 - w.
+// with I_h sums every token of the run), their scores are replaced by 0 and their x pieces read as 0.
 template <int PB>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4)))
 k_ssd_y_mfma(Shape sh, ScanArgs a, ReqTable rt) {
   typedef __attribute__((ext_vector_type(4))) short s16x4;
   constexpr int NJ = TB / 32;  // 32-token runs of a block
+  constexpr int NWV = TB / 16;  // waves: one per 16-token tile
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int nh = sh.nh, P = 16 * PB, N = sh.N, NFG = N / 16;
   const int h = blockIdx.x % nh, q = blockIdx.x / nh;
@@ -576,9 +578,30 @@ k_ssd_y_mfma(Shape sh, ScanArgs a, ReqTable rt) {
   const bf16* gb = static_cast<const bf16*>(a.B) + blk * a.bblk + (int64_t)grp * N * TB;
   const bf16* gc = static_cast<const bf16*>(a.C) + blk * a.cblk + (int64_t)grp * N * TB;
   const float* gd = a.dt + blk * a.dblk + (int64_t)h * TB;
-  lds_stage16<256>(N * TB / 8, bs, [&](int i) { return gb + (int64_t)i * 8; });
-  lds_stage16<256>(N * TB / 8, cs, [&](int i) { return gc + (int64_t)i * 8; });
-  lds_stage16<256>(TB / 4, dts, [&](int i) { return gd + 4 * i; });
+  const float* H0 = a.part + ((int64_t)q * nh + h) * P * N;  // state before the block
+  lds_stage16<512>(N * TB / 8, bs, [&](int i) { return gb + (int64_t)i * 8; });
+  lds_stage16<512>(N * TB / 8, cs, [&](int i) { return gc + (int64_t)i * 8; });
+  lds_stage16<512>(TB / 4, dts, [&](int i) { return gd + 4 * i; });
+  // this wave's output tile, its first x pieces and H0's first feature group, in flight with the
+  // staging (X[s0 + 4 g .. + 3][16 pt + li]: half of a 16-byte chunk of the tiled x)
+  const int t0 = 16 * wave;
+  auto load_x = [&](int s0, s16x4* xv) {
+    const int tok = s0 + 4 * g;
+    const int64_t xo = ((tok / 32) * 64 + ((tok % 32) / 8) * 16 + li) * 8 + tok % 8;
+#pragma unroll
+    for (int pt = 0; pt < PB; ++pt) xv[pt] = *reinterpret_cast<const s16x4*>(gx + (int64_t)pt * NJ * 64 * 8 + xo);
+  };
+  auto load_h = [&](int fg, f32x4* hv) {
+#pragma unroll
+    for (int pt = 0; pt < PB; ++pt)
+      hv[pt] = *reinterpret_cast<const f32x4*>(H0 + (int64_t)(16 * pt + li) * N + 16 * fg + 4 * g);
+  };
+  s16x4 xa[PB];
+  f32x4 hc[PB];
+  if (t0 < len) {
+    load_x(0, xa);
+    load_h(0, hc);
+  }
   vm_wait<0>();
   __syncthreads();
   // ---- turn B and C token-major (each wave its own tiles, in place) and form dt and cum
@@ -588,7 +611,7 @@ k_ssd_y_mfma(Shape sh, ScanArgs a, ReqTable rt) {
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
       for (int e = 0; e < 8; ++e) id[hh][e] = static_cast<bf16>(8 * g + e == 16 * hh + li ? 1.f : 0.f);
-    for (int tile = wave; tile < 2 * NFG * NJ; tile += 4) {
+    for (int tile = wave; tile < 2 * NFG * NJ; tile += NWV) {
       char* tb = (tile < NFG * NJ ? bs : cs) + (tile % (NFG * NJ)) * 1024;
       bf16x8 v = *reinterpret_cast<const bf16x8*>(tb + 16 * lane);
       // tokens past the length may hold NaN or infinity, which a 0 of I_h would not cancel
@@ -629,79 +652,86 @@ k_ssd_y_mfma(Shape sh, ScanArgs a, ReqTable rt) {
     dts[u0 + 1] = d1;
   }
   __syncthreads();
+  if (t0 >= len) return;  // uniform; no barrier follows
 
   // 16 x 16 token-major block (token tile tt, feature group fg) of B or C: lane (i, g) reads token
   // 16 tt + i, features 16 fg + 4 g .. + 3
   auto blk8 = [&](const char* base, int tt, int fg) {
     return *reinterpret_cast<const s16x4*>(base + (fg * NJ + tt / 2) * 1024 + (tt % 2) * 512 + 8 * lane);
   };
-  const float* H0 = a.part + ((int64_t)q * nh + h) * P * N;  // state before the block
-  const float D = a.d_skip[h];
-  bf16* yout = static_cast<bf16*>(a.y) + ((int64_t)rt.row0[r] + s_begin) * nh * P + (int64_t)h * P;
-  for (int pass = 0; pass < 2; ++pass) {
-    const int tt = pass ? TB / 16 - 1 - wave : wave;
-    const int t0 = 16 * tt;
-    if (t0 >= len) continue;  // uniform
-    f32x4 y[PB], ys[PB];
+  const int tt = wave;
+  f32x4 y[PB], ys[PB];
 #pragma unroll
-    for (int pt = 0; pt < PB; ++pt) y[pt] = ys[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const float ct = cum[t0 + li];
-    for (int st = 0; st <= tt && 16 * st < len; ++st) {
-      const int s0 = 16 * st;
-      f32x4 gt = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int fg = 0; fg < NFG; ++fg)
-        gt = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(blk8(bs, st, fg), blk8(cs, tt, fg), gt, 0, 0, 0);
-      // lane (li, g) register rr: G[t0 + li][s0 + 4 g + rr]
-      s16x4 mh, ml;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int sq = s0 + 4 * g + rr;
-        const float m = sq <= t0 + li && sq < len ? gt[rr] * expf(ct - cum[sq]) * dts[sq] : 0.f;
-        const bf16 hb = static_cast<bf16>(m);
-        mh[rr] = __builtin_bit_cast(short, hb);
-        ml[rr] = __builtin_bit_cast(short, static_cast<bf16>(m - static_cast<float>(hb)));
-      }
-      // X[s0 + 4 g .. + 3][16 pt + li]: half of a 16-byte chunk of the tiled x
-      const int tok = s0 + 4 * g;
-      const int64_t xo = ((tok / 32) * 64 + ((tok % 32) / 8) * 16 + li) * 8 + tok % 8;
-#pragma unroll
-      for (int pt = 0; pt < PB; ++pt) {
-        s16x4 xv = *reinterpret_cast<const s16x4*>(gx + (int64_t)pt * NJ * 64 * 8 + xo);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          if (tok + rr >= len) xv[rr] = 0;  // x past the block's length may hold anything
-        y[pt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(mh, xv, y[pt], 0, 0, 0);
-        y[pt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ml, xv, y[pt], 0, 0, 0);
-      }
-    }
-    // state term: ys[t][p] = sum_n C[t][n] H0[p][n], H0 as two bf16 terms
-    for (int fg = 0; fg < NFG; ++fg) {
-      const s16x4 cv = blk8(cs, tt, fg);
-#pragma unroll
-      for (int pt = 0; pt < PB; ++pt) {
-        const f32x4 hv = *reinterpret_cast<const f32x4*>(H0 + (int64_t)(16 * pt + li) * N + 16 * fg + 4 * g);
-        s16x4 hh, hl;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const bf16 hb = static_cast<bf16>(hv[rr]);
-          hh[rr] = __builtin_bit_cast(short, hb);
-          hl[rr] = __builtin_bit_cast(short, static_cast<bf16>(hv[rr] - static_cast<float>(hb)));
-        }
-        ys[pt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(cv, hh, ys[pt], 0, 0, 0);
-        ys[pt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(cv, hl, ys[pt], 0, 0, 0);
-      }
-    }
-    // lane (li, g) register rr: token t0 + 4 g + rr, column 16 pt + li
+  for (int pt = 0; pt < PB; ++pt) y[pt] = ys[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // state term: ys[t][p] = sum_n C[t][n] H0[p][n], H0 as two bf16 terms
+  constexpr bool HPF = PB <= 6;  // H0 one feature group ahead while it fits the registers
+  for (int fg = 0; fg < NFG; ++fg) {
+    f32x4 hn[PB];
+    if (HPF && fg + 1 < NFG) load_h(fg + 1, hn);
+    if (!HPF && fg > 0) load_h(fg, hc);
+    const s16x4 cv = blk8(cs, tt, fg);
 #pragma unroll
     for (int pt = 0; pt < PB; ++pt) {
+      s16x4 hh, hl;
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const int tq = t0 + 4 * g + rr;
-        if (tq < len) {
-          const int p = 16 * pt + li;
-          const float v = y[pt][rr] + expf(cum[tq]) * ys[pt][rr] + D * to_f32(gx[tile_off<bf16>(p, tq)]);
-          yout[(int64_t)tq * nh * P + p] = from_f32<bf16>(v);
-        }
+        const bf16 hb = static_cast<bf16>(hc[pt][rr]);
+        hh[rr] = __builtin_bit_cast(short, hb);
+        hl[rr] = __builtin_bit_cast(short, static_cast<bf16>(hc[pt][rr] - static_cast<float>(hb)));
+      }
+      ys[pt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(cv, hh, ys[pt], 0, 0, 0);
+      ys[pt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(cv, hl, ys[pt], 0, 0, 0);
+    }
+    if (HPF && fg + 1 < NFG)
+#pragma unroll
+      for (int pt = 0; pt < PB; ++pt) hc[pt] = hn[pt];
+  }
+  const float ct = cum[t0 + li];
+  for (int st = 0; st <= tt; ++st) {
+    const int s0 = 16 * st;
+    s16x4 xn[PB];
+    if (st < tt) load_x(s0 + 16, xn);  // the next step's pieces (the diagonal step is always inside len)
+    f32x4 gt = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int fg = 0; fg < NFG; ++fg)
+      gt = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(blk8(bs, st, fg), blk8(cs, tt, fg), gt, 0, 0, 0);
+    // lane (li, g) register rr: G[t0 + li][s0 + 4 g + rr]
+    s16x4 mh, ml;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int sq = s0 + 4 * g + rr;
+      const float m = sq <= t0 + li && sq < len ? gt[rr] * expf(ct - cum[sq]) * dts[sq] : 0.f;
+      const bf16 hb = static_cast<bf16>(m);
+      mh[rr] = __builtin_bit_cast(short, hb);
+      ml[rr] = __builtin_bit_cast(short, static_cast<bf16>(m - static_cast<float>(hb)));
+    }
+    const int tok = s0 + 4 * g;
+#pragma unroll
+    for (int pt = 0; pt < PB; ++pt) {
+      s16x4 xv = xa[pt];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        if (tok + rr >= len) xv[rr] = 0;  // x past the block's length may hold anything
+      y[pt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(mh, xv, y[pt], 0, 0, 0);
+      y[pt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ml, xv, y[pt], 0, 0, 0);
+    }
+    if (st < tt)
+#pragma unroll
+      for (int pt = 0; pt < PB; ++pt) xa[pt] = xn[pt];
+  }
+  // lane (li, g) register rr: token t0 + 4 g + rr, column 16 pt + li; xa holds x at the same places
+  const float D = a.d_skip[h];
+  bf16* yout = static_cast<bf16*>(a.y) + ((int64_t)rt.row0[r] + s_begin) * nh * P + (int64_t)h * P;
+#pragma unroll
+  for (int pt = 0; pt < PB; ++pt) {
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int tq = t0 + 4 * g + rr;
+      if (tq < len) {
+        // the element goes through a scalar first: a bit cast of a vector element itself reads the
+        // vector's first element
+        const short xe = xa[pt][rr];
+        const float xq = static_cast<float>(__builtin_bit_cast(bf16, xe));
+        yout[(int64_t)tq * nh * P + 16 * pt + li] = from_f32<bf16>(y[pt][rr] + expf(cum[tq]) * ys[pt][rr] + D * xq);
       }
     }
   }
@@ -827,7 +857,7 @@ static hipError_t launch_y_mfma_t(const Shape& sh, const ScanArgs& a, const ReqT
                                   hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 256);
   });
   if (set_err != hipSuccess) return set_err;
-  hipLaunchKernelGGL(k_ssd_y_mfma<PB>, dim3(a.total_segs * sh.nh), dim3(256), lds, s, sh, a, rt);
+  hipLaunchKernelGGL(k_ssd_y_mfma<PB>, dim3(a.total_segs * sh.nh), dim3(512), lds, s, sh, a, rt);
   return hipGetLastError();
 }
 
