@@ -96,6 +96,12 @@ Y_CASES = [
     ("phi4_bf16_L256", I.PHI4_LONG, [255, 300]),
     ("odd_bf16", small_shape("bf16", n_heads=3, head_dim=48, d_state=80, n_groups=3, chunk=32), [1, 100]),
     ("odd_fp32", small_shape("f32", n_heads=6, head_dim=32, d_state=48, n_groups=2, chunk=32), [37, 260]),
+    # one 16-dimension tile per head with 256 state columns (16 feature groups, the largest LDS
+    # staging of the bf16 kernel), lengths on and past 16-token tile edges and a whole block
+    ("wide_state_bf16", small_shape("bf16", n_heads=2, head_dim=16, d_state=256, n_groups=1, chunk=32),
+     [16, 17, 128, 129]),
+    # seven dimension tiles (the state read per feature group, not one ahead)
+    ("p112_bf16", small_shape("bf16", n_heads=2, head_dim=112, d_state=32, n_groups=2, chunk=32), [33]),
 ]
 
 
