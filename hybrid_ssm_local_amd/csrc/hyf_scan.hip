@@ -548,7 +548,8 @@ __global__ void __launch_bounds__(256) k_ssd_y(Shape sh, ScanArgs a, ReqTable rt
 //   M[t][s] = exp(cum_t - cum_s) dt_s G[t][s] is the A operand of Y += M X, M entering as two bf16
 //   terms (hi, lo) and X as 8-byte pieces of the tiled x read from global memory one step ahead;
 // and the state term sum_n C[t][n] H0[p][n], H0 (fp32, global, one feature group ahead up to 96
-// head dimensions) as two bf16 terms.  The x pieces of the diagonal step (s = t) are the x_t the skip term D x_t needs.
+// head dimensions) as two bf16 terms.  The x pieces of the diagonal step (s = t) are the x_t the
+// skip term D x_t needs.
 // Inputs past the block's length hold anything: B and C there are zeroed before the turn (a product
 // with I_h sums every token of the run), their scores are replaced by 0 and their x pieces read as 0.
 template <int PB>
