@@ -136,6 +136,22 @@ def test_scan_full_size_qwen_prefix_sampled_heads():
         assert_close(H[sl], ref, "bf16", f"head {h}")
 
 
+def test_scan_full_size_qwen_prefix_per_token_outputs_sampled_heads():
+    # The 8192-token Qwen-shaped prefix with per-token outputs, at the size the benchmark runs the
+    # y-mode kernels (64 blocks x 32 heads); the oracle checks the final state and y on 3 of 32 heads.
+    shape, T = I.QWEN, 8192
+    sc = I.make_scan_inputs(shape, T, I.rng_streams(13)[0], with_c=True, h0_scale=0.5)
+    sc["C"] = sc["C"] * np.float32(2.0 ** -round(np.log2(np.sqrt(shape.d_state))))
+    say("hyf_ssd_scan y qwen T", T)
+    H, y = run_scan(shape, sc, T, with_y=True)
+    for h in (0, 17, 31):
+        sl = slice(h, h + 1)
+        refH, refy = O.ssd_sequential(sc["x"][:, sl], sc["B"], sc["C"], sc["dt_raw"][:, sl], sc["a_log"][sl],
+                                      sc["dt_bias"][sl], sc["d_skip"][sl], sc["H0"][sl])
+        assert_close(H[sl], refH, "bf16", f"head {h} H")
+        assert_close(y[:, sl], refy, "bf16", f"head {h} y")
+
+
 def test_scan_is_deterministic():
     shape, T = I.QWEN, 3000
     sc = I.make_scan_inputs(shape, T, I.rng_streams(12)[0], with_c=False, h0_scale=0.5)
