@@ -744,6 +744,8 @@ k_ssd_y_mfma(Shape sh, ScanArgs a, ReqTable rt) {
 }
 
 bool scan_y_supported(const Shape& sh, int esz) {
+  // bf16 heads of up to 128 dimensions take the matrix-core kernel, which stages B and C only
+  if (esz == 2 && sh.P <= 128) return (size_t)2 * sh.N * TB * 2 + 2 * TB * sizeof(float) <= 160 * 1024 - 256;
   return (size_t)TB * (sh.P + 2 * sh.N) * esz + 2 * TB * sizeof(float) <= 160 * 1024 - 256;
 }
 

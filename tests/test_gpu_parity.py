@@ -102,6 +102,8 @@ Y_CASES = [
      [16, 17, 128, 129]),
     # seven dimension tiles (the state read per feature group, not one ahead)
     ("p112_bf16", small_shape("bf16", n_heads=2, head_dim=112, d_state=32, n_groups=2, chunk=32), [33]),
+    # 128 dimensions with 256 state columns: only the matrix-core kernel's LDS (B and C) fits
+    ("p128_n256_bf16", small_shape("bf16", n_heads=2, head_dim=128, d_state=256, n_groups=1, chunk=32), [130]),
 ]
 
 
