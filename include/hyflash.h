@@ -179,8 +179,10 @@ int hyf_state_reset(const hyf_config* cfg, void* state_pool, int32_t pool_slots,
  * solves, then one state update per chunk; the workspace then holds (N + P + 1) * 64 + 4 floats
  * per chunk and head, which hyf_workspace_bytes includes); y_opt is HYF_EUNSUPPORTED.
  * y_opt (nullable, 16-byte aligned): [cu_rows[n_req]][nh][P] storage dtype, per-token memory
- * outputs y_t = H_t . C_t + D * v_t (H_t after token t, C_t from w_in); HYF_EUNSUPPORTED when a
- * 128-token block of x, B and C does not fit one workgroup's LDS (fp32 with P + 2N > 320).
+ * outputs y_t = H_t . C_t + D * v_t (H_t after token t, C_t from w_in); HYF_EUNSUPPORTED when
+ * the staged 128-token block does not fit one workgroup's LDS: x, B and C for fp32 (P + 2N >= 320)
+ * and for bf16 heads of more than 128 dimensions (P + 2N >= 640); B and C alone for other bf16
+ * heads, which always fit.
  * ws: at least hyf_workspace_bytes(cfg, n_req, cu_rows[n_req], y_opt != NULL) bytes, 256-byte
  * aligned. */
 int hyf_memory_commit(const hyf_config* cfg, const hyf_weights* w, void* state_pool,
