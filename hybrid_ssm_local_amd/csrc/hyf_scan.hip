@@ -540,6 +540,104 @@ __global__ void __launch_bounds__(256) k_ssd_y(Shape sh, ScanArgs a, ReqTable rt
   }
 }
 
+// y-mode block states on bf16 matrix cores: one workgroup per (block, head) forms the block's own
+// contribution to the state, S[p][n] = sum_t w_t x_t[p] B_t[n] with w_t = dt_t exp(suf_t) and suf_t
+// the log-decay of the block's tokens after t (a request's first block adds exp(Lam) H, Lam the
+// block's total log-decay, which goes to lam).  The transposed product S^T = (w B)^T x^T is one
+// 16x16x32 MFMA chain per 16 x 16 output tile whose operands are the tiled layouts as they stand:
+// lane (i, g) of tile (fg, j) of B holds feature 16 fg + i at tokens 32 j + 8 g .. + 7 (the A
+// operand, scaled by the weights and split into two bf16 terms, hi and lo), and lane (i, g) of
+// tile (pt, j) of x holds feature 16 pt + i at the same tokens (the B operand).  Accumulator
+// register r of lane (i, g) is S[16 pt + i][16 fg + 4 g + r]: one 16-byte store per lane and tile.
+// Wave w owns the feature groups w, w + 4, ...  Tokens past the block's length are zeroed on both
+// operands (their stored values may be anything).
+template <int PB>
+__global__ void __launch_bounds__(256) k_ssd_blk_state(Shape sh, ScanArgs a, ReqTable rt) {
+  constexpr int NJ = TB / 32;  // 32-token runs of a block
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ float s_lam;
+  const int nh = sh.nh, P = 16 * PB, N = sh.N, NFG = N / 16;
+  const int h = blockIdx.x % nh, q = blockIdx.x / nh;
+  const int r = find_request(rt, q);
+  const int ls = q - rt.seg0[r];
+  const int Tr = rt.row0[r + 1] - rt.row0[r];
+  const int len = min(TB, Tr - ls * TB);
+  const int64_t blk = rt.blk0[r] + ls;  // y-mode segments are single blocks
+  const int grp = h / (nh / sh.G);
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int li = lane & 15, g = lane >> 4;
+  char* xs = smem;                                           // x: PB x NJ tiles of 1 KiB
+  char* bs = smem + PB * NJ * 1024;                          // B: NFG x NJ tiles
+  float* wt = reinterpret_cast<float*>(bs + NFG * NJ * 1024);  // [TB] raw steps, then weights
+  const bf16* gx = static_cast<const bf16*>(a.x) + blk * a.xblk + (int64_t)h * P * TB;
+  const bf16* gb = static_cast<const bf16*>(a.B) + blk * a.bblk + (int64_t)grp * N * TB;
+  const float* gd = a.dt + blk * a.dblk + (int64_t)h * TB;
+  lds_stage16<256>(P * TB / 8, xs, [&](int i) { return gx + (int64_t)i * 8; });
+  lds_stage16<256>(N * TB / 8, bs, [&](int i) { return gb + (int64_t)i * 8; });
+  lds_stage16<256>(TB / 4, wt, [&](int i) { return gd + 4 * i; });
+  vm_wait<0>();
+  __syncthreads();
+  if (wave == 0) {
+    // lane l holds tokens 2 l, 2 l + 1; a = dt A (0 past len); the log-decay after a token is a
+    // suffix sum over the lanes (a sum of later log-decays, never a difference of prefixes)
+    const float A = -expf(a.a_log[h]), bias = a.dt_bias[h];
+    const int u0 = 2 * lane;
+    const float d0 = u0 < len ? softplus_f(wt[u0] + bias) : 0.f;
+    const float d1 = u0 + 1 < len ? softplus_f(wt[u0 + 1] + bias) : 0.f;
+    const float a0 = d0 * A, a1 = d1 * A;
+    float inc = a0 + a1;  // sum over this lane and the lanes after it
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float v = __shfl_down(inc, o, 64);
+      if (lane + o < 64) inc += v;
+    }
+    const float after = inc - (a0 + a1);  // tokens after 2 l + 1
+    wt[u0] = d0 * expf(after + a1);
+    wt[u0 + 1] = d1 * expf(after);
+    if (lane == 0) s_lam = inc;
+  }
+  __syncthreads();
+  const float lam = s_lam;
+  const float el = expf(lam);
+  const float* Hh = a.h_direct ? a.h_direct + (int64_t)h * P * N
+                               : reinterpret_cast<const float*>(a.state_pool + (int64_t)rt.slot[r] * sh.st_bytes +
+                                                                sh.st_h) + (int64_t)h * P * N;
+  float* dst = a.part + ((int64_t)q * nh + h) * P * N;
+  for (int fg = wave; fg < NFG; fg += 4) {
+    bf16x8 ah[NJ], al[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(bs + (fg * NJ + j) * 1024 + 16 * lane);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int tok = 32 * j + 8 * g + e;
+        const float v = tok < len ? wt[tok] * static_cast<float>(b[e]) : 0.f;
+        const bf16 hb = static_cast<bf16>(v);
+        ah[j][e] = hb;
+        al[j][e] = static_cast<bf16>(v - static_cast<float>(hb));
+      }
+    }
+#pragma unroll
+    for (int pt = 0; pt < PB; ++pt) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        bf16x8 xv = *reinterpret_cast<const bf16x8*>(xs + (pt * NJ + j) * 1024 + 16 * lane);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (32 * j + 8 * g + e >= len) xv[e] = static_cast<bf16>(0.f);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[j], xv, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[j], xv, acc, 0, 0, 0);
+      }
+      const int64_t o = (int64_t)(16 * pt + li) * N + 16 * fg + 4 * g;
+      if (ls == 0) acc += el * *reinterpret_cast<const f32x4*>(Hh + o);
+      *reinterpret_cast<f32x4*>(dst + o) = acc;
+    }
+  }
+  if (t == 0) a.lam[(int64_t)q * nh + h] = lam;
+}
+
 // y-mode outputs of a bf16 block on bf16 matrix cores (16x16x16, fp32 sums), the same chunked
 // form as k_ssd_y, with eight waves: wave w owns output tile w (tokens 16 w .. 16 w + 15).
 // B and C of the block go to LDS in their tiled layout and are turned in place, one 1 KiB tile (16
@@ -888,10 +986,44 @@ static hipError_t launch_y(const Shape& sh, const ScanArgs& a, const ReqTable& r
   return sh.P > 128 ? launch_y_t<T, 16>(sh, a, rt, s) : launch_y_t<T, 8>(sh, a, rt, s);
 }
 
+template <int PB>
+static hipError_t launch_blk_state_t(const Shape& sh, const ScanArgs& a, const ReqTable& rt, hipStream_t s) {
+  const size_t lds = (size_t)(PB + sh.N / 16) * (TB / 32) * 1024 + TB * sizeof(float);
+  static std::once_flag once;
+  static hipError_t set_err = hipSuccess;
+  std::call_once(once, [] {
+    set_err = hipFuncSetAttribute(reinterpret_cast<const void*>(k_ssd_blk_state<PB>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 256);
+  });
+  if (set_err != hipSuccess) return set_err;
+  hipLaunchKernelGGL(k_ssd_blk_state<PB>, dim3(a.total_segs * sh.nh), dim3(256), lds, s, sh, a, rt);
+  return hipGetLastError();
+}
+
+// The states of y-mode blocks: bf16 heads of up to 128 dimensions on the matrix-core block kernel,
+// the rest on the segment kernel (segments of one block).
+static hipError_t launch_y_states(int dtype, const Shape& sh, const ScanArgs& a, const ReqTable& rt, hipStream_t s) {
+  if (dtype == HYF_BF16) {
+    switch (sh.P / 16) {
+      case 1: return launch_blk_state_t<1>(sh, a, rt, s);
+      case 2: return launch_blk_state_t<2>(sh, a, rt, s);
+      case 3: return launch_blk_state_t<3>(sh, a, rt, s);
+      case 4: return launch_blk_state_t<4>(sh, a, rt, s);
+      case 5: return launch_blk_state_t<5>(sh, a, rt, s);
+      case 6: return launch_blk_state_t<6>(sh, a, rt, s);
+      case 7: return launch_blk_state_t<7>(sh, a, rt, s);
+      case 8: return launch_blk_state_t<8>(sh, a, rt, s);
+      default: return launch_seg<bf16>(sh, a, rt, s);
+    }
+  }
+  return launch_seg<float>(sh, a, rt, s);
+}
+
 hipError_t launch_ssd_state(int dtype, const Shape& sh, const ScanArgs& a, const ReqTable& rt,
                             int32_t max_segs_per_req, hipStream_t s) {
   if (a.total_segs <= 0) return hipSuccess;
-  hipError_t e = dtype == HYF_BF16 ? launch_seg<bf16>(sh, a, rt, s) : launch_seg<float>(sh, a, rt, s);
+  hipError_t e = a.y_mode ? launch_y_states(dtype, sh, a, rt, s)
+                          : dtype == HYF_BF16 ? launch_seg<bf16>(sh, a, rt, s) : launch_seg<float>(sh, a, rt, s);
   if (e != hipSuccess) return e;
   const int64_t PN = (int64_t)sh.P * sh.N;
   dim3 grid((unsigned)rt.n_req * sh.nh, (unsigned)((PN / 4 + 255) / 256));
