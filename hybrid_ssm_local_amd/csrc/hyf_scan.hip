@@ -27,9 +27,10 @@
 // (H = P_0, then H = exp(lam_s) H + P_s).  No atomics: the result is deterministic.
 //
 // With per-token outputs y_t = C_t H_t + D x_t (y-mode) the segments are single blocks:
-// k_ssd_seg gives every block's own state, k_ssd_prefix folds them in order into the state before
-// each block (and the final H), and k_ssd_y_mfma (bf16) or k_ssd_y computes each block's outputs in
-// the chunk form from the state before it.
+// k_ssd_blk_state (bf16 heads of up to 128 dimensions) or k_ssd_seg gives every block's own state,
+// k_ssd_prefix folds them in order into the state before each block (and the final H), and
+// k_ssd_y_mfma (the same bf16 heads) or k_ssd_y computes each block's outputs in the chunk form
+// from the state before it.
 #include <array>
 #include <mutex>
 #include <utility>
