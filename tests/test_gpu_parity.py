@@ -163,6 +163,17 @@ def test_scan_is_deterministic():
     assert np.array_equal(a, b)
 
 
+def test_scan_per_token_outputs_are_deterministic():
+    # The y-mode kernels use no atomics: the final state and every output repeat bit for bit.
+    shape, T = I.QWEN, 3000
+    sc = I.make_scan_inputs(shape, T, I.rng_streams(14)[0], with_c=True, h0_scale=0.5)
+    say("hyf_ssd_scan y determinism")
+    Ha, ya = run_scan(shape, sc, T, with_y=True)
+    Hb, yb = run_scan(shape, sc, T, with_y=True)
+    assert np.array_equal(Ha, Hb)
+    assert np.array_equal(ya, yb)
+
+
 def test_scan_zero_length_is_a_noop():
     shape = I.TINY
     sc = I.make_scan_inputs(shape, 4, I.rng_streams(13)[0], with_c=False, h0_scale=1.0)
